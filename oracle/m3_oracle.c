@@ -1,0 +1,206 @@
+/*
+ * m3_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, sequential fp64 CPU evaluation of the Mamba-3 SSM core
+ * recurrence.  It exists to check the HIP library; nothing in the library
+ * may call, link or load it.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header or
+ * constant with the HIP path.
+ *
+ * What it computes (one (batch, head) pair at a time, one token at a time):
+ *
+ *   exponential-trapezoidal three-term update
+ *     [xxxxx.co.kr Mamba-3 article ("2배 작은 상태 크기와 향상된 MIMO 디코딩
+ *      하드웨어 효율..."), section 1.1, the h_t equation]:
+ *       alpha_t = exp(dt_t * A_t)
+ *       beta_t  = (1 - lam_t) * dt_t * alpha_t
+ *       gamma_t = lam_t * dt_t
+ *       h_t = alpha_t h_{t-1} + beta_t B_{t-1} x_{t-1} + gamma_t B_t x_t
+ *
+ *   complex-valued state [same article, section 1.2 ("RoPE trick")]: the
+ *     state's N columns are N/2 complex numbers (column 2k = real part,
+ *     2k+1 = imaginary part).  The discretised transition of pair k is the
+ *     complex number exp(dt_t (A_t + i theta_{t,k})); its modulus is
+ *     alpha_t and its phase phi_{t,k} = dt_t * theta_{t,k}.  Both the
+ *     decayed state and the left-endpoint (beta) term carry that factor;
+ *     the right-endpoint (gamma) term is taken at the current time and is
+ *     not rotated.  The output is the real dot product y = h C, i.e.
+ *     Re(sum_k conj(c_k) h_k).
+ *
+ *   MIMO rank R [same article, section 1.3]: x_t is P x R, B_t and C_t are
+ *     N x R, the input terms are the P x N matrix products X B^T and the
+ *     output is the P x R matrix h C.  R = 1 is the single-input form.
+ *
+ * Readings where the pages leave a choice open (each is shared with the
+ * HIP path and listed in the design notes): phase = dt * theta unless
+ * M3REF_THETA_IS_ANGLE; theta has one angle per complex pair per head per
+ * token; pairs are adjacent columns (2k, 2k+1); the state is multiplied by
+ * e^{+i phi}; the token before t = 0 is x_prev/B_prev (zero when NULL);
+ * A is per head unless M3REF_A_PER_TOKEN; dt and lam arrive already
+ * activated; no skip term, gate or normalisation is applied.
+ *
+ * Layouts (dense, row-major, last index fastest):
+ *   x      [Bsz, T, H, P, R]      B, C  [Bsz, T, H, N, R]
+ *   dt,lam [Bsz, T, H]            theta [Bsz, T, H, N/2]
+ *   A      [H] (or [Bsz, T, H] with M3REF_A_PER_TOKEN)
+ *   h0, hT [Bsz, H, P, N]         x_prev [Bsz, H, P, R]   B_prev [Bsz, H, N, R]
+ *   y      [Bsz, T, H, P, R]
+ * The decode step uses the same layouts without the T axis.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define M3REF_THETA_IS_ANGLE 1u
+#define M3REF_A_PER_TOKEN 2u
+
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, rank;
+  uint32_t flags;
+} m3ref_dims;
+
+/* One token of the recurrence for one (batch, head): S is P x N, updated in
+ * place; xp/bp are the previous token's x (P x R) and B (N x R) or NULL for
+ * zero; x/b/c the current token's; y (P x R) receives S C. */
+static void m3ref_token(int64_t P, int64_t N, int64_t R, uint32_t flags,
+                        double* S, const double* xp, const double* bp,
+                        const double* x, const double* b, const double* c,
+                        double dt, double A, double lam, const double* theta,
+                        double* y) {
+  const double alpha = exp(dt * A);
+  const double beta = (1.0 - lam) * dt * alpha;
+  const double gamma = lam * dt;
+
+  /* decay, then the left-endpoint input term (both get the full-step factor) */
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N; ++n) {
+      double s = alpha * S[p * N + n];
+      if (xp && bp) {
+        double u = 0.0;
+        for (int64_t r = 0; r < R; ++r) u += xp[p * R + r] * bp[n * R + r];
+        s += beta * u;
+      }
+      S[p * N + n] = s;
+    }
+
+  /* phase of the complex eigenvalue: rotate every (2k, 2k+1) pair by +phi */
+  for (int64_t k = 0; k < N / 2; ++k) {
+    const double phi = (flags & M3REF_THETA_IS_ANGLE) ? theta[k] : dt * theta[k];
+    const double cs = cos(phi), sn = sin(phi);
+    for (int64_t p = 0; p < P; ++p) {
+      const double re = S[p * N + 2 * k], im = S[p * N + 2 * k + 1];
+      S[p * N + 2 * k] = cs * re - sn * im;
+      S[p * N + 2 * k + 1] = sn * re + cs * im;
+    }
+  }
+
+  /* right-endpoint input term, taken at the current time: not rotated */
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t n = 0; n < N; ++n) {
+      double u = 0.0;
+      for (int64_t r = 0; r < R; ++r) u += x[p * R + r] * b[n * R + r];
+      S[p * N + n] += gamma * u;
+    }
+
+  /* output y = S C  (P x R) */
+  for (int64_t p = 0; p < P; ++p)
+    for (int64_t r = 0; r < R; ++r) {
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) acc += S[p * N + n] * c[n * R + r];
+      y[p * R + r] = acc;
+    }
+}
+
+static int m3ref_check(const m3ref_dims* d) {
+  if (!d) return 1;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 0) return 2;
+  if (d->headdim <= 0 || d->dstate <= 0 || d->rank <= 0) return 2;
+  if (d->dstate % 2) return 2;
+  return 0;
+}
+
+/* Full sequential scan: y (and hT when non-NULL) from x, dt, A, lam, theta,
+ * B, C, the initial state h0 (NULL = 0) and the token before the first one
+ * (x_prev/B_prev, NULL = 0).  nthreads <= 0 lets OpenMP choose. */
+int m3ref_scan(const m3ref_dims* d, const double* x, const double* dt,
+               const double* A, const double* lam, const double* theta,
+               const double* B, const double* C, const double* h0,
+               const double* x_prev, const double* B_prev, double* y,
+               double* hT, int nthreads) {
+  int rc = m3ref_check(d);
+  if (rc) return rc;
+  const int64_t Bsz = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim,
+                N = d->dstate, R = d->rank;
+  const int64_t units = Bsz * H;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t b = u / H, h = u % H;
+    double* S = (double*)malloc(sizeof(double) * P * N);
+    if (h0)
+      memcpy(S, h0 + (b * H + h) * P * N, sizeof(double) * P * N);
+    else
+      memset(S, 0, sizeof(double) * P * N);
+    const double* xp = x_prev ? x_prev + (b * H + h) * P * R : NULL;
+    const double* bp = B_prev ? B_prev + (b * H + h) * N * R : NULL;
+    if (xp == NULL || bp == NULL) xp = bp = NULL; /* both or neither */
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t bth = (b * T + t) * H + h;
+      const double* xt = x + bth * P * R;
+      const double* bt = B + bth * N * R;
+      const double* ct = C + bth * N * R;
+      const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[bth] : A[h];
+      m3ref_token(P, N, R, d->flags, S, xp, bp, xt, bt, ct, dt[bth], a,
+                  lam[bth], theta + bth * (N / 2), y + bth * P * R);
+      xp = xt;
+      bp = bt;
+    }
+    if (hT) memcpy(hT + (b * H + h) * P * N, S, sizeof(double) * P * N);
+    free(S);
+  }
+  return 0;
+}
+
+/* One decode step: h (in/out, [Bsz,H,P,N]) advances by one token; y_t gets
+ * the output.  x_prev/B_prev NULL = 0.  A is [H] (or [Bsz,H] with the
+ * per-token flag).  seqlen is ignored. */
+int m3ref_decode_step(const m3ref_dims* d, double* h, const double* x_t,
+                      const double* x_prev, const double* B_t,
+                      const double* B_prev, const double* C_t,
+                      const double* dt_t, const double* A,
+                      const double* lam_t, const double* theta_t, double* y_t,
+                      int nthreads) {
+  int rc = m3ref_check(d);
+  if (rc) return rc;
+  const int64_t Bsz = d->batch, H = d->nheads, P = d->headdim, N = d->dstate,
+                R = d->rank;
+  const int64_t units = Bsz * H;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t h_ = u % H;
+    const double* xp = (x_prev && B_prev) ? x_prev + u * P * R : NULL;
+    const double* bp = (x_prev && B_prev) ? B_prev + u * N * R : NULL;
+    const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[u] : A[h_];
+    m3ref_token(P, N, R, d->flags, h + u * P * N, xp, bp, x_t + u * P * R,
+                B_t + u * N * R, C_t + u * N * R, dt_t[u], a, lam_t[u],
+                theta_t + u * (N / 2), y_t + u * P * R);
+  }
+  return 0;
+}
+
+int m3ref_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
