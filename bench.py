@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Benchmark of libm3ssm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline: the SISO decode step at B=128, H=64, P=64, N=128 (bf16 inputs, fp32
+state carried in HBM): K sequential steps after W warm-up steps, every step a
+fresh token from a pool of distinct resident input sets, the state updated in
+place.  `value` is the algorithmic HBM traffic of the K steps divided by their
+wall time on the GPU (GB/s); `us_per_step` is the same time per step.
+`roofline` compares the decode kernel's average duration (HIP events around
+each launch, on the launch stream) with the 8 TB/s HBM peak.
+
+In the same run and the same JSON line, under "workloads": the MIMO rank-4
+decode step (same shape), the SISO chunked prefill (B=4, T=2048, H=32) and the
+MIMO rank-4 long prefill (B=1, T=16384, H=64), each with its own timing and
+roofline fraction, and the fp64 CPU oracle timed on a bounded sample of each
+workload (`cpu_baseline`, a reported baseline only).
+
+Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-step µs & HBM GB/s at B=128,H=64,P=64,N=128; prefill tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (each input read once, outputs written once, state read
+# and written once)
+def decode_bytes(w, in_bytes=2, out_bytes=4):
+    B, H, P, N, R = w.batch, w.nheads, w.headdim, w.dstate, w.rank
+    state = 2 * B * H * P * N * 4
+    inputs = in_bytes * (2 * B * H * P * R + 3 * B * H * N * R + 2 * B * H + B * H * N // 2)
+    return state + inputs + H * 4 + out_bytes * B * H * P * R
+
+
+def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True):
+    B, T, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
+    inputs = in_bytes * (B * T * H * P * R + 2 * B * T * H * N * R + 2 * B * T * H
+                         + B * T * H * N // 2)
+    states = (int(h0) + int(hT)) * B * H * P * N * 4
+    return inputs + states + H * 4 + out_bytes * B * T * H * P * R
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_recurrent_sequence_mamba_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_tag)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def bench_decode(name, steps, warmup, pool_n=8):
+    import torch
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    pool_n = max(2, min(pool_n, steps + warmup))
+    t0 = time.time()
+    pool = []
+    for s in range(pool_n):
+        d = I.decode_step_inputs(w, s)
+        pool.append({k: v.to(dev) for k, v in d.items()})
+    log(f"[{name}] generated {pool_n} input sets in {time.time() - t0:.1f}s")
+    h = I.decode_state(w).to(dev)
+    A = I.head_decay(w).to(dev)
+    y = torch.empty((w.batch, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
+    dims = m3.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32)
+    stream = torch.cuda.current_stream()
+    # validate every argument set once through the checked binding ...
+    for s in range(pool_n):
+        cur, prev = pool[s], pool[(s - 1) % pool_n]
+        m3.m3_decode_step(dims, h, cur["x"], prev["x"], cur["B"], prev["B"], cur["C"], cur["dt"],
+                          A, cur["lam"], cur["theta"], y)
+    torch.cuda.synchronize()
+    # ... then launch through the raw entry point (argument marshalling only)
+    lib = m3.library()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    args = []
+    for s in range(pool_n):
+        cur, prev = pool[s], pool[(s - 1) % pool_n]
+        args.append((ctypes.byref(dims), p(h), p(cur["x"]), p(prev["x"]), p(cur["B"]), p(prev["B"]),
+                     p(cur["C"]), p(cur["dt"]), p(A), p(cur["lam"]), p(cur["theta"]), p(y), sp))
+
+    def launch(s):
+        st = lib.m3_decode_step(*args[s % pool_n])
+        if st != 0:
+            raise RuntimeError(f"m3_decode_step failed: {m3.m3_status_str(st)}")
+
+    for s in range(warmup):
+        launch(s)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(steps):
+        ev0[s].record(stream)
+        launch(warmup + s)
+        ev1[s].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    kms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
+    kern_ms = sum(kms) / len(kms)
+    nbytes = decode_bytes(w)
+
+    # the same K steps replayed from a HIP graph (launch overhead removed)
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                cap = torch.cuda.current_stream()
+                gargs = [a[:-1] + (ctypes.c_void_p(cap.cuda_stream),) for a in args]
+                for s in range(min(steps, 64)):
+                    st = lib.m3_decode_step(*gargs[s % pool_n])
+                    if st != 0:
+                        raise RuntimeError(m3.m3_status_str(st))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // min(steps, 64))
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / (reps * min(steps, 64))
+    except Exception as exc:  # graph capture is reported, not required
+        log(f"[{name}] graph replay skipped: {exc}")
+    return dict(workload=w, steps=steps, total_ms=total_ms, step_ms=total_ms / steps,
+                kernel_ms=kern_ms, kernel_p50_ms=kms[len(kms) // 2], wall_s=wall,
+                bytes=nbytes, graph_step_ms=graph_ms, pool=pool_n)
+
+
+def bench_prefill(name, steps, warmup):
+    import torch
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    n_sets = 2 if prefill_bytes(w) < 1e9 else 1   # two sets when one would fit in cache
+    sets = []
+    for s in range(n_sets):
+        d = I.prefill_inputs(w, stream=s)
+        sets.append({k: (None if v is None else v.to(dev)) for k, v in d.items()})
+    log(f"[{name}] generated {n_sets} input set(s) in {time.time() - t0:.1f}s")
+    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk,
+                        m3.M3_BF16, m3.M3_F32)
+    ws = m3.workspace(dims, dev)
+    y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
+    hT = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch(s):
+        d = sets[s % n_sets]
+        m3.m3_scan_prefill(dims, d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"],
+                           None, None, None, y, hT, ws, stream)
+
+    for s in range(warmup):
+        launch(s)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for s in range(steps):
+        ev0[s].record(stream)
+        launch(warmup + s)
+        ev1[s].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
+    call_ms = sum(ms) / len(ms)
+    return dict(workload=w, steps=steps, call_ms=call_ms, call_p50_ms=ms[len(ms) // 2],
+                bytes=prefill_bytes(w), tokens=w.batch * w.seqlen, ws_bytes=ws.numel())
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on a bounded sample
+def cpu_decode(name, budget_s=8.0):
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+    from oracle import oracle
+    import numpy as np
+
+    w = I.WORKLOADS[name]
+    nb = 16  # batch rows of the sample; every head
+    d = I.decode_step_inputs(w, 0)
+    f = {k: I.to_f64(v)[:nb] for k, v in d.items()}
+    h = I.to_f64(I.decode_state(w))[:nb]
+    A = I.to_f64(I.head_decay(w))
+    oracle.load()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        y, h = oracle.decode_step(h, f["x"], f["x"], f["B"], f["B"], f["C"], f["dt"], A,
+                                  f["lam"], f["theta"])
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    full_s = el / steps * (w.batch / nb)
+    return dict(value=round(decode_bytes(w) / full_s / 1e9, 3), unit="GB/s",
+                us_per_step=round(full_s * 1e6, 1), cores=oracle.max_threads(), kind="oracle",
+                sample=f"{steps} decode steps of {nb} of {w.batch} batch rows x {w.nheads} heads "
+                       f"(fp64, OpenMP over (b,h)); time scaled by {w.batch // nb} to the full step")
+
+
+def cpu_prefill(name, heads, tokens, budget_note=""):
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+    from oracle import oracle
+
+    w = I.WORKLOADS[name]
+    ws = w.with_(batch=1, seqlen=tokens, nheads=heads)
+    d = I.prefill_inputs(ws)
+    f = {k: I.to_f64(v) for k, v in d.items()}
+    t0 = time.perf_counter()
+    oracle.scan(f["x"], f["dt"], f["A"], f["lam"], f["theta"], f["B"], f["C"])
+    el = time.perf_counter() - t0
+    # heads and tokens are independent/sequential units of identical work
+    full_s = el * (w.nheads / heads) * (w.batch) * (w.seqlen / tokens)
+    return dict(value=round(w.batch * w.seqlen / full_s, 1), unit="tokens/s",
+                cores=oracle.max_threads(), kind="oracle",
+                sample=f"{heads} heads x {tokens} tokens of one sequence (fp64); time scaled "
+                       f"linearly to {w.batch} x {w.seqlen} tokens x {w.nheads} heads")
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of workloads to run (default all)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode and prefill kernels run on a "
+              "single MI355X; multi-GPU runs are not part of this library.", file=sys.stderr)
+        sys.exit(2)
+    if a.steps < 1 or a.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    m3.library()  # fail loudly if the HIP library is missing
+    only = set(x for x in a.only.split(",") if x)
+    want = lambda n: not only or n in only
+
+    res = {}
+    if want("siso_decode"):
+        res["siso_decode"] = bench_decode("siso_decode", a.steps, a.warmup)
+    if want("mimo_decode"):
+        res["mimo_decode"] = bench_decode("mimo_decode", a.steps, a.warmup)
+    if want("siso_prefill"):
+        res["siso_prefill"] = bench_prefill("siso_prefill", a.prefill_steps, 2)
+    if want("mimo_prefill"):
+        res["mimo_prefill"] = bench_prefill("mimo_prefill", a.prefill_steps, 2)
+
+    cpu = {}
+    if not a.no_cpu_baseline:
+        t0 = time.time()
+        if "siso_decode" in res:
+            cpu["siso_decode"] = cpu_decode("siso_decode", 8.0)
+        if "mimo_decode" in res:
+            cpu["mimo_decode"] = cpu_decode("mimo_decode", 6.0)
+        if "siso_prefill" in res:
+            cpu["siso_prefill"] = cpu_prefill("siso_prefill", heads=8, tokens=2048)
+        if "mimo_prefill" in res:
+            cpu["mimo_prefill"] = cpu_prefill("mimo_prefill", heads=4, tokens=4096)
+        log(f"cpu baselines took {time.time() - t0:.1f}s")
+
+    def decode_entry(r, tag):
+        w = r["workload"]
+        gbs = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
+        ach = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        traffic = counters_for(tag)
+        return dict(
+            us_per_step=round(r["step_ms"] * 1e3, 2), kernel_us=round(r["kernel_ms"] * 1e3, 2),
+            kernel_p50_us=round(r["kernel_p50_ms"] * 1e3, 2),
+            graph_us_per_step=None if r["graph_step_ms"] is None else round(r["graph_step_ms"] * 1e3, 2),
+            hbm_gbs=round(gbs, 1), tokens_per_s=round(w.batch / (r["step_ms"] * 1e-3), 1),
+            algorithmic_bytes=r["bytes"], input_pool=r["pool"],
+            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
+                          kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}"),
+            cpu_baseline=cpu.get(tag))
+
+    def prefill_entry(r, tag):
+        ach = r["bytes"] / (r["call_ms"] * 1e-3) / 1e9
+        return dict(
+            ms_per_call=round(r["call_ms"], 4), p50_ms=round(r["call_p50_ms"], 4),
+            tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
+            algorithmic_bytes=r["bytes"], workspace_bytes=r["ws_bytes"],
+            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                          kernel="whole call (k_chunk_state + k_state_pass + k_chunk_output)"),
+            cpu_baseline=cpu.get(tag))
+
+    workloads = {}
+    for tag, r in res.items():
+        workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
+
+    head = res.get("siso_decode")
+    line = {"metric": METRIC}
+    if head is not None:
+        e = workloads["siso_decode"]
+        line.update(value=e["hbm_gbs"], unit="GB/s", n_gpus=1, steps=a.steps, warmup=a.warmup,
+                    ms_per_step=round(head["step_ms"], 5), us_per_step=e["us_per_step"],
+                    higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                    data="synthetic",
+                    config={"workload": "SISO decode step B=128 H=64 P=64 N=128, bf16 inputs, "
+                                        "fp32 state in HBM updated in place",
+                            "batch": 128, "nheads": 64, "headdim": 64, "dstate": 128, "rank": 1,
+                            "input_dtype": "bf16", "state_dtype": "f32", "parallelism": "none"},
+                    roofline=e["roofline"], cpu_baseline=e["cpu_baseline"])
+    if "mimo_decode" in workloads and "siso_decode" in workloads:
+        workloads["mimo_decode"]["step_time_vs_siso"] = round(
+            workloads["mimo_decode"]["us_per_step"] / workloads["siso_decode"]["us_per_step"], 3)
+    line["workloads"] = workloads
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

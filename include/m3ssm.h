@@ -1,0 +1,133 @@
+/*
+ * m3ssm.h -- C ABI of libm3ssm: the Mamba-3 SSM core recurrence on gfx950.
+ *
+ * The library computes, for every (batch, head) pair independently, the
+ * exponential-trapezoidal three-term update
+ *
+ *     h_t = alpha_t h_{t-1} + beta_t B_{t-1} x_{t-1} + gamma_t B_t x_t,
+ *     alpha_t = exp(dt_t A_t), beta_t = (1 - lam_t) dt_t alpha_t,
+ *     gamma_t = lam_t dt_t
+ *
+ * [xxxxx.co.kr Mamba-3 article ("2배 작은 상태 크기와 향상된 MIMO 디코딩 하드웨어
+ * 효율..."), section 1.1, the h_t equation], with the complex-valued state
+ * of section 1.2 of the same article (pairs of state columns (2k, 2k+1) form
+ * one complex number whose transition has modulus alpha_t and phase
+ * phi_{t,k} = dt_t theta_{t,k}; the decayed state and the beta term carry the
+ * phase, the gamma term does not; computed in the "RoPE" frame, where B and
+ * C are rotated by minus the cumulative phase), and the MIMO rank-R form of
+ * section 1.3 (x_t is P x R, B_t and C_t are N x R, the output is P x R).
+ * The output of a token is y_t = h_t C_t (a real dot product over N).
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer, owned by the caller, dense
+ *    and row-major (last index fastest), 16-byte aligned.
+ *  - The library never allocates, frees or synchronises.  Work is queued on
+ *    `stream` (a hipStream_t passed as void*; NULL = the default stream) and
+ *    the call returns at once.  Argument checks run on the host before any
+ *    launch; a failed check returns its status and launches nothing.
+ *  - Launch failures return M3_ERR_HIP (m3_last_hip_error() gives the HIP
+ *    code).  Faults inside a kernel surface at the caller's next
+ *    synchronisation.  NaN/Inf inputs propagate; they are not checked.
+ *  - Calls are stateless and re-entrant; concurrent calls on different
+ *    streams must not share output or workspace buffers.
+ *
+ * Layouts (Bsz = batch, T = seqlen, H = nheads, P = headdim, N = dstate,
+ * R = rank):
+ *     x, y           [Bsz, T, H, P, R]      in_dtype / out_dtype
+ *     B, C           [Bsz, T, H, N, R]      in_dtype
+ *     dt, lam        [Bsz, T, H]            in_dtype (already activated)
+ *     theta          [Bsz, T, H, N/2]       in_dtype (one angle per pair)
+ *     A              [H] fp32, or [Bsz, T, H] fp32 with M3_A_PER_TOKEN
+ *     h0, hT, h      [Bsz, H, P, N]         fp32
+ *     x_prev         [Bsz, H, P, R]         in_dtype
+ *     B_prev         [Bsz, H, N, R]         in_dtype
+ * The decode step drops the T axis.  With R = 1 the trailing axis has size 1.
+ */
+#ifndef M3SSM_H
+#define M3SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  M3_OK = 0,
+  M3_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  M3_ERR_SHAPE = 2,       /* a size is <= 0, N is odd, ...                 */
+  M3_ERR_DTYPE = 3,       /* in_dtype / out_dtype not one of m3_dtype      */
+  M3_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this (P, N, R, Q)    */
+  M3_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned              */
+  M3_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required       */
+  M3_ERR_HIP = 7          /* a HIP launch failed                           */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+/* flags */
+#define M3_THETA_IS_ANGLE (1u << 0) /* phase phi_t = theta_t, not dt_t*theta_t */
+#define M3_A_PER_TOKEN (1u << 1)    /* A is [Bsz,T,H] fp32 instead of [H]      */
+
+typedef struct {
+  int32_t batch;     /* Bsz >= 1                                           */
+  int32_t seqlen;    /* T >= 1 (ignored by the decode step)                */
+  int32_t nheads;    /* H >= 1                                             */
+  int32_t headdim;   /* P                                                  */
+  int32_t dstate;    /* N, even                                            */
+  int32_t rank;      /* R >= 1; 1 = single input / single output           */
+  int32_t chunk;     /* prefill chunk length Q; 0 = library default (64)   */
+  int32_t in_dtype;  /* m3_dtype of x, B, C, dt, lam, theta, x_prev, B_prev */
+  int32_t out_dtype; /* m3_dtype of y                                      */
+  uint32_t flags;    /* M3_THETA_IS_ANGLE | M3_A_PER_TOKEN                 */
+} m3_dims;
+
+/* Bytes of device workspace m3_scan_prefill needs for `dims` (0 if dims is
+ * invalid).  The workspace holds per-chunk end states and per-chunk decay
+ * and phase totals; its contents on entry do not matter. */
+size_t m3_prefill_workspace_size(const m3_dims* dims);
+
+/* Chunked prefill scan over T tokens [the same article, sections 1.1-1.3;
+ * the pages name prefill kernels without giving their algorithm, and this
+ * one is the exact chunked evaluation of the recurrence]:
+ *   y  <- outputs y_t for t = 0..T-1
+ *   hT <- state after the last token (not written when NULL)
+ * h0 NULL means a zero initial state.  x_prev/B_prev give the token before
+ * t = 0 for the beta term of the first step (both NULL = zero); passing the
+ * previous call's last x and B makes a split scan equal the whole scan.
+ * h0 may alias hT; no other argument may alias an output.  A NaN or Inf in
+ * one token's inputs stays in its (batch, head) and in its chunk and later
+ * chunks, but may also reach the outputs of the earlier tokens of its own
+ * chunk (masked products multiply it by zero).
+ * ws must be at least m3_prefill_workspace_size(dims) bytes. */
+m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
+                          const float* A, const void* lam, const void* theta,
+                          const void* B, const void* C, const float* h0,
+                          const void* x_prev, const void* B_prev, void* y,
+                          float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step [the same article, sections 1.1-1.3]: the state h
+ * [Bsz,H,P,N] fp32 is advanced in place by the token (x_t, B_t, C_t, dt_t,
+ * lam_t, theta_t), with (x_prev, B_prev) the token before it (both NULL =
+ * zero), and y_t [Bsz,H,P,R] receives h_t C_t.  dims->seqlen is ignored;
+ * A is [H] (or [Bsz,H] with M3_A_PER_TOKEN).  h is read once and written
+ * once. */
+m3_status m3_decode_step(const m3_dims* dims, float* h, const void* x_t,
+                         const void* x_prev, const void* B_t,
+                         const void* B_prev, const void* C_t, const void* dt_t,
+                         const float* A, const void* lam_t,
+                         const void* theta_t, void* y_t, void* stream);
+
+/* Static, human-readable name of a status. */
+const char* m3_status_str(m3_status status);
+
+/* The HIP error code of the last M3_ERR_HIP returned on this thread (0 if
+ * none). */
+int m3_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SSM_H */

@@ -1,0 +1,217 @@
+"""ctypes binding of libm3ssm (include/m3ssm.h).
+
+The functions carry the C names and only marshal arguments: they check that
+the torch tensors match the dims (shape, dtype, device, contiguity) so that
+no kernel can be handed a buffer smaller than it will touch, then pass the
+raw device pointers and the current HIP stream to the library.  All compute
+runs in the library's HIP kernels; there is no fallback path.  If the shared
+library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libm3ssm.so")
+
+M3_F32, M3_BF16 = 0, 1
+M3_THETA_IS_ANGLE = 1 << 0
+M3_A_PER_TOKEN = 1 << 1
+
+STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
+          4: "M3_ERR_UNSUPPORTED", 5: "M3_ERR_ALIGN", 6: "M3_ERR_WORKSPACE", 7: "M3_ERR_HIP"}
+
+
+class m3_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({_status_str(status)})"
+        if status == 7:
+            msg += f", hip error {_lib().m3_last_hip_error()}"
+        super().__init__(msg)
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m linear_recurrent_sequence_mamba_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(m3_dims)
+        lib.m3_prefill_workspace_size.restype = sz
+        lib.m3_prefill_workspace_size.argtypes = [dp]
+        lib.m3_scan_prefill.restype = ctypes.c_int
+        lib.m3_scan_prefill.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        lib.m3_decode_step.restype = ctypes.c_int
+        lib.m3_decode_step.argtypes = [dp] + [vp] * 11 + [vp]
+        lib.m3_status_str.restype = ctypes.c_char_p
+        lib.m3_status_str.argtypes = [ctypes.c_int]
+        lib.m3_last_hip_error.restype = ctypes.c_int
+        lib.m3_last_hip_error.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _lib()
+
+
+def _status_str(s: int) -> str:
+    return _lib().m3_status_str(int(s)).decode()
+
+
+def m3_status_str(status: int) -> str:
+    return _status_str(status)
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, rank=1, chunk=0,
+              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0) -> m3_dims:
+    return m3_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, in_dtype,
+                   out_dtype, flags)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return M3_BF16
+    if t == torch.float32:
+        return M3_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+_TORCH = {M3_BF16: torch.bfloat16, M3_F32: torch.float32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name, t, shape, dtype, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def m3_prefill_workspace_size(dims: m3_dims) -> int:
+    return int(_lib().m3_prefill_workspace_size(ctypes.byref(dims)))
+
+
+def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev,
+                    y, hT, ws, stream=None) -> None:
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        Bsz, T, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        _check("x", x, (Bsz, T, H, P, R), ti)
+        _check("dt", dt, (Bsz, T, H), ti)
+        _check("A", A, (Bsz, T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
+        _check("lam", lam, (Bsz, T, H), ti)
+        _check("theta", theta, (Bsz, T, H, N // 2), ti)
+        _check("B", B, (Bsz, T, H, N, R), ti)
+        _check("C", C, (Bsz, T, H, N, R), ti)
+        _check("h0", h0, (Bsz, H, P, N), torch.float32, optional=True)
+        _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
+        _check("B_prev", B_prev, (Bsz, H, N, R), ti, optional=True)
+        _check("y", y, (Bsz, T, H, P, R), to)
+        _check("hT", hT, (Bsz, H, P, N), torch.float32, optional=True)
+    nbytes = 0
+    if ws is not None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous device tensor")
+        nbytes = ws.numel() * ws.element_size()
+    st = _lib().m3_scan_prefill(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
+                                _ptr(theta), _ptr(B), _ptr(C), _ptr(h0), _ptr(x_prev),
+                                _ptr(B_prev), _ptr(y), _ptr(hT), _ptr(ws), nbytes,
+                                _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_prefill")
+
+
+def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t,
+                   theta_t, y_t, stream=None) -> None:
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        Bsz, H, P, N, R = d.batch, d.nheads, d.headdim, d.dstate, d.rank
+        _check("h", h, (Bsz, H, P, N), torch.float32)
+        _check("x_t", x_t, (Bsz, H, P, R), ti)
+        _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
+        _check("B_t", B_t, (Bsz, H, N, R), ti)
+        _check("B_prev", B_prev, (Bsz, H, N, R), ti, optional=True)
+        _check("C_t", C_t, (Bsz, H, N, R), ti)
+        _check("dt_t", dt_t, (Bsz, H), ti)
+        _check("A", A, (Bsz, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
+        _check("lam_t", lam_t, (Bsz, H), ti)
+        _check("theta_t", theta_t, (Bsz, H, N // 2), ti)
+        _check("y_t", y_t, (Bsz, H, P, R), to)
+    st = _lib().m3_decode_step(ctypes.byref(d), _ptr(h), _ptr(x_t), _ptr(x_prev), _ptr(B_t),
+                               _ptr(B_prev), _ptr(C_t), _ptr(dt_t), _ptr(A), _ptr(lam_t),
+                               _ptr(theta_t), _ptr(y_t), _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_decode_step")
+
+
+# ---------------------------------------------------------------------------
+# allocation helpers (torch only provides the memory)
+def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
+                 chunk=0, out_dtype=torch.float32, flags=0, want_hT=True, ws=None,
+                 stream=None):
+    """Allocate y (and hT, workspace) and call m3_scan_prefill.  Returns (y, hT)."""
+    Bsz, T, H, P, R = x.shape
+    N = B.shape[3]
+    d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags)
+    y = torch.empty((Bsz, T, H, P, R), dtype=out_dtype, device=x.device)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
+    if ws is None:
+        ws = workspace(d, x.device)
+    m3_scan_prefill(d, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws, stream)
+    return y, hT
+
+
+def workspace(dims: m3_dims, device) -> torch.Tensor:
+    n = m3_prefill_workspace_size(dims)
+    if n == 0:
+        raise M3Error(2, "m3_prefill_workspace_size")
+    return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=None,
+                out_dtype=torch.float32, flags=0, y_t=None, stream=None):
+    """Advance h in place by one token; returns y_t (allocated unless given)."""
+    Bsz, H, P, N = h.shape
+    R = x_t.shape[-1]
+    d = make_dims(Bsz, 1, H, P, N, R, 0, dtype_code(x_t.dtype), dtype_code(out_dtype), flags)
+    if y_t is None:
+        y_t = torch.empty((Bsz, H, P, R), dtype=out_dtype, device=h.device)
+    m3_decode_step(d, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t, stream)
+    return y_t

@@ -1,0 +1,154 @@
+// api.cpp -- the C ABI of libm3ssm (include/m3ssm.h): argument checks,
+// workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
+// the host before anything is launched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/m3ssm.h"
+#include "m3_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+m3_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return M3_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return M3_ERR_HIP;
+}
+
+m3_status check_dims(const m3_dims* d, bool need_seqlen) {
+  if (!d) return M3_ERR_NULL;
+  if (d->batch <= 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->rank <= 0)
+    return M3_ERR_SHAPE;
+  if (need_seqlen && d->seqlen <= 0) return M3_ERR_SHAPE;
+  if (d->dstate % 2 != 0) return M3_ERR_SHAPE;
+  if (d->chunk < 0) return M3_ERR_SHAPE;
+  if (d->in_dtype != M3_F32 && d->in_dtype != M3_BF16) return M3_ERR_DTYPE;
+  if (d->out_dtype != M3_F32 && d->out_dtype != M3_BF16) return M3_ERR_DTYPE;
+  if (d->flags & ~(M3_THETA_IS_ANGLE | M3_A_PER_TOKEN)) return M3_ERR_SHAPE;
+  return M3_OK;
+}
+
+int chunk_of(const m3_dims* d) { return d->chunk > 0 ? d->chunk : 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_status_str(m3_status s) {
+  switch (s) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "required pointer is NULL";
+    case M3_ERR_SHAPE: return "invalid shape or flags";
+    case M3_ERR_DTYPE: return "unsupported dtype";
+    case M3_ERR_UNSUPPORTED: return "no kernel for this (headdim, dstate, rank, chunk)";
+    case M3_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case M3_ERR_WORKSPACE: return "workspace missing or too small";
+    case M3_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int m3_last_hip_error(void) { return g_last_hip_error; }
+
+size_t m3_prefill_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true) != M3_OK) return 0;
+  return m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
+                                     chunk_of(d));
+}
+
+m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
+                          const void* lam, const void* theta, const void* B, const void* C,
+                          const float* h0, const void* x_prev, const void* B_prev, void* y,
+                          float* hT, void* ws, size_t ws_bytes, void* stream) {
+  m3_status st = check_dims(d, true);
+  if (st != M3_OK) return st;
+  if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
+  const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  const int Q = chunk_of(d);
+  const int in_bf16 = d->in_dtype == M3_BF16;
+  if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16))
+    return M3_ERR_UNSUPPORTED;
+  const size_t need = m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim,
+                                                  d->dstate, Q);
+  if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
+
+  m3::PrefillArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.B = B;
+  a.C = C;
+  a.h0 = h0;
+  a.xp = x_prev;
+  a.Bp = B_prev;
+  a.y = y;
+  a.hT = hT;
+  a.Bsz = d->batch;
+  a.T = d->seqlen;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.N = d->dstate;
+  a.R = d->rank;
+  a.Q = Q;
+  a.nchunk = (d->seqlen + Q - 1) / Q;
+  a.flags = d->flags;
+  a.has_prev = x_prev != nullptr;
+  m3::prefill_carve(a, ws);
+  hipError_t err = hipSuccess;
+  if (m3::launch_prefill(a, in_bf16, d->out_dtype == M3_BF16,
+                         static_cast<hipStream_t>(stream), &err) != 0)
+    return M3_ERR_UNSUPPORTED;
+  return hip_status(err);
+}
+
+m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void* x_prev,
+                         const void* B_t, const void* B_prev, const void* C_t, const void* dt_t,
+                         const float* A, const void* lam_t, const void* theta_t, void* y_t,
+                         void* stream) {
+  m3_status st = check_dims(d, false);
+  if (st != M3_OK) return st;
+  if (!h || !x_t || !B_t || !C_t || !dt_t || !A || !lam_t || !theta_t || !y_t)
+    return M3_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
+  const void* ptrs[] = {h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  if (!m3::decode_supported(d->headdim, d->dstate, d->rank)) return M3_ERR_UNSUPPORTED;
+  const int64_t units = static_cast<int64_t>(d->batch) * d->nheads;
+  if (units > 0x7fffffff) return M3_ERR_SHAPE;
+
+  m3::DecodeArgs a{};
+  a.h = h;
+  a.x = x_t;
+  a.xp = x_prev;
+  a.Bt = B_t;
+  a.Bp = B_prev;
+  a.Ct = C_t;
+  a.dt = dt_t;
+  a.A = A;
+  a.lam = lam_t;
+  a.theta = theta_t;
+  a.y = y_t;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.N = d->dstate;
+  a.R = d->rank;
+  a.flags = d->flags;
+  a.has_prev = x_prev != nullptr;
+  hipError_t err = hipSuccess;
+  if (m3::launch_decode(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
+                        static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)
+    return M3_ERR_UNSUPPORTED;
+  return hip_status(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// m3_device.h -- device-side helpers shared by the libm3ssm kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// bf16 travels as raw 16-bit patterns; fp32 as float.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v.bits) << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 (NaN stays NaN)
+__device__ __forceinline__ bf16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{static_cast<uint16_t>((u >> 16) | 0x40u)};
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t{static_cast<uint16_t>(u >> 16)};
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return to_bf16(v); }
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* __restrict__ p, int64_t i) {
+  return to_f32(p[i]);
+}
+
+// four consecutive elements starting at a multiple of 4 (8-byte / 16-byte loads)
+__device__ __forceinline__ f4 ld4(const float* __restrict__ p, int64_t i) {
+  return *reinterpret_cast<const f4*>(p + i);
+}
+__device__ __forceinline__ f4 ld4(const bf16_t* __restrict__ p, int64_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  f4 r;
+  r.x = __uint_as_float(u.x << 16);
+  r.y = __uint_as_float(u.x & 0xffff0000u);
+  r.z = __uint_as_float(u.y << 16);
+  r.w = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+
+// two consecutive elements starting at an even index
+__device__ __forceinline__ f2 ld2(const float* __restrict__ p, int64_t i) {
+  return *reinterpret_cast<const f2*>(p + i);
+}
+__device__ __forceinline__ f2 ld2(const bf16_t* __restrict__ p, int64_t i) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p + i);
+  f2 r;
+  r.x = __uint_as_float(u << 16);
+  r.y = __uint_as_float(u & 0xffff0000u);
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void st1(T* __restrict__ p, int64_t i, float v) {
+  p[i] = from_f32<T>(v);
+}
+
+// streaming (non-temporal) 16-byte state access
+__device__ __forceinline__ f4 ld4_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+__device__ __forceinline__ void st4_stream(float* p, f4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+}
+
+// rotate the complex pairs (v.x, v.y) and (v.z, v.w) by the angles whose
+// (cos, sin) are c0 and c1
+__device__ __forceinline__ f4 rot2pairs(f4 v, f2 c0, f2 c1) {
+  f4 r;
+  r.x = c0.x * v.x - c0.y * v.y;
+  r.y = c0.y * v.x + c0.x * v.y;
+  r.z = c1.x * v.z - c1.y * v.w;
+  r.w = c1.y * v.z + c1.x * v.w;
+  return r;
+}
+
+}  // namespace m3

@@ -1,0 +1,65 @@
+// m3_launch.h -- host-side launch interface between the C ABI layer and the
+// kernels of libm3ssm.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+constexpr uint32_t kThetaIsAngle = 1u << 0;
+constexpr uint32_t kAPerToken = 1u << 1;
+
+struct DecodeArgs {
+  float* h;
+  const void* x;
+  const void* xp;
+  const void* Bt;
+  const void* Bp;
+  const void* Ct;
+  const void* dt;
+  const float* A;
+  const void* lam;
+  const void* theta;
+  void* y;
+  int H, P, N, R;
+  uint32_t flags;
+  int has_prev;
+};
+
+bool decode_supported(int P, int N, int R);
+// returns 0 when launched (err = hipGetLastError), -1 when no kernel fits
+int launch_decode(const DecodeArgs& a, int in_bf16, int out_bf16, int units,
+                  hipStream_t s, hipError_t* err);
+
+struct PrefillArgs {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* lam;
+  const void* theta;
+  const void* B;
+  const void* C;
+  const float* h0;
+  const void* xp;
+  const void* Bp;
+  void* y;
+  float* hT;
+  // workspace carve-up
+  float* S;        // [Bsz, H, nchunk, P, N]: chunk end states, then chunk entry states
+  float* rot_end;  // [Bsz, H, nchunk, N/2, 2]: cos/sin of each chunk's total phase
+  float* decay;    // [Bsz, H, nchunk]: exp of each chunk's total log-decay
+  int Bsz, T, H, P, N, R, Q, nchunk;
+  uint32_t flags;
+  int has_prev;
+};
+
+bool prefill_supported(int P, int N, int R, int Q, int in_bf16);
+size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q);
+void prefill_carve(PrefillArgs& a, void* ws);
+// returns 0 when launched (err = first launch error), -1 when no kernel fits
+int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16,
+                   hipStream_t s, hipError_t* err);
+
+}  // namespace m3

@@ -1,0 +1,106 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+that include/m3ssm.h declares, and rejects bad arguments before launching
+anything (no GPU needed: every call here fails its host-side checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrent_sequence_mamba_amd import binding as m3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3ssm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ ]*[\s\*]+(m3_[a-z_]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("m3_scan_prefill", "m3_decode_step", "m3_prefill_workspace_size",
+              "m3_status_str", "m3_last_hip_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m3.library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert m3.m3_status_str(s)
+    assert m3.m3_status_str(99) == "unknown status"
+
+
+def _dims(**kw):
+    base = dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=128, rank=1, chunk=0,
+                in_dtype=m3.M3_BF16, out_dtype=m3.M3_F32, flags=0)
+    base.update(kw)
+    return m3.m3_dims(*base.values())
+
+
+P16 = ctypes.c_void_p(4096)   # a 16-byte aligned non-NULL address that is never dereferenced
+P_MIS = ctypes.c_void_p(4100)
+
+
+def _decode(d, **over):
+    args = dict(h=P16, x=P16, xp=None, Bt=P16, Bp=None, C=P16, dt=P16, A=P16, lam=P16, th=P16, y=P16)
+    args.update(over)
+    return m3.library().m3_decode_step(ctypes.byref(d), *args.values(), None)
+
+
+def _prefill(d, ws_bytes=1 << 40, **over):
+    args = dict(x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None, Bp=None,
+                y=P16, hT=None, ws=P16)
+    args.update(over)
+    return m3.library().m3_scan_prefill(ctypes.byref(d), *args.values(), ws_bytes, None)
+
+
+def test_workspace_size():
+    d = _dims(batch=4, seqlen=2048, nheads=32)
+    n = m3.m3_prefill_workspace_size(d)
+    chunks = 4 * 32 * 32
+    assert n >= chunks * 64 * 128 * 4
+    assert m3.m3_prefill_workspace_size(_dims(dstate=7)) == 0
+    assert m3.library().m3_prefill_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("call", [_decode, _prefill])
+def test_error_paths(call):
+    assert m3.library().m3_decode_step(None, *([None] * 12)) == 1
+    assert call(_dims(), x=None) == 1                           # NULL input
+    assert call(_dims(), xp=P16) == 1                           # x_prev without B_prev
+    assert call(_dims(dstate=127)) == 2                         # odd N
+    assert call(_dims(headdim=0)) == 2
+    assert call(_dims(rank=0)) == 2
+    assert call(_dims(flags=1 << 7)) == 2                       # unknown flag
+    assert call(_dims(in_dtype=5)) == 3
+    assert call(_dims(out_dtype=-1)) == 3
+    assert call(_dims(headdim=24, dstate=6)) == 4               # no kernel for it
+    assert call(_dims(), x=P_MIS) == 5                          # misaligned
+
+
+def test_prefill_specific_errors():
+    assert _prefill(_dims(seqlen=0)) == 2
+    assert _prefill(_dims(chunk=-1)) == 2
+    assert _prefill(_dims(chunk=32)) == 4
+    assert _prefill(_dims(), ws=None) == 6
+    need = m3.m3_prefill_workspace_size(_dims())
+    assert _prefill(_dims(), ws_bytes=need - 1) == 6
+    assert _prefill(_dims(), ws=P_MIS) == 5
+    assert _prefill(_dims(), hT=P_MIS) == 5
+
+
+def test_binding_rejects_mismatched_tensors():
+    torch = pytest.importorskip("torch")
+    d = _dims()
+    h = torch.zeros(2, 3, 64, 128)  # host tensor: rejected before any call
+    with pytest.raises(ValueError):
+        m3.m3_decode_step(d, h, *([None] * 10))

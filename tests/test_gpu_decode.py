@@ -1,0 +1,130 @@
+"""GPU parity of m3_decode_step against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from linear_recurrent_sequence_mamba_amd import binding as m3
+from linear_recurrent_sequence_mamba_amd import inputs as I
+from oracle import oracle
+from tests.util import TOL, cpu64, cuda, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps(w, steps, flags=0, out_dtype=torch.float32, prev=True, check_bh=None):
+    """Run `steps` decode steps on the GPU and the oracle; return max errors."""
+    h_cpu = I.decode_state(w)
+    h_gpu = cuda(h_cpu)
+    h_ref = cpu64(h_cpu)
+    A = I.head_decay(w)
+    if flags & m3.M3_A_PER_TOKEN:
+        A = A[None, :].expand(w.batch, w.nheads).contiguous()
+    A_gpu = cuda(A)
+    sel = slice(None) if check_bh is None else check_bh
+    if check_bh is not None:
+        h_ref = h_ref[sel]
+    prev_in = None
+    ey, eh = 0.0, 0.0
+    for s in range(steps):
+        d = I.decode_step_inputs(w, s)
+        g = {k: cuda(v) for k, v in d.items()}
+        xp = prev_in["x"] if (prev and prev_in is not None) else None
+        Bp = prev_in["B"] if (prev and prev_in is not None) else None
+        y = m3.decode_step(h_gpu, g["x"], g["B"], g["C"], g["dt"], A_gpu, g["lam"], g["theta"],
+                           x_prev=cuda(xp), B_prev=cuda(Bp), out_dtype=out_dtype, flags=flags)
+        Aref = cpu64(A)[sel] if flags & m3.M3_A_PER_TOKEN else cpu64(A)
+        yr, h_ref = oracle.decode_step(
+            h_ref, cpu64(d["x"])[sel], None if xp is None else cpu64(xp)[sel], cpu64(d["B"])[sel],
+            None if Bp is None else cpu64(Bp)[sel], cpu64(d["C"])[sel], cpu64(d["dt"])[sel], Aref,
+            cpu64(d["lam"])[sel], cpu64(d["theta"])[sel], flags=flags)
+        torch.cuda.synchronize()
+        ey = max(ey, rel_err(cpu64(y)[sel], yr))
+        prev_in = d
+    eh = rel_err(cpu64(h_gpu)[sel], h_ref)
+    return ey, eh
+
+
+SMALL = [  # P, N, R, dtype
+    (64, 128, 1, "bf16"), (64, 128, 4, "bf16"), (16, 16, 1, "f32"), (64, 128, 1, "f32"),
+    (64, 128, 4, "f32"), (32, 64, 2, "bf16"), (16, 32, 8, "bf16"), (48, 256, 1, "bf16"),
+    (32, 16, 3, "f32"), (40, 64, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("P,N,R,dt", SMALL)
+def test_decode_small_shapes(P, N, R, dt):
+    w = I.Workload("t", 90, 2, 1, 3, P, N, R, 64, dt, "normal")
+    say(f"decode small P={P} N={N} R={R} {dt}")
+    ey, eh = _run_steps(w, 5)
+    tol = TOL[w.torch_dtype]
+    assert ey <= tol and eh <= tol, (ey, eh)
+
+
+@pytest.mark.parametrize("flags", [m3.M3_THETA_IS_ANGLE, m3.M3_A_PER_TOKEN])
+@pytest.mark.parametrize("R", [1, 4])
+def test_decode_flags(flags, R):
+    w = I.Workload("t", 91, 2, 1, 4, 64, 128, R, 64, "bf16", "normal")
+    say(f"decode flags={flags} R={R}")
+    ey, eh = _run_steps(w, 4, flags=flags)
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_decode_no_prev_and_bf16_out(R):
+    w = I.Workload("t", 92, 2, 1, 4, 64, 128, R, 64, "bf16", "normal")
+    say(f"decode no-prev R={R}")
+    ey, eh = _run_steps(w, 3, prev=False)
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+    # bf16 output: the output rounding alone is up to 2^-8 relative
+    ey, eh = _run_steps(w, 3, out_dtype=torch.bfloat16)
+    assert ey <= 2 ** -8 + 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+@pytest.mark.parametrize("name", ["siso_decode", "mimo_decode"])
+def test_decode_full_shape(name):
+    """Full shape (B=128, H=64, P=64, N=128): every (b, h) for 3 steps, then
+    b in {0, 127} x all heads for 20 steps."""
+    w = I.WORKLOADS[name]
+    say(f"decode full {name}: all (b,h), 3 steps")
+    ey, eh = _run_steps(w, 3)
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+    say(f"decode full {name}: b in (0,127), 20 steps")
+    ey, eh = _run_steps(w, 20, check_bh=np.array([0, 127]))
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+@pytest.mark.parametrize("name", ["siso_decode", "mimo_decode"])
+def test_decode_1000_steps(name):
+    """1000 sequential steps at the full per-(b,h) shape (batch cut to 2)."""
+    w = I.WORKLOADS[name].with_(batch=2)
+    say(f"decode 1000 steps {name}")
+    ey, eh = _run_steps(w, 1000)
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+def test_decode_inplace_matches_copy_and_is_deterministic():
+    w = I.Workload("t", 93, 4, 1, 8, 64, 128, 4, 64, "bf16", "normal")
+    d = {k: cuda(v) for k, v in I.decode_step_inputs(w, 0).items()}
+    A = cuda(I.head_decay(w))
+    h0 = cuda(I.decode_state(w))
+    outs = []
+    for _ in range(2):
+        h = h0.clone()
+        y = m3.decode_step(h, d["x"], d["B"], d["C"], d["dt"], A, d["lam"], d["theta"],
+                           x_prev=d["x"], B_prev=d["B"])
+        torch.cuda.synchronize()
+        outs.append((h.cpu(), y.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_decode_nan_stays_in_its_head():
+    w = I.Workload("t", 94, 2, 1, 4, 64, 128, 1, 64, "bf16", "normal")
+    d = {k: cuda(v) for k, v in I.decode_step_inputs(w, 0).items()}
+    d["x"][1, 2, 5, 0] = float("nan")
+    A = cuda(I.head_decay(w))
+    h = cuda(I.decode_state(w))
+    y = m3.decode_step(h, d["x"], d["B"], d["C"], d["dt"], A, d["lam"], d["theta"])
+    torch.cuda.synchronize()
+    bad = torch.isnan(h).any(dim=(2, 3)).cpu()
+    assert bad[1, 2] and bad.sum() == 1
+    assert torch.isnan(y).any(dim=(2, 3)).cpu().sum() == 1
