@@ -67,6 +67,21 @@ __device__ __forceinline__ f2 ld2(const bf16_t* __restrict__ p, int64_t i) {
   return r;
 }
 
+// eight consecutive elements starting at a multiple of 8 (16-byte loads)
+__device__ __forceinline__ void ld8(const float* __restrict__ p, int64_t i, float* v) {
+  const f4 a = *reinterpret_cast<const f4*>(p + i);
+  const f4 b = *reinterpret_cast<const f4*>(p + i + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void ld8(const bf16_t* __restrict__ p, int64_t i, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p + i);
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+  v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+  v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
 template <typename T>
 __device__ __forceinline__ void st1(T* __restrict__ p, int64_t i, float v) {
   p[i] = from_f32<T>(v);

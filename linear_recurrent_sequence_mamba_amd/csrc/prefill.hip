@@ -70,6 +70,12 @@ struct PolF32 {
   static __device__ __forceinline__ void putx(XStore<ROWS, K>& s, int r, int k, float x) {
     s.v[r][k] = x;
   }
+  // eight consecutive k (k0 a multiple of 8) of one row
+  template <int ROWS, int K>
+  static __device__ __forceinline__ void put8(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    *reinterpret_cast<f4*>(&s.v[r][k0]) = f4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f4*>(&s.v[r][k0 + 4]) = f4{v[4], v[5], v[6], v[7]};
+  }
   template <int ROWS, int K>
   static __device__ __forceinline__ Frag frag(const Store<ROWS, K>& s, int row0, int k0, int lane) {
     return Frag{*reinterpret_cast<const f4*>(&s.v[row0 + (lane & 15)][k0 + 4 * (lane >> 4)])};
@@ -133,6 +139,19 @@ struct PolF16 {
     s.v[r][k] = static_cast<_Float16>(x);
   }
   template <int ROWS, int K>
+  static __device__ __forceinline__ void put8(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    h8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 a, b;
+      split(v[j], a, b);
+      hi[j] = a;
+      lo[j] = b;
+    }
+    *reinterpret_cast<h8*>(&s.hi[r][k0]) = hi;
+    *reinterpret_cast<h8*>(&s.lo[r][k0]) = lo;
+  }
+  template <int ROWS, int K>
   static __device__ __forceinline__ Frag frag(const Store<ROWS, K>& s, int row0, int k0, int lane) {
     const int r = row0 + (lane & 15), k = k0 + 8 * (lane >> 4);
     return Frag{*reinterpret_cast<const h8*>(&s.hi[r][k]), *reinterpret_cast<const h8*>(&s.lo[r][k])};
@@ -177,221 +196,402 @@ struct PolF16 {
   }
 };
 
+
 // --------------------------------------------------------------------------
-// per-chunk token tables: chunk-local cumulative log-decay (double), gamma,
-// beta' = (1 - lam) dt
-template <typename TI>
-__device__ __forceinline__ void token_tables(const PrefillArgs& a, int b, int h, int c0, int Lc,
-                                             double* cs, float* gam, float* bpr) {
+// launch geometry: one block per chunk; each wave owns TPW 16-row tiles of
+// the chunk's Q*R virtual rows (two tiles w and 2NW-1-w when TPW = 2, which
+// balances the causal work across waves)
+template <int P, int N, int R>
+struct Geo {
+  static constexpr int ROWS = kQ * R;
+  static constexpr int TILES = ROWS / 16;
+  static constexpr int NW = TILES >= 8 ? 8 : 4;
+  static constexpr int TPW = TILES / NW;
+  static constexpr int NT = NW * 64;
+  static constexpr int NP = N / 2;
+  static constexpr int PT = P / 16;
+  static constexpr int NTL = N / 16;
+  static constexpr int NUB = ROWS / kRB;
+  static_assert(TPW >= 1 && TILES % NW == 0, "tile split");
+};
+
+// per-chunk tables in LDS
+template <int NT, int N>
+struct Tables {
+  double cs[kQ];      // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
+  float dt[kQ];
+  float gam[kQ];      // lam dt
+  float bpr[kQ];      // (1 - lam) dt
+  float aux[kQ];      // e^{cs_t} (outputs) or the chunk-state weights W_t
+  double seg[NT];
+  double phi_end[N / 2];
+  f2 rot[kQ][N / 2];  // (cos, sin) of Phi_t (mode 0) or of Phi_end - Phi_t (mode 1)
+};
+
+__device__ __forceinline__ float reduce_angle(double phi) {
+  constexpr double inv = 1.0 / kTwoPi;
+  return (float)(phi - kTwoPi * rint(phi * inv));
+}
+
+__device__ __forceinline__ int64_t token_index(const PrefillArgs& a, int b, int t, int h) {
+  return ((int64_t)b * a.T + t) * a.H + h;
+}
+
+// Token scalars, the chunk-local log-decay prefix (double, one wave) and the
+// chunk-local phase prefix of every pair (double; each thread owns one pair
+// and a segment of tokens), then (cos, sin) of the reduced angles.  th_raw
+// is scratch for the chunk's theta (Q x N/2 floats) and is free on return.
+template <typename TI, int N, int NT>
+__device__ void chunk_tables(const PrefillArgs& a, int b, int h, int c0, int Lc,
+                             Tables<NT, N>& tb, float* th_raw, int mode) {
+  constexpr int NP = N / 2;
+  constexpr int VPT = NP / 8;                 // 16-byte vectors per token
+  constexpr int NV = kQ * VPT;
+  constexpr int IT = (NV + NT - 1) / NT;
   const int tid = threadIdx.x;
+  const TI* __restrict__ th = static_cast<const TI*>(a.theta);
+  float v[IT][8];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    const int t = vi / VPT, kv = vi % VPT;
+    if (vi < NV && t < Lc) {
+      ld8(th, token_index(a, b, c0 + t, h) * NP + 8 * kv, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
   if (tid < 64) {
-    double v = 0.0;
-    float gm = 0.0f, bp = 0.0f;
+    double lv = 0.0;
+    float d = 0.0f, gm = 0.0f, bp = 0.0f;
     if (tid < Lc) {
-      const int64_t bth = ((int64_t)b * a.T + c0 + tid) * a.H + h;
-      const float d = ld1(static_cast<const TI*>(a.dt), bth);
+      const int64_t bth = token_index(a, b, c0 + tid, h);
+      d = ld1(static_cast<const TI*>(a.dt), bth);
       const float l = ld1(static_cast<const TI*>(a.lam), bth);
       const float A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
-      v = (double)d * (double)A;
+      lv = (double)d * (double)A;
       gm = l * d;
       bp = (1.0f - l) * d;
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(v, off, 64);
-      if (tid >= off) v += o;
+      const double o = __shfl_up(lv, off, 64);
+      if (tid >= off) lv += o;
     }
-    cs[tid] = v;
-    gam[tid] = gm;
-    bpr[tid] = bp;
+    tb.cs[tid] = lv;
+    tb.dt[tid] = d;
+    tb.gam[tid] = gm;
+    tb.bpr[tid] = bp;
   }
-}
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi < NV) {
+      const int t = vi / VPT, kv = vi % VPT;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[i][j];
+    }
+  }
+  __syncthreads();
 
-__device__ __forceinline__ float reduce_angle(double phi) {
-  return (float)(phi - kTwoPi * rint(phi / kTwoPi));
-}
-
-// Chunk-local cumulative phases Phi[t][k] (double), for all t < Lc and
-// k < N/2.  Each thread owns one pair k and a segment of tokens.  On return
-// phi_end[k] holds Phi[Lc-1][k]; when `store` is true, rot[t][k] receives
-// (cos, sin) of Phi[t][k] (mode 0) or of Phi_end - Phi[t] (mode 1).
-template <typename TI, int N>
-__device__ void phase_tables(const PrefillArgs& a, int b, int h, int c0, int Lc, f2* rot,
-                             double* seg_sum, double* phi_end, int mode) {
-  constexpr int NP = N / 2;
-  constexpr int NSEG = 256 / NP;     // token segments per pair
-  constexpr int SEG = kQ / NSEG;     // tokens per segment
-  const int tid = threadIdx.x;
-  const int k = tid % NP, seg = tid / NP;
-  const TI* __restrict__ th = static_cast<const TI*>(a.theta);
-  const TI* __restrict__ dtp = static_cast<const TI*>(a.dt);
+  constexpr int NSEG = NT / NP;
+  constexpr int SEG = kQ / NSEG;
+  static_assert(NSEG >= 1 && kQ % NSEG == 0, "phase segments");
+  const int k = tid % NP, sg = tid / NP;
   const bool angle = (a.flags & kThetaIsAngle) != 0;
   double loc[SEG];
   double run = 0.0;
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
-    const int t = seg * SEG + i;
-    double p = 0.0;
-    if (t < Lc) {
-      const int64_t bth = ((int64_t)b * a.T + c0 + t) * a.H + h;
-      const double tv = (double)ld1(th, bth * NP + k);
-      p = angle ? tv : tv * (double)ld1(dtp, bth);
-    }
-    run += p;
+    const int t = sg * SEG + i;
+    const double tv = (double)th_raw[t * NP + k];
+    run += angle ? tv : tv * (double)tb.dt[t];
     loc[i] = run;
   }
-  seg_sum[seg * NP + k] = run;
+  tb.seg[sg * NP + k] = run;
   __syncthreads();
   double base = 0.0;
-  for (int s = 0; s < seg; ++s) base += seg_sum[s * NP + k];
-  if (seg == NSEG - 1) {
-    double tot = base + run;
-    phi_end[k] = tot;
-  }
+  for (int s = 0; s < sg; ++s) base += tb.seg[s * NP + k];
+  if (sg == NSEG - 1) tb.phi_end[k] = base + run;
   __syncthreads();
-  const double pe = phi_end[k];
+  const double pe = tb.phi_end[k];
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
-    const int t = seg * SEG + i;
+    const int t = sg * SEG + i;
     if (t < Lc) {
       const double ph = base + loc[i];
-      const float r = reduce_angle(mode == 0 ? ph : pe - ph);
-      float s, c;
-      sincosf(r, &s, &c);
-      rot[t * NP + k] = f2{c, s};
+      float sn, cn;
+      sincosf(reduce_angle(mode == 0 ? ph : pe - ph), &sn, &cn);
+      tb.rot[t][k] = f2{cn, sn};
+    }
+  }
+  __syncthreads();
+}
+
+// Rows [v0, v0 + 64) of the chunk's B or C (virtual row v = t R + r),
+// rotated by -Phi_t, into st[v - v0][n].  16-byte loads, all issued before
+// any is used; rows past the chunk's end are zero.
+template <class Pol, typename TI, int N, int R, int NT>
+__device__ void stage_rows(typename Pol::template Store<kRB, N>& st, const TI* __restrict__ src,
+                           const PrefillArgs& a, int b, int h, int c0, int Lc, int v0,
+                           const f2 (*rot)[N / 2]) {
+  constexpr int E = N * R;
+  constexpr int VPT = E / 8;
+  constexpr int NTOK = kRB / R;
+  constexpr int NV = NTOK * VPT;
+  constexpr int IT = (NV + NT - 1) / NT;
+  constexpr int NPAIR = 4 / R;              // complex pairs per vector
+  const int tid = threadIdx.x;
+  const int t0 = v0 / R;
+  float v[IT][8];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    const int tl = vi / VPT, e0 = (vi % VPT) * 8;
+    if (vi < NV && t0 + tl < Lc) {
+      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi >= NV) continue;
+    const int tl = vi / VPT, e0 = (vi % VPT) * 8;
+    const int t = t0 + tl;
+    const bool ok = t < Lc;
+    float o[8];
+#pragma unroll
+    for (int pi = 0; pi < NPAIR; ++pi) {
+      const int n = e0 / R + 2 * pi;
+      const f2 cs = ok ? rot[t][n / 2] : f2{1.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float u0 = v[i][(2 * pi) * R + r], u1 = v[i][(2 * pi + 1) * R + r];
+        o[(2 * pi) * R + r] = cs.x * u0 + cs.y * u1;        // rotate by -Phi_t
+        o[(2 * pi + 1) * R + r] = -cs.y * u0 + cs.x * u1;
+      }
+    }
+    if constexpr (R == 1) {
+      Pol::put8(st, tl, e0, o);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Pol::put(st, tl * R + j % R, e0 / R + j / R, o[j]);
     }
   }
 }
 
+// Rows [v0, v0 + 64) of B rotated by +(Phi_end - Phi_t) and scaled by the
+// chunk-state weight W_t, stored transposed: st[n][v - v0].  Consecutive
+// lanes take consecutive tokens so the transposed LDS writes do not collide.
+template <class Pol, typename TI, int N, int R, int NT>
+__device__ void stage_rows_T(typename Pol::template Store<N, kRB>& st, const TI* __restrict__ src,
+                             const PrefillArgs& a, int b, int h, int c0, int Lc, int v0,
+                             const f2 (*rot)[N / 2], const float* w) {
+  constexpr int E = N * R;
+  constexpr int VPT = E / 8;
+  constexpr int NTOK = kRB / R;
+  constexpr int NV = NTOK * VPT;
+  constexpr int IT = (NV + NT - 1) / NT;
+  constexpr int NPAIR = 4 / R;
+  const int tid = threadIdx.x;
+  const int t0 = v0 / R;
+  float v[IT][8];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
+    if (vi < NV && t0 + tl < Lc) {
+      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi >= NV) continue;
+    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
+    const int t = t0 + tl;
+    const bool ok = t < Lc;
+    const float wt = ok ? w[t] : 0.0f;
+#pragma unroll
+    for (int pi = 0; pi < NPAIR; ++pi) {
+      const int n = e0 / R + 2 * pi;
+      const f2 cs = ok ? rot[t][n / 2] : f2{1.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float u0 = v[i][(2 * pi) * R + r], u1 = v[i][(2 * pi + 1) * R + r];
+        Pol::put(st, n, tl * R + r, wt * (cs.x * u0 - cs.y * u1));   // rotate by +angle
+        Pol::put(st, n + 1, tl * R + r, wt * (cs.y * u0 + cs.x * u1));
+      }
+    }
+  }
+}
+
+// x rows [v0, v0 + 64) transposed: xs[p][v - v0]
+template <class Pol, typename TI, int P, int R, int NT>
+__device__ void stage_x_T(typename Pol::template XStore<P, kRB>& xs, const TI* __restrict__ src,
+                          const PrefillArgs& a, int b, int h, int c0, int Lc, int v0) {
+  constexpr int E = P * R;
+  constexpr int VPT = E / 8;
+  constexpr int NTOK = kRB / R;
+  constexpr int NV = NTOK * VPT;
+  constexpr int IT = (NV + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  const int t0 = v0 / R;
+  float v[IT][8];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
+    if (vi < NV && t0 + tl < Lc) {
+      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi >= NV) continue;
+    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Pol::putx(xs, (e0 + j) / R, tl * R + (e0 + j) % R, v[i][j]);
+  }
+}
+
 // --------------------------------------------------------------------------
-// K1: per-chunk state S_c and the chunk's decay / phase totals
+// K1: the chunk's own end state S_c (from a zero entry state), rotated into
+// the frame of the chunk's end, plus the next chunk's trapezoid
+// left-endpoint term (1 - lam_{c1}) dt_{c1} x_{c1-1} B_{c1-1}^T; the chunk's
+// total decay and phase go to the workspace.
 template <class Pol, typename TI, int P, int N, int R>
 struct K1Smem {
-  double cs[kQ];
-  float gam[kQ], bpr[kQ], wu[kQ];
-  double seg_sum[256];
-  double phi_end[N / 2];
-  f2 rot[kQ * (N / 2)];
-  typename Pol::template Store<N, kRB> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][u]
-  typename Pol::template XStore<P, kRB> xs;  // x^T  [p][u]
+  Tables<Geo<P, N, R>::NT, N> tb;
+  union U {
+    typename Pol::template Store<N, kRB> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
+    float th_raw[kQ * (N / 2)];
+  } u;
+  typename Pol::template XStore<P, kRB> xs;    // x^T  [p][v]
 };
 
 template <class Pol, typename TI, int P, int N, int R>
-__global__ __launch_bounds__(256) void k_chunk_state(PrefillArgs a) {
+__global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_state(PrefillArgs a) {
+  using G = Geo<P, N, R>;
   __shared__ K1Smem<Pol, TI, P, N, R> sm;
-  constexpr int NP = N / 2;
-  constexpr int NT = N / 16;
-  constexpr int PT = P / 16;
-  constexpr int PTW = (PT + 3) / 4;  // p-tiles per wave
+  constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
+  constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int c0 = c * kQ;
   const int Lc = min(kQ, a.T - c0);
+  const int rows = Lc * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
 
-  token_tables<TI>(a, b, h, c0, Lc, sm.cs, sm.gam, sm.bpr);
-  phase_tables<TI, N>(a, b, h, c0, Lc, sm.rot, sm.seg_sum, sm.phi_end, 1);
-  // (phase_tables synchronises, so the token tables are visible here)
-  const double cs_end = sm.cs[Lc - 1];
+  chunk_tables<TI, N, G::NT>(a, b, h, c0, Lc, sm.tb, sm.u.th_raw, 1);
+  const double cs_end = sm.tb.cs[Lc - 1];
   if (tid < kQ) {
     float w = 0.0f;
     if (tid < Lc) {
-      const float wt = sm.gam[tid] + (tid < Lc - 1 ? sm.bpr[tid + 1] : 0.0f);
-      w = expf((float)(cs_end - sm.cs[tid])) * wt;
+      const float wt = sm.tb.gam[tid] + (tid < Lc - 1 ? sm.tb.bpr[tid + 1] : 0.0f);
+      w = expf((float)(cs_end - sm.tb.cs[tid])) * wt;
     }
-    sm.wu[tid] = w;
+    sm.tb.aux[tid] = w;
   }
-  if (tid < NP) {
-    float s, co;
-    sincosf(reduce_angle(sm.phi_end[tid]), &s, &co);
-    a.rot_end[chunk_id * N + 2 * tid] = co;
-    a.rot_end[chunk_id * N + 2 * tid + 1] = s;
+  if (tid < G::NP) {
+    float sn, cn;
+    sincosf(reduce_angle(sm.tb.phi_end[tid]), &sn, &cn);
+    reinterpret_cast<f2*>(a.rot_end)[chunk_id * G::NP + tid] = f2{cn, sn};
   }
   if (tid == 0) a.decay[chunk_id] = expf((float)cs_end);
 
-  f4 acc[PTW][NT];
+  f4 acc[QPW];
 #pragma unroll
-  for (int i = 0; i < PTW; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f4{0, 0, 0, 0};
+  for (int q = 0; q < QPW; ++q) acc[q] = f4{0, 0, 0, 0};
 
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
-  const int rows = Lc * R;
-  for (int ub = 0; ub * kRB < rows; ++ub) {
+  for (int ub = 0; ub < G::NUB; ++ub) {
+    if (ub * kRB >= rows) break;
     __syncthreads();
-    // stage (W_u R(Phi_end - Phi_u) B_u)^T: thread -> (virtual row, pair)
-    for (int idx = tid; idx < kRB * NP; idx += 256) {
-      const int k = idx % NP, ul = idx / NP;
-      const int v = ub * kRB + ul;
-      float o0 = 0.0f, o1 = 0.0f;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        const int64_t base = (((int64_t)b * a.T + c0 + t) * a.H + h) * N * R;
-        const float u0 = ld1(Bg, base + (2 * k) * R + r);
-        const float u1 = ld1(Bg, base + (2 * k + 1) * R + r);
-        const f2 cs = sm.rot[t * NP + k];
-        const float w = sm.wu[t];
-        o0 = w * (cs.x * u0 - cs.y * u1);
-        o1 = w * (cs.y * u0 + cs.x * u1);
-      }
-      Pol::put(sm.bw, 2 * k, ul, o0);
-      Pol::put(sm.bw, 2 * k + 1, ul, o1);
-    }
-    // stage x^T: thread -> (virtual row, p)
-    for (int idx = tid; idx < kRB * P; idx += 256) {
-      const int p = idx % P, ul = idx / P;
-      const int v = ub * kRB + ul;
-      float xv = 0.0f;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        xv = ld1(Xg, ((((int64_t)b * a.T + c0 + t) * a.H + h) * P + p) * R + r);
-      }
-      Pol::putx(sm.xs, p, ul, xv);
-    }
+    stage_rows_T<Pol, TI, N, R, G::NT>(sm.u.bw, Bg, a, b, h, c0, Lc, ub * kRB, sm.tb.rot, sm.tb.aux);
+    stage_x_T<Pol, TI, P, R, G::NT>(sm.xs, Xg, a, b, h, c0, Lc, ub * kRB);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PTW; ++i) {
-      const int pt = wave + 4 * i;
-      if (pt < PT) {
+    for (int kk = 0; kk < kRB; kk += Pol::KS) {
 #pragma unroll
-        for (int kk = 0; kk < kRB; kk += Pol::KS) {
-          const typename Pol::XFrag xf = Pol::fragx_c(sm.xs, 16 * pt, kk, lane);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[i][nt] = Pol::mma_x(Pol::frag(sm.bw, 16 * nt, kk, lane), xf, acc[i][nt]);
+      for (int q = 0; q < QPW; ++q) {
+        const int qq = wave * QPW + q;
+        if (qq < NQ) {
+          const int pt = qq / G::NTL, nt = qq % G::NTL;
+          acc[q] = Pol::mma_x(Pol::frag(sm.u.bw, 16 * nt, kk, lane),
+                              Pol::fragx_c(sm.xs, 16 * pt, kk, lane), acc[q]);
         }
       }
     }
   }
-  // S_c[p][n..n+3]: D rows are n (16nt + 4g + j), columns p (16pt + lane%16)
+
+  // the next chunk's left-endpoint term, then S_c[p][n..n+3]
+  float bpn = 0.0f;
+  const TI* xe = nullptr;
+  const TI* Be = nullptr;
+  if (c + 1 < a.nchunk) {
+    const int64_t nx = token_index(a, b, c0 + kQ, h);
+    const float d = ld1(static_cast<const TI*>(a.dt), nx);
+    const float l = ld1(static_cast<const TI*>(a.lam), nx);
+    bpn = (1.0f - l) * d;
+    const int64_t last = token_index(a, b, c0 + kQ - 1, h);
+    xe = Xg + last * P * R;
+    Be = Bg + last * N * R;
+  }
   float* __restrict__ S = a.S + chunk_id * P * N;
 #pragma unroll
-  for (int i = 0; i < PTW; ++i) {
-    const int pt = wave + 4 * i;
-    if (pt < PT) {
-      const int p = 16 * pt + (lane & 15);
+  for (int q = 0; q < QPW; ++q) {
+    const int qq = wave * QPW + q;
+    if (qq < NQ) {
+      const int pt = qq / G::NTL, nt = qq % G::NTL;
+      const int p = 16 * pt + l16, n = 16 * nt + 4 * g;
+      f4 s = acc[q];
+      if (xe) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f4*>(S + (int64_t)p * N + 16 * nt + 4 * (lane >> 4)) = acc[i][nt];
+        for (int r = 0; r < R; ++r) {
+          const float xv = bpn * ld1(xe, (int64_t)p * R + r);
+          s.x += xv * ld1(Be, (int64_t)(n + 0) * R + r);
+          s.y += xv * ld1(Be, (int64_t)(n + 1) * R + r);
+          s.z += xv * ld1(Be, (int64_t)(n + 2) * R + r);
+          s.w += xv * ld1(Be, (int64_t)(n + 3) * R + r);
+        }
+      }
+      *reinterpret_cast<f4*>(S + (int64_t)p * N + n) = s;
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// K2: serial pass over the chunks of one (batch, head), 16 state rows per block
+// K2: serial pass over the chunks of one (batch, head), 16 state rows per
+// block.  Entering chunk c the state (plus that chunk's left-endpoint term)
+// is Shat_c; Shat_{c+1} = decay_c R(Phi_end,c) Shat_c + S_c, where S_c
+// already carries the next chunk's left-endpoint term.  Shat_c replaces S_c
+// in the workspace.  The loads of chunk c + D are issued while chunk c is
+// processed.
 template <typename TI, int N, int R>
 __global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
-  constexpr int VPR = N / 4;               // float4 vectors per state row
-  constexpr int NV = 16 * VPR;             // vectors per block
-  constexpr int VPT = (NV + 255) / 256;    // vectors per thread
+  constexpr int VPR = N / 4;
+  constexpr int NV = 16 * VPR;
+  constexpr int VPT = (NV + 255) / 256;
+  constexpr int D = 4;
   const int P = a.P;
   const int slices = P / 16;
   const int bh = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
 
   int pv[VPT], nv[VPT];
   bool ok[VPT];
@@ -405,51 +605,62 @@ __global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
     S[i] = f4{0, 0, 0, 0};
     if (ok[i] && a.h0) S[i] = *reinterpret_cast<const f4*>(a.h0 + ((int64_t)bh * P + pv[i]) * N + nv[i]);
   }
-  const int64_t cbase = (int64_t)bh * a.nchunk;
-  for (int c = 0; c < a.nchunk; ++c) {
-    const int c0 = c * kQ;
-    const int64_t cid = cbase + c;
-    // trapezoid left-endpoint term of the chunk's first token
-    float bp0 = 0.0f;
-    const TI* xh = nullptr;
-    const TI* Bh = nullptr;
-    {
-      const int64_t bth = ((int64_t)b * a.T + c0) * a.H + h;
-      const float d = ld1(static_cast<const TI*>(a.dt), bth);
-      const float l = ld1(static_cast<const TI*>(a.lam), bth);
-      bp0 = (1.0f - l) * d;
-      if (c == 0) {
-        if (a.has_prev) {
-          xh = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
-          Bh = static_cast<const TI*>(a.Bp) + (int64_t)bh * N * R;
-        }
-      } else {
-        const int64_t prev = ((int64_t)b * a.T + c0 - 1) * a.H + h;
-        xh = Xg + prev * P * R;
-        Bh = Bg + prev * N * R;
-      }
-    }
-    const float dec = a.decay[cid];
-    float* __restrict__ Sc = a.S + cid * P * N;
+  if (a.has_prev) {  // left-endpoint term of token 0
+    const int64_t t0 = token_index(a, b, 0, h);
+    const float d = ld1(static_cast<const TI*>(a.dt), t0);
+    const float l = ld1(static_cast<const TI*>(a.lam), t0);
+    const float bp0 = (1.0f - l) * d;
+    const TI* xh = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
+    const TI* Bh = static_cast<const TI*>(a.Bp) + (int64_t)bh * N * R;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       if (!ok[i]) continue;
-      float* ptr = Sc + (int64_t)pv[i] * N + nv[i];
-      const f4 sc = *reinterpret_cast<const f4*>(ptr);
-      f4 sh = S[i];
-      if (xh) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float xv = bp0 * ld1(xh, (int64_t)pv[i] * R + r);
-          sh.x += xv * ld1(Bh, (int64_t)(nv[i] + 0) * R + r);
-          sh.y += xv * ld1(Bh, (int64_t)(nv[i] + 1) * R + r);
-          sh.z += xv * ld1(Bh, (int64_t)(nv[i] + 2) * R + r);
-          sh.w += xv * ld1(Bh, (int64_t)(nv[i] + 3) * R + r);
-        }
+      for (int r = 0; r < R; ++r) {
+        const float xv = bp0 * ld1(xh, (int64_t)pv[i] * R + r);
+        S[i].x += xv * ld1(Bh, (int64_t)(nv[i] + 0) * R + r);
+        S[i].y += xv * ld1(Bh, (int64_t)(nv[i] + 1) * R + r);
+        S[i].z += xv * ld1(Bh, (int64_t)(nv[i] + 2) * R + r);
+        S[i].w += xv * ld1(Bh, (int64_t)(nv[i] + 3) * R + r);
       }
-      *reinterpret_cast<f4*>(ptr) = sh;   // state entering chunk c
-      const f2* re = reinterpret_cast<const f2*>(a.rot_end + cid * N);
-      S[i] = dec * rot2pairs(sh, re[nv[i] / 2], re[nv[i] / 2 + 1]) + sc;
+    }
+  }
+  const int64_t cbase = (int64_t)bh * a.nchunk;
+  const int nch = a.nchunk;
+  f4 bs[D][VPT];
+  f2 br0[D][VPT], br1[D][VPT];
+  float bd[D];
+  auto load = [&](int c, int q) {
+    if (c < nch) {
+      const int64_t cid = cbase + c;
+      const float* Sc = a.S + cid * P * N;
+      const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
+      bd[q] = a.decay[cid];
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        if (!ok[i]) continue;
+        bs[q][i] = *reinterpret_cast<const f4*>(Sc + (int64_t)pv[i] * N + nv[i]);
+        br0[q][i] = re[nv[i] / 2];
+        br1[q][i] = re[nv[i] / 2 + 1];
+      }
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < D; ++q) load(q, q);
+  for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      const int c = c0 + q;
+      if (c < nch) {
+        float* Sc = a.S + (cbase + c) * P * N;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+          if (!ok[i]) continue;
+          *reinterpret_cast<f4*>(Sc + (int64_t)pv[i] * N + nv[i]) = S[i];   // Shat_c
+          S[i] = bd[q] * rot2pairs(S[i], br0[q][i], br1[q][i]) + bs[q][i];
+        }
+        load(c + D, q);
+      }
     }
   }
   if (a.hT) {
@@ -460,202 +671,156 @@ __global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// K3: outputs of one 64-virtual-row block of one chunk
+// K3: all outputs of one chunk
 template <class Pol, typename TI, int P, int N, int R>
 struct K3Smem {
-  double cs[kQ];
-  float gam[kQ], bpr[kQ], ecs[kQ];
-  double seg_sum[256];
-  double phi_end[N / 2];
-  f2 rot[kQ * (N / 2)];
-  float mtok[kRB / R + 1][kQ];
+  Tables<Geo<P, N, R>::NT, N> tb;
   union U {
-    typename Pol::template Store<kRB, N> bt;  // rotated B block  [u][n]
-    typename Pol::template Store<P, N> sh;    // Shat             [p][n]
-    float craw[kRB][N + 4];                   // own C rows (before rotation)
+    typename Pol::template Store<kRB, N> st;   // rotated C or B rows   [v][n]
+    typename Pol::template Store<P, N> sh;     // Shat                  [p][n]
+    float th_raw[kQ * (N / 2)];
   } u;
-  typename Pol::template XStore<P, kRB> xs;   // x^T block        [p][u]
+  typename Pol::template XStore<P, kRB> xs;    // x^T block             [p][v]
 };
 
 template <class Pol, typename TI, typename TO, int P, int N, int R>
-__global__ __launch_bounds__(256) void k_chunk_output(PrefillArgs a) {
+__global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs a) {
+  using G = Geo<P, N, R>;
   __shared__ K3Smem<Pol, TI, P, N, R> sm;
-  constexpr int NP = N / 2;
-  constexpr int PT = P / 16;
   constexpr int NKS = N / Pol::KS;
-  constexpr int NRB = (kQ * R + kRB - 1) / kRB;
-  constexpr int UG = 16 * Pol::DT;    // u rows per A fragment built from D tiles
-  // block -> (chunk, row block); the row blocks of one chunk share an XCD
-  const int bid = blockIdx.x;
-  const int grp = bid / (8 * NRB), rem = bid % (8 * NRB);
-  const int c = grp * 8 + rem % 8, rb = rem / 8;
-  const int h = blockIdx.y, b = blockIdx.z;
-  if (c >= a.nchunk) return;
+  constexpr int UG = 16 * Pol::DT;          // u rows per A fragment built from D tiles
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int c0 = c * kQ;
   const int Lc = min(kQ, a.T - c0);
   const int rows = Lc * R;
-  const int row0 = rb * kRB;
-  if (row0 >= rows) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
-  const int tok0 = row0 / R;                                // first own token
-  const int tok1 = min(Lc - 1, (row0 + kRB - 1) / R);       // last own token
 
-  token_tables<TI>(a, b, h, c0, Lc, sm.cs, sm.gam, sm.bpr);
-  // own C rows -> craw (before the phase tables overwrite nothing: separate)
-  {
-    const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
-    for (int idx = tid; idx < kRB * N; idx += 256) {
-      const int n = idx % N, vl = idx / N;
-      const int v = row0 + vl;
-      float cv = 0.0f;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        cv = ld1(Cg, (((int64_t)b * a.T + c0 + t) * a.H + h) * N * R + (int64_t)n * R + r);
-      }
-      sm.u.craw[vl][n] = cv;
-    }
-  }
-  phase_tables<TI, N>(a, b, h, c0, Lc, sm.rot, sm.seg_sum, sm.phi_end, 0);
-  if (tid < kQ) sm.ecs[tid] = tid < Lc ? expf((float)sm.cs[tid]) : 0.0f;
-  // decay mask for the own tokens: M[t][u] = e^{cs_t - cs_u} w_{t,u}, u <= t
-  for (int idx = tid; idx < (tok1 - tok0 + 1) * kQ; idx += 256) {
-    const int tl = idx / kQ, u = idx % kQ;
-    const int t = tok0 + tl;
-    float m = 0.0f;
-    if (u <= t) {
-      const float w = sm.gam[u] + (u < t ? sm.bpr[u + 1] : 0.0f);
-      m = expf((float)(sm.cs[t] - sm.cs[u])) * w;
-    }
-    sm.mtok[tl][u] = m;
-  }
-  __syncthreads();
+  chunk_tables<TI, N, G::NT>(a, b, h, c0, Lc, sm.tb, sm.u.th_raw, 0);
+  if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
 
-  // own rotated C rows -> fragments in registers: row v = row0 + 16*wave + l16
-  const int vrow = row0 + 16 * wave + l16;
-  const int trow = min(vrow / R, Lc - 1);
-  typename Pol::Frag cf[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    constexpr int KPL = Pol::KS / 4;
-    float v[KPL];
-    const int n0 = s * Pol::KS + KPL * g;
-#pragma unroll
-    for (int j = 0; j < KPL; j += 2) {
-      const float u0 = sm.u.craw[16 * wave + l16][n0 + j];
-      const float u1 = sm.u.craw[16 * wave + l16][n0 + j + 1];
-      const f2 cs = sm.rot[trow * NP + (n0 + j) / 2];
-      v[j] = cs.x * u0 + cs.y * u1;       // rotate by -Phi
-      v[j + 1] = -cs.y * u0 + cs.x * u1;
-    }
-    cf[s] = Pol::make(v);
-  }
-  __syncthreads();
+  int tile[G::TPW];
+  tile[0] = wave;
+  if constexpr (G::TPW == 2) tile[1] = 2 * G::NW - 1 - wave;
 
-  // Y_off = e^{cs_t} Ct Shat^T
-  f4 acc[PT];
-  {
-    const float* __restrict__ Sh = a.S + chunk_id * P * N;
-    for (int idx = tid; idx < P * N / 4; idx += 256) {
-      const int p = idx / (N / 4), n = 4 * (idx % (N / 4));
-      const f4 v = *reinterpret_cast<const f4*>(Sh + (int64_t)p * N + n);
-      Pol::put(sm.u.sh, p, n, v.x);
-      Pol::put(sm.u.sh, p, n + 1, v.y);
-      Pol::put(sm.u.sh, p, n + 2, v.z);
-      Pol::put(sm.u.sh, p, n + 3, v.w);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < PT; ++ct) {
-      f4 d = f4{0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) d = Pol::mma(cf[s], Pol::frag(sm.u.sh, 16 * ct, s * Pol::KS, lane), d);
-      // D rows are virtual rows 16*wave + 4g + j
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int vv = row0 + 16 * wave + 4 * g + j;
-        const float e = vv < rows ? sm.ecs[vv / R] : 0.0f;
-        d[j] *= e;
-      }
-      acc[ct] = d;
-    }
-  }
-
-  // Y_diag over the u blocks that reach the own rows
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
-  const int my_tmax = min(Lc - 1, (row0 + 16 * wave + 15) / R);  // last token of own tile
-  const int ulim = min(rows, (tok1 + 1) * R);                      // u rows needed by the block
-  for (int ub = 0; ub * kRB < ulim; ++ub) {
+
+  // own rotated C rows -> MFMA fragments in registers
+  typename Pol::Frag cf[G::TPW][NKS];
+#pragma unroll
+  for (int j = 0; j < G::TPW; ++j)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) cf[j][s] = typename Pol::Frag{};
+  for (int blk = 0; blk < G::NUB; ++blk) {
+    if (blk * kRB >= rows) break;
     __syncthreads();
-    for (int idx = tid; idx < kRB * NP; idx += 256) {
-      const int k = idx % NP, ul = idx / NP;
-      const int v = ub * kRB + ul;
-      float o0 = 0.0f, o1 = 0.0f;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        const int64_t base = (((int64_t)b * a.T + c0 + t) * a.H + h) * N * R;
-        const float u0 = ld1(Bg, base + (2 * k) * R + r);
-        const float u1 = ld1(Bg, base + (2 * k + 1) * R + r);
-        const f2 cs = sm.rot[t * NP + k];
-        o0 = cs.x * u0 + cs.y * u1;
-        o1 = -cs.y * u0 + cs.x * u1;
-      }
-      Pol::put(sm.u.bt, ul, 2 * k, o0);
-      Pol::put(sm.u.bt, ul, 2 * k + 1, o1);
-    }
-    for (int idx = tid; idx < kRB * P; idx += 256) {
-      const int p = idx % P, ul = idx / P;
-      const int v = ub * kRB + ul;
-      float xv = 0.0f;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        xv = ld1(Xg, ((((int64_t)b * a.T + c0 + t) * a.H + h) * P + p) * R + r);
-      }
-      Pol::putx(sm.xs, p, ul, xv);
-    }
+    stage_rows<Pol, TI, N, R, G::NT>(sm.u.st, Cg, a, b, h, c0, Lc, blk * kRB, sm.tb.rot);
     __syncthreads();
-    for (int ug = 0; ug < kRB; ug += UG) {
-      const int ubase = ub * kRB + ug;
-      if (ubase / R > my_tmax) break;   // causal: nothing left for this tile
-      f4 d[Pol::DT];
 #pragma unroll
-      for (int dt = 0; dt < Pol::DT; ++dt) {
-        f4 gt = f4{0, 0, 0, 0};
+    for (int j = 0; j < G::TPW; ++j)
+      if (tile[j] / 4 == blk) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-          gt = Pol::mma(Pol::frag(sm.u.bt, ug + 16 * dt, s * Pol::KS, lane), cf[s], gt);
-        // gt: rows u = ubase + 16dt + 4g + j, column t-row = own row l16
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int uv = ubase + 16 * dt + 4 * g + j;
-          const int tu = uv / R;
-          const int tt = vrow / R;
-          float m = 0.0f;
-          if (vrow < rows && uv < rows && tu <= tt) m = sm.mtok[tt - tok0][tu];
-          gt[j] *= m;
-        }
-        d[dt] = gt;
+        for (int s = 0; s < NKS; ++s) cf[j][s] = Pol::frag(sm.u.st, 16 * (tile[j] % 4), s * Pol::KS, lane);
       }
-      const typename Pol::Frag af = Pol::frag_from_d(d);
+  }
+
+  // Y_off = e^{cs_t} Ct Shat^T
+  __syncthreads();
+  {
+    const float* __restrict__ Sh = a.S + chunk_id * P * N;
+    constexpr int NV = P * N / 8;
+    constexpr int IT = (NV + G::NT - 1) / G::NT;
+    float v[IT][8];
 #pragma unroll
-      for (int ct = 0; ct < PT; ++ct)
-        acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs, 16 * ct, ug, lane), acc[ct]);
+    for (int i = 0; i < IT; ++i) {
+      const int vi = tid + G::NT * i;
+      if (vi < NV) ld8(Sh, (int64_t)vi * 8, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = tid + G::NT * i;
+      if (vi < NV) Pol::put8(sm.u.sh, (vi * 8) / N, (vi * 8) % N, v[i]);
+    }
+  }
+  __syncthreads();
+  f4 acc[G::TPW][G::PT];
+#pragma unroll
+  for (int j = 0; j < G::TPW; ++j) {
+#pragma unroll
+    for (int ct = 0; ct < G::PT; ++ct) {
+      f4 d = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) d = Pol::mma(cf[j][s], Pol::frag(sm.u.sh, 16 * ct, s * Pol::KS, lane), d);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vv = 16 * tile[j] + 4 * g + jj;
+        d[jj] *= vv < rows ? sm.tb.aux[vv / R] : 0.0f;
+      }
+      acc[j][ct] = d;
     }
   }
 
-  // y[b, c0 + t, h, p, r] for D rows v = row0 + 16*wave + 4g + j, column p
+  // Y_diag: Gram tiles Bt Ct^T (D rows = u, columns = own rows), decay mask,
+  // then the masked tile is the A operand of the product with x
+  for (int ub = 0; ub < G::NUB; ++ub) {
+    if (ub * kRB >= rows) break;
+    __syncthreads();
+    stage_rows<Pol, TI, N, R, G::NT>(sm.u.st, Bg, a, b, h, c0, Lc, ub * kRB, sm.tb.rot);
+    stage_x_T<Pol, TI, P, R, G::NT>(sm.xs, Xg, a, b, h, c0, Lc, ub * kRB);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G::TPW; ++j) {
+      const int i = tile[j];
+      const int vrow = 16 * i + l16;
+      const int tt = vrow / R;
+      const bool row_ok = vrow < rows;
+      const int tmax = min(Lc - 1, (16 * i + 15) / R);
+      const double cst = sm.tb.cs[min(tt, kQ - 1)];
+      for (int ug = 0; ug < kRB; ug += UG) {
+        const int ubase = ub * kRB + ug;
+        if (ubase / R > tmax) break;
+        f4 d[Pol::DT];
+#pragma unroll
+        for (int dt = 0; dt < Pol::DT; ++dt) {
+          f4 gt = f4{0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < NKS; ++s)
+            gt = Pol::mma(Pol::frag(sm.u.st, ug + 16 * dt, s * Pol::KS, lane), cf[j][s], gt);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int tu = (ubase + 16 * dt + 4 * g + jj) / R;
+            float m = 0.0f;
+            if (row_ok && tu <= tt) {
+              const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
+              m = __expf((float)(cst - sm.tb.cs[tu])) * w;
+            }
+            gt[jj] *= m;
+          }
+          d[dt] = gt;
+        }
+        const typename Pol::Frag af = Pol::frag_from_d(d);
+#pragma unroll
+        for (int ct = 0; ct < G::PT; ++ct)
+          acc[j][ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs, 16 * ct, ug, lane), acc[j][ct]);
+      }
+    }
+  }
+
+  // y[b, c0 + t, h, p, r] for D rows v = 16 tile + 4g + jj, column p
   TO* __restrict__ Y = static_cast<TO*>(a.y);
 #pragma unroll
-  for (int ct = 0; ct < PT; ++ct) {
-    const int p = 16 * ct + l16;
+  for (int j = 0; j < G::TPW; ++j) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int v = row0 + 16 * wave + 4 * g + j;
-      if (v < rows) {
-        const int t = v / R, r = v % R;
-        st1(Y, ((((int64_t)b * a.T + c0 + t) * a.H + h) * P + p) * R + r, acc[ct][j]);
+    for (int ct = 0; ct < G::PT; ++ct) {
+      const int p = 16 * ct + l16;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int v = 16 * tile[j] + 4 * g + jj;
+        if (v < rows)
+          st1(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[j][ct][jj]);
       }
     }
   }
@@ -664,16 +829,15 @@ __global__ __launch_bounds__(256) void k_chunk_output(PrefillArgs a) {
 // --------------------------------------------------------------------------
 template <class Pol, typename TI, typename TO, int P, int N, int R>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(256), 0, s, a);
+  using G = Geo<P, N, R>;
+  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_state_pass<TI, N, R>), dim3(a.Bsz * a.H * (P / 16)), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NRB = (kQ * R + kRB - 1) / kRB;
-  const int groups = (a.nchunk + 7) / 8;
-  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(groups * 8 * NRB, a.H, a.Bsz),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G::NT),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -698,7 +862,8 @@ static int dispatch_shape(const PrefillArgs& a, hipStream_t s, hipError_t* e) {
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16) {
   if (Q != kQ) return false;
-  const bool shape = (P == 16 && N == 16 && R == 1) || (P == 64 && N == 128 && (R == 1 || R == 2 || R == 4)) ||
+  const bool shape = (P == 16 && N == 16 && R == 1) ||
+                     (P == 64 && N == 128 && (R == 1 || R == 2 || R == 4)) ||
                      (P == 32 && N == 64 && (R == 1 || R == 4));
   if (!shape) return false;
   if (in_bf16 && N % 32 != 0) return false;  // fp16 fragments span 32 state columns
