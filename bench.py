@@ -218,6 +218,29 @@ def bench_prefill(name, steps, warmup):
                 bytes=prefill_bytes(w), tokens=w.batch * w.seqlen, ws_bytes=ws.numel())
 
 
+def copy_reference(state_bytes, reps=50):
+    """A plain device copy of a state-sized buffer (torch's copy kernel): read
+    + write of the same byte count the decode step streams.  Context for the
+    8 TB/s nominal peak; not a kernel of this library."""
+    import torch
+    n = state_bytes // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return dict(bytes=2 * state_bytes, us=round(ms * 1e3, 2), gbs=round(2 * state_bytes / (ms * 1e-3) / 1e9, 1),
+                kernel="torch copy_ (read + write of a 268 MB fp32 buffer)")
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands, on a bounded sample
 def cpu_decode(name, budget_s=8.0):
@@ -302,6 +325,12 @@ def main():
     if want("mimo_prefill"):
         res["mimo_prefill"] = bench_prefill("mimo_prefill", a.prefill_steps, 2)
 
+    copy_ref = None
+    if "siso_decode" in res:
+        from linear_recurrent_sequence_mamba_amd import inputs as I
+        w = I.WORKLOADS["siso_decode"]
+        copy_ref = copy_reference(w.batch * w.nheads * w.headdim * w.dstate * 4)
+
     cpu = {}
     if not a.no_cpu_baseline:
         t0 = time.time()
@@ -363,6 +392,8 @@ def main():
         workloads["mimo_decode"]["step_time_vs_siso"] = round(
             workloads["mimo_decode"]["us_per_step"] / workloads["siso_decode"]["us_per_step"], 3)
     line["workloads"] = workloads
+    if copy_ref is not None:
+        line["hbm_copy_reference"] = copy_ref
     print(json.dumps(line), flush=True)
 
 

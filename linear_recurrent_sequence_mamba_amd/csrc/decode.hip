@@ -25,69 +25,90 @@
 namespace m3 {
 
 // --------------------------------------------------------------------------
+// The per-token scalars and the phase of one pair are loaded before the
+// state stream is issued: the load counter retires in order, so waiting for
+// a small load issued after the state loads would wait for the whole stream.
+template <typename TI, int N>
+struct TokenIn {
+  float d, l, A, th;
+};
+
+template <typename TI, int N>
+__device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh) {
+  TokenIn<TI, N> in;
+  const int head = bh % a.H;
+  in.d = ld1(static_cast<const TI*>(a.dt), bh);
+  in.l = ld1(static_cast<const TI*>(a.lam), bh);
+  in.A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
+  const int k = threadIdx.x;
+  in.th = k < N / 2 ? ld1(static_cast<const TI*>(a.theta), (int64_t)bh * (N / 2) + k) : 0.0f;
+  return in;
+}
+
+// alpha, beta, gamma; (cos, sin) of the token's phase per pair into LDS
+template <typename TI, int N>
+__device__ __forceinline__ void token_finish(const DecodeArgs& a, const TokenIn<TI, N>& in,
+                                             float& alpha, float& beta, float& gamma, f2* cs_sh) {
+  alpha = expf(in.d * in.A);
+  beta = (1.0f - in.l) * in.d * alpha;
+  gamma = in.l * in.d;
+  const int k = threadIdx.x;
+  if (k < N / 2) {
+    const float phi = (a.flags & kThetaIsAngle) ? in.th : in.d * in.th;
+    float s, c;
+    sincosf(phi, &s, &c);
+    cs_sh[k] = f2{c, s};
+  }
+}
+
+// --------------------------------------------------------------------------
 // single input / single output
-template <typename TI, typename TO, int N>
+template <typename TI, typename TO, int N, bool PREV>
 __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   constexpr int LPR = N / 4;           // lanes per state row
   constexpr int RPW = 64 / LPR;        // rows per wave per pass
   constexpr int RPB = 4 * RPW;         // rows per block per pass
   constexpr int UNR = RPB >= 64 ? 1 : 64 / RPB;  // passes kept in flight
+  static_assert(N / 2 <= 256, "one pair per thread");
   __shared__ f2 cs_sh[N / 2];
 
   const int bh = blockIdx.x;
-  const int head = bh % a.H;
   const int P = a.P;
-  const TI* __restrict__ dt = static_cast<const TI*>(a.dt);
-  const TI* __restrict__ lam = static_cast<const TI*>(a.lam);
-  const TI* __restrict__ theta = static_cast<const TI*>(a.theta);
-
-  const float d = ld1(dt, bh);
-  const float l = ld1(lam, bh);
-  const float A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
-  const float alpha = expf(d * A);
-  const float beta = (1.0f - l) * d * alpha;
-  const float gamma = l * d;
-
-  for (int k = threadIdx.x; k < N / 2; k += blockDim.x) {
-    const float th = ld1(theta, (int64_t)bh * (N / 2) + k);
-    const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
-    float s, c;
-    sincosf(phi, &s, &c);
-    cs_sh[k] = f2{c, s};
-  }
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n0 = 4 * (lane % LPR);
-  const int64_t vec = (int64_t)bh * N + n0;
-  const f4 bt = ld4(static_cast<const TI*>(a.Bt), vec) * gamma;
-  const f4 bp = a.has_prev ? ld4(static_cast<const TI*>(a.Bp), vec) * beta : f4{0, 0, 0, 0};
-  const f4 ct = ld4(static_cast<const TI*>(a.Ct), vec);
-  __syncthreads();
-  const f2 r0 = cs_sh[n0 / 2];
-  const f2 r1 = cs_sh[n0 / 2 + 1];
-
+  const int rsub = wave * RPW + lane / LPR;
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
   const TI* __restrict__ x = static_cast<const TI*>(a.x) + (int64_t)bh * P;
   const TI* __restrict__ xp = static_cast<const TI*>(a.xp) + (int64_t)bh * P;
   TO* __restrict__ y = static_cast<TO*>(a.y) + (int64_t)bh * P;
-  const int rsub = wave * RPW + lane / LPR;
 
-  for (int pbase = 0; pbase < P; pbase += RPB * UNR) {
-    f4 v[UNR];
-    float xv[UNR], xpv[UNR];
+  const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
+  const int64_t vec = (int64_t)bh * N + n0;
+  f4 bt = ld4(static_cast<const TI*>(a.Bt), vec);
+  f4 bp = PREV ? ld4(static_cast<const TI*>(a.Bp), vec) : f4{0, 0, 0, 0};
+  const f4 ct = ld4(static_cast<const TI*>(a.Ct), vec);
+
+  // the state stream; rows past P are clamped for the loads, masked for the stores
+  f4 v[UNR];
+  float xv[UNR], xpv[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int p = pbase + u * RPB + rsub;
-      if (p < P) {
-        v[u] = ld4_stream(hb + (int64_t)p * N + n0);
-        xv[u] = ld1(x, p);
-        xpv[u] = a.has_prev ? ld1(xp, p) : 0.0f;
-      } else {
-        v[u] = f4{0, 0, 0, 0};
-        xv[u] = xpv[u] = 0.0f;
-      }
-    }
+  for (int u = 0; u < UNR; ++u) {
+    const int p = min(u * RPB + rsub, P - 1);
+    v[u] = ld4_stream(hb + (int64_t)p * N + n0);
+    xv[u] = ld1(x, p);
+    xpv[u] = PREV ? ld1(xp, p) : 0.0f;
+  }
+
+  float alpha, beta, gamma;
+  token_finish<TI, N>(a, tin, alpha, beta, gamma, cs_sh);
+  bt *= gamma;
+  bp *= beta;
+  __syncthreads();
+  const f2 r0 = cs_sh[n0 / 2];
+  const f2 r1 = cs_sh[n0 / 2 + 1];
+
+  for (int pbase = 0;;) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int p = pbase + u * RPB + rsub;
@@ -95,60 +116,40 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
       s = rot2pairs(s, r0, r1);
       s += xv[u] * bt;
       if (p < P) st4_stream(hb + (int64_t)p * N + n0, s);
-      float part = s.x * ct.x + s.y * ct.y + s.z * ct.z + s.w * ct.w;
-#pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      const float part = group_sum<LPR>(s.x * ct.x + s.y * ct.y + s.z * ct.z + s.w * ct.w);
       if ((lane % LPR) == 0 && p < P) st1(y, p, part);
+    }
+    pbase += RPB * UNR;
+    if (pbase >= P) break;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int p = min(pbase + u * RPB + rsub, P - 1);
+      v[u] = ld4_stream(hb + (int64_t)p * N + n0);
+      xv[u] = ld1(x, p);
+      xpv[u] = PREV ? ld1(xp, p) : 0.0f;
     }
   }
 }
 
 // --------------------------------------------------------------------------
 // multi input / multi output, rank R (2 <= R <= 16)
-template <typename TI, typename TO, int N, int R>
+template <typename TI, typename TO, int N, int R, bool PREV>
 __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   constexpr int NT = N / 16;          // 16-column tiles per state row block
   constexpr int KB = (R + 3) / 4;     // K blocks of 4 for the MFMA
+  constexpr int RP = (R + 3) & ~3;    // rank padded to a multiple of 4 in LDS
+  constexpr int NE = N * R;           // elements of one B or C
+  constexpr int PER = (NE + 255) / 256;
   __shared__ f2 cs_sh[N / 2];
-  __shared__ float bp_sh[N * R];      // beta * B_{t-1}
-  __shared__ float bt_sh[N * R];      // gamma * B_t
-  __shared__ float c_sh[N * R];       // C_t
+  __shared__ float bp_sh[N * RP];     // beta * B_{t-1}   [n][r]
+  __shared__ float bt_sh[N * RP];     // gamma * B_t      [n][r]
+  __shared__ float c_sh[N * RP];      // C_t              [n][r]
 
   const int bh = blockIdx.x;
-  const int head = bh % a.H;
   const int P = a.P;
-  const TI* __restrict__ dt = static_cast<const TI*>(a.dt);
-  const TI* __restrict__ lam = static_cast<const TI*>(a.lam);
-  const TI* __restrict__ theta = static_cast<const TI*>(a.theta);
-
-  const float d = ld1(dt, bh);
-  const float l = ld1(lam, bh);
-  const float A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
-  const float alpha = expf(d * A);
-  const float beta = (1.0f - l) * d * alpha;
-  const float gamma = l * d;
-
-  for (int k = threadIdx.x; k < N / 2; k += blockDim.x) {
-    const float th = ld1(theta, (int64_t)bh * (N / 2) + k);
-    const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
-    float s, c;
-    sincosf(phi, &s, &c);
-    cs_sh[k] = f2{c, s};
-  }
-  {
-    const TI* __restrict__ Bt = static_cast<const TI*>(a.Bt) + (int64_t)bh * N * R;
-    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + (int64_t)bh * N * R;
-    const TI* __restrict__ Ct = static_cast<const TI*>(a.Ct) + (int64_t)bh * N * R;
-    for (int i = threadIdx.x; i < N * R; i += blockDim.x) {
-      bt_sh[i] = gamma * ld1(Bt, i);
-      bp_sh[i] = a.has_prev ? beta * ld1(Bp, i) : 0.0f;
-      c_sh[i] = ld1(Ct, i);
-    }
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int i16 = lane & 15;   // MFMA column (state row p) / A-operand row
   const int g = lane >> 4;     // MFMA k lane group / D row group
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
@@ -156,44 +157,88 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   const TI* __restrict__ xp = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
   TO* __restrict__ y = static_cast<TO*>(a.y) + (int64_t)bh * P * R;
 
-  for (int pb = wave; pb * 16 < P; pb += 4) {
-    const int p = pb * 16 + i16;
-    f4 v[NT];
+  const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
+  float eb[PER], ep[PER], ec[PER];
+  {
+    const TI* __restrict__ Bt = static_cast<const TI*>(a.Bt) + (int64_t)bh * NE;
+    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + (int64_t)bh * NE;
+    const TI* __restrict__ Ct = static_cast<const TI*>(a.Ct) + (int64_t)bh * NE;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)p * N + 16 * t + 4 * g);
+    for (int q = 0; q < PER; ++q) {
+      const int i = tid + 256 * q;
+      const int ic = min(i, NE - 1);
+      eb[q] = ld1(Bt, ic);
+      ep[q] = PREV ? ld1(Bp, ic) : 0.0f;
+      ec[q] = ld1(Ct, ic);
+    }
+  }
+
+  // the first row block's state stream
+  int pb = wave;
+  f4 v[NT];
+  if (pb * 16 < P) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)(pb * 16 + i16) * N + 16 * t + 4 * g);
+  }
+
+  float alpha, beta, gamma;
+  token_finish<TI, N>(a, tin, alpha, beta, gamma, cs_sh);
+  if constexpr (RP != R) {
+    for (int i = tid; i < N * RP; i += 256) bt_sh[i] = bp_sh[i] = c_sh[i] = 0.0f;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + 256 * q;
+    if (i < NE) {
+      const int j = (i / R) * RP + i % R;
+      bt_sh[j] = gamma * eb[q];
+      bp_sh[j] = beta * ep[q];
+      c_sh[j] = ec[q];
+    }
+  }
+  __syncthreads();
+
+  for (; pb * 16 < P; pb += 4) {
+    const int p = pb * 16 + i16;
     float xo_p[KB], xo_t[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int r = 4 * kb + g;
       xo_t[kb] = (r < R) ? ld1(x, (int64_t)p * R + r) : 0.0f;
-      xo_p[kb] = (r < R && a.has_prev) ? ld1(xp, (int64_t)p * R + r) : 0.0f;
+      xo_p[kb] = (r < R && PREV) ? ld1(xp, (int64_t)p * R + r) : 0.0f;
     }
-    float yp[R];
+    float yp[RP];
 #pragma unroll
-    for (int r = 0; r < R; ++r) yp[r] = 0.0f;
+    for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f4 acc = alpha * v[t];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int r = 4 * kb + g;
-        const float aop = (r < R) ? bp_sh[(16 * t + i16) * R + r] : 0.0f;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, xo_p[kb], acc, 0, 0, 0);
-      }
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bp_sh[(16 * t + i16) * RP + 4 * kb + g], xo_p[kb],
+                                                   acc, 0, 0, 0);
       const int k0 = 8 * t + 2 * g;    // pair index of acc.x/acc.y
       acc = rot2pairs(acc, cs_sh[k0], cs_sh[k0 + 1]);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int r = 4 * kb + g;
-        const float aop = (r < R) ? bt_sh[(16 * t + i16) * R + r] : 0.0f;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, xo_t[kb], acc, 0, 0, 0);
-      }
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bt_sh[(16 * t + i16) * RP + 4 * kb + g], xo_t[kb],
+                                                   acc, 0, 0, 0);
       st4_stream(hb + (int64_t)p * N + 16 * t + 4 * g, acc);
       const int n = 16 * t + 4 * g;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        yp[r] += acc.x * c_sh[n * R + r] + acc.y * c_sh[(n + 1) * R + r] +
-                 acc.z * c_sh[(n + 2) * R + r] + acc.w * c_sh[(n + 3) * R + r];
+      for (int rb = 0; rb < RP; rb += 4) {
+        const f4 c0 = *reinterpret_cast<const f4*>(&c_sh[(n + 0) * RP + rb]);
+        const f4 c1 = *reinterpret_cast<const f4*>(&c_sh[(n + 1) * RP + rb]);
+        const f4 c2 = *reinterpret_cast<const f4*>(&c_sh[(n + 2) * RP + rb]);
+        const f4 c3 = *reinterpret_cast<const f4*>(&c_sh[(n + 3) * RP + rb]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          yp[rb + q] += acc.x * c0[q] + acc.y * c1[q] + acc.z * c2[q] + acc.w * c3[q];
+      }
+      // keep each tile's LDS operands local to it (hoisting them all would
+      // cost ~150 registers and halve the occupancy)
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -204,19 +249,30 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) st1(y, (int64_t)p * R + r, yp[r]);
     }
+    if ((pb + 4) * 16 < P) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        v[t] = ld4_stream(hb + (int64_t)((pb + 4) * 16 + i16) * N + 16 * t + 4 * g);
+    }
   }
 }
 
 // --------------------------------------------------------------------------
 template <typename TI, typename TO, int N>
 static hipError_t launch_siso(const DecodeArgs& a, int units, hipStream_t s) {
-  hipLaunchKernelGGL((k_decode_siso<TI, TO, N>), dim3(units), dim3(256), 0, s, a);
+  if (a.has_prev)
+    hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true>), dim3(units), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false>), dim3(units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename TI, typename TO, int N, int R>
 static hipError_t launch_mimo(const DecodeArgs& a, int units, hipStream_t s) {
-  hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R>), dim3(units), dim3(256), 0, s, a);
+  if (a.has_prev)
+    hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true>), dim3(units), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false>), dim3(units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -106,4 +106,23 @@ __device__ __forceinline__ f4 rot2pairs(f4 v, f2 c0, f2 c1) {
   return r;
 }
 
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of a group receives the group's sum.  Cross-lane steps within
+// 16 lanes use DPP (quad permutes, half-row and row mirrors), wider ones a
+// single lane permute each.
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W >= 2) v += dpp_get<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (W >= 4) v += dpp_get<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (W >= 8) v += dpp_get<0x141>(v);   // row_half_mirror: 7 - i within 8
+  if constexpr (W >= 16) v += dpp_get<0x140>(v);  // row_mirror: 15 - i within 16
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 }  // namespace m3
