@@ -126,54 +126,41 @@ def bench_decode(name, steps, warmup, pool_n=8):
     for s in range(warmup):
         launch(s)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+
+    # stream launches, K steps (reported beside the graph figure)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(steps):
+        launch(warmup + s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    stream_ms = start.elapsed_time(end)
+
+    # the timed K steps: one HIP graph holding the K launches (what a decode
+    # loop captures), replayed once untimed to load it, then timed
+    g = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for s in range(steps):
+                st = lib.m3_decode_step(*(args[s % pool_n][:-1] + (cap,)))
+                if st != 0:
+                    raise RuntimeError(m3.m3_status_str(st))
+    torch.cuda.synchronize()
+    g.replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    for s in range(steps):
-        ev0[s].record(stream)
-        launch(warmup + s)
-        ev1[s].record(stream)
+    g.replay()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    kms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
-    kern_ms = sum(kms) / len(kms)
     nbytes = decode_bytes(w)
-
-    # the same K steps replayed from a HIP graph (launch overhead removed)
-    graph_ms = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        gs = torch.cuda.Stream()
-        gs.wait_stream(stream)
-        with torch.cuda.stream(gs):
-            with torch.cuda.graph(g, stream=gs):
-                cap = torch.cuda.current_stream()
-                gargs = [a[:-1] + (ctypes.c_void_p(cap.cuda_stream),) for a in args]
-                for s in range(min(steps, 64)):
-                    st = lib.m3_decode_step(*gargs[s % pool_n])
-                    if st != 0:
-                        raise RuntimeError(m3.m3_status_str(st))
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, steps // min(steps, 64))
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / (reps * min(steps, 64))
-    except Exception as exc:  # graph capture is reported, not required
-        log(f"[{name}] graph replay skipped: {exc}")
     return dict(workload=w, steps=steps, total_ms=total_ms, step_ms=total_ms / steps,
-                kernel_ms=kern_ms, kernel_p50_ms=kms[len(kms) // 2], wall_s=wall,
-                bytes=nbytes, graph_step_ms=graph_ms, pool=pool_n)
+                stream_step_ms=stream_ms / steps, wall_s=wall, bytes=nbytes, pool=pool_n)
 
 
 def bench_prefill(name, steps, warmup):
@@ -347,17 +334,16 @@ def main():
     def decode_entry(r, tag):
         w = r["workload"]
         gbs = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
-        ach = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
         traffic = counters_for(tag)
         return dict(
-            us_per_step=round(r["step_ms"] * 1e3, 2), kernel_us=round(r["kernel_ms"] * 1e3, 2),
-            kernel_p50_us=round(r["kernel_p50_ms"] * 1e3, 2),
-            graph_us_per_step=None if r["graph_step_ms"] is None else round(r["graph_step_ms"] * 1e3, 2),
+            us_per_step=round(r["step_ms"] * 1e3, 2),
+            stream_launch_us_per_step=round(r["stream_step_ms"] * 1e3, 2),
             hbm_gbs=round(gbs, 1), tokens_per_s=round(w.batch / (r["step_ms"] * 1e-3), 1),
             algorithmic_bytes=r["bytes"], input_pool=r["pool"],
-            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
-                          kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}"),
+            roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                          kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}",
+                          timing="HIP events around a graph of the K launches (one kernel per step)"),
             cpu_baseline=cpu.get(tag))
 
     def prefill_entry(r, tag):

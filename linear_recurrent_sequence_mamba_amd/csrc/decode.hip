@@ -133,6 +133,17 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
 
 // --------------------------------------------------------------------------
 // multi input / multi output, rank R (2 <= R <= 16)
+//
+// The MFMA row axis runs over state columns: D row 4g + i of tile t is
+// column ncol(t, g) + i = 16t + 4g + i, so a lane's accumulator is the
+// 16-byte vector of 4 consecutive columns it loads.  For the store the
+// wave's 16 x N updated rows pass through a padded LDS buffer and leave as
+// row-contiguous non-temporal 16-byte stores: every store instruction then
+// writes whole 128-byte lines (stored straight from the D layout, each
+// instruction would write half lines and HBM would see ~1.3x the bytes).
+template <int NT>
+__device__ __forceinline__ int ncol(int t, int g) { return 16 * t + 4 * g; }
+
 template <typename TI, typename TO, int N, int R, bool PREV>
 __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   constexpr int NT = N / 16;          // 16-column tiles per state row block
@@ -144,6 +155,7 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   __shared__ float bp_sh[N * RP];     // beta * B_{t-1}   [n][r]
   __shared__ float bt_sh[N * RP];     // gamma * B_t      [n][r]
   __shared__ float c_sh[N * RP];      // C_t              [n][r]
+  __shared__ f4 tr_sh[4][16][N / 4 + 1];  // per-wave updated rows (one vector of padding)
 
   const int bh = blockIdx.x;
   const int P = a.P;
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   f4 v[NT];
   if (pb * 16 < P) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)(pb * 16 + i16) * N + 16 * t + 4 * g);
+    for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)(pb * 16 + i16) * N + ncol<NT>(t, g));
   }
 
   float alpha, beta, gamma;
@@ -214,18 +226,16 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f4 acc = alpha * v[t];
+      const int nA = ncol<NT>(t, i16 >> 2) + (i16 & 3);   // state column of A-operand row i16
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bp_sh[(16 * t + i16) * RP + 4 * kb + g], xo_p[kb],
-                                                   acc, 0, 0, 0);
-      const int k0 = 8 * t + 2 * g;    // pair index of acc.x/acc.y
-      acc = rot2pairs(acc, cs_sh[k0], cs_sh[k0 + 1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bp_sh[nA * RP + 4 * kb + g], xo_p[kb], acc, 0, 0, 0);
+      const int n = ncol<NT>(t, g);        // state columns n..n+3 of acc
+      acc = rot2pairs(acc, cs_sh[n / 2], cs_sh[n / 2 + 1]);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bt_sh[(16 * t + i16) * RP + 4 * kb + g], xo_t[kb],
-                                                   acc, 0, 0, 0);
-      st4_stream(hb + (int64_t)p * N + 16 * t + 4 * g, acc);
-      const int n = 16 * t + 4 * g;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bt_sh[nA * RP + 4 * kb + g], xo_t[kb], acc, 0, 0, 0);
+      tr_sh[wave][i16][n / 4] = acc;
 #pragma unroll
       for (int rb = 0; rb < RP; rb += 4) {
         const f4 c0 = *reinterpret_cast<const f4*>(&c_sh[(n + 0) * RP + rb]);
@@ -249,10 +259,26 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) st1(y, (int64_t)p * R + r, yp[r]);
     }
+    // the wave's 16 rows back to HBM, row-contiguous (the buffer is private
+    // to the wave; a wave barrier orders the LDS writes before the reads)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      constexpr int V4 = N / 4;           // vectors per row
+#pragma unroll
+      for (int j = 0; j < 16 * V4 / 64; ++j) {
+        const int q = lane + 64 * j;
+        const int rr = q / V4, c4 = q % V4;
+        st4_stream(hb + (int64_t)(pb * 16 + rr) * N + 4 * c4, tr_sh[wave][rr][c4]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if ((pb + 4) * 16 < P) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        v[t] = ld4_stream(hb + (int64_t)((pb + 4) * 16 + i16) * N + 16 * t + 4 * g);
+      for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)((pb + 4) * 16 + i16) * N + ncol<NT>(t, g));
     }
   }
 }
