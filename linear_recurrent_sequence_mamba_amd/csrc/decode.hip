@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int p = min(u * RPB + rsub, P - 1);
-    v[u] = ld4_stream(hb + (int64_t)p * N + n0);
+    v[u] = ld4_state(hb + (int64_t)p * N + n0);
     xv[u] = ld1(x, p);
     xpv[u] = PREV ? ld1(xp, p) : 0.0f;
   }
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int p = min(pbase + u * RPB + rsub, P - 1);
-      v[u] = ld4_stream(hb + (int64_t)p * N + n0);
+      v[u] = ld4_state(hb + (int64_t)p * N + n0);
       xv[u] = ld1(x, p);
       xpv[u] = PREV ? ld1(xp, p) : 0.0f;
     }
@@ -185,12 +185,18 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
     }
   }
 
-  // the first row block's state stream
+  // the first row block's state stream, row-contiguous (whole 128-byte
+  // lines per load instruction); it reaches the D layout through LDS
+  constexpr int V4 = N / 4;            // 16-byte vectors per row
+  constexpr int LV = 16 * V4 / 64;     // row vectors per lane per 16-row block
   int pb = wave;
-  f4 v[NT];
+  f4 raw[LV];
   if (pb * 16 < P) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)(pb * 16 + i16) * N + ncol<NT>(t, g));
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      raw[j] = ld4_state(hb + (int64_t)(pb * 16 + q / V4) * N + 4 * (q % V4));
+    }
   }
 
   float alpha, beta, gamma;
@@ -213,6 +219,21 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
 
   for (; pb * 16 < P; pb += 4) {
     const int p = pb * 16 + i16;
+    // rows -> LDS -> D layout (the buffer is private to the wave)
+#pragma unroll
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      tr_sh[wave][q / V4][q % V4] = raw[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f4 v[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = tr_sh[wave][i16][ncol<NT>(t, g) / 4];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float xo_p[KB], xo_t[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -265,9 +286,8 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     {
-      constexpr int V4 = N / 4;           // vectors per row
 #pragma unroll
-      for (int j = 0; j < 16 * V4 / 64; ++j) {
+      for (int j = 0; j < LV; ++j) {
         const int q = lane + 64 * j;
         const int rr = q / V4, c4 = q % V4;
         st4_stream(hb + (int64_t)(pb * 16 + rr) * N + 4 * c4, tr_sh[wave][rr][c4]);
@@ -278,7 +298,10 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if ((pb + 4) * 16 < P) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) v[t] = ld4_stream(hb + (int64_t)((pb + 4) * 16 + i16) * N + ncol<NT>(t, g));
+      for (int j = 0; j < LV; ++j) {
+        const int q = lane + 64 * j;
+        raw[j] = ld4_state(hb + (int64_t)((pb + 4) * 16 + q / V4) * N + 4 * (q % V4));
+      }
     }
   }
 }

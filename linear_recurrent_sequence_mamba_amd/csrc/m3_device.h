@@ -87,9 +87,12 @@ __device__ __forceinline__ void st1(T* __restrict__ p, int64_t i, float v) {
   p[i] = from_f32<T>(v);
 }
 
-// streaming (non-temporal) 16-byte state access
-__device__ __forceinline__ f4 ld4_stream(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+// 16-byte state access.  Loads use the default (cached) policy and stores
+// are non-temporal: on gfx950 this pair streams the decode state fastest
+// (measured: 84 us per B=128 H=64 P=64 N=128 step against 88 us with
+// non-temporal loads and 95 us with cached stores).
+__device__ __forceinline__ f4 ld4_state(const float* p) {
+  return *reinterpret_cast<const f4*>(p);
 }
 __device__ __forceinline__ void st4_stream(float* p, f4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
