@@ -58,26 +58,28 @@ def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True):
     return inputs + states + H * 4 + out_bytes * B * T * H * P * R
 
 
-def kernel_source_hash():
+def source_hash(files):
+    """Hash of the named files under the package's csrc/ directory."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrent_sequence_mamba_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def counters_for(kernel_tag):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/hbm_counters.json), if it was taken on the current sources of
+    that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "hbm_counters.json")
     try:
         with open(path) as fh:
             data = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel_tag)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    ent = data.get("kernels", {}).get(kernel_tag)
+    if not ent or ent.get("source_hash") != source_hash(ent.get("sources", [])):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -353,7 +355,7 @@ def main():
             tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
             algorithmic_bytes=r["bytes"], workspace_bytes=r["ws_bytes"],
             roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=counters_for(tag),
                           kernel="whole call (k_chunk_state + k_state_pass + k_chunk_output)"),
             cpu_baseline=cpu.get(tag))
 
