@@ -39,6 +39,8 @@
 #include "m3_device.h"
 #include "m3_launch.h"
 
+#include <type_traits>
+
 namespace m3 {
 
 constexpr int kQ = 64;         // chunk length
@@ -121,14 +123,37 @@ struct PolF16 {
   struct XStore {
     _Float16 v[ROWS][K + 8];
   };
-  // x = hi + lo to about 2^-22 relative.  The empty asm pins x to one fp32
-  // register value: otherwise FP contraction may fold the producer's
-  // multiply into the lo subtraction (using the exact product) while hi is
-  // rounded from the fp32 product, and hi + lo then misses x by an fp16 ulp.
+  // x = hi + lo to about 2^-22 relative: hi = fp16(x) (round to nearest
+  // even), lo = fp16(x - hi) with the difference formed exactly inside
+  // v_fma_mix (x * 1 - hi, one rounding).  Written as asm on purpose: x is
+  // then one fixed fp32 register value, so FP contraction cannot fold the
+  // producer's multiply into lo while hi is rounded from the fp32 product
+  // (hi + lo would then miss x by an fp16 ulp).
   static __device__ __forceinline__ void split(float x, _Float16& hi, _Float16& lo) {
-    asm volatile("" : "+v"(x));
-    hi = static_cast<_Float16>(x);
-    lo = static_cast<_Float16>(x - static_cast<float>(hi));
+    uint32_t h, l = 0;
+    asm volatile("v_cvt_f16_f32 %0, %1" : "=v"(h) : "v"(x));
+    asm volatile("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "+v"(l) : "v"(x), "v"(h));
+    hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xffffu));
+    lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(l & 0xffffu));
+  }
+  // the same for two values, packed (element 0 in the low half)
+  static __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    uint32_t h, l = 0;
+    asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h) : "v"(x0), "v"(x1));
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "+v"(l)
+        : "v"(x0), "v"(h), "v"(x1));
+    hi = h;
+    lo = l;
+  }
+  static __device__ __forceinline__ void split8(const float* v, h8& hi, h8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+    hi = __builtin_bit_cast(h8, uint4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(h8, uint4{l[0], l[1], l[2], l[3]});
   }
   template <int ROWS, int K>
   static __device__ __forceinline__ void put(Store<ROWS, K>& s, int r, int k, float x) {
@@ -141,13 +166,7 @@ struct PolF16 {
   template <int ROWS, int K>
   static __device__ __forceinline__ void put8(Store<ROWS, K>& s, int r, int k0, const float* v) {
     h8 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      _Float16 a, b;
-      split(v[j], a, b);
-      hi[j] = a;
-      lo[j] = b;
-    }
+    split8(v, hi, lo);
     *reinterpret_cast<h8*>(&s.hi[r][k0]) = hi;
     *reinterpret_cast<h8*>(&s.lo[r][k0]) = lo;
   }
@@ -158,13 +177,7 @@ struct PolF16 {
   }
   static __device__ __forceinline__ Frag make(const float* v) {
     Frag f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      _Float16 h, l;
-      split(v[j], h, l);
-      f.hi[j] = h;
-      f.lo[j] = l;
-    }
+    split8(v, f.hi, f.lo);
     return f;
   }
   // slot 8g+j <-> k0 + 4g + j (j < 4) and k0 + 16 + 4g + (j - 4) (j >= 4)
@@ -200,12 +213,13 @@ struct PolF16 {
 // --------------------------------------------------------------------------
 // launch geometry: one block per chunk; each wave owns TPW 16-row tiles of
 // the chunk's Q*R virtual rows (two tiles w and 2NW-1-w when TPW = 2, which
-// balances the causal work across waves)
-template <int P, int N, int R>
+// balances the causal work across waves).  Up to 16 waves per block, so the
+// rank-4 chunk (16 tiles) has one tile per wave.
+template <int P, int N, int R, int MAXW = 16>
 struct Geo {
   static constexpr int ROWS = kQ * R;
   static constexpr int TILES = ROWS / 16;
-  static constexpr int NW = TILES >= 8 ? 8 : 4;
+  static constexpr int NW = (TILES >= 16 && MAXW >= 16) ? 16 : (TILES >= 8 ? 8 : 4);
   static constexpr int TPW = TILES / NW;
   static constexpr int NT = NW * 64;
   static constexpr int NP = N / 2;
@@ -215,8 +229,10 @@ struct Geo {
   static_assert(TPW >= 1 && TILES % NW == 0, "tile split");
 };
 
-// per-chunk tables in LDS
-template <int NT, int N>
+// per-chunk tables in LDS.  ROT: keep (cos, sin) of each angle (computed
+// once); otherwise keep the reduced angle and take its sine and cosine where
+// a row is staged (half the LDS; each angle is then used once).
+template <int NT, int N, bool ROT>
 struct Tables {
   double cs[kQ];      // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
   float dt[kQ];
@@ -225,7 +241,26 @@ struct Tables {
   float aux[kQ];      // e^{cs_t} (outputs) or the chunk-state weights W_t
   double seg[NT];
   double phi_end[N / 2];
-  f2 rot[kQ][N / 2];  // (cos, sin) of Phi_t (mode 0) or of Phi_end - Phi_t (mode 1)
+  typename std::conditional<ROT, f2, float>::type tab[kQ][N / 2];
+  // Phi_t (mode 0) or Phi_end - Phi_t (mode 1), reduced to [-pi, pi]
+  __device__ __forceinline__ void set(int t, int k, float ang) {
+    if constexpr (ROT) {
+      float sn, cn;
+      sincosf(ang, &sn, &cn);
+      tab[t][k] = f2{cn, sn};
+    } else {
+      tab[t][k] = ang;
+    }
+  }
+  __device__ __forceinline__ f2 cs_of(int t, int k) const {
+    if constexpr (ROT) {
+      return tab[t][k];
+    } else {
+      float sn, cn;
+      sincosf(tab[t][k], &sn, &cn);
+      return f2{cn, sn};
+    }
+  }
 };
 
 __device__ __forceinline__ float reduce_angle(double phi) {
@@ -237,60 +272,135 @@ __device__ __forceinline__ int64_t token_index(const PrefillArgs& a, int b, int 
   return ((int64_t)b * a.T + t) * a.H + h;
 }
 
-// Token scalars, the chunk-local log-decay prefix (double, one wave) and the
-// chunk-local phase prefix of every pair (double; each thread owns one pair
-// and a segment of tokens), then (cos, sin) of the reduced angles.  th_raw
-// is scratch for the chunk's theta (Q x N/2 floats) and is free on return.
-template <typename TI, int N, int NT>
-__device__ void chunk_tables(const PrefillArgs& a, int b, int h, int c0, int Lc,
-                             Tables<NT, N>& tb, float* th_raw, int mode) {
-  constexpr int NP = N / 2;
-  constexpr int VPT = NP / 8;                 // 16-byte vectors per token
-  constexpr int NV = kQ * VPT;
-  constexpr int IT = (NV + NT - 1) / NT;
-  const int tid = threadIdx.x;
-  const TI* __restrict__ th = static_cast<const TI*>(a.theta);
-  float v[IT][8];
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    const int t = vi / VPT, kv = vi % VPT;
-    if (vi < NV && t < Lc) {
-      ld8(th, token_index(a, b, c0 + t, h) * NP + 8 * kv, v[i]);
+// Raw 16-byte vectors of eight input elements, held in registers between
+// the load that is issued early and the store into LDS.
+template <typename TI>
+struct Vec8;
+template <>
+struct Vec8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = uint4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+};
+template <>
+struct Vec8<float> {
+  f4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f4*>(p);
+    b = *reinterpret_cast<const f4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// One 64-virtual-row block of a per-token array with E elements per token
+// (B or C: E = N R; x: E = P R) as 16-byte vectors spread over the block's
+// NT threads.  TF: consecutive threads take consecutive tokens (for the
+// transposed LDS layouts); otherwise consecutive threads walk one token.
+template <typename TI, int E, int R, int NT, bool TF>
+struct RowBlock {
+  static constexpr int VPT = E / 8;
+  static constexpr int NTOK = kRB / R;
+  static constexpr int NV = NTOK * VPT;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  Vec8<TI> raw[IT];
+  static __device__ __forceinline__ void where(int vi, int& tl, int& e0) {
+    if constexpr (TF) {
+      tl = vi % NTOK;
+      e0 = (vi / NTOK) * 8;
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+      tl = vi / VPT;
+      e0 = (vi % VPT) * 8;
     }
   }
-  if (tid < 64) {
-    double lv = 0.0;
-    float d = 0.0f, gm = 0.0f, bp = 0.0f;
+  __device__ __forceinline__ void load(const TI* __restrict__ src, const PrefillArgs& a, int b,
+                                       int h, int c0, int Lc, int v0) {
+    const int t0 = v0 / R;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      int tl, e0;
+      where(vi, tl, e0);
+      if (vi < NV && t0 + tl < Lc)
+        raw[i].load(src + token_index(a, b, c0 + t0 + tl, h) * E + e0);
+      else
+        raw[i].zero();
+    }
+  }
+};
+
+// Q x N/2 phase inputs of the chunk plus the first wave's token scalars
+template <typename TI, int N, int NT>
+struct ThetaBlock {
+  static constexpr int NP = N / 2;
+  static constexpr int VPT = NP / 8;
+  static constexpr int NV = kQ * VPT;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  Vec8<TI> raw[IT];
+  float d, l, A;
+  __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      const int t = vi / VPT, kv = vi % VPT;
+      if (vi < NV && t < Lc)
+        raw[i].load(th + token_index(a, b, c0 + t, h) * NP + 8 * kv);
+      else
+        raw[i].zero();
+    }
+    const int tid = threadIdx.x;
+    d = l = A = 0.0f;
     if (tid < Lc) {
       const int64_t bth = token_index(a, b, c0 + tid, h);
       d = ld1(static_cast<const TI*>(a.dt), bth);
-      const float l = ld1(static_cast<const TI*>(a.lam), bth);
-      const float A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
-      lv = (double)d * (double)A;
-      gm = l * d;
-      bp = (1.0f - l) * d;
+      l = ld1(static_cast<const TI*>(a.lam), bth);
+      A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
     }
+  }
+};
+
+// The chunk's tables from its loaded inputs: token scalars, the chunk-local
+// log-decay prefix (double, one wave shuffle scan) and phase prefix of
+// every pair (double; each thread owns one pair and a segment of tokens),
+// then the angles reduced to [-pi, pi]: Phi_t (mode 0) or Phi_end - Phi_t
+// (mode 1), kept as (cos, sin) or as the angle (see Tables).  th_raw is LDS
+// scratch for Q x N/2 floats.
+template <typename TI, int N, int NT, bool ROT>
+__device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& tb_in, int Lc,
+                             Tables<NT, N, ROT>& tb, float* th_raw, int mode) {
+  constexpr int NP = N / 2;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    double lv = (double)tb_in.d * (double)tb_in.A;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(lv, off, 64);
       if (tid >= off) lv += o;
     }
     tb.cs[tid] = lv;
-    tb.dt[tid] = d;
-    tb.gam[tid] = gm;
-    tb.bpr[tid] = bp;
+    tb.dt[tid] = tb_in.d;
+    tb.gam[tid] = tb_in.l * tb_in.d;
+    tb.bpr[tid] = (1.0f - tb_in.l) * tb_in.d;
   }
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
+  for (int i = 0; i < ThetaBlock<TI, N, NT>::IT; ++i) {
     const int vi = tid + NT * i;
-    if (vi < NV) {
-      const int t = vi / VPT, kv = vi % VPT;
+    if (vi < ThetaBlock<TI, N, NT>::NV) {
+      float v[8];
+      tb_in.raw[i].get(v);
+      const int t = vi / ThetaBlock<TI, N, NT>::VPT, kv = vi % ThetaBlock<TI, N, NT>::VPT;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[i][j];
+      for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[j];
     }
   }
   __syncthreads();
@@ -321,56 +431,36 @@ __device__ void chunk_tables(const PrefillArgs& a, int b, int h, int c0, int Lc,
     const int t = sg * SEG + i;
     if (t < Lc) {
       const double ph = base + loc[i];
-      float sn, cn;
-      sincosf(reduce_angle(mode == 0 ? ph : pe - ph), &sn, &cn);
-      tb.rot[t][k] = f2{cn, sn};
+      tb.set(t, k, reduce_angle(mode == 0 ? ph : pe - ph));
     }
   }
   __syncthreads();
 }
 
-// Rows [v0, v0 + 64) of the chunk's B or C (virtual row v = t R + r),
-// rotated by -Phi_t, into st[v - v0][n].  16-byte loads, all issued before
-// any is used; rows past the chunk's end are zero.
-template <class Pol, typename TI, int N, int R, int NT>
-__device__ void stage_rows(typename Pol::template Store<kRB, N>& st, const TI* __restrict__ src,
-                           const PrefillArgs& a, int b, int h, int c0, int Lc, int v0,
-                           const f2 (*rot)[N / 2]) {
-  constexpr int E = N * R;
-  constexpr int VPT = E / 8;
-  constexpr int NTOK = kRB / R;
-  constexpr int NV = NTOK * VPT;
-  constexpr int IT = (NV + NT - 1) / NT;
+// B or C rows of a block, rotated by -Phi_t, into st[v - v0][n]
+template <class Pol, typename TI, int N, int R, int NT, class Tab>
+__device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, false>& rb,
+                                           typename Pol::template Store<kRB, N>& st,
+                                           const Tab& tb, int t0, int Lc) {
+  using RBk = RowBlock<TI, N * R, R, NT, false>;
   constexpr int NPAIR = 4 / R;              // complex pairs per vector
-  const int tid = threadIdx.x;
-  const int t0 = v0 / R;
-  float v[IT][8];
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    const int tl = vi / VPT, e0 = (vi % VPT) * 8;
-    if (vi < NV && t0 + tl < Lc) {
-      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    if (vi >= NV) continue;
-    const int tl = vi / VPT, e0 = (vi % VPT) * 8;
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
     const int t = t0 + tl;
     const bool ok = t < Lc;
-    float o[8];
+    float v[8], o[8];
+    rb.raw[i].get(v);
 #pragma unroll
     for (int pi = 0; pi < NPAIR; ++pi) {
       const int n = e0 / R + 2 * pi;
-      const f2 cs = ok ? rot[t][n / 2] : f2{1.0f, 0.0f};
+      const f2 cs = ok ? tb.cs_of(t, n / 2) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float u0 = v[i][(2 * pi) * R + r], u1 = v[i][(2 * pi + 1) * R + r];
+        const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
         o[(2 * pi) * R + r] = cs.x * u0 + cs.y * u1;        // rotate by -Phi_t
         o[(2 * pi + 1) * R + r] = -cs.y * u0 + cs.x * u1;
       }
@@ -384,48 +474,32 @@ __device__ void stage_rows(typename Pol::template Store<kRB, N>& st, const TI* _
   }
 }
 
-// Rows [v0, v0 + 64) of B rotated by +(Phi_end - Phi_t) and scaled by the
-// chunk-state weight W_t, stored transposed: st[n][v - v0].  Consecutive
-// lanes take consecutive tokens so the transposed LDS writes do not collide.
-template <class Pol, typename TI, int N, int R, int NT>
-__device__ void stage_rows_T(typename Pol::template Store<N, kRB>& st, const TI* __restrict__ src,
-                             const PrefillArgs& a, int b, int h, int c0, int Lc, int v0,
-                             const f2 (*rot)[N / 2], const float* w) {
-  constexpr int E = N * R;
-  constexpr int VPT = E / 8;
-  constexpr int NTOK = kRB / R;
-  constexpr int NV = NTOK * VPT;
-  constexpr int IT = (NV + NT - 1) / NT;
+// B rows of a block rotated by +(Phi_end - Phi_t) and scaled by W_t,
+// transposed: st[n][v - v0]
+template <class Pol, typename TI, int N, int R, int NT, class Tab>
+__device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, true>& rb,
+                                             typename Pol::template Store<N, kRB>& st,
+                                             const Tab& tb, const float* w, int t0, int Lc) {
+  using RBk = RowBlock<TI, N * R, R, NT, true>;
   constexpr int NPAIR = 4 / R;
-  const int tid = threadIdx.x;
-  const int t0 = v0 / R;
-  float v[IT][8];
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
-    if (vi < NV && t0 + tl < Lc) {
-      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    if (vi >= NV) continue;
-    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
     const int t = t0 + tl;
     const bool ok = t < Lc;
     const float wt = ok ? w[t] : 0.0f;
+    float v[8];
+    rb.raw[i].get(v);
 #pragma unroll
     for (int pi = 0; pi < NPAIR; ++pi) {
       const int n = e0 / R + 2 * pi;
-      const f2 cs = ok ? rot[t][n / 2] : f2{1.0f, 0.0f};
+      const f2 cs = ok ? tb.cs_of(t, n / 2) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float u0 = v[i][(2 * pi) * R + r], u1 = v[i][(2 * pi + 1) * R + r];
+        const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
         Pol::put(st, n, tl * R + r, wt * (cs.x * u0 - cs.y * u1));   // rotate by +angle
         Pol::put(st, n + 1, tl * R + r, wt * (cs.y * u0 + cs.x * u1));
       }
@@ -433,38 +507,50 @@ __device__ void stage_rows_T(typename Pol::template Store<N, kRB>& st, const TI*
   }
 }
 
-// x rows [v0, v0 + 64) transposed: xs[p][v - v0]
+// x rows of a block, transposed: xs[p][v - v0]
 template <class Pol, typename TI, int P, int R, int NT>
-__device__ void stage_x_T(typename Pol::template XStore<P, kRB>& xs, const TI* __restrict__ src,
-                          const PrefillArgs& a, int b, int h, int c0, int Lc, int v0) {
-  constexpr int E = P * R;
-  constexpr int VPT = E / 8;
-  constexpr int NTOK = kRB / R;
-  constexpr int NV = NTOK * VPT;
-  constexpr int IT = (NV + NT - 1) / NT;
-  const int tid = threadIdx.x;
-  const int t0 = v0 / R;
-  float v[IT][8];
+__device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, true>& rb,
+                                          typename Pol::template XStore<P, kRB>& xs) {
+  using RBk = RowBlock<TI, P * R, R, NT, true>;
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
-    if (vi < NV && t0 + tl < Lc) {
-      ld8(src, token_index(a, b, c0 + t0 + tl, h) * E + e0, v[i]);
-    } else {
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    float v[8];
+    rb.raw[i].get(v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int vi = tid + NT * i;
-    if (vi >= NV) continue;
-    const int tl = vi % NTOK, e0 = (vi / NTOK) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) Pol::putx(xs, (e0 + j) / R, tl * R + (e0 + j) % R, v[i][j]);
+    for (int j = 0; j < 8; ++j) Pol::putx(xs, (e0 + j) / R, tl * R + (e0 + j) % R, v[j]);
   }
 }
+
+// the P x N entry state of a chunk (fp32) as 16-byte vector pairs
+template <int P, int N, int NT>
+struct StateBlock {
+  static constexpr int NV = P * N / 8;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  Vec8<float> raw[IT];
+  __device__ __forceinline__ void load(const float* __restrict__ src) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      if (vi < NV) raw[i].load(src + (int64_t)vi * 8);
+    }
+  }
+  template <class Pol>
+  __device__ __forceinline__ void store(typename Pol::template Store<P, N>& st) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      if (vi < NV) {
+        float v[8];
+        raw[i].get(v);
+        Pol::put8(st, (vi * 8) / N, (vi * 8) % N, v);
+      }
+    }
+  }
+};
 
 // --------------------------------------------------------------------------
 // K1: the chunk's own end state S_c (from a zero entry state), rotated into
@@ -473,7 +559,7 @@ __device__ void stage_x_T(typename Pol::template XStore<P, kRB>& xs, const TI* _
 // total decay and phase go to the workspace.
 template <class Pol, typename TI, int P, int N, int R>
 struct K1Smem {
-  Tables<Geo<P, N, R>::NT, N> tb;
+  Tables<Geo<P, N, R, 8>::NT, N, false> tb;
   union U {
     typename Pol::template Store<N, kRB> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
     float th_raw[kQ * (N / 2)];
@@ -482,8 +568,8 @@ struct K1Smem {
 };
 
 template <class Pol, typename TI, int P, int N, int R>
-__global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_state(PrefillArgs a) {
-  using G = Geo<P, N, R>;
+__global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillArgs a) {
+  using G = Geo<P, N, R, 8>;
   __shared__ K1Smem<Pol, TI, P, N, R> sm;
   constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
   constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
@@ -495,7 +581,18 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_state(PrefillArgs 
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
 
-  chunk_tables<TI, N, G::NT>(a, b, h, c0, Lc, sm.tb, sm.u.th_raw, 1);
+  // loads first (the load counter retires in order): phase inputs and token
+  // scalars, then the first u-block of B and x
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+  ThetaBlock<TI, N, G::NT> thb;
+  thb.load(a, b, h, c0, Lc);
+  RowBlock<TI, N * R, R, G::NT, true> bb;
+  RowBlock<TI, P * R, R, G::NT, true> xb;
+  bb.load(Bg, a, b, h, c0, Lc, 0);
+  xb.load(Xg, a, b, h, c0, Lc, 0);
+
+  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.th_raw, 1);
   const double cs_end = sm.tb.cs[Lc - 1];
   if (tid < kQ) {
     float w = 0.0f;
@@ -511,30 +608,35 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_state(PrefillArgs 
     reinterpret_cast<f2*>(a.rot_end)[chunk_id * G::NP + tid] = f2{cn, sn};
   }
   if (tid == 0) a.decay[chunk_id] = expf((float)cs_end);
+  __syncthreads();   // W_t visible
 
   f4 acc[QPW];
 #pragma unroll
   for (int q = 0; q < QPW; ++q) acc[q] = f4{0, 0, 0, 0};
 
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
-  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB >= rows) break;
-    __syncthreads();
-    stage_rows_T<Pol, TI, N, R, G::NT>(sm.u.bw, Bg, a, b, h, c0, Lc, ub * kRB, sm.tb.rot, sm.tb.aux);
-    stage_x_T<Pol, TI, P, R, G::NT>(sm.xs, Xg, a, b, h, c0, Lc, ub * kRB);
+    if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
+    store_rows_T<Pol, TI, N, R, G::NT>(bb, sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT>(xb, sm.xs);
+    if ((ub + 1) * kRB < rows) {   // next block's loads fly during this block's MFMAs
+      bb.load(Bg, a, b, h, c0, Lc, (ub + 1) * kRB);
+      xb.load(Xg, a, b, h, c0, Lc, (ub + 1) * kRB);
+    }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < kRB; kk += Pol::KS) {
+    for (int q = 0; q < QPW; ++q) {
+      const int qq = wave * QPW + q;
+      if (qq < NQ) {
+        const int pt = qq / G::NTL, nt = qq % G::NTL;
 #pragma unroll
-      for (int q = 0; q < QPW; ++q) {
-        const int qq = wave * QPW + q;
-        if (qq < NQ) {
-          const int pt = qq / G::NTL, nt = qq % G::NTL;
+        for (int kk = 0; kk < kRB; kk += Pol::KS)
           acc[q] = Pol::mma_x(Pol::frag(sm.u.bw, 16 * nt, kk, lane),
                               Pol::fragx_c(sm.xs, 16 * pt, kk, lane), acc[q]);
-        }
       }
+      // one output tile's operands at a time (hoisting them all costs
+      // registers and occupancy)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -575,36 +677,26 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_state(PrefillArgs 
 }
 
 // --------------------------------------------------------------------------
-// K2: serial pass over the chunks of one (batch, head), 16 state rows per
-// block.  Entering chunk c the state (plus that chunk's left-endpoint term)
-// is Shat_c; Shat_{c+1} = decay_c R(Phi_end,c) Shat_c + S_c, where S_c
-// already carries the next chunk's left-endpoint term.  Shat_c replaces S_c
-// in the workspace.  The loads of chunk c + D are issued while chunk c is
-// processed.
+// K2: serial pass over the chunks of one (batch, head).  Entering chunk c
+// the state (plus that chunk's left-endpoint term) is Shat_c;
+// Shat_{c+1} = decay_c R(Phi_end,c) Shat_c + S_c, where S_c already carries
+// the next chunk's left-endpoint term.  Shat_c replaces S_c in the
+// workspace.  Every element is independent, so each thread carries one
+// 16-byte vector of the state through all chunks (one wave per block, many
+// waves per (batch, head)); the loads of chunk c + 8 are issued while chunk
+// c is processed.
 template <typename TI, int N, int R>
-__global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
-  constexpr int VPR = N / 4;
-  constexpr int NV = 16 * VPR;
-  constexpr int VPT = (NV + 255) / 256;
-  constexpr int D = 4;
+__global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
+  constexpr int D = 8;
   const int P = a.P;
-  const int slices = P / 16;
-  const int bh = blockIdx.x / slices, sl = blockIdx.x % slices;
+  const int wpb = P * N / 4 / 64;          // blocks (waves) per (batch, head)
+  const int bh = blockIdx.x / wpb;
+  const int vi = (blockIdx.x % wpb) * 64 + threadIdx.x;
   const int b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x;
+  const int p = vi / (N / 4), n = 4 * (vi % (N / 4));
 
-  int pv[VPT], nv[VPT];
-  bool ok[VPT];
-  f4 S[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = tid + 256 * i;
-    ok[i] = v < NV;
-    pv[i] = 16 * sl + (ok[i] ? v / VPR : 0);
-    nv[i] = ok[i] ? 4 * (v % VPR) : 0;
-    S[i] = f4{0, 0, 0, 0};
-    if (ok[i] && a.h0) S[i] = *reinterpret_cast<const f4*>(a.h0 + ((int64_t)bh * P + pv[i]) * N + nv[i]);
-  }
+  f4 S = f4{0, 0, 0, 0};
+  if (a.h0) S = *reinterpret_cast<const f4*>(a.h0 + ((int64_t)bh * P + p) * N + n);
   if (a.has_prev) {  // left-endpoint term of token 0
     const int64_t t0 = token_index(a, b, 0, h);
     const float d = ld1(static_cast<const TI*>(a.dt), t0);
@@ -613,36 +705,28 @@ __global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
     const TI* xh = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
     const TI* Bh = static_cast<const TI*>(a.Bp) + (int64_t)bh * N * R;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      if (!ok[i]) continue;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float xv = bp0 * ld1(xh, (int64_t)pv[i] * R + r);
-        S[i].x += xv * ld1(Bh, (int64_t)(nv[i] + 0) * R + r);
-        S[i].y += xv * ld1(Bh, (int64_t)(nv[i] + 1) * R + r);
-        S[i].z += xv * ld1(Bh, (int64_t)(nv[i] + 2) * R + r);
-        S[i].w += xv * ld1(Bh, (int64_t)(nv[i] + 3) * R + r);
-      }
+    for (int r = 0; r < R; ++r) {
+      const float xv = bp0 * ld1(xh, (int64_t)p * R + r);
+      S.x += xv * ld1(Bh, (int64_t)(n + 0) * R + r);
+      S.y += xv * ld1(Bh, (int64_t)(n + 1) * R + r);
+      S.z += xv * ld1(Bh, (int64_t)(n + 2) * R + r);
+      S.w += xv * ld1(Bh, (int64_t)(n + 3) * R + r);
     }
   }
   const int64_t cbase = (int64_t)bh * a.nchunk;
   const int nch = a.nchunk;
-  f4 bs[D][VPT];
-  f2 br0[D][VPT], br1[D][VPT];
+  const int64_t off = (int64_t)p * N + n;
+  f4 bs[D];
+  f2 br0[D], br1[D];
   float bd[D];
   auto load = [&](int c, int q) {
     if (c < nch) {
       const int64_t cid = cbase + c;
-      const float* Sc = a.S + cid * P * N;
       const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
       bd[q] = a.decay[cid];
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        if (!ok[i]) continue;
-        bs[q][i] = *reinterpret_cast<const f4*>(Sc + (int64_t)pv[i] * N + nv[i]);
-        br0[q][i] = re[nv[i] / 2];
-        br1[q][i] = re[nv[i] / 2 + 1];
-      }
+      bs[q] = *reinterpret_cast<const f4*>(a.S + cid * P * N + off);
+      br0[q] = re[n / 2];
+      br1[q] = re[n / 2 + 1];
     }
   };
 #pragma unroll
@@ -652,29 +736,20 @@ __global__ __launch_bounds__(256) void k_state_pass(PrefillArgs a) {
     for (int q = 0; q < D; ++q) {
       const int c = c0 + q;
       if (c < nch) {
-        float* Sc = a.S + (cbase + c) * P * N;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-          if (!ok[i]) continue;
-          *reinterpret_cast<f4*>(Sc + (int64_t)pv[i] * N + nv[i]) = S[i];   // Shat_c
-          S[i] = bd[q] * rot2pairs(S[i], br0[q][i], br1[q][i]) + bs[q][i];
-        }
+        *reinterpret_cast<f4*>(a.S + (cbase + c) * P * N + off) = S;   // Shat_c
+        S = bd[q] * rot2pairs(S, br0[q], br1[q]) + bs[q];
         load(c + D, q);
       }
     }
   }
-  if (a.hT) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (ok[i]) *reinterpret_cast<f4*>(a.hT + ((int64_t)bh * P + pv[i]) * N + nv[i]) = S[i];
-  }
+  if (a.hT) *reinterpret_cast<f4*>(a.hT + ((int64_t)bh * P + p) * N + n) = S;
 }
 
 // --------------------------------------------------------------------------
 // K3: all outputs of one chunk
 template <class Pol, typename TI, int P, int N, int R>
 struct K3Smem {
-  Tables<Geo<P, N, R>::NT, N> tb;
+  Tables<Geo<P, N, R>::NT, N, true> tb;
   union U {
     typename Pol::template Store<kRB, N> st;   // rotated C or B rows   [v][n]
     typename Pol::template Store<P, N> sh;     // Shat                  [p][n]
@@ -697,16 +772,25 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
 
-  chunk_tables<TI, N, G::NT>(a, b, h, c0, Lc, sm.tb, sm.u.th_raw, 0);
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+
+  // loads first (the load counter retires in order): phase inputs and token
+  // scalars, the first C block, the entry state
+  ThetaBlock<TI, N, G::NT> thb;
+  thb.load(a, b, h, c0, Lc);
+  RowBlock<TI, N * R, R, G::NT, false> cb;
+  cb.load(Cg, a, b, h, c0, Lc, 0);
+  StateBlock<P, N, G::NT> sb;
+  sb.load(a.S + chunk_id * P * N);
+
+  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.th_raw, 0);
   if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
 
   int tile[G::TPW];
   tile[0] = wave;
   if constexpr (G::TPW == 2) tile[1] = 2 * G::NW - 1 - wave;
-
-  const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
-  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
 
   // own rotated C rows -> MFMA fragments in registers
   typename Pol::Frag cf[G::TPW][NKS];
@@ -716,8 +800,9 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
     for (int s = 0; s < NKS; ++s) cf[j][s] = typename Pol::Frag{};
   for (int blk = 0; blk < G::NUB; ++blk) {
     if (blk * kRB >= rows) break;
-    __syncthreads();
-    stage_rows<Pol, TI, N, R, G::NT>(sm.u.st, Cg, a, b, h, c0, Lc, blk * kRB, sm.tb.rot);
+    if (blk > 0) __syncthreads();
+    store_rows<Pol, TI, N, R, G::NT>(cb, sm.u.st, sm.tb, blk * kRB / R, Lc);
+    if ((blk + 1) * kRB < rows) cb.load(Cg, a, b, h, c0, Lc, (blk + 1) * kRB);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < G::TPW; ++j)
@@ -727,24 +812,13 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
       }
   }
 
-  // Y_off = e^{cs_t} Ct Shat^T
+  // Y_off = e^{cs_t} Ct Shat^T; the first u-block of B and x is loaded meanwhile
+  RowBlock<TI, N * R, R, G::NT, false> bb;
+  RowBlock<TI, P * R, R, G::NT, true> xb;
   __syncthreads();
-  {
-    const float* __restrict__ Sh = a.S + chunk_id * P * N;
-    constexpr int NV = P * N / 8;
-    constexpr int IT = (NV + G::NT - 1) / G::NT;
-    float v[IT][8];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int vi = tid + G::NT * i;
-      if (vi < NV) ld8(Sh, (int64_t)vi * 8, v[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int vi = tid + G::NT * i;
-      if (vi < NV) Pol::put8(sm.u.sh, (vi * 8) / N, (vi * 8) % N, v[i]);
-    }
-  }
+  sb.template store<Pol>(sm.u.sh);
+  bb.load(Bg, a, b, h, c0, Lc, 0);
+  xb.load(Xg, a, b, h, c0, Lc, 0);
   __syncthreads();
   f4 acc[G::TPW][G::PT];
 #pragma unroll
@@ -768,8 +842,12 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB >= rows) break;
     __syncthreads();
-    stage_rows<Pol, TI, N, R, G::NT>(sm.u.st, Bg, a, b, h, c0, Lc, ub * kRB, sm.tb.rot);
-    stage_x_T<Pol, TI, P, R, G::NT>(sm.xs, Xg, a, b, h, c0, Lc, ub * kRB);
+    store_rows<Pol, TI, N, R, G::NT>(bb, sm.u.st, sm.tb, ub * kRB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT>(xb, sm.xs);
+    if ((ub + 1) * kRB < rows) {
+      bb.load(Bg, a, b, h, c0, Lc, (ub + 1) * kRB);
+      xb.load(Xg, a, b, h, c0, Lc, (ub + 1) * kRB);
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < G::TPW; ++j) {
@@ -789,15 +867,21 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
 #pragma unroll
           for (int s = 0; s < NKS; ++s)
             gt = Pol::mma(Pol::frag(sm.u.st, ug + 16 * dt, s * Pol::KS, lane), cf[j][s], gt);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int tu = (ubase + 16 * dt + 4 * g + jj) / R;
+          // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
+          // each D row; with R a multiple of 4 a lane's 4 rows share one token
+          auto mask = [&](int tu) {
             float m = 0.0f;
             if (row_ok && tu <= tt) {
               const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
               m = __expf((float)(cst - sm.tb.cs[tu])) * w;
             }
-            gt[jj] *= m;
+            return m;
+          };
+          if constexpr (R % 4 == 0) {
+            gt *= mask((ubase + 16 * dt + 4 * g) / R);
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) gt[jj] *= mask((ubase + 16 * dt + 4 * g + jj) / R);
           }
           d[dt] = gt;
         }
@@ -830,10 +914,12 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
 template <class Pol, typename TI, typename TO, int P, int N, int R>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   using G = Geo<P, N, R>;
-  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G::NT), 0, s, a);
+  using G1 = Geo<P, N, R, 8>;
+  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G1::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_state_pass<TI, N, R>), dim3(a.Bsz * a.H * (P / 16)), dim3(256), 0, s, a);
+  static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
+  hipLaunchKernelGGL((k_state_pass<TI, N, R>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G::NT),
