@@ -78,6 +78,26 @@ struct PolF32 {
     *reinterpret_cast<f4*>(&s.v[r][k0]) = f4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f4*>(&s.v[r][k0 + 4]) = f4{v[4], v[5], v[6], v[7]};
   }
+  // M (1, 2 or 4) consecutive k of one row, k0 a multiple of M, one write
+  template <int M, class St>
+  static __device__ __forceinline__ void putm(St& s, int r, int k0, const float* v) {
+    if constexpr (M == 4) {
+      *reinterpret_cast<f4*>(&s.v[r][k0]) = f4{v[0], v[1], v[2], v[3]};
+    } else if constexpr (M == 2) {
+      *reinterpret_cast<f2*>(&s.v[r][k0]) = f2{v[0], v[1]};
+    } else {
+      static_assert(M == 1, "putm");
+      s.v[r][k0] = v[0];
+    }
+  }
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putn(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    putm<M>(s, r, k0, v);
+  }
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putxn(XStore<ROWS, K>& s, int r, int k0, const float* v) {
+    putm<M>(s, r, k0, v);
+  }
   template <int ROWS, int K>
   static __device__ __forceinline__ Frag frag(const Store<ROWS, K>& s, int row0, int k0, int lane) {
     return Frag{*reinterpret_cast<const f4*>(&s.v[row0 + (lane & 15)][k0 + 4 * (lane >> 4)])};
@@ -114,15 +134,29 @@ struct PolF16 {
     h8 hi, lo;
   };
   typedef h8 XFrag;
+  // Rows are padded by 4 halves: a row is then 2 (mod 32) dwords long, so
+  // the 16 rows that one 8-byte LDS access phase touches fall on distinct
+  // banks.  Rows are only 8-byte aligned, so every access below is made of
+  // 8-byte pieces.
+  static constexpr int PAD = 4;
   template <int ROWS, int K>
   struct Store {
-    _Float16 hi[ROWS][K + 8];
-    _Float16 lo[ROWS][K + 8];
+    _Float16 hi[ROWS][K + PAD];
+    _Float16 lo[ROWS][K + PAD];
   };
   template <int ROWS, int K>
   struct XStore {
-    _Float16 v[ROWS][K + 8];
+    _Float16 v[ROWS][K + PAD];
   };
+  static __device__ __forceinline__ h8 ld8h(const _Float16* p) {
+    const h4 a = *reinterpret_cast<const h4*>(p);
+    const h4 b = *reinterpret_cast<const h4*>(p + 4);
+    return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  static __device__ __forceinline__ void st8h(_Float16* p, h8 v) {
+    *reinterpret_cast<h4*>(p) = h4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<h4*>(p + 4) = h4{v[4], v[5], v[6], v[7]};
+  }
   // x = hi + lo to about 2^-22 relative: hi = fp16(x) (round to nearest
   // even), lo = fp16(x - hi) with the difference formed exactly inside
   // v_fma_mix (x * 1 - hi, one rounding).  Written as asm on purpose: x is
@@ -167,13 +201,45 @@ struct PolF16 {
   static __device__ __forceinline__ void put8(Store<ROWS, K>& s, int r, int k0, const float* v) {
     h8 hi, lo;
     split8(v, hi, lo);
-    *reinterpret_cast<h8*>(&s.hi[r][k0]) = hi;
-    *reinterpret_cast<h8*>(&s.lo[r][k0]) = lo;
+    st8h(&s.hi[r][k0], hi);
+    st8h(&s.lo[r][k0], lo);
+  }
+  // M (1, 2 or 4) consecutive k of one row, k0 a multiple of M: one write
+  // per part
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putn(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    if constexpr (M == 4) {
+      uint32_t h0, l0, h1, l1;
+      split2(v[0], v[1], h0, l0);
+      split2(v[2], v[3], h1, l1);
+      *reinterpret_cast<uint2*>(&s.hi[r][k0]) = uint2{h0, h1};
+      *reinterpret_cast<uint2*>(&s.lo[r][k0]) = uint2{l0, l1};
+    } else if constexpr (M == 2) {
+      uint32_t h0, l0;
+      split2(v[0], v[1], h0, l0);
+      *reinterpret_cast<uint32_t*>(&s.hi[r][k0]) = h0;
+      *reinterpret_cast<uint32_t*>(&s.lo[r][k0]) = l0;
+    } else {
+      static_assert(M == 1, "putn");
+      put(s, r, k0, v[0]);
+    }
+  }
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putxn(XStore<ROWS, K>& s, int r, int k0, const float* v) {
+    if constexpr (M == 4) {
+      *reinterpret_cast<h4*>(&s.v[r][k0]) = h4{static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]),
+                                              static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
+    } else if constexpr (M == 2) {
+      *reinterpret_cast<h2*>(&s.v[r][k0]) = h2{static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1])};
+    } else {
+      static_assert(M == 1, "putxn");
+      s.v[r][k0] = static_cast<_Float16>(v[0]);
+    }
   }
   template <int ROWS, int K>
   static __device__ __forceinline__ Frag frag(const Store<ROWS, K>& s, int row0, int k0, int lane) {
     const int r = row0 + (lane & 15), k = k0 + 8 * (lane >> 4);
-    return Frag{*reinterpret_cast<const h8*>(&s.hi[r][k]), *reinterpret_cast<const h8*>(&s.lo[r][k])};
+    return Frag{ld8h(&s.hi[r][k]), ld8h(&s.lo[r][k])};
   }
   static __device__ __forceinline__ Frag make(const float* v) {
     Frag f;
@@ -190,7 +256,7 @@ struct PolF16 {
   }
   template <int ROWS, int K>
   static __device__ __forceinline__ XFrag fragx_c(const XStore<ROWS, K>& s, int col0, int k0, int lane) {
-    return *reinterpret_cast<const h8*>(&s.v[col0 + (lane & 15)][k0 + 8 * (lane >> 4)]);
+    return ld8h(&s.v[col0 + (lane & 15)][k0 + 8 * (lane >> 4)]);
   }
   static __device__ __forceinline__ Frag frag_from_d(const f4* d) {
     const float v[8] = {d[0].x, d[0].y, d[0].z, d[0].w, d[1].x, d[1].y, d[1].z, d[1].w};
@@ -229,36 +295,61 @@ struct Geo {
   static_assert(TPW >= 1 && TILES % NW == 0, "tile split");
 };
 
+// (cos, sin) of an angle already reduced to [-pi, pi], from the hardware
+// sine/cosine (argument in turns).  Measured on gfx950 over 4M angles in
+// [-pi, pi]: max abs error 2.7e-7 (sincosf: 7e-8), far inside every
+// tolerance here, at two instructions instead of ~30.
+__device__ __forceinline__ f2 cos_sin_reduced(float ang) {
+  const float turns = ang * 0.15915494309189535f;
+  return f2{__builtin_amdgcn_cosf(turns), __builtin_amdgcn_sinf(turns)};
+}
+
 // per-chunk tables in LDS.  ROT: keep (cos, sin) of each angle (computed
 // once); otherwise keep the reduced angle and take its sine and cosine where
 // a row is staged (half the LDS; each angle is then used once).
-template <int NT, int N, bool ROT>
+//
+// The angle table is token-major [t][k] for kernels whose lanes run along
+// the pairs of one token, or pair-major [k][t] (rows padded by one entry, so
+// both a column and a row of the table fall on distinct banks) for kernels
+// whose lanes run along the tokens.
+template <int N, bool ROT, bool KMAJ = false>
 struct Tables {
+  static constexpr int NP = N / 2;
+  static constexpr int TS = KMAJ ? kQ + 1 : NP;   // row stride
   double cs[kQ];      // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
   float dt[kQ];
   float gam[kQ];      // lam dt
   float bpr[kQ];      // (1 - lam) dt
   float aux[kQ];      // e^{cs_t} (outputs) or the chunk-state weights W_t
-  double seg[NT];
-  double phi_end[N / 2];
-  typename std::conditional<ROT, f2, float>::type tab[kQ][N / 2];
+  double phi_end[NP];
+  alignas(16) typename std::conditional<ROT, f2, float>::type tab[(KMAJ ? NP : kQ) * TS];
+  static __device__ __forceinline__ int at(int t, int k) { return KMAJ ? k * TS + t : t * TS + k; }
   // Phi_t (mode 0) or Phi_end - Phi_t (mode 1), reduced to [-pi, pi]
   __device__ __forceinline__ void set(int t, int k, float ang) {
     if constexpr (ROT) {
-      float sn, cn;
-      sincosf(ang, &sn, &cn);
-      tab[t][k] = f2{cn, sn};
+      tab[at(t, k)] = cos_sin_reduced(ang);
     } else {
-      tab[t][k] = ang;
+      tab[at(t, k)] = ang;
     }
   }
   __device__ __forceinline__ f2 cs_of(int t, int k) const {
     if constexpr (ROT) {
-      return tab[t][k];
+      return tab[at(t, k)];
     } else {
-      float sn, cn;
-      sincosf(tab[t][k], &sn, &cn);
-      return f2{cn, sn};
+      return cos_sin_reduced(tab[at(t, k)]);
+    }
+  }
+  // (cos, sin) of pairs k0 .. k0 + M - 1 of token t (identity when !ok); a
+  // token-major angle table serves four pairs with one 16-byte read
+  template <int M>
+  __device__ __forceinline__ void cs_run(int t, int k0, bool ok, f2* out) const {
+    if constexpr (M == 4 && !ROT && !KMAJ) {
+      const f4 ang = ok ? *reinterpret_cast<const f4*>(&tab[t * TS + k0]) : f4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) out[m] = cos_sin_reduced(ang[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) out[m] = ok ? cs_of(t, k0 + m) : f2{1.0f, 0.0f};
     }
   }
 };
@@ -373,11 +464,18 @@ struct ThetaBlock {
 // log-decay prefix (double, one wave shuffle scan) and phase prefix of
 // every pair (double; each thread owns one pair and a segment of tokens),
 // then the angles reduced to [-pi, pi]: Phi_t (mode 0) or Phi_end - Phi_t
-// (mode 1), kept as (cos, sin) or as the angle (see Tables).  th_raw is LDS
-// scratch for Q x N/2 floats.
-template <typename TI, int N, int NT, bool ROT>
+// (mode 1), kept as (cos, sin) or as the angle (see Tables).  scr is LDS
+// scratch that is free until the tables are built.
+template <int N, int NT>
+struct TableScratch {
+  float th_raw[kQ * (N / 2)];
+  double seg[NT];
+};
+
+template <typename TI, int N, int NT, bool ROT, bool KMAJ>
 __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& tb_in, int Lc,
-                             Tables<NT, N, ROT>& tb, float* th_raw, int mode) {
+                             Tables<N, ROT, KMAJ>& tb, TableScratch<N, NT>& scr, int mode) {
+  float* th_raw = scr.th_raw;
   constexpr int NP = N / 2;
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -419,10 +517,10 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
     run += angle ? tv : tv * (double)tb.dt[t];
     loc[i] = run;
   }
-  tb.seg[sg * NP + k] = run;
+  scr.seg[sg * NP + k] = run;
   __syncthreads();
   double base = 0.0;
-  for (int s = 0; s < sg; ++s) base += tb.seg[s * NP + k];
+  for (int s = 0; s < sg; ++s) base += scr.seg[s * NP + k];
   if (sg == NSEG - 1) tb.phi_end[k] = base + run;
   __syncthreads();
   const double pe = tb.phi_end[k];
@@ -454,10 +552,11 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
     const bool ok = t < Lc;
     float v[8], o[8];
     rb.raw[i].get(v);
+    f2 csr[NPAIR];
+    tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
 #pragma unroll
     for (int pi = 0; pi < NPAIR; ++pi) {
-      const int n = e0 / R + 2 * pi;
-      const f2 cs = ok ? tb.cs_of(t, n / 2) : f2{1.0f, 0.0f};
+      const f2 cs = csr[pi];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
@@ -468,8 +567,16 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
     if constexpr (R == 1) {
       Pol::put8(st, tl, e0, o);
     } else {
+      // element j is (column e0/R + j/R, rank j%R): row (tl, r) receives
+      // 8/R consecutive columns
+      constexpr int M = 8 / R;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Pol::put(st, tl * R + j % R, e0 / R + j / R, o[j]);
+      for (int r = 0; r < R; ++r) {
+        float w[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) w[m] = o[m * R + r];
+        Pol::template putn<M>(st, tl * R + r, e0 / R, w);
+      }
     }
   }
 }
@@ -493,16 +600,22 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, tr
     const float wt = ok ? w[t] : 0.0f;
     float v[8];
     rb.raw[i].get(v);
+    f2 csr[NPAIR];
+    tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
 #pragma unroll
     for (int pi = 0; pi < NPAIR; ++pi) {
       const int n = e0 / R + 2 * pi;
-      const f2 cs = ok ? tb.cs_of(t, n / 2) : f2{1.0f, 0.0f};
+      const f2 cs = csr[pi];
+      float w0[R], w1[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
-        Pol::put(st, n, tl * R + r, wt * (cs.x * u0 - cs.y * u1));   // rotate by +angle
-        Pol::put(st, n + 1, tl * R + r, wt * (cs.y * u0 + cs.x * u1));
+        w0[r] = wt * (cs.x * u0 - cs.y * u1);   // rotate by +angle
+        w1[r] = wt * (cs.y * u0 + cs.x * u1);
       }
+      // the R virtual rows of token tl are consecutive columns of st
+      Pol::template putn<R>(st, n, tl * R, w0);
+      Pol::template putn<R>(st, n + 1, tl * R, w1);
     }
   }
 }
@@ -520,8 +633,15 @@ __device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, true>
     RBk::where(vi, tl, e0);
     float v[8];
     rb.raw[i].get(v);
+    if constexpr (R == 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Pol::putx(xs, (e0 + j) / R, tl * R + (e0 + j) % R, v[j]);
+      for (int j = 0; j < 8; ++j) Pol::putx(xs, e0 + j, tl, v[j]);
+    } else {
+      // element j is (p = e0/R + j/R, rank j%R): the R ranks of one p are
+      // consecutive columns
+#pragma unroll
+      for (int m = 0; m < 8 / R; ++m) Pol::template putxn<R>(xs, e0 / R + m, tl * R, v + m * R);
+    }
   }
 }
 
@@ -559,10 +679,10 @@ struct StateBlock {
 // total decay and phase go to the workspace.
 template <class Pol, typename TI, int P, int N, int R>
 struct K1Smem {
-  Tables<Geo<P, N, R, 8>::NT, N, false> tb;
+  Tables<N, false, true> tb;
   union U {
     typename Pol::template Store<N, kRB> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
-    float th_raw[kQ * (N / 2)];
+    TableScratch<N, Geo<P, N, R, 8>::NT> scr;
   } u;
   typename Pol::template XStore<P, kRB> xs;    // x^T  [p][v]
 };
@@ -592,7 +712,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   bb.load(Bg, a, b, h, c0, Lc, 0);
   xb.load(Xg, a, b, h, c0, Lc, 0);
 
-  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.th_raw, 1);
+  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 1);
   const double cs_end = sm.tb.cs[Lc - 1];
   if (tid < kQ) {
     float w = 0.0f;
@@ -602,11 +722,8 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     }
     sm.tb.aux[tid] = w;
   }
-  if (tid < G::NP) {
-    float sn, cn;
-    sincosf(reduce_angle(sm.tb.phi_end[tid]), &sn, &cn);
-    reinterpret_cast<f2*>(a.rot_end)[chunk_id * G::NP + tid] = f2{cn, sn};
-  }
+  if (tid < G::NP)
+    reinterpret_cast<f2*>(a.rot_end)[chunk_id * G::NP + tid] = cos_sin_reduced(reduce_angle(sm.tb.phi_end[tid]));
   if (tid == 0) a.decay[chunk_id] = expf((float)cs_end);
   __syncthreads();   // W_t visible
 
@@ -746,165 +863,210 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// K3: all outputs of one chunk
+// K3: the outputs of one chunk.  One wave per 16-row output tile; a rank-4
+// chunk (16 tiles) is split over two blocks of 8 waves (virtual rows 0..127
+// and 128..255), so that two blocks fit on a CU and one block's loads and
+// table work overlap the other's MFMA work.
+template <int P, int N, int R>
+struct Geo3 {
+  static constexpr int ROWS = kQ * R;            // virtual rows per chunk
+  static constexpr int TILES = ROWS / 16;
+  static constexpr int SPLIT = TILES > 8 ? TILES / 8 : 1;
+  static constexpr int NW = TILES / SPLIT;       // waves (= tiles) per block
+  static constexpr int NT = NW * 64;
+  static constexpr int BROWS = ROWS / SPLIT;     // virtual rows per block
+  static constexpr int NCB = BROWS / kRB;        // C row blocks per block
+  static constexpr int NUB = ROWS / kRB;         // u-blocks of a whole chunk
+  static constexpr int PT = P / 16;
+  static_assert(BROWS % kRB == 0 && (SPLIT == 1 || SPLIT == 2) && (NW == 4 || NW == 8),
+                "output block geometry");
+};
+
 template <class Pol, typename TI, int P, int N, int R>
 struct K3Smem {
-  Tables<Geo<P, N, R>::NT, N, true> tb;
+  Tables<N, false> tb;
   union U {
     typename Pol::template Store<kRB, N> st;   // rotated C or B rows   [v][n]
     typename Pol::template Store<P, N> sh;     // Shat                  [p][n]
-    float th_raw[kQ * (N / 2)];
+    TableScratch<N, Geo3<P, N, R>::NT> scr;
   } u;
   typename Pol::template XStore<P, kRB> xs;    // x^T block             [p][v]
 };
 
+// four consecutive outputs (one token's four ranks) in one store
+__device__ __forceinline__ void st4_out(float* __restrict__ p, int64_t i, f4 v) {
+  *reinterpret_cast<f4*>(p + i) = v;
+}
+__device__ __forceinline__ void st4_out(bf16_t* __restrict__ p, int64_t i, f4 v) {
+  const uint32_t lo = to_bf16(v.x).bits | (static_cast<uint32_t>(to_bf16(v.y).bits) << 16);
+  const uint32_t hi = to_bf16(v.z).bits | (static_cast<uint32_t>(to_bf16(v.w).bits) << 16);
+  *reinterpret_cast<uint2*>(p + i) = uint2{lo, hi};
+}
+
 template <class Pol, typename TI, typename TO, int P, int N, int R>
-__global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs a) {
-  using G = Geo<P, N, R>;
+__global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArgs a) {
+  using G = Geo3<P, N, R>;
   __shared__ K3Smem<Pol, TI, P, N, R> sm;
   constexpr int NKS = N / Pol::KS;
   constexpr int UG = 16 * Pol::DT;          // u rows per A fragment built from D tiles
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the two blocks of a split chunk are 8 apart in launch order: same XCD
+  // (blocks go round-robin over the 8 XCDs), so the second one finds the
+  // chunk's state, B and x in that XCD's L2
+  int c, half;
+  if constexpr (G::SPLIT == 2) {
+    c = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    half = (blockIdx.x >> 3) & 1;
+  } else {
+    c = blockIdx.x;
+    half = 0;
+  }
+  if (c >= a.nchunk) return;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int c0 = c * kQ;
   const int Lc = min(kQ, a.T - c0);
   const int rows = Lc * R;
+  const int v0 = half * G::BROWS;           // this block's rows: [v0, vend)
+  if (v0 >= rows) return;
+  const int vend = min(rows, v0 + G::BROWS);
+  const int nub = (vend + kRB - 1) / kRB;   // u-blocks that reach these rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
+  // this wave's tile; with 8 waves, waves w and w + 4 share a SIMD and take
+  // tiles w and 7 - w, which evens out the causal work per SIMD
+  const int lt = (G::NW == 8) ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int tile = v0 / 16 + lt;
 
   const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
 
-  // loads first (the load counter retires in order): phase inputs and token
-  // scalars, the first C block, the entry state
+  // all loads go out first (the load counter retires in order): phase
+  // inputs and token scalars, this block's C rows, the entry state, and the
+  // first two u-blocks of B and x
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
-  RowBlock<TI, N * R, R, G::NT, false> cb;
-  cb.load(Cg, a, b, h, c0, Lc, 0);
+  RowBlock<TI, N * R, R, G::NT, false> cb[G::NCB];
+#pragma unroll
+  for (int k = 0; k < G::NCB; ++k)
+    if (v0 + k * kRB < rows) cb[k].load(Cg, a, b, h, c0, Lc, v0 + k * kRB);
   StateBlock<P, N, G::NT> sb;
   sb.load(a.S + chunk_id * P * N);
-
-  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.th_raw, 0);
-  if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
-
-  int tile[G::TPW];
-  tile[0] = wave;
-  if constexpr (G::TPW == 2) tile[1] = 2 * G::NW - 1 - wave;
-
-  // own rotated C rows -> MFMA fragments in registers
-  typename Pol::Frag cf[G::TPW][NKS];
+  RowBlock<TI, N * R, R, G::NT, false> bb[2];
+  RowBlock<TI, P * R, R, G::NT, true> xb[2];
 #pragma unroll
-  for (int j = 0; j < G::TPW; ++j)
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) cf[j][s] = typename Pol::Frag{};
-  for (int blk = 0; blk < G::NUB; ++blk) {
-    if (blk * kRB >= rows) break;
-    if (blk > 0) __syncthreads();
-    store_rows<Pol, TI, N, R, G::NT>(cb, sm.u.st, sm.tb, blk * kRB / R, Lc);
-    if ((blk + 1) * kRB < rows) cb.load(Cg, a, b, h, c0, Lc, (blk + 1) * kRB);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < G::TPW; ++j)
-      if (tile[j] / 4 == blk) {
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) cf[j][s] = Pol::frag(sm.u.st, 16 * (tile[j] % 4), s * Pol::KS, lane);
-      }
+  for (int q = 0; q < 2; ++q) {
+    if (q < nub) {
+      bb[q].load(Bg, a, b, h, c0, Lc, q * kRB);
+      xb[q].load(Xg, a, b, h, c0, Lc, q * kRB);
+    }
   }
 
-  // Y_off = e^{cs_t} Ct Shat^T; the first u-block of B and x is loaded meanwhile
-  RowBlock<TI, N * R, R, G::NT, false> bb;
-  RowBlock<TI, P * R, R, G::NT, true> xb;
+  chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
+  if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
+
+  // own rotated C rows -> MFMA fragments in registers
+  typename Pol::Frag cf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) cf[s] = typename Pol::Frag{};
+#pragma unroll
+  for (int k = 0; k < G::NCB; ++k) {
+    if (v0 + k * kRB < rows) {
+      if (k > 0) __syncthreads();
+      store_rows<Pol, TI, N, R, G::NT>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc);
+      __syncthreads();
+      if (lt / 4 == k) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) cf[s] = Pol::frag(sm.u.st, 16 * (lt % 4), s * Pol::KS, lane);
+      }
+    }
+  }
+
+  // Y_off = e^{cs_t} Ct Shat^T
   __syncthreads();
   sb.template store<Pol>(sm.u.sh);
-  bb.load(Bg, a, b, h, c0, Lc, 0);
-  xb.load(Xg, a, b, h, c0, Lc, 0);
   __syncthreads();
-  f4 acc[G::TPW][G::PT];
+  f4 acc[G::PT];
 #pragma unroll
-  for (int j = 0; j < G::TPW; ++j) {
+  for (int ct = 0; ct < G::PT; ++ct) {
+    f4 d = f4{0, 0, 0, 0};
 #pragma unroll
-    for (int ct = 0; ct < G::PT; ++ct) {
-      f4 d = f4{0, 0, 0, 0};
+    for (int s = 0; s < NKS; ++s) d = Pol::mma(cf[s], Pol::frag(sm.u.sh, 16 * ct, s * Pol::KS, lane), d);
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) d = Pol::mma(cf[j][s], Pol::frag(sm.u.sh, 16 * ct, s * Pol::KS, lane), d);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int vv = 16 * tile[j] + 4 * g + jj;
-        d[jj] *= vv < rows ? sm.tb.aux[vv / R] : 0.0f;
-      }
-      acc[j][ct] = d;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int vv = 16 * tile + 4 * g + jj;
+      d[jj] *= vv < rows ? sm.tb.aux[vv / R] : 0.0f;
     }
+    acc[ct] = d;
   }
 
   // Y_diag: Gram tiles Bt Ct^T (D rows = u, columns = own rows), decay mask,
   // then the masked tile is the A operand of the product with x
+  const int vrow = 16 * tile + l16;
+  const int tt = vrow / R;
+  const bool row_ok = vrow < rows;
+  const int tmax = min(Lc - 1, (16 * tile + 15) / R);
+#pragma unroll
   for (int ub = 0; ub < G::NUB; ++ub) {
-    if (ub * kRB >= rows) break;
+    if (ub >= nub) break;
     __syncthreads();
-    store_rows<Pol, TI, N, R, G::NT>(bb, sm.u.st, sm.tb, ub * kRB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT>(xb, sm.xs);
-    if ((ub + 1) * kRB < rows) {
-      bb.load(Bg, a, b, h, c0, Lc, (ub + 1) * kRB);
-      xb.load(Xg, a, b, h, c0, Lc, (ub + 1) * kRB);
+    store_rows<Pol, TI, N, R, G::NT>(bb[ub % 2], sm.u.st, sm.tb, ub * kRB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT>(xb[ub % 2], sm.xs);
+    if (ub + 2 < nub) {   // two stages ahead
+      bb[ub % 2].load(Bg, a, b, h, c0, Lc, (ub + 2) * kRB);
+      xb[ub % 2].load(Xg, a, b, h, c0, Lc, (ub + 2) * kRB);
     }
     __syncthreads();
+    const double cst = sm.tb.cs[min(tt, kQ - 1)];
+    for (int ug = 0; ug < kRB; ug += UG) {
+      const int ubase = ub * kRB + ug;
+      if (ubase / R > tmax) break;
+      f4 d[Pol::DT];
 #pragma unroll
-    for (int j = 0; j < G::TPW; ++j) {
-      const int i = tile[j];
-      const int vrow = 16 * i + l16;
-      const int tt = vrow / R;
-      const bool row_ok = vrow < rows;
-      const int tmax = min(Lc - 1, (16 * i + 15) / R);
-      const double cst = sm.tb.cs[min(tt, kQ - 1)];
-      for (int ug = 0; ug < kRB; ug += UG) {
-        const int ubase = ub * kRB + ug;
-        if (ubase / R > tmax) break;
-        f4 d[Pol::DT];
+      for (int dt = 0; dt < Pol::DT; ++dt) {
+        f4 gt = f4{0, 0, 0, 0};
 #pragma unroll
-        for (int dt = 0; dt < Pol::DT; ++dt) {
-          f4 gt = f4{0, 0, 0, 0};
-#pragma unroll
-          for (int s = 0; s < NKS; ++s)
-            gt = Pol::mma(Pol::frag(sm.u.st, ug + 16 * dt, s * Pol::KS, lane), cf[j][s], gt);
-          // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
-          // each D row; with R a multiple of 4 a lane's 4 rows share one token
-          auto mask = [&](int tu) {
-            float m = 0.0f;
-            if (row_ok && tu <= tt) {
-              const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
-              m = __expf((float)(cst - sm.tb.cs[tu])) * w;
-            }
-            return m;
-          };
-          if constexpr (R % 4 == 0) {
-            gt *= mask((ubase + 16 * dt + 4 * g) / R);
-          } else {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) gt[jj] *= mask((ubase + 16 * dt + 4 * g + jj) / R);
+        for (int s = 0; s < NKS; ++s)
+          gt = Pol::mma(Pol::frag(sm.u.st, ug + 16 * dt, s * Pol::KS, lane), cf[s], gt);
+        // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
+        // each D row; with R a multiple of 4 a lane's 4 rows share one token
+        auto mask = [&](int tu) {
+          float m = 0.0f;
+          if (row_ok && tu <= tt) {
+            const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
+            m = __expf((float)(cst - sm.tb.cs[tu])) * w;
           }
-          d[dt] = gt;
-        }
-        const typename Pol::Frag af = Pol::frag_from_d(d);
+          return m;
+        };
+        if constexpr (R % 4 == 0) {
+          gt *= mask((ubase + 16 * dt + 4 * g) / R);
+        } else {
 #pragma unroll
-        for (int ct = 0; ct < G::PT; ++ct)
-          acc[j][ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs, 16 * ct, ug, lane), acc[j][ct]);
+          for (int jj = 0; jj < 4; ++jj) gt[jj] *= mask((ubase + 16 * dt + 4 * g + jj) / R);
+        }
+        d[dt] = gt;
       }
+      const typename Pol::Frag af = Pol::frag_from_d(d);
+#pragma unroll
+      for (int ct = 0; ct < G::PT; ++ct)
+        acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs, 16 * ct, ug, lane), acc[ct]);
     }
   }
 
   // y[b, c0 + t, h, p, r] for D rows v = 16 tile + 4g + jj, column p
   TO* __restrict__ Y = static_cast<TO*>(a.y);
 #pragma unroll
-  for (int j = 0; j < G::TPW; ++j) {
-#pragma unroll
-    for (int ct = 0; ct < G::PT; ++ct) {
-      const int p = 16 * ct + l16;
+  for (int ct = 0; ct < G::PT; ++ct) {
+    const int p = 16 * ct + l16;
+    if constexpr (R % 4 == 0) {
+      // the four rows are ranks v%R .. v%R + 3 of one token
+      const int v = 16 * tile + 4 * g;
+      if (v < rows) st4_out(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[ct]);
+    } else {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int v = 16 * tile[j] + 4 * g + jj;
-        if (v < rows)
-          st1(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[j][ct][jj]);
+        const int v = 16 * tile + 4 * g + jj;
+        if (v < rows) st1(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[ct][jj]);
       }
     }
   }
@@ -913,7 +1075,6 @@ __global__ __launch_bounds__((Geo<P, N, R>::NT)) void k_chunk_output(PrefillArgs
 // --------------------------------------------------------------------------
 template <class Pol, typename TI, typename TO, int P, int N, int R>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
-  using G = Geo<P, N, R>;
   using G1 = Geo<P, N, R, 8>;
   hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G1::NT), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -922,8 +1083,10 @@ static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_state_pass<TI, N, R>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G::NT),
-                     0, s, a);
+  using G3 = Geo3<P, N, R>;
+  // a split chunk's blocks are 8 apart in launch order: pad to whole groups of 8
+  const int nx = G3::SPLIT == 1 ? a.nchunk : G3::SPLIT * ((a.nchunk + 7) / 8) * 8;
+  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(G3::NT), 0, s, a);
   return hipGetLastError();
 }
 
