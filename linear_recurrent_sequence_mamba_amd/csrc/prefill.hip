@@ -39,6 +39,7 @@
 #include "m3_device.h"
 #include "m3_launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace m3 {
@@ -416,13 +417,17 @@ struct RowBlock {
   __device__ __forceinline__ void load(const TI* __restrict__ src, const PrefillArgs& a, int b,
                                        int h, int c0, int Lc, int v0) {
     const int t0 = v0 / R;
+    // the chunk's first token is a block-uniform base; per-lane offsets stay
+    // in 32 bits (the launcher checks that a chunk spans < 2^31 elements)
+    const TI* __restrict__ base = src + token_index(a, b, c0, h) * E;
+    const int tstride = a.H * E;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
       int tl, e0;
       where(vi, tl, e0);
       if (vi < NV && t0 + tl < Lc)
-        raw[i].load(src + token_index(a, b, c0 + t0 + tl, h) * E + e0);
+        raw[i].load(base + ((t0 + tl) * tstride + e0));
       else
         raw[i].zero();
     }
@@ -439,20 +444,21 @@ struct ThetaBlock {
   Vec8<TI> raw[IT];
   float d, l, A;
   __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
-    const TI* __restrict__ th = static_cast<const TI*>(a.theta);
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + token_index(a, b, c0, h) * NP;
+    const int tstride = a.H * NP;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
       const int t = vi / VPT, kv = vi % VPT;
       if (vi < NV && t < Lc)
-        raw[i].load(th + token_index(a, b, c0 + t, h) * NP + 8 * kv);
+        raw[i].load(th + (t * tstride + 8 * kv));
       else
         raw[i].zero();
     }
     const int tid = threadIdx.x;
     d = l = A = 0.0f;
     if (tid < Lc) {
-      const int64_t bth = token_index(a, b, c0 + tid, h);
+      const int64_t bth = token_index(a, b, c0, h) + tid * a.H;
       d = ld1(static_cast<const TI*>(a.dt), bth);
       l = ld1(static_cast<const TI*>(a.lam), bth);
       A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
@@ -701,16 +707,22 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
 
-  // loads first (the load counter retires in order): phase inputs and token
-  // scalars, then the first u-block of B and x
+  // every load goes out first (the load counter retires in order): phase
+  // inputs and token scalars, then all u-blocks of B and x, so that the
+  // block waits for HBM once
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
-  RowBlock<TI, N * R, R, G::NT, true> bb;
-  RowBlock<TI, P * R, R, G::NT, true> xb;
-  bb.load(Bg, a, b, h, c0, Lc, 0);
-  xb.load(Xg, a, b, h, c0, Lc, 0);
+  RowBlock<TI, N * R, R, G::NT, true> bb[G::NUB];
+  RowBlock<TI, P * R, R, G::NT, true> xb[G::NUB];
+#pragma unroll
+  for (int ub = 0; ub < G::NUB; ++ub) {
+    if (ub * kRB < rows) {
+      bb[ub].load(Bg, a, b, h, c0, Lc, ub * kRB);
+      xb[ub].load(Xg, a, b, h, c0, Lc, ub * kRB);
+    }
+  }
 
   chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 1);
   const double cs_end = sm.tb.cs[Lc - 1];
@@ -731,15 +743,12 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
 #pragma unroll
   for (int q = 0; q < QPW; ++q) acc[q] = f4{0, 0, 0, 0};
 
+#pragma unroll
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB >= rows) break;
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
-    store_rows_T<Pol, TI, N, R, G::NT>(bb, sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT>(xb, sm.xs);
-    if ((ub + 1) * kRB < rows) {   // next block's loads fly during this block's MFMAs
-      bb.load(Bg, a, b, h, c0, Lc, (ub + 1) * kRB);
-      xb.load(Xg, a, b, h, c0, Lc, (ub + 1) * kRB);
-    }
+    store_rows_T<Pol, TI, N, R, G::NT>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT>(xb[ub], sm.xs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QPW; ++q) {
@@ -884,6 +893,9 @@ struct Geo3 {
 
 template <class Pol, typename TI, int P, int N, int R>
 struct K3Smem {
+  // with R a multiple of 4 each token-pair mask value serves 16 virtual
+  // (row, column) pairs, so the block's mask rows are tabulated once
+  static constexpr int MT = R % 4 == 0 ? Geo3<P, N, R>::BROWS / R : 1;
   Tables<N, false> tb;
   union U {
     typename Pol::template Store<kRB, N> st;   // rotated C or B rows   [v][n]
@@ -891,6 +903,7 @@ struct K3Smem {
     TableScratch<N, Geo3<P, N, R>::NT> scr;
   } u;
   typename Pol::template XStore<P, kRB> xs;    // x^T block             [p][v]
+  float msk[MT][kQ + 1];                       // M[t - t_lo][u]
 };
 
 // four consecutive outputs (one token's four ranks) in one store
@@ -964,6 +977,21 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
 
   chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
   if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
+  // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} of this block's tokens
+  // (zero above the diagonal and past the chunk's end)
+  const int tlo = v0 / R;
+  if constexpr (R % 4 == 0) {
+    using SM = K3Smem<Pol, TI, P, N, R>;
+    for (int idx = tid; idx < SM::MT * kQ; idx += G::NT) {
+      const int tr = idx / kQ, u = idx % kQ, t = tlo + tr;
+      float m = 0.0f;
+      if (t < Lc && u <= t) {
+        const float w = sm.tb.gam[u] + (u < t ? sm.tb.bpr[u + 1] : 0.0f);
+        m = __expf((float)(sm.tb.cs[t] - sm.tb.cs[u])) * w;
+      }
+      sm.msk[tr][u] = m;
+    }
+  }
 
   // own rotated C rows -> MFMA fragments in registers
   typename Pol::Frag cf[NKS];
@@ -1039,7 +1067,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
           return m;
         };
         if constexpr (R % 4 == 0) {
-          gt *= mask((ubase + 16 * dt + 4 * g) / R);
+          gt *= sm.msk[tt - tlo][(ubase + 16 * dt + 4 * g) / R];
         } else {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) gt[jj] *= mask((ubase + 16 * dt + 4 * g + jj) / R);
@@ -1054,19 +1082,20 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   }
 
   // y[b, c0 + t, h, p, r] for D rows v = 16 tile + 4g + jj, column p
-  TO* __restrict__ Y = static_cast<TO*>(a.y);
+  TO* __restrict__ Y = static_cast<TO*>(a.y) + token_index(a, b, c0, h) * (P * R);
+  const int ystride = a.H * P * R;
 #pragma unroll
   for (int ct = 0; ct < G::PT; ++ct) {
     const int p = 16 * ct + l16;
     if constexpr (R % 4 == 0) {
       // the four rows are ranks v%R .. v%R + 3 of one token
       const int v = 16 * tile + 4 * g;
-      if (v < rows) st4_out(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[ct]);
+      if (v < rows) st4_out(Y, (v / R) * ystride + p * R + v % R, acc[ct]);
     } else {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int v = 16 * tile + 4 * g + jj;
-        if (v < rows) st1(Y, (token_index(a, b, c0 + v / R, h) * P + p) * R + v % R, acc[ct][jj]);
+        if (v < rows) st1(Y, (v / R) * ystride + p * R + v % R, acc[ct][jj]);
       }
     }
   }
@@ -1138,6 +1167,9 @@ void prefill_carve(PrefillArgs& a, void* ws) {
 }
 
 int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16, hipStream_t s, hipError_t* e) {
+  // in-chunk element offsets are 32-bit: Q tokens of the widest per-token row
+  const int64_t row = (int64_t)a.H * std::max(a.N, a.P) * a.R;
+  if ((int64_t)kQ * row >= (int64_t(1) << 31)) return -1;
   if (in_bf16) {
     return out_bf16 ? dispatch_shape<PolF16, bf16_t, bf16_t>(a, s, e)
                     : dispatch_shape<PolF16, bf16_t, float>(a, s, e);
