@@ -398,10 +398,10 @@ struct Vec8<float> {
 // (B or C: E = N R; x: E = P R) as 16-byte vectors spread over the block's
 // NT threads.  TF: consecutive threads take consecutive tokens (for the
 // transposed LDS layouts); otherwise consecutive threads walk one token.
-template <typename TI, int E, int R, int NT, bool TF>
+template <typename TI, int E, int R, int NT, bool TF, int ROWS = kRB>
 struct RowBlock {
   static constexpr int VPT = E / 8;
-  static constexpr int NTOK = kRB / R;
+  static constexpr int NTOK = ROWS / R;
   static constexpr int NV = NTOK * VPT;
   static constexpr int IT = (NV + NT - 1) / NT;
   Vec8<TI> raw[IT];
@@ -542,11 +542,11 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
 }
 
 // B or C rows of a block, rotated by -Phi_t, into st[v - v0][n]
-template <class Pol, typename TI, int N, int R, int NT, class Tab>
-__device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, false>& rb,
-                                           typename Pol::template Store<kRB, N>& st,
+template <class Pol, typename TI, int N, int R, int NT, int ROWS, class Tab>
+__device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, false, ROWS>& rb,
+                                           typename Pol::template Store<ROWS, N>& st,
                                            const Tab& tb, int t0, int Lc) {
-  using RBk = RowBlock<TI, N * R, R, NT, false>;
+  using RBk = RowBlock<TI, N * R, R, NT, false, ROWS>;
   constexpr int NPAIR = 4 / R;              // complex pairs per vector
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {
@@ -627,10 +627,10 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, tr
 }
 
 // x rows of a block, transposed: xs[p][v - v0]
-template <class Pol, typename TI, int P, int R, int NT>
-__device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, true>& rb,
-                                          typename Pol::template XStore<P, kRB>& xs) {
-  using RBk = RowBlock<TI, P * R, R, NT, true>;
+template <class Pol, typename TI, int P, int R, int NT, int ROWS>
+__device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, true, ROWS>& rb,
+                                          typename Pol::template XStore<P, ROWS>& xs) {
+  using RBk = RowBlock<TI, P * R, R, NT, true, ROWS>;
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {
     const int vi = threadIdx.x + NT * i;
@@ -748,7 +748,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     if (ub * kRB >= rows) break;
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
     store_rows_T<Pol, TI, N, R, G::NT>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT>(xb[ub], sm.xs);
+    store_x_T<Pol, TI, P, R, G::NT, kRB>(xb[ub], sm.xs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QPW; ++q) {
@@ -896,13 +896,15 @@ struct K3Smem {
   // with R a multiple of 4 each token-pair mask value serves 16 virtual
   // (row, column) pairs, so the block's mask rows are tabulated once
   static constexpr int MT = R % 4 == 0 ? Geo3<P, N, R>::BROWS / R : 1;
+  static constexpr int UB = 32;                // virtual rows per staged u-block
   Tables<N, false> tb;
   union U {
-    typename Pol::template Store<kRB, N> st;   // rotated C or B rows   [v][n]
+    typename Pol::template Store<kRB, N> st;   // rotated C rows        [v][n]
     typename Pol::template Store<P, N> sh;     // Shat                  [p][n]
+    typename Pol::template Store<UB, N> bst[2];  // rotated B rows, double-buffered
     TableScratch<N, Geo3<P, N, R>::NT> scr;
   } u;
-  typename Pol::template XStore<P, kRB> xs;    // x^T block             [p][v]
+  typename Pol::template XStore<P, UB> xs[2];  // x^T of a u-block      [p][v]
   float msk[MT][kQ + 1];                       // M[t - t_lo][u]
 };
 
@@ -941,7 +943,6 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   const int v0 = half * G::BROWS;           // this block's rows: [v0, vend)
   if (v0 >= rows) return;
   const int vend = min(rows, v0 + G::BROWS);
-  const int nub = (vend + kRB - 1) / kRB;   // u-blocks that reach these rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
@@ -965,13 +966,17 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
     if (v0 + k * kRB < rows) cb[k].load(Cg, a, b, h, c0, Lc, v0 + k * kRB);
   StateBlock<P, N, G::NT> sb;
   sb.load(a.S + chunk_id * P * N);
-  RowBlock<TI, N * R, R, G::NT, false> bb[2];
-  RowBlock<TI, P * R, R, G::NT, true> xb[2];
+  // B and x move in u-blocks of 32 virtual rows, three in flight
+  constexpr int UB = K3Smem<Pol, TI, P, N, R>::UB;
+  constexpr int NKB = G::ROWS / UB;
+  const int nkb = (vend + UB - 1) / UB;
+  RowBlock<TI, N * R, R, G::NT, false, UB> bb[3];
+  RowBlock<TI, P * R, R, G::NT, true, UB> xb[3];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (q < nub) {
-      bb[q].load(Bg, a, b, h, c0, Lc, q * kRB);
-      xb[q].load(Xg, a, b, h, c0, Lc, q * kRB);
+  for (int q = 0; q < 3; ++q) {
+    if (q < nkb) {
+      bb[q].load(Bg, a, b, h, c0, Lc, q * UB);
+      xb[q].load(Xg, a, b, h, c0, Lc, q * UB);
     }
   }
 
@@ -1001,7 +1006,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   for (int k = 0; k < G::NCB; ++k) {
     if (v0 + k * kRB < rows) {
       if (k > 0) __syncthreads();
-      store_rows<Pol, TI, N, R, G::NT>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc);
+      store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc);
       __syncthreads();
       if (lt / 4 == k) {
 #pragma unroll
@@ -1029,56 +1034,70 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   }
 
   // Y_diag: Gram tiles Bt Ct^T (D rows = u, columns = own rows), decay mask,
-  // then the masked tile is the A operand of the product with x
+  // then the masked tile is the A operand of the product with x.  u-block
+  // k + 1 is staged into the other buffer while the MFMAs of u-block k run,
+  // one barrier per u-block.
   const int vrow = 16 * tile + l16;
   const int tt = vrow / R;
   const bool row_ok = vrow < rows;
   const int tmax = min(Lc - 1, (16 * tile + 15) / R);
-#pragma unroll
-  for (int ub = 0; ub < G::NUB; ++ub) {
-    if (ub >= nub) break;
-    __syncthreads();
-    store_rows<Pol, TI, N, R, G::NT>(bb[ub % 2], sm.u.st, sm.tb, ub * kRB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT>(xb[ub % 2], sm.xs);
-    if (ub + 2 < nub) {   // two stages ahead
-      bb[ub % 2].load(Bg, a, b, h, c0, Lc, (ub + 2) * kRB);
-      xb[ub % 2].load(Xg, a, b, h, c0, Lc, (ub + 2) * kRB);
+  const double cst = sm.tb.cs[min(tt, kQ - 1)];
+  auto stage = [&](int k) {
+    store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % 3], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT, UB>(xb[k % 3], sm.xs[k % 2]);
+    if (k + 3 < nkb) {   // the freed slot takes u-block k + 3
+      bb[k % 3].load(Bg, a, b, h, c0, Lc, (k + 3) * UB);
+      xb[k % 3].load(Xg, a, b, h, c0, Lc, (k + 3) * UB);
     }
-    __syncthreads();
-    const double cst = sm.tb.cs[min(tt, kQ - 1)];
-    for (int ug = 0; ug < kRB; ug += UG) {
-      const int ubase = ub * kRB + ug;
-      if (ubase / R > tmax) break;
-      f4 d[Pol::DT];
+  };
+  __syncthreads();   // Shat's reads are done (the buffers share its space)
+  stage(0);
+  __syncthreads();
 #pragma unroll
-      for (int dt = 0; dt < Pol::DT; ++dt) {
+  for (int k = 0; k < NKB; ++k) {
+    if (k >= nkb) break;
+    if (k + 1 < nkb) stage(k + 1);
+    const int ubase = k * UB;
+    if (ubase / R <= tmax) {
+      // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
+      // each D row; with R a multiple of 4 a lane's 4 rows share one token
+      f4 mk[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        if constexpr (R % 4 == 0) {
+          const float m = sm.msk[tt - tlo][(ubase + 16 * dt + 4 * g) / R];
+          mk[dt] = f4{m, m, m, m};
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int tu = (ubase + 16 * dt + 4 * g + jj) / R;
+            float m = 0.0f;
+            if (row_ok && tu <= tt) {
+              const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
+              m = __expf((float)(cst - sm.tb.cs[tu])) * w;
+            }
+            mk[dt][jj] = m;
+          }
+        }
+      }
+      f4 d[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
         f4 gt = f4{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
-          gt = Pol::mma(Pol::frag(sm.u.st, ug + 16 * dt, s * Pol::KS, lane), cf[s], gt);
-        // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
-        // each D row; with R a multiple of 4 a lane's 4 rows share one token
-        auto mask = [&](int tu) {
-          float m = 0.0f;
-          if (row_ok && tu <= tt) {
-            const float w = sm.tb.gam[tu] + (tu < tt ? sm.tb.bpr[tu + 1] : 0.0f);
-            m = __expf((float)(cst - sm.tb.cs[tu])) * w;
-          }
-          return m;
-        };
-        if constexpr (R % 4 == 0) {
-          gt *= sm.msk[tt - tlo][(ubase + 16 * dt + 4 * g) / R];
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) gt[jj] *= mask((ubase + 16 * dt + 4 * g + jj) / R);
-        }
-        d[dt] = gt;
+          gt = Pol::mma(Pol::frag(sm.u.bst[k % 2], 16 * dt, s * Pol::KS, lane), cf[s], gt);
+        d[dt] = gt * mk[dt];
       }
-      const typename Pol::Frag af = Pol::frag_from_d(d);
 #pragma unroll
-      for (int ct = 0; ct < G::PT; ++ct)
-        acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs, 16 * ct, ug, lane), acc[ct]);
+      for (int ug = 0; ug < UB; ug += UG) {
+        const typename Pol::Frag af = Pol::frag_from_d(d + ug / 16);
+#pragma unroll
+        for (int ct = 0; ct < G::PT; ++ct)
+          acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs[k % 2], 16 * ct, ug, lane), acc[ct]);
+      }
     }
+    __syncthreads();
   }
 
   // y[b, c0 + t, h, p, r] for D rows v = 16 tile + 4g + jj, column p
