@@ -611,13 +611,13 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, tr
 #pragma unroll
     for (int pi = 0; pi < NPAIR; ++pi) {
       const int n = e0 / R + 2 * pi;
-      const f2 cs = csr[pi];
+      const f2 cs = wt * csr[pi];   // the weight folded into the rotation
       float w0[R], w1[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
-        w0[r] = wt * (cs.x * u0 - cs.y * u1);   // rotate by +angle
-        w1[r] = wt * (cs.y * u0 + cs.x * u1);
+        w0[r] = cs.x * u0 - cs.y * u1;   // rotate by +angle
+        w1[r] = cs.y * u0 + cs.x * u1;
       }
       // the R virtual rows of token tl are consecutive columns of st
       Pol::template putn<R>(st, n, tl * R, w0);
@@ -753,16 +753,13 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
 #pragma unroll
     for (int q = 0; q < QPW; ++q) {
       const int qq = wave * QPW + q;
-      if (qq < NQ) {
+      if (NQ % G::NW == 0 || qq < NQ) {
         const int pt = qq / G::NTL, nt = qq % G::NTL;
 #pragma unroll
         for (int kk = 0; kk < kRB; kk += Pol::KS)
           acc[q] = Pol::mma_x(Pol::frag(sm.u.bw, 16 * nt, kk, lane),
                               Pol::fragx_c(sm.xs, 16 * pt, kk, lane), acc[q]);
       }
-      // one output tile's operands at a time (hoisting them all costs
-      // registers and occupancy)
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -788,13 +785,34 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
       const int p = 16 * pt + l16, n = 16 * nt + 4 * g;
       f4 s = acc[q];
       if (xe) {
+        // x[p][0..R) and B[n..n+3][0..R) of the chunk's last token, in
+        // 8- and 16-byte pieces
+        float xr[R], br[4 * R];
+        if constexpr (R % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < R / 4; ++i) {
+            const f4 v = ld4(xe, (int64_t)p * R + 4 * i);
+            xr[4 * i] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
+          }
+        } else if constexpr (R == 2) {
+          const f2 v = ld2(xe, (int64_t)p * R);
+          xr[0] = v.x; xr[1] = v.y;
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) xr[r] = ld1(xe, (int64_t)p * R + r);
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const f4 v = ld4(Be, (int64_t)n * R + 4 * i);
+          br[4 * i] = v.x; br[4 * i + 1] = v.y; br[4 * i + 2] = v.z; br[4 * i + 3] = v.w;
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float xv = bpn * ld1(xe, (int64_t)p * R + r);
-          s.x += xv * ld1(Be, (int64_t)(n + 0) * R + r);
-          s.y += xv * ld1(Be, (int64_t)(n + 1) * R + r);
-          s.z += xv * ld1(Be, (int64_t)(n + 2) * R + r);
-          s.w += xv * ld1(Be, (int64_t)(n + 3) * R + r);
+          const float xv = bpn * xr[r];
+          s.x += xv * br[0 * R + r];
+          s.y += xv * br[1 * R + r];
+          s.z += xv * br[2 * R + r];
+          s.w += xv * br[3 * R + r];
         }
       }
       *reinterpret_cast<f4*>(S + (int64_t)p * N + n) = s;
