@@ -589,11 +589,11 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
 
 // B rows of a block rotated by +(Phi_end - Phi_t) and scaled by W_t,
 // transposed: st[n][v - v0]
-template <class Pol, typename TI, int N, int R, int NT, class Tab>
-__device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, true>& rb,
+template <class Pol, typename TI, int N, int R, int NT, bool TF, class Tab>
+__device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF>& rb,
                                              typename Pol::template Store<N, kRB>& st,
                                              const Tab& tb, const float* w, int t0, int Lc) {
-  using RBk = RowBlock<TI, N * R, R, NT, true>;
+  using RBk = RowBlock<TI, N * R, R, NT, TF>;
   constexpr int NPAIR = 4 / R;
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {
@@ -627,10 +627,10 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, tr
 }
 
 // x rows of a block, transposed: xs[p][v - v0]
-template <class Pol, typename TI, int P, int R, int NT, int ROWS>
-__device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, true, ROWS>& rb,
+template <class Pol, typename TI, int P, int R, int NT, int ROWS, bool TF>
+__device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, TF, ROWS>& rb,
                                           typename Pol::template XStore<P, ROWS>& xs) {
-  using RBk = RowBlock<TI, P * R, R, NT, true, ROWS>;
+  using RBk = RowBlock<TI, P * R, R, NT, TF, ROWS>;
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {
     const int vi = threadIdx.x + NT * i;
@@ -714,8 +714,12 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
-  RowBlock<TI, N * R, R, G::NT, true> bb[G::NUB];
-  RowBlock<TI, P * R, R, G::NT, true> xb[G::NUB];
+  // with R >= 2 a token's row of B (N R values) or x (P R) is long enough
+  // for lanes to walk it (whole lines per load); single-rank rows are
+  // spread one token per lane, so the transposed stores pair up lanes
+  constexpr bool TFK1 = R < 2;
+  RowBlock<TI, N * R, R, G::NT, TFK1> bb[G::NUB];
+  RowBlock<TI, P * R, R, G::NT, TFK1> xb[G::NUB];
 #pragma unroll
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB < rows) {
@@ -747,8 +751,8 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB >= rows) break;
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
-    store_rows_T<Pol, TI, N, R, G::NT>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT, kRB>(xb[ub], sm.xs);
+    store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
+    store_x_T<Pol, TI, P, R, G::NT, kRB, TFK1>(xb[ub], sm.xs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QPW; ++q) {
@@ -989,7 +993,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   constexpr int NKB = G::ROWS / UB;
   const int nkb = (vend + UB - 1) / UB;
   RowBlock<TI, N * R, R, G::NT, false, UB> bb[3];
-  RowBlock<TI, P * R, R, G::NT, true, UB> xb[3];
+  RowBlock<TI, P * R, R, G::NT, (R < 2), UB> xb[3];   // x rows walked by lanes when R >= 2
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     if (q < nkb) {
@@ -1062,7 +1066,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   const double cst = sm.tb.cs[min(tt, kQ - 1)];
   auto stage = [&](int k) {
     store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % 3], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT, UB>(xb[k % 3], sm.xs[k % 2]);
+    store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % 3], sm.xs[k % 2]);
     if (k + 3 < nkb) {   // the freed slot takes u-block k + 3
       bb[k % 3].load(Bg, a, b, h, c0, Lc, (k + 3) * UB);
       xb[k % 3].load(Xg, a, b, h, c0, Lc, (k + 3) * UB);
