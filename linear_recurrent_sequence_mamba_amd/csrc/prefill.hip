@@ -1175,6 +1175,8 @@ static int dispatch_shape(const PrefillArgs& a, hipStream_t s, hipError_t* e) {
   M3_SHAPE(64, 128, 2)
   M3_SHAPE(32, 64, 1)
   M3_SHAPE(32, 64, 4)
+  M3_SHAPE(64, 64, 1)
+  M3_SHAPE(64, 64, 4)
 #undef M3_SHAPE
   return -1;
 }
@@ -1183,7 +1185,8 @@ bool prefill_supported(int P, int N, int R, int Q, int in_bf16) {
   if (Q != kQ) return false;
   const bool shape = (P == 16 && N == 16 && R == 1) ||
                      (P == 64 && N == 128 && (R == 1 || R == 2 || R == 4)) ||
-                     (P == 32 && N == 64 && (R == 1 || R == 4));
+                     (P == 32 && N == 64 && (R == 1 || R == 4)) ||
+                     (P == 64 && N == 64 && (R == 1 || R == 4));
   if (!shape) return false;
   if (in_bf16 && N % 32 != 0) return false;  // fp16 fragments span 32 state columns
   return true;

@@ -48,6 +48,7 @@ SMALL = [  # P, N, R, dtype
     (64, 128, 1, "bf16"), (64, 128, 4, "bf16"), (16, 16, 1, "f32"), (64, 128, 1, "f32"),
     (64, 128, 4, "f32"), (32, 64, 2, "bf16"), (16, 32, 8, "bf16"), (48, 256, 1, "bf16"),
     (32, 16, 3, "f32"), (40, 64, 1, "bf16"),
+    (64, 64, 1, "bf16"), (64, 64, 4, "bf16"),   # the half-state size N = 64
 ]
 
 

@@ -73,7 +73,7 @@ def test_lengths_and_ranks(T, R):
 @pytest.mark.parametrize("R", [1, 4])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_other_shapes_and_fp32(R, dt):
-    for P, N in [(64, 128), (32, 64)]:
+    for P, N in [(64, 128), (32, 64), (64, 64)]:   # (64, 64): the half-state size
         w = I.Workload("t", 81, 2, 150, 3, P, N, R, 64, dt)
         say(f"prefill P={P} N={N} R={R} {dt}")
         _check(w, I.prefill_inputs(w, h0="normal", with_prev=True))
