@@ -25,6 +25,7 @@
  *    `stream` (a hipStream_t passed as void*; NULL = the default stream) and
  *    the call returns at once.  Argument checks run on the host before any
  *    launch; a failed check returns its status and launches nothing.
+ *  - ngroups outside [0, nheads] or not dividing nheads is M3_ERR_SHAPE.
  *  - Launch failures return M3_ERR_HIP (m3_last_hip_error() gives the HIP
  *    code).  Faults inside a kernel surface at the caller's next
  *    synchronisation.  NaN/Inf inputs propagate; they are not checked.
@@ -32,15 +33,17 @@
  *    streams must not share output or workspace buffers.
  *
  * Layouts (Bsz = batch, T = seqlen, H = nheads, P = headdim, N = dstate,
- * R = rank):
+ * R = rank, G = ngroups or H when ngroups is 0):
  *     x, y           [Bsz, T, H, P, R]      in_dtype / out_dtype
- *     B, C           [Bsz, T, H, N, R]      in_dtype
+ *     B, C           [Bsz, T, G, N, R]      in_dtype
  *     dt, lam        [Bsz, T, H]            in_dtype (already activated)
- *     theta          [Bsz, T, H, N/2]       in_dtype (one angle per pair)
+ *     theta          [Bsz, T, G, N/2]       in_dtype (one angle per pair)
  *     A              [H] fp32, or [Bsz, T, H] fp32 with M3_A_PER_TOKEN
  *     h0, hT, h      [Bsz, H, P, N]         fp32
  *     x_prev         [Bsz, H, P, R]         in_dtype
- *     B_prev         [Bsz, H, N, R]         in_dtype
+ *     B_prev         [Bsz, G, N, R]         in_dtype
+ * Head h reads B, C and theta of group h / (H / G): the groups of heads
+ * that share one B, C and phase projection (G = H: one per head).
  * The decode step drops the T axis.  With R = 1 the trailing axis has size 1.
  */
 #ifndef M3SSM_H
@@ -81,6 +84,7 @@ typedef struct {
   int32_t in_dtype;  /* m3_dtype of x, B, C, dt, lam, theta, x_prev, B_prev */
   int32_t out_dtype; /* m3_dtype of y                                      */
   uint32_t flags;    /* M3_THETA_IS_ANGLE | M3_A_PER_TOKEN                 */
+  int32_t ngroups;   /* G, groups sharing B, C, theta; 0 = nheads; G | H   */
 } m3_dims;
 
 /* Bytes of device workspace m3_scan_prefill needs for `dims` (0 if dims is

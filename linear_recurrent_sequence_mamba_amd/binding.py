@@ -30,7 +30,8 @@ class m3_dims(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("ngroups", ctypes.c_int32)]
 
 
 class M3Error(RuntimeError):
@@ -81,9 +82,14 @@ def m3_status_str(status: int) -> str:
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, rank=1, chunk=0,
-              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0) -> m3_dims:
+              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0, ngroups=0) -> m3_dims:
     return m3_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, in_dtype,
-                   out_dtype, flags)
+                   out_dtype, flags, ngroups)
+
+
+def groups(d: m3_dims) -> int:
+    """B, C and theta groups of a call (ngroups, or nheads when it is 0)."""
+    return d.ngroups if d.ngroups > 0 else d.nheads
 
 
 def dtype_code(t: torch.dtype) -> int:
@@ -132,16 +138,17 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
     ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
     if ti is not None and to is not None:
         Bsz, T, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
         _check("x", x, (Bsz, T, H, P, R), ti)
         _check("dt", dt, (Bsz, T, H), ti)
         _check("A", A, (Bsz, T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
         _check("lam", lam, (Bsz, T, H), ti)
-        _check("theta", theta, (Bsz, T, H, N // 2), ti)
-        _check("B", B, (Bsz, T, H, N, R), ti)
-        _check("C", C, (Bsz, T, H, N, R), ti)
+        _check("theta", theta, (Bsz, T, G, N // 2), ti)
+        _check("B", B, (Bsz, T, G, N, R), ti)
+        _check("C", C, (Bsz, T, G, N, R), ti)
         _check("h0", h0, (Bsz, H, P, N), torch.float32, optional=True)
         _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
-        _check("B_prev", B_prev, (Bsz, H, N, R), ti, optional=True)
+        _check("B_prev", B_prev, (Bsz, G, N, R), ti, optional=True)
         _check("y", y, (Bsz, T, H, P, R), to)
         _check("hT", hT, (Bsz, H, P, N), torch.float32, optional=True)
     nbytes = 0
@@ -163,16 +170,17 @@ def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam
     ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
     if ti is not None and to is not None:
         Bsz, H, P, N, R = d.batch, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
         _check("h", h, (Bsz, H, P, N), torch.float32)
         _check("x_t", x_t, (Bsz, H, P, R), ti)
         _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
-        _check("B_t", B_t, (Bsz, H, N, R), ti)
-        _check("B_prev", B_prev, (Bsz, H, N, R), ti, optional=True)
-        _check("C_t", C_t, (Bsz, H, N, R), ti)
+        _check("B_t", B_t, (Bsz, G, N, R), ti)
+        _check("B_prev", B_prev, (Bsz, G, N, R), ti, optional=True)
+        _check("C_t", C_t, (Bsz, G, N, R), ti)
         _check("dt_t", dt_t, (Bsz, H), ti)
         _check("A", A, (Bsz, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
         _check("lam_t", lam_t, (Bsz, H), ti)
-        _check("theta_t", theta_t, (Bsz, H, N // 2), ti)
+        _check("theta_t", theta_t, (Bsz, G, N // 2), ti)
         _check("y_t", y_t, (Bsz, H, P, R), to)
     st = _lib().m3_decode_step(ctypes.byref(d), _ptr(h), _ptr(x_t), _ptr(x_prev), _ptr(B_t),
                                _ptr(B_prev), _ptr(C_t), _ptr(dt_t), _ptr(A), _ptr(lam_t),
@@ -186,10 +194,12 @@ def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam
 def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
                  chunk=0, out_dtype=torch.float32, flags=0, want_hT=True, ws=None,
                  stream=None):
-    """Allocate y (and hT, workspace) and call m3_scan_prefill.  Returns (y, hT)."""
+    """Allocate y (and hT, workspace) and call m3_scan_prefill.  Returns (y, hT).
+    B, C and theta may have fewer head slots than x (head groups)."""
     Bsz, T, H, P, R = x.shape
-    N = B.shape[3]
-    d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags)
+    G, N = B.shape[2], B.shape[3]
+    d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
+                  0 if G == H else G)
     y = torch.empty((Bsz, T, H, P, R), dtype=out_dtype, device=x.device)
     hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
     if ws is None:
@@ -207,10 +217,13 @@ def workspace(dims: m3_dims, device) -> torch.Tensor:
 
 def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=None,
                 out_dtype=torch.float32, flags=0, y_t=None, stream=None):
-    """Advance h in place by one token; returns y_t (allocated unless given)."""
+    """Advance h in place by one token; returns y_t (allocated unless given).
+    B_t, C_t and theta_t may have fewer head slots than h (head groups)."""
     Bsz, H, P, N = h.shape
     R = x_t.shape[-1]
-    d = make_dims(Bsz, 1, H, P, N, R, 0, dtype_code(x_t.dtype), dtype_code(out_dtype), flags)
+    G = B_t.shape[1]
+    d = make_dims(Bsz, 1, H, P, N, R, 0, dtype_code(x_t.dtype), dtype_code(out_dtype), flags,
+                  0 if G == H else G)
     if y_t is None:
         y_t = torch.empty((Bsz, H, P, R), dtype=out_dtype, device=h.device)
     m3_decode_step(d, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t, stream)

@@ -29,8 +29,12 @@ m3_status check_dims(const m3_dims* d, bool need_seqlen) {
   if (d->in_dtype != M3_F32 && d->in_dtype != M3_BF16) return M3_ERR_DTYPE;
   if (d->out_dtype != M3_F32 && d->out_dtype != M3_BF16) return M3_ERR_DTYPE;
   if (d->flags & ~(M3_THETA_IS_ANGLE | M3_A_PER_TOKEN)) return M3_ERR_SHAPE;
+  if (d->ngroups < 0 || d->ngroups > d->nheads) return M3_ERR_SHAPE;
+  if (d->ngroups > 0 && d->nheads % d->ngroups != 0) return M3_ERR_SHAPE;
   return M3_OK;
 }
+
+int groups_of(const m3_dims* d) { return d->ngroups > 0 ? d->ngroups : d->nheads; }
 
 int chunk_of(const m3_dims* d) { return d->chunk > 0 ? d->chunk : 64; }
 
@@ -100,6 +104,7 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   a.R = d->rank;
   a.Q = Q;
   a.nchunk = (d->seqlen + Q - 1) / Q;
+  a.G = groups_of(d);
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   m3::prefill_carve(a, ws);
@@ -142,6 +147,7 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
   a.P = d->headdim;
   a.N = d->dstate;
   a.R = d->rank;
+  a.G = groups_of(d);
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   hipError_t err = hipSuccess;

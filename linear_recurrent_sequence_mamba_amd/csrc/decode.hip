@@ -33,6 +33,11 @@ struct TokenIn {
   float d, l, A, th;
 };
 
+// (batch, group) slot of B, C and theta for the unit bh = (batch, head)
+__device__ __forceinline__ int64_t group_slot(const DecodeArgs& a, int bh) {
+  return (int64_t)(bh / a.H) * a.G + (bh % a.H) / (a.H / a.G);
+}
+
 template <typename TI, int N>
 __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh) {
   TokenIn<TI, N> in;
@@ -41,7 +46,7 @@ __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh
   in.l = ld1(static_cast<const TI*>(a.lam), bh);
   in.A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
   const int k = threadIdx.x;
-  in.th = k < N / 2 ? ld1(static_cast<const TI*>(a.theta), (int64_t)bh * (N / 2) + k) : 0.0f;
+  in.th = k < N / 2 ? ld1(static_cast<const TI*>(a.theta), group_slot(a, bh) * (N / 2) + k) : 0.0f;
   return in;
 }
 
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   TO* __restrict__ y = static_cast<TO*>(a.y) + (int64_t)bh * P;
 
   const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
-  const int64_t vec = (int64_t)bh * N + n0;
+  const int64_t vec = group_slot(a, bh) * N + n0;
   f4 bt = ld4(static_cast<const TI*>(a.Bt), vec);
   f4 bp = PREV ? ld4(static_cast<const TI*>(a.Bp), vec) : f4{0, 0, 0, 0};
   const f4 ct = ld4(static_cast<const TI*>(a.Ct), vec);
@@ -172,9 +177,10 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
   float eb[PER], ep[PER], ec[PER];
   {
-    const TI* __restrict__ Bt = static_cast<const TI*>(a.Bt) + (int64_t)bh * NE;
-    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + (int64_t)bh * NE;
-    const TI* __restrict__ Ct = static_cast<const TI*>(a.Ct) + (int64_t)bh * NE;
+    const int64_t gs = group_slot(a, bh);
+    const TI* __restrict__ Bt = static_cast<const TI*>(a.Bt) + gs * NE;
+    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + gs * NE;
+    const TI* __restrict__ Ct = static_cast<const TI*>(a.Ct) + gs * NE;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int i = tid + 256 * q;

@@ -24,6 +24,7 @@ struct DecodeArgs {
   const void* theta;
   void* y;
   int H, P, N, R;
+  int G;           // groups sharing B, C and theta (G divides H)
   uint32_t flags;
   int has_prev;
 };
@@ -51,6 +52,7 @@ struct PrefillArgs {
   float* rot_end;  // [Bsz, H, nchunk, N/2, 2]: cos/sin of each chunk's total phase
   float* decay;    // [Bsz, H, nchunk]: exp of each chunk's total log-decay
   int Bsz, T, H, P, N, R, Q, nchunk;
+  int G;           // groups sharing B, C and theta (G divides H)
   uint32_t flags;
   int has_prev;
 };

@@ -363,6 +363,11 @@ __device__ __forceinline__ float reduce_angle(double phi) {
 __device__ __forceinline__ int64_t token_index(const PrefillArgs& a, int b, int t, int h) {
   return ((int64_t)b * a.T + t) * a.H + h;
 }
+// B, C and theta are shared by groups of H / G heads: [Bsz, T, G, ...]
+__device__ __forceinline__ int head_group(const PrefillArgs& a, int h) { return h / (a.H / a.G); }
+__device__ __forceinline__ int64_t group_index(const PrefillArgs& a, int b, int t, int h) {
+  return ((int64_t)b * a.T + t) * a.G + head_group(a, h);
+}
 
 // Raw 16-byte vectors of eight input elements, held in registers between
 // the load that is issued early and the store into LDS.
@@ -414,13 +419,15 @@ struct RowBlock {
       e0 = (vi % VPT) * 8;
     }
   }
+  // rows of x (GRP false: one per head) or of B, C (GRP true: one per group)
+  template <bool GRP>
   __device__ __forceinline__ void load(const TI* __restrict__ src, const PrefillArgs& a, int b,
                                        int h, int c0, int Lc, int v0) {
     const int t0 = v0 / R;
     // the chunk's first token is a block-uniform base; per-lane offsets stay
     // in 32 bits (the launcher checks that a chunk spans < 2^31 elements)
-    const TI* __restrict__ base = src + token_index(a, b, c0, h) * E;
-    const int tstride = a.H * E;
+    const TI* __restrict__ base = src + (GRP ? group_index(a, b, c0, h) : token_index(a, b, c0, h)) * E;
+    const int tstride = (GRP ? a.G : a.H) * E;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
@@ -444,8 +451,8 @@ struct ThetaBlock {
   Vec8<TI> raw[IT];
   float d, l, A;
   __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
-    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + token_index(a, b, c0, h) * NP;
-    const int tstride = a.H * NP;
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + group_index(a, b, c0, h) * NP;
+    const int tstride = a.G * NP;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
@@ -723,8 +730,8 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
 #pragma unroll
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB < rows) {
-      bb[ub].load(Bg, a, b, h, c0, Lc, ub * kRB);
-      xb[ub].load(Xg, a, b, h, c0, Lc, ub * kRB);
+      bb[ub].template load<true>(Bg, a, b, h, c0, Lc, ub * kRB);
+      xb[ub].template load<false>(Xg, a, b, h, c0, Lc, ub * kRB);
     }
   }
 
@@ -776,9 +783,8 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     const float d = ld1(static_cast<const TI*>(a.dt), nx);
     const float l = ld1(static_cast<const TI*>(a.lam), nx);
     bpn = (1.0f - l) * d;
-    const int64_t last = token_index(a, b, c0 + kQ - 1, h);
-    xe = Xg + last * P * R;
-    Be = Bg + last * N * R;
+    xe = Xg + token_index(a, b, c0 + kQ - 1, h) * P * R;
+    Be = Bg + group_index(a, b, c0 + kQ - 1, h) * N * R;
   }
   float* __restrict__ S = a.S + chunk_id * P * N;
 #pragma unroll
@@ -851,7 +857,7 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
     const float l = ld1(static_cast<const TI*>(a.lam), t0);
     const float bp0 = (1.0f - l) * d;
     const TI* xh = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
-    const TI* Bh = static_cast<const TI*>(a.Bp) + (int64_t)bh * N * R;
+    const TI* Bh = static_cast<const TI*>(a.Bp) + ((int64_t)b * a.G + head_group(a, h)) * N * R;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float xv = bp0 * ld1(xh, (int64_t)p * R + r);
@@ -985,7 +991,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   RowBlock<TI, N * R, R, G::NT, false> cb[G::NCB];
 #pragma unroll
   for (int k = 0; k < G::NCB; ++k)
-    if (v0 + k * kRB < rows) cb[k].load(Cg, a, b, h, c0, Lc, v0 + k * kRB);
+    if (v0 + k * kRB < rows) cb[k].template load<true>(Cg, a, b, h, c0, Lc, v0 + k * kRB);
   StateBlock<P, N, G::NT> sb;
   sb.load(a.S + chunk_id * P * N);
   // B and x move in u-blocks of 32 virtual rows, three in flight
@@ -997,8 +1003,8 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     if (q < nkb) {
-      bb[q].load(Bg, a, b, h, c0, Lc, q * UB);
-      xb[q].load(Xg, a, b, h, c0, Lc, q * UB);
+      bb[q].template load<true>(Bg, a, b, h, c0, Lc, q * UB);
+      xb[q].template load<false>(Xg, a, b, h, c0, Lc, q * UB);
     }
   }
 
@@ -1068,8 +1074,8 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
     store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % 3], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc);
     store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % 3], sm.xs[k % 2]);
     if (k + 3 < nkb) {   // the freed slot takes u-block k + 3
-      bb[k % 3].load(Bg, a, b, h, c0, Lc, (k + 3) * UB);
-      xb[k % 3].load(Xg, a, b, h, c0, Lc, (k + 3) * UB);
+      bb[k % 3].template load<true>(Bg, a, b, h, c0, Lc, (k + 3) * UB);
+      xb[k % 3].template load<false>(Xg, a, b, h, c0, Lc, (k + 3) * UB);
     }
   };
   __syncthreads();   // Shat's reads are done (the buffers share its space)

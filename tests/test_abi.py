@@ -41,7 +41,7 @@ def test_status_strings():
 
 def _dims(**kw):
     base = dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=128, rank=1, chunk=0,
-                in_dtype=m3.M3_BF16, out_dtype=m3.M3_F32, flags=0)
+                in_dtype=m3.M3_BF16, out_dtype=m3.M3_F32, flags=0, ngroups=0)
     base.update(kw)
     return m3.m3_dims(*base.values())
 
@@ -81,6 +81,9 @@ def test_error_paths(call):
     assert call(_dims(headdim=0)) == 2
     assert call(_dims(rank=0)) == 2
     assert call(_dims(flags=1 << 7)) == 2                       # unknown flag
+    assert call(_dims(ngroups=-1)) == 2                         # head groups
+    assert call(_dims(ngroups=4)) == 2                          # more groups than heads
+    assert call(_dims(ngroups=2)) == 2                          # 2 does not divide 3 heads
     assert call(_dims(in_dtype=5)) == 3
     assert call(_dims(out_dtype=-1)) == 3
     assert call(_dims(headdim=24, dstate=6)) == 4               # no kernel for it

@@ -11,8 +11,10 @@ from tests.util import TOL, cpu64, cuda, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def _run_steps(w, steps, flags=0, out_dtype=torch.float32, prev=True, check_bh=None):
-    """Run `steps` decode steps on the GPU and the oracle; return max errors."""
+def _run_steps(w, steps, flags=0, out_dtype=torch.float32, prev=True, check_bh=None, groups=None):
+    """Run `steps` decode steps on the GPU and the oracle; return max errors.
+    With `groups`, B, C and theta are shared by that many groups of heads (the
+    first head slots of the drawn tensors); the oracle sees them repeated per head."""
     h_cpu = I.decode_state(w)
     h_gpu = cuda(h_cpu)
     h_ref = cpu64(h_cpu)
@@ -25,8 +27,19 @@ def _run_steps(w, steps, flags=0, out_dtype=torch.float32, prev=True, check_bh=N
         h_ref = h_ref[sel]
     prev_in = None
     ey, eh = 0.0, 0.0
+    def grouped(d):
+        if groups is None:
+            return d
+        d = dict(d)
+        for k in ("B", "C", "theta"):
+            d[k] = d[k][:, :groups].contiguous()
+        return d
+
+    def per_head(t):
+        return t if (groups is None or t is None) else t.repeat_interleave(w.nheads // groups, dim=1)
+
     for s in range(steps):
-        d = I.decode_step_inputs(w, s)
+        d = grouped(I.decode_step_inputs(w, s))
         g = {k: cuda(v) for k, v in d.items()}
         xp = prev_in["x"] if (prev and prev_in is not None) else None
         Bp = prev_in["B"] if (prev and prev_in is not None) else None
@@ -34,9 +47,10 @@ def _run_steps(w, steps, flags=0, out_dtype=torch.float32, prev=True, check_bh=N
                            x_prev=cuda(xp), B_prev=cuda(Bp), out_dtype=out_dtype, flags=flags)
         Aref = cpu64(A)[sel] if flags & m3.M3_A_PER_TOKEN else cpu64(A)
         yr, h_ref = oracle.decode_step(
-            h_ref, cpu64(d["x"])[sel], None if xp is None else cpu64(xp)[sel], cpu64(d["B"])[sel],
-            None if Bp is None else cpu64(Bp)[sel], cpu64(d["C"])[sel], cpu64(d["dt"])[sel], Aref,
-            cpu64(d["lam"])[sel], cpu64(d["theta"])[sel], flags=flags)
+            h_ref, cpu64(d["x"])[sel], None if xp is None else cpu64(xp)[sel],
+            cpu64(per_head(d["B"]))[sel], None if Bp is None else cpu64(per_head(Bp))[sel],
+            cpu64(per_head(d["C"]))[sel], cpu64(d["dt"])[sel], Aref,
+            cpu64(d["lam"])[sel], cpu64(per_head(d["theta"]))[sel], flags=flags)
         torch.cuda.synchronize()
         ey = max(ey, rel_err(cpu64(y)[sel], yr))
         prev_in = d
@@ -79,6 +93,16 @@ def test_decode_no_prev_and_bf16_out(R):
     # bf16 output: the output rounding alone is up to 2^-8 relative
     ey, eh = _run_steps(w, 3, out_dtype=torch.bfloat16)
     assert ey <= 2 ** -8 + 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_head_groups(R, G):
+    """B, C and theta shared by G groups of the 4 heads."""
+    w = I.Workload("t", 93, 2, 1, 4, 64, 128, R, 64, "bf16", "normal")
+    say(f"decode head groups G={G} of 4, R={R}")
+    ey, eh = _run_steps(w, 4, groups=G)
+    assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
 
 
 @pytest.mark.parametrize("name", ["siso_decode", "mimo_decode"])

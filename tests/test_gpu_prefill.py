@@ -130,6 +130,29 @@ def test_mimo_long_prefill_one_signed_theta_sampled():
     _check(w, d, heads=np.array([0, 5]))
 
 
+@pytest.mark.parametrize("R", [1, 4])
+@pytest.mark.parametrize("G", [1, 2])
+def test_head_groups(R, G):
+    """B, C and theta shared by G groups of the 4 heads: the oracle runs on the
+    same group tensors repeated for every head of the group."""
+    w = I.Workload("t", 91, 2, 150, 4, 64, 128, R, 64, "bf16")
+    d = I.prefill_inputs(w, h0="normal", with_prev=True)
+    g = dict(d)
+    for k in ("B", "C", "theta"):
+        g[k] = d[k][:, :, :G].contiguous()
+    g["B_prev"] = d["B_prev"][:, :G].contiguous()
+    e = dict(g)
+    for k in ("B", "C", "theta"):
+        e[k] = g[k].repeat_interleave(4 // G, dim=2)
+    e["B_prev"] = g["B_prev"].repeat_interleave(4 // G, dim=1)
+    say(f"prefill head groups G={G} of 4, R={R}")
+    y, hT = _gpu_run(g)
+    ref = _oracle(e)
+    ey, eh = rel_err(cpu64(y), ref.y), rel_err(cpu64(hT), ref.hT)
+    say(f"  y err {ey:.2e}  hT err {eh:.2e}")
+    assert ey <= TOL[w.torch_dtype] and eh <= TOL[w.torch_dtype], (ey, eh)
+
+
 # ---------------------------------------------------------------------------
 # invariants of the GPU path
 def _slice_t(d, a, b):
