@@ -15,7 +15,9 @@ In the same run and the same JSON line, under "workloads": the MIMO rank-4
 decode step (same shape), the SISO chunked prefill (B=4, T=2048, H=32) and the
 MIMO rank-4 long prefill (B=1, T=16384, H=64), each with its own timing and
 roofline fraction, and the fp64 CPU oracle timed on a bounded sample of each
-workload (`cpu_baseline`, a reported baseline only).
+workload (`cpu_baseline`, a reported baseline only); also four decode tokens
+per call (m3_decode_tokens, the state crossing HBM once per call) at both
+decode shapes.
 
 Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
 """
@@ -48,6 +50,16 @@ def decode_bytes(w, in_bytes=2, out_bytes=4):
     state = 2 * B * H * P * N * 4
     inputs = in_bytes * (2 * B * H * P * R + 3 * B * H * N * R + 2 * B * H + B * H * N // 2)
     return state + inputs + H * 4 + out_bytes * B * H * P * R
+
+
+def decode_tokens_bytes(w, K, in_bytes=2, out_bytes=4):
+    """K tokens in one call: the state once in and once out, every token's
+    inputs and outputs once, the token before the first once."""
+    B, H, P, N, R = w.batch, w.nheads, w.headdim, w.dstate, w.rank
+    state = 2 * B * H * P * N * 4
+    per_tok = in_bytes * (B * H * P * R + 2 * B * H * N * R + 2 * B * H + B * H * N // 2)
+    prev = in_bytes * (B * H * P * R + B * H * N * R)
+    return state + K * per_tok + prev + H * 4 + K * out_bytes * B * H * P * R
 
 
 def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True):
@@ -163,6 +175,68 @@ def bench_decode(name, steps, warmup, pool_n=8):
     nbytes = decode_bytes(w)
     return dict(workload=w, steps=steps, total_ms=total_ms, step_ms=total_ms / steps,
                 stream_step_ms=stream_ms / steps, wall_s=wall, bytes=nbytes, pool=pool_n)
+
+
+def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
+    """K decode tokens per call (m3_decode_tokens) at the decode shape: `calls`
+    calls captured in one HIP graph, each a fresh set of K tokens."""
+    import torch
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+
+    w = I.WORKLOADS[name].with_(seqlen=K)
+    dev = torch.device("cuda:0")
+    pool = []
+    for s in range(pool_n):
+        d = I.prefill_inputs(w, stream=100 + s)
+        pool.append({k: (None if v is None else v.to(dev)) for k, v in d.items() if k != "h0"})
+    for s in range(pool_n):   # the token before a set is the last token of the one before it
+        prev = pool[(s - 1) % pool_n]
+        pool[s]["x_prev"] = prev["x"][:, -1].contiguous()
+        pool[s]["B_prev"] = prev["B"][:, -1].contiguous()
+    h = I.decode_state(w).to(dev)
+    y = torch.empty((w.batch, K, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
+    dims = m3.make_dims(w.batch, K, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32)
+    for d in pool:   # validate every argument set through the checked binding
+        m3.m3_decode_tokens(dims, h, d["x"], d["x_prev"], d["B"], d["B_prev"], d["C"], d["dt"],
+                            d["A"], d["lam"], d["theta"], y)
+    torch.cuda.synchronize()
+    lib = m3.library()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [(ctypes.byref(dims), p(h), p(d["x"]), p(d["x_prev"]), p(d["B"]), p(d["B_prev"]),
+             p(d["C"]), p(d["dt"]), p(d["A"]), p(d["lam"]), p(d["theta"]), p(y)) for d in pool]
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        lib.m3_decode_tokens(*args[s % pool_n], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for s in range(calls):
+                st = lib.m3_decode_tokens(*args[s % pool_n], cap)
+                if st != 0:
+                    raise RuntimeError(m3.m3_status_str(st))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / calls
+    nbytes = decode_tokens_bytes(w, K)
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    return dict(tokens_per_call=K, us_per_call=round(call_ms * 1e3, 2),
+                us_per_token_step=round(call_ms * 1e3 / K, 2),
+                tokens_per_s=round(w.batch * K / (call_ms * 1e-3), 1), algorithmic_bytes=nbytes,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                              kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}_tok",
+                              timing=f"HIP events around a graph of {calls} calls"))
 
 
 def bench_prefill(name, steps, warmup):
@@ -313,6 +387,10 @@ def main():
         res["siso_prefill"] = bench_prefill("siso_prefill", a.prefill_steps, 2)
     if want("mimo_prefill"):
         res["mimo_prefill"] = bench_prefill("mimo_prefill", a.prefill_steps, 2)
+    tok = {}
+    for base in ("siso_decode", "mimo_decode"):
+        if want(base + "_k4"):
+            tok[base + "_k4"] = bench_decode_tokens(base, 4, 100)
 
     copy_ref = None
     if "siso_decode" in res:
@@ -362,6 +440,7 @@ def main():
     workloads = {}
     for tag, r in res.items():
         workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
+    workloads.update(tok)   # several tokens per call (m3_decode_tokens), same shapes
 
     head = res.get("siso_decode")
     line = {"metric": METRIC}

@@ -123,6 +123,23 @@ m3_status m3_decode_step(const m3_dims* dims, float* h, const void* x_t,
                          const float* A, const void* lam_t,
                          const void* theta_t, void* y_t, void* stream);
 
+/* K = dims->seqlen consecutive decode steps in one call [the same article,
+ * sections 1.1-1.3; the recurrence applied token after token]: the state h
+ * [Bsz,H,P,N] fp32 is advanced in place by the K tokens and y receives y_k
+ * for each of them.  The inputs use the prefill layouts with T = K: x, y
+ * [Bsz,K,H,P,R]; B, C [Bsz,K,G,N,R]; dt, lam [Bsz,K,H]; theta [Bsz,K,G,N/2];
+ * A [H] (or [Bsz,K,H] with M3_A_PER_TOKEN); x_prev [Bsz,H,P,R] and B_prev
+ * [Bsz,G,N,R] are the token before the first (both NULL = zero).  The
+ * result equals K calls of m3_decode_step, but h crosses HBM once in and
+ * once out.  Supported: R = 1 with P <= 8192 / N (N in 16..256), or
+ * R in {2, 3, 4, 8} with P a multiple of 16 up to 64 (N in 16..128);
+ * otherwise M3_ERR_UNSUPPORTED. */
+m3_status m3_decode_tokens(const m3_dims* dims, float* h, const void* x,
+                           const void* x_prev, const void* B,
+                           const void* B_prev, const void* C, const void* dt,
+                           const float* A, const void* lam, const void* theta,
+                           void* y, void* stream);
+
 /* Static, human-readable name of a status. */
 const char* m3_status_str(m3_status status);
 

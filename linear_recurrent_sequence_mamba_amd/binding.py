@@ -60,6 +60,8 @@ def _lib():
         lib.m3_scan_prefill.argtypes = [dp] + [vp] * 13 + [sz, vp]
         lib.m3_decode_step.restype = ctypes.c_int
         lib.m3_decode_step.argtypes = [dp] + [vp] * 11 + [vp]
+        lib.m3_decode_tokens.restype = ctypes.c_int
+        lib.m3_decode_tokens.argtypes = [dp] + [vp] * 11 + [vp]
         lib.m3_status_str.restype = ctypes.c_char_p
         lib.m3_status_str.argtypes = [ctypes.c_int]
         lib.m3_last_hip_error.restype = ctypes.c_int
@@ -189,6 +191,31 @@ def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam
         raise M3Error(st, "m3_decode_step")
 
 
+def m3_decode_tokens(dims: m3_dims, h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y,
+                     stream=None) -> None:
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        Bsz, K, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
+        _check("h", h, (Bsz, H, P, N), torch.float32)
+        _check("x", x, (Bsz, K, H, P, R), ti)
+        _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
+        _check("B", B, (Bsz, K, G, N, R), ti)
+        _check("B_prev", B_prev, (Bsz, G, N, R), ti, optional=True)
+        _check("C", C, (Bsz, K, G, N, R), ti)
+        _check("dt", dt, (Bsz, K, H), ti)
+        _check("A", A, (Bsz, K, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
+        _check("lam", lam, (Bsz, K, H), ti)
+        _check("theta", theta, (Bsz, K, G, N // 2), ti)
+        _check("y", y, (Bsz, K, H, P, R), to)
+    st = _lib().m3_decode_tokens(ctypes.byref(d), _ptr(h), _ptr(x), _ptr(x_prev), _ptr(B),
+                                 _ptr(B_prev), _ptr(C), _ptr(dt), _ptr(A), _ptr(lam),
+                                 _ptr(theta), _ptr(y), _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_decode_tokens")
+
+
 # ---------------------------------------------------------------------------
 # allocation helpers (torch only provides the memory)
 def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
@@ -228,3 +255,18 @@ def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=N
         y_t = torch.empty((Bsz, H, P, R), dtype=out_dtype, device=h.device)
     m3_decode_step(d, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t, stream)
     return y_t
+
+
+def decode_tokens(h, x, B, C, dt, A, lam, theta, x_prev=None, B_prev=None,
+                  out_dtype=torch.float32, flags=0, y=None, stream=None):
+    """Advance h in place by the K tokens of x ([Bsz, K, H, P, R]); returns y
+    ([Bsz, K, H, P, R], allocated unless given)."""
+    Bsz, K, H, P, R = x.shape
+    N = h.shape[3]
+    G = B.shape[2]
+    d = make_dims(Bsz, K, H, P, N, R, 0, dtype_code(x.dtype), dtype_code(out_dtype), flags,
+                  0 if G == H else G)
+    if y is None:
+        y = torch.empty((Bsz, K, H, P, R), dtype=out_dtype, device=h.device)
+    m3_decode_tokens(d, h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y, stream)
+    return y

@@ -148,11 +148,54 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
   a.N = d->dstate;
   a.R = d->rank;
   a.G = groups_of(d);
+  a.K = 1;
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   hipError_t err = hipSuccess;
   if (m3::launch_decode(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
                         static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)
+    return M3_ERR_UNSUPPORTED;
+  return hip_status(err);
+}
+
+m3_status m3_decode_tokens(const m3_dims* d, float* h, const void* x, const void* x_prev,
+                           const void* B, const void* B_prev, const void* C, const void* dt,
+                           const float* A, const void* lam, const void* theta, void* y,
+                           void* stream) {
+  m3_status st = check_dims(d, true);
+  if (st != M3_OK) return st;
+  if (!h || !x || !B || !C || !dt || !A || !lam || !theta || !y) return M3_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
+  const void* ptrs[] = {h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  if (!m3::decode_tokens_supported(d->headdim, d->dstate, d->rank)) return M3_ERR_UNSUPPORTED;
+  const int64_t units = static_cast<int64_t>(d->batch) * d->nheads;
+  if (units > 0x7fffffff) return M3_ERR_SHAPE;
+
+  m3::DecodeArgs a{};
+  a.h = h;
+  a.x = x;
+  a.xp = x_prev;
+  a.Bt = B;
+  a.Bp = B_prev;
+  a.Ct = C;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.y = y;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.N = d->dstate;
+  a.R = d->rank;
+  a.G = groups_of(d);
+  a.K = d->seqlen;
+  a.flags = d->flags;
+  a.has_prev = x_prev != nullptr;
+  hipError_t err = hipSuccess;
+  if (m3::launch_decode_tokens(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
+                               static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)
     return M3_ERR_UNSUPPORTED;
   return hip_status(err);
 }

@@ -1,0 +1,478 @@
+// decode_tokens.hip -- several decode steps in one launch on gfx950.
+//
+// K consecutive tokens advance the fp32 state h [Bsz,H,P,N] in place, the
+// recurrence of the Mamba-3 article [xxxxx.co.kr, sections 1.1-1.3] applied
+// token after token:
+//   h <- R(phi_k) (alpha_k h + beta_k X_{k-1} B_{k-1}^T) + gamma_k X_k B_k^T,
+//   y_k = h C_k.
+// The state of a (batch, head) stays in registers for all K tokens, so it
+// crosses HBM once in and once out per call instead of once per token; the
+// per-token inputs stream past it, the next token's loads in flight while
+// the current token is applied.
+//
+//  * k_decode_siso_tok (R = 1): the thread layout of the single-step kernel
+//    (a state row over N/4 lanes, 4 consecutive columns per lane), with all
+//    P rows held at once (P <= 8 rows per lane).
+//  * k_decode_mimo_tok (R > 1): one 16-row block of the state per wave,
+//    P <= 64, in the MFMA D layout (the rank-R terms are MFMA products with
+//    K = R, as in the single-step kernel); rows enter and leave through a
+//    per-wave LDS transpose so that loads and stores cover whole lines.
+#include "m3_device.h"
+#include "m3_launch.h"
+
+namespace m3 {
+
+namespace {
+
+// token k of the unit bh = (b, h): per-head tensors [Bsz, K, H, ...] and
+// per-group tensors [Bsz, K, G, ...]
+__device__ __forceinline__ int64_t tok_head(const DecodeArgs& a, int bh, int k) {
+  return ((int64_t)(bh / a.H) * a.K + k) * a.H + bh % a.H;
+}
+__device__ __forceinline__ int64_t tok_group(const DecodeArgs& a, int bh, int k) {
+  return ((int64_t)(bh / a.H) * a.K + k) * a.G + (bh % a.H) / (a.H / a.G);
+}
+__device__ __forceinline__ int64_t unit_group(const DecodeArgs& a, int bh) {
+  return (int64_t)(bh / a.H) * a.G + (bh % a.H) / (a.H / a.G);
+}
+
+// the token scalars; pair phases of token k into cs (threads < N/2)
+template <typename TI, int N>
+struct TokScalars {
+  float d, l, A, th;
+  __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k) {
+    const int64_t th_ = tok_head(a, bh, k);
+    d = ld1(static_cast<const TI*>(a.dt), th_);
+    l = ld1(static_cast<const TI*>(a.lam), th_);
+    A = (a.flags & kAPerToken) ? a.A[th_] : a.A[bh % a.H];
+    const int kk = threadIdx.x;
+    th = kk < N / 2 ? ld1(static_cast<const TI*>(a.theta), tok_group(a, bh, k) * (N / 2) + kk) : 0.0f;
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs& a, float& alpha, float& beta,
+                                         float& gamma, f2* cs) const {
+    alpha = expf(d * A);
+    beta = (1.0f - l) * d * alpha;
+    gamma = l * d;
+    const int kk = threadIdx.x;
+    if (kk < N / 2) {
+      const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
+      float s, c;
+      sincosf(phi, &s, &c);
+      cs[kk] = f2{c, s};
+    }
+  }
+};
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+template <typename TI, typename TO, int N, int UNR, bool PREV>
+__global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
+  constexpr int LPR = N / 4;      // lanes per state row
+  constexpr int RPW = 64 / LPR;   // rows per wave per pass
+  constexpr int RPB = 4 * RPW;    // rows per block per pass
+  const int bh = blockIdx.x;
+  const int P = a.P;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = 4 * (lane % LPR);
+  const int rsub = wave * RPW + lane / LPR;
+  float* __restrict__ hb = a.h + (int64_t)bh * P * N;
+  const TI* __restrict__ X = static_cast<const TI*>(a.x);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.Bt);
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.Ct);
+  TO* __restrict__ Y = static_cast<TO*>(a.y);
+
+  // a lane's own two pairs (columns n0..n0+3) need their two phases only:
+  // no table, no barrier between tokens
+  const TI* __restrict__ Tg = static_cast<const TI*>(a.theta);
+  const TI* __restrict__ Dg = static_cast<const TI*>(a.dt);
+  const TI* __restrict__ Lg = static_cast<const TI*>(a.lam);
+  auto scal = [&](int k, float& d, float& l, float& A, f2& th) {
+    const int64_t t = tok_head(a, bh, k);
+    d = ld1(Dg, t);
+    l = ld1(Lg, t);
+    A = (a.flags & kAPerToken) ? a.A[t] : a.A[bh % a.H];
+    th = ld2(Tg, tok_group(a, bh, k) * (N / 2) + n0 / 2);
+  };
+  // token 0's inputs go out first, then the whole state of the unit
+  float dk, lk, Ak;
+  f2 thk;
+  scal(0, dk, lk, Ak, thk);
+  f4 bk = ld4(Bg, tok_group(a, bh, 0) * N + n0);
+  f4 ck = ld4(Cg, tok_group(a, bh, 0) * N + n0);
+  float xk[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) xk[u] = ld1(X, tok_head(a, bh, 0) * P + min(u * RPB + rsub, P - 1));
+  // the token before the first one: x_prev, B_prev (or zero)
+  f4 bo = PREV ? ld4(static_cast<const TI*>(a.Bp), unit_group(a, bh) * N + n0) : f4{0, 0, 0, 0};
+  float xo[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u)
+    xo[u] = PREV ? ld1(static_cast<const TI*>(a.xp), (int64_t)bh * P + min(u * RPB + rsub, P - 1)) : 0.0f;
+  f4 v[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) v[u] = ld4_state(hb + (int64_t)min(u * RPB + rsub, P - 1) * N + n0);
+
+  for (int k = 0; k < a.K; ++k) {
+    // the next token's inputs fly while this one is applied
+    float dn = dk, ln = lk, An = Ak;
+    f2 thn = thk;
+    f4 bn = bk, cn = ck;
+    float xn[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) xn[u] = xk[u];
+    if (k + 1 < a.K) {
+      scal(k + 1, dn, ln, An, thn);
+      bn = ld4(Bg, tok_group(a, bh, k + 1) * N + n0);
+      cn = ld4(Cg, tok_group(a, bh, k + 1) * N + n0);
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) xn[u] = ld1(X, tok_head(a, bh, k + 1) * P + min(u * RPB + rsub, P - 1));
+    }
+    const float alpha = expf(dk * Ak);
+    const float beta = (1.0f - lk) * dk * alpha;
+    const float gamma = lk * dk;
+    const bool ang = (a.flags & kThetaIsAngle) != 0;
+    float s0, c0, s1, c1;
+    sincosf(ang ? thk.x : dk * thk.x, &s0, &c0);
+    sincosf(ang ? thk.y : dk * thk.y, &s1, &c1);
+    const f2 r0 = f2{c0, s0}, r1 = f2{c1, s1};
+    const f4 bt = gamma * bk, bp = beta * bo;
+    TO* __restrict__ yk = Y + tok_head(a, bh, k) * P;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int p = u * RPB + rsub;
+      f4 s = alpha * v[u] + xo[u] * bp;
+      s = rot2pairs(s, r0, r1);
+      s += xk[u] * bt;
+      v[u] = s;
+      const float part = group_sum<LPR>(s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w);
+      if ((lane % LPR) == 0 && p < P) st1(yk, p, part);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      xo[u] = xk[u];
+      xk[u] = xn[u];
+    }
+    bo = bk;
+    bk = bn;
+    ck = cn;
+    dk = dn;
+    lk = ln;
+    Ak = An;
+    thk = thn;
+  }
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int p = u * RPB + rsub;
+    if (p < P) st4_stream(hb + (int64_t)p * N + n0, v[u]);
+  }
+}
+
+// --------------------------------------------------------------------------
+// D row 4g + i of tile t is state column 16t + 4g + i (as in the single-step
+// kernel): a lane's accumulator is the 16-byte vector of 4 consecutive
+// columns of its row.
+template <typename TI, typename TO, int N, int R, bool PREV>
+__global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
+  constexpr int NT = N / 16;
+  constexpr int KB = (R + 3) / 4;
+  constexpr int RP = (R + 3) & ~3;
+  constexpr int NE = N * R;
+  constexpr int PER = (NE + 255) / 256;
+  constexpr int V4 = N / 4;
+  constexpr int LV = 16 * V4 / 64;
+  // per-token operands, double-buffered (token k + 1's are written while
+  // token k is applied: one barrier per token); the row transposes at the
+  // start and the end share the space
+  struct Tok {
+    f2 cs[N / 2];
+    float bp[N * RP];     // beta_k * B_{k-1}   [n][r]
+    float bt[N * RP];     // gamma_k * B_k      [n][r]
+    float c[N * RP];      // C_k                [n][r]
+  };
+  __shared__ union {
+    Tok tok[2];
+    f4 tr[4][16][N / 4 + 1];
+  } sm;
+
+  const int bh = blockIdx.x;
+  const int P = a.P;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const bool rows = wave * 16 < P;   // this wave's 16-row block exists
+  const int p = wave * 16 + i16;
+  float* __restrict__ hb = a.h + (int64_t)bh * P * N;
+  const TI* __restrict__ X = static_cast<const TI*>(a.x);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.Bt);
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.Ct);
+  TO* __restrict__ Y = static_cast<TO*>(a.y);
+
+  auto load_bc = [&](int k, float* eb, float* ec) {
+    const TI* __restrict__ Bk = Bg + tok_group(a, bh, k) * NE;
+    const TI* __restrict__ Ck = Cg + tok_group(a, bh, k) * NE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = min(tid + 256 * q, NE - 1);
+      eb[q] = ld1(Bk, i);
+      ec[q] = ld1(Ck, i);
+    }
+  };
+  auto load_x = [&](const TI* __restrict__ src, float* xr) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int r = 4 * kb + g;
+      xr[kb] = (rows && r < R) ? ld1(src, (int64_t)p * R + r) : 0.0f;
+    }
+  };
+  // token operands into buffer tb: beta/gamma-scaled B, C, phases
+  auto put_tables = [&](Tok& tb, const TokScalars<TI, N>& sc, const float* eb, const float* eo,
+                        const float* ec) {
+    float alpha, beta, gamma;
+    sc.finish(a, alpha, beta, gamma, tb.cs);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = tid + 256 * q;
+      if (i < NE) {
+        const int j = (i / R) * RP + i % R;
+        tb.bt[j] = gamma * eb[q];
+        tb.bp[j] = beta * eo[q];
+        tb.c[j] = ec[q];
+      }
+    }
+  };
+
+  TokScalars<TI, N> sc;
+  sc.load(a, bh, 0);
+  float eb[PER], ec[PER], eo[PER];
+  load_bc(0, eb, ec);
+  float xk[KB], xo[KB];
+  load_x(X + tok_head(a, bh, 0) * P * R, xk);
+  if (PREV) {
+    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + unit_group(a, bh) * NE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) eo[q] = ld1(Bp, min(tid + 256 * q, NE - 1));
+    load_x(static_cast<const TI*>(a.xp) + (int64_t)bh * P * R, xo);
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) eo[q] = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xo[kb] = 0.0f;
+  }
+
+  // the wave's 16 state rows, row-contiguous, then into the D layout
+  f4 v[NT];
+  if (rows) {
+    f4 raw[LV];
+#pragma unroll
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      raw[j] = ld4_state(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4));
+    }
+#pragma unroll
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      sm.tr[wave][q / V4][q % V4] = raw[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = sm.tr[wave][i16][(16 * t + 4 * g) / 4];
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = f4{0, 0, 0, 0};
+  }
+  __syncthreads();   // every wave's transpose is read before the tables take the space
+  if constexpr (RP != R) {
+    for (int i = tid; i < N * RP; i += 256)
+      sm.tok[0].bt[i] = sm.tok[0].bp[i] = sm.tok[0].c[i] = sm.tok[1].bt[i] = sm.tok[1].bp[i] =
+          sm.tok[1].c[i] = 0.0f;
+    __syncthreads();
+  }
+  put_tables(sm.tok[0], sc, eb, eo, ec);
+  __syncthreads();
+
+  for (int k = 0; k < a.K; ++k) {
+    TokScalars<TI, N> scn = sc;
+    float ebn[PER], ecn[PER], xn[KB];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) { ebn[q] = eb[q]; ecn[q] = ec[q]; }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xn[kb] = xk[kb];
+    if (k + 1 < a.K) {
+      scn.load(a, bh, k + 1);
+      load_bc(k + 1, ebn, ecn);
+      load_x(X + tok_head(a, bh, k + 1) * P * R, xn);
+    }
+    const Tok& tb = sm.tok[k & 1];
+    const float alpha = expf(sc.d * sc.A);
+    if (rows) {
+      float yp[RP];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f4 acc = alpha * v[t];
+        const int nA = 16 * t + 4 * (i16 >> 2) + (i16 & 3);   // state column of A-operand row i16
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb.bp[nA * RP + 4 * kb + g], xo[kb], acc, 0, 0, 0);
+        const int n = 16 * t + 4 * g;
+        acc = rot2pairs(acc, tb.cs[n / 2], tb.cs[n / 2 + 1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb.bt[nA * RP + 4 * kb + g], xk[kb], acc, 0, 0, 0);
+        v[t] = acc;
+#pragma unroll
+        for (int rb = 0; rb < RP; rb += 4) {
+          const f4 c0 = *reinterpret_cast<const f4*>(&tb.c[(n + 0) * RP + rb]);
+          const f4 c1 = *reinterpret_cast<const f4*>(&tb.c[(n + 1) * RP + rb]);
+          const f4 c2 = *reinterpret_cast<const f4*>(&tb.c[(n + 2) * RP + rb]);
+          const f4 c3 = *reinterpret_cast<const f4*>(&tb.c[(n + 3) * RP + rb]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            yp[rb + q] += acc.x * c0[q] + acc.y * c1[q] + acc.z * c2[q] + acc.w * c3[q];
+        }
+        // one tile's LDS operands at a time (registers and occupancy)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        yp[r] += __shfl_xor(yp[r], 16, 64);
+        yp[r] += __shfl_xor(yp[r], 32, 64);
+      }
+      if (g == 0) {
+        TO* __restrict__ yk = Y + tok_head(a, bh, k) * P * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) st1(yk, (int64_t)p * R + r, yp[r]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      eo[q] = eb[q];
+      eb[q] = ebn[q];
+      ec[q] = ecn[q];
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      xo[kb] = xk[kb];
+      xk[kb] = xn[kb];
+    }
+    sc = scn;
+    // token k + 1's operands into the other buffer (last read at token k - 1,
+    // before the previous barrier)
+    if (k + 1 < a.K) put_tables(sm.tok[(k + 1) & 1], sc, eb, eo, ec);
+    __syncthreads();
+  }
+
+  // the wave's rows back to HBM, row-contiguous (every wave is past the
+  // last token's tables: the loop ends with a barrier)
+  if (rows) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4), sm.tr[wave][q / V4][q % V4]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+namespace {
+
+template <typename TI, typename TO, int N, int UNR>
+hipError_t launch_siso_tok(const DecodeArgs& a, int units, hipStream_t s) {
+  if (a.has_prev)
+    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true>), dim3(units), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false>), dim3(units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO, int N, int R>
+hipError_t launch_mimo_tok(const DecodeArgs& a, int units, hipStream_t s) {
+  if (a.has_prev)
+    hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true>), dim3(units), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false>), dim3(units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// rows per block pass of the single-input layout: 4 waves x 64 / (N/4) rows
+constexpr int rows_per_pass(int N) { return 4 * (64 / (N / 4)); }
+
+template <typename TI, typename TO, int N>
+hipError_t siso_tok_n(const DecodeArgs& a, int units, hipStream_t s) {
+  constexpr int RPB = rows_per_pass(N);
+  const int passes = (a.P + RPB - 1) / RPB;
+  switch (passes) {
+    case 1: return launch_siso_tok<TI, TO, N, 1>(a, units, s);
+    case 2: return launch_siso_tok<TI, TO, N, 2>(a, units, s);
+    case 3:
+    case 4: return launch_siso_tok<TI, TO, N, 4>(a, units, s);
+    default: return launch_siso_tok<TI, TO, N, 8>(a, units, s);
+  }
+}
+
+template <typename TI, typename TO>
+int dispatch_tok(const DecodeArgs& a, int units, hipStream_t s, hipError_t* err) {
+  if (a.R == 1) {
+    switch (a.N) {
+      case 16: *err = siso_tok_n<TI, TO, 16>(a, units, s); return 0;
+      case 32: *err = siso_tok_n<TI, TO, 32>(a, units, s); return 0;
+      case 64: *err = siso_tok_n<TI, TO, 64>(a, units, s); return 0;
+      case 128: *err = siso_tok_n<TI, TO, 128>(a, units, s); return 0;
+      case 256: *err = siso_tok_n<TI, TO, 256>(a, units, s); return 0;
+      default: return -1;
+    }
+  }
+#define M3_MIMO_N(NN)                                                       \
+  case NN:                                                                  \
+    switch (a.R) {                                                          \
+      case 2: *err = launch_mimo_tok<TI, TO, NN, 2>(a, units, s); return 0; \
+      case 3: *err = launch_mimo_tok<TI, TO, NN, 3>(a, units, s); return 0; \
+      case 4: *err = launch_mimo_tok<TI, TO, NN, 4>(a, units, s); return 0; \
+      case 8: *err = launch_mimo_tok<TI, TO, NN, 8>(a, units, s); return 0; \
+      default: return -1;                                                   \
+    }
+  switch (a.N) {
+    M3_MIMO_N(16)
+    M3_MIMO_N(32)
+    M3_MIMO_N(64)
+    M3_MIMO_N(128)
+    default: return -1;
+  }
+#undef M3_MIMO_N
+}
+
+}  // namespace
+
+bool decode_tokens_supported(int P, int N, int R) {
+  if (R == 1) {
+    if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256)) return false;
+    return P <= 8 * rows_per_pass(N);   // the whole state of a unit in registers
+  }
+  if (P % 16 != 0 || P > 64) return false;   // one 16-row block per wave
+  if (!(N == 16 || N == 32 || N == 64 || N == 128)) return false;
+  return R == 2 || R == 3 || R == 4 || R == 8;
+}
+
+int launch_decode_tokens(const DecodeArgs& a, int in_bf16, int out_bf16, int units,
+                         hipStream_t s, hipError_t* err) {
+  if (in_bf16) {
+    return out_bf16 ? dispatch_tok<bf16_t, bf16_t>(a, units, s, err)
+                    : dispatch_tok<bf16_t, float>(a, units, s, err);
+  }
+  return out_bf16 ? dispatch_tok<float, bf16_t>(a, units, s, err)
+                  : dispatch_tok<float, float>(a, units, s, err);
+}
+
+}  // namespace m3

@@ -25,11 +25,16 @@ struct DecodeArgs {
   void* y;
   int H, P, N, R;
   int G;           // groups sharing B, C and theta (G divides H)
+  int K;           // tokens of a multi-token call (1 for a single step)
   uint32_t flags;
   int has_prev;
 };
 
 bool decode_supported(int P, int N, int R);
+bool decode_tokens_supported(int P, int N, int R);
+// several tokens per launch, the state kept on chip between them
+int launch_decode_tokens(const DecodeArgs& a, int in_bf16, int out_bf16, int units,
+                         hipStream_t s, hipError_t* err);
 // returns 0 when launched (err = hipGetLastError), -1 when no kernel fits
 int launch_decode(const DecodeArgs& a, int in_bf16, int out_bf16, int units,
                   hipStream_t s, hipError_t* err);

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("m3_scan_prefill", "m3_decode_step", "m3_prefill_workspace_size",
-              "m3_status_str", "m3_last_hip_error"):
+    for n in ("m3_scan_prefill", "m3_decode_step", "m3_decode_tokens",
+              "m3_prefill_workspace_size", "m3_status_str", "m3_last_hip_error"):
         assert n in names, names
 
 
@@ -56,6 +56,12 @@ def _decode(d, **over):
     return m3.library().m3_decode_step(ctypes.byref(d), *args.values(), None)
 
 
+def _tokens(d, **over):
+    args = dict(h=P16, x=P16, xp=None, Bt=P16, Bp=None, C=P16, dt=P16, A=P16, lam=P16, th=P16, y=P16)
+    args.update(over)
+    return m3.library().m3_decode_tokens(ctypes.byref(d), *args.values(), None)
+
+
 def _prefill(d, ws_bytes=1 << 40, **over):
     args = dict(x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None, Bp=None,
                 y=P16, hT=None, ws=P16)
@@ -72,7 +78,7 @@ def test_workspace_size():
     assert m3.library().m3_prefill_workspace_size(None) == 0
 
 
-@pytest.mark.parametrize("call", [_decode, _prefill])
+@pytest.mark.parametrize("call", [_decode, _tokens, _prefill])
 def test_error_paths(call):
     assert m3.library().m3_decode_step(None, *([None] * 12)) == 1
     assert call(_dims(), x=None) == 1                           # NULL input
@@ -88,6 +94,12 @@ def test_error_paths(call):
     assert call(_dims(out_dtype=-1)) == 3
     assert call(_dims(headdim=24, dstate=6)) == 4               # no kernel for it
     assert call(_dims(), x=P_MIS) == 5                          # misaligned
+
+
+def test_tokens_specific_errors():
+    assert _tokens(_dims(seqlen=0)) == 2                        # no tokens
+    assert _tokens(_dims(headdim=80)) == 4                      # state rows do not fit on chip
+    assert _tokens(_dims(rank=4, headdim=128)) == 4             # MIMO: P <= 64
 
 
 def test_prefill_specific_errors():
