@@ -131,8 +131,8 @@ m3_status m3_decode_step(const m3_dims* dims, float* h, const void* x_t,
  * A [H] (or [Bsz,K,H] with M3_A_PER_TOKEN); x_prev [Bsz,H,P,R] and B_prev
  * [Bsz,G,N,R] are the token before the first (both NULL = zero).  The
  * result equals K calls of m3_decode_step, but h crosses HBM once in and
- * once out.  Supported: R = 1 with P <= 8192 / N (N in 16..256), or
- * R in {2, 3, 4, 8} with P a multiple of 16 up to 64 (N in 16..128);
+ * once out.  Supported: R = 1 with N in {16, 32, 64, 128, 256}, or R in
+ * {2, 3, 4, 8} with P a multiple of 16 up to 64 and N in {16, 32, 64, 128};
  * otherwise M3_ERR_UNSUPPORTED. */
 m3_status m3_decode_tokens(const m3_dims* dims, float* h, const void* x,
                            const void* x_prev, const void* B,

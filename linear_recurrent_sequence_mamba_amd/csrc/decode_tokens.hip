@@ -11,8 +11,9 @@
 // the current token is applied.
 //
 //  * k_decode_siso_tok (R = 1): the thread layout of the single-step kernel
-//    (a state row over N/4 lanes, 4 consecutive columns per lane), with all
-//    P rows held at once (P <= 8 rows per lane).
+//    (a state row over N/4 lanes, 4 consecutive columns per lane); a block
+//    holds up to 8 rows per lane for all K tokens, and a unit with more rows
+//    is split over several blocks.
 //  * k_decode_mimo_tok (R > 1): one 16-row block of the state per wave,
 //    P <= 64, in the MFMA D layout (the rank-R terms are MFMA products with
 //    K = R, as in the single-step kernel); rows enter and leave through a
@@ -71,12 +72,14 @@ __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
   constexpr int LPR = N / 4;      // lanes per state row
   constexpr int RPW = 64 / LPR;   // rows per wave per pass
   constexpr int RPB = 4 * RPW;    // rows per block per pass
-  const int bh = blockIdx.x;
+  // a unit's rows may be split over several blocks (UNR * RPB rows each)
+  const int nblk = (a.P + UNR * RPB - 1) / (UNR * RPB);
+  const int bh = blockIdx.x / nblk;
   const int P = a.P;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n0 = 4 * (lane % LPR);
-  const int rsub = wave * RPW + lane / LPR;
+  const int rsub = (blockIdx.x % nblk) * UNR * RPB + wave * RPW + lane / LPR;
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
   const TI* __restrict__ X = static_cast<const TI*>(a.x);
   const TI* __restrict__ Bg = static_cast<const TI*>(a.Bt);
@@ -390,10 +393,13 @@ namespace {
 
 template <typename TI, typename TO, int N, int UNR>
 hipError_t launch_siso_tok(const DecodeArgs& a, int units, hipStream_t s) {
+  constexpr int RPB = 4 * (64 / (N / 4));
+  const int nblk = (a.P + UNR * RPB - 1) / (UNR * RPB);
+  const dim3 grid(units * nblk);
   if (a.has_prev)
-    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true>), dim3(units), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false>), dim3(units), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -413,6 +419,9 @@ template <typename TI, typename TO, int N>
 hipError_t siso_tok_n(const DecodeArgs& a, int units, hipStream_t s) {
   constexpr int RPB = rows_per_pass(N);
   const int passes = (a.P + RPB - 1) / RPB;
+  // up to 8 row passes per block; more rows go to further blocks (measured:
+  // one block of 8 passes beats two of 4 at P = 64, N = 128, since every
+  // block loads the token inputs)
   switch (passes) {
     case 1: return launch_siso_tok<TI, TO, N, 1>(a, units, s);
     case 2: return launch_siso_tok<TI, TO, N, 2>(a, units, s);
@@ -456,10 +465,7 @@ int dispatch_tok(const DecodeArgs& a, int units, hipStream_t s, hipError_t* err)
 }  // namespace
 
 bool decode_tokens_supported(int P, int N, int R) {
-  if (R == 1) {
-    if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256)) return false;
-    return P <= 8 * rows_per_pass(N);   // the whole state of a unit in registers
-  }
+  if (R == 1) return N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
   if (P % 16 != 0 || P > 64) return false;   // one 16-row block per wave
   if (!(N == 16 || N == 32 || N == 64 || N == 128)) return false;
   return R == 2 || R == 3 || R == 4 || R == 8;

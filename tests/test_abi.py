@@ -98,7 +98,7 @@ def test_error_paths(call):
 
 def test_tokens_specific_errors():
     assert _tokens(_dims(seqlen=0)) == 2                        # no tokens
-    assert _tokens(_dims(headdim=80)) == 4                      # state rows do not fit on chip
+    assert _tokens(_dims(dstate=24)) == 4                       # no kernel for N = 24
     assert _tokens(_dims(rank=4, headdim=128)) == 4             # MIMO: P <= 64
 
 

@@ -70,6 +70,7 @@ def test_tokens_bf16(K, R):
     (32, 64, 1, "bf16"), (64, 64, 1, "bf16"), (64, 64, 4, "bf16"), (16, 16, 1, "f32"),
     (64, 128, 1, "f32"), (32, 256, 1, "bf16"), (40, 64, 1, "bf16"), (32, 64, 2, "bf16"),
     (16, 32, 8, "bf16"), (48, 16, 3, "f32"), (64, 128, 4, "f32"),
+    (80, 128, 1, "bf16"), (48, 256, 1, "f32"),   # rows of a unit split over blocks
 ])
 def test_tokens_shapes(P, N, R, dt):
     w = I.Workload("t", 96, 2, 5, 3, P, N, R, 64, dt)
