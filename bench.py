@@ -234,7 +234,7 @@ def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
                 us_per_token_step=round(call_ms * 1e3 / K, 2),
                 tokens_per_s=round(w.batch * K / (call_ms * 1e-3), 1), algorithmic_bytes=nbytes,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=counters_for(f"{name}_k{K}"),
                               kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}_tok",
                               timing=f"HIP events around a graph of {calls} calls"))
 
@@ -300,8 +300,27 @@ def copy_reference(state_bytes, reps=50):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del src, dst
-    return dict(bytes=2 * state_bytes, us=round(ms * 1e3, 2), gbs=round(2 * state_bytes / (ms * 1e-3) / 1e9, 1),
-                kernel="torch copy_ (read + write of a 268 MB fp32 buffer)")
+    out = dict(bytes=2 * state_bytes, us=round(ms * 1e3, 2), gbs=round(2 * state_bytes / (ms * 1e-3) / 1e9, 1),
+               kernel="torch copy_ (read + write of a 268 MB fp32 buffer)")
+    # in-place updates (read and write the same buffer, as the decode state
+    # is): at the state's size, which the 256 MB last-level cache partly
+    # holds between passes, and at twice that, which it cannot
+    for mult in (1, 2):
+        buf = torch.ones(n * mult, dtype=torch.float32, device="cuda:0")
+        for _ in range(3):
+            buf.mul_(1.0)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            buf.mul_(1.0)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nb = 2 * state_bytes * mult
+        out[f"inplace_x{mult}"] = dict(bytes=nb, us=round(ms * 1e3, 2), gbs=round(nb / (ms * 1e-3) / 1e9, 1),
+                                       kernel=f"torch mul_ in place on a {state_bytes * mult // 2**20} MiB fp32 buffer")
+        del buf
+    return out
 
 
 # ---------------------------------------------------------------------------
