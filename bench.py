@@ -17,7 +17,8 @@ MIMO rank-4 long prefill (B=1, T=16384, H=64), each with its own timing and
 roofline fraction, and the fp64 CPU oracle timed on a bounded sample of each
 workload (`cpu_baseline`, a reported baseline only); also four decode tokens
 per call (m3_decode_tokens, the state crossing HBM once per call) at both
-decode shapes.
+decode shapes, and the two prefill shapes' tokens packed as sequences of
+drawn lengths (m3_scan_prefill_varlen).
 
 Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
 """
@@ -62,11 +63,12 @@ def decode_tokens_bytes(w, K, in_bytes=2, out_bytes=4):
     return state + K * per_tok + prev + H * 4 + K * out_bytes * B * H * P * R
 
 
-def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True):
+def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True, nseq=None):
+    """nseq: packed sequences (one final state each) in w's T token rows."""
     B, T, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
     inputs = in_bytes * (B * T * H * P * R + 2 * B * T * H * N * R + 2 * B * T * H
                          + B * T * H * N // 2)
-    states = (int(h0) + int(hT)) * B * H * P * N * 4
+    states = (int(h0) + int(hT)) * (nseq or B) * H * P * N * 4
     return inputs + states + H * 4 + out_bytes * B * T * H * P * R
 
 
@@ -281,6 +283,47 @@ def bench_prefill(name, steps, warmup):
                 bytes=prefill_bytes(w), tokens=w.batch * w.seqlen, ws_bytes=ws.numel())
 
 
+def bench_prefill_varlen(name, steps, warmup):
+    """A packed serving mix (m3_scan_prefill_varlen): the same tokens as the
+    dense prefill shape, split into sequences of drawn lengths."""
+    import torch
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+
+    w, max_len = I.PACKED[name]
+    lengths = I.packed_lengths(w, max_len)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = {k: (None if v is None else v.to(dev)) for k, v in I.packed_inputs(w, lengths).items()}
+    log(f"[{name}] {len(lengths)} sequences, generated in {time.time() - t0:.1f}s")
+    S, T = len(lengths), w.seqlen
+    dims = m3.make_dims(S, T, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, m3.M3_BF16, m3.M3_F32)
+    ws = m3.workspace(dims, dev, varlen=True)
+    y = torch.empty((T, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
+    hT = torch.empty((S, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        m3.m3_scan_prefill_varlen(dims, d["cu_seqlens"], d["x"], d["dt"], d["A"], d["lam"],
+                                  d["theta"], d["B"], d["C"], None, None, None, y, hT, ws, stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for s in range(steps):
+        ev0[s].record(stream)
+        launch()
+        ev1[s].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
+    call_ms = sum(ms) / len(ms)
+    return dict(workload=w, steps=steps, call_ms=call_ms, call_p50_ms=ms[len(ms) // 2],
+                bytes=prefill_bytes(w, nseq=S), tokens=T, ws_bytes=ws.numel(), nseq=S,
+                lengths=dict(min=min(lengths), max=max(lengths), mean=round(T / S, 1)))
+
+
 def copy_reference(state_bytes, reps=50):
     """A plain device copy of a state-sized buffer (torch's copy kernel): read
     + write of the same byte count the decode step streams.  Context for the
@@ -406,6 +449,9 @@ def main():
         res["siso_prefill"] = bench_prefill("siso_prefill", a.prefill_steps, 2)
     if want("mimo_prefill"):
         res["mimo_prefill"] = bench_prefill("mimo_prefill", a.prefill_steps, 2)
+    for name in ("siso_prefill_varlen", "mimo_prefill_varlen"):
+        if want(name):
+            res[name] = bench_prefill_varlen(name, a.prefill_steps, 2)
     tok = {}
     for base in ("siso_decode", "mimo_decode"):
         if want(base + "_k4"):
@@ -447,6 +493,12 @@ def main():
 
     def prefill_entry(r, tag):
         ach = r["bytes"] / (r["call_ms"] * 1e-3) / 1e9
+        if "nseq" in r:   # packed sequences: no separate counters or CPU leg
+            return dict(
+                ms_per_call=round(r["call_ms"], 4), p50_ms=round(r["call_p50_ms"], 4),
+                tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
+                sequences=r["nseq"], lengths=r["lengths"], algorithmic_bytes=r["bytes"],
+                workspace_bytes=r["ws_bytes"], hbm_frac=round(ach / HBM_PEAK_GBS, 4))
         return dict(
             ms_per_call=round(r["call_ms"], 4), p50_ms=round(r["call_p50_ms"], 4),
             tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
@@ -460,6 +512,10 @@ def main():
     for tag, r in res.items():
         workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
     workloads.update(tok)   # several tokens per call (m3_decode_tokens), same shapes
+    for base in ("siso_prefill", "mimo_prefill"):
+        if base in workloads and base + "_varlen" in workloads:
+            workloads[base + "_varlen"]["tokens_per_s_vs_dense"] = round(
+                workloads[base + "_varlen"]["tokens_per_s"] / workloads[base]["tokens_per_s"], 3)
 
     head = res.get("siso_decode")
     line = {"metric": METRIC}

@@ -111,6 +111,41 @@ m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
                           const void* x_prev, const void* B_prev, void* y,
                           float* hT, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace m3_scan_prefill_varlen needs for `dims`
+ * (dims->batch = number of sequences S, dims->seqlen = total tokens T); 0
+ * if dims is invalid.  Besides the per-chunk totals it holds two small
+ * tables built from cu_seqlens on every call. */
+size_t m3_prefill_varlen_workspace_size(const m3_dims* dims);
+
+/* Chunked prefill of S = dims->batch independent sequences packed back to
+ * back into T = dims->seqlen token rows [the recurrence of the same
+ * article, sections 1.1-1.3, run separately for each sequence; packing is a
+ * serving layout that the pages do not describe].  cu_seqlens is a DEVICE
+ * array of S + 1 int32 offsets, 4-byte aligned: sequence s is rows
+ * [cu_seqlens[s], cu_seqlens[s+1]).  Layouts are those of m3_scan_prefill
+ * with Bsz = 1 for the token rows and Bsz = S for the per-sequence arrays:
+ *     x, y           [T, H, P, R]       B, C     [T, G, N, R]
+ *     dt, lam        [T, H]             theta    [T, G, N/2]
+ *     A              [H] fp32, or [T, H] fp32 with M3_A_PER_TOKEN
+ *     h0, hT         [S, H, P, N] fp32  x_prev   [S, H, P, R]
+ *     B_prev         [S, G, N, R]
+ * Each sequence starts from its own h0 row (NULL = zero) and token before
+ * (x_prev/B_prev rows; NULL = zero) and ends in its own hT row, so the
+ * result equals one m3_scan_prefill per sequence.  A sequence may be empty
+ * (its hT row is then its h0 row).  The offsets are meant to rise from
+ * cu_seqlens[0] = 0 to cu_seqlens[S] = T; they cannot be checked on the
+ * host, so the kernels clamp each one into [0, T] and raise it to the
+ * largest offset before it: no access leaves the buffers whatever the array
+ * holds, and y rows that no sequence covers are left unwritten.  The rest
+ * of m3_scan_prefill's contract applies; ws must be at least
+ * m3_prefill_varlen_workspace_size(dims) bytes. */
+m3_status m3_scan_prefill_varlen(const m3_dims* dims, const int32_t* cu_seqlens,
+                                 const void* x, const void* dt, const float* A,
+                                 const void* lam, const void* theta, const void* B,
+                                 const void* C, const float* h0, const void* x_prev,
+                                 const void* B_prev, void* y, float* hT, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* One decode step [the same article, sections 1.1-1.3]: the state h
  * [Bsz,H,P,N] fp32 is advanced in place by the token (x_t, B_t, C_t, dt_t,
  * lam_t, theta_t), with (x_prev, B_prev) the token before it (both NULL =

@@ -58,6 +58,10 @@ def _lib():
         lib.m3_prefill_workspace_size.argtypes = [dp]
         lib.m3_scan_prefill.restype = ctypes.c_int
         lib.m3_scan_prefill.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        lib.m3_prefill_varlen_workspace_size.restype = sz
+        lib.m3_prefill_varlen_workspace_size.argtypes = [dp]
+        lib.m3_scan_prefill_varlen.restype = ctypes.c_int
+        lib.m3_scan_prefill_varlen.argtypes = [dp] + [vp] * 14 + [sz, vp]
         lib.m3_decode_step.restype = ctypes.c_int
         lib.m3_decode_step.argtypes = [dp] + [vp] * 11 + [vp]
         lib.m3_decode_tokens.restype = ctypes.c_int
@@ -166,6 +170,45 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
         raise M3Error(st, "m3_scan_prefill")
 
 
+def m3_prefill_varlen_workspace_size(dims: m3_dims) -> int:
+    return int(_lib().m3_prefill_varlen_workspace_size(ctypes.byref(dims)))
+
+
+def m3_scan_prefill_varlen(dims: m3_dims, cu_seqlens, x, dt, A, lam, theta, B, C, h0, x_prev,
+                           B_prev, y, hT, ws, stream=None) -> None:
+    """Packed sequences: dims.batch = S sequences, dims.seqlen = T total
+    tokens; cu_seqlens is a device int32 tensor of S + 1 offsets."""
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        S, T, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
+        _check("cu_seqlens", cu_seqlens, (S + 1,), torch.int32)
+        _check("x", x, (T, H, P, R), ti)
+        _check("dt", dt, (T, H), ti)
+        _check("A", A, (T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
+        _check("lam", lam, (T, H), ti)
+        _check("theta", theta, (T, G, N // 2), ti)
+        _check("B", B, (T, G, N, R), ti)
+        _check("C", C, (T, G, N, R), ti)
+        _check("h0", h0, (S, H, P, N), torch.float32, optional=True)
+        _check("x_prev", x_prev, (S, H, P, R), ti, optional=True)
+        _check("B_prev", B_prev, (S, G, N, R), ti, optional=True)
+        _check("y", y, (T, H, P, R), to)
+        _check("hT", hT, (S, H, P, N), torch.float32, optional=True)
+    nbytes = 0
+    if ws is not None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous device tensor")
+        nbytes = ws.numel() * ws.element_size()
+    st = _lib().m3_scan_prefill_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(x), _ptr(dt),
+                                       _ptr(A), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
+                                       _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(hT),
+                                       _ptr(ws), nbytes, _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_prefill_varlen")
+
+
 def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t,
                    theta_t, y_t, stream=None) -> None:
     d = dims
@@ -235,11 +278,30 @@ def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
     return y, hT
 
 
-def workspace(dims: m3_dims, device) -> torch.Tensor:
-    n = m3_prefill_workspace_size(dims)
+def workspace(dims: m3_dims, device, varlen=False) -> torch.Tensor:
+    n = (m3_prefill_varlen_workspace_size if varlen else m3_prefill_workspace_size)(dims)
     if n == 0:
         raise M3Error(2, "m3_prefill_workspace_size")
     return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=None,
+                        B_prev=None, chunk=0, out_dtype=torch.float32, flags=0, want_hT=True,
+                        ws=None, stream=None):
+    """Allocate y (and hT, workspace) and call m3_scan_prefill_varlen on
+    sequences packed into x [T, H, P, R].  Returns (y, hT)."""
+    T, H, P, R = x.shape
+    G, N = B.shape[1], B.shape[2]
+    S = cu_seqlens.numel() - 1
+    d = make_dims(S, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
+                  0 if G == H else G)
+    y = torch.empty((T, H, P, R), dtype=out_dtype, device=x.device)
+    hT = torch.empty((S, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
+    if ws is None:
+        ws = workspace(d, x.device, varlen=True)
+    m3_scan_prefill_varlen(d, cu_seqlens, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y,
+                           hT, ws, stream)
+    return y, hT
 
 
 def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=None,

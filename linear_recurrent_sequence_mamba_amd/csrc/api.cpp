@@ -115,6 +115,67 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   return hip_status(err);
 }
 
+size_t m3_prefill_varlen_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true) != M3_OK) return 0;
+  return m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
+                                            chunk_of(d));
+}
+
+m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, const void* x,
+                                 const void* dt, const float* A, const void* lam,
+                                 const void* theta, const void* B, const void* C,
+                                 const float* h0, const void* x_prev, const void* B_prev, void* y,
+                                 float* hT, void* ws, size_t ws_bytes, void* stream) {
+  m3_status st = check_dims(d, true);
+  if (st != M3_OK) return st;
+  if (!cu_seqlens || !x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
+  const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return M3_ERR_ALIGN;
+  const int Q = chunk_of(d);
+  const int in_bf16 = d->in_dtype == M3_BF16;
+  if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16) ||
+      !m3::prefill_offsets_fit(d->nheads, d->headdim, d->dstate, d->rank))
+    return M3_ERR_UNSUPPORTED;
+  const size_t need = m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads,
+                                                         d->headdim, d->dstate, Q);
+  if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
+
+  m3::PrefillArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.B = B;
+  a.C = C;
+  a.h0 = h0;
+  a.xp = x_prev;
+  a.Bp = B_prev;
+  a.y = y;
+  a.hT = hT;
+  a.Bsz = d->batch;
+  a.T = d->seqlen;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.N = d->dstate;
+  a.R = d->rank;
+  a.Q = Q;
+  a.nchunk = static_cast<int>(m3::varlen_slots(d->batch, d->seqlen, Q));
+  a.G = groups_of(d);
+  a.flags = d->flags;
+  a.has_prev = x_prev != nullptr;
+  m3::prefill_varlen_carve(a, ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = m3::launch_varlen_map(a, cu_seqlens, s);
+  if (err != hipSuccess) return hip_status(err);
+  if (m3::launch_prefill(a, in_bf16, d->out_dtype == M3_BF16, s, &err) != 0)
+    return M3_ERR_UNSUPPORTED;
+  return hip_status(err);
+}
+
 m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void* x_prev,
                          const void* B_t, const void* B_prev, const void* C_t, const void* dt_t,
                          const float* A, const void* lam_t, const void* theta_t, void* y_t,

@@ -56,6 +56,12 @@ struct PrefillArgs {
   float* S;        // [Bsz, H, nchunk, P, N]: chunk end states, then chunk entry states
   float* rot_end;  // [Bsz, H, nchunk, N/2, 2]: cos/sin of each chunk's total phase
   float* decay;    // [Bsz, H, nchunk]: exp of each chunk's total log-decay
+  // packed sequences (null for [Bsz, T] inputs): the token rows are one
+  // [T, ...] array holding Bsz sequences back to back; nchunk is then the
+  // number of chunk slots per head, and the two tables are built on the
+  // device from the caller's sequence offsets
+  int4* seqs;      // [Bsz]: {first slot, chunks, first token, length}
+  int4* cmap;      // [nchunk]: {sequence, first token, end token, chunk}, sequence -1 = unused
   int Bsz, T, H, P, N, R, Q, nchunk;
   int G;           // groups sharing B, C and theta (G divides H)
   uint32_t flags;
@@ -63,8 +69,16 @@ struct PrefillArgs {
 };
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16);
+bool prefill_offsets_fit(int H, int P, int N, int R);
 size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q);
 void prefill_carve(PrefillArgs& a, void* ws);
+// packed sequences: chunk slots per head (an upper bound of the chunk count
+// for any split of T tokens into Bsz sequences), workspace and carve-up
+int64_t varlen_slots(int Bsz, int T, int Q);
+size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q);
+void prefill_varlen_carve(PrefillArgs& a, void* ws);
+// builds seqs and cmap from the sequence offsets cu [Bsz + 1] (device)
+hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s);
 // returns 0 when launched (err = first launch error), -1 when no kernel fits
 int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16,
                    hipStream_t s, hipError_t* err);

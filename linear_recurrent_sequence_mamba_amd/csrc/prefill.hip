@@ -369,6 +369,35 @@ __device__ __forceinline__ int64_t group_index(const PrefillArgs& a, int b, int 
   return ((int64_t)b * a.T + t) * a.G + head_group(a, h);
 }
 
+// One chunk of the scan: tokens [t0, t0 + Lc) of token row bt, its slot in
+// the workspace, and whether its sequence goes on after it.  [Bsz, T]
+// inputs: chunk c of batch row b.  Packed sequences: chunk slot c of the
+// slot table (row 0 of a [1, T] array), which may be unused.
+struct ChunkRef {
+  int bt, t0, Lc;
+  bool next;
+  int64_t id;
+};
+__device__ __forceinline__ bool chunk_ref(const PrefillArgs& a, int c, int h, int b, ChunkRef& r) {
+  if (c >= a.nchunk) return false;   // grid padding
+  if (a.cmap) {
+    const int4 e = a.cmap[c];
+    if (e.x < 0) return false;
+    r.bt = 0;
+    r.t0 = e.y;
+    r.Lc = min(kQ, e.z - e.y);
+    r.next = e.y + kQ < e.z;
+    r.id = (int64_t)h * a.nchunk + c;
+  } else {
+    r.bt = b;
+    r.t0 = c * kQ;
+    r.Lc = min(kQ, a.T - r.t0);
+    r.next = c + 1 < a.nchunk;
+    r.id = ((int64_t)b * a.H + h) * a.nchunk + c;
+  }
+  return true;
+}
+
 // Raw 16-byte vectors of eight input elements, held in registers between
 // the load that is issued early and the store into LDS.
 template <typename TI>
@@ -706,13 +735,14 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   __shared__ K1Smem<Pol, TI, P, N, R> sm;
   constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
   constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int c0 = c * kQ;
-  const int Lc = min(kQ, a.T - c0);
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
   const int rows = Lc * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
+  const int64_t chunk_id = ck.id;
 
   // every load goes out first (the load counter retires in order): phase
   // inputs and token scalars, then all u-blocks of B and x, so that the
@@ -778,7 +808,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   float bpn = 0.0f;
   const TI* xe = nullptr;
   const TI* Be = nullptr;
-  if (c + 1 < a.nchunk) {
+  if (ck.next) {
     const int64_t nx = token_index(a, b, c0 + kQ, h);
     const float d = ld1(static_cast<const TI*>(a.dt), nx);
     const float l = ld1(static_cast<const TI*>(a.lam), nx);
@@ -831,7 +861,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
 }
 
 // --------------------------------------------------------------------------
-// K2: serial pass over the chunks of one (batch, head).  Entering chunk c
+// K2: serial pass over the chunks of one (batch, head) or (sequence, head).  Entering chunk c
 // the state (plus that chunk's left-endpoint term) is Shat_c;
 // Shat_{c+1} = decay_c R(Phi_end,c) Shat_c + S_c, where S_c already carries
 // the next chunk's left-endpoint term.  Shat_c replaces S_c in the
@@ -848,11 +878,26 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
   const int vi = (blockIdx.x % wpb) * 64 + threadIdx.x;
   const int b = bh / a.H, h = bh % a.H;
   const int p = vi / (N / 4), n = 4 * (vi % (N / 4));
+  // this sequence's chunks are workspace slots cbase .. cbase + nch - 1
+  int64_t cbase, t0;
+  int nch;
+  bool any;
+  if (a.seqs) {
+    const int4 q = a.seqs[b];
+    cbase = (int64_t)h * a.nchunk + q.x;
+    nch = q.y;
+    t0 = token_index(a, 0, q.z, h);
+    any = q.w > 0;
+  } else {
+    cbase = (int64_t)bh * a.nchunk;
+    nch = a.nchunk;
+    t0 = token_index(a, b, 0, h);
+    any = true;
+  }
 
   f4 S = f4{0, 0, 0, 0};
   if (a.h0) S = *reinterpret_cast<const f4*>(a.h0 + ((int64_t)bh * P + p) * N + n);
-  if (a.has_prev) {  // left-endpoint term of token 0
-    const int64_t t0 = token_index(a, b, 0, h);
+  if (a.has_prev && any) {  // left-endpoint term of token 0
     const float d = ld1(static_cast<const TI*>(a.dt), t0);
     const float l = ld1(static_cast<const TI*>(a.lam), t0);
     const float bp0 = (1.0f - l) * d;
@@ -867,8 +912,6 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
       S.w += xv * ld1(Bh, (int64_t)(n + 3) * R + r);
     }
   }
-  const int64_t cbase = (int64_t)bh * a.nchunk;
-  const int nch = a.nchunk;
   const int64_t off = (int64_t)p * N + n;
   f4 bs[D];
   f2 br0[D], br1[D];
@@ -963,17 +1006,17 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
     c = blockIdx.x;
     half = 0;
   }
-  if (c >= a.nchunk) return;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int c0 = c * kQ;
-  const int Lc = min(kQ, a.T - c0);
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, c, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
   const int rows = Lc * R;
   const int v0 = half * G::BROWS;           // this block's rows: [v0, vend)
   if (v0 >= rows) return;
   const int vend = min(rows, v0 + G::BROWS);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t chunk_id = ((int64_t)b * a.H + h) * a.nchunk + c;
+  const int64_t chunk_id = ck.id;
   // this wave's tile; with 8 waves, waves w and w + 4 share a SIMD and take
   // tiles w and 7 - w, which evens out the causal work per SIMD
   const int lt = (G::NW == 8) ? (wave < 4 ? wave : 11 - wave) : wave;
@@ -1152,7 +1195,9 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
 template <class Pol, typename TI, typename TO, int P, int N, int R>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   using G1 = Geo<P, N, R, 8>;
-  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, a.Bsz), dim3(G1::NT), 0, s, a);
+  // packed sequences: one row of chunk slots per head
+  const int nz = a.cmap ? 1 : a.Bsz;
+  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, nz), dim3(G1::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
@@ -1162,7 +1207,7 @@ static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   using G3 = Geo3<P, N, R>;
   // a split chunk's blocks are 8 apart in launch order: pad to whole groups of 8
   const int nx = G3::SPLIT == 1 ? a.nchunk : G3::SPLIT * ((a.nchunk + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(G3::NT), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(nx, a.H, nz), dim3(G3::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1216,10 +1261,119 @@ void prefill_carve(PrefillArgs& a, void* ws) {
   a.decay = reinterpret_cast<float*>(p);
 }
 
-int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16, hipStream_t s, hipError_t* e) {
+// --------------------------------------------------------------------------
+// Packed sequences.  The caller's offsets cu[0..S] are read once on the
+// device and made safe: each is clamped into [0, T] and raised to the
+// largest offset before it, so the sequences are disjoint, ordered ranges
+// of the T token rows whatever the array holds (rows outside every range
+// are not written).  Sequence s has ceil(len_s / Q) chunks; its chunks take
+// consecutive slots from first_s = sum of the earlier counts.
+
+int64_t varlen_slots(int Bsz, int T, int Q) {
+  // every chunk holds >= 1 token, and ceil(len / Q) <= (len + Q - 1) / Q
+  return std::min<int64_t>(T, ((int64_t)T + (int64_t)Bsz * (Q - 1)) / Q);
+}
+
+size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q) {
+  const size_t units = (size_t)H * varlen_slots(Bsz, T, Q);
+  return align256(units * P * N * 4) + align256(units * N * 4) + align256(units * 4) +
+         align256((size_t)Bsz * sizeof(int4)) + align256((size_t)varlen_slots(Bsz, T, Q) * sizeof(int4));
+}
+
+void prefill_varlen_carve(PrefillArgs& a, void* ws) {
+  const size_t units = (size_t)a.H * a.nchunk;
+  char* p = static_cast<char*>(ws);
+  a.S = reinterpret_cast<float*>(p);
+  p += align256(units * a.P * a.N * 4);
+  a.rot_end = reinterpret_cast<float*>(p);
+  p += align256(units * a.N * 4);
+  a.decay = reinterpret_cast<float*>(p);
+  p += align256(units * 4);
+  a.seqs = reinterpret_cast<int4*>(p);
+  p += align256((size_t)a.Bsz * sizeof(int4));
+  a.cmap = reinterpret_cast<int4*>(p);
+}
+
+// inclusive block scans over 1024 threads (sixteen waves)
+template <class Op>
+__device__ __forceinline__ int block_scan(int v, int* wtot, Op op) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v = op(v, o);
+  }
+  if (lane == 63) wtot[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v = op(v, wtot[w]);
+  __syncthreads();   // wtot is reused by the next scan
+  return v;
+}
+
+// seqs[s] = {first slot, chunks, first token, length}: one block of 1024
+// threads walks the offsets in tiles, carrying the running maximum offset
+// and the running chunk count from tile to tile
+__global__ __launch_bounds__(1024) void k_varlen_seqs(const int32_t* __restrict__ cu, int S, int T,
+                                                      int4* __restrict__ seqs) {
+  __shared__ int wtot[16];
+  __shared__ int edge[1025];
+  __shared__ int tile_sum;
+  const int tid = threadIdx.x;
+  int carry_max = 0, carry_sum = 0;
+  for (int base = 0; base <= S; base += 1024) {
+    const int i = base + tid;
+    const int v = i <= S ? min(max(cu[i], 0), T) : 0;
+    const int m = max(block_scan(v, wtot, [](int x, int y) { return max(x, y); }), carry_max);
+    edge[tid + 1] = m;
+    if (tid == 0) edge[0] = carry_max;
+    __syncthreads();
+    const bool is_seq = i >= 1 && i <= S;   // offset i closes sequence i - 1
+    const int len = is_seq ? edge[tid + 1] - edge[tid] : 0;
+    const int nch = (len + kQ - 1) / kQ;
+    const int incl = block_scan(nch, wtot, [](int x, int y) { return x + y; });
+    if (is_seq) seqs[i - 1] = int4{carry_sum + incl - nch, nch, edge[tid], len};
+    if (tid == 1023) tile_sum = incl;
+    __syncthreads();
+    carry_max = edge[1024];
+    carry_sum += tile_sum;
+    __syncthreads();   // edge and tile_sum are rewritten by the next tile
+  }
+}
+
+// cmap[j] for every slot j: the sequence whose chunks cover slot j (the
+// last one starting at or before j) or -1 past the last chunk
+__global__ __launch_bounds__(256) void k_varlen_slots(const int4* __restrict__ seqs, int S, int nslot,
+                                                      int4* __restrict__ cmap) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= nslot) return;
+  int lo = 0, hi = S;   // seqs[lo].x <= j (seqs[0].x = 0); hi = S or seqs[hi].x > j
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (seqs[mid].x <= j) lo = mid;
+    else hi = mid;
+  }
+  const int4 q = seqs[lo];
+  const int c = j - q.x;
+  cmap[j] = c < q.y ? int4{lo, q.z + c * kQ, q.z + q.w, c} : int4{-1, 0, 0, 0};
+}
+
+hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s) {
+  hipLaunchKernelGGL(k_varlen_seqs, dim3(1), dim3(1024), 0, s, cu, a.Bsz, a.T, a.seqs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_varlen_slots, dim3((a.nchunk + 255) / 256), dim3(256), 0, s, a.seqs, a.Bsz,
+                     a.nchunk, a.cmap);
+  return hipGetLastError();
+}
+
+bool prefill_offsets_fit(int H, int P, int N, int R) {
   // in-chunk element offsets are 32-bit: Q tokens of the widest per-token row
-  const int64_t row = (int64_t)a.H * std::max(a.N, a.P) * a.R;
-  if ((int64_t)kQ * row >= (int64_t(1) << 31)) return -1;
+  const int64_t row = (int64_t)H * std::max(N, P) * R;
+  return (int64_t)kQ * row < (int64_t(1) << 31);
+}
+
+int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16, hipStream_t s, hipError_t* e) {
+  if (!prefill_offsets_fit(a.H, a.P, a.N, a.R)) return -1;
   if (in_bf16) {
     return out_bf16 ? dispatch_shape<PolF16, bf16_t, bf16_t>(a, s, e)
                     : dispatch_shape<PolF16, bf16_t, float>(a, s, e);

@@ -61,6 +61,49 @@ WORKLOADS = {
 }
 
 
+# Packed serving mixes: the two prefill shapes with their tokens split into
+# sequences whose lengths are drawn uniformly from 1..4096 (the article's
+# Table 7 times prompts of 512 to 16384 tokens; this draw averages about
+# 2048 and leaves almost every sequence with a ragged last chunk).
+PACKED = {
+    "siso_prefill_varlen": (Workload("siso_prefill_varlen", 5, 1, 8192, 32, 64, 128, 1, 64, "bf16",
+                                     "zero"), 4096),
+    "mimo_prefill_varlen": (Workload("mimo_prefill_varlen", 6, 1, 16384, 64, 64, 128, 4, 64, "bf16",
+                                     "zero"), 4096),
+}
+
+
+def packed_lengths(w: Workload, max_len: int) -> list:
+    """Sequence lengths U{1..max_len} from ``default_rng([cfg_id, 0x1E5])``
+    until they fill w.seqlen tokens (the last one is cut to fit)."""
+    rng = np.random.default_rng([w.cfg_id, 0x1E5])
+    out, left = [], w.seqlen
+    while left > 0:
+        n = min(int(rng.integers(1, max_len + 1)), left)
+        out.append(n)
+        left -= n
+    return out
+
+
+def packed_inputs(w: Workload, lengths, stream: int = 0, h0: str | None = None,
+                  with_prev: bool = False) -> dict:
+    """Inputs of a packed-sequence prefill: the token arrays of ``w`` (batch
+    1, seqlen = sum(lengths)) without their batch axis, the offsets
+    ``cu_seqlens`` (int32, len(lengths) + 1), and one h0 / x_prev / B_prev row
+    per sequence.  Lengths may be 0."""
+    assert w.batch == 1 and sum(lengths) == w.seqlen
+    tok = prefill_inputs(w, stream=stream)
+    out = {k: v[0] for k, v in tok.items() if k not in ("A", "h0", "x_prev", "B_prev")}
+    out["A"] = tok["A"]
+    per = prefill_inputs(w.with_(batch=len(lengths), seqlen=1), stream=stream + 500, h0=h0,
+                         with_prev=with_prev)
+    for k in ("h0", "x_prev", "B_prev"):
+        out[k] = per[k]
+    out["cu_seqlens"] = torch.from_numpy(
+        np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32))
+    return out
+
+
 def _softplus(v):
     return np.logaddexp(np.float32(0.0), v).astype(np.float32)
 

@@ -22,8 +22,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("m3_scan_prefill", "m3_decode_step", "m3_decode_tokens",
-              "m3_prefill_workspace_size", "m3_status_str", "m3_last_hip_error"):
+    for n in ("m3_scan_prefill", "m3_scan_prefill_varlen", "m3_decode_step",
+              "m3_decode_tokens", "m3_prefill_workspace_size",
+              "m3_prefill_varlen_workspace_size", "m3_status_str", "m3_last_hip_error"):
         assert n in names, names
 
 
@@ -69,6 +70,13 @@ def _prefill(d, ws_bytes=1 << 40, **over):
     return m3.library().m3_scan_prefill(ctypes.byref(d), *args.values(), ws_bytes, None)
 
 
+def _varlen(d, ws_bytes=1 << 40, **over):
+    args = dict(cu=P16, x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None,
+                Bp=None, y=P16, hT=None, ws=P16)
+    args.update(over)
+    return m3.library().m3_scan_prefill_varlen(ctypes.byref(d), *args.values(), ws_bytes, None)
+
+
 def test_workspace_size():
     d = _dims(batch=4, seqlen=2048, nheads=32)
     n = m3.m3_prefill_workspace_size(d)
@@ -78,7 +86,7 @@ def test_workspace_size():
     assert m3.library().m3_prefill_workspace_size(None) == 0
 
 
-@pytest.mark.parametrize("call", [_decode, _tokens, _prefill])
+@pytest.mark.parametrize("call", [_decode, _tokens, _prefill, _varlen])
 def test_error_paths(call):
     assert m3.library().m3_decode_step(None, *([None] * 12)) == 1
     assert call(_dims(), x=None) == 1                           # NULL input
@@ -111,6 +119,30 @@ def test_prefill_specific_errors():
     assert _prefill(_dims(), ws_bytes=need - 1) == 6
     assert _prefill(_dims(), ws=P_MIS) == 5
     assert _prefill(_dims(), hT=P_MIS) == 5
+
+
+def test_varlen_specific_errors():
+    assert _varlen(_dims(), cu=None) == 1
+    assert _varlen(_dims(), cu=ctypes.c_void_p(4098)) == 5      # offsets are int32
+    assert _varlen(_dims(seqlen=0)) == 2
+    assert _varlen(_dims(chunk=32)) == 4
+    assert _varlen(_dims(), ws=None) == 6
+    need = m3.m3_prefill_varlen_workspace_size(_dims())
+    assert _varlen(_dims(), ws_bytes=need - 1) == 6
+
+
+def test_varlen_workspace_size():
+    # S sequences over T tokens take at most min(T, (T + 63 S) / 64) chunks;
+    # the per-chunk state (P N fp32) dominates the workspace
+    for S, T in ((1, 100), (7, 100), (300, 100), (5, 64 * 40)):
+        d = _dims(batch=S, seqlen=T, nheads=3)
+        slots = min(T, (T + 63 * S) // 64)
+        n = m3.m3_prefill_varlen_workspace_size(d)
+        assert 3 * slots * 64 * 128 * 4 <= n <= 3 * slots * (64 * 128 + 129) * 4 + 16 * (S + slots) + 1280
+    assert m3.m3_prefill_varlen_workspace_size(_dims(dstate=7)) == 0
+    # one sequence needs as many chunks as the dense call
+    assert m3.m3_prefill_varlen_workspace_size(_dims(batch=1)) >= \
+        m3.m3_prefill_workspace_size(_dims(batch=1))
 
 
 def test_binding_rejects_mismatched_tensors():
