@@ -37,7 +37,9 @@
  * token; pairs are adjacent columns (2k, 2k+1); the state is multiplied by
  * e^{+i phi}; the token before t = 0 is x_prev/B_prev (zero when NULL);
  * A is per head unless M3REF_A_PER_TOKEN; dt and lam arrive already
- * activated; no skip term, gate or normalisation is applied.
+ * activated; no skip term or gate is applied, and B and C enter the
+ * recurrence as given (m3ref_bc_prep below prepares them when the
+ * normalisation and bias of section 2 are wanted).
  *
  * Layouts (dense, row-major, last index fastest):
  *   x      [Bsz, T, H, P, R]      B, C  [Bsz, T, H, N, R]
@@ -194,6 +196,48 @@ int m3ref_decode_step(const m3ref_dims* d, double* h, const double* x_t,
                 B_t + u * N * R, C_t + u * N * R, dt_t[u], a, lam_t[u],
                 theta_t + u * (N / 2), y_t + u * P * R);
   }
+  return 0;
+}
+
+/*
+ * Preparation of B and C for the recurrence [the same article, section 2:
+ * B and C go through an RMS normalisation, the way attention normalises Q
+ * and K, and then get a learned bias per head and per channel].  For each
+ * row (one token of one batch), each head h of group g = h / (H / G) and
+ * each rank column r:
+ *   rms = sqrt( (1/N) sum_n in[g][n][r]^2 + eps )          (when rms_on)
+ *   out[h][n][r] = w[n] * in[g][n][r] / rms + bias[h][n][r]
+ * With rms_on == 0 the division is skipped; w NULL means 1, bias NULL
+ * means 0.  Readings: the normalisation runs over the N state channels of
+ * one rank column; the weight has one value per channel, shared by heads
+ * and ranks; the bias is per head (so heads of one group differ after it)
+ * and is added after the normalisation and the weight.
+ * Layouts: in [rows, G, N, R], w [N], bias [H, N, R], out [rows, H, N, R].
+ */
+int m3ref_bc_prep(int64_t rows, int64_t G, int64_t H, int64_t N, int64_t R,
+                  const double* in, const double* w, const double* bias,
+                  double eps, int rms_on, double* out) {
+  if (rows < 0 || G <= 0 || H <= 0 || H % G != 0 || N <= 0 || R <= 0 || !in || !out)
+    return 1;
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / G);
+      const double* v = in + (i * G + g) * N * R;
+      double* o = out + (i * H + h) * N * R;
+      for (int64_t r = 0; r < R; ++r) {
+        double scale = 1.0;
+        if (rms_on) {
+          double ms = 0.0;
+          for (int64_t n = 0; n < N; ++n) ms += v[n * R + r] * v[n * R + r];
+          scale = 1.0 / sqrt(ms / (double)N + eps);
+        }
+        for (int64_t n = 0; n < N; ++n) {
+          const double wn = w ? w[n] : 1.0;
+          const double bn = bias ? bias[(h * N + n) * R + r] : 0.0;
+          o[n * R + r] = wn * v[n * R + r] * scale + bn;
+        }
+      }
+    }
   return 0;
 }
 

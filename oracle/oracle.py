@@ -57,6 +57,9 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.m3ref_scan.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 12 + [ctypes.c_int]
     lib.m3ref_decode_step.restype = ctypes.c_int
     lib.m3ref_decode_step.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 11 + [ctypes.c_int]
+    lib.m3ref_bc_prep.restype = ctypes.c_int
+    lib.m3ref_bc_prep.argtypes = [ctypes.c_int64] * 5 + [dp] * 3 + [ctypes.c_double,
+                                                                    ctypes.c_int, dp]
     lib.m3ref_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -120,6 +123,23 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t,
     if rc:
         raise ValueError("m3ref_decode_step rejected its arguments (code %d)" % rc)
     return y, h
+
+
+def bc_prep(v, nheads, weight=None, bias=None, eps=1e-6, rms=True, lib_path: str = _LIB):
+    """B or C as the recurrence sees them after the section-2 preparation:
+    v [..., G, N, R] (one slot per head group) -> [..., H, N, R], each head
+    normalised over N per rank column, scaled by weight [N] and offset by its
+    own bias [H, N, R] (see m3ref_bc_prep)."""
+    lib = load(lib_path)
+    v = _f64(v)
+    *lead, G, N, R = v.shape
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.zeros(tuple(lead) + (nheads, N, R), np.float64)
+    rc = lib.m3ref_bc_prep(rows, G, nheads, N, R, _ptr(v), _ptr(_f64(weight)),
+                           _ptr(_f64(bias)), float(eps), int(bool(rms)), _ptr(out))
+    if rc:
+        raise ValueError("m3ref_bc_prep rejected its arguments (code %d)" % rc)
+    return out
 
 
 def max_threads(lib_path: str = _LIB) -> int:

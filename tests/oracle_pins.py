@@ -358,7 +358,64 @@ def check_a_per_token(lib):
     _close(r2.y, r1.y, tol=0.0, what="A per token y")
 
 
+# ---------------------------------------------------------------------------
+# B/C preparation (RMS normalisation, weight, per-head bias)
+def _bc_case(seed, rows=3, G=2, H=4, N=8, R=3):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, G, N, R)) * rng.uniform(0.2, 5.0, size=(rows, G, 1, R))
+    w = rng.uniform(0.5, 2.0, size=N)
+    bias = rng.standard_normal((H, N, R)) * 3.0
+    return v, w, bias
+
+
+def check_bc_prep_unit_rms(lib):
+    """With weight 1, no bias and eps 0, every (row, head, rank column) comes
+    out with mean square exactly 1 over N, as a positive multiple of its input
+    column: what an RMS normalisation over the state channels is."""
+    v, _, _ = _bc_case(30)
+    out = oracle.bc_prep(v, 4, eps=0.0, lib_path=lib)
+    _close(np.mean(out ** 2, axis=-2), np.ones(out.shape[:-2] + out.shape[-1:]), tol=1e-13,
+           what="mean square over N")
+    vg = np.repeat(v, 2, axis=1)                      # group g serves heads 2g, 2g + 1
+    ratio = out / vg
+    assert np.all(ratio > 0), "direction of the column"
+    _close(ratio, np.broadcast_to(ratio[..., :1, :], ratio.shape), tol=1e-13, what="one factor per column")
+
+
+def check_bc_prep_scale_invariance(lib):
+    """Scaling one rank column of one token by c > 0 changes nothing (eps 0):
+    the normalisation runs per column, not over the whole N x R block."""
+    v, w, bias = _bc_case(31)
+    base = oracle.bc_prep(v, 4, w, bias, eps=0.0, lib_path=lib)
+    v2 = v.copy()
+    v2[1, 0, :, 2] *= 7.5
+    v2[2, 1, :, 0] *= 0.01
+    _close(oracle.bc_prep(v2, 4, w, bias, eps=0.0, lib_path=lib), base, tol=1e-13,
+           what="per-column scale invariance")
+
+
+def check_bc_prep_bias_weight_eps(lib):
+    """Zero input columns come out as exactly the bias of each head (heads
+    of one group get their own bias, added after the normalisation); an input
+    c u with u of unit mean square comes out as w c u / sqrt(c^2 + eps) plus
+    the bias (the closed form of the normalisation with eps)."""
+    v, w, bias = _bc_case(32)
+    z = np.zeros_like(v)
+    _close(oracle.bc_prep(z, 4, w, bias, eps=1e-3, lib_path=lib),
+           np.broadcast_to(bias, (3, 4, 8, 3)), tol=0.0, what="zero input gives the head's bias")
+    u = v / np.sqrt(np.mean(v ** 2, axis=-2, keepdims=True))
+    c, eps = 0.3, 0.05
+    got = oracle.bc_prep(c * u, 4, w, bias, eps=eps, lib_path=lib)
+    ug = np.repeat(u, 2, axis=1)
+    want = w[:, None] * c * ug / math.sqrt(c * c + eps) + bias
+    _close(got, want, tol=1e-13, what="closed form with eps")
+    # without the normalisation only the weight and bias act
+    _close(oracle.bc_prep(v, 4, w, None, rms=False, lib_path=lib),
+           w[:, None] * np.repeat(v, 2, axis=1), tol=0.0, what="weight alone")
+
+
 ALL_CHECKS = [check_euler_special_case, check_complex_form, check_rope_frame,
               check_unrolled, check_closed_form, check_parity, check_second_order,
               check_mimo_sum_of_siso, check_split_and_decode,
-              check_linearity_and_independence, check_a_per_token]
+              check_linearity_and_independence, check_a_per_token, check_bc_prep_unit_rms,
+              check_bc_prep_scale_invariance, check_bc_prep_bias_weight_eps]

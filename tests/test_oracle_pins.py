@@ -83,6 +83,13 @@ MUTANTS = {
                            "const double im = S[p * N + 2 * k], re = S[p * N + 2 * k + 1];"),
     "decay_sign": ("exp(dt * A)", "exp(-dt * A)"),
     "prev_not_advanced": ("      xp = xt;\n      bp = bt;\n", "\n"),
+    "bc_sum_not_mean": ("sqrt(ms / (double)N + eps)", "sqrt(ms + eps)"),
+    "bc_eps_outside_sqrt": ("1.0 / sqrt(ms / (double)N + eps)", "1.0 / (sqrt(ms / (double)N) + eps)"),
+    "bc_bias_by_group": ("bias[(h * N + n) * R + r]", "bias[(g * N + n) * R + r]"),
+    "bc_bias_inside_norm": ("wn * v[n * R + r] * scale + bn;", "wn * (v[n * R + r] + bn) * scale;"),
+    "bc_weight_by_rank": ("w ? w[n] : 1.0", "w ? w[r] : 1.0"),
+    "bc_norm_over_all_ranks": ("for (int64_t n = 0; n < N; ++n) ms += v[n * R + r] * v[n * R + r];",
+                               "for (int64_t n = 0; n < N * R; ++n) ms += v[n] * v[n];"),
 }
 
 
