@@ -73,6 +73,29 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 #define M3_THETA_IS_ANGLE (1u << 0) /* phase phi_t = theta_t, not dt_t*theta_t */
 #define M3_A_PER_TOKEN (1u << 1)    /* A is [Bsz,T,H] fp32 instead of [H]      */
 
+/* Optional preparation of B and C inside the kernels [the same article,
+ * section 2: B and C are RMS-normalised, as attention normalises Q and K,
+ * and get a learned bias per head and channel].  With dims->bc set, every
+ * call reads B_t, C_t and B_prev as the raw projections and uses, for head
+ * h of group g and rank column r,
+ *     B'[n][r] = B_weight[n] * B[g][n][r] / rms_r + B_bias[h][n][r],
+ *     rms_r    = sqrt(mean over n of B[g][n][r]^2 + eps)   (rms != 0; else 1)
+ * and the same for C, before the phase rotation.  Readings: the
+ * normalisation runs over the N channels of each rank column; the weight is
+ * per channel, shared by heads and ranks; the bias is per head, so heads
+ * that share a group's B and C differ after it.  All four arrays are
+ * optional DEVICE pointers (NULL: weight 1, bias 0), 16-byte aligned.  A
+ * raw column of zeros with eps = 0 gives NaN.  eps must be finite and >= 0
+ * (else M3_ERR_SHAPE). */
+typedef struct {
+  const float* B_weight; /* [N] fp32 or NULL                               */
+  const float* C_weight; /* [N] fp32 or NULL                               */
+  const float* B_bias;   /* [H, N, R] fp32 or NULL                         */
+  const float* C_bias;   /* [H, N, R] fp32 or NULL                         */
+  float eps;             /* added to the mean square                       */
+  int32_t rms;           /* nonzero: RMS-normalise over N                  */
+} m3_bc_prep;
+
 typedef struct {
   int32_t batch;     /* Bsz >= 1                                           */
   int32_t seqlen;    /* T >= 1 (ignored by the decode step)                */
@@ -85,6 +108,7 @@ typedef struct {
   int32_t out_dtype; /* m3_dtype of y                                      */
   uint32_t flags;    /* M3_THETA_IS_ANGLE | M3_A_PER_TOKEN                 */
   int32_t ngroups;   /* G, groups sharing B, C, theta; 0 = nheads; G | H   */
+  const m3_bc_prep* bc; /* host pointer; NULL = B and C are used as given */
 } m3_dims;
 
 /* Bytes of device workspace m3_scan_prefill needs for `dims` (0 if dims is

@@ -25,13 +25,41 @@ STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
           4: "M3_ERR_UNSUPPORTED", 5: "M3_ERR_ALIGN", 6: "M3_ERR_WORKSPACE", 7: "M3_ERR_HIP"}
 
 
+class m3_bc_prep(ctypes.Structure):
+    _fields_ = [("B_weight", ctypes.c_void_p), ("C_weight", ctypes.c_void_p),
+                ("B_bias", ctypes.c_void_p), ("C_bias", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("rms", ctypes.c_int32)]
+
+
 class m3_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("ngroups", ctypes.c_int32)]
+                ("ngroups", ctypes.c_int32), ("bc", ctypes.POINTER(m3_bc_prep))]
+
+
+class BCPrep:
+    """The in-kernel preparation of B and C (m3_bc_prep): RMS normalisation
+    over N per rank column, weight [N] and per-head bias [H, N, R], all fp32
+    device tensors or None."""
+
+    def __init__(self, B_weight=None, C_weight=None, B_bias=None, C_bias=None, eps=1e-6,
+                 rms=True):
+        self.B_weight, self.C_weight = B_weight, C_weight
+        self.B_bias, self.C_bias = B_bias, C_bias
+        self.eps, self.rms = float(eps), bool(rms)
+
+    def struct(self) -> m3_bc_prep:
+        return m3_bc_prep(_ptr(self.B_weight), _ptr(self.C_weight), _ptr(self.B_bias),
+                          _ptr(self.C_bias), self.eps, int(self.rms))
+
+    def check(self, H, N, R):
+        for name in ("B_weight", "C_weight"):
+            _check(name, getattr(self, name), (N,), torch.float32, optional=True)
+        for name in ("B_bias", "C_bias"):
+            _check(name, getattr(self, name), (H, N, R), torch.float32, optional=True)
 
 
 class M3Error(RuntimeError):
@@ -88,9 +116,21 @@ def m3_status_str(status: int) -> str:
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, rank=1, chunk=0,
-              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0, ngroups=0) -> m3_dims:
-    return m3_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, in_dtype,
-                   out_dtype, flags, ngroups)
+              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0, ngroups=0, bc=None) -> m3_dims:
+    """bc: a BCPrep (kept alive by the returned dims) or None."""
+    d = m3_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, in_dtype,
+                out_dtype, flags, ngroups)
+    if bc is not None:
+        d._bc_struct = bc.struct()
+        d._bc = bc
+        d.bc = ctypes.pointer(d._bc_struct)
+    return d
+
+
+def _check_bc(d: m3_dims):
+    bc = getattr(d, "_bc", None)
+    if bc is not None:
+        bc.check(d.nheads, d.dstate, d.rank)
 
 
 def groups(d: m3_dims) -> int:
@@ -162,6 +202,7 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
         if not ws.is_cuda or not ws.is_contiguous():
             raise ValueError("ws must be a contiguous device tensor")
         nbytes = ws.numel() * ws.element_size()
+    _check_bc(d)
     st = _lib().m3_scan_prefill(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
                                 _ptr(theta), _ptr(B), _ptr(C), _ptr(h0), _ptr(x_prev),
                                 _ptr(B_prev), _ptr(y), _ptr(hT), _ptr(ws), nbytes,
@@ -201,6 +242,7 @@ def m3_scan_prefill_varlen(dims: m3_dims, cu_seqlens, x, dt, A, lam, theta, B, C
         if not ws.is_cuda or not ws.is_contiguous():
             raise ValueError("ws must be a contiguous device tensor")
         nbytes = ws.numel() * ws.element_size()
+    _check_bc(d)
     st = _lib().m3_scan_prefill_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(x), _ptr(dt),
                                        _ptr(A), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
                                        _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(hT),
@@ -227,6 +269,7 @@ def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam
         _check("lam_t", lam_t, (Bsz, H), ti)
         _check("theta_t", theta_t, (Bsz, G, N // 2), ti)
         _check("y_t", y_t, (Bsz, H, P, R), to)
+    _check_bc(d)
     st = _lib().m3_decode_step(ctypes.byref(d), _ptr(h), _ptr(x_t), _ptr(x_prev), _ptr(B_t),
                                _ptr(B_prev), _ptr(C_t), _ptr(dt_t), _ptr(A), _ptr(lam_t),
                                _ptr(theta_t), _ptr(y_t), _stream(stream))
@@ -252,6 +295,7 @@ def m3_decode_tokens(dims: m3_dims, h, x, x_prev, B, B_prev, C, dt, A, lam, thet
         _check("lam", lam, (Bsz, K, H), ti)
         _check("theta", theta, (Bsz, K, G, N // 2), ti)
         _check("y", y, (Bsz, K, H, P, R), to)
+    _check_bc(d)
     st = _lib().m3_decode_tokens(ctypes.byref(d), _ptr(h), _ptr(x), _ptr(x_prev), _ptr(B),
                                  _ptr(B_prev), _ptr(C), _ptr(dt), _ptr(A), _ptr(lam),
                                  _ptr(theta), _ptr(y), _stream(stream))
@@ -263,13 +307,13 @@ def m3_decode_tokens(dims: m3_dims, h, x, x_prev, B, B_prev, C, dt, A, lam, thet
 # allocation helpers (torch only provides the memory)
 def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
                  chunk=0, out_dtype=torch.float32, flags=0, want_hT=True, ws=None,
-                 stream=None):
+                 stream=None, bc=None):
     """Allocate y (and hT, workspace) and call m3_scan_prefill.  Returns (y, hT).
     B, C and theta may have fewer head slots than x (head groups)."""
     Bsz, T, H, P, R = x.shape
     G, N = B.shape[2], B.shape[3]
     d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G)
+                  0 if G == H else G, bc)
     y = torch.empty((Bsz, T, H, P, R), dtype=out_dtype, device=x.device)
     hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
     if ws is None:
@@ -287,14 +331,14 @@ def workspace(dims: m3_dims, device, varlen=False) -> torch.Tensor:
 
 def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=None,
                         B_prev=None, chunk=0, out_dtype=torch.float32, flags=0, want_hT=True,
-                        ws=None, stream=None):
+                        ws=None, stream=None, bc=None):
     """Allocate y (and hT, workspace) and call m3_scan_prefill_varlen on
     sequences packed into x [T, H, P, R].  Returns (y, hT)."""
     T, H, P, R = x.shape
     G, N = B.shape[1], B.shape[2]
     S = cu_seqlens.numel() - 1
     d = make_dims(S, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G)
+                  0 if G == H else G, bc)
     y = torch.empty((T, H, P, R), dtype=out_dtype, device=x.device)
     hT = torch.empty((S, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
     if ws is None:
@@ -305,14 +349,14 @@ def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=
 
 
 def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=None,
-                out_dtype=torch.float32, flags=0, y_t=None, stream=None):
+                out_dtype=torch.float32, flags=0, y_t=None, stream=None, bc=None):
     """Advance h in place by one token; returns y_t (allocated unless given).
     B_t, C_t and theta_t may have fewer head slots than h (head groups)."""
     Bsz, H, P, N = h.shape
     R = x_t.shape[-1]
     G = B_t.shape[1]
     d = make_dims(Bsz, 1, H, P, N, R, 0, dtype_code(x_t.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G)
+                  0 if G == H else G, bc)
     if y_t is None:
         y_t = torch.empty((Bsz, H, P, R), dtype=out_dtype, device=h.device)
     m3_decode_step(d, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t, stream)
@@ -320,14 +364,14 @@ def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=N
 
 
 def decode_tokens(h, x, B, C, dt, A, lam, theta, x_prev=None, B_prev=None,
-                  out_dtype=torch.float32, flags=0, y=None, stream=None):
+                  out_dtype=torch.float32, flags=0, y=None, stream=None, bc=None):
     """Advance h in place by the K tokens of x ([Bsz, K, H, P, R]); returns y
     ([Bsz, K, H, P, R], allocated unless given)."""
     Bsz, K, H, P, R = x.shape
     N = h.shape[3]
     G = B.shape[2]
     d = make_dims(Bsz, K, H, P, N, R, 0, dtype_code(x.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G)
+                  0 if G == H else G, bc)
     if y is None:
         y = torch.empty((Bsz, K, H, P, R), dtype=out_dtype, device=h.device)
     m3_decode_tokens(d, h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y, stream)

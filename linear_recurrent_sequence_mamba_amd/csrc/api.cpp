@@ -2,6 +2,7 @@
 // workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
 // the host before anything is launched.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/m3ssm.h"
@@ -36,6 +37,25 @@ m3_status check_dims(const m3_dims* d, bool need_seqlen) {
 
 int groups_of(const m3_dims* d) { return d->ngroups > 0 ? d->ngroups : d->nheads; }
 
+// the B/C preparation of dims->bc into kernel arguments (off when absent)
+m3_status bc_args(const m3_dims* d, m3::BCPrep* out) {
+  *out = m3::BCPrep{};
+  const m3_bc_prep* bc = d->bc;
+  if (!bc) return M3_OK;
+  if (!isfinite(bc->eps) || bc->eps < 0.0f) return M3_ERR_SHAPE;
+  const void* ptrs[] = {bc->B_weight, bc->C_weight, bc->B_bias, bc->C_bias};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  out->Bw = bc->B_weight;
+  out->Cw = bc->C_weight;
+  out->Bb = bc->B_bias;
+  out->Cb = bc->C_bias;
+  out->eps = bc->eps;
+  out->rms = bc->rms != 0;
+  out->on = 1;
+  return M3_OK;
+}
+
 int chunk_of(const m3_dims* d) { return d->chunk > 0 ? d->chunk : 64; }
 
 }  // namespace
@@ -61,7 +81,7 @@ int m3_last_hip_error(void) { return g_last_hip_error; }
 size_t m3_prefill_workspace_size(const m3_dims* d) {
   if (check_dims(d, true) != M3_OK) return 0;
   return m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
-                                     chunk_of(d));
+                                     d->rank, chunk_of(d), d->bc != nullptr);
 }
 
 m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
@@ -70,6 +90,8 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
                           float* hT, void* ws, size_t ws_bytes, void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
+  m3::BCPrep bcp;
+  if ((st = bc_args(d, &bcp)) != M3_OK) return st;
   if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
@@ -80,7 +102,7 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16))
     return M3_ERR_UNSUPPORTED;
   const size_t need = m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim,
-                                                  d->dstate, Q);
+                                                  d->dstate, d->rank, Q, bcp.on != 0);
   if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
 
   m3::PrefillArgs a{};
@@ -107,6 +129,7 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   a.G = groups_of(d);
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
+  a.bc = bcp;
   m3::prefill_carve(a, ws);
   hipError_t err = hipSuccess;
   if (m3::launch_prefill(a, in_bf16, d->out_dtype == M3_BF16,
@@ -118,7 +141,7 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
 size_t m3_prefill_varlen_workspace_size(const m3_dims* d) {
   if (check_dims(d, true) != M3_OK) return 0;
   return m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
-                                            chunk_of(d));
+                                            d->rank, chunk_of(d), d->bc != nullptr);
 }
 
 m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, const void* x,
@@ -128,6 +151,8 @@ m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, co
                                  float* hT, void* ws, size_t ws_bytes, void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
+  m3::BCPrep bcp;
+  if ((st = bc_args(d, &bcp)) != M3_OK) return st;
   if (!cu_seqlens || !x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
@@ -140,7 +165,8 @@ m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, co
       !m3::prefill_offsets_fit(d->nheads, d->headdim, d->dstate, d->rank))
     return M3_ERR_UNSUPPORTED;
   const size_t need = m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads,
-                                                         d->headdim, d->dstate, Q);
+                                                         d->headdim, d->dstate, d->rank, Q,
+                                                         bcp.on != 0);
   if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
 
   m3::PrefillArgs a{};
@@ -167,6 +193,7 @@ m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, co
   a.G = groups_of(d);
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
+  a.bc = bcp;
   m3::prefill_varlen_carve(a, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = m3::launch_varlen_map(a, cu_seqlens, s);
@@ -182,6 +209,8 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
                          void* stream) {
   m3_status st = check_dims(d, false);
   if (st != M3_OK) return st;
+  m3::BCPrep bcp;
+  if ((st = bc_args(d, &bcp)) != M3_OK) return st;
   if (!h || !x_t || !B_t || !C_t || !dt_t || !A || !lam_t || !theta_t || !y_t)
     return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
@@ -212,6 +241,7 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
   a.K = 1;
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
+  a.bc = bcp;
   hipError_t err = hipSuccess;
   if (m3::launch_decode(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
                         static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)
@@ -225,6 +255,8 @@ m3_status m3_decode_tokens(const m3_dims* d, float* h, const void* x, const void
                            void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
+  m3::BCPrep bcp;
+  if ((st = bc_args(d, &bcp)) != M3_OK) return st;
   if (!h || !x || !B || !C || !dt || !A || !lam || !theta || !y) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y};
@@ -254,6 +286,7 @@ m3_status m3_decode_tokens(const m3_dims* d, float* h, const void* x, const void
   a.K = d->seqlen;
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
+  a.bc = bcp;
   hipError_t err = hipSuccess;
   if (m3::launch_decode_tokens(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
                                static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)

@@ -68,7 +68,7 @@ __device__ __forceinline__ void token_finish(const DecodeArgs& a, const TokenIn<
 
 // --------------------------------------------------------------------------
 // single input / single output
-template <typename TI, typename TO, int N, bool PREV>
+template <typename TI, typename TO, int N, bool PREV, bool PREP>
 __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   constexpr int LPR = N / 4;           // lanes per state row
   constexpr int RPW = 64 / LPR;        // rows per wave per pass
@@ -92,7 +92,16 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   const int64_t vec = group_slot(a, bh) * N + n0;
   f4 bt = ld4(static_cast<const TI*>(a.Bt), vec);
   f4 bp = PREV ? ld4(static_cast<const TI*>(a.Bp), vec) : f4{0, 0, 0, 0};
-  const f4 ct = ld4(static_cast<const TI*>(a.Ct), vec);
+  f4 ct = ld4(static_cast<const TI*>(a.Ct), vec);
+  // B/C preparation: weight and this head's bias of columns n0..n0+3
+  f4 bw = f4{1, 1, 1, 1}, cw = bw, bb = f4{0, 0, 0, 0}, cb = bb;
+  if constexpr (PREP) {
+    const int64_t hb0 = (int64_t)(bh % a.H) * N + n0;
+    if (a.bc.Bw) bw = ld4(a.bc.Bw, n0);
+    if (a.bc.Cw) cw = ld4(a.bc.Cw, n0);
+    if (a.bc.Bb) bb = ld4(a.bc.Bb, hb0);
+    if (a.bc.Cb) cb = ld4(a.bc.Cb, hb0);
+  }
 
   // the state stream; rows past P are clamped for the loads, masked for the stores
   f4 v[UNR];
@@ -107,6 +116,16 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
 
   float alpha, beta, gamma;
   token_finish<TI, N>(a, tin, alpha, beta, gamma, cs_sh);
+  if constexpr (PREP) {
+    // a row's N/4 lanes hold the whole of B, B_prev and C
+    auto prep = [&](f4 v, f4 w, f4 b) {
+      const float inv = bc_inv_rms(a.bc, group_sum<LPR>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w), N);
+      return v * inv * w + b;
+    };
+    bt = prep(bt, bw, bb);
+    if (PREV) bp = prep(bp, bw, bb);
+    ct = prep(ct, cw, cb);
+  }
   bt *= gamma;
   bp *= beta;
   __syncthreads();
@@ -149,8 +168,11 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
 template <int NT>
 __device__ __forceinline__ int ncol(int t, int g) { return 16 * t + 4 * g; }
 
-template <typename TI, typename TO, int N, int R, bool PREV>
-__global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
+// (the B/C preparation's prologue would otherwise cost the rank <= 4
+// kernels a wave per SIMD: the register count is held to four waves)
+template <typename TI, typename TO, int N, int R, bool PREV, bool PREP>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(DecodeArgs a) {
   constexpr int NT = N / 16;          // 16-column tiles per state row block
   constexpr int KB = (R + 3) / 4;     // K blocks of 4 for the MFMA
   constexpr int RP = (R + 3) & ~3;    // rank padded to a multiple of 4 in LDS
@@ -161,6 +183,7 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
   __shared__ float bt_sh[N * RP];     // gamma * B_t      [n][r]
   __shared__ float c_sh[N * RP];      // C_t              [n][r]
   __shared__ f4 tr_sh[4][16][N / 4 + 1];  // per-wave updated rows (one vector of padding)
+  __shared__ float inv_sh[PREP ? 3 : 1][R];  // B/C preparation: inverse RMS per rank column
 
   const int bh = blockIdx.x;
   const int P = a.P;
@@ -190,6 +213,20 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
       ec[q] = ld1(Ct, ic);
     }
   }
+  // B/C preparation: weight and this head's bias of each element, loaded
+  // before the state stream so that the preparation does not wait for it
+  float wbv[PREP ? PER : 1], wcv[PREP ? PER : 1], bbv[PREP ? PER : 1], cbv[PREP ? PER : 1];
+  if constexpr (PREP) {
+    const int64_t hb0 = (int64_t)(bh % a.H) * NE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int ic = min(tid + 256 * q, NE - 1);
+      wbv[q] = a.bc.Bw ? a.bc.Bw[ic / R] : 1.0f;
+      wcv[q] = a.bc.Cw ? a.bc.Cw[ic / R] : 1.0f;
+      bbv[q] = a.bc.Bb ? a.bc.Bb[hb0 + ic] : 0.0f;
+      cbv[q] = a.bc.Cb ? a.bc.Cb[hb0 + ic] : 0.0f;
+    }
+  }
 
   // the first row block's state stream, row-contiguous (whole 128-byte
   // lines per load instruction); it reaches the D layout through LDS
@@ -211,17 +248,51 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
     for (int i = tid; i < N * RP; i += 256) bt_sh[i] = bp_sh[i] = c_sh[i] = 0.0f;
     __syncthreads();
   }
+  // with the B/C preparation the tables first take the raw rows; waves 0-2
+  // reduce one table each to inverse RMS per rank column, then every
+  // element is normalised, weighted, biased and scaled in place
+  const float sbt = PREP ? 1.0f : gamma, sbp = PREP ? 1.0f : beta;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int i = tid + 256 * q;
     if (i < NE) {
       const int j = (i / R) * RP + i % R;
-      bt_sh[j] = gamma * eb[q];
-      bp_sh[j] = beta * ep[q];
+      bt_sh[j] = sbt * eb[q];
+      bp_sh[j] = sbp * ep[q];
       c_sh[j] = ec[q];
     }
   }
   __syncthreads();
+  if constexpr (PREP) {
+    if (wave < 3 && (wave != 1 || PREV)) {
+      const float* tab = wave == 0 ? bt_sh : (wave == 1 ? bp_sh : c_sh);
+      float part[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[r] = 0.0f;
+      for (int n = lane; n < N; n += 64) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r] += tab[n * RP + r] * tab[n * RP + r];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[r] = group_sum<64>(part[r]);
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) inv_sh[wave][r] = bc_inv_rms(a.bc, part[r], N);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {   // each thread its own elements, from registers
+      const int i = tid + 256 * q;
+      if (i < NE) {
+        const int r = i % R, j = (i / R) * RP + r;
+        bt_sh[j] = gamma * (eb[q] * inv_sh[0][r] * wbv[q] + bbv[q]);
+        if (PREV) bp_sh[j] = beta * (ep[q] * inv_sh[1][r] * wbv[q] + bbv[q]);
+        c_sh[j] = ec[q] * inv_sh[2][r] * wcv[q] + cbv[q];
+      }
+    }
+    __syncthreads();
+  }
 
   for (; pb * 16 < P; pb += 4) {
     const int p = pb * 16 + i16;
@@ -315,19 +386,27 @@ __global__ __launch_bounds__(256) void k_decode_mimo(DecodeArgs a) {
 // --------------------------------------------------------------------------
 template <typename TI, typename TO, int N>
 static hipError_t launch_siso(const DecodeArgs& a, int units, hipStream_t s) {
-  if (a.has_prev)
-    hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true>), dim3(units), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false>), dim3(units), dim3(256), 0, s, a);
+  const dim3 g(units), b(256);
+  if (a.bc.on) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, true>), g, b, 0, s, a);
+  } else {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <typename TI, typename TO, int N, int R>
 static hipError_t launch_mimo(const DecodeArgs& a, int units, hipStream_t s) {
-  if (a.has_prev)
-    hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true>), dim3(units), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false>), dim3(units), dim3(256), 0, s, a);
+  const dim3 g(units), b(256);
+  if (a.bc.on) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, true>), g, b, 0, s, a);
+  } else {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ struct TokScalars {
 }  // namespace
 
 // --------------------------------------------------------------------------
-template <typename TI, typename TO, int N, int UNR, bool PREV>
+template <typename TI, typename TO, int N, int UNR, bool PREV, bool PREP>
 __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
   constexpr int LPR = N / 4;      // lanes per state row
   constexpr int RPW = 64 / LPR;   // rows per wave per pass
@@ -113,9 +113,24 @@ __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < UNR; ++u)
     xo[u] = PREV ? ld1(static_cast<const TI*>(a.xp), (int64_t)bh * P + min(u * RPB + rsub, P - 1)) : 0.0f;
+  // B/C preparation: weight and this head's bias of columns n0..n0+3
+  f4 bw = f4{1, 1, 1, 1}, cw = bw, bbias = f4{0, 0, 0, 0}, cbias = bbias;
+  if constexpr (PREP) {
+    const int64_t hb0 = (int64_t)(bh % a.H) * N + n0;
+    if (a.bc.Bw) bw = ld4(a.bc.Bw, n0);
+    if (a.bc.Cw) cw = ld4(a.bc.Cw, n0);
+    if (a.bc.Bb) bbias = ld4(a.bc.Bb, hb0);
+    if (a.bc.Cb) cbias = ld4(a.bc.Cb, hb0);
+  }
+  // a row's N/4 lanes hold a token's whole B and C
+  auto prep = [&](f4 u, f4 w, f4 b) {
+    const float inv = bc_inv_rms(a.bc, group_sum<LPR>(u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w), N);
+    return u * inv * w + b;
+  };
   f4 v[UNR];
 #pragma unroll
   for (int u = 0; u < UNR; ++u) v[u] = ld4_state(hb + (int64_t)min(u * RPB + rsub, P - 1) * N + n0);
+  if (PREP && PREV) bo = prep(bo, bw, bbias);   // bo always holds a prepared B
 
   for (int k = 0; k < a.K; ++k) {
     // the next token's inputs fly while this one is applied
@@ -140,6 +155,10 @@ __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
     sincosf(ang ? thk.x : dk * thk.x, &s0, &c0);
     sincosf(ang ? thk.y : dk * thk.y, &s1, &c1);
     const f2 r0 = f2{c0, s0}, r1 = f2{c1, s1};
+    if constexpr (PREP) {
+      bk = prep(bk, bw, bbias);
+      ck = prep(ck, cw, cbias);
+    }
     const f4 bt = gamma * bk, bp = beta * bo;
     TO* __restrict__ yk = Y + tok_head(a, bh, k) * P;
 #pragma unroll
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
 // D row 4g + i of tile t is state column 16t + 4g + i (as in the single-step
 // kernel): a lane's accumulator is the 16-byte vector of 4 consecutive
 // columns of its row.
-template <typename TI, typename TO, int N, int R, bool PREV>
+template <typename TI, typename TO, int N, int R, bool PREV, bool PREP>
 __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
   constexpr int NT = N / 16;
   constexpr int KB = (R + 3) / 4;
@@ -198,6 +217,12 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
     Tok tok[2];
     f4 tr[4][16][N / 4 + 1];
   } sm;
+  // B/C preparation: this head's weights and biases ([0] B, [1] C), and
+  // each wave's partial sums of squares per rank column of the B, C and
+  // (first token) B_prev that a table build prepares
+  __shared__ float pw_sh[PREP ? 2 : 1][PREP ? N : 1];
+  __shared__ float pb_sh[PREP ? 2 : 1][PREP ? NE : 1];
+  __shared__ float part_sh[4][3][R];
 
   const int bh = blockIdx.x;
   const int P = a.P;
@@ -231,11 +256,52 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
       xr[kb] = (rows && r < R) ? ld1(src, (int64_t)p * R + r) : 0.0f;
     }
   };
-  // token operands into buffer tb: beta/gamma-scaled B, C, phases
-  auto put_tables = [&](Tok& tb, const TokScalars<TI, N>& sc, const float* eb, const float* eo,
-                        const float* ec) {
+  // token operands into buffer tb: beta/gamma-scaled B, C, phases.  With
+  // the preparation, eb and ec (and eo when prep_prev) are raw on entry and
+  // prepared on return: each wave reduces its elements' squares per rank
+  // column into part_sh, and after a barrier every thread sums the four
+  // waves' parts (the sums' last readers are past the barrier that ends
+  // each token, before the next build writes them).
+  auto put_tables = [&](Tok& tb, const TokScalars<TI, N>& sc, float* eb, float* eo, float* ec,
+                        bool prep_prev) {
     float alpha, beta, gamma;
     sc.finish(a, alpha, beta, gamma, tb.cs);
+    if constexpr (PREP) {
+      auto wave_parts = [&](const float* e, int arr) {
+        float part[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = tid + 256 * q;
+          const float v = i < NE ? e[q] : 0.0f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) part[r] += (i % R == r) ? v * v : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r] = group_sum<64>(part[r]);
+        if (lane == 0) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) part_sh[wave][arr][r] = part[r];
+        }
+      };
+      wave_parts(eb, 0);
+      wave_parts(ec, 2);
+      if (prep_prev) wave_parts(eo, 1);
+      __syncthreads();
+      auto inv = [&](int arr, int r) {
+        return bc_inv_rms(a.bc, part_sh[0][arr][r] + part_sh[1][arr][r] + part_sh[2][arr][r] +
+                                    part_sh[3][arr][r], N);
+      };
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int i = min(tid + 256 * q, NE - 1);
+        const int r = i % R, n = i / R;
+        eb[q] = eb[q] * inv(0, r) * pw_sh[0][n] + pb_sh[0][i];
+        ec[q] = ec[q] * inv(2, r) * pw_sh[1][n] + pb_sh[1][i];
+        if (prep_prev) eo[q] = eo[q] * inv(1, r) * pw_sh[0][n] + pb_sh[0][i];
+      }
+    }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int i = tid + 256 * q;
@@ -289,6 +355,17 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) v[t] = f4{0, 0, 0, 0};
   }
+  if constexpr (PREP) {   // this head's weights and biases (1 and 0 when absent)
+    const int64_t hb0 = (int64_t)(bh % a.H) * NE;
+    for (int i = tid; i < N; i += 256) {
+      pw_sh[0][i] = a.bc.Bw ? a.bc.Bw[i] : 1.0f;
+      pw_sh[1][i] = a.bc.Cw ? a.bc.Cw[i] : 1.0f;
+    }
+    for (int i = tid; i < NE; i += 256) {
+      pb_sh[0][i] = a.bc.Bb ? a.bc.Bb[hb0 + i] : 0.0f;
+      pb_sh[1][i] = a.bc.Cb ? a.bc.Cb[hb0 + i] : 0.0f;
+    }
+  }
   __syncthreads();   // every wave's transpose is read before the tables take the space
   if constexpr (RP != R) {
     for (int i = tid; i < N * RP; i += 256)
@@ -296,7 +373,7 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
           sm.tok[1].c[i] = 0.0f;
     __syncthreads();
   }
-  put_tables(sm.tok[0], sc, eb, eo, ec);
+  put_tables(sm.tok[0], sc, eb, eo, ec, PREV);
   __syncthreads();
 
   for (int k = 0; k < a.K; ++k) {
@@ -368,7 +445,7 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
     sc = scn;
     // token k + 1's operands into the other buffer (last read at token k - 1,
     // before the previous barrier)
-    if (k + 1 < a.K) put_tables(sm.tok[(k + 1) & 1], sc, eb, eo, ec);
+    if (k + 1 < a.K) put_tables(sm.tok[(k + 1) & 1], sc, eb, eo, ec, false);
     __syncthreads();
   }
 
@@ -395,20 +472,27 @@ template <typename TI, typename TO, int N, int UNR>
 hipError_t launch_siso_tok(const DecodeArgs& a, int units, hipStream_t s) {
   constexpr int RPB = 4 * (64 / (N / 4));
   const int nblk = (a.P + UNR * RPB - 1) / (UNR * RPB);
-  const dim3 grid(units * nblk);
-  if (a.has_prev)
-    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false>), grid, dim3(256), 0, s, a);
+  const dim3 g(units * nblk), b(256);
+  if (a.bc.on) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, true>), g, b, 0, s, a);
+  } else {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <typename TI, typename TO, int N, int R>
 hipError_t launch_mimo_tok(const DecodeArgs& a, int units, hipStream_t s) {
-  if (a.has_prev)
-    hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true>), dim3(units), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false>), dim3(units), dim3(256), 0, s, a);
+  const dim3 g(units), b(256);
+  if (a.bc.on) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false, true>), g, b, 0, s, a);
+  } else {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

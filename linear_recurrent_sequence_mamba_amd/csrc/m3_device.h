@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "m3_launch.h"
+
 namespace m3 {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -127,6 +129,14 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
   if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// Inverse RMS of one rank column of B or C from its sum of squares over the
+// N channels (1 when the normalisation is off), with the hardware reciprocal
+// square root (about 1 ulp; the correctly rounded sqrt-and-divide sequence
+// costs the decode step a few percent).
+__device__ __forceinline__ float bc_inv_rms(const BCPrep& p, float sumsq, int N) {
+  return p.rms ? __builtin_amdgcn_rsqf(sumsq * (1.0f / (float)N) + p.eps) : 1.0f;
 }
 
 }  // namespace m3

@@ -11,6 +11,19 @@ namespace m3 {
 constexpr uint32_t kThetaIsAngle = 1u << 0;
 constexpr uint32_t kAPerToken = 1u << 1;
 
+// the preparation of B and C applied inside the kernels when `on`:
+// B' = Bw[n] * B / rms + Bb[h][n][r], rms over the N channels of a rank
+// column (1 when !rms); the same for C
+struct BCPrep {
+  const float* Bw;   // [N] or null (1)
+  const float* Cw;
+  const float* Bb;   // [H, N, R] or null (0)
+  const float* Cb;
+  float eps;
+  int rms;
+  int on;
+};
+
 struct DecodeArgs {
   float* h;
   const void* x;
@@ -28,6 +41,7 @@ struct DecodeArgs {
   int K;           // tokens of a multi-token call (1 for a single step)
   uint32_t flags;
   int has_prev;
+  BCPrep bc;
 };
 
 bool decode_supported(int P, int N, int R);
@@ -66,16 +80,19 @@ struct PrefillArgs {
   int G;           // groups sharing B, C and theta (G divides H)
   uint32_t flags;
   int has_prev;
+  BCPrep bc;
+  float* rsB;      // with bc.on: [units, Q, R] inverse RMS of the chunk's B rows
 };
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16);
 bool prefill_offsets_fit(int H, int P, int N, int R);
-size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q);
+size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep);
+// carve-ups read a.bc.on, so set it first
 void prefill_carve(PrefillArgs& a, void* ws);
 // packed sequences: chunk slots per head (an upper bound of the chunk count
 // for any split of T tokens into Bsz sequences), workspace and carve-up
 int64_t varlen_slots(int Bsz, int T, int Q);
-size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q);
+size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep);
 void prefill_varlen_carve(PrefillArgs& a, void* ws);
 // builds seqs and cmap from the sequence offsets cu [Bsz + 1] (device)
 hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s);

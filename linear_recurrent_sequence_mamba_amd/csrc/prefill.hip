@@ -502,6 +502,127 @@ struct ThetaBlock {
   }
 };
 
+// B/C preparation tables of one block: the weight [N], one head's bias
+// [N][R] and the inverse RMS [t][r] of the chunk's tokens.  NoTab stands in
+// when the preparation is off.
+template <int N, int R>
+struct alignas(16) PrepTab {
+  float w[N];
+  float b[N * R];
+  float inv[kQ * R];
+};
+struct NoTab {};
+template <bool PREP, int N, int R>
+using PrepTabT = typename std::conditional<PREP, PrepTab<N, R>, NoTab>::type;
+
+// weight and bias of head h (1 and 0 where the arrays are absent), loaded
+// into registers early and stored into a PrepTab once the tables exist
+template <int N, int R, int NT>
+struct PrepLoad {
+  static constexpr int NE = N + N * R;
+  static constexpr int IT = (NE + NT - 1) / NT;
+  float v[IT];
+  __device__ __forceinline__ void load(const float* w, const float* bias, int h) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e = threadIdx.x + NT * i;
+      if (e < N) v[i] = w ? w[e] : 1.0f;
+      else if (e < NE) v[i] = bias ? bias[(int64_t)h * N * R + (e - N)] : 0.0f;
+      else v[i] = 0.0f;
+    }
+  }
+  __device__ __forceinline__ void store(PrepTab<N, R>& t) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e = threadIdx.x + NT * i;
+      if (e < N) t.w[e] = v[i];
+      else if (e < NE) t.b[e - N] = v[i];
+    }
+  }
+};
+
+// the preparation of one vector of eight elements (e0 .. e0 + 7 of token t's
+// N x R row) in place; NoPrep leaves it as loaded
+struct NoPrep {
+  __device__ __forceinline__ void operator()(int, int, float*) const {}
+};
+template <int N, int R>
+struct TabPrep {
+  const PrepTab<N, R>* tab;
+  // the vector's R inverse RMS, 8/R weights and 8 biases in 16-byte (or
+  // smaller) LDS reads
+  __device__ __forceinline__ void operator()(int t, int e0, float* v) const {
+    static_assert(8 % R == 0, "a vector holds whole rank groups");
+    float iv[R], wv[8 / R], bv[8];
+    if constexpr (R == 4) {
+      const f4 q = *reinterpret_cast<const f4*>(&tab->inv[t * 4]);
+      iv[0] = q.x; iv[1] = q.y; iv[2] = q.z; iv[3] = q.w;
+    } else if constexpr (R == 2) {
+      const f2 q = *reinterpret_cast<const f2*>(&tab->inv[t * 2]);
+      iv[0] = q.x; iv[1] = q.y;
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) iv[r] = tab->inv[t * R + r];
+    }
+    if constexpr (8 / R >= 4) {
+#pragma unroll
+      for (int m = 0; m < 8 / R; m += 4) {
+        const f4 q = *reinterpret_cast<const f4*>(&tab->w[e0 / R + m]);
+        wv[m] = q.x; wv[m + 1] = q.y; wv[m + 2] = q.z; wv[m + 3] = q.w;
+      }
+    } else if constexpr (8 / R == 2) {
+      const f2 q = *reinterpret_cast<const f2*>(&tab->w[e0 / R]);
+      wv[0] = q.x; wv[1] = q.y;
+    } else {
+      wv[0] = tab->w[e0 / R];
+    }
+    const f4 b0 = *reinterpret_cast<const f4*>(&tab->b[e0]);
+    const f4 b1 = *reinterpret_cast<const f4*>(&tab->b[e0 + 4]);
+    bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
+    bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * (iv[j % R] * wv[j / R]) + bv[j];
+  }
+};
+
+// Sums of squares over the N channels of each rank column for the tokens
+// of a row block of B or C (t = t0 + tl < Lc).  When one token's vectors sit
+// on VPT consecutive lanes (TF false) they are summed with lane shuffles and
+// the token's first lane stores the inverse RMS into out[t][r]; a
+// token-per-lane block (TF true, single rank) adds its partial sums into a
+// cleared out[t] with LDS atomics, to be turned into inverse RMS later.
+template <typename TI, int E, int R, int NT, bool TF, int ROWS>
+__device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, TF, ROWS>& rb,
+                                          const BCPrep& bc, int N, int t0, int Lc, float* out) {
+  using RBk = RowBlock<TI, E, R, NT, TF, ROWS>;
+#pragma unroll
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    const int t = t0 + tl;
+    float v[8], part[R];
+    rb.raw[i].get(v);
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[j % R] += v[j] * v[j];
+    if constexpr (TF) {
+      static_assert(R == 1, "token-per-lane blocks carry a single rank");
+      if (vi < RBk::NV && t < Lc) atomicAdd(&out[t], part[0]);
+    } else {
+      static_assert(RBk::VPT <= 64 && 64 % RBk::VPT == 0 && NT % RBk::VPT == 0,
+                    "a token's vectors on one aligned lane group");
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[r] = group_sum<RBk::VPT>(part[r]);
+      if (vi < RBk::NV && t < Lc && vi % RBk::VPT == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) out[t * R + r] = bc_inv_rms(bc, part[r], N);
+      }
+    }
+  }
+}
+
 // The chunk's tables from its loaded inputs: token scalars, the chunk-local
 // log-decay prefix (double, one wave shuffle scan) and phase prefix of
 // every pair (double; each thread owns one pair and a segment of tokens),
@@ -578,10 +699,10 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
 }
 
 // B or C rows of a block, rotated by -Phi_t, into st[v - v0][n]
-template <class Pol, typename TI, int N, int R, int NT, int ROWS, class Tab>
+template <class Pol, typename TI, int N, int R, int NT, int ROWS, class Tab, class Prep>
 __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, false, ROWS>& rb,
                                            typename Pol::template Store<ROWS, N>& st,
-                                           const Tab& tb, int t0, int Lc) {
+                                           const Tab& tb, int t0, int Lc, const Prep& prep) {
   using RBk = RowBlock<TI, N * R, R, NT, false, ROWS>;
   constexpr int NPAIR = 4 / R;              // complex pairs per vector
 #pragma unroll
@@ -594,6 +715,7 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
     const bool ok = t < Lc;
     float v[8], o[8];
     rb.raw[i].get(v);
+    if (ok) prep(t, e0, v);
     f2 csr[NPAIR];
     tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
 #pragma unroll
@@ -625,10 +747,11 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
 
 // B rows of a block rotated by +(Phi_end - Phi_t) and scaled by W_t,
 // transposed: st[n][v - v0]
-template <class Pol, typename TI, int N, int R, int NT, bool TF, class Tab>
+template <class Pol, typename TI, int N, int R, int NT, bool TF, class Tab, class Prep>
 __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF>& rb,
                                              typename Pol::template Store<N, kRB>& st,
-                                             const Tab& tb, const float* w, int t0, int Lc) {
+                                             const Tab& tb, const float* w, int t0, int Lc,
+                                             const Prep& prep) {
   using RBk = RowBlock<TI, N * R, R, NT, TF>;
   constexpr int NPAIR = 4 / R;
 #pragma unroll
@@ -642,6 +765,7 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF
     const float wt = ok ? w[t] : 0.0f;
     float v[8];
     rb.raw[i].get(v);
+    if (ok) prep(t, e0, v);
     f2 csr[NPAIR];
     tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
 #pragma unroll
@@ -718,8 +842,10 @@ struct StateBlock {
 // K1: the chunk's own end state S_c (from a zero entry state), rotated into
 // the frame of the chunk's end, plus the next chunk's trapezoid
 // left-endpoint term (1 - lam_{c1}) dt_{c1} x_{c1-1} B_{c1-1}^T; the chunk's
-// total decay and phase go to the workspace.
-template <class Pol, typename TI, int P, int N, int R>
+// total decay and phase go to the workspace.  With the B/C preparation the
+// chunk's B rows are normalised, weighted and biased as they are staged, and
+// their inverse RMS goes to the workspace for the output kernel.
+template <class Pol, typename TI, int P, int N, int R, bool PREP>
 struct K1Smem {
   Tables<N, false, true> tb;
   union U {
@@ -727,12 +853,13 @@ struct K1Smem {
     TableScratch<N, Geo<P, N, R, 8>::NT> scr;
   } u;
   typename Pol::template XStore<P, kRB> xs;    // x^T  [p][v]
+  PrepTabT<PREP, N, R> pb;                     // B preparation
 };
 
-template <class Pol, typename TI, int P, int N, int R>
+template <class Pol, typename TI, int P, int N, int R, bool PREP>
 __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillArgs a) {
   using G = Geo<P, N, R, 8>;
-  __shared__ K1Smem<Pol, TI, P, N, R> sm;
+  __shared__ K1Smem<Pol, TI, P, N, R, PREP> sm;
   constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
   constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
   const int h = blockIdx.y;
@@ -749,12 +876,17 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   // block waits for HBM once
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+  constexpr bool TFK1 = R < 2;
+  PrepLoad<N, R, G::NT> pl;
+  if constexpr (PREP) {
+    pl.load(a.bc.Bw, a.bc.Bb, h);
+    if (TFK1 && tid < kQ) sm.pb.inv[tid] = 0.0f;   // sums of squares, added atomically
+  }
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
   // with R >= 2 a token's row of B (N R values) or x (P R) is long enough
   // for lanes to walk it (whole lines per load); single-rank rows are
   // spread one token per lane, so the transposed stores pair up lanes
-  constexpr bool TFK1 = R < 2;
   RowBlock<TI, N * R, R, G::NT, TFK1> bb[G::NUB];
   RowBlock<TI, P * R, R, G::NT, TFK1> xb[G::NUB];
 #pragma unroll
@@ -778,7 +910,22 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   if (tid < G::NP)
     reinterpret_cast<f2*>(a.rot_end)[chunk_id * G::NP + tid] = cos_sin_reduced(reduce_angle(sm.tb.phi_end[tid]));
   if (tid == 0) a.decay[chunk_id] = expf((float)cs_end);
-  __syncthreads();   // W_t visible
+  float* __restrict__ rsB = nullptr;
+  if constexpr (PREP) {
+    rsB = a.rsB + chunk_id * (kQ * R);
+    pl.store(sm.pb);
+#pragma unroll
+    for (int ub = 0; ub < G::NUB; ++ub)
+      if (ub * kRB < rows) row_sumsq(bb[ub], a.bc, N, ub * kRB / R, Lc, sm.pb.inv);
+  }
+  __syncthreads();   // W_t visible (and the B preparation tables)
+  if constexpr (PREP) {
+    if constexpr (TFK1) {   // sums of squares -> inverse RMS
+      if (tid < kQ) sm.pb.inv[tid] = bc_inv_rms(a.bc, sm.pb.inv[tid], N);
+      __syncthreads();
+    }
+    if (tid < kQ * R) rsB[tid] = sm.pb.inv[tid];
+  }
 
   f4 acc[QPW];
 #pragma unroll
@@ -788,7 +935,12 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   for (int ub = 0; ub < G::NUB; ++ub) {
     if (ub * kRB >= rows) break;
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
-    store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc);
+    if constexpr (PREP)
+      store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc,
+                                               TabPrep<N, R>{&sm.pb});
+    else
+      store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc,
+                                               NoPrep{});
     store_x_T<Pol, TI, P, R, G::NT, kRB, TFK1>(xb[ub], sm.xs);
     __syncthreads();
 #pragma unroll
@@ -845,6 +997,11 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
         for (int i = 0; i < R; ++i) {
           const f4 v = ld4(Be, (int64_t)n * R + 4 * i);
           br[4 * i] = v.x; br[4 * i + 1] = v.y; br[4 * i + 2] = v.z; br[4 * i + 3] = v.w;
+        }
+        if constexpr (PREP) {   // the last token's B, prepared like the staged rows
+#pragma unroll
+          for (int e = 0; e < 4 * R; ++e)
+            br[e] = br[e] * sm.pb.inv[(kQ - 1) * R + e % R] * sm.pb.w[n + e / R] + sm.pb.b[n * R + e];
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -903,13 +1060,32 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
     const float bp0 = (1.0f - l) * d;
     const TI* xh = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
     const TI* Bh = static_cast<const TI*>(a.Bp) + ((int64_t)b * a.G + head_group(a, h)) * N * R;
+    float bv[4][R];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) bv[j][r] = ld1(Bh, (int64_t)(n + j) * R + r);
+    if (a.bc.on) {
+      // B_prev prepared like every B: the N / 4 lanes of row p hold all of it
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += bv[j][r] * bv[j][r];
+        const float inv = bc_inv_rms(a.bc, group_sum<N / 4>(ss), N);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bv[j][r] = bv[j][r] * inv * (a.bc.Bw ? a.bc.Bw[n + j] : 1.0f) +
+                     (a.bc.Bb ? a.bc.Bb[((int64_t)h * N + n + j) * R + r] : 0.0f);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float xv = bp0 * ld1(xh, (int64_t)p * R + r);
-      S.x += xv * ld1(Bh, (int64_t)(n + 0) * R + r);
-      S.y += xv * ld1(Bh, (int64_t)(n + 1) * R + r);
-      S.z += xv * ld1(Bh, (int64_t)(n + 2) * R + r);
-      S.w += xv * ld1(Bh, (int64_t)(n + 3) * R + r);
+      S.x += xv * bv[0][r];
+      S.y += xv * bv[1][r];
+      S.z += xv * bv[2][r];
+      S.w += xv * bv[3][r];
     }
   }
   const int64_t off = (int64_t)p * N + n;
@@ -962,7 +1138,7 @@ struct Geo3 {
                 "output block geometry");
 };
 
-template <class Pol, typename TI, int P, int N, int R>
+template <class Pol, typename TI, int P, int N, int R, bool PREP>
 struct K3Smem {
   // with R a multiple of 4 each token-pair mask value serves 16 virtual
   // (row, column) pairs, so the block's mask rows are tabulated once
@@ -977,6 +1153,7 @@ struct K3Smem {
   } u;
   typename Pol::template XStore<P, UB> xs[2];  // x^T of a u-block      [p][v]
   float msk[MT][kQ + 1];                       // M[t - t_lo][u]
+  PrepTabT<PREP, N, R> pb, pc;                 // B and C preparation
 };
 
 // four consecutive outputs (one token's four ranks) in one store
@@ -989,10 +1166,19 @@ __device__ __forceinline__ void st4_out(bf16_t* __restrict__ p, int64_t i, f4 v)
   *reinterpret_cast<uint2*>(p + i) = uint2{lo, hi};
 }
 
-template <class Pol, typename TI, typename TO, int P, int N, int R>
-__global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArgs a) {
+// the rank-4 bf16 kernel runs two 8-wave blocks per CU (four waves per
+// SIMD); the B/C preparation's few extra registers must not break that
+template <class Pol, int R, bool PREP>
+constexpr int k3_min_waves() {
+  return (PREP && R % 4 == 0 && std::is_same<Pol, PolF16>::value) ? 4 : 1;
+}
+
+template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP>
+__global__ __launch_bounds__((Geo3<P, N, R>::NT))
+__attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_output(PrefillArgs a) {
   using G = Geo3<P, N, R>;
-  __shared__ K3Smem<Pol, TI, P, N, R> sm;
+  using SMT = K3Smem<Pol, TI, P, N, R, PREP>;
+  __shared__ SMT sm;
   constexpr int NKS = N / Pol::KS;
   constexpr int UG = 16 * Pol::DT;          // u rows per A fragment built from D tiles
   // the two blocks of a split chunk are 8 apart in launch order: same XCD
@@ -1026,9 +1212,21 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
 
+  // the B/C preparation's weights, biases and the chunk's B inverse RMS
+  // (small, L2-resident) go straight into LDS, so that no register holds
+  // them across the loads below
+  if constexpr (PREP) {
+    PrepLoad<N, R, G::NT> plb, plc;
+    plb.load(a.bc.Bw, a.bc.Bb, h);
+    plc.load(a.bc.Cw, a.bc.Cb, h);
+    const float rsb = tid < kQ * R ? a.rsB[chunk_id * (kQ * R) + tid] : 0.0f;
+    plb.store(sm.pb);
+    plc.store(sm.pc);
+    if (tid < kQ * R) sm.pb.inv[tid] = rsb;
+  }
   // all loads go out first (the load counter retires in order): phase
   // inputs and token scalars, this block's C rows, the entry state, and the
-  // first two u-blocks of B and x
+  // first u-blocks of B and x
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
   RowBlock<TI, N * R, R, G::NT, false> cb[G::NCB];
@@ -1037,14 +1235,16 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
     if (v0 + k * kRB < rows) cb[k].template load<true>(Cg, a, b, h, c0, Lc, v0 + k * kRB);
   StateBlock<P, N, G::NT> sb;
   sb.load(a.S + chunk_id * P * N);
-  // B and x move in u-blocks of 32 virtual rows, three in flight
-  constexpr int UB = K3Smem<Pol, TI, P, N, R>::UB;
+  // B and x move in u-blocks of 32 virtual rows, three in flight (two with
+  // the B/C preparation, whose staging needs the registers of the third)
+  constexpr int NS = PREP ? 2 : 3;
+  constexpr int UB = SMT::UB;
   constexpr int NKB = G::ROWS / UB;
   const int nkb = (vend + UB - 1) / UB;
-  RowBlock<TI, N * R, R, G::NT, false, UB> bb[3];
-  RowBlock<TI, P * R, R, G::NT, (R < 2), UB> xb[3];   // x rows walked by lanes when R >= 2
+  RowBlock<TI, N * R, R, G::NT, false, UB> bb[NS];
+  RowBlock<TI, P * R, R, G::NT, (R < 2), UB> xb[NS];   // x rows walked by lanes when R >= 2
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < NS; ++q) {
     if (q < nkb) {
       bb[q].template load<true>(Bg, a, b, h, c0, Lc, q * UB);
       xb[q].template load<false>(Xg, a, b, h, c0, Lc, q * UB);
@@ -1057,8 +1257,7 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   // (zero above the diagonal and past the chunk's end)
   const int tlo = v0 / R;
   if constexpr (R % 4 == 0) {
-    using SM = K3Smem<Pol, TI, P, N, R>;
-    for (int idx = tid; idx < SM::MT * kQ; idx += G::NT) {
+    for (int idx = tid; idx < SMT::MT * kQ; idx += G::NT) {
       const int tr = idx / kQ, u = idx % kQ, t = tlo + tr;
       float m = 0.0f;
       if (t < Lc && u <= t) {
@@ -1067,6 +1266,12 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
       }
       sm.msk[tr][u] = m;
     }
+  }
+  if constexpr (PREP) {
+#pragma unroll
+    for (int k = 0; k < G::NCB; ++k)
+      if (v0 + k * kRB < rows) row_sumsq(cb[k], a.bc, N, (v0 + k * kRB) / R, Lc, sm.pc.inv);
+    __syncthreads();
   }
 
   // own rotated C rows -> MFMA fragments in registers
@@ -1077,7 +1282,11 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   for (int k = 0; k < G::NCB; ++k) {
     if (v0 + k * kRB < rows) {
       if (k > 0) __syncthreads();
-      store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc);
+      if constexpr (PREP)
+        store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc,
+                                              TabPrep<N, R>{&sm.pc});
+      else
+        store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc, NoPrep{});
       __syncthreads();
       if (lt / 4 == k) {
 #pragma unroll
@@ -1114,11 +1323,15 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
   const int tmax = min(Lc - 1, (16 * tile + 15) / R);
   const double cst = sm.tb.cs[min(tt, kQ - 1)];
   auto stage = [&](int k) {
-    store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % 3], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc);
-    store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % 3], sm.xs[k % 2]);
-    if (k + 3 < nkb) {   // the freed slot takes u-block k + 3
-      bb[k % 3].template load<true>(Bg, a, b, h, c0, Lc, (k + 3) * UB);
-      xb[k % 3].template load<false>(Xg, a, b, h, c0, Lc, (k + 3) * UB);
+    if constexpr (PREP)
+      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc,
+                                           TabPrep<N, R>{&sm.pb});
+    else
+      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc, NoPrep{});
+    store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % NS], sm.xs[k % 2]);
+    if (k + NS < nkb) {   // the freed slot takes u-block k + NS
+      bb[k % NS].template load<true>(Bg, a, b, h, c0, Lc, (k + NS) * UB);
+      xb[k % NS].template load<false>(Xg, a, b, h, c0, Lc, (k + NS) * UB);
     }
   };
   __syncthreads();   // Shat's reads are done (the buffers share its space)
@@ -1192,12 +1405,12 @@ __global__ __launch_bounds__((Geo3<P, N, R>::NT)) void k_chunk_output(PrefillArg
 }
 
 // --------------------------------------------------------------------------
-template <class Pol, typename TI, typename TO, int P, int N, int R>
+template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   using G1 = Geo<P, N, R, 8>;
   // packed sequences: one row of chunk slots per head
   const int nz = a.cmap ? 1 : a.Bsz;
-  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R>), dim3(a.nchunk, a.H, nz), dim3(G1::NT), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R, PREP>), dim3(a.nchunk, a.H, nz), dim3(G1::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
@@ -1207,7 +1420,7 @@ static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
   using G3 = Geo3<P, N, R>;
   // a split chunk's blocks are 8 apart in launch order: pad to whole groups of 8
   const int nx = G3::SPLIT == 1 ? a.nchunk : G3::SPLIT * ((a.nchunk + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R>), dim3(nx, a.H, nz), dim3(G3::NT), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R, PREP>), dim3(nx, a.H, nz), dim3(G3::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1216,7 +1429,8 @@ static int dispatch_shape(const PrefillArgs& a, hipStream_t s, hipError_t* e) {
 #define M3_SHAPE(PP, NN, RR)                                  \
   if constexpr (NN % Pol::KS == 0) {                          \
     if (a.P == PP && a.N == NN && a.R == RR) {                \
-      *e = run_prefill<Pol, TI, TO, PP, NN, RR>(a, s);        \
+      *e = a.bc.on ? run_prefill<Pol, TI, TO, PP, NN, RR, true>(a, s)  \
+                   : run_prefill<Pol, TI, TO, PP, NN, RR, false>(a, s); \
       return 0;                                               \
     }                                                         \
   }
@@ -1245,20 +1459,35 @@ bool prefill_supported(int P, int N, int R, int Q, int in_bf16) {
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q) {
-  const size_t nchunk = (size_t)(T + Q - 1) / Q;
-  const size_t units = (size_t)Bsz * H * nchunk;
-  return align256(units * P * N * 4) + align256(units * N * 4) + align256(units * 4);
+// per chunk unit: the state (P N), the end phase (N) and the decay (1), and
+// with the B/C preparation the inverse RMS of the chunk's B rows (Q R)
+static size_t unit_bytes(size_t units, int P, int N, int R, int Q, bool prep) {
+  return align256(units * P * N * 4) + align256(units * N * 4) + align256(units * 4) +
+         (prep ? align256(units * Q * R * 4) : 0);
 }
 
-void prefill_carve(PrefillArgs& a, void* ws) {
-  const size_t units = (size_t)a.Bsz * a.H * a.nchunk;
-  char* p = static_cast<char*>(ws);
+static char* carve_units(PrefillArgs& a, size_t units, char* p) {
   a.S = reinterpret_cast<float*>(p);
   p += align256(units * a.P * a.N * 4);
   a.rot_end = reinterpret_cast<float*>(p);
   p += align256(units * a.N * 4);
   a.decay = reinterpret_cast<float*>(p);
+  p += align256(units * 4);
+  a.rsB = nullptr;
+  if (a.bc.on) {
+    a.rsB = reinterpret_cast<float*>(p);
+    p += align256(units * kQ * a.R * 4);
+  }
+  return p;
+}
+
+size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep) {
+  const size_t nchunk = (size_t)(T + Q - 1) / Q;
+  return unit_bytes((size_t)Bsz * H * nchunk, P, N, R, Q, prep);
+}
+
+void prefill_carve(PrefillArgs& a, void* ws) {
+  carve_units(a, (size_t)a.Bsz * a.H * a.nchunk, static_cast<char*>(ws));
 }
 
 // --------------------------------------------------------------------------
@@ -1274,21 +1503,14 @@ int64_t varlen_slots(int Bsz, int T, int Q) {
   return std::min<int64_t>(T, ((int64_t)T + (int64_t)Bsz * (Q - 1)) / Q);
 }
 
-size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int Q) {
-  const size_t units = (size_t)H * varlen_slots(Bsz, T, Q);
-  return align256(units * P * N * 4) + align256(units * N * 4) + align256(units * 4) +
-         align256((size_t)Bsz * sizeof(int4)) + align256((size_t)varlen_slots(Bsz, T, Q) * sizeof(int4));
+size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep) {
+  const size_t slots = (size_t)varlen_slots(Bsz, T, Q);
+  return unit_bytes((size_t)H * slots, P, N, R, Q, prep) + align256((size_t)Bsz * sizeof(int4)) +
+         align256(slots * sizeof(int4));
 }
 
 void prefill_varlen_carve(PrefillArgs& a, void* ws) {
-  const size_t units = (size_t)a.H * a.nchunk;
-  char* p = static_cast<char*>(ws);
-  a.S = reinterpret_cast<float*>(p);
-  p += align256(units * a.P * a.N * 4);
-  a.rot_end = reinterpret_cast<float*>(p);
-  p += align256(units * a.N * 4);
-  a.decay = reinterpret_cast<float*>(p);
-  p += align256(units * 4);
+  char* p = carve_units(a, (size_t)a.H * a.nchunk, static_cast<char*>(ws));
   a.seqs = reinterpret_cast<int4*>(p);
   p += align256((size_t)a.Bsz * sizeof(int4));
   a.cmap = reinterpret_cast<int4*>(p);

@@ -104,6 +104,34 @@ def packed_inputs(w: Workload, lengths, stream: int = 0, h0: str | None = None,
     return out
 
 
+def bc_prep_inputs(w: Workload, d: dict, stream: int = 0, eps: float = 1e-6):
+    """Inputs of the in-kernel B/C preparation for the tensors of ``d``
+    (prefill or token layouts, B/C with their group axis third from the end):
+    B and C (and B_prev) become raw projections by a scale U(0.2, 5) per
+    token, group and rank column, cast back to the input dtype; the weights
+    are U(0.5, 1.5) [N] and the per-head biases N(0, 0.5^2) [H, N, R], fp32.
+    Returns (d2, params) with params = dict(B_weight, C_weight, B_bias, C_bias,
+    eps) as CPU tensors."""
+    rng = np.random.default_rng([w.cfg_id, 0xBC, stream])
+    f32 = np.float32
+    out = dict(d)
+    for k in ("B", "C", "B_prev"):
+        v = d.get(k)
+        if v is None:
+            continue
+        shape = tuple(v.shape[:-2]) + (1, v.shape[-1])
+        sc = rng.uniform(0.2, 5.0, size=shape).astype(f32)
+        out[k] = _cast(v.to(torch.float32).numpy() * sc, v.dtype)
+    N, H, R = w.dstate, w.nheads, w.rank
+    params = dict(
+        B_weight=torch.from_numpy(rng.uniform(0.5, 1.5, size=N).astype(f32)),
+        C_weight=torch.from_numpy(rng.uniform(0.5, 1.5, size=N).astype(f32)),
+        B_bias=torch.from_numpy((rng.standard_normal((H, N, R)) * 0.5).astype(f32)),
+        C_bias=torch.from_numpy((rng.standard_normal((H, N, R)) * 0.5).astype(f32)),
+        eps=eps)
+    return out, params
+
+
 def _softplus(v):
     return np.logaddexp(np.float32(0.0), v).astype(np.float32)
 

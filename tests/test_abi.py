@@ -145,6 +145,27 @@ def test_varlen_workspace_size():
         m3.m3_prefill_workspace_size(_dims(batch=1))
 
 
+def test_bc_prep_errors():
+    for call in (_decode, _tokens, _prefill, _varlen):
+        bad_eps = m3.m3_bc_prep(None, None, None, None, -1.0, 1)
+        d = _dims()
+        d.bc = ctypes.pointer(bad_eps)
+        assert call(d) == 2                                     # eps < 0
+        nan_eps = m3.m3_bc_prep(None, None, None, None, float("nan"), 1)
+        d.bc = ctypes.pointer(nan_eps)
+        assert call(d) == 2
+        mis = m3.m3_bc_prep(P16, P_MIS, None, None, 1e-6, 1)
+        d.bc = ctypes.pointer(mis)
+        assert call(d) == 5                                     # misaligned weight
+    # the prefill workspace grows by the chunk's B inverse RMS (Q R floats per chunk)
+    d = _dims(rank=4)
+    plain = m3.m3_prefill_workspace_size(d)
+    ok = m3.m3_bc_prep(None, None, None, None, 1e-6, 1)
+    d.bc = ctypes.pointer(ok)
+    assert m3.m3_prefill_workspace_size(d) >= plain + 2 * 3 * 2 * 64 * 4 * 4
+    assert m3.m3_prefill_varlen_workspace_size(d) > m3.m3_prefill_varlen_workspace_size(_dims(rank=4))
+
+
 def test_binding_rejects_mismatched_tensors():
     torch = pytest.importorskip("torch")
     d = _dims()
