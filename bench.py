@@ -17,8 +17,10 @@ MIMO rank-4 long prefill (B=1, T=16384, H=64), each with its own timing and
 roofline fraction, and the fp64 CPU oracle timed on a bounded sample of each
 workload (`cpu_baseline`, a reported baseline only); also four decode tokens
 per call (m3_decode_tokens, the state crossing HBM once per call) at both
-decode shapes, and the two prefill shapes' tokens packed as sequences of
-drawn lengths (m3_scan_prefill_varlen).
+decode shapes, the two prefill shapes' tokens packed as sequences of
+drawn lengths (m3_scan_prefill_varlen), and the decode steps and prefills
+again with the in-kernel B/C preparation (RMS normalisation, weight and
+per-head bias of B and C; "_bcprep").
 
 Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
 """
@@ -99,7 +101,18 @@ def counters_for(kernel_tag):
 
 
 # ---------------------------------------------------------------------------
-def bench_decode(name, steps, warmup, pool_n=8):
+def bc_prep_for(w, dev):
+    """The in-kernel B/C preparation (weights, per-head biases, eps) of a
+    workload's shape, on the device."""
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+    _, prm = I.bc_prep_inputs(w, {})
+    return m3.BCPrep(**{k: prm[k].to(dev) for k in ("B_weight", "C_weight", "B_bias", "C_bias")},
+                     eps=prm["eps"])
+
+
+def bench_decode(name, steps, warmup, pool_n=8, prep=False):
+    """prep: with the in-kernel B/C preparation (m3_dims.bc)."""
     import torch
     from linear_recurrent_sequence_mamba_amd import binding as m3
     from linear_recurrent_sequence_mamba_amd import inputs as I
@@ -116,7 +129,8 @@ def bench_decode(name, steps, warmup, pool_n=8):
     h = I.decode_state(w).to(dev)
     A = I.head_decay(w).to(dev)
     y = torch.empty((w.batch, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
-    dims = m3.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32)
+    dims = m3.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32,
+                        bc=bc_prep_for(w, dev) if prep else None)
     stream = torch.cuda.current_stream()
     # validate every argument set once through the checked binding ...
     for s in range(pool_n):
@@ -241,7 +255,8 @@ def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
                               timing=f"HIP events around a graph of {calls} calls"))
 
 
-def bench_prefill(name, steps, warmup):
+def bench_prefill(name, steps, warmup, prep=False):
+    """prep: with the in-kernel B/C preparation (m3_dims.bc)."""
     import torch
     from linear_recurrent_sequence_mamba_amd import binding as m3
     from linear_recurrent_sequence_mamba_amd import inputs as I
@@ -256,7 +271,7 @@ def bench_prefill(name, steps, warmup):
         sets.append({k: (None if v is None else v.to(dev)) for k, v in d.items()})
     log(f"[{name}] generated {n_sets} input set(s) in {time.time() - t0:.1f}s")
     dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk,
-                        m3.M3_BF16, m3.M3_F32)
+                        m3.M3_BF16, m3.M3_F32, bc=bc_prep_for(w, dev) if prep else None)
     ws = m3.workspace(dims, dev)
     y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
     hT = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
@@ -452,6 +467,13 @@ def main():
     for name in ("siso_prefill_varlen", "mimo_prefill_varlen"):
         if want(name):
             res[name] = bench_prefill_varlen(name, a.prefill_steps, 2)
+    prep = {}   # the same shapes with the in-kernel B/C preparation
+    for name in ("siso_decode", "mimo_decode"):
+        if want(name + "_bcprep"):
+            prep[name] = bench_decode(name, a.steps, a.warmup, prep=True)
+    for name in ("siso_prefill", "mimo_prefill"):
+        if want(name + "_bcprep"):
+            prep[name] = bench_prefill(name, a.prefill_steps, 2, prep=True)
     tok = {}
     for base in ("siso_decode", "mimo_decode"):
         if want(base + "_k4"):
@@ -512,6 +534,19 @@ def main():
     for tag, r in res.items():
         workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
     workloads.update(tok)   # several tokens per call (m3_decode_tokens), same shapes
+    for base, r in prep.items():
+        if "decode" in base:
+            e = dict(us_per_step=round(r["step_ms"] * 1e3, 2),
+                     tokens_per_s=round(r["workload"].batch / (r["step_ms"] * 1e-3), 1),
+                     hbm_frac=round(r["bytes"] / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+            if base in workloads:
+                e["step_time_vs_plain"] = round(e["us_per_step"] / workloads[base]["us_per_step"], 3)
+        else:
+            e = dict(ms_per_call=round(r["call_ms"], 4),
+                     tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1))
+            if base in workloads:
+                e["call_time_vs_plain"] = round(e["ms_per_call"] / workloads[base]["ms_per_call"], 3)
+        workloads[base + "_bcprep"] = e
     for base in ("siso_prefill", "mimo_prefill"):
         if base in workloads and base + "_varlen" in workloads:
             workloads[base + "_varlen"]["tokens_per_s_vs_dense"] = round(
