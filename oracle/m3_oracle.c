@@ -200,6 +200,190 @@ int m3ref_decode_step(const m3ref_dims* d, double* h, const double* x_t,
 }
 
 /*
+ * Gradients of the scan (reverse-mode, the adjoint of the token recurrence
+ * above, taken step by step in reverse order).  Given dL/dy (dy) and
+ * dL/dhT (dhT, NULL = 0) it returns dL/d of every input: x, dt, A, lam,
+ * theta, B, C, h0, x_prev, B_prev (any output may be NULL).  Per token t,
+ * with U = alpha S_{t-1} + beta X_{t-1} B_{t-1}^T, W = R(phi) U and
+ * S_t = W + gamma X_t B_t^T, and G the gradient of S_t:
+ *   G += dy_t C_t^T;  dC_t = S_t^T dy_t;  dgamma = <G, X_t B_t^T>;
+ *   dX_t += gamma G B_t;  dB_t += gamma G^T X_t;
+ *   dphi_k = sum_p <G_pair, J W_pair>, J (a, b) = (-b, a)  (d R(phi)/dphi = J R(phi));
+ *   V = R(-phi) G;  dalpha = <V, S_{t-1}>;  dbeta = <V, X_{t-1} B_{t-1}^T>;
+ *   dX_{t-1} += beta V B_{t-1};  dB_{t-1} += beta V^T X_{t-1};  G <- alpha V;
+ * then the chain through alpha = exp(dt A), beta = (1 - lam) dt alpha,
+ * gamma = lam dt and phi = dt theta (theta with M3REF_THETA_IS_ANGLE).
+ * dA is [H] (summed over batch and time) or [Bsz, T, H] with
+ * M3REF_A_PER_TOKEN.  The forward states of a (batch, head) are kept
+ * (T + 1 of them), so this is for small cases.
+ */
+int m3ref_scan_backward(const m3ref_dims* d, const double* x, const double* dt,
+                        const double* A, const double* lam, const double* theta,
+                        const double* B, const double* C, const double* h0,
+                        const double* x_prev, const double* B_prev, const double* dy,
+                        const double* dhT, double* dx, double* ddt, double* dA,
+                        double* dlam, double* dtheta, double* dB, double* dC,
+                        double* dh0, double* dx_prev, double* dB_prev, int nthreads) {
+  int rc = m3ref_check(d);
+  if (rc) return rc;
+  if (!x || !dt || !A || !lam || !theta || !B || !C || !dy) return 3;
+  const int64_t Bsz = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim,
+                N = d->dstate, R = d->rank, K = N / 2;
+  const int64_t units = Bsz * H, PN = P * N;
+  const int angle = (d->flags & M3REF_THETA_IS_ANGLE) != 0;
+  const int a_tok = (d->flags & M3REF_A_PER_TOKEN) != 0;
+  /* per-token dA, summed per head at the end unless A is per token */
+  double* dA_tok = (double*)calloc((size_t)(Bsz * T * H > 0 ? Bsz * T * H : 1), sizeof(double));
+  if (!dA_tok) return 4;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t b = u / H, h = u % H;
+    const int prev = x_prev && B_prev;
+    const double* xp0 = prev ? x_prev + u * P * R : NULL;
+    const double* bp0 = prev ? B_prev + u * N * R : NULL;
+    /* forward: states S_{-1} .. S_{T-1} */
+    double* St = (double*)calloc((size_t)((T + 1) * PN), sizeof(double));
+    double* G = (double*)calloc((size_t)PN, sizeof(double));
+    double* V = (double*)calloc((size_t)PN, sizeof(double));
+    double* yt = (double*)calloc((size_t)(P * R), sizeof(double));
+    double* gx = (double*)calloc((size_t)((T + 1) * P * R), sizeof(double));  /* dX_{-1..T-1} */
+    double* gb = (double*)calloc((size_t)((T + 1) * N * R), sizeof(double));  /* dB_{-1..T-1} */
+    if (h0) memcpy(St, h0 + u * PN, sizeof(double) * PN);
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t bth = (b * T + t) * H + h;
+      memcpy(St + (t + 1) * PN, St + t * PN, sizeof(double) * PN);
+      const double* xp = t == 0 ? xp0 : x + (bth - H) * P * R;
+      const double* bp = t == 0 ? bp0 : B + (bth - H) * N * R;
+      m3ref_token(P, N, R, d->flags, St + (t + 1) * PN, xp, bp, x + bth * P * R, B + bth * N * R,
+                  C + bth * N * R, dt[bth], a_tok ? A[bth] : A[h], lam[bth], theta + bth * K, yt);
+    }
+    /* reverse */
+    if (dhT) memcpy(G, dhT + u * PN, sizeof(double) * PN);
+    for (int64_t t = T - 1; t >= 0; --t) {
+      const int64_t bth = (b * T + t) * H + h;
+      const double* S1 = St + (t + 1) * PN; /* S_t */
+      const double* S0 = St + t * PN;       /* S_{t-1} */
+      const double* xt = x + bth * P * R;
+      const double* bt = B + bth * N * R;
+      const double* ct = C + bth * N * R;
+      const double* dyt = dy + bth * P * R;
+      const double* xp = t == 0 ? xp0 : x + (bth - H) * P * R;
+      const double* bp = t == 0 ? bp0 : B + (bth - H) * N * R;
+      const double DT = dt[bth], LM = lam[bth], AA = a_tok ? A[bth] : A[h];
+      const double alpha = exp(DT * AA), beta = (1.0 - LM) * DT * alpha, gamma = LM * DT;
+      /* the output of token t */
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+          double v = 0.0;
+          for (int64_t r = 0; r < R; ++r) v += dyt[p * R + r] * ct[n * R + r];
+          G[p * N + n] += v;
+        }
+      if (dC)
+        for (int64_t n = 0; n < N; ++n)
+          for (int64_t r = 0; r < R; ++r) {
+            double v = 0.0;
+            for (int64_t p = 0; p < P; ++p) v += S1[p * N + n] * dyt[p * R + r];
+            dC[bth * N * R + n * R + r] = v;
+          }
+      /* the gamma term */
+      double dgamma = 0.0;
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+          double xb = 0.0;
+          for (int64_t r = 0; r < R; ++r) xb += xt[p * R + r] * bt[n * R + r];
+          dgamma += G[p * N + n] * xb;
+        }
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t r = 0; r < R; ++r) {
+          double v = 0.0;
+          for (int64_t n = 0; n < N; ++n) v += G[p * N + n] * bt[n * R + r];
+          gx[(t + 1) * P * R + p * R + r] += gamma * v;
+        }
+      for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < R; ++r) {
+          double v = 0.0;
+          for (int64_t p = 0; p < P; ++p) v += G[p * N + n] * xt[p * R + r];
+          gb[(t + 1) * N * R + n * R + r] += gamma * v;
+        }
+      /* the rotation: W = S_t - gamma X_t B_t^T */
+      double dphi_dt = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double phi = angle ? theta[bth * K + k] : DT * theta[bth * K + k];
+        const double cs = cos(phi), sn = sin(phi);
+        double dphi = 0.0;
+        for (int64_t p = 0; p < P; ++p) {
+          double w0 = S1[p * N + 2 * k], w1 = S1[p * N + 2 * k + 1];
+          for (int64_t r = 0; r < R; ++r) {
+            w0 -= gamma * xt[p * R + r] * bt[(2 * k) * R + r];
+            w1 -= gamma * xt[p * R + r] * bt[(2 * k + 1) * R + r];
+          }
+          const double g0 = G[p * N + 2 * k], g1 = G[p * N + 2 * k + 1];
+          dphi += -g0 * w1 + g1 * w0;
+          V[p * N + 2 * k] = cs * g0 + sn * g1;
+          V[p * N + 2 * k + 1] = -sn * g0 + cs * g1;
+        }
+        if (dtheta) dtheta[bth * K + k] = angle ? dphi : DT * dphi;
+        dphi_dt += theta[bth * K + k] * dphi;
+      }
+      /* decay and the beta term */
+      double dalpha = 0.0, dbeta = 0.0;
+      for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+          dalpha += V[p * N + n] * S0[p * N + n];
+          if (xp) {
+            double xb = 0.0;
+            for (int64_t r = 0; r < R; ++r) xb += xp[p * R + r] * bp[n * R + r];
+            dbeta += V[p * N + n] * xb;
+          }
+        }
+      if (xp) {
+        for (int64_t p = 0; p < P; ++p)
+          for (int64_t r = 0; r < R; ++r) {
+            double v = 0.0;
+            for (int64_t n = 0; n < N; ++n) v += V[p * N + n] * bp[n * R + r];
+            gx[t * P * R + p * R + r] += beta * v;
+          }
+        for (int64_t n = 0; n < N; ++n)
+          for (int64_t r = 0; r < R; ++r) {
+            double v = 0.0;
+            for (int64_t p = 0; p < P; ++p) v += V[p * N + n] * xp[p * R + r];
+            gb[t * N * R + n * R + r] += beta * v;
+          }
+      }
+      for (int64_t i = 0; i < PN; ++i) G[i] = alpha * V[i];
+      /* chain to dt, lam, A */
+      if (ddt)
+        ddt[bth] = AA * alpha * dalpha + (1.0 - LM) * alpha * (1.0 + DT * AA) * dbeta + LM * dgamma +
+                   (angle ? 0.0 : dphi_dt);
+      if (dlam) dlam[bth] = -DT * alpha * dbeta + DT * dgamma;
+      dA_tok[bth] = DT * alpha * dalpha + (1.0 - LM) * DT * DT * alpha * dbeta;
+    }
+    if (dh0) memcpy(dh0 + u * PN, G, sizeof(double) * PN);
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t bth = (b * T + t) * H + h;
+      if (dx) memcpy(dx + bth * P * R, gx + (t + 1) * P * R, sizeof(double) * P * R);
+      if (dB) memcpy(dB + bth * N * R, gb + (t + 1) * N * R, sizeof(double) * N * R);
+    }
+    if (prev && dx_prev) memcpy(dx_prev + u * P * R, gx, sizeof(double) * P * R);
+    if (prev && dB_prev) memcpy(dB_prev + u * N * R, gb, sizeof(double) * N * R);
+    free(St); free(G); free(V); free(yt); free(gx); free(gb);
+  }
+  if (dA) {
+    if (a_tok) {
+      memcpy(dA, dA_tok, sizeof(double) * Bsz * T * H);
+    } else {
+      for (int64_t h = 0; h < H; ++h) dA[h] = 0.0;
+      for (int64_t i = 0; i < Bsz * T * H; ++i) dA[i % H] += dA_tok[i];
+    }
+  }
+  free(dA_tok);
+  return 0;
+}
+
+/*
  * Preparation of B and C for the recurrence [the same article, section 2:
  * B and C go through an RMS normalisation, the way attention normalises Q
  * and K, and then get a learned bias per head and per channel].  For each

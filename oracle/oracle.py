@@ -57,6 +57,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.m3ref_scan.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 12 + [ctypes.c_int]
     lib.m3ref_decode_step.restype = ctypes.c_int
     lib.m3ref_decode_step.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 11 + [ctypes.c_int]
+    lib.m3ref_scan_backward.restype = ctypes.c_int
+    lib.m3ref_scan_backward.argtypes = [ctypes.POINTER(_Dims)] + [dp] * 22 + [ctypes.c_int]
     lib.m3ref_bc_prep.restype = ctypes.c_int
     lib.m3ref_bc_prep.argtypes = [ctypes.c_int64] * 5 + [dp] * 3 + [ctypes.c_double,
                                                                     ctypes.c_int, dp]
@@ -123,6 +125,39 @@ def decode_step(h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t,
     if rc:
         raise ValueError("m3ref_decode_step rejected its arguments (code %d)" % rc)
     return y, h
+
+
+GRAD_NAMES = ("x", "dt", "A", "lam", "theta", "B", "C", "h0", "x_prev", "B_prev")
+
+
+def scan_backward(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None, dy=None,
+                  dhT=None, flags: int = 0, nthreads: int = 0, lib_path: str = _LIB) -> dict:
+    """Gradients of L = <y, dy> + <hT, dhT> with respect to every input of
+    scan() (same layouts; dA is [H] unless A_PER_TOKEN).  Returns a dict keyed
+    by GRAD_NAMES; the entries of h0 / x_prev / B_prev are None when those
+    inputs are None."""
+    lib = load(lib_path)
+    x, dt, A, lam, theta, B, C = map(_f64, (x, dt, A, lam, theta, B, C))
+    h0, x_prev, B_prev, dy, dhT = map(_f64, (h0, x_prev, B_prev, dy, dhT))
+    Bsz, T, H, P, R = x.shape
+    N = B.shape[3]
+    d = _Dims(Bsz, T, H, P, N, R, flags)
+    prev = x_prev is not None and B_prev is not None
+    g = {k: np.zeros_like(v) for k, v in (("x", x), ("dt", dt), ("A", A), ("lam", lam),
+                                           ("theta", theta), ("B", B), ("C", C))}
+    g["h0"] = np.zeros((Bsz, H, P, N)) if h0 is not None else None
+    g["x_prev"] = np.zeros_like(x_prev) if prev else None
+    g["B_prev"] = np.zeros_like(B_prev) if prev else None
+    dh0 = g["h0"] if g["h0"] is not None else np.zeros((Bsz, H, P, N))
+    rc = lib.m3ref_scan_backward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
+                                 _ptr(theta), _ptr(B), _ptr(C), _ptr(h0), _ptr(x_prev),
+                                 _ptr(B_prev), _ptr(dy), _ptr(dhT), _ptr(g["x"]), _ptr(g["dt"]),
+                                 _ptr(g["A"]), _ptr(g["lam"]), _ptr(g["theta"]), _ptr(g["B"]),
+                                 _ptr(g["C"]), _ptr(dh0), _ptr(g["x_prev"]), _ptr(g["B_prev"]),
+                                 int(nthreads))
+    if rc:
+        raise ValueError("m3ref_scan_backward rejected its arguments (code %d)" % rc)
+    return g
 
 
 def bc_prep(v, nheads, weight=None, bias=None, eps=1e-6, rms=True, lib_path: str = _LIB):

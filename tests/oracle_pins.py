@@ -359,6 +359,53 @@ def check_a_per_token(lib):
 
 
 # ---------------------------------------------------------------------------
+# gradients: central finite differences of the forward scan
+def _loss(lib, d, dy, dhT, flags):
+    r = _scan(lib, d, flags)
+    return float(np.sum(r.y * dy) + (np.sum(r.hT * dhT) if dhT is not None else 0.0))
+
+
+def _fd_case(lib, seed, flags=0, R=1, h0=True, prev=True, with_dhT=True, tol=1e-7):
+    """Each gradient's inner product with a random direction against
+    (L(p + e v) - L(p - e v)) / 2e, L = <y, dy> + <hT, dhT>, in fp64."""
+    d = _rand_case(seed, Bsz=2, T=7, H=2, P=3, N=4, R=R, h0=h0, prev=prev)
+    rng = np.random.default_rng(seed + 1000)
+    if flags & oracle.A_PER_TOKEN:
+        d["A"] = -np.exp(rng.uniform(-4, 0, size=d["dt"].shape))
+    dy = rng.standard_normal(d["x"].shape)
+    dhT = rng.standard_normal((2, 2, 3, 4)) if with_dhT else None
+    g = oracle.scan_backward(d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"], d["C"],
+                             d["h0"], d["x_prev"], d["B_prev"], dy, dhT, flags=flags, lib_path=lib)
+    eps = 1e-6
+    for name in oracle.GRAD_NAMES:
+        if d.get(name) is None:
+            assert g[name] is None, name
+            continue
+        v = rng.standard_normal(d[name].shape)
+        dp = dict(d)
+        dp[name] = d[name] + eps * v
+        dm = dict(d)
+        dm[name] = d[name] - eps * v
+        fd = (_loss(lib, dp, dy, dhT, flags) - _loss(lib, dm, dy, dhT, flags)) / (2 * eps)
+        an = float(np.sum(g[name] * v))
+        assert abs(fd - an) <= tol * max(1.0, abs(fd)), f"d{name}: analytic {an:.10e} vs fd {fd:.10e}"
+
+
+def check_backward_siso(lib):
+    """Gradients of the single-input scan, with h0, the token before and dhT."""
+    _fd_case(lib, 40, R=1)
+
+
+def check_backward_mimo_and_flags(lib):
+    """Rank 3; theta as the angle itself; A per token; no h0 / previous
+    token / dhT."""
+    _fd_case(lib, 41, R=3)
+    _fd_case(lib, 42, flags=oracle.THETA_IS_ANGLE, R=2)
+    _fd_case(lib, 43, flags=oracle.A_PER_TOKEN, R=1)
+    _fd_case(lib, 44, R=2, h0=False, prev=False, with_dhT=False)
+
+
+# ---------------------------------------------------------------------------
 # B/C preparation (RMS normalisation, weight, per-head bias)
 def _bc_case(seed, rows=3, G=2, H=4, N=8, R=3):
     rng = np.random.default_rng(seed)
@@ -418,4 +465,5 @@ ALL_CHECKS = [check_euler_special_case, check_complex_form, check_rope_frame,
               check_unrolled, check_closed_form, check_parity, check_second_order,
               check_mimo_sum_of_siso, check_split_and_decode,
               check_linearity_and_independence, check_a_per_token, check_bc_prep_unit_rms,
-              check_bc_prep_scale_invariance, check_bc_prep_bias_weight_eps]
+              check_bc_prep_scale_invariance, check_bc_prep_bias_weight_eps, check_backward_siso,
+              check_backward_mimo_and_flags]

@@ -88,6 +88,13 @@ MUTANTS = {
     "bc_bias_by_group": ("bias[(h * N + n) * R + r]", "bias[(g * N + n) * R + r]"),
     "bc_bias_inside_norm": ("wn * v[n * R + r] * scale + bn;", "wn * (v[n * R + r] + bn) * scale;"),
     "bc_weight_by_rank": ("w ? w[n] : 1.0", "w ? w[r] : 1.0"),
+    "bwd_rotation_derivative_sign": ("dphi += -g0 * w1 + g1 * w0;", "dphi += g0 * w1 - g1 * w0;"),
+    "bwd_adjoint_rotation_sign": ("V[p * N + 2 * k] = cs * g0 + sn * g1;", "V[p * N + 2 * k] = cs * g0 - sn * g1;"),
+    "bwd_state_gradient_without_decay": ("G[i] = alpha * V[i];", "G[i] = V[i];"),
+    "bwd_beta_chain_without_decay_term": ("(1.0 - LM) * alpha * (1.0 + DT * AA) * dbeta", "(1.0 - LM) * alpha * dbeta"),
+    "bwd_theta_without_dt": ("dtheta[bth * K + k] = angle ? dphi : DT * dphi;", "dtheta[bth * K + k] = dphi;"),
+    "bwd_output_grad_skipped": ("G[p * N + n] += v;", "G[p * N + n] += 0.0 * v;"),
+    "bwd_prev_x_uses_gamma": ("gx[t * P * R + p * R + r] += beta * v;", "gx[t * P * R + p * R + r] += gamma * v;"),
     "bc_norm_over_all_ranks": ("for (int64_t n = 0; n < N; ++n) ms += v[n * R + r] * v[n * R + r];",
                                "for (int64_t n = 0; n < N * R; ++n) ms += v[n] * v[n];"),
 }
