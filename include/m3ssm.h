@@ -135,6 +135,34 @@ m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
                           const void* x_prev, const void* B_prev, void* y,
                           float* hT, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace m3_scan_prefill_backward needs for `dims` (0
+ * if dims is invalid). */
+size_t m3_prefill_backward_workspace_size(const m3_dims* dims);
+
+/* Gradients of the prefill scan [the recurrence of the same article,
+ * sections 1.1-1.3, differentiated; the pages do not describe a backward
+ * pass]: for the loss L = <y, dy> + <hT, dhT> (dhT NULL = 0) over the
+ * outputs of m3_scan_prefill with the same inputs, writes dL/d of each
+ * input, all fp32 in the layout of that input:
+ *   dx [Bsz,T,H,P,R], ddt and dlam [Bsz,T,H], dA [H] (or [Bsz,T,H] with
+ *   M3_A_PER_TOKEN), dtheta [Bsz,T,G,N/2], dB and dC [Bsz,T,G,N,R],
+ *   dh0 [Bsz,H,P,N] (NULL: not written), dx_prev [Bsz,H,P,R] and dB_prev
+ *   [Bsz,G,N,R] (written when x_prev/B_prev are given and the pointers are
+ *   not NULL).
+ * dy has out_dtype and the layout of y.  dA and, with head groups, dB, dC,
+ * dtheta and dB_prev are sums over heads (and tokens), accumulated in place
+ * after the library clears them.  The forward chunk states are recomputed
+ * into ws.  Supported: R = 1 with the prefill's (P, N) shapes and Q = 64;
+ * dims->bc must be NULL; otherwise M3_ERR_UNSUPPORTED. */
+m3_status m3_scan_prefill_backward(const m3_dims* dims, const void* x, const void* dt,
+                                   const float* A, const void* lam, const void* theta,
+                                   const void* B, const void* C, const float* h0,
+                                   const void* x_prev, const void* B_prev, const void* dy,
+                                   const float* dhT, float* dx, float* ddt, float* dA,
+                                   float* dlam, float* dtheta, float* dB, float* dC,
+                                   float* dh0, float* dx_prev, float* dB_prev, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace m3_scan_prefill_varlen needs for `dims`
  * (dims->batch = number of sequences S, dims->seqlen = total tokens T); 0
  * if dims is invalid.  Besides the per-chunk totals it holds two small

@@ -86,6 +86,10 @@ def _lib():
         lib.m3_prefill_workspace_size.argtypes = [dp]
         lib.m3_scan_prefill.restype = ctypes.c_int
         lib.m3_scan_prefill.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        lib.m3_prefill_backward_workspace_size.restype = sz
+        lib.m3_prefill_backward_workspace_size.argtypes = [dp]
+        lib.m3_scan_prefill_backward.restype = ctypes.c_int
+        lib.m3_scan_prefill_backward.argtypes = [dp] + [vp] * 23 + [sz, vp]
         lib.m3_prefill_varlen_workspace_size.restype = sz
         lib.m3_prefill_varlen_workspace_size.argtypes = [dp]
         lib.m3_scan_prefill_varlen.restype = ctypes.c_int
@@ -211,6 +215,54 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
         raise M3Error(st, "m3_scan_prefill")
 
 
+def m3_prefill_backward_workspace_size(dims: m3_dims) -> int:
+    return int(_lib().m3_prefill_backward_workspace_size(ctypes.byref(dims)))
+
+
+GRAD_NAMES = ("x", "dt", "A", "lam", "theta", "B", "C", "h0", "x_prev", "B_prev")
+
+
+def m3_scan_prefill_backward(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, dy,
+                             dhT, grads: dict, ws, stream=None) -> None:
+    """grads: fp32 device tensors keyed by GRAD_NAMES (h0, x_prev, B_prev may
+    be missing or None)."""
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        Bsz, T, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
+        f32 = torch.float32
+        shapes = dict(x=(Bsz, T, H, P, R), dt=(Bsz, T, H), lam=(Bsz, T, H),
+                      A=(Bsz, T, H) if d.flags & M3_A_PER_TOKEN else (H,),
+                      theta=(Bsz, T, G, N // 2), B=(Bsz, T, G, N, R), C=(Bsz, T, G, N, R),
+                      h0=(Bsz, H, P, N), x_prev=(Bsz, H, P, R), B_prev=(Bsz, G, N, R))
+        for k, t in (("x", x), ("dt", dt), ("lam", lam), ("theta", theta), ("B", B), ("C", C)):
+            _check(k, t, shapes[k], ti)
+        _check("A", A, shapes["A"], f32)
+        _check("h0", h0, shapes["h0"], f32, optional=True)
+        _check("x_prev", x_prev, shapes["x_prev"], ti, optional=True)
+        _check("B_prev", B_prev, shapes["B_prev"], ti, optional=True)
+        _check("dy", dy, shapes["x"], to)
+        _check("dhT", dhT, shapes["h0"], f32, optional=True)
+        for k in GRAD_NAMES:
+            _check("d" + k, grads.get(k), shapes[k], f32,
+                   optional=k in ("h0", "x_prev", "B_prev"))
+    nbytes = 0
+    if ws is not None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous device tensor")
+        nbytes = ws.numel() * ws.element_size()
+    _check_bc(d)
+    gp = lambda k: _ptr(grads.get(k))
+    st = _lib().m3_scan_prefill_backward(
+        ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta), _ptr(B), _ptr(C),
+        _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(dy), _ptr(dhT), gp("x"), gp("dt"), gp("A"),
+        gp("lam"), gp("theta"), gp("B"), gp("C"), gp("h0"), gp("x_prev"), gp("B_prev"), _ptr(ws),
+        nbytes, _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_prefill_backward")
+
+
 def m3_prefill_varlen_workspace_size(dims: m3_dims) -> int:
     return int(_lib().m3_prefill_varlen_workspace_size(ctypes.byref(dims)))
 
@@ -327,6 +379,29 @@ def workspace(dims: m3_dims, device, varlen=False) -> torch.Tensor:
     if n == 0:
         raise M3Error(2, "m3_prefill_workspace_size")
     return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def scan_prefill_backward(x, dt, A, lam, theta, B, C, dy, h0=None, x_prev=None, B_prev=None,
+                          dhT=None, flags=0, chunk=0, stream=None) -> dict:
+    """Allocate the fp32 gradients (and workspace) and call
+    m3_scan_prefill_backward.  Returns a dict keyed by GRAD_NAMES."""
+    Bsz, T, H, P, R = x.shape
+    G, N = B.shape[2], B.shape[3]
+    d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(dy.dtype), flags,
+                  0 if G == H else G)
+    dev, f32 = x.device, torch.float32
+    like = lambda t: None if t is None else torch.empty(t.shape, dtype=f32, device=dev)
+    grads = {k: like(v) for k, v in (("x", x), ("dt", dt), ("A", A), ("lam", lam),
+                                      ("theta", theta), ("B", B), ("C", C), ("x_prev", x_prev),
+                                      ("B_prev", B_prev))}
+    grads["h0"] = torch.empty((Bsz, H, P, N), dtype=f32, device=dev) if h0 is not None else None
+    n = m3_prefill_backward_workspace_size(d)
+    if n == 0:
+        raise M3Error(2, "m3_prefill_backward_workspace_size")
+    ws = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    m3_scan_prefill_backward(d, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, dy, dhT, grads,
+                             ws, stream)
+    return grads
 
 
 def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=None,

@@ -138,6 +138,82 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   return hip_status(err);
 }
 
+size_t m3_prefill_backward_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true) != M3_OK) return 0;
+  return m3::backward_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
+                                      groups_of(d), chunk_of(d));
+}
+
+m3_status m3_scan_prefill_backward(const m3_dims* d, const void* x, const void* dt,
+                                   const float* A, const void* lam, const void* theta,
+                                   const void* B, const void* C, const float* h0,
+                                   const void* x_prev, const void* B_prev, const void* dy,
+                                   const float* dhT, float* dx, float* ddt, float* dA,
+                                   float* dlam, float* dtheta, float* dB, float* dC, float* dh0,
+                                   float* dx_prev, float* dB_prev, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  m3_status st = check_dims(d, true);
+  if (st != M3_OK) return st;
+  if (d->bc) return M3_ERR_UNSUPPORTED;
+  if (!x || !dt || !A || !lam || !theta || !B || !C || !dy) return M3_ERR_NULL;
+  if (!dx || !ddt || !dA || !dlam || !dtheta || !dB || !dC) return M3_ERR_NULL;
+  if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
+  const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, dy, dhT, dx, ddt, dA,
+                        dlam, dtheta, dB, dC, dh0, dx_prev, dB_prev, ws};
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return M3_ERR_ALIGN;
+  const int Q = chunk_of(d);
+  const int in_bf16 = d->in_dtype == M3_BF16;
+  if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16) ||
+      !m3::backward_supported(d->headdim, d->dstate, d->rank, Q))
+    return M3_ERR_UNSUPPORTED;
+  const size_t need = m3::backward_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim,
+                                                   d->dstate, groups_of(d), Q);
+  if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
+
+  m3::BackwardArgs g{};
+  m3::PrefillArgs& a = g.f;
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.lam = lam;
+  a.theta = theta;
+  a.B = B;
+  a.C = C;
+  a.h0 = h0;
+  a.xp = x_prev;
+  a.Bp = B_prev;
+  a.Bsz = d->batch;
+  a.T = d->seqlen;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.N = d->dstate;
+  a.R = d->rank;
+  a.Q = Q;
+  a.nchunk = (d->seqlen + Q - 1) / Q;
+  a.G = groups_of(d);
+  a.flags = d->flags;
+  a.has_prev = x_prev != nullptr;
+  g.dy = dy;
+  g.dhT = dhT;
+  g.dx = dx;
+  g.ddt = ddt;
+  g.dA = dA;
+  g.dlam = dlam;
+  g.dtheta = dtheta;
+  g.dB = dB;
+  g.dC = dC;
+  g.dh0 = dh0;
+  g.dx_prev = x_prev ? dx_prev : nullptr;
+  g.dB_prev = x_prev ? dB_prev : nullptr;
+  m3::backward_carve(g, ws);
+  hipError_t err = hipSuccess;
+  if (m3::launch_backward(g, in_bf16, d->out_dtype == M3_BF16, static_cast<hipStream_t>(stream),
+                          &err) != 0)
+    return M3_ERR_UNSUPPORTED;
+  return hip_status(err);
+}
+
 size_t m3_prefill_varlen_workspace_size(const m3_dims* d) {
   if (check_dims(d, true) != M3_OK) return 0;
   return m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,

@@ -1,0 +1,724 @@
+// backward.hip -- gradients of the chunked prefill scan (single input), gfx950.
+//
+// For L = <y, dy> + <h_T, dh_T> the kernels return dL/d of x, dt, A, lam,
+// theta, B, C, h0, x_prev and B_prev, for the recurrence of the Mamba-3
+// article [xxxxx.co.kr, sections 1.1-1.3] in the chunked form the forward
+// kernels use (prefill.hip): inside a chunk, with Bt = R(-Phi_t) B_t and
+// Ct = R(-Phi_t) C_t,
+//   y_t   = e^{cs_t} Shat Ct_t + sum_{u<=t} M[t,u] (Ct_t . Bt_u) x_u,
+//   M[t,u] = e^{cs_t - cs_u} (gamma_u + [u < t] (1 - lam_{u+1}) dt_{u+1}),
+//   S_end = R(Phi_end) (e^{cs_end} Shat + sum_u M[end,u] x_u Bt_u^T).
+// Gradients, with G_end = dL/dS_end (the next chunk's dL/dShat, or dh_T)
+// and Gt = the rows of G_end rotated by -Phi_end:
+//   dShat_c = sum_t e^{cs_t} dy_t Ct_t^T + e^{cs_end} Gt        (chunk to chunk)
+//   W1 = M o (Ct Bt^T),  W2 = M o (dY X^T)
+//   dx  = W1^T dY + diag(m_end) Bt Gt^T
+//   dBt = W2^T Ct + diag(m_end) X Gt,   dCt = W2 Bt + diag(e^{cs}) dY Shat
+//   dM[t,u] = (Ct_t . Bt_u)(dy_t . x_u) -> cs, gamma, (1 - lam) dt
+//   dPhi_t = cross(dBt_t, Bt_t) + cross(dCt_t, Ct_t) (+ <G_end, J S_end> at the end)
+// then prefix-sum adjoints (reverse cumulative sums over the chunk) give the
+// per-token log-decay and phase gradients, chained to dt, A, lam, theta;
+// dB = R(Phi) dBt, dC = R(Phi) dCt.  The trapezoid's left-endpoint term
+// that crosses into the next chunk is (1 - lam) dt of that chunk's first
+// token times x B^T of this chunk's last token: its x and B gradients are
+// added here, its scalar gradient by the next chunk.
+//
+// Launches: the forward chunk kernels (entry states and h_T into the
+// workspace), then
+//  k_bwd_chunk_adjoint (batch, head, chunk): sum_t e^{cs_t} dy_t Ct_t^T;
+//  k_bwd_state_pass    (batch, head, slice): the reverse pass over chunks;
+//  k_bwd_chunk         (batch, head, chunk): every per-token gradient.
+// Arithmetic is plain fp32 FMA on LDS tiles.
+#include "chunk_common.h"
+
+namespace m3 {
+
+namespace {
+
+constexpr int kNT1 = 256;   // threads of the chunk-adjoint kernel
+constexpr int kNT3 = 512;   // threads of the per-chunk gradient kernel
+
+template <typename T>
+__device__ __forceinline__ float ldy(const void* p, int64_t i) {
+  return ld1(static_cast<const T*>(p), i);
+}
+
+// rotate one pair by -angle / +angle given (cos, sin)
+__device__ __forceinline__ f2 rot_neg(f2 v, f2 cs) { return f2{cs.x * v.x + cs.y * v.y, -cs.y * v.x + cs.x * v.y}; }
+__device__ __forceinline__ f2 rot_pos(f2 v, f2 cs) { return f2{cs.x * v.x - cs.y * v.y, cs.y * v.x + cs.x * v.y}; }
+
+// --------------------------------------------------------------------------
+// sum_t e^{cs_t} dy_t Ct_t^T of one chunk (P x N) into dS
+template <typename TI, typename TY, int P, int N>
+__global__ __launch_bounds__(kNT1) void k_bwd_chunk_adjoint(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  constexpr int EPT = P * N / kNT1;   // outputs per thread, along one row
+  static_assert(EPT >= 1 && N % EPT == 0, "outputs per thread");
+  __shared__ Tables<N, false> tb;
+  __shared__ TableScratch<N, kNT1> scr;
+  __shared__ alignas(16) float Cs[kQ][N];
+  __shared__ alignas(16) float Ys[kQ][P];
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
+  ThetaBlock<TI, N, kNT1> thb;
+  thb.load(a, b, h, c0, Lc);
+  chunk_tables<TI, N, kNT1>(a, thb, Lc, tb, scr, 0);
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C) + group_index(a, b, c0, h) * N;
+  for (int i = tid; i < kQ * (N / 2); i += kNT1) {
+    const int t = i / (N / 2), k = i % (N / 2);
+    f2 v = f2{0.0f, 0.0f};
+    if (t < Lc) {
+      const f2 c = ld2(Cg, (int64_t)t * a.G * N + 2 * k);
+      v = rot_neg(c, tb.cs_of(t, k)) * expf((float)tb.cs[t]);
+    }
+    Cs[t][2 * k] = v.x;
+    Cs[t][2 * k + 1] = v.y;
+  }
+  const int64_t y0 = token_index(a, b, c0, h) * P;
+  for (int i = tid; i < kQ * P; i += kNT1) {
+    const int t = i / P, p = i % P;
+    Ys[t][p] = t < Lc ? ldy<TY>(g.dy, y0 + (int64_t)t * a.H * P + p) : 0.0f;
+  }
+  __syncthreads();
+  const int e0 = tid * EPT, p = e0 / N, n0 = e0 % N;
+  float acc[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) acc[j] = 0.0f;
+  for (int t = 0; t < Lc; ++t) {
+    const float yv = Ys[t][p];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) acc[j] += yv * Cs[t][n0 + j];
+  }
+  float* __restrict__ out = g.dS + ck.id * (P * N) + e0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) out[j] = acc[j];
+}
+
+// --------------------------------------------------------------------------
+// reverse pass over the chunks of one (batch, head): dShat_c = D_c +
+// decay_c R(-Phi_end,c) dShat_{c+1} (rows), from dShat_C = dh_T; one 4-vector
+// of the state per lane
+template <int N>
+__global__ __launch_bounds__(64) void k_bwd_state_pass(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  const int P = a.P;
+  const int wpb = P * N / 4 / 64;
+  const int bh = blockIdx.x / wpb;
+  const int vi = (blockIdx.x % wpb) * 64 + threadIdx.x;
+  const int p = vi / (N / 4), n = 4 * (vi % (N / 4));
+  const int64_t off = (int64_t)p * N + n;
+  f4 G = g.dhT ? *reinterpret_cast<const f4*>(g.dhT + (int64_t)bh * P * N + off) : f4{0, 0, 0, 0};
+  const int64_t cbase = (int64_t)bh * a.nchunk;
+  for (int c = a.nchunk - 1; c >= 0; --c) {
+    const int64_t cid = cbase + c;
+    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
+    const f2 r0 = re[n / 2], r1 = re[n / 2 + 1];
+    const float dcy = a.decay[cid];
+    f4* dst = reinterpret_cast<f4*>(g.dS + cid * P * N + off);
+    const f2 g0 = rot_neg(f2{G.x, G.y}, r0), g1 = rot_neg(f2{G.z, G.w}, r1);
+    const f4 D = *dst;
+    G = f4{D.x + dcy * g0.x, D.y + dcy * g0.y, D.z + dcy * g1.x, D.w + dcy * g1.y};
+    *dst = G;
+  }
+  if (g.dh0) *reinterpret_cast<f4*>(g.dh0 + (int64_t)bh * P * N + off) = G;
+}
+
+// --------------------------------------------------------------------------
+template <int P, int N>
+struct BwdSmem {
+  Tables<N, false> tb;
+  float lam[kQ], Av[kQ], ecs[kQ];
+  float dcs[kQ], dgam[kQ], dbpr[kQ], dmend[kQ];
+  float dphi_end[N / 2];
+  float red[kNT3 / 64];
+  float part[kNT3];               // per-thread partial sums, summed in a fixed order
+  union alignas(16) {
+    TableScratch<N, kNT3> scr;
+    float Bt[kQ][N];              // rotated B rows
+  } ub;
+  alignas(16) float Ct[kQ][N];    // rotated C rows
+  alignas(16) float Xs[kQ][P];
+  alignas(16) float Ys[kQ][P];    // dy
+  union alignas(16) {
+    float W[kQ][kQ];              // masked Gram products
+    float Z[P][N];                // Shat, then the rotated G_end
+    float dphi[kQ][N / 2];        // phase gradients, then their suffix sums
+  } uz;
+};
+
+// block-wide sum (all threads receive it); red holds one value per wave
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = group_sum<64>(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kNT3 / 64; ++w) s += red[w];
+  return s;
+}
+
+template <typename TI, typename TY, int P, int N>
+__global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  constexpr int NP = N / 2;
+  constexpr int WP = P / 8, WN = N / 8;   // a row's columns per thread (8 threads per row)
+  static_assert(WP >= 1 && WN >= 2 && WN % 2 == 0, "row split");
+  __shared__ BwdSmem<P, N> sm;
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const bool last = c + 1 >= a.nchunk;
+  const int row = tid >> 3, cg = tid & 7;
+  const int p0 = cg * WP, n0 = cg * WN;
+  const int G = a.G;
+  const bool shared_grp = G != a.H;   // several heads add into one B, C, theta gradient
+
+  ThetaBlock<TI, N, kNT3> thb;
+  thb.load(a, b, h, c0, Lc);
+  chunk_tables<TI, N, kNT3>(a, thb, Lc, sm.tb, sm.ub.scr, 0);
+  if (tid < kQ) {
+    sm.lam[tid] = thb.l;
+    sm.Av[tid] = thb.A;
+    sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
+    sm.dcs[tid] = sm.dgam[tid] = sm.dbpr[tid] = sm.dmend[tid] = 0.0f;
+  }
+  if (tid < NP) sm.dphi_end[tid] = 0.0f;
+  __syncthreads();   // th_raw (in ub) is free
+
+  // rotated B and C rows, x and dy
+  const int64_t gi = group_index(a, b, c0, h);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B) + gi * N;
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C) + gi * N;
+  for (int i = tid; i < kQ * NP; i += kNT3) {
+    const int t = i / NP, k = i % NP;
+    f2 bv = f2{0.0f, 0.0f}, cv = bv;
+    if (t < Lc) {
+      const f2 cs = sm.tb.cs_of(t, k);
+      bv = rot_neg(ld2(Bg, (int64_t)t * G * N + 2 * k), cs);
+      cv = rot_neg(ld2(Cg, (int64_t)t * G * N + 2 * k), cs);
+    }
+    sm.ub.Bt[t][2 * k] = bv.x;
+    sm.ub.Bt[t][2 * k + 1] = bv.y;
+    sm.Ct[t][2 * k] = cv.x;
+    sm.Ct[t][2 * k + 1] = cv.y;
+  }
+  const int64_t ti0 = token_index(a, b, c0, h);
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x) + ti0 * P;
+  for (int i = tid; i < kQ * P; i += kNT3) {
+    const int t = i / P, p = i % P;
+    const bool ok = t < Lc;
+    sm.Xs[t][p] = ok ? ld1(Xg, (int64_t)t * a.H * P + p) : 0.0f;
+    sm.Ys[t][p] = ok ? ldy<TY>(g.dy, (ti0 + (int64_t)t * a.H) * P + p) : 0.0f;
+  }
+  __syncthreads();
+
+  const double cs_end = sm.tb.cs[Lc - 1];
+  auto wgt = [&](int t, int u) {   // w_{t,u}, u <= t
+    return sm.tb.gam[u] + (u < t ? sm.tb.bpr[u + 1] : 0.0f);
+  };
+
+  // ---- Gram products of a 2 x 4 block of (t, u), the decay mask and its gradient
+  float w2v[2][4];
+  {
+    const int tb0 = 2 * (tid >> 4), ub0 = 4 * (tid & 15);
+    float k1[2][4], k2[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k1[i][j] = k2[i][j] = 0.0f;
+#pragma unroll 2
+    for (int n = 0; n < N; n += 4) {
+      f4 cr[2], br[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) cr[i] = *reinterpret_cast<const f4*>(&sm.Ct[tb0 + i][n]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) br[j] = *reinterpret_cast<const f4*>(&sm.ub.Bt[ub0 + j][n]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          k1[i][j] += cr[i].x * br[j].x + cr[i].y * br[j].y + cr[i].z * br[j].z + cr[i].w * br[j].w;
+    }
+#pragma unroll 2
+    for (int p = 0; p < P; p += 2) {
+      f2 yr[2], xr[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) yr[i] = *reinterpret_cast<const f2*>(&sm.Ys[tb0 + i][p]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const f2*>(&sm.Xs[ub0 + j][p]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) k2[i][j] += yr[i].x * xr[j].x + yr[i].y * xr[j].y;
+    }
+    // the mask gradient dM = (Ct . Bt)(dy . x) goes through W twice so that
+    // its row and column sums run in a fixed order: first dM M (log-decay),
+    // then dM e^{cs_t - cs_u} (the trapezoid weights); then W takes W1
+    float em[2][4], mm[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = tb0 + i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = ub0 + j;
+        const bool in = u <= t && t < Lc;
+        em[i][j] = in ? expf((float)(sm.tb.cs[t] - sm.tb.cs[u])) : 0.0f;
+        mm[i][j] = in ? em[i][j] * wgt(t, u) : 0.0f;
+        sm.uz.W[t][u] = k1[i][j] * k2[i][j] * mm[i][j];
+      }
+    }
+    __syncthreads();
+    if (tid < kQ) {   // dcs[x] = sum_u dM M [x][u] - sum_t dM M [t][x]
+      float r = 0.0f, cl = 0.0f;
+      for (int u = 0; u < kQ; ++u) r += sm.uz.W[tid][u];
+      for (int t = 0; t < kQ; ++t) cl += sm.uz.W[t][tid];
+      sm.dcs[tid] = r - cl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.uz.W[tb0 + i][ub0 + j] = k1[i][j] * k2[i][j] * em[i][j];
+    __syncthreads();
+    if (tid < kQ) {   // dgam[u] = sum_{t >= u}, dbpr[u + 1] = sum_{t > u}
+      const int u = tid;
+      float off = 0.0f;
+      for (int t = u + 1; t < kQ; ++t) off += sm.uz.W[t][u];
+      sm.dgam[u] = off + sm.uz.W[u][u];
+      if (u + 1 < kQ) sm.dbpr[u + 1] = off;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sm.uz.W[tb0 + i][ub0 + j] = mm[i][j] * k1[i][j];
+        w2v[i][j] = mm[i][j] * k2[i][j];
+      }
+  }
+  __syncthreads();
+
+  // ---- dx = W1^T dY
+  float dxv[WP];
+#pragma unroll
+  for (int j = 0; j < WP; ++j) dxv[j] = 0.0f;
+  for (int t = row; t < Lc; ++t) {
+    const float w = sm.uz.W[t][row];
+#pragma unroll
+    for (int j = 0; j < WP; ++j) dxv[j] += w * sm.Ys[t][p0 + j];
+  }
+  __syncthreads();
+  {
+    const int tb0 = 2 * (tid >> 4), ub0 = 4 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.uz.W[tb0 + i][ub0 + j] = w2v[i][j];
+  }
+  __syncthreads();
+
+  // ---- dCt = W2 Bt, dBt = W2^T Ct
+  float dcv[WN], dbv[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) dcv[j] = dbv[j] = 0.0f;
+  for (int u = 0; u <= row && u < Lc; ++u) {
+    const float w = sm.uz.W[row][u];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) dcv[j] += w * sm.ub.Bt[u][n0 + j];
+  }
+  for (int t = row; t < Lc; ++t) {
+    const float w = sm.uz.W[t][row];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) dbv[j] += w * sm.Ct[t][n0 + j];
+  }
+  __syncthreads();
+
+  // ---- the entry state: dCt += e^{cs_t} dY Shat, and d(e^{cs_t})
+  const float* __restrict__ Sh = a.S + ck.id * (P * N);
+  for (int i = tid; i < P * N / 4; i += kNT3)
+    reinterpret_cast<f4*>(&sm.uz.Z[0][0])[i] = reinterpret_cast<const f4*>(Sh)[i];
+  __syncthreads();
+  {
+    float q[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) q[j] = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const float yv = sm.Ys[row][p];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) q[j] += yv * sm.uz.Z[p][n0 + j];
+    }
+    float de = 0.0f;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      dcv[j] += sm.ecs[row] * q[j];
+      de += sm.Ct[row][n0 + j] * q[j];
+    }
+    de = group_sum<8>(de);
+    if (cg == 0 && row < Lc) sm.dcs[row] += sm.ecs[row] * de;
+  }
+  __syncthreads();
+
+  // ---- the end state: Gt (rows of G_end rotated by -Phi_end), <Gt, Shat>,
+  // the end rotation's phase gradient <G_end, J S_end> and the own token 0's
+  // left-endpoint term <dShat_c, x_{c0-1} B_{c0-1}^T>
+  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
+                                        : g.dS + (ck.id + 1) * (P * N);
+  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
+                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
+                            : 0.0f;
+  const TI* __restrict__ Blast = Bg + (int64_t)(Lc - 1) * G * N;   // raw B of the last token
+  // the token before this chunk: x_{c0-1}, B_{c0-1} (x_prev / B_prev at the start)
+  const TI* xprev = nullptr;
+  const TI* bprev = nullptr;
+  if (c > 0) {
+    xprev = Xg - (int64_t)a.H * P;
+    bprev = Bg - (int64_t)G * N;
+  } else if (a.has_prev) {
+    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P;
+    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G + head_group(a, h)) * N;
+  }
+  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
+  static_assert(kNT3 % NP == 0, "each thread keeps one pair in the end-state loop");
+  {
+    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
+    const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
+                                           : a.S + (ck.id + 1) * (P * N);
+    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
+    for (int i = tid; i < P * NP; i += kNT3) {
+      const int p = i / NP, k = i % NP;
+      const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * k) : f2{0.0f, 0.0f};
+      const f2 gt = rot_neg(gv, re[k]);
+      sm.uz.Z[p][2 * k] = gt.x;
+      sm.uz.Z[p][2 * k + 1] = gt.y;
+      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)p * N + 2 * k);
+      e_part += gt.x * sh.x + gt.y * sh.y;
+      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * k);
+      if (ck.next) {
+        const float xl = sm.Xs[Lc - 1][p];
+        const f2 bl = ld2(Blast, 2 * k);
+        se.x -= bpL * xl * bl.x;
+        se.y -= bpL * xl * bl.y;
+      }
+      ph_part += -gv.x * se.y + gv.y * se.x;   // pair k = tid % NP throughout
+      if (xprev) {
+        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * k);
+        const f2 bq = ld2(bprev, 2 * k);
+        h_part += ld1(xprev, p) * (ds.x * bq.x + ds.y * bq.y);
+      }
+    }
+  }
+  sm.part[tid] = ph_part;
+  const float e_end = block_sum(e_part, sm.red);
+  const float h_end = block_sum(h_part, sm.red);   // also orders the Z and part writes
+  if (tid < NP) {
+    float v = 0.0f;
+    for (int m = 0; m < kNT3 / NP; ++m) v += sm.part[tid + NP * m];
+    sm.dphi_end[tid] = v;
+  }
+  // dx += m_end Bt Gt^T (with the crossing left-endpoint term of the last
+  // token), dm_end, dBt += m_end X Gt.  The crossing term's B gradient is
+  // kept apart (hbv): that term holds the raw B, so it adds nothing to the
+  // phase gradient of the token's rotated row.
+  float hbv[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) hbv[j] = 0.0f;
+  if (row < Lc) {
+    const float e = expf((float)(cs_end - sm.tb.cs[row]));
+    const float cu = e * wgt(Lc - 1, row) + (row == Lc - 1 ? bpL : 0.0f);
+    float v[WP];
+#pragma unroll
+    for (int j = 0; j < WP; ++j) v[j] = 0.0f;
+#pragma unroll 2
+    for (int n = 0; n < N; n += 4) {
+      const f4 bt = *reinterpret_cast<const f4*>(&sm.ub.Bt[row][n]);
+#pragma unroll
+      for (int j = 0; j < WP; ++j) {
+        const f4 z = *reinterpret_cast<const f4*>(&sm.uz.Z[p0 + j][n]);
+        v[j] += bt.x * z.x + bt.y * z.y + bt.z * z.z + bt.w * z.w;
+      }
+    }
+    float dme = 0.0f;
+#pragma unroll
+    for (int j = 0; j < WP; ++j) {
+      dxv[j] += cu * v[j];
+      dme += sm.Xs[row][p0 + j] * v[j];
+    }
+    dme = group_sum<8>(dme);
+    if (cg == 0) sm.dmend[row] = dme;
+    float w[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) w[j] = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const float xv = sm.Xs[row][p];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) w[j] += xv * sm.uz.Z[p][n0 + j];
+    }
+    const float mu = cu - (row == Lc - 1 ? bpL : 0.0f);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      dbv[j] += mu * w[j];
+      hbv[j] = (cu - mu) * w[j];
+    }
+  }
+  __syncthreads();
+  if (tid < Lc) {   // the end-state weights m_end[u] = e^{cs_end - cs_u} w_{end,u}
+    const int u = tid;
+    const float e = expf((float)(cs_end - sm.tb.cs[u]));
+    const float m = e * wgt(Lc - 1, u);
+    const float d = sm.dmend[u];
+    sm.part[u] = 0.0f;
+    if (u < Lc - 1) {
+      sm.part[u] = d * m;
+      sm.dcs[u] -= d * m;
+      sm.dbpr[u + 1] += d * e;
+    }
+    sm.dgam[u] += d * e;
+  }
+  __syncthreads();
+  if (tid == 0) {   // the chunk's last token: the end state's decay and weights
+    float v = expf((float)cs_end) * e_end;
+    for (int u = 0; u < Lc - 1; ++u) v += sm.part[u];
+    sm.dcs[Lc - 1] += v;
+    sm.dbpr[0] += h_end;
+  }
+  __syncthreads();   // Z is free
+
+  // ---- phase gradients per (token, pair), then suffix sums over the chunk
+#pragma unroll
+  for (int j = 0; j < WN; j += 2) {
+    const int n = n0 + j;
+    float v = 0.0f;
+    if (row < Lc) {
+      v = dbv[j] * sm.ub.Bt[row][n + 1] - dbv[j + 1] * sm.ub.Bt[row][n] +
+          dcv[j] * sm.Ct[row][n + 1] - dcv[j + 1] * sm.Ct[row][n];
+    }
+    sm.uz.dphi[row][n / 2] = v;
+  }
+  __syncthreads();
+  if (tid < NP) {
+    const int k = tid;
+    float run = sm.dphi_end[k];
+    for (int t = Lc - 1; t >= 0; --t) {
+      run += sm.uz.dphi[t][k];
+      sm.uz.dphi[t][k] = run;
+    }
+  } else if (tid == NP) {   // log-decay: suffix sums of dcs
+    float run = 0.0f;
+    for (int t = Lc - 1; t >= 0; --t) {
+      run += sm.dcs[t];
+      sm.dcs[t] = run;
+    }
+  }
+  __syncthreads();
+
+  // ---- outputs
+  const bool angle = (a.flags & kThetaIsAngle) != 0;
+  float dt_theta = 0.0f;
+  if (row < Lc) {
+    const int t = row;
+    const int64_t tok = ti0 + (int64_t)t * a.H;                    // (b, c0 + t, h)
+    const int64_t grp = gi + (int64_t)t * G;                      // (b, c0 + t, group)
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + grp * NP;
+    const float dtt = sm.tb.dt[t];
+#pragma unroll
+    for (int j = 0; j < WN; j += 2) {
+      const int k = (n0 + j) / 2;
+      const float dph = sm.uz.dphi[t][k];
+      const float dth = angle ? dph : dtt * dph;
+      if (!angle) dt_theta += ld1(th, k) * dph;
+      const f2 cs = sm.tb.cs_of(t, k);
+      const f2 db = rot_pos(f2{dbv[j] + hbv[j], dbv[j + 1] + hbv[j + 1]}, cs);
+      const f2 dc = rot_pos(f2{dcv[j], dcv[j + 1]}, cs);
+      // with head groups every head writes its own slot; a final pass sums
+      // the group's heads in a fixed order
+      const int64_t slot = shared_grp ? tok : grp;
+      *reinterpret_cast<f2*>((shared_grp ? g.dBh : g.dB) + slot * N + n0 + j) = db;
+      *reinterpret_cast<f2*>((shared_grp ? g.dCh : g.dC) + slot * N + n0 + j) = dc;
+      (shared_grp ? g.dthh : g.dtheta)[slot * NP + k] = dth;
+    }
+#pragma unroll
+    for (int j = 0; j < WP; ++j) g.dx[tok * P + p0 + j] = dxv[j];
+  }
+  dt_theta = group_sum<8>(dt_theta);
+  float da_part = 0.0f;
+  if (row < Lc && cg == 0) {
+    const int t = row;
+    const int64_t tok = ti0 + (int64_t)t * a.H;
+    const float dtt = sm.tb.dt[t], lm = sm.lam[t], da = sm.dcs[t];
+    g.ddt[tok] = sm.Av[t] * da + lm * sm.dgam[t] + (1.0f - lm) * sm.dbpr[t] + dt_theta;
+    g.dlam[tok] = dtt * (sm.dgam[t] - sm.dbpr[t]);
+    if (a.flags & kAPerToken) g.dA[tok] = dtt * da;
+    else da_part = dtt * da;
+  }
+  if (!(a.flags & kAPerToken)) {   // per chunk; a final pass sums them per head
+    const float s = block_sum(da_part, sm.red);
+    if (tid == 0) g.dApart[ck.id] = s;
+  }
+  // the token before the sequence: dx_prev = beta'_0 dShat_0 B_prev,
+  // dB_prev = beta'_0 dShat_0^T x_prev
+  if (c == 0 && a.has_prev && (g.dx_prev || g.dB_prev)) {
+    const float bp0 = sm.tb.bpr[0];
+    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
+    if (g.dx_prev && tid < P) {
+      float v = 0.0f;
+      for (int n = 0; n < N; ++n) v += dSc[(int64_t)tid * N + n] * ld1(bprev, n);
+      g.dx_prev[((int64_t)b * a.H + h) * P + tid] = bp0 * v;
+    }
+    if (g.dB_prev && tid < N) {
+      float v = 0.0f;
+      for (int p = 0; p < P; ++p) v += dSc[(int64_t)p * N + tid] * ld1(xprev, p);
+      if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N + tid] = bp0 * v;
+      else g.dB_prev[((int64_t)b * G + head_group(a, h)) * N + tid] = bp0 * v;
+    }
+  }
+}
+
+// the sums a chunk kernel cannot finish alone, in a fixed order: dA over
+// (batch, chunk) per head, and with head groups the heads of each group
+__global__ void k_bwd_reduce_dA(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= a.H) return;
+  float v = 0.0f;
+  for (int b = 0; b < a.Bsz; ++b)
+    for (int c = 0; c < a.nchunk; ++c) v += g.dApart[((int64_t)b * a.H + h) * a.nchunk + c];
+  g.dA[h] = v;
+}
+
+// dst[i] = sum_j src[(i / (G E)) H E + (i / E % G) (H / G) E + j E + i % E], j < H / G
+__global__ void k_bwd_reduce_groups(const float* __restrict__ src, float* __restrict__ dst,
+                                    int64_t n, int H, int G, int E) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t row = i / ((int64_t)G * E);
+  const int grp = (int)(i / E % G), e = (int)(i % E), hpg = H / G;
+  const float* s = src + (row * H + (int64_t)grp * hpg) * E + e;
+  float v = 0.0f;
+  for (int j = 0; j < hpg; ++j) v += s[(int64_t)j * E];
+  dst[i] = v;
+}
+
+template <typename TI, typename TY, int P, int N>
+hipError_t run_backward(const BackwardArgs& g, int in_bf16, hipStream_t s) {
+  const PrefillArgs& a = g.f;
+  const dim3 grid(a.nchunk, a.H, a.Bsz);
+  hipLaunchKernelGGL((k_bwd_chunk_adjoint<TI, TY, P, N>), grid, dim3(kNT1), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
+  hipLaunchKernelGGL((k_bwd_state_pass<N>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(kNT3), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!(a.flags & kAPerToken)) {
+    hipLaunchKernelGGL(k_bwd_reduce_dA, dim3((a.H + 63) / 64), dim3(64), 0, s, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.G != a.H) {
+    auto red = [&](const float* src, float* dst, int64_t rows, int E) {
+      const int64_t n = rows * a.G * E;
+      hipLaunchKernelGGL(k_bwd_reduce_groups, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src,
+                         dst, n, a.H, a.G, E);
+      return hipGetLastError();
+    };
+    const int64_t tokens = (int64_t)a.Bsz * a.T;
+    if ((e = red(g.dBh, g.dB, tokens, N)) != hipSuccess) return e;
+    if ((e = red(g.dCh, g.dC, tokens, N)) != hipSuccess) return e;
+    if ((e = red(g.dthh, g.dtheta, tokens, N / 2)) != hipSuccess) return e;
+    if (g.dB_prev && (e = red(g.dBph, g.dB_prev, a.Bsz, N)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TI, typename TY>
+int dispatch_bwd(const BackwardArgs& g, int in_bf16, hipStream_t s, hipError_t* e) {
+  const PrefillArgs& a = g.f;
+#define M3_BWD_SHAPE(PP, NN)                                        \
+  if (a.P == PP && a.N == NN) {                                     \
+    *e = run_backward<TI, TY, PP, NN>(g, in_bf16, s);               \
+    return 0;                                                       \
+  }
+  M3_BWD_SHAPE(16, 16)
+  M3_BWD_SHAPE(64, 128)
+  M3_BWD_SHAPE(32, 64)
+  M3_BWD_SHAPE(64, 64)
+#undef M3_BWD_SHAPE
+  return -1;
+}
+
+size_t align256b(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+bool backward_supported(int P, int N, int R, int Q) {
+  if (R != 1 || Q != kQ) return false;
+  return (P == 16 && N == 16) || (P == 64 && N == 128) || (P == 32 && N == 64) || (P == 64 && N == 64);
+}
+
+// forward part, the chunk adjoints (P N per chunk), h_T, the per-chunk dA
+// partials and, with head groups, per-head B, C, theta and B_prev gradients
+static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int G, int Q, size_t* off) {
+  const size_t nchunk = (size_t)(T + Q - 1) / Q;
+  const size_t units = (size_t)Bsz * H * nchunk;
+  const size_t tokens = (size_t)Bsz * T;
+  size_t sz[8] = {prefill_workspace_bytes(Bsz, T, H, P, N, 1, Q, false), units * P * N * 4,
+                  (size_t)Bsz * H * P * N * 4, units * 4, 0, 0, 0, 0};
+  if (G != H) {
+    sz[4] = tokens * H * N * 4;
+    sz[5] = tokens * H * N * 4;
+    sz[6] = tokens * H * (N / 2) * 4;
+    sz[7] = (size_t)Bsz * H * N * 4;
+  }
+  size_t total = 0;
+  for (int i = 0; i < 8; ++i) {
+    if (off) off[i] = total;
+    total += align256b(sz[i]);
+  }
+  return total;
+}
+
+size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int G, int Q) {
+  return bwd_parts(Bsz, T, H, P, N, G, Q, nullptr);
+}
+
+void backward_carve(BackwardArgs& g, void* ws) {
+  PrefillArgs& a = g.f;
+  prefill_carve(a, ws);
+  size_t off[8];
+  bwd_parts(a.Bsz, a.T, a.H, a.P, a.N, a.G, a.Q, off);
+  char* p = static_cast<char*>(ws);
+  g.dS = reinterpret_cast<float*>(p + off[1]);
+  g.hTw = reinterpret_cast<float*>(p + off[2]);
+  g.dApart = reinterpret_cast<float*>(p + off[3]);
+  const bool grp = a.G != a.H;
+  g.dBh = grp ? reinterpret_cast<float*>(p + off[4]) : nullptr;
+  g.dCh = grp ? reinterpret_cast<float*>(p + off[5]) : nullptr;
+  g.dthh = grp ? reinterpret_cast<float*>(p + off[6]) : nullptr;
+  g.dBph = grp ? reinterpret_cast<float*>(p + off[7]) : nullptr;
+}
+
+int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
+  BackwardArgs g = g0;
+  const PrefillArgs& a = g.f;
+  if (!backward_supported(a.P, a.N, a.R, a.Q) || !prefill_offsets_fit(a.H, a.P, a.N, a.R)) return -1;
+  // the forward chunk entry states and h_T, into the workspace
+  PrefillArgs fw = a;
+  fw.states_only = 1;
+  fw.hT = g.hTw;
+  fw.y = nullptr;
+  if (launch_prefill(fw, in_bf16, 0, s, e) != 0) return -1;
+  if (*e != hipSuccess) return 0;
+  if (in_bf16) {
+    return dy_bf16 ? dispatch_bwd<bf16_t, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<bf16_t, float>(g, in_bf16, s, e);
+  }
+  return dy_bf16 ? dispatch_bwd<float, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<float, float>(g, in_bf16, s, e);
+}
+
+}  // namespace m3

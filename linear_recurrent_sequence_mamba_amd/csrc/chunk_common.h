@@ -1,0 +1,297 @@
+// chunk_common.h -- the pieces of the chunked scan shared by the prefill
+// kernels and their gradients (gfx950): chunk geometry, the per-chunk decay
+// and phase tables, token indexing and 16-byte row loaders.  Not part of the
+// public ABI.
+#pragma once
+
+#include "m3_device.h"
+#include "m3_launch.h"
+
+namespace m3 {
+
+constexpr int kQ = 64;         // chunk length
+constexpr int kRB = 64;        // virtual rows per output block / u-block
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+// (cos, sin) of an angle already reduced to [-pi, pi], from the hardware
+// sine/cosine (argument in turns).  Measured on gfx950 over 4M angles in
+// [-pi, pi]: max abs error 2.7e-7 (sincosf: 7e-8), far inside every
+// tolerance here, at two instructions instead of ~30.
+__device__ __forceinline__ f2 cos_sin_reduced(float ang) {
+  const float turns = ang * 0.15915494309189535f;
+  return f2{__builtin_amdgcn_cosf(turns), __builtin_amdgcn_sinf(turns)};
+}
+
+// per-chunk tables in LDS.  ROT: keep (cos, sin) of each angle (computed
+// once); otherwise keep the reduced angle and take its sine and cosine where
+// a row is staged (half the LDS; each angle is then used once).
+//
+// The angle table is token-major [t][k] for kernels whose lanes run along
+// the pairs of one token, or pair-major [k][t] (rows padded by one entry, so
+// both a column and a row of the table fall on distinct banks) for kernels
+// whose lanes run along the tokens.
+template <int N, bool ROT, bool KMAJ = false>
+struct Tables {
+  static constexpr int NP = N / 2;
+  static constexpr int TS = KMAJ ? kQ + 1 : NP;   // row stride
+  double cs[kQ];      // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
+  float dt[kQ];
+  float gam[kQ];      // lam dt
+  float bpr[kQ];      // (1 - lam) dt
+  float aux[kQ];      // e^{cs_t} (outputs) or the chunk-state weights W_t
+  double phi_end[NP];
+  alignas(16) typename std::conditional<ROT, f2, float>::type tab[(KMAJ ? NP : kQ) * TS];
+  static __device__ __forceinline__ int at(int t, int k) { return KMAJ ? k * TS + t : t * TS + k; }
+  // Phi_t (mode 0) or Phi_end - Phi_t (mode 1), reduced to [-pi, pi]
+  __device__ __forceinline__ void set(int t, int k, float ang) {
+    if constexpr (ROT) {
+      tab[at(t, k)] = cos_sin_reduced(ang);
+    } else {
+      tab[at(t, k)] = ang;
+    }
+  }
+  __device__ __forceinline__ f2 cs_of(int t, int k) const {
+    if constexpr (ROT) {
+      return tab[at(t, k)];
+    } else {
+      return cos_sin_reduced(tab[at(t, k)]);
+    }
+  }
+  // (cos, sin) of pairs k0 .. k0 + M - 1 of token t (identity when !ok); a
+  // token-major angle table serves four pairs with one 16-byte read
+  template <int M>
+  __device__ __forceinline__ void cs_run(int t, int k0, bool ok, f2* out) const {
+    if constexpr (M == 4 && !ROT && !KMAJ) {
+      const f4 ang = ok ? *reinterpret_cast<const f4*>(&tab[t * TS + k0]) : f4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) out[m] = cos_sin_reduced(ang[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) out[m] = ok ? cs_of(t, k0 + m) : f2{1.0f, 0.0f};
+    }
+  }
+};
+
+__device__ __forceinline__ float reduce_angle(double phi) {
+  constexpr double inv = 1.0 / kTwoPi;
+  return (float)(phi - kTwoPi * rint(phi * inv));
+}
+
+__device__ __forceinline__ int64_t token_index(const PrefillArgs& a, int b, int t, int h) {
+  return ((int64_t)b * a.T + t) * a.H + h;
+}
+// B, C and theta are shared by groups of H / G heads: [Bsz, T, G, ...]
+__device__ __forceinline__ int head_group(const PrefillArgs& a, int h) { return h / (a.H / a.G); }
+__device__ __forceinline__ int64_t group_index(const PrefillArgs& a, int b, int t, int h) {
+  return ((int64_t)b * a.T + t) * a.G + head_group(a, h);
+}
+
+// One chunk of the scan: tokens [t0, t0 + Lc) of token row bt, its slot in
+// the workspace, and whether its sequence goes on after it.  [Bsz, T]
+// inputs: chunk c of batch row b.  Packed sequences: chunk slot c of the
+// slot table (row 0 of a [1, T] array), which may be unused.
+struct ChunkRef {
+  int bt, t0, Lc;
+  bool next;
+  int64_t id;
+};
+__device__ __forceinline__ bool chunk_ref(const PrefillArgs& a, int c, int h, int b, ChunkRef& r) {
+  if (c >= a.nchunk) return false;   // grid padding
+  if (a.cmap) {
+    const int4 e = a.cmap[c];
+    if (e.x < 0) return false;
+    r.bt = 0;
+    r.t0 = e.y;
+    r.Lc = min(kQ, e.z - e.y);
+    r.next = e.y + kQ < e.z;
+    r.id = (int64_t)h * a.nchunk + c;
+  } else {
+    r.bt = b;
+    r.t0 = c * kQ;
+    r.Lc = min(kQ, a.T - r.t0);
+    r.next = c + 1 < a.nchunk;
+    r.id = ((int64_t)b * a.H + h) * a.nchunk + c;
+  }
+  return true;
+}
+
+// Raw 16-byte vectors of eight input elements, held in registers between
+// the load that is issued early and the store into LDS.
+template <typename TI>
+struct Vec8;
+template <>
+struct Vec8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = uint4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+};
+template <>
+struct Vec8<float> {
+  f4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f4*>(p);
+    b = *reinterpret_cast<const f4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// One 64-virtual-row block of a per-token array with E elements per token
+// (B or C: E = N R; x: E = P R) as 16-byte vectors spread over the block's
+// NT threads.  TF: consecutive threads take consecutive tokens (for the
+// transposed LDS layouts); otherwise consecutive threads walk one token.
+template <typename TI, int E, int R, int NT, bool TF, int ROWS = kRB>
+struct RowBlock {
+  static constexpr int VPT = E / 8;
+  static constexpr int NTOK = ROWS / R;
+  static constexpr int NV = NTOK * VPT;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  Vec8<TI> raw[IT];
+  static __device__ __forceinline__ void where(int vi, int& tl, int& e0) {
+    if constexpr (TF) {
+      tl = vi % NTOK;
+      e0 = (vi / NTOK) * 8;
+    } else {
+      tl = vi / VPT;
+      e0 = (vi % VPT) * 8;
+    }
+  }
+  // rows of x (GRP false: one per head) or of B, C (GRP true: one per group)
+  template <bool GRP>
+  __device__ __forceinline__ void load(const TI* __restrict__ src, const PrefillArgs& a, int b,
+                                       int h, int c0, int Lc, int v0) {
+    const int t0 = v0 / R;
+    // the chunk's first token is a block-uniform base; per-lane offsets stay
+    // in 32 bits (the launcher checks that a chunk spans < 2^31 elements)
+    const TI* __restrict__ base = src + (GRP ? group_index(a, b, c0, h) : token_index(a, b, c0, h)) * E;
+    const int tstride = (GRP ? a.G : a.H) * E;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      int tl, e0;
+      where(vi, tl, e0);
+      if (vi < NV && t0 + tl < Lc)
+        raw[i].load(base + ((t0 + tl) * tstride + e0));
+      else
+        raw[i].zero();
+    }
+  }
+};
+
+// Q x N/2 phase inputs of the chunk plus the first wave's token scalars
+template <typename TI, int N, int NT>
+struct ThetaBlock {
+  static constexpr int NP = N / 2;
+  static constexpr int VPT = NP / 8;
+  static constexpr int NV = kQ * VPT;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  Vec8<TI> raw[IT];
+  float d, l, A;
+  __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + group_index(a, b, c0, h) * NP;
+    const int tstride = a.G * NP;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      const int t = vi / VPT, kv = vi % VPT;
+      if (vi < NV && t < Lc)
+        raw[i].load(th + (t * tstride + 8 * kv));
+      else
+        raw[i].zero();
+    }
+    const int tid = threadIdx.x;
+    d = l = A = 0.0f;
+    if (tid < Lc) {
+      const int64_t bth = token_index(a, b, c0, h) + tid * a.H;
+      d = ld1(static_cast<const TI*>(a.dt), bth);
+      l = ld1(static_cast<const TI*>(a.lam), bth);
+      A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
+    }
+  }
+};
+
+// The chunk's tables from its loaded inputs: token scalars, the chunk-local
+// log-decay prefix (double, one wave shuffle scan) and phase prefix of
+// every pair (double; each thread owns one pair and a segment of tokens),
+// then the angles reduced to [-pi, pi]: Phi_t (mode 0) or Phi_end - Phi_t
+// (mode 1), kept as (cos, sin) or as the angle (see Tables).  scr is LDS
+// scratch that is free until the tables are built.
+template <int N, int NT>
+struct TableScratch {
+  float th_raw[kQ * (N / 2)];
+  double seg[NT];
+};
+
+template <typename TI, int N, int NT, bool ROT, bool KMAJ>
+__device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& tb_in, int Lc,
+                             Tables<N, ROT, KMAJ>& tb, TableScratch<N, NT>& scr, int mode) {
+  float* th_raw = scr.th_raw;
+  constexpr int NP = N / 2;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    double lv = (double)tb_in.d * (double)tb_in.A;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(lv, off, 64);
+      if (tid >= off) lv += o;
+    }
+    tb.cs[tid] = lv;
+    tb.dt[tid] = tb_in.d;
+    tb.gam[tid] = tb_in.l * tb_in.d;
+    tb.bpr[tid] = (1.0f - tb_in.l) * tb_in.d;
+  }
+#pragma unroll
+  for (int i = 0; i < ThetaBlock<TI, N, NT>::IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi < ThetaBlock<TI, N, NT>::NV) {
+      float v[8];
+      tb_in.raw[i].get(v);
+      const int t = vi / ThetaBlock<TI, N, NT>::VPT, kv = vi % ThetaBlock<TI, N, NT>::VPT;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[j];
+    }
+  }
+  __syncthreads();
+
+  constexpr int NSEG = NT / NP;
+  constexpr int SEG = kQ / NSEG;
+  static_assert(NSEG >= 1 && kQ % NSEG == 0, "phase segments");
+  const int k = tid % NP, sg = tid / NP;
+  const bool angle = (a.flags & kThetaIsAngle) != 0;
+  double loc[SEG];
+  double run = 0.0;
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int t = sg * SEG + i;
+    const double tv = (double)th_raw[t * NP + k];
+    run += angle ? tv : tv * (double)tb.dt[t];
+    loc[i] = run;
+  }
+  scr.seg[sg * NP + k] = run;
+  __syncthreads();
+  double base = 0.0;
+  for (int s = 0; s < sg; ++s) base += scr.seg[s * NP + k];
+  if (sg == NSEG - 1) tb.phi_end[k] = base + run;
+  __syncthreads();
+  const double pe = tb.phi_end[k];
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int t = sg * SEG + i;
+    if (t < Lc) {
+      const double ph = base + loc[i];
+      tb.set(t, k, reduce_angle(mode == 0 ? ph : pe - ph));
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace m3

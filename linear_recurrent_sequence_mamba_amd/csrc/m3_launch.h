@@ -82,6 +82,7 @@ struct PrefillArgs {
   int has_prev;
   BCPrep bc;
   float* rsB;      // with bc.on: [units, Q, R] inverse RMS of the chunk's B rows
+  int states_only; // stop after the chunk entry states (and h_T): no outputs
 };
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16);
@@ -94,6 +95,24 @@ void prefill_carve(PrefillArgs& a, void* ws);
 int64_t varlen_slots(int Bsz, int T, int Q);
 size_t prefill_varlen_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep);
 void prefill_varlen_carve(PrefillArgs& a, void* ws);
+// gradients of the dense prefill (single input): the chunk entry states are
+// recomputed into the workspace first
+struct BackwardArgs {
+  PrefillArgs f;      // forward inputs; workspace carved for the chunk states
+  const void* dy;     // [Bsz, T, H, P, R], out dtype
+  const float* dhT;   // [Bsz, H, P, N] or null
+  float* dS;          // workspace [units, P, N]: chunk adjoints, then dL/dShat_c
+  float* hTw;         // workspace [Bsz, H, P, N]: the forward's final state
+  float *dx, *ddt, *dA, *dlam, *dtheta, *dB, *dC, *dh0, *dx_prev, *dB_prev;
+  // workspace: per-chunk dA partials; with head groups, per-head gradients
+  // of B, C, theta and B_prev before the fixed-order sum over each group
+  float *dApart, *dBh, *dCh, *dthh, *dBph;
+};
+bool backward_supported(int P, int N, int R, int Q);
+size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int G, int Q);
+void backward_carve(BackwardArgs& a, void* ws);
+int launch_backward(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e);
+
 // builds seqs and cmap from the sequence offsets cu [Bsz + 1] (device)
 hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s);
 // returns 0 when launched (err = first launch error), -1 when no kernel fits

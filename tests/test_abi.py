@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("m3_scan_prefill", "m3_scan_prefill_varlen", "m3_decode_step",
+    for n in ("m3_scan_prefill", "m3_scan_prefill_varlen", "m3_scan_prefill_backward",
+              "m3_prefill_backward_workspace_size", "m3_decode_step",
               "m3_decode_tokens", "m3_prefill_workspace_size",
               "m3_prefill_varlen_workspace_size", "m3_status_str", "m3_last_hip_error"):
         assert n in names, names
@@ -77,6 +78,14 @@ def _varlen(d, ws_bytes=1 << 40, **over):
     return m3.library().m3_scan_prefill_varlen(ctypes.byref(d), *args.values(), ws_bytes, None)
 
 
+def _backward(d, ws_bytes=1 << 40, **over):
+    args = dict(x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None, Bp=None,
+                dy=P16, dhT=None, gx=P16, gdt=P16, gA=P16, glam=P16, gth=P16, gB=P16, gC=P16,
+                gh0=None, gxp=None, gBp=None, ws=P16)
+    args.update(over)
+    return m3.library().m3_scan_prefill_backward(ctypes.byref(d), *args.values(), ws_bytes, None)
+
+
 def test_workspace_size():
     d = _dims(batch=4, seqlen=2048, nheads=32)
     n = m3.m3_prefill_workspace_size(d)
@@ -86,7 +95,7 @@ def test_workspace_size():
     assert m3.library().m3_prefill_workspace_size(None) == 0
 
 
-@pytest.mark.parametrize("call", [_decode, _tokens, _prefill, _varlen])
+@pytest.mark.parametrize("call", [_decode, _tokens, _prefill, _varlen, _backward])
 def test_error_paths(call):
     assert m3.library().m3_decode_step(None, *([None] * 12)) == 1
     assert call(_dims(), x=None) == 1                           # NULL input
@@ -129,6 +138,21 @@ def test_varlen_specific_errors():
     assert _varlen(_dims(), ws=None) == 6
     need = m3.m3_prefill_varlen_workspace_size(_dims())
     assert _varlen(_dims(), ws_bytes=need - 1) == 6
+
+
+def test_backward_specific_errors():
+    assert _backward(_dims(), gx=None) == 1                     # a gradient output is required
+    assert _backward(_dims(), dy=None) == 1
+    assert _backward(_dims(rank=4)) == 4                        # single input only
+    assert _backward(_dims(seqlen=0)) == 2
+    assert _backward(_dims(), ws=None) == 6
+    need = m3.m3_prefill_backward_workspace_size(_dims())
+    assert need > m3.m3_prefill_workspace_size(_dims())
+    assert _backward(_dims(), ws_bytes=need - 1) == 6
+    d = _dims()
+    ok = m3.m3_bc_prep(None, None, None, None, 1e-6, 1)
+    d.bc = ctypes.pointer(ok)
+    assert _backward(d) == 4                                    # no B/C preparation
 
 
 def test_varlen_workspace_size():
