@@ -20,7 +20,8 @@ per call (m3_decode_tokens, the state crossing HBM once per call) at both
 decode shapes, the two prefill shapes' tokens packed as sequences of
 drawn lengths (m3_scan_prefill_varlen), and the decode steps and prefills
 again with the in-kernel B/C preparation (RMS normalisation, weight and
-per-head bias of B and C; "_bcprep").
+per-head bias of B and C; "_bcprep"), and the gradients of the SISO
+prefill (m3_scan_prefill_backward; "siso_prefill_backward").
 
 Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
 """
@@ -339,6 +340,59 @@ def bench_prefill_varlen(name, steps, warmup):
                 lengths=dict(min=min(lengths), max=max(lengths), mean=round(T / S, 1)))
 
 
+def backward_bytes(w, in_bytes=2, dy_bytes=4):
+    """Inputs and dy read once, every gradient written once (fp32)."""
+    B, T, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    tok = B * T * H
+    inputs = in_bytes * tok * (P + 2 * N + 2 + N // 2) + dy_bytes * tok * P
+    grads = 4 * tok * (P + 2 * N + 2 + N // 2) + 4 * H
+    return inputs + grads
+
+
+def bench_backward(name, steps, warmup):
+    """m3_scan_prefill_backward at a single-input prefill shape (fp32 dy)."""
+    import torch
+    from linear_recurrent_sequence_mamba_amd import binding as m3
+    from linear_recurrent_sequence_mamba_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in I.prefill_inputs(w).items()}
+    gen = torch.Generator(device="cpu").manual_seed(w.cfg_id)
+    dy = torch.randn(tuple(d["x"].shape), generator=gen).to(dev)
+    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, 1, w.chunk, m3.M3_BF16,
+                        m3.M3_F32)
+    n = m3.m3_prefill_backward_workspace_size(dims)
+    ws = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    grads = {k: torch.empty(d[k].shape, dtype=f32, device=dev)
+             for k in ("x", "dt", "A", "lam", "theta", "B", "C")}
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        m3.m3_scan_prefill_backward(dims, d["x"], d["dt"], d["A"], d["lam"], d["theta"], d["B"],
+                                    d["C"], None, None, None, dy, None, grads, ws, stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    call_ms = sum(ms) / len(ms)
+    nbytes = backward_bytes(w)
+    return dict(ms_per_call=round(call_ms, 4), p50_ms=round(ms[len(ms) // 2], 4),
+                tokens_per_s=round(w.batch * w.seqlen / (call_ms * 1e-3), 1),
+                algorithmic_bytes=nbytes,
+                hbm_frac=round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                note="forward chunk states recomputed inside the call; fp32 dy and gradients")
+
+
 def copy_reference(state_bytes, reps=50):
     """A plain device copy of a state-sized buffer (torch's copy kernel): read
     + write of the same byte count the decode step streams.  Context for the
@@ -474,6 +528,9 @@ def main():
     for name in ("siso_prefill", "mimo_prefill"):
         if want(name + "_bcprep"):
             prep[name] = bench_prefill(name, a.prefill_steps, 2, prep=True)
+    bwd = {}
+    if want("siso_prefill_backward"):
+        bwd["siso_prefill_backward"] = bench_backward("siso_prefill", a.prefill_steps, 2)
     tok = {}
     for base in ("siso_decode", "mimo_decode"):
         if want(base + "_k4"):
@@ -534,6 +591,11 @@ def main():
     for tag, r in res.items():
         workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
     workloads.update(tok)   # several tokens per call (m3_decode_tokens), same shapes
+    for k, e in bwd.items():
+        base = k.replace("_backward", "")
+        if base in workloads:
+            e["call_time_vs_forward"] = round(e["ms_per_call"] / workloads[base]["ms_per_call"], 3)
+        workloads[k] = e
     for base, r in prep.items():
         if "decode" in base:
             e = dict(us_per_step=round(r["step_ms"] * 1e3, 2),
