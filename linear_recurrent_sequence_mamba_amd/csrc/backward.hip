@@ -35,8 +35,20 @@ namespace m3 {
 
 namespace {
 
-constexpr int kNT1 = 256;   // threads of the chunk-adjoint kernel
-constexpr int kNT3 = 512;   // threads of the per-chunk gradient kernel
+// threads of the chunk-adjoint kernel (one to eight state elements each)
+template <int P, int N>
+constexpr int nt_adjoint() { return P * N < 1024 ? P * N : 1024; }
+
+// the per-chunk gradient kernel: TPR threads per token row (each holding
+// P / TPR columns of x and N / TPR of B and C, at least one pair), 64 rows
+template <int P, int N>
+struct BwdGeo {
+  static constexpr int TPR = (N / 2 < 16 ? N / 2 : 16) < P ? (N / 2 < 16 ? N / 2 : 16) : P;
+  static constexpr int NT = 64 * TPR;
+  static constexpr int WP = P / TPR, WN = N / TPR;
+  static constexpr int GU = 4096 / NT / 2;   // Gram entries per thread: 2 rows x GU columns
+  static_assert(WP >= 1 && WN >= 2 && WN % 2 == 0 && GU >= 1 && 64 % GU == 0, "row split");
+};
 
 template <typename T>
 __device__ __forceinline__ float ldy(const void* p, int64_t i) {
@@ -50,8 +62,9 @@ __device__ __forceinline__ f2 rot_pos(f2 v, f2 cs) { return f2{cs.x * v.x - cs.y
 // --------------------------------------------------------------------------
 // sum_t e^{cs_t} dy_t Ct_t^T of one chunk (P x N) into dS
 template <typename TI, typename TY, int P, int N>
-__global__ __launch_bounds__(kNT1) void k_bwd_chunk_adjoint(BackwardArgs g) {
+__global__ __launch_bounds__((nt_adjoint<P, N>())) void k_bwd_chunk_adjoint(BackwardArgs g) {
   const PrefillArgs& a = g.f;
+  constexpr int kNT1 = nt_adjoint<P, N>();
   constexpr int EPT = P * N / kNT1;   // outputs per thread, along one row
   static_assert(EPT >= 1 && N % EPT == 0, "outputs per thread");
   __shared__ Tables<N, false> tb;
@@ -128,27 +141,32 @@ __global__ __launch_bounds__(64) void k_bwd_state_pass(BackwardArgs g) {
 // --------------------------------------------------------------------------
 template <int P, int N>
 struct BwdSmem {
+  static constexpr int kNT3 = BwdGeo<P, N>::NT;
   Tables<N, false> tb;
   float lam[kQ], Av[kQ], ecs[kQ];
   float dcs[kQ], dgam[kQ], dbpr[kQ], dmend[kQ];
   float dphi_end[N / 2];
   float red[kNT3 / 64];
   float part[kNT3];               // per-thread partial sums, summed in a fixed order
+  // rows padded by 4 floats: lanes that read the same columns of
+  // different rows (Gram tiles, the G_end products) fall in different banks
+  static constexpr int NS = N + 4, PS = P + 4;
   union alignas(16) {
     TableScratch<N, kNT3> scr;
-    float Bt[kQ][N];              // rotated B rows
+    float Bt[kQ][NS];             // rotated B rows
   } ub;
-  alignas(16) float Ct[kQ][N];    // rotated C rows
-  alignas(16) float Xs[kQ][P];
-  alignas(16) float Ys[kQ][P];    // dy
+  alignas(16) float Ct[kQ][NS];   // rotated C rows
+  alignas(16) float Xs[kQ][PS];
+  alignas(16) float Ys[kQ][PS];   // dy
   union alignas(16) {
-    float W[kQ][kQ];              // masked Gram products
-    float Z[P][N];                // Shat, then the rotated G_end
+    float W[kQ][kQ + 1];          // masked Gram products
+    float Z[P][NS];               // Shat, then the rotated G_end
     float dphi[kQ][N / 2];        // phase gradients, then their suffix sums
   } uz;
 };
 
 // block-wide sum (all threads receive it); red holds one value per wave
+template <int kNT3>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = group_sum<64>(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -162,11 +180,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 template <typename TI, typename TY, int P, int N>
-__global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
+__global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk(BackwardArgs g) {
   const PrefillArgs& a = g.f;
+  using GEO = BwdGeo<P, N>;
   constexpr int NP = N / 2;
-  constexpr int WP = P / 8, WN = N / 8;   // a row's columns per thread (8 threads per row)
-  static_assert(WP >= 1 && WN >= 2 && WN % 2 == 0, "row split");
+  constexpr int kNT3 = GEO::NT, TPR = GEO::TPR, GU = GEO::GU;
+  constexpr int WP = GEO::WP, WN = GEO::WN;   // a row's columns per thread
   __shared__ BwdSmem<P, N> sm;
   const int h = blockIdx.y;
   ChunkRef ck;
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
   const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
   const int c = blockIdx.x;
   const bool last = c + 1 >= a.nchunk;
-  const int row = tid >> 3, cg = tid & 7;
+  const int row = tid / TPR, cg = tid % TPR;
   const int p0 = cg * WP, n0 = cg * WN;
   const int G = a.G;
   const bool shared_grp = G != a.H;   // several heads add into one B, C, theta gradient
@@ -223,49 +242,50 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
     return sm.tb.gam[u] + (u < t ? sm.tb.bpr[u + 1] : 0.0f);
   };
 
-  // ---- Gram products of a 2 x 4 block of (t, u), the decay mask and its gradient
-  float w2v[2][4];
+  // ---- Gram products of a 2 x GU block of (t, u), the decay mask and its gradient
+  constexpr int GC = 64 / GU;   // threads per pair of rows
+  float w2v[2][GU];
   {
-    const int tb0 = 2 * (tid >> 4), ub0 = 4 * (tid & 15);
-    float k1[2][4], k2[2][4];
+    const int tb0 = 2 * (tid / GC), ub0 = GU * (tid % GC);
+    float k1[2][GU], k2[2][GU];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) k1[i][j] = k2[i][j] = 0.0f;
+      for (int j = 0; j < GU; ++j) k1[i][j] = k2[i][j] = 0.0f;
 #pragma unroll 2
     for (int n = 0; n < N; n += 4) {
-      f4 cr[2], br[4];
+      f4 cr[2], br[GU];
 #pragma unroll
       for (int i = 0; i < 2; ++i) cr[i] = *reinterpret_cast<const f4*>(&sm.Ct[tb0 + i][n]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) br[j] = *reinterpret_cast<const f4*>(&sm.ub.Bt[ub0 + j][n]);
+      for (int j = 0; j < GU; ++j) br[j] = *reinterpret_cast<const f4*>(&sm.ub.Bt[ub0 + j][n]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < GU; ++j)
           k1[i][j] += cr[i].x * br[j].x + cr[i].y * br[j].y + cr[i].z * br[j].z + cr[i].w * br[j].w;
     }
 #pragma unroll 2
     for (int p = 0; p < P; p += 2) {
-      f2 yr[2], xr[4];
+      f2 yr[2], xr[GU];
 #pragma unroll
       for (int i = 0; i < 2; ++i) yr[i] = *reinterpret_cast<const f2*>(&sm.Ys[tb0 + i][p]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const f2*>(&sm.Xs[ub0 + j][p]);
+      for (int j = 0; j < GU; ++j) xr[j] = *reinterpret_cast<const f2*>(&sm.Xs[ub0 + j][p]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) k2[i][j] += yr[i].x * xr[j].x + yr[i].y * xr[j].y;
+        for (int j = 0; j < GU; ++j) k2[i][j] += yr[i].x * xr[j].x + yr[i].y * xr[j].y;
     }
     // the mask gradient dM = (Ct . Bt)(dy . x) goes through W twice so that
     // its row and column sums run in a fixed order: first dM M (log-decay),
     // then dM e^{cs_t - cs_u} (the trapezoid weights); then W takes W1
-    float em[2][4], mm[2][4];
+    float em[2][GU], mm[2][GU];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = tb0 + i;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < GU; ++j) {
         const int u = ub0 + j;
         const bool in = u <= t && t < Lc;
         em[i][j] = in ? expf((float)(sm.tb.cs[t] - sm.tb.cs[u])) : 0.0f;
@@ -284,7 +304,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.uz.W[tb0 + i][ub0 + j] = k1[i][j] * k2[i][j] * em[i][j];
+      for (int j = 0; j < GU; ++j) sm.uz.W[tb0 + i][ub0 + j] = k1[i][j] * k2[i][j] * em[i][j];
     __syncthreads();
     if (tid < kQ) {   // dgam[u] = sum_{t >= u}, dbpr[u + 1] = sum_{t > u}
       const int u = tid;
@@ -297,7 +317,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < GU; ++j) {
         sm.uz.W[tb0 + i][ub0 + j] = mm[i][j] * k1[i][j];
         w2v[i][j] = mm[i][j] * k2[i][j];
       }
@@ -315,11 +335,11 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
   }
   __syncthreads();
   {
-    const int tb0 = 2 * (tid >> 4), ub0 = 4 * (tid & 15);
+    const int tb0 = 2 * (tid / GC), ub0 = GU * (tid % GC);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.uz.W[tb0 + i][ub0 + j] = w2v[i][j];
+      for (int j = 0; j < GU; ++j) sm.uz.W[tb0 + i][ub0 + j] = w2v[i][j];
   }
   __syncthreads();
 
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
   // ---- the entry state: dCt += e^{cs_t} dY Shat, and d(e^{cs_t})
   const float* __restrict__ Sh = a.S + ck.id * (P * N);
   for (int i = tid; i < P * N / 4; i += kNT3)
-    reinterpret_cast<f4*>(&sm.uz.Z[0][0])[i] = reinterpret_cast<const f4*>(Sh)[i];
+    *reinterpret_cast<f4*>(&sm.uz.Z[i / (N / 4)][4 * (i % (N / 4))]) = reinterpret_cast<const f4*>(Sh)[i];
   __syncthreads();
   {
     float q[WN];
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
       dcv[j] += sm.ecs[row] * q[j];
       de += sm.Ct[row][n0 + j] * q[j];
     }
-    de = group_sum<8>(de);
+    de = group_sum<TPR>(de);
     if (cg == 0 && row < Lc) sm.dcs[row] += sm.ecs[row] * de;
   }
   __syncthreads();
@@ -414,8 +434,8 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
     }
   }
   sm.part[tid] = ph_part;
-  const float e_end = block_sum(e_part, sm.red);
-  const float h_end = block_sum(h_part, sm.red);   // also orders the Z and part writes
+  const float e_end = block_sum<kNT3>(e_part, sm.red);
+  const float h_end = block_sum<kNT3>(h_part, sm.red);   // also orders the Z and part writes
   if (tid < NP) {
     float v = 0.0f;
     for (int m = 0; m < kNT3 / NP; ++m) v += sm.part[tid + NP * m];
@@ -449,7 +469,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
       dxv[j] += cu * v[j];
       dme += sm.Xs[row][p0 + j] * v[j];
     }
-    dme = group_sum<8>(dme);
+    dme = group_sum<TPR>(dme);
     if (cg == 0) sm.dmend[row] = dme;
     float w[WN];
 #pragma unroll
@@ -545,7 +565,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
 #pragma unroll
     for (int j = 0; j < WP; ++j) g.dx[tok * P + p0 + j] = dxv[j];
   }
-  dt_theta = group_sum<8>(dt_theta);
+  dt_theta = group_sum<TPR>(dt_theta);
   float da_part = 0.0f;
   if (row < Lc && cg == 0) {
     const int t = row;
@@ -557,7 +577,7 @@ __global__ __launch_bounds__(kNT3) void k_bwd_chunk(BackwardArgs g) {
     else da_part = dtt * da;
   }
   if (!(a.flags & kAPerToken)) {   // per chunk; a final pass sums them per head
-    const float s = block_sum(da_part, sm.red);
+    const float s = block_sum<kNT3>(da_part, sm.red);
     if (tid == 0) g.dApart[ck.id] = s;
   }
   // the token before the sequence: dx_prev = beta'_0 dShat_0 B_prev,
@@ -608,14 +628,14 @@ template <typename TI, typename TY, int P, int N>
 hipError_t run_backward(const BackwardArgs& g, int in_bf16, hipStream_t s) {
   const PrefillArgs& a = g.f;
   const dim3 grid(a.nchunk, a.H, a.Bsz);
-  hipLaunchKernelGGL((k_bwd_chunk_adjoint<TI, TY, P, N>), grid, dim3(kNT1), 0, s, g);
+  hipLaunchKernelGGL((k_bwd_chunk_adjoint<TI, TY, P, N>), grid, dim3(nt_adjoint<P, N>()), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
   hipLaunchKernelGGL((k_bwd_state_pass<N>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(kNT3), 0, s, g);
+  hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!(a.flags & kAPerToken)) {
     hipLaunchKernelGGL(k_bwd_reduce_dA, dim3((a.H + 63) / 64), dim3(64), 0, s, g);
