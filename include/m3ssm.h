@@ -150,10 +150,12 @@ size_t m3_prefill_backward_workspace_size(const m3_dims* dims);
  *   [Bsz,G,N,R] (written when x_prev/B_prev are given and the pointers are
  *   not NULL).
  * dy has out_dtype and the layout of y.  dA and, with head groups, dB, dC,
- * dtheta and dB_prev are sums over heads (and tokens), accumulated in place
- * after the library clears them.  The forward chunk states are recomputed
- * into ws.  Supported: R = 1 with the prefill's (P, N) shapes and Q = 64;
- * dims->bc must be NULL; otherwise M3_ERR_UNSUPPORTED. */
+ * dtheta and dB_prev are sums over heads (and tokens), taken in a fixed
+ * order in ws (no atomics), so equal calls return equal bits.  The forward
+ * chunk states are recomputed into ws.  Supported: Q = 64 and (P, N, R) in
+ * (16, 16, 1), (64, 128, 1 | 2 | 4), (32, 64, 1 | 4), (64, 64, 1 | 4), the
+ * shapes of m3_scan_prefill; dims->bc must be NULL; otherwise
+ * M3_ERR_UNSUPPORTED. */
 m3_status m3_scan_prefill_backward(const m3_dims* dims, const void* x, const void* dt,
                                    const float* A, const void* lam, const void* theta,
                                    const void* B, const void* C, const float* h0,

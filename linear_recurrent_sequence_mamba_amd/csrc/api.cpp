@@ -141,7 +141,7 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
 size_t m3_prefill_backward_workspace_size(const m3_dims* d) {
   if (check_dims(d, true) != M3_OK) return 0;
   return m3::backward_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
-                                      groups_of(d), chunk_of(d));
+                                      d->rank, groups_of(d), chunk_of(d));
 }
 
 m3_status m3_scan_prefill_backward(const m3_dims* d, const void* x, const void* dt,
@@ -168,7 +168,7 @@ m3_status m3_scan_prefill_backward(const m3_dims* d, const void* x, const void* 
       !m3::backward_supported(d->headdim, d->dstate, d->rank, Q))
     return M3_ERR_UNSUPPORTED;
   const size_t need = m3::backward_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim,
-                                                   d->dstate, groups_of(d), Q);
+                                                   d->dstate, d->rank, groups_of(d), Q);
   if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
 
   m3::BackwardArgs g{};

@@ -109,7 +109,7 @@ struct BackwardArgs {
   float *dApart, *dBh, *dCh, *dthh, *dBph;
 };
 bool backward_supported(int P, int N, int R, int Q);
-size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int G, int Q);
+size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int G, int Q);
 void backward_carve(BackwardArgs& a, void* ws);
 int launch_backward(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e);
 

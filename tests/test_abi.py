@@ -143,7 +143,8 @@ def test_varlen_specific_errors():
 def test_backward_specific_errors():
     assert _backward(_dims(), gx=None) == 1                     # a gradient output is required
     assert _backward(_dims(), dy=None) == 1
-    assert _backward(_dims(rank=4)) == 4                        # single input only
+    assert _backward(_dims(rank=3)) == 4                        # ranks 1, 2 and 4 only
+    assert _backward(_dims(rank=2, headdim=32, dstate=64)) == 4  # R = 2 only with (64, 128)
     assert _backward(_dims(seqlen=0)) == 2
     assert _backward(_dims(), ws=None) == 6
     need = m3.m3_prefill_backward_workspace_size(_dims())

@@ -124,6 +124,47 @@ def test_backward_variants():
     _check(w, base, dy.to(torch.bfloat16), dhT)
 
 
+@pytest.mark.parametrize("P,N,R,dt", [(64, 128, 2, "bf16"), (64, 128, 4, "f32"), (32, 64, 4, "bf16"),
+                                      (64, 64, 4, "f32")])
+def test_backward_mimo_shapes(P, N, R, dt):
+    """Rank R > 1: every token is R columns of x, B and C; the gradients of
+    every rank against the oracle's (which runs the rank-R recurrence)."""
+    w = I.Workload("g", 134, 2, 150, 2, P, N, R, 64, dt)
+    d = I.prefill_inputs(w, h0="normal", with_prev=True)
+    dy, dhT = _cotangents(w, d)
+    say(f"backward P={P} N={N} R={R} {dt}")
+    _check(w, d, dy, dhT)
+
+
+@pytest.mark.parametrize("T", [1, 64, 97])
+def test_backward_mimo_lengths(T):
+    w = I.Workload("g", 135, 1, T, 2, 64, 128, 4, 64, "bf16")
+    d = I.prefill_inputs(w, h0="normal", with_prev=True)
+    dy, dhT = _cotangents(w, d)
+    say(f"backward R=4 T={T}")
+    _check(w, d, dy, dhT)
+
+
+def test_backward_mimo_variants():
+    w = I.Workload("g", 136, 2, 140, 4, 64, 128, 4, 64, "bf16")
+    base = I.prefill_inputs(w, h0="normal", with_prev=True)
+    dy, dhT = _cotangents(w, base)
+    say("backward R=4, head groups G=2")
+    d = dict(base)
+    for k in ("B", "C", "theta"):
+        d[k] = base[k][:, :, :2].contiguous()
+    d["B_prev"] = base["B_prev"][:, :2].contiguous()
+    _check(w, d, dy, dhT)
+    say("backward R=4, no h0, no previous token, no dhT")
+    d = I.prefill_inputs(w, h0="zero", with_prev=False)
+    _check(w, d, dy, None)
+    say("backward R=4, theta is the angle, A per token, bf16 dy")
+    d = dict(base)
+    rng = np.random.default_rng(6)
+    d["A"] = torch.from_numpy(-np.exp(rng.uniform(-4, 0, size=(2, 140, 4))).astype(np.float32))
+    _check(w, d, dy.to(torch.bfloat16), dhT, flags=m3.M3_THETA_IS_ANGLE | m3.M3_A_PER_TOKEN)
+
+
 def test_backward_is_deterministic_and_matches_split():
     """Two calls give identical gradients; the h0 gradient of the second half
     of a split scan is the dhT that the first half's backward needs."""
@@ -152,17 +193,17 @@ def test_backward_is_deterministic_and_matches_split():
     assert e <= 1e-4
 
 
-@pytest.mark.parametrize("name", ["siso_prefill"])
+@pytest.mark.parametrize("name", ["siso_prefill", "mimo_prefill"])
 def test_backward_full_workload_sampled(name):
-    """The SISO prefill workload (B=4, T=2048, H=32) in the launch
-    configuration of the benchmark; the gradients of sampled (batch, head)
-    pairs against the oracle."""
+    """The prefill workloads (SISO B=4, T=2048, H=32; MIMO B=1, T=16384,
+    H=64, R=4) in the launch configuration of the benchmark; the gradients of
+    sampled (batch, head) pairs against the oracle."""
     w = I.WORKLOADS[name]
     d = I.prefill_inputs(w)
     dy, dhT = _cotangents(w, d, dhT=False)
     say(f"backward {name}")
     got = _gpu(d, dy, None)
-    for b, h in ((0, 0), (3, 17)):
+    for b, h in ((0, 0), (w.batch - 1, 17)):
         sub = {k: (v[b:b + 1, :, h:h + 1].contiguous() if k in ("x", "dt", "lam", "theta", "B", "C")
                    else v) for k, v in d.items()}
         sub["A"] = d["A"][h:h + 1]
