@@ -20,8 +20,8 @@ per call (m3_decode_tokens, the state crossing HBM once per call) at both
 decode shapes, the two prefill shapes' tokens packed as sequences of
 drawn lengths (m3_scan_prefill_varlen), and the decode steps and prefills
 again with the in-kernel B/C preparation (RMS normalisation, weight and
-per-head bias of B and C; "_bcprep"), and the gradients of the SISO
-prefill (m3_scan_prefill_backward; "siso_prefill_backward").
+per-head bias of B and C; "_bcprep"), and the gradients of both prefills
+(m3_scan_prefill_backward; "siso_prefill_backward", "mimo_prefill_backward").
 
 Prints one JSON line.  Only one GPU is supported: --gpus N > 1 exits.
 """
@@ -342,15 +342,15 @@ def bench_prefill_varlen(name, steps, warmup):
 
 def backward_bytes(w, in_bytes=2, dy_bytes=4):
     """Inputs and dy read once, every gradient written once (fp32)."""
-    B, T, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    B, T, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
     tok = B * T * H
-    inputs = in_bytes * tok * (P + 2 * N + 2 + N // 2) + dy_bytes * tok * P
-    grads = 4 * tok * (P + 2 * N + 2 + N // 2) + 4 * H
+    inputs = in_bytes * tok * (P * R + 2 * N * R + 2 + N // 2) + dy_bytes * tok * P * R
+    grads = 4 * tok * (P * R + 2 * N * R + 2 + N // 2) + 4 * H
     return inputs + grads
 
 
 def bench_backward(name, steps, warmup):
-    """m3_scan_prefill_backward at a single-input prefill shape (fp32 dy)."""
+    """m3_scan_prefill_backward at a prefill workload's shape (fp32 dy)."""
     import torch
     from linear_recurrent_sequence_mamba_amd import binding as m3
     from linear_recurrent_sequence_mamba_amd import inputs as I
@@ -360,8 +360,8 @@ def bench_backward(name, steps, warmup):
     d = {k: (None if v is None else v.to(dev)) for k, v in I.prefill_inputs(w).items()}
     gen = torch.Generator(device="cpu").manual_seed(w.cfg_id)
     dy = torch.randn(tuple(d["x"].shape), generator=gen).to(dev)
-    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, 1, w.chunk, m3.M3_BF16,
-                        m3.M3_F32)
+    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk,
+                        m3.M3_BF16, m3.M3_F32)
     n = m3.m3_prefill_backward_workspace_size(dims)
     ws = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=dev)
     f32 = torch.float32
@@ -531,6 +531,8 @@ def main():
     bwd = {}
     if want("siso_prefill_backward"):
         bwd["siso_prefill_backward"] = bench_backward("siso_prefill", a.prefill_steps, 2)
+    if want("mimo_prefill_backward"):
+        bwd["mimo_prefill_backward"] = bench_backward("mimo_prefill", a.prefill_steps, 2)
     tok = {}
     for base in ("siso_decode", "mimo_decode"):
         if want(base + "_k4"):

@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libm3ssm.so")
-SOURCES = ["api.cpp", "backward.hip", "decode.hip", "decode_tokens.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "backward.hip", "backward_mma.hip", "decode.hip", "decode_tokens.hip",
+           "prefill.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -50,15 +50,6 @@ struct BwdGeo {
   static_assert(WP >= 1 && WN >= 2 && WN % 2 == 0 && GU >= 1 && 64 % GU == 0, "row split");
 };
 
-template <typename T>
-__device__ __forceinline__ float ldy(const void* p, int64_t i) {
-  return ld1(static_cast<const T*>(p), i);
-}
-
-// rotate one pair by -angle / +angle given (cos, sin)
-__device__ __forceinline__ f2 rot_neg(f2 v, f2 cs) { return f2{cs.x * v.x + cs.y * v.y, -cs.y * v.x + cs.x * v.y}; }
-__device__ __forceinline__ f2 rot_pos(f2 v, f2 cs) { return f2{cs.x * v.x - cs.y * v.y, cs.y * v.x + cs.x * v.y}; }
-
 // --------------------------------------------------------------------------
 // sum_{t,r} e^{cs_t} dy_{t,r} Ct_{t,r}^T of one chunk (P x N) into dS, one
 // rank column at a time
@@ -169,20 +160,6 @@ struct BwdSmem {
     float dphi[kQ][N / 2];        // phase gradients, then their suffix sums
   } uz;
 };
-
-// block-wide sum (all threads receive it); red holds one value per wave
-template <int kNT3>
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = group_sum<64>(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kNT3 / 64; ++w) s += red[w];
-  return s;
-}
 
 template <typename TI, typename TY, int P, int N>
 __global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk(BackwardArgs g) {
@@ -1139,35 +1116,14 @@ hipError_t run_backward(const BackwardArgs& g, int in_bf16, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_chunk_adjoint<TI, TY, P, N, R>), grid, dim3(nt_adjoint<P, N>()), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
-  hipLaunchKernelGGL((k_bwd_state_pass<N>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, g);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = launch_bwd_state_pass(g, s)) != hipSuccess) return e;
   if constexpr (R == 1) {
     hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
   } else {
     static_assert(P * R <= BwdGeo<P, N>::NT && N * R <= BwdGeo<P, N>::NT, "x_prev, B_prev: one thread each");
     hipLaunchKernelGGL((k_bwd_chunk_mimo<TI, TY, P, N, R>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (!(a.flags & kAPerToken)) {
-    hipLaunchKernelGGL(k_bwd_reduce_dA, dim3((a.H + 63) / 64), dim3(64), 0, s, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (a.G != a.H) {
-    auto red = [&](const float* src, float* dst, int64_t rows, int E) {
-      const int64_t n = rows * a.G * E;
-      hipLaunchKernelGGL(k_bwd_reduce_groups, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src,
-                         dst, n, a.H, a.G, E);
-      return hipGetLastError();
-    };
-    const int64_t tokens = (int64_t)a.Bsz * a.T;
-    if ((e = red(g.dBh, g.dB, tokens, N * R)) != hipSuccess) return e;
-    if ((e = red(g.dCh, g.dC, tokens, N * R)) != hipSuccess) return e;
-    if ((e = red(g.dthh, g.dtheta, tokens, N / 2)) != hipSuccess) return e;
-    if (g.dB_prev && (e = red(g.dBph, g.dB_prev, a.Bsz, N * R)) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 template <typename TI, typename TY>
@@ -1190,9 +1146,47 @@ int dispatch_bwd(const BackwardArgs& g, int in_bf16, hipStream_t s, hipError_t* 
   return -1;
 }
 
+// the sums over (batch, chunk) of dA and over the heads of each group
+hipError_t bwd_reduce(const BackwardArgs& g, hipStream_t s) {
+  const PrefillArgs& a = g.f;
+  const int N = a.N, R = a.R;
+  hipError_t e = hipSuccess;
+  if (!(a.flags & kAPerToken)) {
+    hipLaunchKernelGGL(k_bwd_reduce_dA, dim3((a.H + 63) / 64), dim3(64), 0, s, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.G != a.H) {
+    auto red = [&](const float* src, float* dst, int64_t rows, int E) {
+      const int64_t n = rows * a.G * E;
+      hipLaunchKernelGGL(k_bwd_reduce_groups, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src,
+                         dst, n, a.H, a.G, E);
+      return hipGetLastError();
+    };
+    const int64_t tokens = (int64_t)a.Bsz * a.T;
+    if ((e = red(g.dBh, g.dB, tokens, N * R)) != hipSuccess) return e;
+    if ((e = red(g.dCh, g.dC, tokens, N * R)) != hipSuccess) return e;
+    if ((e = red(g.dthh, g.dtheta, tokens, N / 2)) != hipSuccess) return e;
+    if (g.dB_prev && (e = red(g.dBph, g.dB_prev, a.Bsz, N * R)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 size_t align256b(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
+
+hipError_t launch_bwd_state_pass(const BackwardArgs& g, hipStream_t s) {
+  const PrefillArgs& a = g.f;
+  if (a.P * a.N % 256 != 0) return hipErrorInvalidValue;   // whole waves per (batch, head)
+  const dim3 grid(a.Bsz * a.H * (a.P * a.N / 256));
+  switch (a.N) {
+    case 16: hipLaunchKernelGGL((k_bwd_state_pass<16>), grid, dim3(64), 0, s, g); break;
+    case 64: hipLaunchKernelGGL((k_bwd_state_pass<64>), grid, dim3(64), 0, s, g); break;
+    case 128: hipLaunchKernelGGL((k_bwd_state_pass<128>), grid, dim3(64), 0, s, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool backward_supported(int P, int N, int R, int Q) {
   if (Q != kQ) return false;
@@ -1202,20 +1196,25 @@ bool backward_supported(int P, int N, int R, int Q) {
 
 // forward part, the chunk adjoints (P N per chunk), h_T, the per-chunk dA
 // partials and, with head groups, per-head B, C, theta and B_prev gradients
+static constexpr int kParts = 10;
 static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int R, int G, int Q, size_t* off) {
   const size_t nchunk = (size_t)(T + Q - 1) / Q;
   const size_t units = (size_t)Bsz * H * nchunk;
   const size_t tokens = (size_t)Bsz * T;
-  size_t sz[8] = {prefill_workspace_bytes(Bsz, T, H, P, N, R, Q, false), units * P * N * 4,
-                  (size_t)Bsz * H * P * N * 4, units * 4, 0, 0, 0, 0};
+  size_t sz[kParts] = {prefill_workspace_bytes(Bsz, T, H, P, N, R, Q, false), units * P * N * 4,
+                       (size_t)Bsz * H * P * N * 4, units * 4, 0, 0, 0, 0, 0, 0};
   if (G != H) {
     sz[4] = tokens * H * N * R * 4;
     sz[5] = tokens * H * N * R * 4;
     sz[6] = tokens * H * (N / 2) * 4;
     sz[7] = (size_t)Bsz * H * N * R * 4;
   }
+  if (R > 1) {   // the rank-R kernels' token sums and u-side phase gradients
+    sz[8] = units * 6 * Q * 4;
+    sz[9] = units * Q * (N / 2) * 4;
+  }
   size_t total = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kParts; ++i) {
     if (off) off[i] = total;
     total += align256b(sz[i]);
   }
@@ -1229,7 +1228,7 @@ size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int 
 void backward_carve(BackwardArgs& g, void* ws) {
   PrefillArgs& a = g.f;
   prefill_carve(a, ws);
-  size_t off[8];
+  size_t off[kParts];
   bwd_parts(a.Bsz, a.T, a.H, a.P, a.N, a.R, a.G, a.Q, off);
   char* p = static_cast<char*>(ws);
   g.dS = reinterpret_cast<float*>(p + off[1]);
@@ -1240,6 +1239,8 @@ void backward_carve(BackwardArgs& g, void* ws) {
   g.dCh = grp ? reinterpret_cast<float*>(p + off[5]) : nullptr;
   g.dthh = grp ? reinterpret_cast<float*>(p + off[6]) : nullptr;
   g.dBph = grp ? reinterpret_cast<float*>(p + off[7]) : nullptr;
+  g.tokw = a.R > 1 ? reinterpret_cast<float*>(p + off[8]) : nullptr;
+  g.dphiB = a.R > 1 ? reinterpret_cast<float*>(p + off[9]) : nullptr;
 }
 
 int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
@@ -1253,10 +1254,15 @@ int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_
   fw.y = nullptr;
   if (launch_prefill(fw, in_bf16, 0, s, e) != 0) return -1;
   if (*e != hipSuccess) return 0;
-  if (in_bf16) {
-    return dy_bf16 ? dispatch_bwd<bf16_t, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<bf16_t, float>(g, in_bf16, s, e);
-  }
-  return dy_bf16 ? dispatch_bwd<float, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<float, float>(g, in_bf16, s, e);
+  int rc;
+  if (a.R > 1) rc = launch_backward_mma(g, in_bf16, dy_bf16, s, e);
+  else if (in_bf16)
+    rc = dy_bf16 ? dispatch_bwd<bf16_t, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<bf16_t, float>(g, in_bf16, s, e);
+  else
+    rc = dy_bf16 ? dispatch_bwd<float, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<float, float>(g, in_bf16, s, e);
+  if (rc != 0 || *e != hipSuccess) return rc;
+  *e = bwd_reduce(g, s);
+  return 0;
 }
 
 }  // namespace m3

@@ -1,0 +1,984 @@
+// backward_mma.hip -- gradients of the rank-R chunked prefill scan on the
+// matrix cores (gfx950).
+//
+// The gradients are those of backward.hip (the recurrence of the Mamba-3
+// article [xxxxx.co.kr, sections 1.1-1.3], differentiated in the chunked
+// form of prefill.hip).  With rank R every token is R virtual rows (t, r)
+// of the chunk, and every contraction over them is a dense product of the
+// chunk's Q R = 64 R rows, here on MFMA tiles (mfma_pol.h: fp32 operands
+// for fp32 inputs, fp16 hi + lo splits for bf16 inputs):
+//   K1 = Ct Bt^T,  K2 = dY X^T,  W1 = M o K1,  W2 = M o K2   (M: decay mask)
+//   dx  = W1^T dY + diag(m_end) Bt Gt^T
+//   dBt = W2^T Ct + diag(m_end) X Gt
+//   dCt = W2 Bt + diag(e^{cs}) dY Shat
+//   dM[t, u] = sum over the R x R rank pairs of K1 o K2
+// Launches after the forward states (which launch_backward runs):
+//  k_bwd_adjoint_mma (batch, head, chunk): sum_t e^{cs_t} dY_t Ct_t^T;
+//  k_bwd_state_pass  (backward.hip): the reverse pass over chunks;
+//  k_bwd_u  (batch, head, chunk [x 2]): one wave per 16 u rows, walking the
+//           t rows at or after them: dx, dB, the mask's column sums, the
+//           u side of the phase gradient;
+//  k_bwd_t  (batch, head, chunk): one wave per 16 t rows, walking the u rows
+//           at or before them: dC and the C side of the phase gradient,
+//           then the per-token gradients of the chunk (dt, lam, A, theta)
+//           from the token sums of both.
+// Every sum runs in a fixed order (no atomics): equal calls give equal bits.
+#include "chunk_common.h"
+#include "mfma_pol.h"
+
+namespace m3 {
+
+namespace {
+
+constexpr int kTB = 32;   // virtual rows of a staged block (two 16-row tiles)
+
+// x or dy rows of a block as loaded, into st[v - v0][e] (split or fp32)
+template <class Pol, typename TI, int E, int R, int NT, int ROWS>
+__device__ __forceinline__ void put_rows(const RowBlock<TI, E * R, R, NT, false, ROWS>& rb,
+                                         typename Pol::template Store<ROWS, E>& st) {
+  using RBk = RowBlock<TI, E * R, R, NT, false, ROWS>;
+#pragma unroll
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    float v[8];
+    rb.raw[i].get(v);
+    if constexpr (R == 1) {
+      Pol::put8(st, tl, e0, v);
+    } else {
+      constexpr int M = 8 / R;   // element j is (column e0/R + j/R, rank j%R)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float w[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) w[m] = v[m * R + r];
+        Pol::template putn<M>(st, tl * R + r, e0 / R, w);
+      }
+    }
+  }
+}
+
+// x rows of a block into an XStore, natural k order: xs[v - v0][p]
+template <class Pol, typename TI, int P, int R, int NT, int ROWS>
+__device__ __forceinline__ void put_xrows(const RowBlock<TI, P * R, R, NT, false, ROWS>& rb,
+                                          typename Pol::template XStore<ROWS, P>& xs) {
+  using RBk = RowBlock<TI, P * R, R, NT, false, ROWS>;
+#pragma unroll
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    float v[8];
+    rb.raw[i].get(v);
+    if constexpr (R == 1) {
+      Pol::template putxn<4>(xs, tl, e0, v);
+      Pol::template putxn<4>(xs, tl, e0 + 4, v + 4);
+    } else {
+      constexpr int M = 8 / R;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float w[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) w[m] = v[m * R + r];
+        Pol::template putxn<M>(xs, tl * R + r, e0 / R, w);
+      }
+    }
+  }
+}
+
+// rows of a block transposed, st[e][v - v0]: B or C rotated by -Phi_t
+// (ROT) and scaled by sc[t] (when given), or x / dy as loaded
+template <class Pol, typename TI, int E, int R, int NT, int ROWS, bool ROT, class Tab>
+__device__ __forceinline__ void put_rows_T(const RowBlock<TI, E * R, R, NT, false, ROWS>& rb,
+                                           typename Pol::template Store<E, ROWS>& st, const Tab& tb,
+                                           const float* sc, int t0, int Lc) {
+  using RBk = RowBlock<TI, E * R, R, NT, false, ROWS>;
+  constexpr int NPAIR = 4 / R;   // complex pairs per vector
+#pragma unroll
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    const int t = t0 + tl;
+    const bool ok = t < Lc;
+    float v[8];
+    rb.raw[i].get(v);
+    if constexpr (ROT) {
+      f2 csr[NPAIR];
+      tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
+      const float w = (sc && ok) ? sc[t] : 1.0f;
+#pragma unroll
+      for (int pi = 0; pi < NPAIR; ++pi) {
+        const f2 cs = w * csr[pi];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
+          v[(2 * pi) * R + r] = cs.x * u0 + cs.y * u1;
+          v[(2 * pi + 1) * R + r] = -cs.y * u0 + cs.x * u1;
+        }
+      }
+    }
+    // the R virtual rows of token tl are consecutive columns of st
+#pragma unroll
+    for (int m = 0; m < 8 / R; ++m) Pol::template putn<R>(st, e0 / R + m, tl * R, v + m * R);
+  }
+}
+
+// the rotated value (by -Phi) of element n of a (column n, partner n ^ 1)
+// pair, from both raw elements
+__device__ __forceinline__ float rot_own(float own, float oth, bool odd, f2 cs) {
+  return odd ? -cs.y * oth + cs.x * own : cs.x * own + cs.y * oth;
+}
+
+// sum of a lane's four D rows by token (rows 4g .. 4g + 3 hold whole tokens
+// when R divides 4) into out[token]: out gets one write per token
+template <int R, class F>
+__device__ __forceinline__ void rows_by_token(const float* v, int row0, F&& put) {
+  float s = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    s += v[jj];
+    if (jj % R == R - 1) {
+      put((row0 + jj) / R, s);
+      s = 0.0f;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// sum_{t,r} e^{cs_t} dy_{t,r} Ct_{t,r}^T of one chunk (P x N) into dS: the
+// P x N output tiles over four waves, t in blocks of 32 virtual rows
+template <int P, int N>
+struct AdjGeo {
+  static constexpr int NW = 4, NT = 256;
+  static constexpr int NTN = N / 16, TILES = (P / 16) * NTN, TPW = TILES / NW;
+  static_assert(TPW >= 1 && NTN % TPW == 0, "one output row of tiles per wave");
+};
+
+template <class Pol, int P, int N>
+struct AdjSmem {
+  Tables<N, false> tb;
+  union U {
+    TableScratch<N, AdjGeo<P, N>::NT> scr;
+    struct S {
+      typename Pol::template Store<P, kTB> y;   // dy^T     [p][v]
+      typename Pol::template Store<N, kTB> c;   // e^cs Ct^T [n][v]
+    } st;
+  } u;
+};
+
+template <class Pol, typename TI, typename TY, int P, int N, int R>
+__global__ __launch_bounds__(256) void k_bwd_adjoint_mma(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  using AG = AdjGeo<P, N>;
+  constexpr int NT = AG::NT;
+  __shared__ AdjSmem<Pol, P, N> sm;
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, l16 = lane & 15;
+  const int rows = Lc * R, nkb = (rows + kTB - 1) / kTB;
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
+  const TY* __restrict__ Yg = static_cast<const TY*>(g.dy);
+  ThetaBlock<TI, N, NT> thb;
+  thb.load(a, b, h, c0, Lc);
+  RowBlock<TY, P * R, R, NT, false, kTB> yb;
+  RowBlock<TI, N * R, R, NT, false, kTB> cb;
+  yb.template load<false>(Yg, a, b, h, c0, Lc, 0);
+  cb.template load<true>(Cg, a, b, h, c0, Lc, 0);
+  chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
+  if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? __expf((float)sm.tb.cs[tid]) : 0.0f;
+
+  const int tile0 = wave * AG::TPW, pt = tile0 / AG::NTN, nt0 = tile0 % AG::NTN;
+  f4 acc[AG::TPW];
+#pragma unroll
+  for (int i = 0; i < AG::TPW; ++i) acc[i] = f4{0, 0, 0, 0};
+  for (int k = 0; k < nkb; ++k) {
+    __syncthreads();   // the tables are built; the previous block is read
+    put_rows_T<Pol, TY, P, R, NT, kTB, false>(yb, sm.u.st.y, sm.tb, nullptr, k * kTB / R, Lc);
+    put_rows_T<Pol, TI, N, R, NT, kTB, true>(cb, sm.u.st.c, sm.tb, sm.tb.aux, k * kTB / R, Lc);
+    if (k + 1 < nkb) {
+      yb.template load<false>(Yg, a, b, h, c0, Lc, (k + 1) * kTB);
+      cb.template load<true>(Cg, a, b, h, c0, Lc, (k + 1) * kTB);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kTB; kk += Pol::KS) {
+      const typename Pol::Frag af = Pol::frag(sm.u.st.y, 16 * pt, kk, lane);
+#pragma unroll
+      for (int i = 0; i < AG::TPW; ++i)
+        acc[i] = Pol::mma(af, Pol::frag(sm.u.st.c, 16 * (nt0 + i), kk, lane), acc[i]);
+    }
+  }
+  // D[p][n]: column n = 16 nt + l16, rows p = 16 pt + 4 g + jj
+  float* __restrict__ out = g.dS + ck.id * (P * N);
+#pragma unroll
+  for (int i = 0; i < AG::TPW; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) out[(16 * pt + 4 * gq + jj) * N + 16 * (nt0 + i) + l16] = acc[i][jj];
+}
+
+// --------------------------------------------------------------------------
+// The u side.  One wave per 16-row u tile; a rank-4 chunk (16 tiles) is
+// split over two blocks of 8 waves, the u rows 0..127 and 128..255.
+template <int P, int N, int R>
+struct GeoU {
+  static constexpr int ROWS = kQ * R, TILES = ROWS / 16;
+  static constexpr int NW = TILES > 8 ? 8 : TILES;
+  static constexpr int SPLIT = TILES / NW;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BROWS = ROWS / SPLIT;   // u rows per block
+  static_assert((SPLIT == 1 || SPLIT == 2) && BROWS % 64 == 0, "u-side geometry");
+};
+
+// per-chunk token sums in the workspace: [units][6][Q]
+enum TokSum { kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5 };
+
+template <class Pol, int P, int N, int R>
+struct USmem {
+  using G = GeoU<P, N, R>;
+  Tables<N, false> tb;
+  float rowpart[G::NW][kQ];   // each wave's row sums of dM o M
+  union U {
+    TableScratch<N, G::NT> scr;
+    struct O {
+      typename Pol::template Store<64, N> b;    // own rotated B rows
+      typename Pol::template XStore<64, P> x;   // own x rows
+    } own;
+    struct S {
+      typename Pol::template Store<kTB, N> c;   // Ct rows   [v][n]
+      typename Pol::template Store<kTB, P> y;   // dy rows   [v][p]
+      typename Pol::template Store<N, kTB> ct;  // Ct^T      [n][v]
+      typename Pol::template Store<P, kTB> yt;  // dy^T      [p][v]
+    } st;
+    typename Pol::template Store<P, N> gt;      // Gt        [p][n]
+    typename Pol::template Store<N, P> gtt;     // Gt^T      [n][p]
+  } u;
+};
+
+template <class Pol, typename TI, typename TY, int P, int N, int R>
+__global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  using G = GeoU<P, N, R>;
+  constexpr int NT = G::NT, NW = G::NW, KS = Pol::KS;
+  constexpr int NKS = N / KS, PKS = P / KS, PT = P / 16, NTL = N / 16, NP = N / 2;
+  __shared__ USmem<Pol, P, N, R> sm;
+  // the two blocks of a split chunk are 8 apart in launch order (same XCD)
+  int c, half;
+  if constexpr (G::SPLIT == 2) {
+    c = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    half = (blockIdx.x >> 3) & 1;
+  } else {
+    c = blockIdx.x;
+    half = 0;
+  }
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, c, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
+  const int rows = Lc * R;
+  const int v0 = half * G::BROWS;
+  if (v0 >= rows) return;   // k_bwd_t reads this half's row sums only when it exists
+  const bool last = c + 1 >= a.nchunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, l16 = lane & 15;
+  // waves w and w + 4 share a SIMD: tiles w and 7 - w even out the causal work
+  const int lt = (NW == 8) ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int utile = v0 / 16 + lt;
+  const bool live = 16 * utile < rows;
+  const int uv = 16 * utile + l16;   // this lane's u column in the Gram tiles
+  const int utok = uv / R;
+
+  const int G_ = a.G;
+  const int64_t gi = group_index(a, b, c0, h), ti0 = token_index(a, b, c0, h);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
+  const TI* __restrict__ Cg = static_cast<const TI*>(a.C);
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+  const TY* __restrict__ Yg = static_cast<const TY*>(g.dy);
+  const TI* __restrict__ Bc = Bg + gi * N * R;   // this chunk's first token
+  const TI* __restrict__ Xc = Xg + ti0 * P * R;
+
+  ThetaBlock<TI, N, NT> thb;
+  thb.load(a, b, h, c0, Lc);
+  for (int i = tid; i < NW * kQ; i += NT) (&sm.rowpart[0][0])[i] = 0.0f;
+  chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
+
+  // own rotated B rows and x rows -> fragments in registers
+  typename Pol::Frag bf[NKS];
+  typename Pol::XFrag xf[PKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) bf[s] = typename Pol::Frag{};
+#pragma unroll
+  for (int s = 0; s < PKS; ++s) xf[s] = typename Pol::XFrag{};
+#pragma unroll
+  for (int piece = 0; piece < G::BROWS / 64; ++piece) {
+    const int pv0 = v0 + 64 * piece;
+    if (pv0 >= rows) break;
+    RowBlock<TI, N * R, R, NT, false, 64> rb;
+    RowBlock<TI, P * R, R, NT, false, 64> rx;
+    rb.template load<true>(Bg, a, b, h, c0, Lc, pv0);
+    rx.template load<false>(Xg, a, b, h, c0, Lc, pv0);
+    __syncthreads();   // the table scratch (or the previous piece) is free
+    store_rows<Pol, TI, N, R, NT, 64>(rb, sm.u.own.b, sm.tb, pv0 / R, Lc, NoPrep{});
+    put_xrows<Pol, TI, P, R, NT, 64>(rx, sm.u.own.x);
+    __syncthreads();
+    if (lt / 4 == piece) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) bf[s] = Pol::frag(sm.u.own.b, 16 * (lt % 4), s * KS, lane);
+#pragma unroll
+      for (int s = 0; s < PKS; ++s) xf[s] = Pol::fragx_c(sm.u.own.x, 16 * (lt % 4), s * KS, lane);
+    }
+  }
+
+  // ---- walk the t rows at or after this block's first u row
+  f4 accx[PT], accb[NTL];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) accx[i] = f4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < NTL; ++i) accb[i] = f4{0, 0, 0, 0};
+  float mcol = 0.0f, ecol = 0.0f, edg = 0.0f;
+  const int kb0 = v0 / kTB, nkb = (rows + kTB - 1) / kTB;
+  RowBlock<TI, N * R, R, NT, false, kTB> cb;
+  RowBlock<TY, P * R, R, NT, false, kTB> yb;
+  cb.template load<true>(Cg, a, b, h, c0, Lc, kb0 * kTB);
+  yb.template load<false>(Yg, a, b, h, c0, Lc, kb0 * kTB);
+  const float gu = utok < kQ ? sm.tb.gam[utok] : 0.0f;
+  const float bu = utok + 1 < kQ ? sm.tb.bpr[utok + 1] : 0.0f;
+  const double csu = sm.tb.cs[min(utok, kQ - 1)];
+  for (int k = kb0; k < nkb; ++k) {
+    __syncthreads();   // the previous block's reads are done
+    store_rows<Pol, TI, N, R, NT, kTB>(cb, sm.u.st.c, sm.tb, k * kTB / R, Lc, NoPrep{});
+    put_rows_T<Pol, TI, N, R, NT, kTB, true>(cb, sm.u.st.ct, sm.tb, nullptr, k * kTB / R, Lc);
+    put_rows<Pol, TY, P, R, NT, kTB>(yb, sm.u.st.y);
+    put_rows_T<Pol, TY, P, R, NT, kTB, false>(yb, sm.u.st.yt, sm.tb, nullptr, k * kTB / R, Lc);
+    if (k + 1 < nkb) {
+      cb.template load<true>(Cg, a, b, h, c0, Lc, (k + 1) * kTB);
+      yb.template load<false>(Yg, a, b, h, c0, Lc, (k + 1) * kTB);
+    }
+    __syncthreads();
+    const int ttok_max = min(Lc - 1, (k * kTB + kTB - 1) / R);
+    if (!live || (16 * utile) / R > ttok_max) continue;
+    f4 w1[2], w2[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      f4 d1 = f4{0, 0, 0, 0}, d2 = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) d1 = Pol::mma(Pol::frag(sm.u.st.c, 16 * dt, s * KS, lane), bf[s], d1);
+#pragma unroll
+      for (int s = 0; s < PKS; ++s) d2 = Pol::mma_x(Pol::frag(sm.u.st.y, 16 * dt, s * KS, lane), xf[s], d2);
+      // D[t][u]: column u = uv, rows t = k kTB + 16 dt + 4 g + jj
+      const int trow0 = k * kTB + 16 * dt + 4 * gq;
+      float rv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int ttok = (trow0 + jj) / R;
+        float em = 0.0f, mm = 0.0f;
+        if (ttok < Lc && ttok >= utok && uv < rows) {
+          em = __expf((float)(sm.tb.cs[ttok] - csu));
+          mm = em * (gu + (utok < ttok ? bu : 0.0f));
+        }
+        const float pr = d1[jj] * d2[jj];
+        mcol += pr * mm;
+        if (ttok > utok) ecol += pr * em;
+        else edg += pr * em;
+        rv[jj] = group_sum<16>(pr * mm);   // over this tile's 16 u columns
+        w1[dt][jj] = d1[jj] * mm;
+        w2[dt][jj] = d2[jj] * mm;
+      }
+      if (l16 == 0) rows_by_token<R>(rv, trow0, [&](int t, float v) { sm.rowpart[wave][t] = v; });
+    }
+#pragma unroll
+    for (int q = 0; q < 2 / Pol::DT; ++q) {
+      const typename Pol::Frag a1 = Pol::frag_from_d(w1 + q * Pol::DT);
+      const typename Pol::Frag a2 = Pol::frag_from_d(w2 + q * Pol::DT);
+      const int kk = 16 * Pol::DT * q;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) accx[i] = Pol::mma(a1, Pol::fragp(sm.u.st.yt, 16 * i, kk, lane), accx[i]);
+#pragma unroll
+      for (int i = 0; i < NTL; ++i) accb[i] = Pol::mma(a2, Pol::fragp(sm.u.st.ct, 16 * i, kk, lane), accb[i]);
+    }
+  }
+
+  // ---- token sums: the mask's column sums (over the row groups, then the
+  // ranks of a token) and the row sums of this block's u columns
+  float* __restrict__ tk = g.tokw + ck.id * (6 * kQ);
+  mcol += __shfl_xor(mcol, 16, 64);
+  mcol += __shfl_xor(mcol, 32, 64);
+  ecol += __shfl_xor(ecol, 16, 64);
+  ecol += __shfl_xor(ecol, 32, 64);
+  edg += __shfl_xor(edg, 16, 64);
+  edg += __shfl_xor(edg, 32, 64);
+  mcol = group_sum<R>(mcol);
+  ecol = group_sum<R>(ecol);
+  edg = group_sum<R>(edg);
+  if (live && gq == 0 && l16 % R == 0 && utok < Lc) {
+    tk[kMcol * kQ + utok] = mcol;
+    tk[kEcol * kQ + utok] = ecol;
+    tk[kEdiag * kQ + utok] = edg;
+  }
+  __syncthreads();   // the row sums are in; the staging buffers are free
+  if (tid < kQ) {
+    float s = 0.0f;
+    for (int w = 0; w < NW; ++w) s += sm.rowpart[w][tid];
+    tk[(kRrow0 + half) * kQ + tid] = s;
+  }
+
+  // ---- the end state: Gt = rows of G_end rotated by -Phi_end
+  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
+                                        : g.dS + (ck.id + 1) * (P * N);
+  const f2* __restrict__ re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
+  for (int i = tid; i < P * NP; i += NT) {
+    const int p = i / NP, kp = i % NP;
+    const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
+    const f2 gt = rot_neg(gv, re[kp]);
+    const float v2[2] = {gt.x, gt.y};
+    Pol::template putn<2>(sm.u.gt, p, 2 * kp, v2);
+  }
+  __syncthreads();
+  const double cs_end = sm.tb.cs[Lc - 1];
+  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
+                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
+                            : 0.0f;
+  // this lane's D rows (u) in the end-state products: 16 utile + 4 g + jj
+  const int urow0 = 16 * utile + 4 * gq;
+  float mu[4], cu[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int ut = (urow0 + jj) / R;
+    mu[jj] = cu[jj] = 0.0f;
+    if (urow0 + jj < rows) {
+      const float e = __expf((float)(cs_end - sm.tb.cs[ut]));
+      mu[jj] = e * (sm.tb.gam[ut] + (ut < Lc - 1 ? sm.tb.bpr[ut + 1] : 0.0f));
+      cu[jj] = mu[jj] + (ut == Lc - 1 ? bpL : 0.0f);
+    }
+  }
+  // v = Bt Gt^T: dx += cu v, dm_end[u] = sum over p and ranks of x v
+  {
+    float dmv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      f4 v = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) v = Pol::mma(bf[s], Pol::frag(sm.u.gt, 16 * i, s * KS, lane), v);
+      const int p = 16 * i + l16;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vr = urow0 + jj;
+        const float xv = vr < rows ? ld1(Xc, (int64_t)(vr / R) * a.H * P * R + p * R + vr % R) : 0.0f;
+        accx[i][jj] += cu[jj] * v[jj];
+        dmv[jj] += xv * v[jj];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dmv[jj] = group_sum<16>(dmv[jj]);
+    if (live && l16 == 0)
+      rows_by_token<R>(dmv, urow0, [&](int t, float v) {
+        if (t < Lc) tk[kDmend * kQ + t] = v;
+      });
+  }
+  __syncthreads();   // Gt is read
+  for (int i = tid; i < P * NP; i += NT) {
+    const int p = i / NP, kp = i % NP;
+    const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
+    const f2 gt = rot_neg(gv, re[kp]);
+    Pol::put(sm.u.gtt, 2 * kp, p, gt.x);
+    Pol::put(sm.u.gtt, 2 * kp + 1, p, gt.y);
+  }
+  __syncthreads();
+
+  // ---- outputs: dx; w = X Gt: dBt += m_end w, the crossing term of the
+  // last token (raw frame, kept out of the phase gradient), dB back in the
+  // raw frame and the u side of the phase gradient
+  const bool shared_grp = G_ != a.H;
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int p = 16 * i + l16;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vr = urow0 + jj;
+        if (vr < rows) g.dx[(ti0 + (int64_t)(vr / R) * a.H) * P * R + p * R + vr % R] = accx[i][jj];
+      }
+    }
+  }
+  float* __restrict__ dBo = shared_grp ? g.dBh : g.dB;
+  float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
+#pragma unroll
+  for (int i = 0; i < NTL; ++i) {
+    f4 w = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < PKS; ++s) w = Pol::mma_xa(xf[s], Pol::frag(sm.u.gtt, 16 * i, s * KS, lane), w);
+    const int n = 16 * i + l16, kp = n >> 1;
+    const bool odd = n & 1;
+    float ph[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int vr = urow0 + jj, ut = vr / R, r = vr % R;
+      const bool ok = live && vr < rows;
+      const float dbt = accb[i][jj] + mu[jj] * w[jj];
+      float bo = 0.0f, bq = 0.0f;
+      f2 cs = f2{1.0f, 0.0f};
+      if (ok) {
+        const int64_t e = (int64_t)ut * G_ * N * R + r;
+        bo = ld1(Bc, e + (int64_t)n * R);
+        bq = ld1(Bc, e + (int64_t)(n ^ 1) * R);
+        cs = sm.tb.cs_of(ut, kp);
+      }
+      // cross(dBt, Bt) of pair kp: this lane's half
+      ph[jj] = odd ? -dbt * rot_own(bq, bo, false, cs) : dbt * rot_own(bq, bo, true, cs);
+      const float v = dbt + (ck.next && ut == Lc - 1 ? bpL * w[jj] : 0.0f);
+      const float pv = __shfl_xor(v, 1, 64);
+      const float raw = odd ? cs.y * pv + cs.x * v : cs.x * v - cs.y * pv;
+      if (ok) dBo[(ti0 + (int64_t)ut * a.H) * N * R + (int64_t)n * R + r] = raw;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
+    if (live && !odd)
+      rows_by_token<R>(ph, urow0, [&](int t, float v) {
+        if (t < Lc) dph[t * NP + kp] = v;
+      });
+  }
+}
+
+// --------------------------------------------------------------------------
+// The t side and the chunk's per-token gradients.  One wave per 16-row t
+// tile, the whole chunk in one block.
+template <int P, int N, int R>
+struct GeoT {
+  static constexpr int ROWS = kQ * R, TILES = ROWS / 16;
+  static constexpr int NW = TILES, NT = 64 * NW;
+  static constexpr int TPT = NT / kQ;   // threads per token in the token passes
+  static_assert(NW == 4 || NW == 8 || NW == 16, "t-side geometry");
+};
+
+template <class Pol, int P, int N, int R>
+struct TSmem {
+  using G = GeoT<P, N, R>;
+  static constexpr int NP = N / 2;
+  Tables<N, false> tb;
+  float lam[kQ], Av[kQ], ecs[kQ], de[kQ];
+  float dcs[kQ], dgam[kQ], dbpr[kQ], part[G::NT];
+  float dphi_end[NP];
+  float red[G::NW];
+  float dphi[kQ][NP + 1];
+  union U {
+    TableScratch<N, G::NT> scr;
+    typename Pol::template Store<64, P> own;   // own dy rows
+    typename Pol::template Store<N, P> sht;    // Shat^T [n][p]
+    struct S {
+      typename Pol::template XStore<kTB, P> x;   // x rows [v][p]
+      typename Pol::template Store<N, kTB> bt;   // Bt^T   [n][v]
+    } stg[2];
+  } u;
+};
+
+template <int NW>
+__device__ __forceinline__ int t_tile_of(int wave) {
+  if constexpr (NW == 16) {
+    // the four waves of a SIMD (w, w + 4, ...) take tiles s, 7 - s, 8 + s, 15 - s
+    const int s = wave & 3, q = wave >> 2;
+    return q == 0 ? s : q == 1 ? 7 - s : q == 2 ? 8 + s : 15 - s;
+  } else if constexpr (NW == 8) {
+    return wave < 4 ? wave : 11 - wave;
+  } else {
+    return wave;
+  }
+}
+
+template <class Pol, typename TI, typename TY, int P, int N, int R>
+__global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  using G = GeoT<P, N, R>;
+  using GU = GeoU<P, N, R>;
+  constexpr int NT = G::NT, NW = G::NW, KS = Pol::KS;
+  constexpr int PKS = P / KS, NTL = N / 16, NP = N / 2;
+  __shared__ TSmem<Pol, P, N, R> sm;
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
+  const int c = blockIdx.x;
+  const bool last = c + 1 >= a.nchunk;
+  const int rows = Lc * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, l16 = lane & 15;
+  const int ttile = t_tile_of<NW>(wave);
+  const bool live = 16 * ttile < rows;
+  const int tv = 16 * ttile + l16;   // this lane's t column in the Gram tiles
+  const int ttok = tv / R;
+  const int G_ = a.G;
+  const bool shared_grp = G_ != a.H;
+  const int64_t gi = group_index(a, b, c0, h), ti0 = token_index(a, b, c0, h);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+  const TY* __restrict__ Yg = static_cast<const TY*>(g.dy);
+  const TI* __restrict__ Bc = Bg + gi * N * R;
+  const TI* __restrict__ Cc = static_cast<const TI*>(a.C) + gi * N * R;
+  const TI* __restrict__ Xc = Xg + ti0 * P * R;
+
+  ThetaBlock<TI, N, NT> thb;
+  thb.load(a, b, h, c0, Lc);
+  chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
+  if (tid < kQ) {
+    sm.lam[tid] = thb.l;
+    sm.Av[tid] = thb.A;
+    sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
+  }
+
+  // own dy rows -> fragments
+  typename Pol::Frag yf[PKS];
+#pragma unroll
+  for (int s = 0; s < PKS; ++s) yf[s] = typename Pol::Frag{};
+#pragma unroll
+  for (int piece = 0; piece < R; ++piece) {
+    const int pv0 = 64 * piece;
+    if (pv0 >= rows) break;
+    RowBlock<TY, P * R, R, NT, false, 64> yb;
+    yb.template load<false>(Yg, a, b, h, c0, Lc, pv0);
+    __syncthreads();
+    put_rows<Pol, TY, P, R, NT, 64>(yb, sm.u.own);
+    __syncthreads();
+    if (ttile / 4 == piece) {
+#pragma unroll
+      for (int s = 0; s < PKS; ++s) yf[s] = Pol::frag(sm.u.own, 16 * (ttile % 4), s * KS, lane);
+    }
+  }
+  __syncthreads();
+  // the entry state: q = dY Shat, dCt = e^{cs_t} q, de_t = sum Ct . q
+  const float* __restrict__ Sh = a.S + ck.id * (P * N);
+  for (int i = tid; i < P * N / 4; i += NT) {
+    const int p = (4 * i) / N, n = (4 * i) % N;
+    const f4 v = reinterpret_cast<const f4*>(Sh)[i];
+    Pol::put(sm.u.sht, n, p, v.x);
+    Pol::put(sm.u.sht, n + 1, p, v.y);
+    Pol::put(sm.u.sht, n + 2, p, v.z);
+    Pol::put(sm.u.sht, n + 3, p, v.w);
+  }
+  __syncthreads();
+  const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
+  f4 acc[NTL];
+  {
+    float dev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      f4 q = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < PKS; ++s) q = Pol::mma(yf[s], Pol::frag(sm.u.sht, 16 * i, s * KS, lane), q);
+      const int n = 16 * i + l16;
+      const bool odd = n & 1;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vr = trow0 + jj, t = vr / R, r = vr % R;
+        float ct = 0.0f, sc = 0.0f;
+        if (live && vr < rows) {
+          const int64_t e = (int64_t)t * G_ * N * R + r;
+          ct = rot_own(ld1(Cc, e + (int64_t)n * R), ld1(Cc, e + (int64_t)(n ^ 1) * R), odd, sm.tb.cs_of(t, n >> 1));
+          sc = sm.ecs[t];
+        }
+        dev[jj] += ct * q[jj];
+        acc[i][jj] = sc * q[jj];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dev[jj] = group_sum<16>(dev[jj]);
+    if (live && l16 == 0)
+      rows_by_token<R>(dev, trow0, [&](int t, float v) { sm.de[t] = v; });
+  }
+
+  // ---- walk the u rows at or before this wave's t rows: dCt += W2 Bt
+  const int nkb = (rows + kTB - 1) / kTB;
+  const int ttok_max = min(Lc - 1, (16 * ttile + 15) / R);
+  RowBlock<TI, N * R, R, NT, false, kTB> bb;
+  RowBlock<TI, P * R, R, NT, false, kTB> xb;
+  bb.template load<true>(Bg, a, b, h, c0, Lc, 0);
+  xb.template load<false>(Xg, a, b, h, c0, Lc, 0);
+  auto stage = [&](int k) {
+    put_rows_T<Pol, TI, N, R, NT, kTB, true>(bb, sm.u.stg[k & 1].bt, sm.tb, nullptr, k * kTB / R, Lc);
+    put_xrows<Pol, TI, P, R, NT, kTB>(xb, sm.u.stg[k & 1].x);
+    if (k + 1 < nkb) {
+      bb.template load<true>(Bg, a, b, h, c0, Lc, (k + 1) * kTB);
+      xb.template load<false>(Xg, a, b, h, c0, Lc, (k + 1) * kTB);
+    }
+  };
+  __syncthreads();   // Shat^T is read
+  stage(0);
+  __syncthreads();
+  const double cst = sm.tb.cs[min(ttok, kQ - 1)];
+  for (int k = 0; k < nkb; ++k) {
+    if (k + 1 < nkb) stage(k + 1);
+    if (live && (k * kTB) / R <= ttok_max) {
+      f4 w[2];
+#pragma unroll
+      for (int du = 0; du < 2; ++du) {
+        f4 d = f4{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < PKS; ++s)
+          d = Pol::mma_xa(Pol::fragx_c(sm.u.stg[k & 1].x, 16 * du, s * KS, lane), yf[s], d);
+        // D[u][t]: column t = tv, rows u = k kTB + 16 du + 4 g + jj
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int ut = (k * kTB + 16 * du + 4 * gq + jj) / R;
+          float mm = 0.0f;
+          if (ttok < Lc && ut <= ttok)
+            mm = __expf((float)(cst - sm.tb.cs[ut])) * (sm.tb.gam[ut] + (ut < ttok ? sm.tb.bpr[ut + 1] : 0.0f));
+          w[du][jj] = d[jj] * mm;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2 / Pol::DT; ++q) {
+        const typename Pol::Frag af = Pol::frag_from_d(w + q * Pol::DT);
+#pragma unroll
+        for (int i = 0; i < NTL; ++i)
+          acc[i] = Pol::mma(af, Pol::fragp(sm.u.stg[k & 1].bt, 16 * i, 16 * Pol::DT * q, lane), acc[i]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- dC back in the raw frame; the phase gradient of every (token, pair)
+  // = the C side here + the u side from k_bwd_u
+  float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
+  const float* __restrict__ dphB = g.dphiB + ck.id * (kQ * NP);
+#pragma unroll
+  for (int i = 0; i < NTL; ++i) {
+    const int n = 16 * i + l16, kp = n >> 1;
+    const bool odd = n & 1;
+    float ph[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int vr = trow0 + jj, t = vr / R, r = vr % R;
+      const bool ok = live && vr < rows;
+      const float dct = acc[i][jj];
+      float co = 0.0f, cq = 0.0f;
+      f2 cs = f2{1.0f, 0.0f};
+      if (ok) {
+        const int64_t e = (int64_t)t * G_ * N * R + r;
+        co = ld1(Cc, e + (int64_t)n * R);
+        cq = ld1(Cc, e + (int64_t)(n ^ 1) * R);
+        cs = sm.tb.cs_of(t, kp);
+      }
+      ph[jj] = odd ? -dct * rot_own(cq, co, false, cs) : dct * rot_own(cq, co, true, cs);
+      const float pv = __shfl_xor(dct, 1, 64);
+      const float raw = odd ? cs.y * pv + cs.x * dct : cs.x * dct - cs.y * pv;
+      if (ok) dCo[(ti0 + (int64_t)t * a.H) * N * R + (int64_t)n * R + r] = raw;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
+    if (live && !odd)
+      rows_by_token<R>(ph, trow0, [&](int t, float v) {
+        if (t < Lc) sm.dphi[t][kp] = v + dphB[t * NP + kp];
+      });
+  }
+
+  // ---- the end state's scalars: <Gt, Shat>, the end rotation's phase
+  // gradient <G_end, J S_end> per pair, and <dShat_c, x_{c0-1} B_{c0-1}^T>
+  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
+                                        : g.dS + (ck.id + 1) * (P * N);
+  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
+                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
+                            : 0.0f;
+  const TI* __restrict__ Blast = Bc + (int64_t)(Lc - 1) * G_ * N * R;
+  const TI* __restrict__ Xlast = Xc + (int64_t)(Lc - 1) * a.H * P * R;
+  const TI* xprev = nullptr;
+  const TI* bprev = nullptr;
+  if (c > 0) {
+    xprev = Xc - (int64_t)a.H * P * R;
+    bprev = Bc - (int64_t)G_ * N * R;
+  } else if (a.has_prev) {
+    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
+    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
+  }
+  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
+  static_assert(NT % NP == 0, "each thread keeps one pair in the end-state loop");
+  {
+    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
+    const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
+                                           : a.S + (ck.id + 1) * (P * N);
+    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
+    for (int i = tid; i < P * NP; i += NT) {
+      const int p = i / NP, kp = i % NP;
+      const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
+      const f2 gt = rot_neg(gv, re[kp]);
+      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)p * N + 2 * kp);
+      e_part += gt.x * sh.x + gt.y * sh.y;
+      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * kp);
+      if (ck.next) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float xl = ld1(Xlast, (int64_t)p * R + r);
+          se.x -= bpL * xl * ld1(Blast, (int64_t)(2 * kp) * R + r);
+          se.y -= bpL * xl * ld1(Blast, (int64_t)(2 * kp + 1) * R + r);
+        }
+      }
+      ph_part += -gv.x * se.y + gv.y * se.x;
+      if (xprev) {
+        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * kp);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          h_part += ld1(xprev, (int64_t)p * R + r) *
+                    (ds.x * ld1(bprev, (int64_t)(2 * kp) * R + r) + ds.y * ld1(bprev, (int64_t)(2 * kp + 1) * R + r));
+      }
+    }
+  }
+  sm.part[tid] = ph_part;
+  const float e_end = block_sum<NT>(e_part, sm.red);
+  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the part and de writes
+  if (tid < NP) {
+    float v = 0.0f;
+    for (int m = 0; m < NT / NP; ++m) v += sm.part[tid + NP * m];
+    sm.dphi_end[tid] = v;
+  }
+  __syncthreads();   // part is read
+
+  // ---- the token sums: log-decay (cs), trapezoid weights (gamma, beta')
+  const float* __restrict__ tk = g.tokw + ck.id * (6 * kQ);
+  const double cs_end = sm.tb.cs[Lc - 1];
+  if (tid < kQ) {
+    const int u = tid;
+    float dc = 0.0f, dg = 0.0f, dbn = 0.0f, pm = 0.0f;
+    if (u < Lc) {
+      const float e = expf((float)(cs_end - sm.tb.cs[u]));
+      const float m = e * (sm.tb.gam[u] + (u < Lc - 1 ? sm.tb.bpr[u + 1] : 0.0f));
+      const float d = tk[kDmend * kQ + u];
+      float rr = tk[kRrow0 * kQ + u];
+      if (GU::SPLIT == 2 && rows > GU::BROWS) rr += tk[kRrow1 * kQ + u];
+      const float ec = tk[kEcol * kQ + u];
+      dc = rr - tk[kMcol * kQ + u] + sm.ecs[u] * sm.de[u];
+      dg = ec + tk[kEdiag * kQ + u] + d * e;
+      dbn = ec;
+      if (u < Lc - 1) {
+        pm = d * m;
+        dc -= pm;
+        dbn += d * e;
+      }
+    }
+    sm.dcs[u] = dc;
+    sm.dgam[u] = dg;
+    if (u + 1 < kQ) sm.dbpr[u + 1] = dbn;
+    if (u == 0) sm.dbpr[0] = h_end;
+    sm.part[u] = pm;
+  }
+  __syncthreads();
+  if (tid == 0) {   // the chunk's last token: the end state's decay and weights
+    float v = expf((float)cs_end) * e_end;
+    for (int u = 0; u < Lc - 1; ++u) v += sm.part[u];
+    sm.dcs[Lc - 1] += v;
+  }
+  __syncthreads();
+  // suffix sums over the chunk: phase (from the end rotation) and log-decay
+  if (tid < NP) {
+    const int k = tid;
+    float run = sm.dphi_end[k];
+    for (int t = Lc - 1; t >= 0; --t) {
+      run += sm.dphi[t][k];
+      sm.dphi[t][k] = run;
+    }
+  } else if (tid == NP) {
+    float run = 0.0f;
+    for (int t = Lc - 1; t >= 0; --t) {
+      run += sm.dcs[t];
+      sm.dcs[t] = run;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-token outputs: theta, dt, lam, A
+  constexpr int TPT = G::TPT, KPT = NP / TPT;
+  static_assert(KPT >= 1 && NP % TPT == 0, "pairs per thread");
+  const bool angle = (a.flags & kThetaIsAngle) != 0;
+  const int tt = tid / TPT, cg = tid % TPT;
+  float dt_theta = 0.0f;
+  if (tt < Lc) {
+    const int64_t tok = ti0 + (int64_t)tt * a.H, grp = gi + (int64_t)tt * G_;
+    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + grp * NP;
+    const float dtt = sm.tb.dt[tt];
+    float* __restrict__ dth = shared_grp ? g.dthh + tok * NP : g.dtheta + grp * NP;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int k = cg * KPT + j;
+      const float dphv = sm.dphi[tt][k];
+      if (!angle) dt_theta += ld1(th, k) * dphv;
+      dth[k] = angle ? dphv : dtt * dphv;
+    }
+  }
+  dt_theta = group_sum<TPT>(dt_theta);
+  float da_part = 0.0f;
+  if (tt < Lc && cg == 0) {
+    const int64_t tok = ti0 + (int64_t)tt * a.H;
+    const float dtt = sm.tb.dt[tt], lm = sm.lam[tt], da = sm.dcs[tt];
+    g.ddt[tok] = sm.Av[tt] * da + lm * sm.dgam[tt] + (1.0f - lm) * sm.dbpr[tt] + dt_theta;
+    g.dlam[tok] = dtt * (sm.dgam[tt] - sm.dbpr[tt]);
+    if (a.flags & kAPerToken) g.dA[tok] = dtt * da;
+    else da_part = dtt * da;
+  }
+  if (!(a.flags & kAPerToken)) {   // per chunk; a final pass sums them per head
+    const float sA = block_sum<NT>(da_part, sm.red);
+    if (tid == 0) g.dApart[ck.id] = sA;
+  }
+  // the token before the sequence: dx_prev = beta'_0 dShat_0 B_prev,
+  // dB_prev = beta'_0 dShat_0^T x_prev
+  if (c == 0 && a.has_prev && (g.dx_prev || g.dB_prev)) {
+    const float bp0 = sm.tb.bpr[0];
+    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
+    static_assert(P * R <= NT && N * R <= NT, "one thread per element");
+    if (g.dx_prev && tid < P * R) {
+      const int p = tid / R, r = tid % R;
+      float v = 0.0f;
+      for (int n = 0; n < N; ++n) v += dSc[(int64_t)p * N + n] * ld1(bprev, (int64_t)n * R + r);
+      g.dx_prev[((int64_t)b * a.H + h) * P * R + tid] = bp0 * v;
+    }
+    if (g.dB_prev && tid < N * R) {
+      const int n = tid / R, r = tid % R;
+      float v = 0.0f;
+      for (int p = 0; p < P; ++p) v += dSc[(int64_t)p * N + n] * ld1(xprev, (int64_t)p * R + r);
+      if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N * R + tid] = bp0 * v;
+      else g.dB_prev[((int64_t)b * G_ + head_group(a, h)) * N * R + tid] = bp0 * v;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+template <class Pol, typename TI, typename TY, int P, int N, int R>
+hipError_t run_mma(const BackwardArgs& g, hipStream_t s) {
+  const PrefillArgs& a = g.f;
+  const dim3 grid(a.nchunk, a.H, a.Bsz);
+  hipLaunchKernelGGL((k_bwd_adjoint_mma<Pol, TI, TY, P, N, R>), grid, dim3(AdjGeo<P, N>::NT), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_bwd_state_pass(g, s)) != hipSuccess) return e;
+  using GU = GeoU<P, N, R>;
+  const int nx = GU::SPLIT == 1 ? a.nchunk : GU::SPLIT * ((a.nchunk + 7) / 8) * 8;
+  hipLaunchKernelGGL((k_bwd_u<Pol, TI, TY, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(GU::NT), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_t<Pol, TI, TY, P, N, R>), grid, dim3(GeoT<P, N, R>::NT), 0, s, g);
+  return hipGetLastError();
+}
+
+template <class Pol, typename TI, typename TY>
+int dispatch_mma(const BackwardArgs& g, hipStream_t s, hipError_t* e) {
+  const PrefillArgs& a = g.f;
+#define M3_MMA_SHAPE(PP, NN, RR)                                    \
+  if (a.P == PP && a.N == NN && a.R == RR) {                        \
+    *e = run_mma<Pol, TI, TY, PP, NN, RR>(g, s);                    \
+    return 0;                                                       \
+  }
+  M3_MMA_SHAPE(64, 128, 2)
+  M3_MMA_SHAPE(64, 128, 4)
+  M3_MMA_SHAPE(32, 64, 4)
+  M3_MMA_SHAPE(64, 64, 4)
+#undef M3_MMA_SHAPE
+  return -1;
+}
+
+}  // namespace
+
+int launch_backward_mma(const BackwardArgs& g, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
+  if (in_bf16)
+    return dy_bf16 ? dispatch_mma<PolF16, bf16_t, bf16_t>(g, s, e) : dispatch_mma<PolF16, bf16_t, float>(g, s, e);
+  return dy_bf16 ? dispatch_mma<PolF32, float, bf16_t>(g, s, e) : dispatch_mma<PolF32, float, float>(g, s, e);
+}
+
+}  // namespace m3

@@ -294,4 +294,29 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
   __syncthreads();
 }
 
+// element i of an input array of type T
+template <typename T>
+__device__ __forceinline__ float ldy(const void* p, int64_t i) {
+  return ld1(static_cast<const T*>(p), i);
+}
+
+// rotate one pair by -angle / +angle given (cos, sin)
+__device__ __forceinline__ f2 rot_neg(f2 v, f2 cs) { return f2{cs.x * v.x + cs.y * v.y, -cs.y * v.x + cs.x * v.y}; }
+__device__ __forceinline__ f2 rot_pos(f2 v, f2 cs) { return f2{cs.x * v.x - cs.y * v.y, cs.y * v.x + cs.x * v.y}; }
+
+// block-wide sum in a fixed order (all threads receive it); red holds one
+// value per wave
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = group_sum<64>(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) s += red[w];
+  return s;
+}
+
 }  // namespace m3

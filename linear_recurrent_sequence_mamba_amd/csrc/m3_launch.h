@@ -107,11 +107,20 @@ struct BackwardArgs {
   // workspace: per-chunk dA partials; with head groups, per-head gradients
   // of B, C, theta and B_prev before the fixed-order sum over each group
   float *dApart, *dBh, *dCh, *dthh, *dBph;
+  // workspace of the rank-R kernels: per-chunk token sums of the u-side
+  // kernel [units, 6, Q] and its phase-gradient part [units, Q, N/2]
+  float *tokw, *dphiB;
 };
 bool backward_supported(int P, int N, int R, int Q);
 size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int G, int Q);
 void backward_carve(BackwardArgs& a, void* ws);
 int launch_backward(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e);
+// the chunk kernels of the rank-R backward on matrix cores (after the
+// forward states): 0 when launched (*e = the launch status), -1 when the
+// shape has no such kernels
+int launch_backward_mma(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e);
+// the reverse pass over chunks turning chunk adjoints into dL/dShat_c (and dh0)
+hipError_t launch_bwd_state_pass(const BackwardArgs& a, hipStream_t s);
 
 // builds seqs and cmap from the sequence offsets cu [Bsz + 1] (device)
 hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s);
