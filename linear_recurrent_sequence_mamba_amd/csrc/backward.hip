@@ -1210,7 +1210,7 @@ static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int R, int G, int Q
     sz[7] = (size_t)Bsz * H * N * R * 4;
   }
   if (R > 1) {   // the rank-R kernels' token sums and u-side phase gradients
-    sz[8] = units * 6 * Q * 4;
+    sz[8] = units * 7 * Q * 4;
     sz[9] = units * Q * (N / 2) * 4;
   }
   size_t total = 0;

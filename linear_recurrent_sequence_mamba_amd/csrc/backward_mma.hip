@@ -18,10 +18,11 @@
 //  k_bwd_u  (batch, head, chunk [x 2]): one wave per 16 u rows, walking the
 //           t rows at or after them: dx, dB, the mask's column sums, the
 //           u side of the phase gradient;
-//  k_bwd_t  (batch, head, chunk): one wave per 16 t rows, walking the u rows
-//           at or before them: dC and the C side of the phase gradient,
-//           then the per-token gradients of the chunk (dt, lam, A, theta)
-//           from the token sums of both.
+//  k_bwd_t  (batch, head, chunk [x 2]): one wave per 16 t rows, walking the
+//           u rows at or before them: dC and the C side of the phase
+//           gradient;
+//  k_bwd_fin (batch, head, chunk): the per-token gradients of the chunk (dt,
+//           lam, A, theta) from the token sums of both sides.
 // Every sum runs in a fixed order (no atomics): equal calls give equal bits.
 #include "chunk_common.h"
 #include "mfma_pol.h"
@@ -125,6 +126,92 @@ __device__ __forceinline__ void put_rows_T(const RowBlock<TI, E * R, R, NT, fals
     // the R virtual rows of token tl are consecutive columns of st
 #pragma unroll
     for (int m = 0; m < 8 / R; ++m) Pol::template putn<R>(st, e0 / R + m, tl * R, v + m * R);
+  }
+}
+
+// rows of a block into both layouts, st[v - v0][e] and stT[e][v - v0]: B or
+// C rotated by -Phi_t (ROT; one rotation for both), or x / dy as loaded
+template <class Pol, typename TI, int E, int R, int NT, int ROWS, bool ROT, class Tab>
+__device__ __forceinline__ void put_rows_both(const RowBlock<TI, E * R, R, NT, false, ROWS>& rb,
+                                              typename Pol::template Store<ROWS, E>& st,
+                                              typename Pol::template Store<E, ROWS>& stT, const Tab& tb,
+                                              int t0, int Lc) {
+  using RBk = RowBlock<TI, E * R, R, NT, false, ROWS>;
+  constexpr int NPAIR = 4 / R;
+#pragma unroll
+  for (int i = 0; i < RBk::IT; ++i) {
+    const int vi = threadIdx.x + NT * i;
+    if (vi >= RBk::NV) continue;
+    int tl, e0;
+    RBk::where(vi, tl, e0);
+    const int t = t0 + tl;
+    float v[8];
+    rb.raw[i].get(v);
+    if constexpr (ROT) {
+      f2 csr[NPAIR];
+      tb.template cs_run<NPAIR>(t, e0 / R / 2, t < Lc, csr);
+#pragma unroll
+      for (int pi = 0; pi < NPAIR; ++pi) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float u0 = v[(2 * pi) * R + r], u1 = v[(2 * pi + 1) * R + r];
+          v[(2 * pi) * R + r] = csr[pi].x * u0 + csr[pi].y * u1;
+          v[(2 * pi + 1) * R + r] = -csr[pi].y * u0 + csr[pi].x * u1;
+        }
+      }
+    }
+    if constexpr (R == 1) {
+      Pol::put8(st, tl, e0, v);
+    } else {
+      constexpr int M = 8 / R;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float w[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) w[m] = v[m * R + r];
+        Pol::template putn<M>(st, tl * R + r, e0 / R, w);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 8 / R; ++m) Pol::template putn<R>(stT, e0 / R + m, tl * R, v + m * R);
+  }
+}
+
+// the R ranks of one (token, column) element: R consecutive values, one
+// vector access (16-byte aligned arrays, so R * 4 or R * 2 bytes aligned)
+template <int R>
+__device__ __forceinline__ void ldr(const float* __restrict__ p, float* v) {
+  if constexpr (R == 4) {
+    const f4 q = *reinterpret_cast<const f4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else if constexpr (R == 2) {
+    const f2 q = *reinterpret_cast<const f2*>(p);
+    v[0] = q.x; v[1] = q.y;
+  } else {
+    v[0] = *p;
+  }
+}
+template <int R>
+__device__ __forceinline__ void ldr(const bf16_t* __restrict__ p, float* v) {
+  if constexpr (R == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  } else if constexpr (R == 2) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = __uint_as_float(q << 16); v[1] = __uint_as_float(q & 0xffff0000u);
+  } else {
+    v[0] = ld1(p, 0);
+  }
+}
+template <int R>
+__device__ __forceinline__ void str(float* __restrict__ p, const float* v) {
+  if constexpr (R == 4) {
+    *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (R == 2) {
+    *reinterpret_cast<f2*>(p) = f2{v[0], v[1]};
+  } else {
+    *p = v[0];
   }
 }
 
@@ -236,8 +323,8 @@ struct GeoU {
   static_assert((SPLIT == 1 || SPLIT == 2) && BROWS % 64 == 0, "u-side geometry");
 };
 
-// per-chunk token sums in the workspace: [units][6][Q]
-enum TokSum { kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5 };
+// per-chunk token sums in the workspace: [units][kTokSums][Q]
+enum TokSum { kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5, kDe = 6, kTokSums = 7 };
 
 template <class Pol, int P, int N, int R>
 struct USmem {
@@ -255,7 +342,7 @@ struct USmem {
       typename Pol::template Store<kTB, P> y;   // dy rows   [v][p]
       typename Pol::template Store<N, kTB> ct;  // Ct^T      [n][v]
       typename Pol::template Store<P, kTB> yt;  // dy^T      [p][v]
-    } st;
+    } st[2];                                    // double-buffered
     typename Pol::template Store<P, N> gt;      // Gt        [p][n]
     typename Pol::template Store<N, P> gtt;     // Gt^T      [n][p]
   } u;
@@ -349,63 +436,80 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
   const float gu = utok < kQ ? sm.tb.gam[utok] : 0.0f;
   const float bu = utok + 1 < kQ ? sm.tb.bpr[utok + 1] : 0.0f;
   const double csu = sm.tb.cs[min(utok, kQ - 1)];
-  for (int k = kb0; k < nkb; ++k) {
-    __syncthreads();   // the previous block's reads are done
-    store_rows<Pol, TI, N, R, NT, kTB>(cb, sm.u.st.c, sm.tb, k * kTB / R, Lc, NoPrep{});
-    put_rows_T<Pol, TI, N, R, NT, kTB, true>(cb, sm.u.st.ct, sm.tb, nullptr, k * kTB / R, Lc);
-    put_rows<Pol, TY, P, R, NT, kTB>(yb, sm.u.st.y);
-    put_rows_T<Pol, TY, P, R, NT, kTB, false>(yb, sm.u.st.yt, sm.tb, nullptr, k * kTB / R, Lc);
+  // t block k goes into buffer k & 1 while the MFMAs of block k - 1 run;
+  // one barrier per block
+  auto stage = [&](int k) {
+    auto& st = sm.u.st[k & 1];
+    put_rows_both<Pol, TI, N, R, NT, kTB, true>(cb, st.c, st.ct, sm.tb, k * kTB / R, Lc);
+    put_rows_both<Pol, TY, P, R, NT, kTB, false>(yb, st.y, st.yt, sm.tb, k * kTB / R, Lc);
     if (k + 1 < nkb) {
       cb.template load<true>(Cg, a, b, h, c0, Lc, (k + 1) * kTB);
       yb.template load<false>(Yg, a, b, h, c0, Lc, (k + 1) * kTB);
     }
-    __syncthreads();
+  };
+  __syncthreads();   // the own-row buffers are read
+  stage(kb0);
+  __syncthreads();
+  for (int k = kb0; k < nkb; ++k) {
+    if (k + 1 < nkb) stage(k + 1);
+    const auto& st = sm.u.st[k & 1];
     const int ttok_max = min(Lc - 1, (k * kTB + kTB - 1) / R);
-    if (!live || (16 * utile) / R > ttok_max) continue;
-    f4 w1[2], w2[2];
+    if (live && (16 * utile) / R <= ttok_max) {
+      f4 w1[2], w2[2];
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      f4 d1 = f4{0, 0, 0, 0}, d2 = f4{0, 0, 0, 0};
+      for (int dt = 0; dt < 2; ++dt) {
+        f4 d1 = f4{0, 0, 0, 0}, d2 = f4{0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) d1 = Pol::mma(Pol::frag(sm.u.st.c, 16 * dt, s * KS, lane), bf[s], d1);
+        for (int s = 0; s < NKS; ++s) d1 = Pol::mma(Pol::frag(st.c, 16 * dt, s * KS, lane), bf[s], d1);
 #pragma unroll
-      for (int s = 0; s < PKS; ++s) d2 = Pol::mma_x(Pol::frag(sm.u.st.y, 16 * dt, s * KS, lane), xf[s], d2);
-      // D[t][u]: column u = uv, rows t = k kTB + 16 dt + 4 g + jj
-      const int trow0 = k * kTB + 16 * dt + 4 * gq;
-      float rv[4];
+        for (int s = 0; s < PKS; ++s) d2 = Pol::mma_x(Pol::frag(st.y, 16 * dt, s * KS, lane), xf[s], d2);
+        // D[t][u]: column u = uv, rows t = k kTB + 16 dt + 4 g + jj; the R
+        // rows of one t token share its mask value
+        const int trow0 = k * kTB + 16 * dt + 4 * gq;
+        float rv[4 / R];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int ttok = (trow0 + jj) / R;
-        float em = 0.0f, mm = 0.0f;
-        if (ttok < Lc && ttok >= utok && uv < rows) {
-          em = __expf((float)(sm.tb.cs[ttok] - csu));
-          mm = em * (gu + (utok < ttok ? bu : 0.0f));
+        for (int j0 = 0; j0 < 4; j0 += R) {
+          const int ttok = (trow0 + j0) / R;
+          float em = 0.0f, mm = 0.0f;
+          if (ttok < Lc && ttok >= utok && uv < rows) {
+            em = __expf((float)(sm.tb.cs[ttok] - csu));
+            mm = em * (gu + (utok < ttok ? bu : 0.0f));
+          }
+          float ps = 0.0f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int jj = j0 + r;
+            ps += d1[jj] * d2[jj];
+            w1[dt][jj] = d1[jj] * mm;
+            w2[dt][jj] = d2[jj] * mm;
+          }
+          mcol += ps * mm;
+          if (ttok > utok) ecol += ps * em;
+          else edg += ps * em;
+          rv[j0 / R] = group_sum<16>(ps * mm);   // over this tile's 16 u columns
         }
-        const float pr = d1[jj] * d2[jj];
-        mcol += pr * mm;
-        if (ttok > utok) ecol += pr * em;
-        else edg += pr * em;
-        rv[jj] = group_sum<16>(pr * mm);   // over this tile's 16 u columns
-        w1[dt][jj] = d1[jj] * mm;
-        w2[dt][jj] = d2[jj] * mm;
+        if (l16 == 0) {
+#pragma unroll
+          for (int j0 = 0; j0 < 4; j0 += R) sm.rowpart[wave][(trow0 + j0) / R] = rv[j0 / R];
+        }
       }
-      if (l16 == 0) rows_by_token<R>(rv, trow0, [&](int t, float v) { sm.rowpart[wave][t] = v; });
+#pragma unroll
+      for (int q = 0; q < 2 / Pol::DT; ++q) {
+        const typename Pol::Frag a1 = Pol::frag_from_d(w1 + q * Pol::DT);
+        const typename Pol::Frag a2 = Pol::frag_from_d(w2 + q * Pol::DT);
+        const int kk = 16 * Pol::DT * q;
+#pragma unroll
+        for (int i = 0; i < PT; ++i) accx[i] = Pol::mma(a1, Pol::fragp(st.yt, 16 * i, kk, lane), accx[i]);
+#pragma unroll
+        for (int i = 0; i < NTL; ++i) accb[i] = Pol::mma(a2, Pol::fragp(st.ct, 16 * i, kk, lane), accb[i]);
+      }
     }
-#pragma unroll
-    for (int q = 0; q < 2 / Pol::DT; ++q) {
-      const typename Pol::Frag a1 = Pol::frag_from_d(w1 + q * Pol::DT);
-      const typename Pol::Frag a2 = Pol::frag_from_d(w2 + q * Pol::DT);
-      const int kk = 16 * Pol::DT * q;
-#pragma unroll
-      for (int i = 0; i < PT; ++i) accx[i] = Pol::mma(a1, Pol::fragp(sm.u.st.yt, 16 * i, kk, lane), accx[i]);
-#pragma unroll
-      for (int i = 0; i < NTL; ++i) accb[i] = Pol::mma(a2, Pol::fragp(sm.u.st.ct, 16 * i, kk, lane), accb[i]);
-    }
+    __syncthreads();
   }
 
   // ---- token sums: the mask's column sums (over the row groups, then the
   // ranks of a token) and the row sums of this block's u columns
-  float* __restrict__ tk = g.tokw + ck.id * (6 * kQ);
+  float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
   mcol += __shfl_xor(mcol, 16, 64);
   mcol += __shfl_xor(mcol, 32, 64);
   ecol += __shfl_xor(ecol, 16, 64);
@@ -465,12 +569,19 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 #pragma unroll
       for (int s = 0; s < NKS; ++s) v = Pol::mma(bf[s], Pol::frag(sm.u.gt, 16 * i, s * KS, lane), v);
       const int p = 16 * i + l16;
+      float xv[4];
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += R) {
+        const int vr = urow0 + j0;
+        if (vr < rows) ldr<R>(Xc + (int64_t)(vr / R) * a.H * P * R + p * R, xv + j0);
+        else
+#pragma unroll
+          for (int r = 0; r < R; ++r) xv[j0 + r] = 0.0f;
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int vr = urow0 + jj;
-        const float xv = vr < rows ? ld1(Xc, (int64_t)(vr / R) * a.H * P * R + p * R + vr % R) : 0.0f;
         accx[i][jj] += cu[jj] * v[jj];
-        dmv[jj] += xv * v[jj];
+        dmv[jj] += xv[jj] * v[jj];
       }
     }
 #pragma unroll
@@ -498,10 +609,11 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int p = 16 * i + l16;
+      const float xo[4] = {accx[i][0], accx[i][1], accx[i][2], accx[i][3]};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int vr = urow0 + jj;
-        if (vr < rows) g.dx[(ti0 + (int64_t)(vr / R) * a.H) * P * R + p * R + vr % R] = accx[i][jj];
+      for (int j0 = 0; j0 < 4; j0 += R) {
+        const int vr = urow0 + j0;
+        if (vr < rows) str<R>(g.dx + (ti0 + (int64_t)(vr / R) * a.H) * P * R + p * R, xo + j0);
       }
     }
   }
@@ -514,26 +626,36 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     for (int s = 0; s < PKS; ++s) w = Pol::mma_xa(xf[s], Pol::frag(sm.u.gtt, 16 * i, s * KS, lane), w);
     const int n = 16 * i + l16, kp = n >> 1;
     const bool odd = n & 1;
-    float ph[4];
+    // raw B of this lane's column (the pair partner's from the next lane)
+    float bo[4], raw[4], ph[4];
+    f2 cs[4];
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      const int vr = urow0 + j0, ut = vr / R;
+      const bool ok = live && vr < rows;
+      if (ok) ldr<R>(Bc + (int64_t)ut * G_ * N * R + (int64_t)n * R, bo + j0);
+      else
+#pragma unroll
+        for (int r = 0; r < R; ++r) bo[j0 + r] = 0.0f;
+      const f2 c2 = ok ? sm.tb.cs_of(ut, kp) : f2{1.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < R; ++r) cs[j0 + r] = c2;
+    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int vr = urow0 + jj, ut = vr / R, r = vr % R;
-      const bool ok = live && vr < rows;
+      const int ut = (urow0 + jj) / R;
+      const float bq = __shfl_xor(bo[jj], 1, 64);
       const float dbt = accb[i][jj] + mu[jj] * w[jj];
-      float bo = 0.0f, bq = 0.0f;
-      f2 cs = f2{1.0f, 0.0f};
-      if (ok) {
-        const int64_t e = (int64_t)ut * G_ * N * R + r;
-        bo = ld1(Bc, e + (int64_t)n * R);
-        bq = ld1(Bc, e + (int64_t)(n ^ 1) * R);
-        cs = sm.tb.cs_of(ut, kp);
-      }
       // cross(dBt, Bt) of pair kp: this lane's half
-      ph[jj] = odd ? -dbt * rot_own(bq, bo, false, cs) : dbt * rot_own(bq, bo, true, cs);
+      ph[jj] = odd ? -dbt * rot_own(bq, bo[jj], false, cs[jj]) : dbt * rot_own(bq, bo[jj], true, cs[jj]);
       const float v = dbt + (ck.next && ut == Lc - 1 ? bpL * w[jj] : 0.0f);
       const float pv = __shfl_xor(v, 1, 64);
-      const float raw = odd ? cs.y * pv + cs.x * v : cs.x * v - cs.y * pv;
-      if (ok) dBo[(ti0 + (int64_t)ut * a.H) * N * R + (int64_t)n * R + r] = raw;
+      raw[jj] = odd ? cs[jj].y * pv + cs[jj].x * v : cs[jj].x * v - cs[jj].y * pv;
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      const int vr = urow0 + j0;
+      if (live && vr < rows) str<R>(dBo + (ti0 + (int64_t)(vr / R) * a.H) * N * R + (int64_t)n * R, raw + j0);
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
@@ -545,26 +667,12 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 }
 
 // --------------------------------------------------------------------------
-// The t side and the chunk's per-token gradients.  One wave per 16-row t
-// tile, the whole chunk in one block.
-template <int P, int N, int R>
-struct GeoT {
-  static constexpr int ROWS = kQ * R, TILES = ROWS / 16;
-  static constexpr int NW = TILES, NT = 64 * NW;
-  static constexpr int TPT = NT / kQ;   // threads per token in the token passes
-  static_assert(NW == 4 || NW == 8 || NW == 16, "t-side geometry");
-};
-
+// The t side.  One wave per 16-row t tile, split over blocks as the u side.
 template <class Pol, int P, int N, int R>
 struct TSmem {
-  using G = GeoT<P, N, R>;
-  static constexpr int NP = N / 2;
+  using G = GeoU<P, N, R>;
   Tables<N, false> tb;
-  float lam[kQ], Av[kQ], ecs[kQ], de[kQ];
-  float dcs[kQ], dgam[kQ], dbpr[kQ], part[G::NT];
-  float dphi_end[NP];
-  float red[G::NW];
-  float dphi[kQ][NP + 1];
+  float ecs[kQ];
   union U {
     TableScratch<N, G::NT> scr;
     typename Pol::template Store<64, P> own;   // own dy rows
@@ -576,36 +684,32 @@ struct TSmem {
   } u;
 };
 
-template <int NW>
-__device__ __forceinline__ int t_tile_of(int wave) {
-  if constexpr (NW == 16) {
-    // the four waves of a SIMD (w, w + 4, ...) take tiles s, 7 - s, 8 + s, 15 - s
-    const int s = wave & 3, q = wave >> 2;
-    return q == 0 ? s : q == 1 ? 7 - s : q == 2 ? 8 + s : 15 - s;
-  } else if constexpr (NW == 8) {
-    return wave < 4 ? wave : 11 - wave;
-  } else {
-    return wave;
-  }
-}
-
 template <class Pol, typename TI, typename TY, int P, int N, int R>
-__global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
+__global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   const PrefillArgs& a = g.f;
-  using G = GeoT<P, N, R>;
-  using GU = GeoU<P, N, R>;
+  using G = GeoU<P, N, R>;
   constexpr int NT = G::NT, NW = G::NW, KS = Pol::KS;
   constexpr int PKS = P / KS, NTL = N / 16, NP = N / 2;
   __shared__ TSmem<Pol, P, N, R> sm;
+  int c, half;
+  if constexpr (G::SPLIT == 2) {
+    c = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+    half = (blockIdx.x >> 3) & 1;
+  } else {
+    c = blockIdx.x;
+    half = 0;
+  }
   const int h = blockIdx.y;
   ChunkRef ck;
-  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  if (!chunk_ref(a, c, h, blockIdx.z, ck)) return;
   const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
-  const int c = blockIdx.x;
-  const bool last = c + 1 >= a.nchunk;
   const int rows = Lc * R;
+  const int v0 = half * G::BROWS;
+  if (v0 >= rows) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, gq = lane >> 4, l16 = lane & 15;
-  const int ttile = t_tile_of<NW>(wave);
+  // waves w and w + 4 share a SIMD: tiles w and 7 - w even out the causal work
+  const int lt = (NW == 8) ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int ttile = v0 / 16 + lt;
   const bool live = 16 * ttile < rows;
   const int tv = 16 * ttile + l16;   // this lane's t column in the Gram tiles
   const int ttok = tv / R;
@@ -615,40 +719,34 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
   const TY* __restrict__ Yg = static_cast<const TY*>(g.dy);
-  const TI* __restrict__ Bc = Bg + gi * N * R;
   const TI* __restrict__ Cc = static_cast<const TI*>(a.C) + gi * N * R;
-  const TI* __restrict__ Xc = Xg + ti0 * P * R;
 
   ThetaBlock<TI, N, NT> thb;
   thb.load(a, b, h, c0, Lc);
   chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
-  if (tid < kQ) {
-    sm.lam[tid] = thb.l;
-    sm.Av[tid] = thb.A;
-    sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
-  }
+  if (tid < kQ) sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
 
   // own dy rows -> fragments
   typename Pol::Frag yf[PKS];
 #pragma unroll
   for (int s = 0; s < PKS; ++s) yf[s] = typename Pol::Frag{};
 #pragma unroll
-  for (int piece = 0; piece < R; ++piece) {
-    const int pv0 = 64 * piece;
+  for (int piece = 0; piece < G::BROWS / 64; ++piece) {
+    const int pv0 = v0 + 64 * piece;
     if (pv0 >= rows) break;
     RowBlock<TY, P * R, R, NT, false, 64> yb;
     yb.template load<false>(Yg, a, b, h, c0, Lc, pv0);
-    __syncthreads();
+    __syncthreads();   // the table scratch (or the previous piece) is free
     put_rows<Pol, TY, P, R, NT, 64>(yb, sm.u.own);
     __syncthreads();
-    if (ttile / 4 == piece) {
+    if (lt / 4 == piece) {
 #pragma unroll
-      for (int s = 0; s < PKS; ++s) yf[s] = Pol::frag(sm.u.own, 16 * (ttile % 4), s * KS, lane);
+      for (int s = 0; s < PKS; ++s) yf[s] = Pol::frag(sm.u.own, 16 * (lt % 4), s * KS, lane);
     }
   }
-  __syncthreads();
   // the entry state: q = dY Shat, dCt = e^{cs_t} q, de_t = sum Ct . q
   const float* __restrict__ Sh = a.S + ck.id * (P * N);
+  __syncthreads();   // the own-row buffer is read
   for (int i = tid; i < P * N / 4; i += NT) {
     const int p = (4 * i) / N, n = (4 * i) % N;
     const f4 v = reinterpret_cast<const f4*>(Sh)[i];
@@ -659,6 +757,7 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   }
   __syncthreads();
   const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
+  float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
   f4 acc[NTL];
   {
     float dev[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -669,27 +768,41 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       for (int s = 0; s < PKS; ++s) q = Pol::mma(yf[s], Pol::frag(sm.u.sht, 16 * i, s * KS, lane), q);
       const int n = 16 * i + l16;
       const bool odd = n & 1;
+      float co[4], sc[4];
+      f2 cs[4];
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += R) {
+        const int vr = trow0 + j0, t = vr / R;
+        const bool ok = live && vr < rows;
+        if (ok) ldr<R>(Cc + (int64_t)t * G_ * N * R + (int64_t)n * R, co + j0);
+        else
+#pragma unroll
+          for (int r = 0; r < R; ++r) co[j0 + r] = 0.0f;
+        const f2 c2 = ok ? sm.tb.cs_of(t, n >> 1) : f2{1.0f, 0.0f};
+        const float e = ok ? sm.ecs[t] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          cs[j0 + r] = c2;
+          sc[j0 + r] = e;
+        }
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int vr = trow0 + jj, t = vr / R, r = vr % R;
-        float ct = 0.0f, sc = 0.0f;
-        if (live && vr < rows) {
-          const int64_t e = (int64_t)t * G_ * N * R + r;
-          ct = rot_own(ld1(Cc, e + (int64_t)n * R), ld1(Cc, e + (int64_t)(n ^ 1) * R), odd, sm.tb.cs_of(t, n >> 1));
-          sc = sm.ecs[t];
-        }
-        dev[jj] += ct * q[jj];
-        acc[i][jj] = sc * q[jj];
+        const float cq = __shfl_xor(co[jj], 1, 64);
+        dev[jj] += rot_own(co[jj], cq, odd, cs[jj]) * q[jj];
+        acc[i][jj] = sc[jj] * q[jj];
       }
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) dev[jj] = group_sum<16>(dev[jj]);
     if (live && l16 == 0)
-      rows_by_token<R>(dev, trow0, [&](int t, float v) { sm.de[t] = v; });
+      rows_by_token<R>(dev, trow0, [&](int t, float v) {
+        if (t < Lc) tk[kDe * kQ + t] = v;
+      });
   }
 
   // ---- walk the u rows at or before this wave's t rows: dCt += W2 Bt
-  const int nkb = (rows + kTB - 1) / kTB;
+  const int nkb = (min(rows, v0 + G::BROWS) + kTB - 1) / kTB;
   const int ttok_max = min(Lc - 1, (16 * ttile + 15) / R);
   RowBlock<TI, N * R, R, NT, false, kTB> bb;
   RowBlock<TI, P * R, R, NT, false, kTB> xb;
@@ -717,14 +830,16 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
 #pragma unroll
         for (int s = 0; s < PKS; ++s)
           d = Pol::mma_xa(Pol::fragx_c(sm.u.stg[k & 1].x, 16 * du, s * KS, lane), yf[s], d);
-        // D[u][t]: column t = tv, rows u = k kTB + 16 du + 4 g + jj
+        // D[u][t]: column t = tv, rows u = k kTB + 16 du + 4 g + jj; the R
+        // rows of one u token share its mask value
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int ut = (k * kTB + 16 * du + 4 * gq + jj) / R;
+        for (int j0 = 0; j0 < 4; j0 += R) {
+          const int ut = (k * kTB + 16 * du + 4 * gq + j0) / R;
           float mm = 0.0f;
           if (ttok < Lc && ut <= ttok)
             mm = __expf((float)(cst - sm.tb.cs[ut])) * (sm.tb.gam[ut] + (ut < ttok ? sm.tb.bpr[ut + 1] : 0.0f));
-          w[du][jj] = d[jj] * mm;
+#pragma unroll
+          for (int r = 0; r < R; ++r) w[du][j0 + r] = d[j0 + r] * mm;
         }
       }
 #pragma unroll
@@ -739,42 +854,108 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   }
 
   // ---- dC back in the raw frame; the phase gradient of every (token, pair)
-  // = the C side here + the u side from k_bwd_u
+  // = the u side (from k_bwd_u, in place) + the C side
   float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
-  const float* __restrict__ dphB = g.dphiB + ck.id * (kQ * NP);
+  float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
 #pragma unroll
   for (int i = 0; i < NTL; ++i) {
     const int n = 16 * i + l16, kp = n >> 1;
     const bool odd = n & 1;
-    float ph[4];
+    float co[4], raw[4], ph[4];
+    f2 cs[4];
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      const int vr = trow0 + j0, t = vr / R;
+      const bool ok = live && vr < rows;
+      if (ok) ldr<R>(Cc + (int64_t)t * G_ * N * R + (int64_t)n * R, co + j0);
+      else
+#pragma unroll
+        for (int r = 0; r < R; ++r) co[j0 + r] = 0.0f;
+      const f2 c2 = ok ? sm.tb.cs_of(t, kp) : f2{1.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < R; ++r) cs[j0 + r] = c2;
+    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int vr = trow0 + jj, t = vr / R, r = vr % R;
-      const bool ok = live && vr < rows;
       const float dct = acc[i][jj];
-      float co = 0.0f, cq = 0.0f;
-      f2 cs = f2{1.0f, 0.0f};
-      if (ok) {
-        const int64_t e = (int64_t)t * G_ * N * R + r;
-        co = ld1(Cc, e + (int64_t)n * R);
-        cq = ld1(Cc, e + (int64_t)(n ^ 1) * R);
-        cs = sm.tb.cs_of(t, kp);
-      }
-      ph[jj] = odd ? -dct * rot_own(cq, co, false, cs) : dct * rot_own(cq, co, true, cs);
+      const float cq = __shfl_xor(co[jj], 1, 64);
+      ph[jj] = odd ? -dct * rot_own(cq, co[jj], false, cs[jj]) : dct * rot_own(cq, co[jj], true, cs[jj]);
       const float pv = __shfl_xor(dct, 1, 64);
-      const float raw = odd ? cs.y * pv + cs.x * dct : cs.x * dct - cs.y * pv;
-      if (ok) dCo[(ti0 + (int64_t)t * a.H) * N * R + (int64_t)n * R + r] = raw;
+      raw[jj] = odd ? cs[jj].y * pv + cs[jj].x * dct : cs[jj].x * dct - cs[jj].y * pv;
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      const int vr = trow0 + j0;
+      if (live && vr < rows) str<R>(dCo + (ti0 + (int64_t)(vr / R) * a.H) * N * R + (int64_t)n * R, raw + j0);
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
     if (live && !odd)
       rows_by_token<R>(ph, trow0, [&](int t, float v) {
-        if (t < Lc) sm.dphi[t][kp] = v + dphB[t * NP + kp];
+        if (t < Lc) dph[t * NP + kp] += v;
       });
   }
+}
 
-  // ---- the end state's scalars: <Gt, Shat>, the end rotation's phase
-  // gradient <G_end, J S_end> per pair, and <dShat_c, x_{c0-1} B_{c0-1}^T>
+// --------------------------------------------------------------------------
+// The chunk's per-token gradients from the token sums of both sides: the
+// end state's scalars, suffix sums over the chunk, dt, lam, A, theta and
+// the token before the sequence.  256 threads per chunk.
+template <int P, int N>
+struct FinSmem {
+  static constexpr int NT = 256, NP = N / 2;
+  double cs[kQ];
+  float dt[kQ], lam[kQ], Av[kQ], gam[kQ], bpr[kQ];
+  float dcs[kQ], dgam[kQ], dbpr[kQ], part[NT];
+  float dphi_end[NP];
+  float red[NT / 64];
+  float dphi[kQ][NP + 1];
+};
+
+template <typename TI, int P, int N, int R>
+__global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
+  const PrefillArgs& a = g.f;
+  constexpr int NT = 256, NP = N / 2;
+  __shared__ FinSmem<P, N> sm;
+  const int h = blockIdx.y;
+  ChunkRef ck;
+  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const bool last = c + 1 >= a.nchunk;
+  const int G_ = a.G;
+  const bool shared_grp = G_ != a.H;
+  const int64_t gi = group_index(a, b, c0, h), ti0 = token_index(a, b, c0, h);
+  const TI* __restrict__ Bc = static_cast<const TI*>(a.B) + gi * N * R;
+  const TI* __restrict__ Xc = static_cast<const TI*>(a.x) + ti0 * P * R;
+  // token scalars and the chunk-local log-decay prefix (double)
+  if (tid < 64) {
+    float d = 0.0f, l = 0.0f, A = 0.0f;
+    if (tid < Lc) {
+      const int64_t bth = ti0 + (int64_t)tid * a.H;
+      d = ld1(static_cast<const TI*>(a.dt), bth);
+      l = ld1(static_cast<const TI*>(a.lam), bth);
+      A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
+    }
+    double lv = (double)d * (double)A;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(lv, off, 64);
+      if (tid >= off) lv += o;
+    }
+    sm.cs[tid] = lv;
+    sm.dt[tid] = d;
+    sm.lam[tid] = l;
+    sm.Av[tid] = A;
+    sm.gam[tid] = l * d;
+    sm.bpr[tid] = (1.0f - l) * d;
+  }
+  // the phase gradients of both sides
+  const float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
+  for (int i = tid; i < Lc * NP; i += NT) sm.dphi[i / NP][i % NP] = dph[i];
+
+  // the end state's scalars: <Gt, Shat>, the end rotation's phase gradient
+  // <G_end, J S_end> per pair, and <dShat_c, x_{c0-1} B_{c0-1}^T>
   const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
                                         : g.dS + (ck.id + 1) * (P * N);
   const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
@@ -794,6 +975,7 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
   static_assert(NT % NP == 0, "each thread keeps one pair in the end-state loop");
   {
+    const float* __restrict__ Sh = a.S + ck.id * (P * N);
     const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
     const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
                                            : a.S + (ck.id + 1) * (P * N);
@@ -806,26 +988,31 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       e_part += gt.x * sh.x + gt.y * sh.y;
       f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * kp);
       if (ck.next) {
+        float xl[R], b0[R], b1[R];
+        ldr<R>(Xlast + (int64_t)p * R, xl);
+        ldr<R>(Blast + (int64_t)(2 * kp) * R, b0);
+        ldr<R>(Blast + (int64_t)(2 * kp + 1) * R, b1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float xl = ld1(Xlast, (int64_t)p * R + r);
-          se.x -= bpL * xl * ld1(Blast, (int64_t)(2 * kp) * R + r);
-          se.y -= bpL * xl * ld1(Blast, (int64_t)(2 * kp + 1) * R + r);
+          se.x -= bpL * xl[r] * b0[r];
+          se.y -= bpL * xl[r] * b1[r];
         }
       }
       ph_part += -gv.x * se.y + gv.y * se.x;
       if (xprev) {
         const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * kp);
+        float xq[R], b0[R], b1[R];
+        ldr<R>(xprev + (int64_t)p * R, xq);
+        ldr<R>(bprev + (int64_t)(2 * kp) * R, b0);
+        ldr<R>(bprev + (int64_t)(2 * kp + 1) * R, b1);
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          h_part += ld1(xprev, (int64_t)p * R + r) *
-                    (ds.x * ld1(bprev, (int64_t)(2 * kp) * R + r) + ds.y * ld1(bprev, (int64_t)(2 * kp + 1) * R + r));
+        for (int r = 0; r < R; ++r) h_part += xq[r] * (ds.x * b0[r] + ds.y * b1[r]);
       }
     }
   }
   sm.part[tid] = ph_part;
   const float e_end = block_sum<NT>(e_part, sm.red);
-  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the part and de writes
+  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the LDS writes above
   if (tid < NP) {
     float v = 0.0f;
     for (int m = 0; m < NT / NP; ++m) v += sm.part[tid + NP * m];
@@ -834,19 +1021,20 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   __syncthreads();   // part is read
 
   // ---- the token sums: log-decay (cs), trapezoid weights (gamma, beta')
-  const float* __restrict__ tk = g.tokw + ck.id * (6 * kQ);
-  const double cs_end = sm.tb.cs[Lc - 1];
+  using GU = GeoU<P, N, R>;
+  const float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
+  const double cs_end = sm.cs[Lc - 1];
   if (tid < kQ) {
     const int u = tid;
     float dc = 0.0f, dg = 0.0f, dbn = 0.0f, pm = 0.0f;
     if (u < Lc) {
-      const float e = expf((float)(cs_end - sm.tb.cs[u]));
-      const float m = e * (sm.tb.gam[u] + (u < Lc - 1 ? sm.tb.bpr[u + 1] : 0.0f));
+      const float e = expf((float)(cs_end - sm.cs[u]));
+      const float m = e * (sm.gam[u] + (u < Lc - 1 ? sm.bpr[u + 1] : 0.0f));
       const float d = tk[kDmend * kQ + u];
       float rr = tk[kRrow0 * kQ + u];
-      if (GU::SPLIT == 2 && rows > GU::BROWS) rr += tk[kRrow1 * kQ + u];
+      if (GU::SPLIT == 2 && Lc * R > GU::BROWS) rr += tk[kRrow1 * kQ + u];
       const float ec = tk[kEcol * kQ + u];
-      dc = rr - tk[kMcol * kQ + u] + sm.ecs[u] * sm.de[u];
+      dc = rr - tk[kMcol * kQ + u] + expf((float)sm.cs[u]) * tk[kDe * kQ + u];
       dg = ec + tk[kEdiag * kQ + u] + d * e;
       dbn = ec;
       if (u < Lc - 1) {
@@ -886,7 +1074,7 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   __syncthreads();
 
   // ---- per-token outputs: theta, dt, lam, A
-  constexpr int TPT = G::TPT, KPT = NP / TPT;
+  constexpr int TPT = NT / kQ, KPT = NP / TPT;
   static_assert(KPT >= 1 && NP % TPT == 0, "pairs per thread");
   const bool angle = (a.flags & kThetaIsAngle) != 0;
   const int tt = tid / TPT, cg = tid % TPT;
@@ -894,7 +1082,7 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   if (tt < Lc) {
     const int64_t tok = ti0 + (int64_t)tt * a.H, grp = gi + (int64_t)tt * G_;
     const TI* __restrict__ th = static_cast<const TI*>(a.theta) + grp * NP;
-    const float dtt = sm.tb.dt[tt];
+    const float dtt = sm.dt[tt];
     float* __restrict__ dth = shared_grp ? g.dthh + tok * NP : g.dtheta + grp * NP;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -908,7 +1096,7 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   float da_part = 0.0f;
   if (tt < Lc && cg == 0) {
     const int64_t tok = ti0 + (int64_t)tt * a.H;
-    const float dtt = sm.tb.dt[tt], lm = sm.lam[tt], da = sm.dcs[tt];
+    const float dtt = sm.dt[tt], lm = sm.lam[tt], da = sm.dcs[tt];
     g.ddt[tok] = sm.Av[tt] * da + lm * sm.dgam[tt] + (1.0f - lm) * sm.dbpr[tt] + dt_theta;
     g.dlam[tok] = dtt * (sm.dgam[tt] - sm.dbpr[tt]);
     if (a.flags & kAPerToken) g.dA[tok] = dtt * da;
@@ -921,21 +1109,24 @@ __global__ __launch_bounds__((GeoT<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   // the token before the sequence: dx_prev = beta'_0 dShat_0 B_prev,
   // dB_prev = beta'_0 dShat_0^T x_prev
   if (c == 0 && a.has_prev && (g.dx_prev || g.dB_prev)) {
-    const float bp0 = sm.tb.bpr[0];
+    const float bp0 = sm.bpr[0];
     const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-    static_assert(P * R <= NT && N * R <= NT, "one thread per element");
-    if (g.dx_prev && tid < P * R) {
-      const int p = tid / R, r = tid % R;
-      float v = 0.0f;
-      for (int n = 0; n < N; ++n) v += dSc[(int64_t)p * N + n] * ld1(bprev, (int64_t)n * R + r);
-      g.dx_prev[((int64_t)b * a.H + h) * P * R + tid] = bp0 * v;
+    if (g.dx_prev) {
+      for (int i = tid; i < P * R; i += NT) {
+        const int p = i / R, r = i % R;
+        float v = 0.0f;
+        for (int n = 0; n < N; ++n) v += dSc[(int64_t)p * N + n] * ld1(bprev, (int64_t)n * R + r);
+        g.dx_prev[((int64_t)b * a.H + h) * P * R + i] = bp0 * v;
+      }
     }
-    if (g.dB_prev && tid < N * R) {
-      const int n = tid / R, r = tid % R;
-      float v = 0.0f;
-      for (int p = 0; p < P; ++p) v += dSc[(int64_t)p * N + n] * ld1(xprev, (int64_t)p * R + r);
-      if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N * R + tid] = bp0 * v;
-      else g.dB_prev[((int64_t)b * G_ + head_group(a, h)) * N * R + tid] = bp0 * v;
+    if (g.dB_prev) {
+      for (int i = tid; i < N * R; i += NT) {
+        const int n = i / R, r = i % R;
+        float v = 0.0f;
+        for (int p = 0; p < P; ++p) v += dSc[(int64_t)p * N + n] * ld1(xprev, (int64_t)p * R + r);
+        if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N * R + i] = bp0 * v;
+        else g.dB_prev[((int64_t)b * G_ + head_group(a, h)) * N * R + i] = bp0 * v;
+      }
     }
   }
 }
@@ -953,7 +1144,9 @@ hipError_t run_mma(const BackwardArgs& g, hipStream_t s) {
   const int nx = GU::SPLIT == 1 ? a.nchunk : GU::SPLIT * ((a.nchunk + 7) / 8) * 8;
   hipLaunchKernelGGL((k_bwd_u<Pol, TI, TY, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(GU::NT), 0, s, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_t<Pol, TI, TY, P, N, R>), grid, dim3(GeoT<P, N, R>::NT), 0, s, g);
+  hipLaunchKernelGGL((k_bwd_t<Pol, TI, TY, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(GU::NT), 0, s, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_fin<TI, P, N, R>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
