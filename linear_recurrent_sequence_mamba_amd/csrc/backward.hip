@@ -1,4 +1,7 @@
-// backward.hip -- gradients of the chunked prefill scan (rank 1 and rank R), gfx950.
+// backward.hip -- gradients of the chunked prefill scan, gfx950: the launcher,
+// the workspace, the reverse state pass and the fixed-order sums shared by
+// every shape, and plain-FMA chunk kernels for the 16 x 16 state (the other
+// shapes run the matrix-core kernels of backward_mma.hip).
 //
 // For L = <y, dy> + <h_T, dh_T> the kernels return dL/d of x, dt, A, lam,
 // theta, B, C, h0, x_prev and B_prev, for the recurrence of the Mamba-3
@@ -27,8 +30,9 @@
 // workspace), then
 //  k_bwd_chunk_adjoint (batch, head, chunk): sum_t e^{cs_t} dy_t Ct_t^T;
 //  k_bwd_state_pass    (batch, head, slice): the reverse pass over chunks;
-//  k_bwd_chunk         (batch, head, chunk): every per-token gradient.
-// Arithmetic is plain fp32 FMA on LDS tiles.
+//  k_bwd_chunk         (batch, head, chunk): every per-token gradient;
+//  k_bwd_reduce_*: dA over chunks, head groups' sums.
+// The chunk kernels here are plain fp32 FMA on LDS tiles (single input).
 #include "chunk_common.h"
 
 namespace m3 {
@@ -581,509 +585,6 @@ __global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk(BackwardArgs g
   }
 }
 
-// --------------------------------------------------------------------------
-// The same gradients with rank R > 1.  Every token is R virtual rows (t, r);
-// the products pair rank r of the output side (C, dy) with rank r' of the
-// input side (B, x), so the kernel stages one rank column of each side at a
-// time into the single-rank LDS rows and loops over the R x R pairs:
-//   dx_{u,r'} = sum_r W1^{(r,r')T} dY^{(r)},  dBt_{u,r'} = sum_r W2^{(r,r')T} Ct^{(r)},
-//   dCt_{t,r} = sum_{r'} W2^{(r,r')} Bt^{(r')},  dM = sum_{r,r'} (Ct^{(r)} Bt^{(r')T}) o (dY^{(r)} X^{(r')T}).
-// The per-rank x, B and C gradients collect in their output arrays (in the
-// rotated frame until the end); each thread owns the same elements in every
-// pass, so the sums are read and written by one thread in a fixed order.
-template <typename TI, typename TY, int P, int N, int R>
-__global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk_mimo(BackwardArgs g) {
-  const PrefillArgs& a = g.f;
-  using GEO = BwdGeo<P, N>;
-  constexpr int NP = N / 2;
-  constexpr int kNT3 = GEO::NT, TPR = GEO::TPR, GU = GEO::GU;
-  constexpr int WP = GEO::WP, WN = GEO::WN;
-  constexpr int GC = 64 / GU;
-  __shared__ BwdSmem<P, N> sm;
-  const int h = blockIdx.y;
-  ChunkRef ck;
-  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
-  const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const bool last = c + 1 >= a.nchunk;
-  const int row = tid / TPR, cg = tid % TPR;
-  const int p0 = cg * WP, n0 = cg * WN;
-  const int G = a.G;
-  const bool shared_grp = G != a.H;
-  const bool own = row < Lc;   // this thread's token row exists
-
-  ThetaBlock<TI, N, kNT3> thb;
-  thb.load(a, b, h, c0, Lc);
-  chunk_tables<TI, N, kNT3>(a, thb, Lc, sm.tb, sm.ub.scr, 0);
-  if (tid < kQ) {
-    sm.lam[tid] = thb.l;
-    sm.Av[tid] = thb.A;
-    sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
-    sm.dcs[tid] = sm.dgam[tid] = sm.dbpr[tid] = sm.dmend[tid] = 0.0f;
-  }
-  if (tid < NP) sm.dphi_end[tid] = 0.0f;
-  __syncthreads();
-
-  const int64_t gi = group_index(a, b, c0, h);
-  const int64_t ti0 = token_index(a, b, c0, h);
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.B) + gi * N * R;
-  const TI* __restrict__ Cg = static_cast<const TI*>(a.C) + gi * N * R;
-  const TI* __restrict__ Xg = static_cast<const TI*>(a.x) + ti0 * P * R;
-  const int64_t tok = ti0 + (int64_t)row * a.H;   // this thread's token (b, c0 + row, h)
-  // per-head accumulators: the outputs themselves, or the per-head workspace with groups
-  float* __restrict__ dXo = g.dx + tok * P * R;
-  float* __restrict__ dBo = (shared_grp ? g.dBh : g.dB) + tok * N * R;
-  float* __restrict__ dCo = (shared_grp ? g.dCh : g.dC) + tok * N * R;
-
-  // rank r of the rotated B (into Bt) or C (into Ct) rows, of x (Xs) or dy (Ys)
-  auto stage_in = [&](int r, bool rows = true) {   // B and x: the input side
-    for (int i = tid; i < kQ * NP; i += kNT3) {
-      const int t = i / NP, k = i % NP;
-      f2 v = f2{0.0f, 0.0f};
-      if (t < Lc) {
-        const int64_t e = (int64_t)t * G * N * R + (2 * k) * R + r;
-        v = rot_neg(f2{ld1(Bg, e), ld1(Bg, e + R)}, sm.tb.cs_of(t, k));
-      }
-      sm.ub.Bt[t][2 * k] = v.x;
-      sm.ub.Bt[t][2 * k + 1] = v.y;
-    }
-    if (!rows) return;
-    for (int i = tid; i < kQ * P; i += kNT3) {
-      const int t = i / P, pp = i % P;
-      sm.Xs[t][pp] = t < Lc ? ld1(Xg, (int64_t)t * a.H * P * R + pp * R + r) : 0.0f;
-    }
-  };
-  auto stage_out = [&](int r, bool rows = true) {  // C and dy: the output side
-    for (int i = tid; i < kQ * NP; i += kNT3) {
-      const int t = i / NP, k = i % NP;
-      f2 v = f2{0.0f, 0.0f};
-      if (t < Lc) {
-        const int64_t e = (int64_t)t * G * N * R + (2 * k) * R + r;
-        v = rot_neg(f2{ld1(Cg, e), ld1(Cg, e + R)}, sm.tb.cs_of(t, k));
-      }
-      sm.Ct[t][2 * k] = v.x;
-      sm.Ct[t][2 * k + 1] = v.y;
-    }
-    if (!rows) return;
-    for (int i = tid; i < kQ * P; i += kNT3) {
-      const int t = i / P, pp = i % P;
-      sm.Ys[t][pp] = t < Lc ? ldy<TY>(g.dy, (ti0 + (int64_t)t * a.H) * P * R + pp * R + r) : 0.0f;
-    }
-  };
-
-  const double cs_end = sm.tb.cs[Lc - 1];
-  auto wgt = [&](int t, int u) { return sm.tb.gam[u] + (u < t ? sm.tb.bpr[u + 1] : 0.0f); };
-  const int tb0 = 2 * (tid / GC), ub0 = GU * (tid % GC);
-  float em[2][GU], mm[2][GU], dmacc[2][GU];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < GU; ++j) {
-      const int t = tb0 + i, u = ub0 + j;
-      const bool in = u <= t && t < Lc;
-      em[i][j] = in ? expf((float)(sm.tb.cs[t] - sm.tb.cs[u])) : 0.0f;
-      mm[i][j] = in ? em[i][j] * wgt(t, u) : 0.0f;
-      dmacc[i][j] = 0.0f;
-    }
-
-  // ---- the R x R rank pairs
-  #pragma unroll 1
-  for (int rp = 0; rp < R; ++rp) {
-    __syncthreads();   // the previous pass's reads of Bt and Xs are done
-    stage_in(rp);
-    float dxv[WP], dbv[WN];
-#pragma unroll
-    for (int j = 0; j < WP; ++j) dxv[j] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < WN; ++j) dbv[j] = 0.0f;
-    #pragma unroll 1
-    for (int r = 0; r < R; ++r) {
-      __syncthreads();   // Ct, Ys and W are free
-      stage_out(r);
-      __syncthreads();
-      float k1[2][GU], k2[2][GU];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < GU; ++j) k1[i][j] = k2[i][j] = 0.0f;
-#pragma unroll 2
-      for (int n = 0; n < N; n += 4) {
-        f4 cr[2], br[GU];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) cr[i] = *reinterpret_cast<const f4*>(&sm.Ct[tb0 + i][n]);
-#pragma unroll
-        for (int j = 0; j < GU; ++j) br[j] = *reinterpret_cast<const f4*>(&sm.ub.Bt[ub0 + j][n]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < GU; ++j)
-            k1[i][j] += cr[i].x * br[j].x + cr[i].y * br[j].y + cr[i].z * br[j].z + cr[i].w * br[j].w;
-      }
-#pragma unroll 2
-      for (int pp = 0; pp < P; pp += 2) {
-        f2 yr[2], xr[GU];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) yr[i] = *reinterpret_cast<const f2*>(&sm.Ys[tb0 + i][pp]);
-#pragma unroll
-        for (int j = 0; j < GU; ++j) xr[j] = *reinterpret_cast<const f2*>(&sm.Xs[ub0 + j][pp]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < GU; ++j) k2[i][j] += yr[i].x * xr[j].x + yr[i].y * xr[j].y;
-      }
-      float w2v[2][GU];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < GU; ++j) {
-          dmacc[i][j] += k1[i][j] * k2[i][j];
-          sm.uz.W[tb0 + i][ub0 + j] = mm[i][j] * k1[i][j];
-          w2v[i][j] = mm[i][j] * k2[i][j];
-        }
-      __syncthreads();
-      for (int t = row; t < Lc; ++t) {   // dx_{.,rp} += W1^T dY^{(r)}
-        const float w = sm.uz.W[t][row];
-#pragma unroll
-        for (int j = 0; j < WP; ++j) dxv[j] += w * sm.Ys[t][p0 + j];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < GU; ++j) sm.uz.W[tb0 + i][ub0 + j] = w2v[i][j];
-      __syncthreads();
-      float dcv[WN];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) dcv[j] = 0.0f;
-      for (int u = 0; u <= row && u < Lc; ++u) {   // dCt_{.,r} += W2 Bt^{(rp)}
-        const float w = sm.uz.W[row][u];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) dcv[j] += w * sm.ub.Bt[u][n0 + j];
-      }
-      for (int t = row; t < Lc; ++t) {   // dBt_{.,rp} += W2^T Ct^{(r)}
-        const float w = sm.uz.W[t][row];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) dbv[j] += w * sm.Ct[t][n0 + j];
-      }
-      if (own) {
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          float* q = dCo + (int64_t)(n0 + j) * R + r;
-          *q = rp == 0 ? dcv[j] : *q + dcv[j];
-        }
-      }
-    }
-    if (own) {
-#pragma unroll
-      for (int j = 0; j < WP; ++j) dXo[(int64_t)(p0 + j) * R + rp] = dxv[j];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) dBo[(int64_t)(n0 + j) * R + rp] = dbv[j];
-    }
-  }
-  __syncthreads();
-
-  // ---- the mask gradient summed over the rank pairs: row and column sums
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < GU; ++j) sm.uz.W[tb0 + i][ub0 + j] = dmacc[i][j] * mm[i][j];
-  __syncthreads();
-  if (tid < kQ) {
-    float rs = 0.0f, cl = 0.0f;
-    for (int u = 0; u < kQ; ++u) rs += sm.uz.W[tid][u];
-    for (int t = 0; t < kQ; ++t) cl += sm.uz.W[t][tid];
-    sm.dcs[tid] = rs - cl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < GU; ++j) sm.uz.W[tb0 + i][ub0 + j] = dmacc[i][j] * em[i][j];
-  __syncthreads();
-  if (tid < kQ) {
-    const int u = tid;
-    float off = 0.0f;
-    for (int t = u + 1; t < kQ; ++t) off += sm.uz.W[t][u];
-    sm.dgam[u] = off + sm.uz.W[u][u];
-    if (u + 1 < kQ) sm.dbpr[u + 1] = off;
-  }
-  __syncthreads();
-
-  // ---- the entry state: dCt_{.,r} += e^{cs_t} dY^{(r)} Shat, and d(e^{cs_t})
-  const float* __restrict__ Sh = a.S + ck.id * (P * N);
-  for (int i = tid; i < P * N / 4; i += kNT3)
-    *reinterpret_cast<f4*>(&sm.uz.Z[i / (N / 4)][4 * (i % (N / 4))]) = reinterpret_cast<const f4*>(Sh)[i];
-  float de = 0.0f;
-  #pragma unroll 1
-  for (int r = 0; r < R; ++r) {
-    __syncthreads();   // Z loaded; the previous rank's rows are read
-    stage_out(r);
-    __syncthreads();
-    float q[WN];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) q[j] = 0.0f;
-    #pragma unroll 4
-    for (int pp = 0; pp < P; ++pp) {
-      const float yv = sm.Ys[row][pp];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) q[j] += yv * sm.uz.Z[pp][n0 + j];
-    }
-#pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      de += sm.Ct[row][n0 + j] * q[j];
-      if (own) dCo[(int64_t)(n0 + j) * R + r] += sm.ecs[row] * q[j];
-    }
-  }
-  de = group_sum<TPR>(de);
-  if (cg == 0 && own) sm.dcs[row] += sm.ecs[row] * de;
-  __syncthreads();
-
-  // ---- the end state (as in the single-rank kernel, with rank sums)
-  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
-                                        : g.dS + (ck.id + 1) * (P * N);
-  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
-                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
-                            : 0.0f;
-  const TI* __restrict__ Blast = Bg + (int64_t)(Lc - 1) * G * N * R;
-  const TI* __restrict__ Xlast = Xg + (int64_t)(Lc - 1) * a.H * P * R;
-  const TI* xprev = nullptr;
-  const TI* bprev = nullptr;
-  if (c > 0) {
-    xprev = Xg - (int64_t)a.H * P * R;
-    bprev = Bg - (int64_t)G * N * R;
-  } else if (a.has_prev) {
-    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
-    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G + head_group(a, h)) * N * R;
-  }
-  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
-  static_assert(kNT3 % NP == 0, "each thread keeps one pair in the end-state loop");
-  {
-    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
-    const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
-                                           : a.S + (ck.id + 1) * (P * N);
-    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-    for (int i = tid; i < P * NP; i += kNT3) {
-      const int pp = i / NP, k = i % NP;
-      const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)pp * N + 2 * k) : f2{0.0f, 0.0f};
-      const f2 gt = rot_neg(gv, re[k]);
-      sm.uz.Z[pp][2 * k] = gt.x;
-      sm.uz.Z[pp][2 * k + 1] = gt.y;
-      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)pp * N + 2 * k);
-      e_part += gt.x * sh.x + gt.y * sh.y;
-      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)pp * N + 2 * k);
-      if (ck.next) {
-        #pragma unroll 1
-        for (int r = 0; r < R; ++r) {
-          const float xl = ld1(Xlast, (int64_t)pp * R + r);
-          se.x -= bpL * xl * ld1(Blast, (int64_t)(2 * k) * R + r);
-          se.y -= bpL * xl * ld1(Blast, (int64_t)(2 * k + 1) * R + r);
-        }
-      }
-      ph_part += -gv.x * se.y + gv.y * se.x;
-      if (xprev) {
-        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)pp * N + 2 * k);
-        #pragma unroll 1
-        for (int r = 0; r < R; ++r)
-          h_part += ld1(xprev, (int64_t)pp * R + r) *
-                    (ds.x * ld1(bprev, (int64_t)(2 * k) * R + r) + ds.y * ld1(bprev, (int64_t)(2 * k + 1) * R + r));
-      }
-    }
-  }
-  sm.part[tid] = ph_part;
-  const float e_end = block_sum<kNT3>(e_part, sm.red);
-  const float h_end = block_sum<kNT3>(h_part, sm.red);   // also orders the Z and part writes
-  if (tid < NP) {
-    float v = 0.0f;
-    for (int m = 0; m < kNT3 / NP; ++m) v += sm.part[tid + NP * m];
-    sm.dphi_end[tid] = v;
-  }
-  // dx_{.,r'} += m_end Bt^{(r')} Gt^T (+ the crossing term of the last token),
-  // dm_end, dBt_{.,r'} += m_end X^{(r')} Gt (the crossing term's B part is
-  // added in the raw frame at the end)
-  float dme = 0.0f;
-  float cu = 0.0f, mu = 0.0f;
-  if (own) {
-    const float e = expf((float)(cs_end - sm.tb.cs[row]));
-    mu = e * wgt(Lc - 1, row);
-    cu = mu + (row == Lc - 1 ? bpL : 0.0f);
-  }
-  #pragma unroll 1
-  for (int rp = 0; rp < R; ++rp) {
-    __syncthreads();   // Z written; the previous rank's rows are read
-    stage_in(rp);
-    __syncthreads();
-    if (own) {
-      float v[WP];
-#pragma unroll
-      for (int j = 0; j < WP; ++j) v[j] = 0.0f;
-#pragma unroll 2
-      for (int n = 0; n < N; n += 4) {
-        const f4 bt = *reinterpret_cast<const f4*>(&sm.ub.Bt[row][n]);
-#pragma unroll
-        for (int j = 0; j < WP; ++j) {
-          const f4 z = *reinterpret_cast<const f4*>(&sm.uz.Z[p0 + j][n]);
-          v[j] += bt.x * z.x + bt.y * z.y + bt.z * z.z + bt.w * z.w;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < WP; ++j) {
-        dXo[(int64_t)(p0 + j) * R + rp] += cu * v[j];
-        dme += sm.Xs[row][p0 + j] * v[j];
-      }
-      float w[WN];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) w[j] = 0.0f;
-      #pragma unroll 4
-      for (int pp = 0; pp < P; ++pp) {
-        const float xv = sm.Xs[row][pp];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) w[j] += xv * sm.uz.Z[pp][n0 + j];
-      }
-#pragma unroll
-      for (int j = 0; j < WN; ++j) dBo[(int64_t)(n0 + j) * R + rp] += mu * w[j];
-    }
-  }
-  dme = group_sum<TPR>(dme);
-  if (cg == 0 && own) sm.dmend[row] = dme;
-  __syncthreads();
-  if (tid < Lc) {   // the end-state weights m_end[u] = e^{cs_end - cs_u} w_{end,u}
-    const int u = tid;
-    const float e = expf((float)(cs_end - sm.tb.cs[u]));
-    const float m = e * wgt(Lc - 1, u);
-    const float d = sm.dmend[u];
-    sm.part[u] = 0.0f;
-    if (u < Lc - 1) {
-      sm.part[u] = d * m;
-      sm.dcs[u] -= d * m;
-      sm.dbpr[u + 1] += d * e;
-    }
-    sm.dgam[u] += d * e;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float v = expf((float)cs_end) * e_end;
-    for (int u = 0; u < Lc - 1; ++u) v += sm.part[u];
-    sm.dcs[Lc - 1] += v;
-    sm.dbpr[0] += h_end;
-  }
-
-  // ---- phase gradients: cross products of every rank's rotated rows and gradients
-  float dph[WN / 2];
-#pragma unroll
-  for (int j = 0; j < WN / 2; ++j) dph[j] = 0.0f;
-  #pragma unroll 1
-  for (int r = 0; r < R; ++r) {
-    __syncthreads();
-    stage_in(r, false);
-    stage_out(r, false);
-    __syncthreads();
-    if (own) {
-#pragma unroll
-      for (int j = 0; j < WN; j += 2) {
-        const int n = n0 + j;
-        const float b0 = dBo[(int64_t)n * R + r], b1 = dBo[(int64_t)(n + 1) * R + r];
-        const float q0 = dCo[(int64_t)n * R + r], q1 = dCo[(int64_t)(n + 1) * R + r];
-        dph[j / 2] += b0 * sm.ub.Bt[row][n + 1] - b1 * sm.ub.Bt[row][n] + q0 * sm.Ct[row][n + 1] -
-                      q1 * sm.Ct[row][n];
-      }
-    }
-  }
-  __syncthreads();   // Z is free
-#pragma unroll
-  for (int j = 0; j < WN; j += 2) sm.uz.dphi[row][(n0 + j) / 2] = dph[j / 2];
-  __syncthreads();
-  if (tid < NP) {
-    const int k = tid;
-    float run = sm.dphi_end[k];
-    for (int t = Lc - 1; t >= 0; --t) {
-      run += sm.uz.dphi[t][k];
-      sm.uz.dphi[t][k] = run;
-    }
-  } else if (tid == NP) {
-    float run = 0.0f;
-    for (int t = Lc - 1; t >= 0; --t) {
-      run += sm.dcs[t];
-      sm.dcs[t] = run;
-    }
-  }
-  __syncthreads();
-
-  // ---- outputs: B and C gradients back to the raw frame (with the crossing
-  // term of the last token), theta, dt, lam, A
-  const bool angle = (a.flags & kThetaIsAngle) != 0;
-  float dt_theta = 0.0f;
-  if (own) {
-    const int t = row;
-    const int64_t grp = gi + (int64_t)t * G;
-    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + grp * NP;
-    const float dtt = sm.tb.dt[t];
-    const bool cross = ck.next && t == Lc - 1;
-#pragma unroll
-    for (int j = 0; j < WN; j += 2) {
-      const int k = (n0 + j) / 2;
-      const float dphv = sm.uz.dphi[t][k];
-      if (!angle) dt_theta += ld1(th, k) * dphv;
-      (shared_grp ? g.dthh : g.dtheta)[(shared_grp ? tok : grp) * NP + k] = angle ? dphv : dtt * dphv;
-      const f2 cs = sm.tb.cs_of(t, k);
-      #pragma unroll 1
-      for (int r = 0; r < R; ++r) {
-        float* bq = dBo + (int64_t)(n0 + j) * R + r;
-        float* cq = dCo + (int64_t)(n0 + j) * R + r;
-        f2 db = rot_pos(f2{bq[0], bq[R]}, cs);
-        const f2 dc = rot_pos(f2{cq[0], cq[R]}, cs);
-        if (cross) {   // (1 - lam) dt of the next token times x B^T of this one, raw B
-          float h0v = 0.0f, h1v = 0.0f;
-#pragma unroll 4
-          for (int pp = 0; pp < P; ++pp) {
-            const float xv = ld1(Xlast, (int64_t)pp * R + r);
-            h0v += Gend[(int64_t)pp * N + n0 + j] * xv;
-            h1v += Gend[(int64_t)pp * N + n0 + j + 1] * xv;
-          }
-          db.x += bpL * h0v;
-          db.y += bpL * h1v;
-        }
-        bq[0] = db.x;
-        bq[R] = db.y;
-        cq[0] = dc.x;
-        cq[R] = dc.y;
-      }
-    }
-  }
-  dt_theta = group_sum<TPR>(dt_theta);
-  float da_part = 0.0f;
-  if (own && cg == 0) {
-    const int t = row;
-    const float dtt = sm.tb.dt[t], lm = sm.lam[t], da = sm.dcs[t];
-    g.ddt[tok] = sm.Av[t] * da + lm * sm.dgam[t] + (1.0f - lm) * sm.dbpr[t] + dt_theta;
-    g.dlam[tok] = dtt * (sm.dgam[t] - sm.dbpr[t]);
-    if (a.flags & kAPerToken) g.dA[tok] = dtt * da;
-    else da_part = dtt * da;
-  }
-  if (!(a.flags & kAPerToken)) {
-    const float sA = block_sum<kNT3>(da_part, sm.red);
-    if (tid == 0) g.dApart[ck.id] = sA;
-  }
-  if (c == 0 && a.has_prev && (g.dx_prev || g.dB_prev)) {
-    const float bp0 = sm.tb.bpr[0];
-    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-    if (g.dx_prev && tid < P * R) {
-      const int pp = tid / R, r = tid % R;
-      float v = 0.0f;
-#pragma unroll 4
-      for (int n = 0; n < N; ++n) v += dSc[(int64_t)pp * N + n] * ld1(bprev, (int64_t)n * R + r);
-      g.dx_prev[((int64_t)b * a.H + h) * P * R + tid] = bp0 * v;
-    }
-    if (g.dB_prev && tid < N * R) {
-      const int n = tid / R, r = tid % R;
-      float v = 0.0f;
-#pragma unroll 4
-      for (int pp = 0; pp < P; ++pp) v += dSc[(int64_t)pp * N + n] * ld1(xprev, (int64_t)pp * R + r);
-      if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N * R + tid] = bp0 * v;
-      else g.dB_prev[((int64_t)b * G + head_group(a, h)) * N * R + tid] = bp0 * v;
-    }
-  }
-}
-
 // the sums a chunk kernel cannot finish alone, in a fixed order: dA over
 // (batch, chunk) per head, and with head groups the heads of each group
 __global__ void k_bwd_reduce_dA(BackwardArgs g) {
@@ -1117,12 +618,8 @@ hipError_t run_backward(const BackwardArgs& g, int in_bf16, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_bwd_state_pass(g, s)) != hipSuccess) return e;
-  if constexpr (R == 1) {
-    hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
-  } else {
-    static_assert(P * R <= BwdGeo<P, N>::NT && N * R <= BwdGeo<P, N>::NT, "x_prev, B_prev: one thread each");
-    hipLaunchKernelGGL((k_bwd_chunk_mimo<TI, TY, P, N, R>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
-  }
+  static_assert(R == 1, "single input");
+  hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1135,13 +632,6 @@ int dispatch_bwd(const BackwardArgs& g, int in_bf16, hipStream_t s, hipError_t* 
     return 0;                                                       \
   }
   M3_BWD_SHAPE(16, 16, 1)
-  M3_BWD_SHAPE(64, 128, 1)
-  M3_BWD_SHAPE(32, 64, 1)
-  M3_BWD_SHAPE(64, 64, 1)
-  M3_BWD_SHAPE(64, 128, 2)
-  M3_BWD_SHAPE(64, 128, 4)
-  M3_BWD_SHAPE(32, 64, 4)
-  M3_BWD_SHAPE(64, 64, 4)
 #undef M3_BWD_SHAPE
   return -1;
 }
@@ -1209,7 +699,7 @@ static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int R, int G, int Q
     sz[6] = tokens * H * (N / 2) * 4;
     sz[7] = (size_t)Bsz * H * N * R * 4;
   }
-  if (R > 1) {   // the rank-R kernels' token sums and u-side phase gradients
+  if (!(P == 16 && N == 16)) {   // the matrix-core kernels' token sums and phase gradients
     sz[8] = units * 7 * Q * 4;
     sz[9] = units * Q * (N / 2) * 4;
   }
@@ -1239,8 +729,9 @@ void backward_carve(BackwardArgs& g, void* ws) {
   g.dCh = grp ? reinterpret_cast<float*>(p + off[5]) : nullptr;
   g.dthh = grp ? reinterpret_cast<float*>(p + off[6]) : nullptr;
   g.dBph = grp ? reinterpret_cast<float*>(p + off[7]) : nullptr;
-  g.tokw = a.R > 1 ? reinterpret_cast<float*>(p + off[8]) : nullptr;
-  g.dphiB = a.R > 1 ? reinterpret_cast<float*>(p + off[9]) : nullptr;
+  const bool mma = !(a.P == 16 && a.N == 16);
+  g.tokw = mma ? reinterpret_cast<float*>(p + off[8]) : nullptr;
+  g.dphiB = mma ? reinterpret_cast<float*>(p + off[9]) : nullptr;
 }
 
 int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
@@ -1254,12 +745,15 @@ int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_
   fw.y = nullptr;
   if (launch_prefill(fw, in_bf16, 0, s, e) != 0) return -1;
   if (*e != hipSuccess) return 0;
-  int rc;
-  if (a.R > 1) rc = launch_backward_mma(g, in_bf16, dy_bf16, s, e);
-  else if (in_bf16)
-    rc = dy_bf16 ? dispatch_bwd<bf16_t, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<bf16_t, float>(g, in_bf16, s, e);
-  else
-    rc = dy_bf16 ? dispatch_bwd<float, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<float, float>(g, in_bf16, s, e);
+  // the matrix-core kernels (backward_mma.hip) serve every shape but the
+  // 16 x 16 state, which has too few output tiles for them
+  int rc = launch_backward_mma(g, in_bf16, dy_bf16, s, e);
+  if (rc != 0) {
+    if (in_bf16)
+      rc = dy_bf16 ? dispatch_bwd<bf16_t, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<bf16_t, float>(g, in_bf16, s, e);
+    else
+      rc = dy_bf16 ? dispatch_bwd<float, bf16_t>(g, in_bf16, s, e) : dispatch_bwd<float, float>(g, in_bf16, s, e);
+  }
   if (rc != 0 || *e != hipSuccess) return rc;
   *e = bwd_reduce(g, s);
   return 0;

@@ -900,10 +900,12 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
 // --------------------------------------------------------------------------
 // The chunk's per-token gradients from the token sums of both sides: the
 // end state's scalars, suffix sums over the chunk, dt, lam, A, theta and
-// the token before the sequence.  256 threads per chunk.
+// the token before the sequence.  1024 threads per chunk: every load of the
+// end-state sums is issued before any is used.
+constexpr int kFinNT = 1024;
 template <int P, int N>
 struct FinSmem {
-  static constexpr int NT = 256, NP = N / 2;
+  static constexpr int NT = kFinNT, NP = N / 2;
   double cs[kQ];
   float dt[kQ], lam[kQ], Av[kQ], gam[kQ], bpr[kQ];
   float dcs[kQ], dgam[kQ], dbpr[kQ], part[NT];
@@ -913,9 +915,9 @@ struct FinSmem {
 };
 
 template <typename TI, int P, int N, int R>
-__global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
+__global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   const PrefillArgs& a = g.f;
-  constexpr int NT = 256, NP = N / 2;
+  constexpr int NT = kFinNT, NP = N / 2;
   __shared__ FinSmem<P, N> sm;
   const int h = blockIdx.y;
   ChunkRef ck;
@@ -973,14 +975,16 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
     bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
   }
   float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
-  static_assert(NT % NP == 0, "each thread keeps one pair in the end-state loop");
+  static_assert(NT % NP == 0 && P * NP % NT == 0, "each thread keeps one pair in the end-state loop");
   {
     const float* __restrict__ Sh = a.S + ck.id * (P * N);
     const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
     const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
                                            : a.S + (ck.id + 1) * (P * N);
     const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-    for (int i = tid; i < P * NP; i += NT) {
+#pragma unroll
+    for (int it = 0; it < P * NP / NT; ++it) {
+      const int i = tid + NT * it;
       const int p = i / NP, kp = i % NP;
       const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
       const f2 gt = rot_neg(gv, re[kp]);
@@ -1056,19 +1060,25 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
     sm.dcs[Lc - 1] += v;
   }
   __syncthreads();
-  // suffix sums over the chunk: phase (from the end rotation) and log-decay
-  if (tid < NP) {
-    const int k = tid;
-    float run = sm.dphi_end[k];
-    for (int t = Lc - 1; t >= 0; --t) {
-      run += sm.dphi[t][k];
-      sm.dphi[t][k] = run;
+  // suffix sums over the chunk's tokens (one lane per token, a wave per
+  // column): phase (from the end rotation) and log-decay
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    auto suffix = [&](float v) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_down(v, off, 64);
+        if (lane + off < 64) v += o;
+      }
+      return v;
+    };
+    for (int k = wave; k < NP; k += NT / 64) {
+      const float v = suffix(lane < Lc ? sm.dphi[lane][k] : 0.0f);
+      if (lane < Lc) sm.dphi[lane][k] = v + sm.dphi_end[k];
     }
-  } else if (tid == NP) {
-    float run = 0.0f;
-    for (int t = Lc - 1; t >= 0; --t) {
-      run += sm.dcs[t];
-      sm.dcs[t] = run;
+    if (wave == (NP % (NT / 64))) {
+      const float v = suffix(lane < Lc ? sm.dcs[lane] : 0.0f);
+      if (lane < Lc) sm.dcs[lane] = v;
     }
   }
   __syncthreads();
@@ -1115,6 +1125,7 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
       for (int i = tid; i < P * R; i += NT) {
         const int p = i / R, r = i % R;
         float v = 0.0f;
+#pragma unroll 8
         for (int n = 0; n < N; ++n) v += dSc[(int64_t)p * N + n] * ld1(bprev, (int64_t)n * R + r);
         g.dx_prev[((int64_t)b * a.H + h) * P * R + i] = bp0 * v;
       }
@@ -1123,6 +1134,7 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BackwardArgs g) {
       for (int i = tid; i < N * R; i += NT) {
         const int n = i / R, r = i % R;
         float v = 0.0f;
+#pragma unroll 8
         for (int p = 0; p < P; ++p) v += dSc[(int64_t)p * N + n] * ld1(xprev, (int64_t)p * R + r);
         if (shared_grp) g.dBph[((int64_t)b * a.H + h) * N * R + i] = bp0 * v;
         else g.dB_prev[((int64_t)b * G_ + head_group(a, h)) * N * R + i] = bp0 * v;
@@ -1146,7 +1158,7 @@ hipError_t run_mma(const BackwardArgs& g, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_t<Pol, TI, TY, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(GU::NT), 0, s, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_fin<TI, P, N, R>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_bwd_fin<TI, P, N, R>), grid, dim3(kFinNT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1158,6 +1170,9 @@ int dispatch_mma(const BackwardArgs& g, hipStream_t s, hipError_t* e) {
     *e = run_mma<Pol, TI, TY, PP, NN, RR>(g, s);                    \
     return 0;                                                       \
   }
+  M3_MMA_SHAPE(64, 128, 1)
+  M3_MMA_SHAPE(32, 64, 1)
+  M3_MMA_SHAPE(64, 64, 1)
   M3_MMA_SHAPE(64, 128, 2)
   M3_MMA_SHAPE(64, 128, 4)
   M3_MMA_SHAPE(32, 64, 4)
