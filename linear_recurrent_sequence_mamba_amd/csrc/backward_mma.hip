@@ -389,8 +389,25 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
   const TI* __restrict__ Bc = Bg + gi * N * R;   // this chunk's first token
   const TI* __restrict__ Xc = Xg + ti0 * P * R;
 
+  // every prologue load goes out first: phase inputs and token scalars,
+  // this block's own B and x rows, the first t block of C and dy
+  constexpr int NPC = G::BROWS / 64;   // own-row pieces of 64 rows
+  const int kb0 = v0 / kTB, nkb = (rows + kTB - 1) / kTB;
   ThetaBlock<TI, N, NT> thb;
   thb.load(a, b, h, c0, Lc);
+  RowBlock<TI, N * R, R, NT, false, 64> rb[NPC];
+  RowBlock<TI, P * R, R, NT, false, 64> rx[NPC];
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc) {
+    if (v0 + 64 * pc < rows) {
+      rb[pc].template load<true>(Bg, a, b, h, c0, Lc, v0 + 64 * pc);
+      rx[pc].template load<false>(Xg, a, b, h, c0, Lc, v0 + 64 * pc);
+    }
+  }
+  RowBlock<TI, N * R, R, NT, false, kTB> cb;
+  RowBlock<TY, P * R, R, NT, false, kTB> yb;
+  cb.template load<true>(Cg, a, b, h, c0, Lc, kb0 * kTB);
+  yb.template load<false>(Yg, a, b, h, c0, Lc, kb0 * kTB);
   for (int i = tid; i < NW * kQ; i += NT) (&sm.rowpart[0][0])[i] = 0.0f;
   chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
 
@@ -402,18 +419,14 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 #pragma unroll
   for (int s = 0; s < PKS; ++s) xf[s] = typename Pol::XFrag{};
 #pragma unroll
-  for (int piece = 0; piece < G::BROWS / 64; ++piece) {
-    const int pv0 = v0 + 64 * piece;
+  for (int pc = 0; pc < NPC; ++pc) {
+    const int pv0 = v0 + 64 * pc;
     if (pv0 >= rows) break;
-    RowBlock<TI, N * R, R, NT, false, 64> rb;
-    RowBlock<TI, P * R, R, NT, false, 64> rx;
-    rb.template load<true>(Bg, a, b, h, c0, Lc, pv0);
-    rx.template load<false>(Xg, a, b, h, c0, Lc, pv0);
-    __syncthreads();   // the table scratch (or the previous piece) is free
-    store_rows<Pol, TI, N, R, NT, 64>(rb, sm.u.own.b, sm.tb, pv0 / R, Lc, NoPrep{});
-    put_xrows<Pol, TI, P, R, NT, 64>(rx, sm.u.own.x);
+    if (pc > 0) __syncthreads();   // the previous piece is read
+    store_rows<Pol, TI, N, R, NT, 64>(rb[pc], sm.u.own.b, sm.tb, pv0 / R, Lc, NoPrep{});
+    put_xrows<Pol, TI, P, R, NT, 64>(rx[pc], sm.u.own.x);
     __syncthreads();
-    if (lt / 4 == piece) {
+    if (lt / 4 == pc) {
 #pragma unroll
       for (int s = 0; s < NKS; ++s) bf[s] = Pol::frag(sm.u.own.b, 16 * (lt % 4), s * KS, lane);
 #pragma unroll
@@ -428,11 +441,6 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 #pragma unroll
   for (int i = 0; i < NTL; ++i) accb[i] = f4{0, 0, 0, 0};
   float mcol = 0.0f, ecol = 0.0f, edg = 0.0f;
-  const int kb0 = v0 / kTB, nkb = (rows + kTB - 1) / kTB;
-  RowBlock<TI, N * R, R, NT, false, kTB> cb;
-  RowBlock<TY, P * R, R, NT, false, kTB> yb;
-  cb.template load<true>(Cg, a, b, h, c0, Lc, kb0 * kTB);
-  yb.template load<false>(Yg, a, b, h, c0, Lc, kb0 * kTB);
   const float gu = utok < kQ ? sm.tb.gam[utok] : 0.0f;
   const float bu = utok + 1 < kQ ? sm.tb.bpr[utok + 1] : 0.0f;
   const double csu = sm.tb.cs[min(utok, kQ - 1)];
@@ -721,8 +729,22 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   const TY* __restrict__ Yg = static_cast<const TY*>(g.dy);
   const TI* __restrict__ Cc = static_cast<const TI*>(a.C) + gi * N * R;
 
+  // every prologue load goes out first: phase inputs and token scalars,
+  // this block's own dy rows, the entry state, the first u block of B and x
+  constexpr int NPC = G::BROWS / 64;   // own-row pieces of 64 rows
   ThetaBlock<TI, N, NT> thb;
   thb.load(a, b, h, c0, Lc);
+  RowBlock<TY, P * R, R, NT, false, 64> ybp[NPC];
+#pragma unroll
+  for (int pc = 0; pc < NPC; ++pc)
+    if (v0 + 64 * pc < rows) ybp[pc].template load<false>(Yg, a, b, h, c0, Lc, v0 + 64 * pc);
+  StateBlock<P, N, NT> sb;
+  sb.load(a.S + ck.id * (P * N));
+  const int nkb = (min(rows, v0 + G::BROWS) + kTB - 1) / kTB;
+  RowBlock<TI, N * R, R, NT, false, kTB> bb;
+  RowBlock<TI, P * R, R, NT, false, kTB> xb;
+  bb.template load<true>(Bg, a, b, h, c0, Lc, 0);
+  xb.template load<false>(Xg, a, b, h, c0, Lc, 0);
   chunk_tables<TI, N, NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
   if (tid < kQ) sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
 
@@ -731,29 +753,28 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
 #pragma unroll
   for (int s = 0; s < PKS; ++s) yf[s] = typename Pol::Frag{};
 #pragma unroll
-  for (int piece = 0; piece < G::BROWS / 64; ++piece) {
-    const int pv0 = v0 + 64 * piece;
-    if (pv0 >= rows) break;
-    RowBlock<TY, P * R, R, NT, false, 64> yb;
-    yb.template load<false>(Yg, a, b, h, c0, Lc, pv0);
-    __syncthreads();   // the table scratch (or the previous piece) is free
-    put_rows<Pol, TY, P, R, NT, 64>(yb, sm.u.own);
+  for (int pc = 0; pc < NPC; ++pc) {
+    if (v0 + 64 * pc >= rows) break;
+    if (pc > 0) __syncthreads();   // the previous piece is read
+    put_rows<Pol, TY, P, R, NT, 64>(ybp[pc], sm.u.own);
     __syncthreads();
-    if (lt / 4 == piece) {
+    if (lt / 4 == pc) {
 #pragma unroll
       for (int s = 0; s < PKS; ++s) yf[s] = Pol::frag(sm.u.own, 16 * (lt % 4), s * KS, lane);
     }
   }
   // the entry state: q = dY Shat, dCt = e^{cs_t} q, de_t = sum Ct . q
-  const float* __restrict__ Sh = a.S + ck.id * (P * N);
   __syncthreads();   // the own-row buffer is read
-  for (int i = tid; i < P * N / 4; i += NT) {
-    const int p = (4 * i) / N, n = (4 * i) % N;
-    const f4 v = reinterpret_cast<const f4*>(Sh)[i];
-    Pol::put(sm.u.sht, n, p, v.x);
-    Pol::put(sm.u.sht, n + 1, p, v.y);
-    Pol::put(sm.u.sht, n + 2, p, v.z);
-    Pol::put(sm.u.sht, n + 3, p, v.w);
+#pragma unroll
+  for (int i = 0; i < StateBlock<P, N, NT>::IT; ++i) {
+    const int vi = tid + NT * i;
+    if (vi < StateBlock<P, N, NT>::NV) {
+      float v[8];
+      sb.raw[i].get(v);
+      const int p = (8 * vi) / N, n = (8 * vi) % N;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Pol::put(sm.u.sht, n + j, p, v[j]);
+    }
   }
   __syncthreads();
   const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
@@ -802,12 +823,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   }
 
   // ---- walk the u rows at or before this wave's t rows: dCt += W2 Bt
-  const int nkb = (min(rows, v0 + G::BROWS) + kTB - 1) / kTB;
   const int ttok_max = min(Lc - 1, (16 * ttile + 15) / R);
-  RowBlock<TI, N * R, R, NT, false, kTB> bb;
-  RowBlock<TI, P * R, R, NT, false, kTB> xb;
-  bb.template load<true>(Bg, a, b, h, c0, Lc, 0);
-  xb.template load<false>(Xg, a, b, h, c0, Lc, 0);
   auto stage = [&](int k) {
     put_rows_T<Pol, TI, N, R, NT, kTB, true>(bb, sm.u.stg[k & 1].bt, sm.tb, nullptr, k * kTB / R, Lc);
     put_xrows<Pol, TI, P, R, NT, kTB>(xb, sm.u.stg[k & 1].x);
