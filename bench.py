@@ -75,6 +75,19 @@ def prefill_bytes(w, in_bytes=2, out_bytes=4, h0=False, hT=True, nseq=None):
     return inputs + states + H * 4 + out_bytes * B * T * H * P * R
 
 
+def prefill_flops(w):
+    """Dense chunk contractions of the chunked prefill, 2 flops per multiply-add:
+    per chunk-head the Gram (QR)^2 N and Y_diag (QR)^2 P over the chunk's QR
+    virtual rows, Y_off and the chunk state QR N P each."""
+    Q, R, N, P = w.chunk, w.rank, w.dstate, w.headdim
+    chunks = w.batch * w.nheads * ((w.seqlen + Q - 1) // Q)
+    V = Q * R
+    return 2 * chunks * (V * V * (N + P) + 2 * V * N * P)
+
+
+MFMA_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA (MI355X); the split operands run on it
+
+
 def source_hash(files):
     """Hash of the named files under the package's csrc/ directory."""
     h = hashlib.sha256()
@@ -580,6 +593,8 @@ def main():
                 tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
                 sequences=r["nseq"], lengths=r["lengths"], algorithmic_bytes=r["bytes"],
                 workspace_bytes=r["ws_bytes"], hbm_frac=round(ach / HBM_PEAK_GBS, 4))
+        fl = prefill_flops(r["workload"])
+        tf = fl / (r["call_ms"] * 1e-3) / 1e12
         return dict(
             ms_per_call=round(r["call_ms"], 4), p50_ms=round(r["call_p50_ms"], 4),
             tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
@@ -587,6 +602,10 @@ def main():
             roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                           frac=round(ach / HBM_PEAK_GBS, 4), traffic=counters_for(tag),
                           kernel="whole call (k_chunk_state + k_state_pass + k_chunk_output)"),
+            mfma=dict(flops=fl, achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=round(tf / MFMA_PEAK_TFLOPS, 4),
+                      counting="dense chunk contractions: Gram (QR)^2 N, Y_diag (QR)^2 P, Y_off and "
+                               "chunk state QR N P each, 2 flops per multiply-add"),
             cpu_baseline=cpu.get(tag))
 
     workloads = {}

@@ -64,11 +64,43 @@ struct TokScalars {
   }
 };
 
+// One halving exchange of a reduce-scatter over lanes: of W values a lane
+// keeps the lower half (bit O of its lane index clear) or the upper half,
+// each summed with its partner's (lane ^ O).
+template <int O, int W>
+__device__ __forceinline__ void rs_step(float* v, int j) {
+  const bool hi = (j & O) != 0;
+#pragma unroll
+  for (int i = 0; i < W / 2; ++i) {
+    const float send = hi ? v[i] : v[i + W / 2];
+    const float keep = hi ? v[i + W / 2] : v[i];
+    v[i] = keep + __shfl_xor(send, O, 64);
+  }
+}
+
+// The sums of UNR values over each aligned group of LPR lanes (UNR <= LPR,
+// both powers of two), one per lane: log2(UNR) halving exchanges, then plain
+// sums.  Lane j of a group ends with the sum of value j / (LPR / UNR).
+template <int LPR, int UNR>
+__device__ __forceinline__ float rows_sum(float* v, int j) {
+  static_assert(UNR <= LPR && UNR <= 8, "rows per lane group");
+  if constexpr (UNR >= 2) rs_step<LPR / 2, UNR>(v, j);
+  if constexpr (UNR >= 4) rs_step<LPR / 4, UNR / 2>(v, j);
+  if constexpr (UNR >= 8) rs_step<LPR / 8, UNR / 4>(v, j);
+  float s = v[0];
+#pragma unroll
+  for (int o = LPR / UNR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------
+// four waves per SIMD (at most 128 registers) for the 8-row blocks; the
+// B/C preparation needs more registers than that
 template <typename TI, typename TO, int N, int UNR, bool PREV, bool PREP>
-__global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 && !PREP ? 4 : 1))) void k_decode_siso_tok(
+    DecodeArgs a) {
   constexpr int LPR = N / 4;      // lanes per state row
   constexpr int RPW = 64 / LPR;   // rows per wave per pass
   constexpr int RPB = 4 * RPW;    // rows per block per pass
@@ -151,25 +183,36 @@ __global__ __launch_bounds__(256) void k_decode_siso_tok(DecodeArgs a) {
     const float beta = (1.0f - lk) * dk * alpha;
     const float gamma = lk * dk;
     const bool ang = (a.flags & kThetaIsAngle) != 0;
-    float s0, c0, s1, c1;
-    sincosf(ang ? thk.x : dk * thk.x, &s0, &c0);
-    sincosf(ang ? thk.y : dk * thk.y, &s1, &c1);
-    const f2 r0 = f2{c0, s0}, r1 = f2{c1, s1};
+    const f2 r0 = cos_sin_turns(ang ? thk.x : dk * thk.x);
+    const f2 r1 = cos_sin_turns(ang ? thk.y : dk * thk.y);
     if constexpr (PREP) {
       bk = prep(bk, bw, bbias);
       ck = prep(ck, cw, cbias);
     }
     const f4 bt = gamma * bk, bp = beta * bo;
     TO* __restrict__ yk = Y + tok_head(a, bh, k) * P;
+    float part[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int p = u * RPB + rsub;
       f4 s = alpha * v[u] + xo[u] * bp;
       s = rot2pairs(s, r0, r1);
       s += xk[u] * bt;
       v[u] = s;
-      const float part = group_sum<LPR>(s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w);
-      if ((lane % LPR) == 0 && p < P) st1(yk, p, part);
+      part[u] = s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w;
+    }
+    // y of the lane's UNR rows: summed over the row's LPR lanes
+    if constexpr (UNR <= LPR) {
+      const int j = lane % LPR;
+      const float tot = rows_sum<LPR, UNR>(part, j);
+      const int p = (j / (LPR / UNR)) * RPB + rsub;
+      if (j % (LPR / UNR) == 0 && p < P) st1(yk, p, tot);
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int p = u * RPB + rsub;
+        const float tot = group_sum<LPR>(part[u]);
+        if ((lane % LPR) == 0 && p < P) st1(yk, p, tot);
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
