@@ -215,6 +215,55 @@ __device__ __forceinline__ void str(float* __restrict__ p, const float* v) {
   }
 }
 
+// the R ranks of one (token, column) element as loaded (bf16 stays packed),
+// held in registers from an early load until use
+template <typename TI, int R>
+struct RankRaw;
+template <int R>
+struct RankRaw<float, R> {
+  float v[R];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { ldr<R>(p, v); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = 0.0f;
+  }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) o[r] = v[r];
+  }
+};
+template <int R>
+struct RankRaw<bf16_t, R> {
+  static_assert(R == 1 || R == 2 || R == 4, "ranks per element");
+  uint32_t u[(R + 1) / 2];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+    if constexpr (R == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      u[0] = q.x;
+      u[1] = q.y;
+    } else if constexpr (R == 2) {
+      u[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      u[0] = p->bits;
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < (R + 1) / 2; ++i) u[i] = 0u;
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    if constexpr (R == 1) {
+      o[0] = __uint_as_float(u[0] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) {
+        o[2 * i] = __uint_as_float(u[i] << 16);
+        o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  }
+};
+
 // the rotated value (by -Phi) of element n of a (column n, partner n ^ 1)
 // pair, from both raw elements
 __device__ __forceinline__ float rot_own(float own, float oth, bool odd, f2 cs) {
@@ -343,8 +392,10 @@ struct USmem {
       typename Pol::template Store<N, kTB> ct;  // Ct^T      [n][v]
       typename Pol::template Store<P, kTB> yt;  // dy^T      [p][v]
     } st[2];                                    // double-buffered
-    typename Pol::template Store<P, N> gt;      // Gt        [p][n]
-    typename Pol::template Store<N, P> gtt;     // Gt^T      [n][p]
+    struct E {
+      typename Pol::template Store<P, N> gt;    // Gt        [p][n]
+      typename Pol::template Store<N, P> gtt;   // Gt^T      [n][p]
+    } e;
   } u;
 };
 
@@ -431,6 +482,37 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
       for (int s = 0; s < NKS; ++s) bf[s] = Pol::frag(sm.u.own.b, 16 * (lt % 4), s * KS, lane);
 #pragma unroll
       for (int s = 0; s < PKS; ++s) xf[s] = Pol::fragx_c(sm.u.own.x, 16 * (lt % 4), s * KS, lane);
+    }
+  }
+
+  // the end-state and output operands go out now and arrive during the walk:
+  // G_end (this thread's pairs of it), and the raw B and x of this lane's D
+  // rows (u) and columns in the end-state products
+  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
+                                        : g.dS + (ck.id + 1) * (P * N);
+  constexpr int GPT = P * NP / NT;   // G_end pairs per thread
+  static_assert(P * NP % NT == 0, "G_end pairs per thread");
+  f2 gpre[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int e = tid + NT * i, p = e / NP, kp = e % NP;
+    gpre[i] = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
+  }
+  const int urow0 = 16 * utile + 4 * gq;   // this lane's D rows (u) in the end-state products
+  RankRaw<TI, R> bpre[NTL][4 / R], xpre[PT][4 / R];
+#pragma unroll
+  for (int j0 = 0; j0 < 4; j0 += R) {
+    const int vr = urow0 + j0, ut = vr / R;
+    const bool ok = live && vr < rows;
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      if (ok) bpre[i][j0 / R].load(Bc + (int64_t)ut * G_ * N * R + (int64_t)(16 * i + l16) * R);
+      else bpre[i][j0 / R].zero();
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      if (ok) xpre[i][j0 / R].load(Xc + (int64_t)ut * a.H * P * R + (int64_t)(16 * i + l16) * R);
+      else xpre[i][j0 / R].zero();
     }
   }
 
@@ -539,24 +621,24 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     tk[(kRrow0 + half) * kQ + tid] = s;
   }
 
-  // ---- the end state: Gt = rows of G_end rotated by -Phi_end
-  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
-                                        : g.dS + (ck.id + 1) * (P * N);
+  // ---- the end state: Gt = rows of G_end rotated by -Phi_end, in both
+  // layouts (the staging buffers are free: the row sums above are past a
+  // barrier)
   const f2* __restrict__ re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
-  for (int i = tid; i < P * NP; i += NT) {
-    const int p = i / NP, kp = i % NP;
-    const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
-    const f2 gt = rot_neg(gv, re[kp]);
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int e = tid + NT * i, p = e / NP, kp = e % NP;
+    const f2 gt = rot_neg(gpre[i], re[kp]);
     const float v2[2] = {gt.x, gt.y};
-    Pol::template putn<2>(sm.u.gt, p, 2 * kp, v2);
+    Pol::template putn<2>(sm.u.e.gt, p, 2 * kp, v2);
+    Pol::put(sm.u.e.gtt, 2 * kp, p, gt.x);
+    Pol::put(sm.u.e.gtt, 2 * kp + 1, p, gt.y);
   }
   __syncthreads();
   const double cs_end = sm.tb.cs[Lc - 1];
   const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
                                   ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
                             : 0.0f;
-  // this lane's D rows (u) in the end-state products: 16 utile + 4 g + jj
-  const int urow0 = 16 * utile + 4 * gq;
   float mu[4], cu[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -575,17 +657,10 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     for (int i = 0; i < PT; ++i) {
       f4 v = f4{0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) v = Pol::mma(bf[s], Pol::frag(sm.u.gt, 16 * i, s * KS, lane), v);
-      const int p = 16 * i + l16;
+      for (int s = 0; s < NKS; ++s) v = Pol::mma(bf[s], Pol::frag(sm.u.e.gt, 16 * i, s * KS, lane), v);
       float xv[4];
 #pragma unroll
-      for (int j0 = 0; j0 < 4; j0 += R) {
-        const int vr = urow0 + j0;
-        if (vr < rows) ldr<R>(Xc + (int64_t)(vr / R) * a.H * P * R + p * R, xv + j0);
-        else
-#pragma unroll
-          for (int r = 0; r < R; ++r) xv[j0 + r] = 0.0f;
-      }
+      for (int j0 = 0; j0 < 4; j0 += R) xpre[i][j0 / R].get(xv + j0);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         accx[i][jj] += cu[jj] * v[jj];
@@ -599,15 +674,6 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
         if (t < Lc) tk[kDmend * kQ + t] = v;
       });
   }
-  __syncthreads();   // Gt is read
-  for (int i = tid; i < P * NP; i += NT) {
-    const int p = i / NP, kp = i % NP;
-    const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
-    const f2 gt = rot_neg(gv, re[kp]);
-    Pol::put(sm.u.gtt, 2 * kp, p, gt.x);
-    Pol::put(sm.u.gtt, 2 * kp + 1, p, gt.y);
-  }
-  __syncthreads();
 
   // ---- outputs: dx; w = X Gt: dBt += m_end w, the crossing term of the
   // last token (raw frame, kept out of the phase gradient), dB back in the
@@ -631,7 +697,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
   for (int i = 0; i < NTL; ++i) {
     f4 w = f4{0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < PKS; ++s) w = Pol::mma_xa(xf[s], Pol::frag(sm.u.gtt, 16 * i, s * KS, lane), w);
+    for (int s = 0; s < PKS; ++s) w = Pol::mma_xa(xf[s], Pol::frag(sm.u.e.gtt, 16 * i, s * KS, lane), w);
     const int n = 16 * i + l16, kp = n >> 1;
     const bool odd = n & 1;
     // raw B of this lane's column (the pair partner's from the next lane)
@@ -641,10 +707,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     for (int j0 = 0; j0 < 4; j0 += R) {
       const int vr = urow0 + j0, ut = vr / R;
       const bool ok = live && vr < rows;
-      if (ok) ldr<R>(Bc + (int64_t)ut * G_ * N * R + (int64_t)n * R, bo + j0);
-      else
-#pragma unroll
-        for (int r = 0; r < R; ++r) bo[j0 + r] = 0.0f;
+      bpre[i][j0 / R].get(bo + j0);
       const f2 c2 = ok ? sm.tb.cs_of(ut, kp) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) cs[j0 + r] = c2;
@@ -763,6 +826,20 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       for (int s = 0; s < PKS; ++s) yf[s] = Pol::frag(sm.u.own, 16 * (lt % 4), s * KS, lane);
     }
   }
+  // the raw C of this lane's D rows (t) and columns, for the entry-state
+  // and phase products: loaded once, now
+  const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
+  RankRaw<TI, R> cpre[NTL][4 / R];
+#pragma unroll
+  for (int j0 = 0; j0 < 4; j0 += R) {
+    const int vr = trow0 + j0;
+    const bool ok = live && vr < rows;
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      if (ok) cpre[i][j0 / R].load(Cc + (int64_t)(vr / R) * G_ * N * R + (int64_t)(16 * i + l16) * R);
+      else cpre[i][j0 / R].zero();
+    }
+  }
   // the entry state: q = dY Shat, dCt = e^{cs_t} q, de_t = sum Ct . q
   __syncthreads();   // the own-row buffer is read
 #pragma unroll
@@ -777,7 +854,6 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
     }
   }
   __syncthreads();
-  const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
   float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
   f4 acc[NTL];
   {
@@ -795,10 +871,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       for (int j0 = 0; j0 < 4; j0 += R) {
         const int vr = trow0 + j0, t = vr / R;
         const bool ok = live && vr < rows;
-        if (ok) ldr<R>(Cc + (int64_t)t * G_ * N * R + (int64_t)n * R, co + j0);
-        else
-#pragma unroll
-          for (int r = 0; r < R; ++r) co[j0 + r] = 0.0f;
+        cpre[i][j0 / R].get(co + j0);
         const f2 c2 = ok ? sm.tb.cs_of(t, n >> 1) : f2{1.0f, 0.0f};
         const float e = ok ? sm.ecs[t] : 0.0f;
 #pragma unroll
@@ -883,10 +956,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
     for (int j0 = 0; j0 < 4; j0 += R) {
       const int vr = trow0 + j0, t = vr / R;
       const bool ok = live && vr < rows;
-      if (ok) ldr<R>(Cc + (int64_t)t * G_ * N * R + (int64_t)n * R, co + j0);
-      else
-#pragma unroll
-        for (int r = 0; r < R; ++r) co[j0 + r] = 0.0f;
+      cpre[i][j0 / R].get(co + j0);
       const f2 c2 = ok ? sm.tb.cs_of(t, kp) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) cs[j0 + r] = c2;
