@@ -700,7 +700,7 @@ static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int R, int G, int Q
     sz[7] = (size_t)Bsz * H * N * R * 4;
   }
   if (!(P == 16 && N == 16)) {   // the matrix-core kernels' token sums and phase gradients
-    sz[8] = units * 7 * Q * 4;
+    sz[8] = units * 10 * Q * 4;
     sz[9] = units * Q * (N / 2) * 4;
   }
   size_t total = 0;

@@ -373,13 +373,20 @@ struct GeoU {
 };
 
 // per-chunk token sums in the workspace: [units][kTokSums][Q]
-enum TokSum { kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5, kDe = 6, kTokSums = 7 };
+// (slots 7 and 8: each half's part of the end rotation's phase gradient per
+// pair; slot 9: the halves' <Gt, Shat> and previous-token sums)
+enum TokSum {
+  kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5, kDe = 6,
+  kDphiE0 = 7, kDphiE1 = 8, kEndSums = 9, kTokSums = 10
+};
 
 template <class Pol, int P, int N, int R>
 struct USmem {
   using G = GeoU<P, N, R>;
   Tables<N, false> tb;
   float rowpart[G::NW][kQ];   // each wave's row sums of dM o M
+  float part[G::NT];          // per-thread parts of the end-state sums
+  float red[G::NW];
   union U {
     TableScratch<N, G::NT> scr;
     struct O {
@@ -624,21 +631,82 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
   // ---- the end state: Gt = rows of G_end rotated by -Phi_end, in both
   // layouts (the staging buffers are free: the row sums above are past a
   // barrier)
+  // The chunk's end-state sums ride along, over this block's share of the
+  // pairs (half of them each when the other half of a split chunk runs):
+  // <Gt, Shat>, the end rotation's phase gradient <G_end, J S_end> per pair
+  // (S_end = the next entry state without the crossing left-endpoint term)
+  // and the previous token's <dShat_c, x_{c0-1} B_{c0-1}^T>.
   const f2* __restrict__ re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
+  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
+                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
+                            : 0.0f;
+  static_assert(NT % NP == 0 && GPT % 2 == 0, "a thread's pairs share one column pair");
+  const bool both = G::SPLIT == 2 && rows > G::BROWS;   // the other half runs too
+  const int i_lo = both ? half * (GPT / 2) : 0, i_hi = both ? i_lo + GPT / 2 : GPT;
+  const TI* xprev = nullptr;
+  const TI* bprev = nullptr;
+  if (c > 0) {
+    xprev = Xc - (int64_t)a.H * P * R;
+    bprev = Bc - (int64_t)G_ * N * R;
+  } else if (a.has_prev) {
+    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
+    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
+  }
+  const float* __restrict__ Sh = a.S + ck.id * (P * N);
+  const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N : a.S + (ck.id + 1) * (P * N);
+  const float* __restrict__ dSc = g.dS + ck.id * (P * N);
+  const TI* __restrict__ Blast = Bc + (int64_t)(Lc - 1) * G_ * N * R;
+  const TI* __restrict__ Xlast = Xc + (int64_t)(Lc - 1) * a.H * P * R;
+  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
     const int e = tid + NT * i, p = e / NP, kp = e % NP;
-    const f2 gt = rot_neg(gpre[i], re[kp]);
+    const f2 gv = gpre[i];
+    const f2 gt = rot_neg(gv, re[kp]);
     const float v2[2] = {gt.x, gt.y};
     Pol::template putn<2>(sm.u.e.gt, p, 2 * kp, v2);
     Pol::put(sm.u.e.gtt, 2 * kp, p, gt.x);
     Pol::put(sm.u.e.gtt, 2 * kp + 1, p, gt.y);
+    if (i >= i_lo && i < i_hi) {
+      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)p * N + 2 * kp);
+      e_part += gt.x * sh.x + gt.y * sh.y;
+      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * kp);
+      if (ck.next) {
+        float xl[R], b0[R], b1[R];
+        ldr<R>(Xlast + (int64_t)p * R, xl);
+        ldr<R>(Blast + (int64_t)(2 * kp) * R, b0);
+        ldr<R>(Blast + (int64_t)(2 * kp + 1) * R, b1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          se.x -= bpL * xl[r] * b0[r];
+          se.y -= bpL * xl[r] * b1[r];
+        }
+      }
+      ph_part += -gv.x * se.y + gv.y * se.x;
+      if (xprev) {
+        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * kp);
+        float xq[R], b0[R], b1[R];
+        ldr<R>(xprev + (int64_t)p * R, xq);
+        ldr<R>(bprev + (int64_t)(2 * kp) * R, b0);
+        ldr<R>(bprev + (int64_t)(2 * kp + 1) * R, b1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) h_part += xq[r] * (ds.x * b0[r] + ds.y * b1[r]);
+      }
+    }
   }
-  __syncthreads();
+  sm.part[tid] = ph_part;
+  const float e_end = block_sum<NT>(e_part, sm.red);
+  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the LDS writes above
+  if (tid < NP) {
+    float v = 0.0f;
+    for (int m = 0; m < NT / NP; ++m) v += sm.part[tid + NP * m];
+    tk[(kDphiE0 + half) * kQ + tid] = v;
+  }
+  if (tid == 0) {
+    tk[kEndSums * kQ + half] = e_end;
+    tk[kEndSums * kQ + 2 + half] = h_end;
+  }
   const double cs_end = sm.tb.cs[Lc - 1];
-  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
-                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
-                            : 0.0f;
   float mu[4], cu[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -984,10 +1052,9 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
 }
 
 // --------------------------------------------------------------------------
-// The chunk's per-token gradients from the token sums of both sides: the
-// end state's scalars, suffix sums over the chunk, dt, lam, A, theta and
-// the token before the sequence.  1024 threads per chunk: every load of the
-// end-state sums is issued before any is used.
+// The chunk's per-token gradients from the token sums of both sides:
+// suffix sums over the chunk, dt, lam, A, theta and the token before the
+// sequence.  1024 threads per chunk.
 constexpr int kFinNT = 1024;
 template <int P, int N>
 struct FinSmem {
@@ -1010,12 +1077,9 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
   const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc, tid = threadIdx.x;
   const int c = blockIdx.x;
-  const bool last = c + 1 >= a.nchunk;
   const int G_ = a.G;
   const bool shared_grp = G_ != a.H;
   const int64_t gi = group_index(a, b, c0, h), ti0 = token_index(a, b, c0, h);
-  const TI* __restrict__ Bc = static_cast<const TI*>(a.B) + gi * N * R;
-  const TI* __restrict__ Xc = static_cast<const TI*>(a.x) + ti0 * P * R;
   // token scalars and the chunk-local log-decay prefix (double)
   if (tid < 64) {
     float d = 0.0f, l = 0.0f, A = 0.0f;
@@ -1042,77 +1106,16 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   const float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
   for (int i = tid; i < Lc * NP; i += NT) sm.dphi[i / NP][i % NP] = dph[i];
 
-  // the end state's scalars: <Gt, Shat>, the end rotation's phase gradient
-  // <G_end, J S_end> per pair, and <dShat_c, x_{c0-1} B_{c0-1}^T>
-  const float* __restrict__ Gend = last ? g.dhT ? g.dhT + ((int64_t)b * a.H + h) * P * N : nullptr
-                                        : g.dS + (ck.id + 1) * (P * N);
-  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
-                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
-                            : 0.0f;
-  const TI* __restrict__ Blast = Bc + (int64_t)(Lc - 1) * G_ * N * R;
-  const TI* __restrict__ Xlast = Xc + (int64_t)(Lc - 1) * a.H * P * R;
-  const TI* xprev = nullptr;
-  const TI* bprev = nullptr;
-  if (c > 0) {
-    xprev = Xc - (int64_t)a.H * P * R;
-    bprev = Bc - (int64_t)G_ * N * R;
-  } else if (a.has_prev) {
-    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
-    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
-  }
-  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
-  static_assert(NT % NP == 0 && P * NP % NT == 0, "each thread keeps one pair in the end-state loop");
-  {
-    const float* __restrict__ Sh = a.S + ck.id * (P * N);
-    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
-    const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N
-                                           : a.S + (ck.id + 1) * (P * N);
-    const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-#pragma unroll
-    for (int it = 0; it < P * NP / NT; ++it) {
-      const int i = tid + NT * it;
-      const int p = i / NP, kp = i % NP;
-      const f2 gv = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
-      const f2 gt = rot_neg(gv, re[kp]);
-      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)p * N + 2 * kp);
-      e_part += gt.x * sh.x + gt.y * sh.y;
-      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * kp);
-      if (ck.next) {
-        float xl[R], b0[R], b1[R];
-        ldr<R>(Xlast + (int64_t)p * R, xl);
-        ldr<R>(Blast + (int64_t)(2 * kp) * R, b0);
-        ldr<R>(Blast + (int64_t)(2 * kp + 1) * R, b1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          se.x -= bpL * xl[r] * b0[r];
-          se.y -= bpL * xl[r] * b1[r];
-        }
-      }
-      ph_part += -gv.x * se.y + gv.y * se.x;
-      if (xprev) {
-        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * kp);
-        float xq[R], b0[R], b1[R];
-        ldr<R>(xprev + (int64_t)p * R, xq);
-        ldr<R>(bprev + (int64_t)(2 * kp) * R, b0);
-        ldr<R>(bprev + (int64_t)(2 * kp + 1) * R, b1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) h_part += xq[r] * (ds.x * b0[r] + ds.y * b1[r]);
-      }
-    }
-  }
-  sm.part[tid] = ph_part;
-  const float e_end = block_sum<NT>(e_part, sm.red);
-  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the LDS writes above
-  if (tid < NP) {
-    float v = 0.0f;
-    for (int m = 0; m < NT / NP; ++m) v += sm.part[tid + NP * m];
-    sm.dphi_end[tid] = v;
-  }
-  __syncthreads();   // part is read
-
-  // ---- the token sums: log-decay (cs), trapezoid weights (gamma, beta')
+  // the end state's sums from the u side (one part per half of a split chunk)
   using GU = GeoU<P, N, R>;
   const float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
+  const bool both = GU::SPLIT == 2 && Lc * R > GU::BROWS;
+  const float e_end = tk[kEndSums * kQ] + (both ? tk[kEndSums * kQ + 1] : 0.0f);
+  const float h_end = tk[kEndSums * kQ + 2] + (both ? tk[kEndSums * kQ + 3] : 0.0f);
+  if (tid < NP) sm.dphi_end[tid] = tk[kDphiE0 * kQ + tid] + (both ? tk[kDphiE1 * kQ + tid] : 0.0f);
+  __syncthreads();   // the tables, dphi and dphi_end are in
+
+  // ---- the token sums: log-decay (cs), trapezoid weights (gamma, beta')
   const double cs_end = sm.cs[Lc - 1];
   if (tid < kQ) {
     const int u = tid;
@@ -1205,6 +1208,8 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   // the token before the sequence: dx_prev = beta'_0 dShat_0 B_prev,
   // dB_prev = beta'_0 dShat_0^T x_prev
   if (c == 0 && a.has_prev && (g.dx_prev || g.dB_prev)) {
+    const TI* __restrict__ xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
+    const TI* __restrict__ bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
     const float bp0 = sm.bpr[0];
     const float* __restrict__ dSc = g.dS + ck.id * (P * N);
     if (g.dx_prev) {

@@ -107,8 +107,8 @@ struct BackwardArgs {
   // workspace: per-chunk dA partials; with head groups, per-head gradients
   // of B, C, theta and B_prev before the fixed-order sum over each group
   float *dApart, *dBh, *dCh, *dthh, *dBph;
-  // workspace of the rank-R kernels: per-chunk token sums [units, 7, Q] and
-  // phase gradients [units, Q, N/2]
+  // workspace of the matrix-core kernels: per-chunk token and end-state sums
+  // [units, 10, Q] and phase gradients [units, Q, N/2]
   float *tokw, *dphiB;
 };
 bool backward_supported(int P, int N, int R, int Q);
