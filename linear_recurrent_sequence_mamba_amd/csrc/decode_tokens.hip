@@ -55,12 +55,7 @@ struct TokScalars {
     beta = (1.0f - l) * d * alpha;
     gamma = l * d;
     const int kk = threadIdx.x;
-    if (kk < N / 2) {
-      const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
-      float s, c;
-      sincosf(phi, &s, &c);
-      cs[kk] = f2{c, s};
-    }
+    if (kk < N / 2) cs[kk] = cos_sin_turns((a.flags & kThetaIsAngle) ? th : d * th);
   }
 };
 
