@@ -165,10 +165,11 @@ def test_backward_mimo_variants():
     _check(w, d, dy.to(torch.bfloat16), dhT, flags=m3.M3_THETA_IS_ANGLE | m3.M3_A_PER_TOKEN)
 
 
-def test_backward_is_deterministic_and_matches_split():
+@pytest.mark.parametrize("R", [1, 4])
+def test_backward_is_deterministic_and_matches_split(R):
     """Two calls give identical gradients; the h0 gradient of the second half
     of a split scan is the dhT that the first half's backward needs."""
-    w = I.Workload("g", 133, 2, 200, 3, 64, 128, 1, 64, "bf16")
+    w = I.Workload("g", 133, 2, 200, 3, 64, 128, R, 64, "bf16")
     d = I.prefill_inputs(w, h0="normal", with_prev=True)
     dy, dhT = _cotangents(w, d)
     g1 = _gpu(d, dy, dhT)
@@ -188,9 +189,12 @@ def test_backward_is_deterministic_and_matches_split():
     # x and B of token k - 1 also feed the second half as its token before
     gx = torch.cat([ga["x"], gb["x"]], 1)
     gx[:, k - 1] += gb["x_prev"]
+    gB = torch.cat([ga["B"], gb["B"]], 1)
+    gB[:, k - 1] += gb["B_prev"]
     e = rel_err(cpu64(gx), cpu64(g1["x"]))
-    say(f"  split: dx err {e:.1e}")
-    assert e <= 1e-4
+    eb = rel_err(cpu64(gB), cpu64(g1["B"]))
+    say(f"  split: dx err {e:.1e}  dB err {eb:.1e}")
+    assert e <= 1e-4 and eb <= 1e-4
 
 
 @pytest.mark.parametrize("name", ["siso_prefill", "mimo_prefill"])
