@@ -325,12 +325,12 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
 
 // B rows of a block rotated by +(Phi_end - Phi_t) and scaled by W_t,
 // transposed: st[n][v - v0]
-template <class Pol, typename TI, int N, int R, int NT, bool TF, class Tab, class Prep>
-__device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF>& rb,
-                                             typename Pol::template Store<N, kRB>& st,
+template <class Pol, typename TI, int N, int R, int NT, bool TF, int ROWS, class Tab, class Prep>
+__device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF, ROWS>& rb,
+                                             typename Pol::template Store<N, ROWS>& st,
                                              const Tab& tb, const float* w, int t0, int Lc,
                                              const Prep& prep) {
-  using RBk = RowBlock<TI, N * R, R, NT, TF>;
+  using RBk = RowBlock<TI, N * R, R, NT, TF, ROWS>;
   constexpr int NPAIR = 4 / R;
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {

@@ -188,14 +188,20 @@ __device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, TF, ROWS>
 // total decay and phase go to the workspace.  With the B/C preparation the
 // chunk's B rows are normalised, weighted and biased as they are staged, and
 // their inverse RMS goes to the workspace for the output kernel.
+// virtual rows per staged u-block: 32 for a single input (a smaller LDS
+// footprint, three blocks per CU), 64 otherwise
+template <int R>
+constexpr int k1_rows() { return R == 1 ? 32 : kRB; }
+
 template <class Pol, typename TI, int P, int N, int R, bool PREP>
 struct K1Smem {
+  static constexpr int UBR = k1_rows<R>();
   Tables<N, false, true> tb;
   union U {
-    typename Pol::template Store<N, kRB> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
+    typename Pol::template Store<N, UBR> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
     TableScratch<N, Geo<P, N, R, 8>::NT> scr;
   } u;
-  typename Pol::template XStore<P, kRB> xs;    // x^T  [p][v]
+  typename Pol::template XStore<P, UBR> xs;    // x^T  [p][v]
   PrepTabT<PREP, N, R> pb;                     // B preparation
 };
 
@@ -203,6 +209,7 @@ template <class Pol, typename TI, int P, int N, int R, bool PREP>
 __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillArgs a) {
   using G = Geo<P, N, R, 8>;
   __shared__ K1Smem<Pol, TI, P, N, R, PREP> sm;
+  constexpr int UBR = k1_rows<R>(), NUB = G::ROWS / UBR;   // staged u-blocks
   constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
   constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
   const int h = blockIdx.y;
@@ -230,13 +237,13 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   // with R >= 2 a token's row of B (N R values) or x (P R) is long enough
   // for lanes to walk it (whole lines per load); single-rank rows are
   // spread one token per lane, so the transposed stores pair up lanes
-  RowBlock<TI, N * R, R, G::NT, TFK1> bb[G::NUB];
-  RowBlock<TI, P * R, R, G::NT, TFK1> xb[G::NUB];
+  RowBlock<TI, N * R, R, G::NT, TFK1, UBR> bb[NUB];
+  RowBlock<TI, P * R, R, G::NT, TFK1, UBR> xb[NUB];
 #pragma unroll
-  for (int ub = 0; ub < G::NUB; ++ub) {
-    if (ub * kRB < rows) {
-      bb[ub].template load<true>(Bg, a, b, h, c0, Lc, ub * kRB);
-      xb[ub].template load<false>(Xg, a, b, h, c0, Lc, ub * kRB);
+  for (int ub = 0; ub < NUB; ++ub) {
+    if (ub * UBR < rows) {
+      bb[ub].template load<true>(Bg, a, b, h, c0, Lc, ub * UBR);
+      xb[ub].template load<false>(Xg, a, b, h, c0, Lc, ub * UBR);
     }
   }
 
@@ -258,8 +265,8 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     rsB = a.rsB + chunk_id * (kQ * R);
     pl.store(sm.pb);
 #pragma unroll
-    for (int ub = 0; ub < G::NUB; ++ub)
-      if (ub * kRB < rows) row_sumsq(bb[ub], a.bc, N, ub * kRB / R, Lc, sm.pb.inv);
+    for (int ub = 0; ub < NUB; ++ub)
+      if (ub * UBR < rows) row_sumsq(bb[ub], a.bc, N, ub * UBR / R, Lc, sm.pb.inv);
   }
   __syncthreads();   // W_t visible (and the B preparation tables)
   if constexpr (PREP) {
@@ -275,16 +282,16 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   for (int q = 0; q < QPW; ++q) acc[q] = f4{0, 0, 0, 0};
 
 #pragma unroll
-  for (int ub = 0; ub < G::NUB; ++ub) {
-    if (ub * kRB >= rows) break;
+  for (int ub = 0; ub < NUB; ++ub) {
+    if (ub * UBR >= rows) break;
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
     if constexpr (PREP)
-      store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc,
-                                               TabPrep<N, R>{&sm.pb});
+      store_rows_T<Pol, TI, N, R, G::NT, TFK1, UBR>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * UBR / R, Lc,
+                                                    TabPrep<N, R>{&sm.pb});
     else
-      store_rows_T<Pol, TI, N, R, G::NT, TFK1>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * kRB / R, Lc,
-                                               NoPrep{});
-    store_x_T<Pol, TI, P, R, G::NT, kRB, TFK1>(xb[ub], sm.xs);
+      store_rows_T<Pol, TI, N, R, G::NT, TFK1, UBR>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * UBR / R, Lc,
+                                                    NoPrep{});
+    store_x_T<Pol, TI, P, R, G::NT, UBR, TFK1>(xb[ub], sm.xs);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QPW; ++q) {
@@ -292,7 +299,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
       if (NQ % G::NW == 0 || qq < NQ) {
         const int pt = qq / G::NTL, nt = qq % G::NTL;
 #pragma unroll
-        for (int kk = 0; kk < kRB; kk += Pol::KS)
+        for (int kk = 0; kk < UBR; kk += Pol::KS)
           acc[q] = Pol::mma_x(Pol::frag(sm.u.bw, 16 * nt, kk, lane),
                               Pol::fragx_c(sm.xs, 16 * pt, kk, lane), acc[q]);
       }
