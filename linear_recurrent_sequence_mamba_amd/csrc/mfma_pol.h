@@ -402,6 +402,20 @@ struct StateBlock {
       if (vi < NV) raw[i].load(src + (int64_t)vi * 8);
     }
   }
+  // rows [p0, p0 + ROWS) only, into st[p - p0][n]
+  template <class Pol, int ROWS>
+  __device__ __forceinline__ void store_part(typename Pol::template Store<ROWS, N>& st, int p0) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int vi = threadIdx.x + NT * i;
+      const int p = (vi * 8) / N;
+      if (vi < NV && p >= p0 && p < p0 + ROWS) {
+        float v[8];
+        raw[i].get(v);
+        Pol::put8(st, p - p0, (vi * 8) % N, v);
+      }
+    }
+  }
   template <class Pol>
   __device__ __forceinline__ void store(typename Pol::template Store<P, N>& st) const {
 #pragma unroll

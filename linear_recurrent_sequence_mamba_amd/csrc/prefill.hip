@@ -494,14 +494,21 @@ struct K3Smem {
   // (row, column) pairs, so the block's mask rows are tabulated once
   static constexpr int MT = R % 4 == 0 ? Geo3<P, N, R>::BROWS / R : 1;
   static constexpr int UB = 32;                // virtual rows per staged u-block
+  // a single-input chunk (one 4-wave block) keeps its LDS small enough for
+  // three blocks per CU: C rows staged 32 at a time, Shat in two halves,
+  // one u-block buffer
+  static constexpr bool LEAN = R == 1;
+  static constexpr int CRB = LEAN ? 32 : kRB;  // C rows per staged piece
+  static constexpr int SHP = LEAN && P >= 32 ? P / 2 : P;  // Shat rows per staged part (whole tiles)
+  static constexpr int NBUF = LEAN ? 1 : 2;    // u-block buffers
   Tables<N, false> tb;
   union U {
-    typename Pol::template Store<kRB, N> st;   // rotated C rows        [v][n]
-    typename Pol::template Store<P, N> sh;     // Shat                  [p][n]
-    typename Pol::template Store<UB, N> bst[2];  // rotated B rows, double-buffered
+    typename Pol::template Store<CRB, N> st;   // rotated C rows        [v][n]
+    typename Pol::template Store<SHP, N> sh;   // Shat                  [p][n]
+    typename Pol::template Store<UB, N> bst[NBUF];  // rotated B rows
     TableScratch<N, Geo3<P, N, R>::NT> scr;
   } u;
-  typename Pol::template XStore<P, UB> xs[2];  // x^T of a u-block      [p][v]
+  typename Pol::template XStore<P, UB> xs[NBUF];  // x^T of a u-block   [p][v]
   float msk[MT][kQ + 1];                       // M[t - t_lo][u]
   PrepTabT<PREP, N, R> pb, pc;                 // B and C preparation
 };
@@ -577,17 +584,21 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   // all loads go out first (the load counter retires in order): phase
   // inputs and token scalars, this block's C rows, the entry state, and the
   // first u-blocks of B and x
+  constexpr int CRB = SMT::CRB, NCB = G::BROWS / CRB, NBUF = SMT::NBUF;
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
-  RowBlock<TI, N * R, R, G::NT, false> cb[G::NCB];
+  RowBlock<TI, N * R, R, G::NT, false, CRB> cb[NCB];
 #pragma unroll
-  for (int k = 0; k < G::NCB; ++k)
-    if (v0 + k * kRB < rows) cb[k].template load<true>(Cg, a, b, h, c0, Lc, v0 + k * kRB);
+  for (int k = 0; k < NCB; ++k)
+    if (v0 + k * CRB < rows) cb[k].template load<true>(Cg, a, b, h, c0, Lc, v0 + k * CRB);
+  // the entry state (a single-input block loads it once its C rows are
+  // staged, to stay within the registers of three blocks per CU)
   StateBlock<P, N, G::NT> sb;
-  sb.load(a.S + chunk_id * P * N);
+  if constexpr (!SMT::LEAN) sb.load(a.S + chunk_id * P * N);
   // B and x move in u-blocks of 32 virtual rows, three in flight (two with
-  // the B/C preparation, whose staging needs the registers of the third)
-  constexpr int NS = PREP ? 2 : 3;
+  // the B/C preparation, whose staging needs the registers of the third,
+  // and for a single input)
+  constexpr int NS = (PREP || SMT::LEAN) ? 2 : 3;
   constexpr int UB = SMT::UB;
   constexpr int NKB = G::ROWS / UB;
   const int nkb = (vend + UB - 1) / UB;
@@ -619,8 +630,8 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   }
   if constexpr (PREP) {
 #pragma unroll
-    for (int k = 0; k < G::NCB; ++k)
-      if (v0 + k * kRB < rows) row_sumsq(cb[k], a.bc, N, (v0 + k * kRB) / R, Lc, sm.pc.inv);
+    for (int k = 0; k < NCB; ++k)
+      if (v0 + k * CRB < rows) row_sumsq(cb[k], a.bc, N, (v0 + k * CRB) / R, Lc, sm.pc.inv);
     __syncthreads();
   }
 
@@ -628,39 +639,48 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   typename Pol::Frag cf[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) cf[s] = typename Pol::Frag{};
+  constexpr int TPC = CRB / 16;   // tiles per staged piece of C rows
 #pragma unroll
-  for (int k = 0; k < G::NCB; ++k) {
-    if (v0 + k * kRB < rows) {
+  for (int k = 0; k < NCB; ++k) {
+    if (v0 + k * CRB < rows) {
       if (k > 0) __syncthreads();
       if constexpr (PREP)
-        store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc,
+        store_rows<Pol, TI, N, R, G::NT, CRB>(cb[k], sm.u.st, sm.tb, (v0 + k * CRB) / R, Lc,
                                               TabPrep<N, R>{&sm.pc});
       else
-        store_rows<Pol, TI, N, R, G::NT, kRB>(cb[k], sm.u.st, sm.tb, (v0 + k * kRB) / R, Lc, NoPrep{});
+        store_rows<Pol, TI, N, R, G::NT, CRB>(cb[k], sm.u.st, sm.tb, (v0 + k * CRB) / R, Lc, NoPrep{});
       __syncthreads();
-      if (lt / 4 == k) {
+      if (lt / TPC == k) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) cf[s] = Pol::frag(sm.u.st, 16 * (lt % 4), s * Pol::KS, lane);
+        for (int s = 0; s < NKS; ++s) cf[s] = Pol::frag(sm.u.st, 16 * (lt % TPC), s * Pol::KS, lane);
       }
     }
   }
+  if constexpr (SMT::LEAN) sb.load(a.S + chunk_id * P * N);
 
-  // Y_off = e^{cs_t} Ct Shat^T
-  __syncthreads();
-  sb.template store<Pol>(sm.u.sh);
-  __syncthreads();
+  // Y_off = e^{cs_t} Ct Shat^T (Shat staged in parts of SHP rows)
+  constexpr int SHP = SMT::SHP, CPS = SHP / 16;   // output column tiles per part
+  static_assert(SHP % 16 == 0 && P % SHP == 0, "Shat parts of whole tiles");
   f4 acc[G::PT];
 #pragma unroll
-  for (int ct = 0; ct < G::PT; ++ct) {
-    f4 d = f4{0, 0, 0, 0};
+  for (int hs = 0; hs < P / SHP; ++hs) {
+    __syncthreads();   // the C rows (or the previous part) are read
+    if constexpr (SHP == P) sb.template store<Pol>(sm.u.sh);
+    else sb.template store_part<Pol, SHP>(sm.u.sh, hs * SHP);
+    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) d = Pol::mma(cf[s], Pol::frag(sm.u.sh, 16 * ct, s * Pol::KS, lane), d);
+    for (int ct = hs * CPS; ct < (hs + 1) * CPS; ++ct) {
+      f4 d = f4{0, 0, 0, 0};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int vv = 16 * tile + 4 * g + jj;
-      d[jj] *= vv < rows ? sm.tb.aux[vv / R] : 0.0f;
+      for (int s = 0; s < NKS; ++s)
+        d = Pol::mma(cf[s], Pol::frag(sm.u.sh, 16 * (ct - hs * CPS), s * Pol::KS, lane), d);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vv = 16 * tile + 4 * g + jj;
+        d[jj] *= vv < rows ? sm.tb.aux[vv / R] : 0.0f;
+      }
+      acc[ct] = d;
     }
-    acc[ct] = d;
   }
 
   // Y_diag: Gram tiles Bt Ct^T (D rows = u, columns = own rows), decay mask,
@@ -674,23 +694,31 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   const double cst = sm.tb.cs[min(tt, kQ - 1)];
   auto stage = [&](int k) {
     if constexpr (PREP)
-      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc,
+      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % NBUF], sm.tb, k * UB / R, Lc,
                                            TabPrep<N, R>{&sm.pb});
     else
-      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % 2], sm.tb, k * UB / R, Lc, NoPrep{});
-    store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % NS], sm.xs[k % 2]);
+      store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % NBUF], sm.tb, k * UB / R, Lc, NoPrep{});
+    store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % NS], sm.xs[k % NBUF]);
     if (k + NS < nkb) {   // the freed slot takes u-block k + NS
       bb[k % NS].template load<true>(Bg, a, b, h, c0, Lc, (k + NS) * UB);
       xb[k % NS].template load<false>(Xg, a, b, h, c0, Lc, (k + NS) * UB);
     }
   };
   __syncthreads();   // Shat's reads are done (the buffers share its space)
-  stage(0);
-  __syncthreads();
+  if constexpr (NBUF == 2) {
+    stage(0);
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 0; k < NKB; ++k) {
     if (k >= nkb) break;
-    if (k + 1 < nkb) stage(k + 1);
+    if constexpr (NBUF == 2) {
+      if (k + 1 < nkb) stage(k + 1);
+    } else {   // one buffer (the previous u-block's reads ended at the loop's barrier)
+      stage(k);
+      __syncthreads();
+    }
+    const int buf = k % NBUF;
     const int ubase = k * UB;
     if (ubase / R <= tmax) {
       // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} for the token u of
@@ -720,7 +748,7 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
         f4 gt = f4{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
-          gt = Pol::mma(Pol::frag(sm.u.bst[k % 2], 16 * dt, s * Pol::KS, lane), cf[s], gt);
+          gt = Pol::mma(Pol::frag(sm.u.bst[buf], 16 * dt, s * Pol::KS, lane), cf[s], gt);
         d[dt] = gt * mk[dt];
       }
 #pragma unroll
@@ -728,7 +756,7 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
         const typename Pol::Frag af = Pol::frag_from_d(d + ug / 16);
 #pragma unroll
         for (int ct = 0; ct < G::PT; ++ct)
-          acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs[k % 2], 16 * ct, ug, lane), acc[ct]);
+          acc[ct] = Pol::mma_x(af, Pol::fragx_d(sm.xs[buf], 16 * ct, ug, lane), acc[ct]);
       }
     }
     __syncthreads();
