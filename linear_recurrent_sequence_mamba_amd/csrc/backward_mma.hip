@@ -1011,9 +1011,21 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   }
 
   // ---- dC back in the raw frame; the phase gradient of every (token, pair)
-  // = the u side (from k_bwd_u, in place) + the C side
+  // = the u side (from k_bwd_u, in place) + the C side.  The u side's values
+  // of this lane's (token, pair) entries are read in one batch first.
   float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
   float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
+  float dpre[NTL][4 / R];
+#pragma unroll
+  for (int j0 = 0; j0 < 4; j0 += R) {
+    const int t = (trow0 + j0) / R;
+    const bool ok = live && trow0 + j0 < rows;
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      const int n = 16 * i + l16;
+      dpre[i][j0 / R] = (ok && !(n & 1)) ? dph[t * NP + (n >> 1)] : 0.0f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NTL; ++i) {
     const int n = 16 * i + l16, kp = n >> 1;
@@ -1044,10 +1056,16 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
-    if (live && !odd)
-      rows_by_token<R>(ph, trow0, [&](int t, float v) {
-        if (t < Lc) dph[t * NP + kp] += v;
-      });
+    if (live && !odd) {
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += R) {
+        float v = dpre[i][j0 / R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) v += ph[j0 + r];
+        const int t = (trow0 + j0) / R;
+        if (t < Lc) dph[t * NP + kp] = v;
+      }
+    }
   }
 }
 
