@@ -124,16 +124,39 @@ __global__ __launch_bounds__(64) void k_bwd_state_pass(BackwardArgs g) {
   const int64_t off = (int64_t)p * N + n;
   f4 G = g.dhT ? *reinterpret_cast<const f4*>(g.dhT + (int64_t)bh * P * N + off) : f4{0, 0, 0, 0};
   const int64_t cbase = (int64_t)bh * a.nchunk;
-  for (int c = a.nchunk - 1; c >= 0; --c) {
-    const int64_t cid = cbase + c;
-    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
-    const f2 r0 = re[n / 2], r1 = re[n / 2 + 1];
-    const float dcy = a.decay[cid];
-    f4* dst = reinterpret_cast<f4*>(g.dS + cid * P * N + off);
-    const f2 g0 = rot_neg(f2{G.x, G.y}, r0), g1 = rot_neg(f2{G.z, G.w}, r1);
-    const f4 D = *dst;
-    G = f4{D.x + dcy * g0.x, D.y + dcy * g0.y, D.z + dcy * g1.x, D.w + dcy * g1.y};
-    *dst = G;
+  // the chunk inputs (D_c, the end rotation and the decay) of the next DP
+  // chunks are in flight while the chain runs: each chunk's slot is written
+  // only after its own read, so the reads never see a written value
+  constexpr int DP = 8;
+  f4 dv[DP];
+  f2 rr0[DP], rr1[DP];
+  float dd[DP];
+  auto load = [&](int k, int q) {   // k-th chunk from the end
+    const int c = a.nchunk - 1 - k;
+    if (c >= 0) {
+      const int64_t cid = cbase + c;
+      const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
+      rr0[q] = re[n / 2];
+      rr1[q] = re[n / 2 + 1];
+      dd[q] = a.decay[cid];
+      dv[q] = *reinterpret_cast<const f4*>(g.dS + cid * P * N + off);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < DP; ++q) load(q, q);
+  for (int k0 = 0; k0 < a.nchunk; k0 += DP) {
+#pragma unroll
+    for (int q = 0; q < DP; ++q) {
+      const int k = k0 + q;
+      if (k < a.nchunk) {
+        const int64_t cid = cbase + (a.nchunk - 1 - k);
+        const f2 g0 = rot_neg(f2{G.x, G.y}, rr0[q]), g1 = rot_neg(f2{G.z, G.w}, rr1[q]);
+        const f4 D = dv[q];
+        G = f4{D.x + dd[q] * g0.x, D.y + dd[q] * g0.y, D.z + dd[q] * g1.x, D.w + dd[q] * g1.y};
+        *reinterpret_cast<f4*>(g.dS + cid * P * N + off) = G;
+        load(k + DP, q);
+      }
+    }
   }
   if (g.dh0) *reinterpret_cast<f4*>(g.dh0 + (int64_t)bh * P * N + off) = G;
 }
