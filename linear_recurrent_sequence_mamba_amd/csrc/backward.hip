@@ -211,8 +211,8 @@ __global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk(BackwardArgs g
   thb.load(a, b, h, c0, Lc);
   chunk_tables<TI, N, kNT3>(a, thb, Lc, sm.tb, sm.ub.scr, 0);
   if (tid < kQ) {
-    sm.lam[tid] = thb.l;
-    sm.Av[tid] = thb.A;
+    sm.lam[tid] = thb.l();
+    sm.Av[tid] = thb.A();
     sm.ecs[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
     sm.dcs[tid] = sm.dgam[tid] = sm.dbpr[tid] = sm.dmend[tid] = 0.0f;
   }

@@ -45,7 +45,7 @@ __device__ __forceinline__ void put_rows(const RowBlock<TI, E * R, R, NT, false,
     int tl, e0;
     RBk::where(vi, tl, e0);
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if constexpr (R == 1) {
       Pol::put8(st, tl, e0, v);
     } else {
@@ -73,7 +73,7 @@ __device__ __forceinline__ void put_xrows(const RowBlock<TI, P * R, R, NT, false
     int tl, e0;
     RBk::where(vi, tl, e0);
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if constexpr (R == 1) {
       Pol::template putxn<4>(xs, tl, e0, v);
       Pol::template putxn<4>(xs, tl, e0 + 4, v + 4);
@@ -107,7 +107,7 @@ __device__ __forceinline__ void put_rows_T(const RowBlock<TI, E * R, R, NT, fals
     const int t = t0 + tl;
     const bool ok = t < Lc;
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if constexpr (ROT) {
       f2 csr[NPAIR];
       tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
@@ -146,7 +146,7 @@ __device__ __forceinline__ void put_rows_both(const RowBlock<TI, E * R, R, NT, f
     RBk::where(vi, tl, e0);
     const int t = t0 + tl;
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if constexpr (ROT) {
       f2 csr[NPAIR];
       tb.template cs_run<NPAIR>(t, e0 / R / 2, t < Lc, csr);
@@ -231,6 +231,10 @@ struct RankRaw<float, R> {
 #pragma unroll
     for (int r = 0; r < R; ++r) o[r] = v[r];
   }
+  __device__ __forceinline__ void get(float* o, bool keep) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) o[r] = keep ? v[r] : 0.0f;
+  }
 };
 template <int R>
 struct RankRaw<bf16_t, R> {
@@ -261,6 +265,13 @@ struct RankRaw<bf16_t, R> {
         o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
       }
     }
+  }
+  // the values, or zeros when keep is false
+  __device__ __forceinline__ void get(float* o, bool keep) const {
+    RankRaw k = *this;
+#pragma unroll
+    for (int i = 0; i < (R + 1) / 2; ++i) k.u[i] = keep ? u[i] : 0u;
+    k.get(o);
   }
 };
 
@@ -506,21 +517,19 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     gpre[i] = Gend ? *reinterpret_cast<const f2*>(Gend + (int64_t)p * N + 2 * kp) : f2{0.0f, 0.0f};
   }
   const int urow0 = 16 * utile + 4 * gq;   // this lane's D rows (u) in the end-state products
+  // (a row past the chunk re-reads its first token and reads as zeros)
   RankRaw<TI, R> bpre[NTL][4 / R], xpre[PT][4 / R];
+  uint32_t uok = 0u;   // bit j0 / R: the D rows urow0 + j0 .. + R - 1 are rows of the chunk
 #pragma unroll
   for (int j0 = 0; j0 < 4; j0 += R) {
-    const int vr = urow0 + j0, ut = vr / R;
+    const int vr = urow0 + j0;
     const bool ok = live && vr < rows;
+    const int ut = ok ? vr / R : 0;
+    uok |= static_cast<uint32_t>(ok) << (j0 / R);
 #pragma unroll
-    for (int i = 0; i < NTL; ++i) {
-      if (ok) bpre[i][j0 / R].load(Bc + (int64_t)ut * G_ * N * R + (int64_t)(16 * i + l16) * R);
-      else bpre[i][j0 / R].zero();
-    }
+    for (int i = 0; i < NTL; ++i) bpre[i][j0 / R].load(Bc + (int64_t)ut * G_ * N * R + (int64_t)(16 * i + l16) * R);
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      if (ok) xpre[i][j0 / R].load(Xc + (int64_t)ut * a.H * P * R + (int64_t)(16 * i + l16) * R);
-      else xpre[i][j0 / R].zero();
-    }
+    for (int i = 0; i < PT; ++i) xpre[i][j0 / R].load(Xc + (int64_t)ut * a.H * P * R + (int64_t)(16 * i + l16) * R);
   }
 
   // ---- walk the t rows at or after this block's first u row
@@ -728,7 +737,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
       for (int s = 0; s < NKS; ++s) v = Pol::mma(bf[s], Pol::frag(sm.u.e.gt, 16 * i, s * KS, lane), v);
       float xv[4];
 #pragma unroll
-      for (int j0 = 0; j0 < 4; j0 += R) xpre[i][j0 / R].get(xv + j0);
+      for (int j0 = 0; j0 < 4; j0 += R) xpre[i][j0 / R].get(xv + j0, (uok >> (j0 / R)) & 1u);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         accx[i][jj] += cu[jj] * v[jj];
@@ -775,7 +784,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
     for (int j0 = 0; j0 < 4; j0 += R) {
       const int vr = urow0 + j0, ut = vr / R;
       const bool ok = live && vr < rows;
-      bpre[i][j0 / R].get(bo + j0);
+      bpre[i][j0 / R].get(bo + j0, (uok >> (j0 / R)) & 1u);
       const f2 c2 = ok ? sm.tb.cs_of(ut, kp) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) cs[j0 + r] = c2;
@@ -897,16 +906,17 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
   // the raw C of this lane's D rows (t) and columns, for the entry-state
   // and phase products: loaded once, now
   const int trow0 = 16 * ttile + 4 * gq;   // this lane's D rows (t) in the dC tiles
+  // (a row past the chunk re-reads its first token and reads as zeros)
   RankRaw<TI, R> cpre[NTL][4 / R];
+  uint32_t tok_rows = 0u;   // bit j0 / R: the D rows trow0 + j0 .. + R - 1 are rows of the chunk
 #pragma unroll
   for (int j0 = 0; j0 < 4; j0 += R) {
     const int vr = trow0 + j0;
     const bool ok = live && vr < rows;
+    const int t = ok ? vr / R : 0;
+    tok_rows |= static_cast<uint32_t>(ok) << (j0 / R);
 #pragma unroll
-    for (int i = 0; i < NTL; ++i) {
-      if (ok) cpre[i][j0 / R].load(Cc + (int64_t)(vr / R) * G_ * N * R + (int64_t)(16 * i + l16) * R);
-      else cpre[i][j0 / R].zero();
-    }
+    for (int i = 0; i < NTL; ++i) cpre[i][j0 / R].load(Cc + (int64_t)t * G_ * N * R + (int64_t)(16 * i + l16) * R);
   }
   // the entry state: q = dY Shat, dCt = e^{cs_t} q, de_t = sum Ct . q
   __syncthreads();   // the own-row buffer is read
@@ -939,7 +949,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       for (int j0 = 0; j0 < 4; j0 += R) {
         const int vr = trow0 + j0, t = vr / R;
         const bool ok = live && vr < rows;
-        cpre[i][j0 / R].get(co + j0);
+        cpre[i][j0 / R].get(co + j0, (tok_rows >> (j0 / R)) & 1u);
         const f2 c2 = ok ? sm.tb.cs_of(t, n >> 1) : f2{1.0f, 0.0f};
         const float e = ok ? sm.ecs[t] : 0.0f;
 #pragma unroll
@@ -1036,7 +1046,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
     for (int j0 = 0; j0 < 4; j0 += R) {
       const int vr = trow0 + j0, t = vr / R;
       const bool ok = live && vr < rows;
-      cpre[i][j0 / R].get(co + j0);
+      cpre[i][j0 / R].get(co + j0, (tok_rows >> (j0 / R)) & 1u);
       const f2 c2 = ok ? sm.tb.cs_of(t, kp) : f2{1.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < R; ++r) cs[j0 + r] = c2;

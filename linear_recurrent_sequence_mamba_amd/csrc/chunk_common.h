@@ -130,6 +130,15 @@ struct Vec8<bf16_t> {
     v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
     v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
   }
+  // the values, or zeros when keep is false
+  __device__ __forceinline__ void get(float* v, bool keep) const {
+    const uint32_t m = keep ? 0xffffffffu : 0u;
+    const uint4 k = uint4{u.x & m, u.y & m, u.z & m, u.w & m};
+    v[0] = __uint_as_float(k.x << 16); v[1] = __uint_as_float(k.x & 0xffff0000u);
+    v[2] = __uint_as_float(k.y << 16); v[3] = __uint_as_float(k.y & 0xffff0000u);
+    v[4] = __uint_as_float(k.z << 16); v[5] = __uint_as_float(k.z & 0xffff0000u);
+    v[6] = __uint_as_float(k.w << 16); v[7] = __uint_as_float(k.w & 0xffff0000u);
+  }
 };
 template <>
 struct Vec8<float> {
@@ -142,6 +151,11 @@ struct Vec8<float> {
   __device__ __forceinline__ void get(float* v) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void get(float* v, bool keep) const {
+    get(v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = keep ? v[j] : 0.0f;
   }
 };
 
@@ -156,6 +170,7 @@ struct RowBlock {
   static constexpr int NV = NTOK * VPT;
   static constexpr int IT = (NV + NT - 1) / NT;
   Vec8<TI> raw[IT];
+  uint32_t okm;   // bit i: raw[i] holds elements of the chunk's rows (else it reads as zeros)
   static __device__ __forceinline__ void where(int vi, int& tl, int& e0) {
     if constexpr (TF) {
       tl = vi % NTOK;
@@ -174,17 +189,21 @@ struct RowBlock {
     // in 32 bits (the launcher checks that a chunk spans < 2^31 elements)
     const TI* __restrict__ base = src + (GRP ? group_index(a, b, c0, h) : token_index(a, b, c0, h)) * E;
     const int tstride = (GRP ? a.G : a.H) * E;
+    // every lane loads (a lane past the rows re-reads the chunk's first
+    // vector and reads as zeros): no branch around a load, so no load waits
+    // for the ones before it
+    okm = 0u;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
       int tl, e0;
       where(vi, tl, e0);
-      if (vi < NV && t0 + tl < Lc)
-        raw[i].load(base + ((t0 + tl) * tstride + e0));
-      else
-        raw[i].zero();
+      const bool ok = vi < NV && t0 + tl < Lc;
+      raw[i].load(base + (ok ? (t0 + tl) * tstride + e0 : 0));
+      okm |= static_cast<uint32_t>(ok) << i;
     }
   }
+  __device__ __forceinline__ void get(int i, float* v) const { raw[i].get(v, (okm >> i) & 1u); }
 };
 
 // Q x N/2 phase inputs of the chunk plus the first wave's token scalars
@@ -195,28 +214,36 @@ struct ThetaBlock {
   static constexpr int NV = kQ * VPT;
   static constexpr int IT = (NV + NT - 1) / NT;
   Vec8<TI> raw[IT];
-  float d, l, A;
+  uint32_t okm;      // bit i: raw[i] holds phases of the chunk's tokens
+  bool tok;          // this thread's token scalars are a token of the chunk
+  float d_, l_, A_;  // as loaded (any value when !tok)
+  // every lane loads from a valid address (the chunk's first token when it
+  // has none of its own) and the values are masked where they are read: no
+  // branch around a load, so no load waits for the ones before it
   __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
     const TI* __restrict__ th = static_cast<const TI*>(a.theta) + group_index(a, b, c0, h) * NP;
     const int tstride = a.G * NP;
+    okm = 0u;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int vi = threadIdx.x + NT * i;
       const int t = vi / VPT, kv = vi % VPT;
-      if (vi < NV && t < Lc)
-        raw[i].load(th + (t * tstride + 8 * kv));
-      else
-        raw[i].zero();
+      const bool ok = vi < NV && t < Lc;
+      raw[i].load(th + (ok ? t * tstride + 8 * kv : 0));
+      okm |= static_cast<uint32_t>(ok) << i;
     }
     const int tid = threadIdx.x;
-    d = l = A = 0.0f;
-    if (tid < Lc) {
-      const int64_t bth = token_index(a, b, c0, h) + tid * a.H;
-      d = ld1(static_cast<const TI*>(a.dt), bth);
-      l = ld1(static_cast<const TI*>(a.lam), bth);
-      A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
-    }
+    tok = tid < Lc;
+    const int64_t bth = token_index(a, b, c0, h) + (tok ? tid : 0) * a.H;
+    d_ = ld1(static_cast<const TI*>(a.dt), bth);
+    l_ = ld1(static_cast<const TI*>(a.lam), bth);
+    A_ = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
   }
+  __device__ __forceinline__ void get(int i, float* v) const { raw[i].get(v, (okm >> i) & 1u); }
+  // dt, lam and A of token threadIdx.x (zero past the chunk)
+  __device__ __forceinline__ float d() const { return tok ? d_ : 0.0f; }
+  __device__ __forceinline__ float l() const { return tok ? l_ : 0.0f; }
+  __device__ __forceinline__ float A() const { return tok ? A_ : 0.0f; }
 };
 
 // The chunk's tables from its loaded inputs: token scalars, the chunk-local
@@ -238,23 +265,24 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
   constexpr int NP = N / 2;
   const int tid = threadIdx.x;
   if (tid < 64) {
-    double lv = (double)tb_in.d * (double)tb_in.A;
+    const float d = tb_in.d(), l = tb_in.l();
+    double lv = (double)d * (double)tb_in.A();
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(lv, off, 64);
       if (tid >= off) lv += o;
     }
     tb.cs[tid] = lv;
-    tb.dt[tid] = tb_in.d;
-    tb.gam[tid] = tb_in.l * tb_in.d;
-    tb.bpr[tid] = (1.0f - tb_in.l) * tb_in.d;
+    tb.dt[tid] = d;
+    tb.gam[tid] = l * d;
+    tb.bpr[tid] = (1.0f - l) * d;
   }
 #pragma unroll
   for (int i = 0; i < ThetaBlock<TI, N, NT>::IT; ++i) {
     const int vi = tid + NT * i;
     if (vi < ThetaBlock<TI, N, NT>::NV) {
       float v[8];
-      tb_in.raw[i].get(v);
+      tb_in.get(i, v);
       const int t = vi / ThetaBlock<TI, N, NT>::VPT, kv = vi % ThetaBlock<TI, N, NT>::VPT;
 #pragma unroll
       for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[j];

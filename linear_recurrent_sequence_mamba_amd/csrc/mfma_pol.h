@@ -292,7 +292,7 @@ __device__ __forceinline__ void store_rows(const RowBlock<TI, N * R, R, NT, fals
     const int t = t0 + tl;
     const bool ok = t < Lc;
     float v[8], o[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if (ok) prep(t, e0, v);
     f2 csr[NPAIR];
     tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
@@ -342,7 +342,7 @@ __device__ __forceinline__ void store_rows_T(const RowBlock<TI, N * R, R, NT, TF
     const bool ok = t < Lc;
     const float wt = ok ? w[t] : 0.0f;
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if (ok) prep(t, e0, v);
     f2 csr[NPAIR];
     tb.template cs_run<NPAIR>(t, e0 / R / 2, ok, csr);
@@ -376,7 +376,7 @@ __device__ __forceinline__ void store_x_T(const RowBlock<TI, P * R, R, NT, TF, R
     int tl, e0;
     RBk::where(vi, tl, e0);
     float v[8];
-    rb.raw[i].get(v);
+    rb.get(i, v);
     if constexpr (R == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) Pol::putx(xs, e0 + j, tl, v[j]);

@@ -160,7 +160,7 @@ __device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, TF, ROWS>
     RBk::where(vi, tl, e0);
     const int t = t0 + tl;
     float v[8], part[R];
-    rb.raw[i].get(v);
+    rb.get(i, v);
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = 0.0f;
 #pragma unroll
