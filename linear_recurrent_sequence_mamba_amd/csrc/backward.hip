@@ -110,50 +110,189 @@ __global__ __launch_bounds__((nt_adjoint<P, N>())) void k_bwd_chunk_adjoint(Back
 }
 
 // --------------------------------------------------------------------------
+// K contiguous input elements of one token row (x or B), as loaded; bf16
+// stays packed until get
+template <typename TI, int K>
+struct RowRaw;
+template <int K>
+struct RowRaw<float, K> {
+  float v[K];
+  __device__ __forceinline__ void load(const float* __restrict__ p) {
+    if constexpr (K % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < K / 4; ++i) {
+        const f4 q = reinterpret_cast<const f4*>(p)[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) v[i] = p[i];
+    }
+  }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = v[i];
+  }
+};
+template <int K>
+struct RowRaw<bf16_t, K> {
+  static constexpr int W = (K + 1) / 2;   // 32-bit words
+  uint32_t u[W];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+    if constexpr (K == 1) {
+      u[0] = p->bits;
+    } else if constexpr (W % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        u[4 * i] = q.x; u[4 * i + 1] = q.y; u[4 * i + 2] = q.z; u[4 * i + 3] = q.w;
+      }
+    } else if constexpr (W == 2) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      u[0] = q.x; u[1] = q.y;
+    } else {
+      u[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    if constexpr (K == 1) {
+      o[0] = __uint_as_float(u[0] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        o[2 * i] = __uint_as_float(u[i] << 16);
+        o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  }
+};
+
 // reverse pass over the chunks of one (batch, head): dShat_c = D_c +
 // decay_c R(-Phi_end,c) dShat_{c+1} (rows), from dShat_C = dh_T; one 4-vector
-// of the state per lane
-template <int N>
+// of the state per lane, the inputs of the next DP chunks in flight.
+//
+// SUMS: each wave also forms its part of three end-state sums of every chunk
+// c, for the per-token gradients (they need G_end = dShat_{c+1}, which the
+// pass holds):
+//   <Gt, Shat_c>, Gt = G_end rotated by -Phi_end (the pass's own rotation);
+//   per pair, <G_end, J S_end>, S_end = Shat_{c+1} (or the final state) less
+//   the next chunk's left-endpoint term (1 - lam) dt x_last B_last^T;
+//   <dShat_c, x_prev B_prev^T> of the token before the chunk;
+// into endp[unit][wave][N/2 + 2] (pairs, then the two scalars).  Shat_{c+1}
+// and the last token's x and B are the previous chunk's reads.
+template <typename TI, int N, int R, bool SUMS>
 __global__ __launch_bounds__(64) void k_bwd_state_pass(BackwardArgs g) {
   const PrefillArgs& a = g.f;
+  constexpr int NP = N / 2, LPR = N / 4;   // lanes per state row
   const int P = a.P;
   const int wpb = P * N / 4 / 64;
-  const int bh = blockIdx.x / wpb;
-  const int vi = (blockIdx.x % wpb) * 64 + threadIdx.x;
-  const int p = vi / (N / 4), n = 4 * (vi % (N / 4));
+  const int bh = blockIdx.x / wpb, w = blockIdx.x % wpb;
+  const int lane = threadIdx.x;
+  const int vi = w * 64 + lane;
+  const int p = vi / LPR, n = 4 * (vi % LPR);
   const int64_t off = (int64_t)p * N + n;
+  const int nch = a.nchunk;
   f4 G = g.dhT ? *reinterpret_cast<const f4*>(g.dhT + (int64_t)bh * P * N + off) : f4{0, 0, 0, 0};
-  const int64_t cbase = (int64_t)bh * a.nchunk;
-  // the chunk inputs (D_c, the end rotation and the decay) of the next DP
-  // chunks are in flight while the chain runs: each chunk's slot is written
-  // only after its own read, so the reads never see a written value
-  constexpr int DP = 8;
-  f4 dv[DP];
+  const int64_t cbase = (int64_t)bh * nch;
+  const int b = bh / a.H, h = bh % a.H;
+  // the chunk inputs of the next DP chunks are in flight while the chain
+  // runs; each chunk's slot of dS is written only after its own read.  Loads
+  // past chunk 0 re-read chunk 0 (no branch around a load).
+  constexpr int DP = !SUMS ? 8 : R >= 4 ? 4 : 6;   // within two waves per SIMD
+  f4 dv[DP], sv[DP];
   f2 rr0[DP], rr1[DP];
-  float dd[DP];
+  float dd[DP], bpn[DP];
+  RowRaw<TI, R> xq[DP];
+  RowRaw<TI, 4 * R> bq[DP];
+  const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
+  const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   auto load = [&](int k, int q) {   // k-th chunk from the end
-    const int c = a.nchunk - 1 - k;
-    if (c >= 0) {
-      const int64_t cid = cbase + c;
-      const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * (N / 2);
-      rr0[q] = re[n / 2];
-      rr1[q] = re[n / 2 + 1];
-      dd[q] = a.decay[cid];
-      dv[q] = *reinterpret_cast<const f4*>(g.dS + cid * P * N + off);
+    const int c = max(nch - 1 - k, 0);
+    const int64_t cid = cbase + c;
+    const f2* re = reinterpret_cast<const f2*>(a.rot_end) + cid * NP;
+    rr0[q] = re[n / 2];
+    rr1[q] = re[n / 2 + 1];
+    dd[q] = a.decay[cid];
+    dv[q] = *reinterpret_cast<const f4*>(g.dS + cid * P * N + off);
+    if constexpr (SUMS) {
+      sv[q] = *reinterpret_cast<const f4*>(a.S + cid * P * N + off);
+      // the token before chunk c (chunk 0: the one before the sequence,
+      // read only with has_prev) and the next chunk's left-endpoint weight
+      const int tp = max(c * kQ - 1, 0);
+      const TI* xs = (c == 0 && a.has_prev) ? static_cast<const TI*>(a.xp) + (int64_t)bh * P * R
+                                           : Xg + token_index(a, b, tp, h) * P * R;
+      const TI* bs = (c == 0 && a.has_prev) ? static_cast<const TI*>(a.Bp) + ((int64_t)b * a.G + head_group(a, h)) * N * R
+                                           : Bg + group_index(a, b, tp, h) * N * R;
+      xq[q].load(xs + (int64_t)p * R);
+      bq[q].load(bs + (int64_t)n * R);
+      const int64_t tn = token_index(a, b, min((c + 1) * kQ, a.T - 1), h);
+      bpn[q] = (1.0f - ldy<TI>(a.lam, tn)) * ldy<TI>(a.dt, tn);
     }
   };
 #pragma unroll
   for (int q = 0; q < DP; ++q) load(q, q);
-  for (int k0 = 0; k0 < a.nchunk; k0 += DP) {
+  f4 Snx = f4{0, 0, 0, 0};            // S_end of the chunk: the next entry state (raw)
+  float xl[R] = {}, bl[4][R] = {};    // x and B of the chunk's last token
+  if constexpr (SUMS) Snx = *reinterpret_cast<const f4*>(g.hTw + (int64_t)bh * P * N + off);
+  float* __restrict__ ep = SUMS ? g.endp + (cbase * wpb + w) * (NP + 2) : nullptr;
+  for (int k0 = 0; k0 < nch; k0 += DP) {
 #pragma unroll
     for (int q = 0; q < DP; ++q) {
       const int k = k0 + q;
-      if (k < a.nchunk) {
-        const int64_t cid = cbase + (a.nchunk - 1 - k);
+      if (k < nch) {
+        const int c = nch - 1 - k;
+        const int64_t cid = cbase + c;
         const f2 g0 = rot_neg(f2{G.x, G.y}, rr0[q]), g1 = rot_neg(f2{G.z, G.w}, rr1[q]);
         const f4 D = dv[q];
-        G = f4{D.x + dd[q] * g0.x, D.y + dd[q] * g0.y, D.z + dd[q] * g1.x, D.w + dd[q] * g1.y};
-        *reinterpret_cast<f4*>(g.dS + cid * P * N + off) = G;
+        const f4 Gn = f4{D.x + dd[q] * g0.x, D.y + dd[q] * g0.y, D.z + dd[q] * g1.x, D.w + dd[q] * g1.y};
+        *reinterpret_cast<f4*>(g.dS + cid * P * N + off) = Gn;
+        if constexpr (SUMS) {
+          const f4 Sh = sv[q];
+          float e = g0.x * Sh.x + g0.y * Sh.y + g1.x * Sh.z + g1.y * Sh.w;
+          f4 se = Snx;
+          if (k > 0) {   // a next chunk: its first token's left-endpoint term
+            const float bp = bpn[q];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const float xv = bp * xl[r];
+              se.x -= xv * bl[0][r];
+              se.y -= xv * bl[1][r];
+              se.z -= xv * bl[2][r];
+              se.w -= xv * bl[3][r];
+            }
+          }
+          float ph0 = -G.x * se.y + G.y * se.x, ph1 = -G.z * se.w + G.w * se.z;
+          // the token before the chunk (this chunk's x_prev, B_prev)
+          float xv[R], bv[4 * R];
+          xq[q].get(xv);
+          bq[q].get(bv);
+          float hs = 0.0f;
+          if (c > 0 || a.has_prev) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              hs += xv[r] * (Gn.x * bv[r] + Gn.y * bv[R + r] + Gn.z * bv[2 * R + r] + Gn.w * bv[3 * R + r]);
+          }
+          // the next step's chunk ends with this token
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            xl[r] = xv[r];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bl[j][r] = bv[j * R + r];
+          }
+          Snx = Sh;
+          // this wave's part: pairs summed over the wave's rows, scalars over all
+#pragma unroll
+          for (int o = LPR; o < 64; o <<= 1) {
+            ph0 += __shfl_xor(ph0, o, 64);
+            ph1 += __shfl_xor(ph1, o, 64);
+          }
+          e = group_sum<64>(e);
+          hs = group_sum<64>(hs);
+          float* __restrict__ eo = ep + (int64_t)c * wpb * (NP + 2);
+          if (lane < LPR) *reinterpret_cast<f2*>(eo + n / 2) = f2{ph0, ph1};
+          if (lane == 0) *reinterpret_cast<f2*>(eo + NP) = f2{e, hs};
+        }
+        G = Gn;
         load(k + DP, q);
       }
     }
@@ -640,7 +779,7 @@ hipError_t run_backward(const BackwardArgs& g, int in_bf16, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_chunk_adjoint<TI, TY, P, N, R>), grid, dim3(nt_adjoint<P, N>()), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = launch_bwd_state_pass(g, s)) != hipSuccess) return e;
+  if ((e = launch_bwd_state_pass(g, in_bf16, s)) != hipSuccess) return e;
   static_assert(R == 1, "single input");
   hipLaunchKernelGGL((k_bwd_chunk<TI, TY, P, N>), grid, dim3(BwdGeo<P, N>::NT), 0, s, g);
   return hipGetLastError();
@@ -688,14 +827,32 @@ size_t align256b(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
 
-hipError_t launch_bwd_state_pass(const BackwardArgs& g, hipStream_t s) {
+template <typename TI>
+static hipError_t state_pass_sums(const BackwardArgs& g, const dim3& grid, hipStream_t s) {
+  const PrefillArgs& a = g.f;
+#define M3_PASS(NN, RR)                                                                   \
+  if (a.N == NN && a.R == RR) {                                                           \
+    hipLaunchKernelGGL((k_bwd_state_pass<TI, NN, RR, true>), grid, dim3(64), 0, s, g);   \
+    return hipGetLastError();                                                             \
+  }
+  M3_PASS(128, 1)
+  M3_PASS(128, 2)
+  M3_PASS(128, 4)
+  M3_PASS(64, 1)
+  M3_PASS(64, 4)
+#undef M3_PASS
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_state_pass(const BackwardArgs& g, int in_bf16, hipStream_t s) {
   const PrefillArgs& a = g.f;
   if (a.P * a.N % 256 != 0) return hipErrorInvalidValue;   // whole waves per (batch, head)
   const dim3 grid(a.Bsz * a.H * (a.P * a.N / 256));
+  if (g.endp) return in_bf16 ? state_pass_sums<bf16_t>(g, grid, s) : state_pass_sums<float>(g, grid, s);
   switch (a.N) {
-    case 16: hipLaunchKernelGGL((k_bwd_state_pass<16>), grid, dim3(64), 0, s, g); break;
-    case 64: hipLaunchKernelGGL((k_bwd_state_pass<64>), grid, dim3(64), 0, s, g); break;
-    case 128: hipLaunchKernelGGL((k_bwd_state_pass<128>), grid, dim3(64), 0, s, g); break;
+    case 16: hipLaunchKernelGGL((k_bwd_state_pass<float, 16, 1, false>), grid, dim3(64), 0, s, g); break;
+    case 64: hipLaunchKernelGGL((k_bwd_state_pass<float, 64, 1, false>), grid, dim3(64), 0, s, g); break;
+    case 128: hipLaunchKernelGGL((k_bwd_state_pass<float, 128, 1, false>), grid, dim3(64), 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -709,22 +866,23 @@ bool backward_supported(int P, int N, int R, int Q) {
 
 // forward part, the chunk adjoints (P N per chunk), h_T, the per-chunk dA
 // partials and, with head groups, per-head B, C, theta and B_prev gradients
-static constexpr int kParts = 10;
+static constexpr int kParts = 11;
 static size_t bwd_parts(int Bsz, int T, int H, int P, int N, int R, int G, int Q, size_t* off) {
   const size_t nchunk = (size_t)(T + Q - 1) / Q;
   const size_t units = (size_t)Bsz * H * nchunk;
   const size_t tokens = (size_t)Bsz * T;
   size_t sz[kParts] = {prefill_workspace_bytes(Bsz, T, H, P, N, R, Q, false), units * P * N * 4,
-                       (size_t)Bsz * H * P * N * 4, units * 4, 0, 0, 0, 0, 0, 0};
+                       (size_t)Bsz * H * P * N * 4, units * 4, 0, 0, 0, 0, 0, 0, 0};
   if (G != H) {
     sz[4] = tokens * H * N * R * 4;
     sz[5] = tokens * H * N * R * 4;
     sz[6] = tokens * H * (N / 2) * 4;
     sz[7] = (size_t)Bsz * H * N * R * 4;
   }
-  if (!(P == 16 && N == 16)) {   // the matrix-core kernels' token sums and phase gradients
-    sz[8] = units * 10 * Q * 4;
+  if (!(P == 16 && N == 16)) {   // the matrix-core kernels' token sums, phase gradients, end sums
+    sz[8] = units * kBwdTokSums * Q * 4;
     sz[9] = units * Q * (N / 2) * 4;
+    sz[10] = units * (P * N / 256) * (N / 2 + 2) * 4;
   }
   size_t total = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -755,6 +913,7 @@ void backward_carve(BackwardArgs& g, void* ws) {
   const bool mma = !(a.P == 16 && a.N == 16);
   g.tokw = mma ? reinterpret_cast<float*>(p + off[8]) : nullptr;
   g.dphiB = mma ? reinterpret_cast<float*>(p + off[9]) : nullptr;
+  g.endp = mma ? reinterpret_cast<float*>(p + off[10]) : nullptr;
 }
 
 int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {

@@ -14,7 +14,8 @@
 //   dM[t, u] = sum over the R x R rank pairs of K1 o K2
 // Launches after the forward states (which launch_backward runs):
 //  k_bwd_adjoint_mma (batch, head, chunk): sum_t e^{cs_t} dY_t Ct_t^T;
-//  k_bwd_state_pass  (backward.hip): the reverse pass over chunks;
+//  k_bwd_state_pass  (backward.hip): the reverse pass over chunks, with
+//           each chunk's end-state sums;
 //  k_bwd_u  (batch, head, chunk [x 2]): one wave per 16 u rows, walking the
 //           t rows at or after them: dx, dB, the mask's column sums, the
 //           u side of the phase gradient;
@@ -384,12 +385,10 @@ struct GeoU {
 };
 
 // per-chunk token sums in the workspace: [units][kTokSums][Q]
-// (slots 7 and 8: each half's part of the end rotation's phase gradient per
-// pair; slot 9: the halves' <Gt, Shat> and previous-token sums)
 enum TokSum {
-  kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5, kDe = 6,
-  kDphiE0 = 7, kDphiE1 = 8, kEndSums = 9, kTokSums = 10
+  kMcol = 0, kEcol = 1, kEdiag = 2, kRrow0 = 3, kRrow1 = 4, kDmend = 5, kDe = 6, kTokSums = 7
 };
+static_assert(kTokSums == kBwdTokSums, "token sum slots");
 
 template <class Pol, int P, int N, int R>
 struct USmem {
@@ -639,82 +638,20 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 
   // ---- the end state: Gt = rows of G_end rotated by -Phi_end, in both
   // layouts (the staging buffers are free: the row sums above are past a
-  // barrier)
-  // The chunk's end-state sums ride along, over this block's share of the
-  // pairs (half of them each when the other half of a split chunk runs):
-  // <Gt, Shat>, the end rotation's phase gradient <G_end, J S_end> per pair
-  // (S_end = the next entry state without the crossing left-endpoint term)
-  // and the previous token's <dShat_c, x_{c0-1} B_{c0-1}^T>.
+  // barrier).  The chunk's end-state sums come from the reverse state pass.
   const f2* __restrict__ re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
-  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) *
-                                  ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
+  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) * ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
                             : 0.0f;
-  static_assert(NT % NP == 0 && GPT % 2 == 0, "a thread's pairs share one column pair");
-  const bool both = G::SPLIT == 2 && rows > G::BROWS;   // the other half runs too
-  const int i_lo = both ? half * (GPT / 2) : 0, i_hi = both ? i_lo + GPT / 2 : GPT;
-  const TI* xprev = nullptr;
-  const TI* bprev = nullptr;
-  if (c > 0) {
-    xprev = Xc - (int64_t)a.H * P * R;
-    bprev = Bc - (int64_t)G_ * N * R;
-  } else if (a.has_prev) {
-    xprev = static_cast<const TI*>(a.xp) + ((int64_t)b * a.H + h) * P * R;
-    bprev = static_cast<const TI*>(a.Bp) + ((int64_t)b * G_ + head_group(a, h)) * N * R;
-  }
-  const float* __restrict__ Sh = a.S + ck.id * (P * N);
-  const float* __restrict__ Snext = last ? g.hTw + ((int64_t)b * a.H + h) * P * N : a.S + (ck.id + 1) * (P * N);
-  const float* __restrict__ dSc = g.dS + ck.id * (P * N);
-  const TI* __restrict__ Blast = Bc + (int64_t)(Lc - 1) * G_ * N * R;
-  const TI* __restrict__ Xlast = Xc + (int64_t)(Lc - 1) * a.H * P * R;
-  float e_part = 0.0f, h_part = 0.0f, ph_part = 0.0f;
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
     const int e = tid + NT * i, p = e / NP, kp = e % NP;
-    const f2 gv = gpre[i];
-    const f2 gt = rot_neg(gv, re[kp]);
+    const f2 gt = rot_neg(gpre[i], re[kp]);
     const float v2[2] = {gt.x, gt.y};
     Pol::template putn<2>(sm.u.e.gt, p, 2 * kp, v2);
     Pol::put(sm.u.e.gtt, 2 * kp, p, gt.x);
     Pol::put(sm.u.e.gtt, 2 * kp + 1, p, gt.y);
-    if (i >= i_lo && i < i_hi) {
-      const f2 sh = *reinterpret_cast<const f2*>(Sh + (int64_t)p * N + 2 * kp);
-      e_part += gt.x * sh.x + gt.y * sh.y;
-      f2 se = *reinterpret_cast<const f2*>(Snext + (int64_t)p * N + 2 * kp);
-      if (ck.next) {
-        float xl[R], b0[R], b1[R];
-        ldr<R>(Xlast + (int64_t)p * R, xl);
-        ldr<R>(Blast + (int64_t)(2 * kp) * R, b0);
-        ldr<R>(Blast + (int64_t)(2 * kp + 1) * R, b1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          se.x -= bpL * xl[r] * b0[r];
-          se.y -= bpL * xl[r] * b1[r];
-        }
-      }
-      ph_part += -gv.x * se.y + gv.y * se.x;
-      if (xprev) {
-        const f2 ds = *reinterpret_cast<const f2*>(dSc + (int64_t)p * N + 2 * kp);
-        float xq[R], b0[R], b1[R];
-        ldr<R>(xprev + (int64_t)p * R, xq);
-        ldr<R>(bprev + (int64_t)(2 * kp) * R, b0);
-        ldr<R>(bprev + (int64_t)(2 * kp + 1) * R, b1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) h_part += xq[r] * (ds.x * b0[r] + ds.y * b1[r]);
-      }
-    }
   }
-  sm.part[tid] = ph_part;
-  const float e_end = block_sum<NT>(e_part, sm.red);
-  const float h_end = block_sum<NT>(h_part, sm.red);   // also orders the LDS writes above
-  if (tid < NP) {
-    float v = 0.0f;
-    for (int m = 0; m < NT / NP; ++m) v += sm.part[tid + NP * m];
-    tk[(kDphiE0 + half) * kQ + tid] = v;
-  }
-  if (tid == 0) {
-    tk[kEndSums * kQ + half] = e_end;
-    tk[kEndSums * kQ + 2 + half] = h_end;
-  }
+  __syncthreads();
   const double cs_end = sm.tb.cs[Lc - 1];
   float mu[4], cu[4];
 #pragma unroll
@@ -1090,7 +1027,7 @@ struct FinSmem {
   double cs[kQ];
   float dt[kQ], lam[kQ], Av[kQ], gam[kQ], bpr[kQ];
   float dcs[kQ], dgam[kQ], dbpr[kQ], part[NT];
-  float dphi_end[NP];
+  float dphi_end[NP + 2];   // the end rotation's phase gradient per pair, then two sums
   float red[NT / 64];
   float dphi[kQ][NP + 1];
 };
@@ -1134,14 +1071,21 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   const float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
   for (int i = tid; i < Lc * NP; i += NT) sm.dphi[i / NP][i % NP] = dph[i];
 
-  // the end state's sums from the u side (one part per half of a split chunk)
+  // the end state's sums: the state pass waves' parts, in wave order
   using GU = GeoU<P, N, R>;
   const float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
-  const bool both = GU::SPLIT == 2 && Lc * R > GU::BROWS;
-  const float e_end = tk[kEndSums * kQ] + (both ? tk[kEndSums * kQ + 1] : 0.0f);
-  const float h_end = tk[kEndSums * kQ + 2] + (both ? tk[kEndSums * kQ + 3] : 0.0f);
-  if (tid < NP) sm.dphi_end[tid] = tk[kDphiE0 * kQ + tid] + (both ? tk[kDphiE1 * kQ + tid] : 0.0f);
-  __syncthreads();   // the tables, dphi and dphi_end are in
+  {
+    constexpr int WPB = P * N / 256, EW = NP + 2;
+    const float* __restrict__ ep = g.endp + ck.id * (WPB * EW);
+    if (tid < EW) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPB; ++w) v += ep[w * EW + tid];
+      sm.dphi_end[tid] = v;   // pairs, then <Gt, Shat> and the previous token's sum
+    }
+  }
+  __syncthreads();   // the tables, dphi and the end sums are in
+  const float e_end = sm.dphi_end[NP], h_end = sm.dphi_end[NP + 1];
 
   // ---- the token sums: log-decay (cs), trapezoid weights (gamma, beta')
   const double cs_end = sm.cs[Lc - 1];
@@ -1270,7 +1214,7 @@ hipError_t run_mma(const BackwardArgs& g, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_adjoint_mma<Pol, TI, TY, P, N, R>), grid, dim3(AdjGeo<P, N>::NT), 0, s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = launch_bwd_state_pass(g, s)) != hipSuccess) return e;
+  if ((e = launch_bwd_state_pass(g, std::is_same<TI, bf16_t>::value, s)) != hipSuccess) return e;
   using GU = GeoU<P, N, R>;
   const int nx = GU::SPLIT == 1 ? a.nchunk : GU::SPLIT * ((a.nchunk + 7) / 8) * 8;
   hipLaunchKernelGGL((k_bwd_u<Pol, TI, TY, P, N, R>), dim3(nx, a.H, a.Bsz), dim3(GU::NT), 0, s, g);

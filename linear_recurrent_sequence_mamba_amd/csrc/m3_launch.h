@@ -107,10 +107,12 @@ struct BackwardArgs {
   // workspace: per-chunk dA partials; with head groups, per-head gradients
   // of B, C, theta and B_prev before the fixed-order sum over each group
   float *dApart, *dBh, *dCh, *dthh, *dBph;
-  // workspace of the matrix-core kernels: per-chunk token and end-state sums
-  // [units, 10, Q] and phase gradients [units, Q, N/2]
-  float *tokw, *dphiB;
+  // workspace of the matrix-core kernels: per-chunk token sums
+  // [units, kBwdTokSums, Q], phase gradients [units, Q, N/2] and each state
+  // pass wave's part of the end-state sums [units, P N / 256, N/2 + 2]
+  float *tokw, *dphiB, *endp;
 };
+constexpr int kBwdTokSums = 7;
 bool backward_supported(int P, int N, int R, int Q);
 size_t backward_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int G, int Q);
 void backward_carve(BackwardArgs& a, void* ws);
@@ -119,8 +121,9 @@ int launch_backward(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t
 // forward states): 0 when launched (*e = the launch status), -1 when the
 // shape has no such kernels
 int launch_backward_mma(const BackwardArgs& a, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e);
-// the reverse pass over chunks turning chunk adjoints into dL/dShat_c (and dh0)
-hipError_t launch_bwd_state_pass(const BackwardArgs& a, hipStream_t s);
+// the reverse pass over chunks turning chunk adjoints into dL/dShat_c (and
+// dh0); with a.endp also the end-state sums of every chunk
+hipError_t launch_bwd_state_pass(const BackwardArgs& a, int in_bf16, hipStream_t s);
 
 // builds seqs and cmap from the sequence offsets cu [Bsz + 1] (device)
 hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s);
