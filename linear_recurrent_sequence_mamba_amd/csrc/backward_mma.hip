@@ -530,6 +530,12 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) xpre[i][j0 / R].load(Xc + (int64_t)ut * a.H * P * R + (int64_t)(16 * i + l16) * R);
   }
+  // this thread's end rotation (the pair tid % NP of every G_end pair it
+  // holds) and the next chunk's left-endpoint weight, also for after the walk
+  static_assert(NT % NP == 0, "a thread's G_end pairs share one column pair");
+  const f2 rek = reinterpret_cast<const f2*>(a.rot_end)[ck.id * NP + tid % NP];
+  const int64_t tnx = ti0 + (int64_t)(ck.next ? kQ : 0) * a.H;   // (a valid token when there is none)
+  const float lam_n = ldy<TI>(a.lam, tnx), dt_n = ldy<TI>(a.dt, tnx);
 
   // ---- walk the t rows at or after this block's first u row
   f4 accx[PT], accb[NTL];
@@ -639,13 +645,11 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_u(BackwardArgs g) {
   // ---- the end state: Gt = rows of G_end rotated by -Phi_end, in both
   // layouts (the staging buffers are free: the row sums above are past a
   // barrier).  The chunk's end-state sums come from the reverse state pass.
-  const f2* __restrict__ re = reinterpret_cast<const f2*>(a.rot_end) + ck.id * NP;
-  const float bpL = ck.next ? (1.0f - ldy<TI>(a.lam, ti0 + (int64_t)kQ * a.H)) * ldy<TI>(a.dt, ti0 + (int64_t)kQ * a.H)
-                            : 0.0f;
+  const float bpL = ck.next ? (1.0f - lam_n) * dt_n : 0.0f;
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
     const int e = tid + NT * i, p = e / NP, kp = e % NP;
-    const f2 gt = rot_neg(gpre[i], re[kp]);
+    const f2 gt = rot_neg(gpre[i], rek);
     const float v2[2] = {gt.x, gt.y};
     Pol::template putn<2>(sm.u.e.gt, p, 2 * kp, v2);
     Pol::put(sm.u.e.gtt, 2 * kp, p, gt.x);
@@ -959,25 +963,26 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
 
   // ---- dC back in the raw frame; the phase gradient of every (token, pair)
   // = the u side (from k_bwd_u, in place) + the C side.  The u side's values
-  // of this lane's (token, pair) entries are read in one batch first.
+  // of this lane's (token, pair) entries are read in one batch first (every
+  // lane reads; an odd column or a row past the chunk re-reads a valid entry
+  // and drops it).  All values are formed (in acc and dpre, in place) before
+  // the first store: a use of a loaded value after a store would wait for
+  // the store too.
   float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
   float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
   float dpre[NTL][4 / R];
 #pragma unroll
   for (int j0 = 0; j0 < 4; j0 += R) {
-    const int t = (trow0 + j0) / R;
     const bool ok = live && trow0 + j0 < rows;
+    const int t = ok ? (trow0 + j0) / R : 0;
 #pragma unroll
-    for (int i = 0; i < NTL; ++i) {
-      const int n = 16 * i + l16;
-      dpre[i][j0 / R] = (ok && !(n & 1)) ? dph[t * NP + (n >> 1)] : 0.0f;
-    }
+    for (int i = 0; i < NTL; ++i) dpre[i][j0 / R] = dph[t * NP + ((16 * i + l16) >> 1)];
   }
 #pragma unroll
   for (int i = 0; i < NTL; ++i) {
     const int n = 16 * i + l16, kp = n >> 1;
     const bool odd = n & 1;
-    float co[4], raw[4], ph[4];
+    float co[4], ph[4];
     f2 cs[4];
 #pragma unroll
     for (int j0 = 0; j0 < 4; j0 += R) {
@@ -994,23 +999,34 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
       const float cq = __shfl_xor(co[jj], 1, 64);
       ph[jj] = odd ? -dct * rot_own(cq, co[jj], false, cs[jj]) : dct * rot_own(cq, co[jj], true, cs[jj]);
       const float pv = __shfl_xor(dct, 1, 64);
-      raw[jj] = odd ? cs[jj].y * pv + cs[jj].x * dct : cs[jj].x * dct - cs[jj].y * pv;
-    }
-#pragma unroll
-    for (int j0 = 0; j0 < 4; j0 += R) {
-      const int vr = trow0 + j0;
-      if (live && vr < rows) str<R>(dCo + (ti0 + (int64_t)(vr / R) * a.H) * N * R + (int64_t)n * R, raw + j0);
+      acc[i][jj] = odd ? cs[jj].y * pv + cs[jj].x * dct : cs[jj].x * dct - cs[jj].y * pv;
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) ph[jj] += __shfl_xor(ph[jj], 1, 64);
-    if (live && !odd) {
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      float v = dpre[i][j0 / R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) v += ph[j0 + r];
+      dpre[i][j0 / R] = v;
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      const int n = 16 * i + l16;
+      const float raw[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
 #pragma unroll
       for (int j0 = 0; j0 < 4; j0 += R) {
-        float v = dpre[i][j0 / R];
+        const int vr = trow0 + j0;
+        if (vr < rows) str<R>(dCo + (ti0 + (int64_t)(vr / R) * a.H) * N * R + (int64_t)n * R, raw + j0);
+      }
+      if (!(n & 1)) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) v += ph[j0 + r];
-        const int t = (trow0 + j0) / R;
-        if (t < Lc) dph[t * NP + kp] = v;
+        for (int j0 = 0; j0 < 4; j0 += R) {
+          const int t = (trow0 + j0) / R;
+          if (trow0 + j0 < rows) dph[t * NP + (n >> 1)] = dpre[i][j0 / R];
+        }
       }
     }
   }
@@ -1045,15 +1061,25 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   const int G_ = a.G;
   const bool shared_grp = G_ != a.H;
   const int64_t gi = group_index(a, b, c0, h), ti0 = token_index(a, b, c0, h);
+  // every global read of the token phase goes out first, from every thread
+  // (thread tid reads token tid % 64; a token past the chunk reads token 0
+  // and drops it): no branch around a load
+  const int ut = tid & 63;
+  const bool uok = ut < Lc;
+  const int64_t bth = ti0 + (int64_t)(uok ? ut : 0) * a.H;
+  const float d_in = ld1(static_cast<const TI*>(a.dt), bth);
+  const float l_in = ld1(static_cast<const TI*>(a.lam), bth);
+  const float A_in = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
+  const float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
+  using GU = GeoU<P, N, R>;
+  const bool both_rows = GU::SPLIT == 2 && Lc * R > GU::BROWS;
+  const float t_dmend = tk[kDmend * kQ + ut], t_rr0 = tk[kRrow0 * kQ + ut];
+  const float t_rr1 = both_rows ? tk[kRrow1 * kQ + ut] : 0.0f;
+  const float t_ecol = tk[kEcol * kQ + ut], t_mcol = tk[kMcol * kQ + ut];
+  const float t_de = tk[kDe * kQ + ut], t_edg = tk[kEdiag * kQ + ut];
   // token scalars and the chunk-local log-decay prefix (double)
   if (tid < 64) {
-    float d = 0.0f, l = 0.0f, A = 0.0f;
-    if (tid < Lc) {
-      const int64_t bth = ti0 + (int64_t)tid * a.H;
-      d = ld1(static_cast<const TI*>(a.dt), bth);
-      l = ld1(static_cast<const TI*>(a.lam), bth);
-      A = (a.flags & kAPerToken) ? a.A[bth] : a.A[h];
-    }
+    const float d = uok ? d_in : 0.0f, l = uok ? l_in : 0.0f, A = uok ? A_in : 0.0f;
     double lv = (double)d * (double)A;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1072,8 +1098,6 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
   for (int i = tid; i < Lc * NP; i += NT) sm.dphi[i / NP][i % NP] = dph[i];
 
   // the end state's sums: the state pass waves' parts, in wave order
-  using GU = GeoU<P, N, R>;
-  const float* __restrict__ tk = g.tokw + ck.id * (kTokSums * kQ);
   {
     constexpr int WPB = P * N / 256, EW = NP + 2;
     const float* __restrict__ ep = g.endp + ck.id * (WPB * EW);
@@ -1095,12 +1119,11 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
     if (u < Lc) {
       const float e = expf((float)(cs_end - sm.cs[u]));
       const float m = e * (sm.gam[u] + (u < Lc - 1 ? sm.bpr[u + 1] : 0.0f));
-      const float d = tk[kDmend * kQ + u];
-      float rr = tk[kRrow0 * kQ + u];
-      if (GU::SPLIT == 2 && Lc * R > GU::BROWS) rr += tk[kRrow1 * kQ + u];
-      const float ec = tk[kEcol * kQ + u];
-      dc = rr - tk[kMcol * kQ + u] + expf((float)sm.cs[u]) * tk[kDe * kQ + u];
-      dg = ec + tk[kEdiag * kQ + u] + d * e;
+      const float d = t_dmend;
+      const float rr = t_rr0 + t_rr1;
+      const float ec = t_ecol;
+      dc = rr - t_mcol + expf((float)sm.cs[u]) * t_de;
+      dg = ec + t_edg + d * e;
       dbn = ec;
       if (u < Lc - 1) {
         pm = d * m;
@@ -1155,11 +1178,14 @@ __global__ __launch_bounds__(kFinNT) void k_bwd_fin(BackwardArgs g) {
     const TI* __restrict__ th = static_cast<const TI*>(a.theta) + grp * NP;
     const float dtt = sm.dt[tt];
     float* __restrict__ dth = shared_grp ? g.dthh + tok * NP : g.dtheta + grp * NP;
+    float thv[KPT];   // read before the stores below (a read after a store waits for it)
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) thv[j] = ld1(th, cg * KPT + j);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int k = cg * KPT + j;
       const float dphv = sm.dphi[tt][k];
-      if (!angle) dt_theta += ld1(th, k) * dphv;
+      if (!angle) dt_theta += thv[j] * dphv;
       dth[k] = angle ? dphv : dtt * dphv;
     }
   }
