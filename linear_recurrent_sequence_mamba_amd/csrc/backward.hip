@@ -110,63 +110,6 @@ __global__ __launch_bounds__((nt_adjoint<P, N>())) void k_bwd_chunk_adjoint(Back
 }
 
 // --------------------------------------------------------------------------
-// K contiguous input elements of one token row (x or B), as loaded; bf16
-// stays packed until get
-template <typename TI, int K>
-struct RowRaw;
-template <int K>
-struct RowRaw<float, K> {
-  float v[K];
-  __device__ __forceinline__ void load(const float* __restrict__ p) {
-    if constexpr (K % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < K / 4; ++i) {
-        const f4 q = reinterpret_cast<const f4*>(p)[i];
-        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < K; ++i) v[i] = p[i];
-    }
-  }
-  __device__ __forceinline__ void get(float* o) const {
-#pragma unroll
-    for (int i = 0; i < K; ++i) o[i] = v[i];
-  }
-};
-template <int K>
-struct RowRaw<bf16_t, K> {
-  static constexpr int W = (K + 1) / 2;   // 32-bit words
-  uint32_t u[W];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
-    if constexpr (K == 1) {
-      u[0] = p->bits;
-    } else if constexpr (W % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < W / 4; ++i) {
-        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
-        u[4 * i] = q.x; u[4 * i + 1] = q.y; u[4 * i + 2] = q.z; u[4 * i + 3] = q.w;
-      }
-    } else if constexpr (W == 2) {
-      const uint2 q = *reinterpret_cast<const uint2*>(p);
-      u[0] = q.x; u[1] = q.y;
-    } else {
-      u[0] = *reinterpret_cast<const uint32_t*>(p);
-    }
-  }
-  __device__ __forceinline__ void get(float* o) const {
-    if constexpr (K == 1) {
-      o[0] = __uint_as_float(u[0] << 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < W; ++i) {
-        o[2 * i] = __uint_as_float(u[i] << 16);
-        o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-      }
-    }
-  }
-};
-
 // reverse pass over the chunks of one (batch, head): dShat_c = D_c +
 // decay_c R(-Phi_end,c) dShat_{c+1} (rows), from dShat_C = dh_T; one 4-vector
 // of the state per lane, the inputs of the next DP chunks in flight.
@@ -202,8 +145,8 @@ __global__ __launch_bounds__(64) void k_bwd_state_pass(BackwardArgs g) {
   f4 dv[DP], sv[DP];
   f2 rr0[DP], rr1[DP];
   float dd[DP], bpn[DP];
-  RowRaw<TI, R> xq[DP];
-  RowRaw<TI, 4 * R> bq[DP];
+  RawVec<TI, R> xq[DP];
+  RawVec<TI, 4 * R> bq[DP];
   const TI* __restrict__ Xg = static_cast<const TI*>(a.x);
   const TI* __restrict__ Bg = static_cast<const TI*>(a.B);
   auto load = [&](int k, int q) {   // k-th chunk from the end

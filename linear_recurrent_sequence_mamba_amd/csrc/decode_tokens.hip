@@ -40,17 +40,22 @@ __device__ __forceinline__ int64_t unit_group(const DecodeArgs& a, int bh) {
 // the token scalars; pair phases of token k into cs (threads < N/2)
 template <typename TI, int N>
 struct TokScalars {
-  float d, l, A, th;
+  Raw1<TI> d_, l_, th_;   // as loaded; converted where used
+  float A;
   __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k) {
-    const int64_t th_ = tok_head(a, bh, k);
-    d = ld1(static_cast<const TI*>(a.dt), th_);
-    l = ld1(static_cast<const TI*>(a.lam), th_);
-    A = (a.flags & kAPerToken) ? a.A[th_] : a.A[bh % a.H];
-    const int kk = threadIdx.x;
-    th = kk < N / 2 ? ld1(static_cast<const TI*>(a.theta), tok_group(a, bh, k) * (N / 2) + kk) : 0.0f;
+    const int64_t t = tok_head(a, bh, k);
+    d_.load(static_cast<const TI*>(a.dt), t);
+    l_.load(static_cast<const TI*>(a.lam), t);
+    A = (a.flags & kAPerToken) ? a.A[t] : a.A[bh % a.H];
+    // every thread reads (threads past the pairs re-read the last pair and
+    // never use it): no branch around the load
+    const int kk = min(static_cast<int>(threadIdx.x), N / 2 - 1);
+    th_.load(static_cast<const TI*>(a.theta), tok_group(a, bh, k) * (N / 2) + kk);
   }
+  __device__ __forceinline__ float d() const { return d_.f(); }
   __device__ __forceinline__ void finish(const DecodeArgs& a, float& alpha, float& beta,
                                          float& gamma, f2* cs) const {
+    const float d = d_.f(), l = l_.f(), th = th_.f();
     alpha = expf(d * A);
     beta = (1.0f - l) * d * alpha;
     gamma = l * d;
@@ -160,20 +165,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
   if (PREP && PREV) bo = prep(bo, bw, bbias);   // bo always holds a prepared B
 
   for (int k = 0; k < a.K; ++k) {
-    // the next token's inputs fly while this one is applied
-    float dn = dk, ln = lk, An = Ak;
-    f2 thn = thk;
-    f4 bn = bk, cn = ck;
-    float xn[UNR];
+    // the next token's inputs fly, as loaded, while this one is applied (the
+    // last token re-reads its own and drops them: no branch around a load)
+    const int kn = min(k + 1, a.K - 1);
+    const int64_t tn = tok_head(a, bh, kn);
+    Raw1<TI> dn, ln, xn[UNR];
+    dn.load(Dg, tn);
+    ln.load(Lg, tn);
+    const float An = (a.flags & kAPerToken) ? a.A[tn] : a.A[bh % a.H];
+    RawVec<TI, 2> thn;
+    RawVec<TI, 4> bn, cn;
+    thn.load(Tg + tok_group(a, bh, kn) * (N / 2) + n0 / 2);
+    bn.load(Bg + tok_group(a, bh, kn) * N + n0);
+    cn.load(Cg + tok_group(a, bh, kn) * N + n0);
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) xn[u] = xk[u];
-    if (k + 1 < a.K) {
-      scal(k + 1, dn, ln, An, thn);
-      bn = ld4(Bg, tok_group(a, bh, k + 1) * N + n0);
-      cn = ld4(Cg, tok_group(a, bh, k + 1) * N + n0);
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) xn[u] = ld1(X, tok_head(a, bh, k + 1) * P + min(u * RPB + rsub, P - 1));
-    }
+    for (int u = 0; u < UNR; ++u) xn[u].load(X, tn * P + min(u * RPB + rsub, P - 1));
     const float alpha = expf(dk * Ak);
     const float beta = (1.0f - lk) * dk * alpha;
     const float gamma = lk * dk;
@@ -196,31 +202,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
       part[u] = s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w;
     }
     // y of the lane's UNR rows: summed over the row's LPR lanes
+    float tot[UNR];
+    if constexpr (UNR <= LPR) {
+      tot[0] = rows_sum<LPR, UNR>(part, lane % LPR);
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) tot[u] = group_sum<LPR>(part[u]);
+    }
+    // the next token's inputs come into use before this token's y stores: a
+    // loaded value used after a store would wait for the store as well
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      xo[u] = xk[u];
+      xk[u] = xn[u].f();
+    }
+    bo = bk;
+    {
+      float t4[4], t2[2];
+      bn.get(t4);
+      bk = f4{t4[0], t4[1], t4[2], t4[3]};
+      cn.get(t4);
+      ck = f4{t4[0], t4[1], t4[2], t4[3]};
+      thn.get(t2);
+      thk = f2{t2[0], t2[1]};
+    }
+    dk = dn.f();
+    lk = ln.f();
+    Ak = An;
     if constexpr (UNR <= LPR) {
       const int j = lane % LPR;
-      const float tot = rows_sum<LPR, UNR>(part, j);
       const int p = (j / (LPR / UNR)) * RPB + rsub;
-      if (j % (LPR / UNR) == 0 && p < P) st1(yk, p, tot);
+      if (j % (LPR / UNR) == 0 && p < P) st1(yk, p, tot[0]);
     } else {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int p = u * RPB + rsub;
-        const float tot = group_sum<LPR>(part[u]);
-        if ((lane % LPR) == 0 && p < P) st1(yk, p, tot);
+        if ((lane % LPR) == 0 && p < P) st1(yk, p, tot[u]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      xo[u] = xk[u];
-      xk[u] = xn[u];
-    }
-    bo = bk;
-    bk = bn;
-    ck = cn;
-    dk = dn;
-    lk = ln;
-    Ak = An;
-    thk = thn;
   }
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
@@ -287,12 +306,29 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
       ec[q] = ld1(Ck, i);
     }
   };
-  auto load_x = [&](const TI* __restrict__ src, float* xr) {
+  // the next token's B and C elements, as loaded
+  auto load_bc_raw = [&](int k, Raw1<TI>* eb, Raw1<TI>* ec) {
+    const TI* __restrict__ Bk = Bg + tok_group(a, bh, k) * NE;
+    const TI* __restrict__ Ck = Cg + tok_group(a, bh, k) * NE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = min(tid + 256 * q, NE - 1);
+      eb[q].load(Bk, i);
+      ec[q].load(Ck, i);
+    }
+  };
+  // x of this lane's rank r = 4 kb + g, as loaded (lanes with no such row or
+  // rank read element 0; xval zeroes them): no branch around the load
+  auto load_x = [&](const TI* __restrict__ src, Raw1<TI>* xr) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int r = 4 * kb + g;
-      xr[kb] = (rows && r < R) ? ld1(src, (int64_t)p * R + r) : 0.0f;
+      xr[kb].load(src, (rows && r < R) ? (int64_t)p * R + r : 0);
     }
+  };
+  auto xval = [&](const Raw1<TI>* xr, float* xv) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xv[kb] = (rows && 4 * kb + g < R) ? xr[kb].f() : 0.0f;
   };
   // token operands into buffer tb: beta/gamma-scaled B, C, phases.  With
   // the preparation, eb and ec (and eo when prep_prev) are raw on entry and
@@ -357,17 +393,16 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
   float eb[PER], ec[PER], eo[PER];
   load_bc(0, eb, ec);
   float xk[KB], xo[KB];
-  load_x(X + tok_head(a, bh, 0) * P * R, xk);
+  Raw1<TI> xkr[KB], xor_[KB];
+  load_x(X + tok_head(a, bh, 0) * P * R, xkr);
   if (PREV) {
     const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + unit_group(a, bh) * NE;
 #pragma unroll
     for (int q = 0; q < PER; ++q) eo[q] = ld1(Bp, min(tid + 256 * q, NE - 1));
-    load_x(static_cast<const TI*>(a.xp) + (int64_t)bh * P * R, xo);
+    load_x(static_cast<const TI*>(a.xp) + (int64_t)bh * P * R, xor_);
   } else {
 #pragma unroll
     for (int q = 0; q < PER; ++q) eo[q] = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xo[kb] = 0.0f;
   }
 
   // the wave's 16 state rows, row-contiguous, then into the D layout
@@ -413,25 +448,30 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
   }
   put_tables(sm.tok[0], sc, eb, eo, ec, PREV);
   __syncthreads();
+  xval(xkr, xk);
+  if (PREV) {
+    xval(xor_, xo);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xo[kb] = 0.0f;
+  }
 
   for (int k = 0; k < a.K; ++k) {
-    TokScalars<TI, N> scn = sc;
-    float ebn[PER], ecn[PER], xn[KB];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) { ebn[q] = eb[q]; ecn[q] = ec[q]; }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xn[kb] = xk[kb];
-    if (k + 1 < a.K) {
-      scn.load(a, bh, k + 1);
-      load_bc(k + 1, ebn, ecn);
-      load_x(X + tok_head(a, bh, k + 1) * P * R, xn);
-    }
+    // token k + 1's inputs, as loaded (the last token re-reads its own and
+    // drops them): no branch around the loads, no conversion before the
+    // state update below
+    const int kn = min(k + 1, a.K - 1);
+    TokScalars<TI, N> scn;
+    scn.load(a, bh, kn);
+    Raw1<TI> ebn[PER], ecn[PER], xn[KB];
+    load_bc_raw(kn, ebn, ecn);
+    load_x(X + tok_head(a, bh, kn) * P * R, xn);
     const Tok& tb = sm.tok[k & 1];
-    const float alpha = expf(sc.d * sc.A);
-    if (rows) {
-      float yp[RP];
+    const float alpha = expf(sc.d() * sc.A);
+    float yp[RP];
 #pragma unroll
-      for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
+    for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
+    if (rows) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         f4 acc = alpha * v[t];
@@ -463,27 +503,26 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
         yp[r] += __shfl_xor(yp[r], 16, 64);
         yp[r] += __shfl_xor(yp[r], 32, 64);
       }
-      if (g == 0) {
-        TO* __restrict__ yk = Y + tok_head(a, bh, k) * P * R;
-#pragma unroll
-        for (int r = 0; r < R; ++r) st1(yk, (int64_t)p * R + r, yp[r]);
-      }
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       eo[q] = eb[q];
-      eb[q] = ebn[q];
-      ec[q] = ecn[q];
+      eb[q] = ebn[q].f();
+      ec[q] = ecn[q].f();
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      xo[kb] = xk[kb];
-      xk[kb] = xn[kb];
-    }
+    for (int kb = 0; kb < KB; ++kb) xo[kb] = xk[kb];
+    xval(xn, xk);
     sc = scn;
     // token k + 1's operands into the other buffer (last read at token k - 1,
-    // before the previous barrier)
+    // before the previous barrier), before token k's y stores: a loaded value
+    // used after a store would wait for the store as well
     if (k + 1 < a.K) put_tables(sm.tok[(k + 1) & 1], sc, eb, eo, ec, false);
+    if (rows && g == 0) {
+      TO* __restrict__ yk = Y + tok_head(a, bh, k) * P * R;
+#pragma unroll
+      for (int r = 0; r < R; ++r) st1(yk, (int64_t)p * R + r, yp[r]);
+    }
     __syncthreads();
   }
 

@@ -44,6 +44,84 @@ __device__ __forceinline__ float ld1(const T* __restrict__ p, int64_t i) {
   return to_f32(p[i]);
 }
 
+// one element as loaded (a bf16 keeps its bit pattern), for a read issued
+// early and turned into a float only where it is used: the conversion does
+// not make the read wait at the place it is issued
+template <typename T>
+struct Raw1;
+template <>
+struct Raw1<float> {
+  float v;
+  __device__ __forceinline__ void load(const float* __restrict__ p, int64_t i) { v = p[i]; }
+  __device__ __forceinline__ float f() const { return v; }
+};
+template <>
+struct Raw1<bf16_t> {
+  uint32_t u;
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p, int64_t i) { u = p[i].bits; }
+  __device__ __forceinline__ float f() const { return __uint_as_float(u << 16); }
+};
+
+// K consecutive elements as loaded (bf16 keeps its bit patterns; the first
+// element aligned to the whole vector), likewise converted only where used
+template <typename T, int K>
+struct RawVec;
+template <int K>
+struct RawVec<float, K> {
+  float v[K];
+  __device__ __forceinline__ void load(const float* __restrict__ p) {
+    if constexpr (K % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < K / 4; ++i) {
+        const f4 q = reinterpret_cast<const f4*>(p)[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      }
+    } else if constexpr (K == 2) {
+      const f2 q = *reinterpret_cast<const f2*>(p);
+      v[0] = q.x; v[1] = q.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) v[i] = p[i];
+    }
+  }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = v[i];
+  }
+};
+template <int K>
+struct RawVec<bf16_t, K> {
+  static constexpr int W = (K + 1) / 2;   // 32-bit words
+  uint32_t u[W];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+    if constexpr (K == 1) {
+      u[0] = p->bits;
+    } else if constexpr (W % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        u[4 * i] = q.x; u[4 * i + 1] = q.y; u[4 * i + 2] = q.z; u[4 * i + 3] = q.w;
+      }
+    } else if constexpr (W == 2) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      u[0] = q.x; u[1] = q.y;
+    } else {
+      u[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    if constexpr (K == 1) {
+      o[0] = __uint_as_float(u[0] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        o[2 * i] = __uint_as_float(u[i] << 16);
+        o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  }
+};
+
 // four consecutive elements starting at a multiple of 4 (8-byte / 16-byte loads)
 __device__ __forceinline__ f4 ld4(const float* __restrict__ p, int64_t i) {
   return *reinterpret_cast<const f4*>(p + i);
