@@ -28,9 +28,13 @@ namespace m3 {
 // The per-token scalars and the phase of one pair are loaded before the
 // state stream is issued: the load counter retires in order, so waiting for
 // a small load issued after the state loads would wait for the whole stream.
+// They are kept as loaded (bf16 bit patterns) until token_finish, and every
+// thread reads a phase (threads past the pairs re-read the last one): with
+// no conversion and no branch at the loads, nothing waits for them there.
 template <typename TI, int N>
 struct TokenIn {
-  float d, l, A, th;
+  Raw1<TI> d, l, th;
+  float A;
 };
 
 // (batch, group) slot of B, C and theta for the unit bh = (batch, head)
@@ -42,11 +46,14 @@ template <typename TI, int N>
 __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh) {
   TokenIn<TI, N> in;
   const int head = bh % a.H;
-  in.d = ld1(static_cast<const TI*>(a.dt), bh);
-  in.l = ld1(static_cast<const TI*>(a.lam), bh);
+  in.d.load(static_cast<const TI*>(a.dt), bh);
+  in.l.load(static_cast<const TI*>(a.lam), bh);
   in.A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
-  const int k = threadIdx.x;
-  in.th = k < N / 2 ? ld1(static_cast<const TI*>(a.theta), group_slot(a, bh) * (N / 2) + k) : 0.0f;
+  const int k = min(static_cast<int>(threadIdx.x), N / 2 - 1);
+  in.th.load(static_cast<const TI*>(a.theta), group_slot(a, bh) * (N / 2) + k);
+  // the compiler may not move these loads past this point (towards their
+  // uses, which come after the state stream)
+  asm volatile("" ::: "memory");
   return in;
 }
 
@@ -54,12 +61,14 @@ __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh
 template <typename TI, int N>
 __device__ __forceinline__ void token_finish(const DecodeArgs& a, const TokenIn<TI, N>& in,
                                              float& alpha, float& beta, float& gamma, f2* cs_sh) {
-  alpha = expf(in.d * in.A);
-  beta = (1.0f - in.l) * in.d * alpha;
-  gamma = in.l * in.d;
+  const float d = in.d.f(), l = in.l.f();
+  alpha = expf(d * in.A);
+  beta = (1.0f - l) * d * alpha;
+  gamma = l * d;
   const int k = threadIdx.x;
   if (k < N / 2) {
-    const float phi = (a.flags & kThetaIsAngle) ? in.th : in.d * in.th;
+    const float th = in.th.f();
+    const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
     float s, c;
     sincosf(phi, &s, &c);
     cs_sh[k] = f2{c, s};
