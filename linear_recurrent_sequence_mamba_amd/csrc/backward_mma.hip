@@ -773,8 +773,13 @@ struct TSmem {
   } u;
 };
 
+// a single input's t-side block is 64 KB of LDS: two fit on a CU once the
+// registers allow two waves per SIMD (a few spill; the call measured 2-3% faster)
+template <class Pol, int R>
+constexpr int t_min_waves() { return R == 1 && std::is_same<Pol, PolF16>::value ? 2 : 1; }
+
 template <class Pol, typename TI, typename TY, int P, int N, int R>
-__global__ __launch_bounds__((GeoU<P, N, R>::NT)) void k_bwd_t(BackwardArgs g) {
+__global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_per_eu(t_min_waves<Pol, R>()))) void k_bwd_t(BackwardArgs g) {
   const PrefillArgs& a = g.f;
   using G = GeoU<P, N, R>;
   constexpr int NT = G::NT, NW = G::NW, KS = Pol::KS;
