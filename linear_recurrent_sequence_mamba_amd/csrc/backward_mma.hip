@@ -919,6 +919,24 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_pe
       });
   }
 
+  // the u side's phase gradients of this lane's (token, pair) entries (k_bwd_u
+  // wrote them before this kernel): with few ranks per lane (R >= 2) they are
+  // read now and arrive during the walk
+  float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
+  float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
+  float dpre[NTL][4 / R];
+  auto read_dph = [&]() {
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += R) {
+      const bool ok = live && trow0 + j0 < rows;
+      const int t = ok ? (trow0 + j0) / R : 0;
+#pragma unroll
+      for (int i = 0; i < NTL; ++i) dpre[i][j0 / R] = dph[t * NP + ((16 * i + l16) >> 1)];
+    }
+  };
+  constexpr bool kEarlyDph = R >= 2;
+  if constexpr (kEarlyDph) read_dph();
+
   // ---- walk the u rows at or before this wave's t rows: dCt += W2 Bt
   const int ttok_max = min(Lc - 1, (16 * ttile + 15) / R);
   auto stage = [&](int k) {
@@ -973,16 +991,7 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_pe
   // and drops it).  All values are formed (in acc and dpre, in place) before
   // the first store: a use of a loaded value after a store would wait for
   // the store too.
-  float* __restrict__ dCo = shared_grp ? g.dCh : g.dC;
-  float* __restrict__ dph = g.dphiB + ck.id * (kQ * NP);
-  float dpre[NTL][4 / R];
-#pragma unroll
-  for (int j0 = 0; j0 < 4; j0 += R) {
-    const bool ok = live && trow0 + j0 < rows;
-    const int t = ok ? (trow0 + j0) / R : 0;
-#pragma unroll
-    for (int i = 0; i < NTL; ++i) dpre[i][j0 / R] = dph[t * NP + ((16 * i + l16) >> 1)];
-  }
+  if constexpr (!kEarlyDph) read_dph();
 #pragma unroll
   for (int i = 0; i < NTL; ++i) {
     const int n = 16 * i + l16, kp = n >> 1;
