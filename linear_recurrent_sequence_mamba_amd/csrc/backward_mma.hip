@@ -762,7 +762,7 @@ struct TSmem {
   using G = GeoU<P, N, R>;
   Tables<N, false> tb;
   float ecs[kQ];
-  union U {
+  union alignas(16) U {
     TableScratch<N, G::NT> scr;
     typename Pol::template Store<64, P> own;   // own dy rows
     typename Pol::template Store<N, P> sht;    // Shat^T [n][p]
@@ -991,7 +991,34 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_pe
   // and drops it).  All values are formed (in acc and dpre, in place) before
   // the first store: a use of a loaded value after a store would wait for
   // the store too.
-  if constexpr (!kEarlyDph) read_dph();
+  // A single input (one token per row, the whole chunk in the block) moves
+  // these per-lane scalars through LDS, which is free after the walk: the
+  // chunk's phase-gradient rows come in, and dC and the phase gradients go
+  // out, as 16-byte row vectors (a fifth of the memory instructions)
+  constexpr bool kLdsIo = R == 1;
+  constexpr int CS = N + 4, DS = NP + 4;   // LDS row strides (16-byte aligned rows)
+  static_assert(!kLdsIo || (G::BROWS == kQ && sizeof(sm.u) >= sizeof(float) * kQ * CS &&
+                            sizeof(sm.u) >= sizeof(float) * kQ * DS),
+                "the staging space holds a chunk's dC and phase-gradient rows");
+  static_assert(alignof(decltype(sm.u)) >= 16, "16-byte LDS rows");
+  float* __restrict__ lio = reinterpret_cast<float*>(&sm.u);
+  if constexpr (kLdsIo) {
+    for (int q = tid; q < Lc * (NP / 4); q += NT) {
+      const int t = q / (NP / 4), k4 = 4 * (q % (NP / 4));
+      *reinterpret_cast<f4*>(lio + t * DS + k4) = *reinterpret_cast<const f4*>(dph + t * NP + k4);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NTL; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = trow0 + jj;   // < kQ
+        dpre[i][jj] = t < Lc ? lio[t * DS + ((16 * i + l16) >> 1)] : 0.0f;
+      }
+    __syncthreads();   // the rows are read before dC takes the space
+  } else if constexpr (!kEarlyDph) {
+    read_dph();
+  }
 #pragma unroll
   for (int i = 0; i < NTL; ++i) {
     const int n = 16 * i + l16, kp = n >> 1;
@@ -1025,7 +1052,30 @@ __global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_pe
       dpre[i][j0 / R] = v;
     }
   }
-  if (live) {
+  if constexpr (kLdsIo) {
+#pragma unroll
+    for (int i = 0; i < NTL; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) lio[(trow0 + jj) * CS + 16 * i + l16] = acc[i][jj];
+    __syncthreads();
+    for (int q = tid; q < Lc * (N / 4); q += NT) {
+      const int t = q / (N / 4), n4 = 4 * (q % (N / 4));
+      *reinterpret_cast<f4*>(dCo + (ti0 + (int64_t)t * a.H) * N + n4) = *reinterpret_cast<const f4*>(lio + t * CS + n4);
+    }
+    __syncthreads();   // dC is read before the phase gradients take the space
+#pragma unroll
+    for (int i = 0; i < NTL; ++i) {
+      if (!(l16 & 1)) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) lio[(trow0 + jj) * DS + ((16 * i + l16) >> 1)] = dpre[i][jj];
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < Lc * (NP / 4); q += NT) {
+      const int t = q / (NP / 4), k4 = 4 * (q % (NP / 4));
+      *reinterpret_cast<f4*>(dph + t * NP + k4) = *reinterpret_cast<const f4*>(lio + t * DS + k4);
+    }
+  } else if (live) {
 #pragma unroll
     for (int i = 0; i < NTL; ++i) {
       const int n = 16 * i + l16;
