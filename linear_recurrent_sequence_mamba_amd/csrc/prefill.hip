@@ -306,18 +306,28 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     }
   }
 
-  // the next chunk's left-endpoint term, then S_c[p][n..n+3]
-  float bpn = 0.0f;
-  const TI* xe = nullptr;
-  const TI* Be = nullptr;
-  if (ck.next) {
-    const int64_t nx = token_index(a, b, c0 + kQ, h);
-    const float d = ld1(static_cast<const TI*>(a.dt), nx);
-    const float l = ld1(static_cast<const TI*>(a.lam), nx);
-    bpn = (1.0f - l) * d;
-    xe = Xg + token_index(a, b, c0 + kQ - 1, h) * P * R;
-    Be = Bg + group_index(a, b, c0 + kQ - 1, h) * N * R;
+  // the next chunk's left-endpoint term, then S_c[p][n..n+3].  Every read
+  // of the term (this chunk's last x and B rows for each tile, the next
+  // chunk's first dt and lam) goes out before any is used, kept as loaded,
+  // with no branch around it: a chunk with no next one reads its own tokens
+  // and drops the term.
+  const bool nxt = ck.next;
+  const int64_t nx = token_index(a, b, nxt ? c0 + kQ : c0, h);
+  Raw1<TI> dnr, lnr;
+  dnr.load(static_cast<const TI*>(a.dt), nx);
+  lnr.load(static_cast<const TI*>(a.lam), nx);
+  const TI* __restrict__ xe = Xg + token_index(a, b, c0 + Lc - 1, h) * P * R;
+  const TI* __restrict__ Be = Bg + group_index(a, b, c0 + Lc - 1, h) * N * R;
+  RawVec<TI, R> xraw[QPW];
+  RawVec<TI, 4 * R> braw[QPW];
+#pragma unroll
+  for (int q = 0; q < QPW; ++q) {
+    const int qq = min(wave * QPW + q, NQ - 1);
+    const int pt = qq / G::NTL, nt = qq % G::NTL;
+    xraw[q].load(xe + (int64_t)(16 * pt + l16) * R);
+    braw[q].load(Be + (int64_t)(16 * nt + 4 * g) * R);
   }
+  const float bpn = nxt ? (1.0f - lnr.f()) * dnr.f() : 0.0f;
   float* __restrict__ S = a.S + chunk_id * P * N;
 #pragma unroll
   for (int q = 0; q < QPW; ++q) {
@@ -326,28 +336,11 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
       const int pt = qq / G::NTL, nt = qq % G::NTL;
       const int p = 16 * pt + l16, n = 16 * nt + 4 * g;
       f4 s = acc[q];
-      if (xe) {
-        // x[p][0..R) and B[n..n+3][0..R) of the chunk's last token, in
-        // 8- and 16-byte pieces
+      if (nxt) {
+        // x[p][0..R) and B[n..n+3][0..R) of the chunk's last token
         float xr[R], br[4 * R];
-        if constexpr (R % 4 == 0) {
-#pragma unroll
-          for (int i = 0; i < R / 4; ++i) {
-            const f4 v = ld4(xe, (int64_t)p * R + 4 * i);
-            xr[4 * i] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
-          }
-        } else if constexpr (R == 2) {
-          const f2 v = ld2(xe, (int64_t)p * R);
-          xr[0] = v.x; xr[1] = v.y;
-        } else {
-#pragma unroll
-          for (int r = 0; r < R; ++r) xr[r] = ld1(xe, (int64_t)p * R + r);
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const f4 v = ld4(Be, (int64_t)n * R + 4 * i);
-          br[4 * i] = v.x; br[4 * i + 1] = v.y; br[4 * i + 2] = v.z; br[4 * i + 3] = v.w;
-        }
+        xraw[q].get(xr);
+        braw[q].get(br);
         if constexpr (PREP) {   // the last token's B, prepared like the staged rows
 #pragma unroll
           for (int e = 0; e < 4 * R; ++e)
