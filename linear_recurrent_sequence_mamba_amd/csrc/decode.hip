@@ -106,12 +106,16 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   f4 bw = f4{1, 1, 1, 1}, cw = bw, bb = f4{0, 0, 0, 0}, cb = bb;
   if constexpr (PREP) {
     const int64_t hb0 = (int64_t)(bh % a.H) * N + n0;
+    // (read under branches: the branch-free form measured 4 us slower here)
     if (a.bc.Bw) bw = ld4(a.bc.Bw, n0);
     if (a.bc.Cw) cw = ld4(a.bc.Cw, n0);
     if (a.bc.Bb) bb = ld4(a.bc.Bb, hb0);
     if (a.bc.Cb) cb = ld4(a.bc.Cb, hb0);
   }
 
+  // the token-side reads stay ahead of the state stream (the compiler may not
+  // move them past it: a use would then wait for the whole stream)
+  asm volatile("" ::: "memory");
   // the state stream; rows past P are clamped for the loads, masked for the stores
   f4 v[UNR];
   float xv[UNR], xpv[UNR];
@@ -230,13 +234,16 @@ __attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int ic = min(tid + 256 * q, NE - 1);
-      wbv[q] = a.bc.Bw ? a.bc.Bw[ic / R] : 1.0f;
-      wcv[q] = a.bc.Cw ? a.bc.Cw[ic / R] : 1.0f;
-      bbv[q] = a.bc.Bb ? a.bc.Bb[hb0 + ic] : 0.0f;
-      cbv[q] = a.bc.Cb ? a.bc.Cb[hb0 + ic] : 0.0f;
+      wbv[q] = ld_or(a.bc.Bw, ic / R, 1.0f);
+      wcv[q] = ld_or(a.bc.Cw, ic / R, 1.0f);
+      bbv[q] = ld_or(a.bc.Bb, hb0 + ic, 0.0f);
+      cbv[q] = ld_or(a.bc.Cb, hb0 + ic, 0.0f);
     }
   }
 
+  // the token-side reads stay ahead of the state stream (as in the
+  // single-input kernel)
+  asm volatile("" ::: "memory");
   // the first row block's state stream, row-contiguous (whole 128-byte
   // lines per load instruction); it reaches the D layout through LDS
   constexpr int V4 = N / 4;            // 16-byte vectors per row

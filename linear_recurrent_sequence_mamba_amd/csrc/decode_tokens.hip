@@ -149,10 +149,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
   f4 bw = f4{1, 1, 1, 1}, cw = bw, bbias = f4{0, 0, 0, 0}, cbias = bbias;
   if constexpr (PREP) {
     const int64_t hb0 = (int64_t)(bh % a.H) * N + n0;
-    if (a.bc.Bw) bw = ld4(a.bc.Bw, n0);
-    if (a.bc.Cw) cw = ld4(a.bc.Cw, n0);
-    if (a.bc.Bb) bbias = ld4(a.bc.Bb, hb0);
-    if (a.bc.Cb) cbias = ld4(a.bc.Cb, hb0);
+    bw = ld4_or(a.bc.Bw, n0, bw);
+    cw = ld4_or(a.bc.Cw, n0, cw);
+    bbias = ld4_or(a.bc.Bb, hb0, bbias);
+    cbias = ld4_or(a.bc.Cb, hb0, cbias);
   }
   // a row's N/4 lanes hold a token's whole B and C
   auto prep = [&](f4 u, f4 w, f4 b) {
@@ -431,12 +431,12 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
   if constexpr (PREP) {   // this head's weights and biases (1 and 0 when absent)
     const int64_t hb0 = (int64_t)(bh % a.H) * NE;
     for (int i = tid; i < N; i += 256) {
-      pw_sh[0][i] = a.bc.Bw ? a.bc.Bw[i] : 1.0f;
-      pw_sh[1][i] = a.bc.Cw ? a.bc.Cw[i] : 1.0f;
+      pw_sh[0][i] = ld_or(a.bc.Bw, i, 1.0f);
+      pw_sh[1][i] = ld_or(a.bc.Cw, i, 1.0f);
     }
     for (int i = tid; i < NE; i += 256) {
-      pb_sh[0][i] = a.bc.Bb ? a.bc.Bb[hb0 + i] : 0.0f;
-      pb_sh[1][i] = a.bc.Cb ? a.bc.Cb[hb0 + i] : 0.0f;
+      pb_sh[0][i] = ld_or(a.bc.Bb, hb0 + i, 0.0f);
+      pb_sh[1][i] = ld_or(a.bc.Cb, hb0 + i, 0.0f);
     }
   }
   __syncthreads();   // every wave's transpose is read before the tables take the space

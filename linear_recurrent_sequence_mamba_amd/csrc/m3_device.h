@@ -44,6 +44,23 @@ __device__ __forceinline__ float ld1(const T* __restrict__ p, int64_t i) {
   return to_f32(p[i]);
 }
 
+// p[i] when p is set, else v; f4 likewise (i a multiple of 4).  Every lane
+// reads a valid address (a sink when p is null) and the value is selected
+// afterwards: no branch surrounds the read, so it need not wait there.  The
+// sink is only read; it is not const so that it lives in global memory like
+// p (a pointer that may be either stays a global one, not a generic one).
+static __device__ __align__(16) float kReadSink[4];
+typedef __attribute__((address_space(1))) const float gfloat;   // global memory
+typedef __attribute__((address_space(1))) const f4 gf4;
+__device__ __forceinline__ float ld_or(const float* p, int64_t i, float v) {
+  const float r = *(const gfloat*)(p ? p + i : kReadSink);
+  return p ? r : v;
+}
+__device__ __forceinline__ f4 ld4_or(const float* p, int64_t i, f4 v) {
+  const f4 r = *(const gf4*)(p ? p + i : kReadSink);
+  return p ? r : v;
+}
+
 // one element as loaded (a bf16 keeps its bit pattern), for a read issued
 // early and turned into a float only where it is used: the conversion does
 // not make the read wait at the place it is issued

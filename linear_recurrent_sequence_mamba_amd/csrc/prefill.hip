@@ -83,13 +83,15 @@ struct PrepLoad {
   static constexpr int NE = N + N * R;
   static constexpr int IT = (NE + NT - 1) / NT;
   float v[IT];
+  // every lane reads a valid address (see ld_or) and selects after
   __device__ __forceinline__ void load(const float* w, const float* bias, int h) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int e = threadIdx.x + NT * i;
-      if (e < N) v[i] = w ? w[e] : 1.0f;
-      else if (e < NE) v[i] = bias ? bias[(int64_t)h * N * R + (e - N)] : 0.0f;
-      else v[i] = 0.0f;
+      const bool isw = e < N;
+      const float r = isw ? ld_or(w, min(e, N - 1), 1.0f)
+                          : ld_or(bias, (int64_t)h * N * R + min(e - N, N * R - 1), 0.0f);
+      v[i] = e < NE ? r : 0.0f;
     }
   }
   __device__ __forceinline__ void store(PrepTab<N, R>& t) const {
@@ -418,8 +420,8 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
         const float inv = bc_inv_rms(a.bc, group_sum<N / 4>(ss), N);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bv[j][r] = bv[j][r] * inv * (a.bc.Bw ? a.bc.Bw[n + j] : 1.0f) +
-                     (a.bc.Bb ? a.bc.Bb[((int64_t)h * N + n + j) * R + r] : 0.0f);
+          bv[j][r] = bv[j][r] * inv * ld_or(a.bc.Bw, n + j, 1.0f) +
+                     ld_or(a.bc.Bb, ((int64_t)h * N + n + j) * R + r, 0.0f);
       }
     }
 #pragma unroll
@@ -569,7 +571,8 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
     PrepLoad<N, R, G::NT> plb, plc;
     plb.load(a.bc.Bw, a.bc.Bb, h);
     plc.load(a.bc.Cw, a.bc.Cb, h);
-    const float rsb = tid < kQ * R ? a.rsB[chunk_id * (kQ * R) + tid] : 0.0f;
+    const float rsb_in = a.rsB[chunk_id * (kQ * R) + min(tid, kQ * R - 1)];   // (no branch around the read)
+    const float rsb = tid < kQ * R ? rsb_in : 0.0f;
     plb.store(sm.pb);
     plc.store(sm.pc);
     if (tid < kQ * R) sm.pb.inv[tid] = rsb;
