@@ -240,15 +240,20 @@ def test_decode_tokens_prep(P, N, R):
     say(f"decode tokens prep, groups G=2, no previous token")
     d, params = I.bc_prep_inputs(w, _decode_inputs(w, groups=2, prev=False, K=K))
     _check_tokens(w, d, params)
+    # absent weights or biases are read from a sink and replaced by 1 / 0
+    d, params = I.bc_prep_inputs(w, _decode_inputs(w, K=K))
+    for drop in (("B_weight", "C_weight"), ("B_bias", "C_bias"), ("B_weight", "C_bias")):
+        say(f"decode tokens prep without {', '.join(drop)}")
+        _check_tokens(w, d, params, drop)
 
 
-def _check_tokens(w, d, params):
+def _check_tokens(w, d, params, drop=()):
     g = {k: cuda(v) for k, v in d.items()}
     h = g["h0"].clone()
     y = m3.decode_tokens(h, g["x"], g["B"], g["C"], g["dt"], g["A"], g["lam"], g["theta"],
-                         x_prev=g["x_prev"], B_prev=g["B_prev"], bc=_bc(params))
+                         x_prev=g["x_prev"], B_prev=g["B_prev"], bc=_bc(params, drop))
     torch.cuda.synchronize()
-    ref = _oracle_scan(d, params)
+    ref = _oracle_scan(d, params, drop=drop)
     ey, eh = rel_err(cpu64(y), ref.y), rel_err(cpu64(h), ref.hT)
     say(f"  y err {ey:.2e}  h err {eh:.2e}")
     assert ey <= TOL[w.torch_dtype] and eh <= TOL[w.torch_dtype], (ey, eh)
