@@ -139,3 +139,26 @@ def test_tokens_full_shape_sampled(name):
     ey, eh = rel_err(cpu64(y)[rows], ref.y), rel_err(cpu64(h)[rows], ref.hT)
     say(f"  y err {ey:.2e}  h err {eh:.2e}")
     assert ey <= 3e-3 and eh <= 3e-3, (ey, eh)
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_tokens_deterministic_and_nan_stays_in_its_head(R):
+    """Two calls on the same inputs agree bit for bit; a NaN in one head's x at
+    token 2 reaches that head's state and its outputs from token 2 on, and
+    nothing else (heads are independent and earlier outputs do not see it)."""
+    K = 4
+    w = I.Workload("t", 96, 2, K, 4, 64, 128, R, 64, "bf16", "normal")
+    d = _inputs(w)
+    say(f"decode_tokens determinism and NaN isolation R={R}")
+    y1, h1 = _gpu(d)
+    y2, h2 = _gpu(d)
+    assert torch.equal(y1.cpu(), y2.cpu()) and torch.equal(h1.cpu(), h2.cpu())
+    x = d["x"].clone()
+    x[1, 2, 3].view(-1)[5] = float("nan")
+    y, h = _gpu(dict(d, x=x))
+    bad_h = torch.isnan(h).flatten(2).any(dim=2).cpu()
+    assert bad_h[1, 3] and bad_h.sum() == 1
+    bad_y = torch.isnan(y).flatten(3).any(dim=3).cpu()          # [batch, token, head]
+    expect = torch.zeros_like(bad_y)
+    expect[1, 2:, 3] = True
+    assert torch.equal(bad_y, expect)
