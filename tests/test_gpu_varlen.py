@@ -245,3 +245,29 @@ def test_varlen_serving_mix_full_size(name):
         ey, eh = rel_err(cpu64(y[a:b]), ry), rel_err(cpu64(hT[s:s + 1]), rh)
         say(f"  sequence {s} ({b - a} tokens): y err {ey:.2e}  hT err {eh:.2e}")
         assert ey <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_varlen_deterministic_and_nan_stays_in_its_sequence(R):
+    """Two calls agree bit for bit.  A NaN in one token of the middle sequence
+    stays in that sequence and head: every sequence starts its own chunks, so
+    the neighbours packed before and after it never see it, and inside it the
+    NaN reaches the outputs from its chunk's first token on (the chunk's masked
+    products multiply it by zero)."""
+    lengths = [100, 150, 37]
+    w = I.Workload("v", 115, 1, 1, 3, 64, 128, R, 64, "bf16")
+    d = _packed(w, lengths)
+    say(f"varlen determinism and NaN isolation R={R}")
+    y1, h1 = _run_varlen(d)
+    y2, h2 = _run_varlen(d)
+    assert torch.equal(y1.cpu(), y2.cpu()) and torch.equal(h1.cpu(), h2.cpu())
+    cu = _cu(d)
+    x = d["x"].clone()
+    x[cu[1] + 70, 2].view(-1)[5] = float("nan")   # sequence 1, its chunk 1 (tokens 64..127)
+    y, hT = _run_varlen(dict(d, x=x))
+    bad_y = torch.isnan(y).flatten(2).any(dim=2).cpu()          # [token, head]
+    expect = torch.zeros_like(bad_y)
+    expect[cu[1] + 64:cu[2], 2] = True
+    assert torch.equal(bad_y, expect)
+    bad_h = torch.isnan(hT).flatten(2).any(dim=2).cpu()         # [sequence, head]
+    assert bad_h[1, 2] and bad_h.sum() == 1
