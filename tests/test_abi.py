@@ -102,6 +102,10 @@ def test_error_paths(call):
     assert call(_dims(), xp=P16) == 1                           # x_prev without B_prev
     assert call(_dims(dstate=127)) == 2                         # odd N
     assert call(_dims(headdim=0)) == 2
+    assert call(_dims(batch=0)) == 2                            # empty batch
+    assert call(_dims(nheads=0)) == 2
+    if call is not _decode:
+        assert call(_dims(seqlen=0)) == 2                       # no tokens
     assert call(_dims(rank=0)) == 2
     assert call(_dims(flags=1 << 7)) == 2                       # unknown flag
     assert call(_dims(ngroups=-1)) == 2                         # head groups
