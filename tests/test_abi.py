@@ -201,3 +201,13 @@ def test_binding_rejects_mismatched_tensors():
     h = torch.zeros(2, 3, 64, 128)  # host tensor: rejected before any call
     with pytest.raises(ValueError):
         m3.m3_decode_step(d, h, *([None] * 10))
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library every entry point raises: there is no other path."""
+    monkeypatch.setattr(m3, "_LIB", None)
+    monkeypatch.setattr(m3, "LIB_PATH", "/nonexistent/libm3ssm.so")
+    with pytest.raises(RuntimeError, match="is not built"):
+        m3.library()
+    with pytest.raises(RuntimeError, match="is not built"):
+        m3.m3_prefill_workspace_size(_dims())
