@@ -170,6 +170,14 @@ def head_decay(w: Workload) -> torch.Tensor:
     return torch.from_numpy(-np.exp(rng.uniform(-4.0, 0.0, size=(w.nheads,))).astype(np.float32))
 
 
+def token_decay(w: Workload, lead: tuple, stream: int = 0) -> torch.Tensor:
+    """A drawn independently for every leading index (tokens, or (batch,
+    head) pairs of a decode step): -exp(U(-4, 0)), fp32, shape lead + (H,)."""
+    rng = np.random.default_rng([w.cfg_id, 0x0A7, stream])
+    return torch.from_numpy(-np.exp(rng.uniform(-4.0, 0.0, size=tuple(lead) + (w.nheads,)))
+                            .astype(np.float32))
+
+
 def prefill_inputs(w: Workload, stream: int = 0, h0: str | None = None,
                    with_prev: bool = False) -> dict:
     """Inputs of one prefill call as CPU torch tensors (input dtype; A, h0 fp32).

@@ -349,13 +349,59 @@ def check_linearity_and_independence(lib):
     _close(rs.hT, rd.hT[:, h:h + 1], tol=0.0, what="head slice hT")
 
 
+def _complex_token(hc, xp, bp, xt, bt, ct, dt, a, lam, ang):
+    """One token of the complex-valued SSM in complex numbers (see
+    check_complex_form): hc [P, N/2] complex, bp/bt/ct [N/2, R] complex."""
+    z = np.exp(dt * a + 1j * ang)
+    hc = z[None, :] * hc + lam * dt * (xt @ bt.T)
+    if xp is not None:
+        hc = hc + (1 - lam) * dt * z[None, :] * (xp @ bp.T)
+    return hc, np.real(hc @ np.conj(ct))
+
+
 def check_a_per_token(lib):
-    """With per-token A broadcast from the per-head A the result is unchanged."""
-    d = _rand_case(21, R=1)
-    r1 = _scan(lib, d)
-    d2 = dict(d, A=np.broadcast_to(d["A"][None, None, :], d["dt"].shape).copy())
-    r2 = _scan(lib, d2, flags=oracle.A_PER_TOKEN)
-    _close(r2.y, r1.y, tol=0.0, what="A per token y")
+    """A_t drawn independently for every (batch, token, head) [xxxxx.co.kr
+    Mamba-3 article, section 1.1 writes the decay as exp(dt_t A_t)]: the
+    scan with the per-token flag against the complex-valued SSM evaluated
+    with that token's own A; then one decode step with A drawn per (batch,
+    head) against one complex token from the same state."""
+    d = _rand_case(21, R=2)
+    rng = np.random.default_rng(22)
+    Bsz, T, H, P, R = d["x"].shape
+    d["A"] = -np.exp(rng.uniform(-4, 0.5, size=(Bsz, T, H)))
+    got = _scan(lib, d, flags=oracle.A_PER_TOKEN)
+    for b in range(Bsz):
+        for h in range(H):
+            hc = _cplx(d["h0"][b, h], 1)
+            xp, bp = d["x_prev"][b, h], _cplx(d["B_prev"][b, h], 0)
+            for t in range(T):
+                dt = d["dt"][b, t, h]
+                xt, bt = d["x"][b, t, h], _cplx(d["B"][b, t, h], 0)
+                hc, y = _complex_token(hc, xp, bp, xt, bt, _cplx(d["C"][b, t, h], 0), dt,
+                                       d["A"][b, t, h], d["lam"][b, t, h],
+                                       dt * d["theta"][b, t, h])
+                _close(got.y[b, t, h], y, what="A per token y")
+                xp, bp = xt, bt
+            hr = np.empty((P, hc.shape[1] * 2))
+            hr[:, 0::2], hr[:, 1::2] = hc.real, hc.imag
+            _close(got.hT[b, h], hr, what="A per token hT")
+    # decode step: A [Bsz, H], one value per (batch, head)
+    A2 = -np.exp(rng.uniform(-4, 0.5, size=(Bsz, H)))
+    t = 3
+    y, hn = oracle.decode_step(d["h0"], d["x"][:, t], d["x"][:, t - 1], d["B"][:, t],
+                               d["B"][:, t - 1], d["C"][:, t], d["dt"][:, t], A2,
+                               d["lam"][:, t], d["theta"][:, t], flags=oracle.A_PER_TOKEN,
+                               lib_path=lib)
+    for b in range(Bsz):
+        for h in range(H):
+            dt = d["dt"][b, t, h]
+            hc, yc = _complex_token(_cplx(d["h0"][b, h], 1), d["x"][b, t - 1, h],
+                                    _cplx(d["B"][b, t - 1, h], 0), d["x"][b, t, h],
+                                    _cplx(d["B"][b, t, h], 0), _cplx(d["C"][b, t, h], 0), dt,
+                                    A2[b, h], d["lam"][b, t, h], dt * d["theta"][b, t, h])
+            _close(y[b, h], yc, what="decode A per (batch, head) y")
+            _close(hn[b, h, :, 0::2], hc.real, what="decode A per (batch, head) h")
+            _close(hn[b, h, :, 1::2], hc.imag, what="decode A per (batch, head) h")
 
 
 # ---------------------------------------------------------------------------

@@ -95,6 +95,10 @@ MUTANTS = {
     "bwd_theta_without_dt": ("dtheta[bth * K + k] = angle ? dphi : DT * dphi;", "dtheta[bth * K + k] = dphi;"),
     "bwd_output_grad_skipped": ("G[p * N + n] += v;", "G[p * N + n] += 0.0 * v;"),
     "bwd_prev_x_uses_gamma": ("gx[t * P * R + p * R + r] += beta * v;", "gx[t * P * R + p * R + r] += gamma * v;"),
+    "scan_a_per_token_read_per_head": ("const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[bth] : A[h];",
+                                       "const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[h] : A[h];"),
+    "decode_a_per_token_read_per_head": ("const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[u] : A[h_];",
+                                         "const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[h_] : A[h_];"),
     "bc_norm_over_all_ranks": ("for (int64_t n = 0; n < N; ++n) ms += v[n * R + r] * v[n * R + r];",
                                "for (int64_t n = 0; n < N * R; ++n) ms += v[n] * v[n];"),
 }
