@@ -146,15 +146,15 @@ struct TabPrep {
 };
 
 // Sums of squares over the N channels of each rank column for the tokens
-// of a row block of B or C (t = t0 + tl < Lc).  When one token's vectors sit
-// on VPT consecutive lanes (TF false) they are summed with lane shuffles and
-// the token's first lane stores the inverse RMS into out[t][r]; a
-// token-per-lane block (TF true, single rank) adds its partial sums into a
-// cleared out[t] with LDS atomics, to be turned into inverse RMS later.
-template <typename TI, int E, int R, int NT, bool TF, int ROWS>
-__device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, TF, ROWS>& rb,
+// of a row block of B or C (t = t0 + tl < Lc), when one token's vectors sit
+// on VPT consecutive lanes: they are summed with lane shuffles and the
+// token's first lane stores the inverse RMS into out[t][r].
+template <typename TI, int E, int R, int NT, int ROWS>
+__device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, false, ROWS>& rb,
                                           const BCPrep& bc, int N, int t0, int Lc, float* out) {
-  using RBk = RowBlock<TI, E, R, NT, TF, ROWS>;
+  using RBk = RowBlock<TI, E, R, NT, false, ROWS>;
+  static_assert(RBk::VPT <= 64 && 64 % RBk::VPT == 0 && NT % RBk::VPT == 0,
+                "a token's vectors on one aligned lane group");
 #pragma unroll
   for (int i = 0; i < RBk::IT; ++i) {
     const int vi = threadIdx.x + NT * i;
@@ -167,20 +167,45 @@ __device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, TF, ROWS>
     for (int r = 0; r < R; ++r) part[r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) part[j % R] += v[j] * v[j];
-    if constexpr (TF) {
-      static_assert(R == 1, "token-per-lane blocks carry a single rank");
-      if (vi < RBk::NV && t < Lc) atomicAdd(&out[t], part[0]);
-    } else {
-      static_assert(RBk::VPT <= 64 && 64 % RBk::VPT == 0 && NT % RBk::VPT == 0,
-                    "a token's vectors on one aligned lane group");
 #pragma unroll
-      for (int r = 0; r < R; ++r) part[r] = group_sum<RBk::VPT>(part[r]);
-      if (vi < RBk::NV && t < Lc && vi % RBk::VPT == 0) {
+    for (int r = 0; r < R; ++r) part[r] = group_sum<RBk::VPT>(part[r]);
+    if (vi < RBk::NV && t < Lc && vi % RBk::VPT == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) out[t * R + r] = bc_inv_rms(bc, part[r], N);
-      }
+      for (int r = 0; r < R; ++r) out[t * R + r] = bc_inv_rms(bc, part[r], N);
     }
   }
+}
+
+// The same sums for a token-per-lane single-rank block (TF: token tl's
+// vectors sit on threads tl + NTOK j), in a fixed order so that equal
+// inputs give equal bits: each thread adds its own vectors in index order,
+// then the lanes of a wave that hold one token are added by xor steps (the
+// two operands of each step are the same on both lanes), and this wave's
+// sum of token t0 + tl goes to part[wave][t0 + tl] (zero for a block that
+// was not loaded, live false).  The caller adds the waves' parts in wave
+// order after a barrier.
+template <typename TI, int E, int NT, int ROWS>
+__device__ __forceinline__ void row_sumsq_tf(const RowBlock<TI, E, 1, NT, true, ROWS>& rb, int t0,
+                                             bool live, float* part) {
+  using RBk = RowBlock<TI, E, 1, NT, true, ROWS>;
+  constexpr int NTOK = RBk::NTOK;
+  static_assert(NT % NTOK == 0 && 64 % NTOK == 0, "a token's vectors in fixed lanes of every wave");
+  float s = 0.0f;
+  if (live) {   // block-uniform
+#pragma unroll
+    for (int i = 0; i < RBk::IT; ++i) {
+      float v[8];
+      rb.get(i, v);   // zeros outside the chunk's rows
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p += v[j] * v[j];
+      s += p;
+    }
+  }
+#pragma unroll
+  for (int off = NTOK; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+  const int lane = threadIdx.x & 63;
+  if (lane < NTOK) part[(threadIdx.x >> 6) * kQ + t0 + lane] = s;
 }
 
 // --------------------------------------------------------------------------
@@ -205,6 +230,9 @@ struct K1Smem {
   } u;
   typename Pol::template XStore<P, UBR> xs;    // x^T  [p][v]
   PrepTabT<PREP, N, R> pb;                     // B preparation
+  // single rank with the preparation: each wave's part of every token's
+  // sum of squares [wave][t]
+  float sq[(PREP && R == 1) ? Geo<P, N, R, 8>::NW * kQ : 1];
 };
 
 template <class Pol, typename TI, int P, int N, int R, bool PREP>
@@ -232,7 +260,6 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   PrepLoad<N, R, G::NT> pl;
   if constexpr (PREP) {
     pl.load(a.bc.Bw, a.bc.Bb, h);
-    if (TFK1 && tid < kQ) sm.pb.inv[tid] = 0.0f;   // sums of squares, added atomically
   }
   ThetaBlock<TI, N, G::NT> thb;
   thb.load(a, b, h, c0, Lc);
@@ -267,13 +294,23 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     rsB = a.rsB + chunk_id * (kQ * R);
     pl.store(sm.pb);
 #pragma unroll
-    for (int ub = 0; ub < NUB; ++ub)
-      if (ub * UBR < rows) row_sumsq(bb[ub], a.bc, N, ub * UBR / R, Lc, sm.pb.inv);
+    for (int ub = 0; ub < NUB; ++ub) {
+      if constexpr (TFK1) {   // every u-block writes its tokens' parts (zeros past the chunk)
+        row_sumsq_tf(bb[ub], ub * UBR, ub * UBR < rows, sm.sq);
+      } else {
+        if (ub * UBR < rows) row_sumsq(bb[ub], a.bc, N, ub * UBR / R, Lc, sm.pb.inv);
+      }
+    }
   }
   __syncthreads();   // W_t visible (and the B preparation tables)
   if constexpr (PREP) {
-    if constexpr (TFK1) {   // sums of squares -> inverse RMS
-      if (tid < kQ) sm.pb.inv[tid] = bc_inv_rms(a.bc, sm.pb.inv[tid], N);
+    if constexpr (TFK1) {   // the waves' parts in wave order -> inverse RMS
+      if (tid < kQ) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) ss += sm.sq[w * kQ + tid];
+        sm.pb.inv[tid] = bc_inv_rms(a.bc, ss, N);
+      }
       __syncthreads();
     }
     if (tid < kQ * R) rsB[tid] = sm.pb.inv[tid];

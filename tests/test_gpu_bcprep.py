@@ -127,6 +127,20 @@ def test_prefill_prep_split_equals_whole():
     assert rel_err(cpu64(h2), cpu64(hT)) <= 1e-5
 
 
+@pytest.mark.parametrize("R", [1, 4])
+def test_prefill_prep_deterministic(R):
+    """Two equal prepared prefill calls return equal bits: the sums of
+    squares behind each token's inverse RMS are added in a fixed order (the
+    single-rank chunk-state kernel spreads one token over lanes of several
+    waves)."""
+    w = I.Workload("p", 124, 2, 200, 3, 64, 128, R, 64, "bf16")
+    d, params = I.bc_prep_inputs(w, I.prefill_inputs(w, h0="normal", with_prev=True))
+    say(f"prefill prep R={R}: two calls, equal bits")
+    y1, h1 = _gpu_scan(d, params)
+    y2, h2 = _gpu_scan(d, params)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
 def test_prefill_prep_varlen():
     """Packed sequences with the preparation: equal to one prepared call per
     sequence, bit for bit, and to the oracle on each sequence."""
