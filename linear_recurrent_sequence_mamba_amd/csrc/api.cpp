@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/m3ssm.h"
 #include "m3_launch.h"
@@ -63,7 +64,11 @@ int chunk_of(const m3_dims* d) { return d->chunk > 0 ? d->chunk : 64; }
 extern "C" {
 
 const char* m3_status_str(m3_status s) {
-  switch (s) {
+  // a C caller may pass any int; read its bits as an int, since a C++ load
+  // of an enum value outside the enumerators' range is undefined
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case M3_OK: return "ok";
     case M3_ERR_NULL: return "required pointer is NULL";
     case M3_ERR_SHAPE: return "invalid shape or flags";
