@@ -425,6 +425,28 @@ int m3ref_bc_prep(int64_t rows, int64_t G, int64_t H, int64_t N, int64_t R,
   return 0;
 }
 
+/*
+ * Angle projection [the same article, section 1.2: the rotation angles of
+ * the complex state are data-dependent, produced from the layer's input like
+ * B and C].  For each row (one token of one batch), group g and pair k:
+ *   out[g][k] = sum_j W[g][k][j] * u[j]
+ * Layouts: u [rows, D], W [G, K, D], out [rows, G, K] (K = N/2 pairs).
+ * Reading: one linear map per head group, of the same input row that feeds
+ * the group's B and C; no bias and no activation.
+ */
+int m3ref_theta_proj(int64_t rows, int64_t G, int64_t K, int64_t D, const double* u,
+                     const double* W, double* out) {
+  if (rows < 0 || G <= 0 || K <= 0 || D <= 0 || !u || !W || !out) return 1;
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t g = 0; g < G; ++g)
+      for (int64_t k = 0; k < K; ++k) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < D; ++j) acc += W[(g * K + k) * D + j] * u[i * D + j];
+        out[(i * G + g) * K + k] = acc;
+      }
+  return 0;
+}
+
 int m3ref_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -62,6 +62,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.m3ref_bc_prep.restype = ctypes.c_int
     lib.m3ref_bc_prep.argtypes = [ctypes.c_int64] * 5 + [dp] * 3 + [ctypes.c_double,
                                                                     ctypes.c_int, dp]
+    lib.m3ref_theta_proj.restype = ctypes.c_int
+    lib.m3ref_theta_proj.argtypes = [ctypes.c_int64] * 4 + [dp] * 3
     lib.m3ref_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -174,6 +176,23 @@ def bc_prep(v, nheads, weight=None, bias=None, eps=1e-6, rms=True, lib_path: str
                            _ptr(_f64(bias)), float(eps), int(bool(rms)), _ptr(out))
     if rc:
         raise ValueError("m3ref_bc_prep rejected its arguments (code %d)" % rc)
+    return out
+
+
+def theta_proj(u, W, lib_path: str = _LIB):
+    """Angles from the projection: u [..., D], W [G, K, D] -> [..., G, K]."""
+    lib = load(lib_path)
+    u, W = _f64(u), _f64(W)
+    lead = u.shape[:-1]
+    D = u.shape[-1]
+    G, K, D2 = W.shape
+    if D2 != D:
+        raise ValueError("W and u disagree on the projection width")
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.zeros(tuple(lead) + (G, K), np.float64)
+    rc = lib.m3ref_theta_proj(rows, G, K, D, _ptr(u), _ptr(W), _ptr(out))
+    if rc:
+        raise ValueError("m3ref_theta_proj rejected its arguments (code %d)" % rc)
     return out
 
 

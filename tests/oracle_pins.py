@@ -507,9 +507,49 @@ def check_bc_prep_bias_weight_eps(lib):
            w[:, None] * np.repeat(v, 2, axis=1), tol=0.0, what="weight alone")
 
 
+# ---------------------------------------------------------------------------
+# angle projection (theta from the layer input)
+def check_theta_proj_columns_and_linearity(lib):
+    """A linear map per head group is fixed by its response to the unit
+    inputs (column j of each group's matrix) and by linearity; a zero input
+    gives zero angles."""
+    rng = np.random.default_rng(40)
+    G, K, D = 3, 5, 7
+    W = rng.standard_normal((G, K, D))
+    eye = np.eye(D)
+    got = oracle.theta_proj(eye, W, lib_path=lib)            # [D, G, K]
+    for j in range(D):
+        _close(got[j], W[:, :, j], tol=0.0, what=f"unit input {j}")
+    u1, u2 = rng.standard_normal((4, D)), rng.standard_normal((4, D))
+    a = oracle.theta_proj(2.5 * u1 - 0.75 * u2, W, lib_path=lib)
+    b = 2.5 * oracle.theta_proj(u1, W, lib_path=lib) - 0.75 * oracle.theta_proj(u2, W, lib_path=lib)
+    _close(a, b, tol=1e-13, what="linearity")
+    _close(oracle.theta_proj(np.zeros((2, D)), W, lib_path=lib), np.zeros((2, G, K)), tol=0.0,
+           what="zero input")
+
+
+def check_theta_proj_parity(lib):
+    """The parity construction [no1joon.github.io Mamba-3 review, the paper's
+    three answers; xxxxx.co.kr Mamba-3 article, section 1.2] with its angles
+    produced by the projection: u_t = (bit_t, noise) and a group matrix that
+    reads pi times the first input only, so the scan still tracks parity."""
+    bits = np.random.default_rng(41).integers(0, 2, size=24)
+    d = parity_case(bits)
+    T = len(bits)
+    rng = np.random.default_rng(42)
+    u = np.stack([bits.astype(float), rng.standard_normal(T), rng.standard_normal(T)], axis=-1)
+    W = np.array([[[math.pi, 0.0, 0.0]]])                     # G = 1, K = 1, D = 3
+    d["theta"] = oracle.theta_proj(u.reshape(1, T, 3), W, lib_path=lib)   # [1, T, 1, 1]
+    got = _scan(lib, d)
+    y = got.y[0, :, 0, 0, 0]
+    expect = np.array([(-1.0) ** (int(np.sum(bits[1:t + 1])) % 2) for t in range(T)])
+    _close(y, expect, tol=1e-9, what="parity through the projection")
+
+
 ALL_CHECKS = [check_euler_special_case, check_complex_form, check_rope_frame,
               check_unrolled, check_closed_form, check_parity, check_second_order,
               check_mimo_sum_of_siso, check_split_and_decode,
               check_linearity_and_independence, check_a_per_token, check_bc_prep_unit_rms,
               check_bc_prep_scale_invariance, check_bc_prep_bias_weight_eps, check_backward_siso,
-              check_backward_mimo_and_flags]
+              check_backward_mimo_and_flags, check_theta_proj_columns_and_linearity,
+              check_theta_proj_parity]

@@ -99,6 +99,9 @@ MUTANTS = {
                                        "const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[h] : A[h];"),
     "decode_a_per_token_read_per_head": ("const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[u] : A[h_];",
                                          "const double a = (d->flags & M3REF_A_PER_TOKEN) ? A[h_] : A[h_];"),
+    "theta_proj_transposed": ("W[(g * K + k) * D + j]", "W[(g * D + j) * K + k]"),
+    "theta_proj_group_ignored": ("out[(i * G + g) * K + k] = acc;", "out[(i * G + g) * K + k] = g ? 0.0 : acc;"),
+    "theta_proj_last_input_dropped": ("for (int64_t j = 0; j < D; ++j) acc +=", "for (int64_t j = 0; j < D - 1; ++j) acc +="),
     "bc_norm_over_all_ranks": ("for (int64_t n = 0; n < N; ++n) ms += v[n * R + r] * v[n * R + r];",
                                "for (int64_t n = 0; n < N * R; ++n) ms += v[n] * v[n];"),
 }
