@@ -125,8 +125,30 @@ def bc_prep_for(w, dev):
                      eps=prm["eps"])
 
 
-def bench_decode(name, steps, warmup, pool_n=8, prep=False):
-    """prep: with the in-kernel B/C preparation (m3_dims.bc)."""
+def _replay_ms(g, stream, replays):
+    """Per-replay times (ms) of a captured graph, HIP events on `stream`."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def _spread(ms, per):
+    """Median and range of per-replay times, divided by `per` (µs)."""
+    v = sorted(m / per * 1e3 for m in ms)
+    return dict(median=round(v[len(v) // 2], 2), min=round(v[0], 2), max=round(v[-1], 2),
+                replays=len(v))
+
+
+def bench_decode(name, steps, warmup, pool_n=8, prep=False, replays=11, cold=False):
+    """prep: with the in-kernel B/C preparation (m3_dims.bc).  cold: step s
+    updates state s % 2 of two separate states, so that every step streams a
+    state the other one has pushed out of the 256 MB last-level cache."""
     import torch
     from linear_recurrent_sequence_mamba_amd import binding as m3
     from linear_recurrent_sequence_mamba_amd import inputs as I
@@ -140,7 +162,8 @@ def bench_decode(name, steps, warmup, pool_n=8, prep=False):
         d = I.decode_step_inputs(w, s)
         pool.append({k: v.to(dev) for k, v in d.items()})
     log(f"[{name}] generated {pool_n} input sets in {time.time() - t0:.1f}s")
-    h = I.decode_state(w).to(dev)
+    nstate = 2 if cold else 1
+    hs = [I.decode_state(w).to(dev) for _ in range(nstate)]
     A = I.head_decay(w).to(dev)
     y = torch.empty((w.batch, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
     dims = m3.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32,
@@ -149,21 +172,23 @@ def bench_decode(name, steps, warmup, pool_n=8, prep=False):
     # validate every argument set once through the checked binding ...
     for s in range(pool_n):
         cur, prev = pool[s], pool[(s - 1) % pool_n]
-        m3.m3_decode_step(dims, h, cur["x"], prev["x"], cur["B"], prev["B"], cur["C"], cur["dt"],
-                          A, cur["lam"], cur["theta"], y)
+        for h in hs:
+            m3.m3_decode_step(dims, h, cur["x"], prev["x"], cur["B"], prev["B"], cur["C"],
+                              cur["dt"], A, cur["lam"], cur["theta"], y)
     torch.cuda.synchronize()
     # ... then launch through the raw entry point (argument marshalling only)
     lib = m3.library()
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     sp = ctypes.c_void_p(stream.cuda_stream)
-    args = []
-    for s in range(pool_n):
-        cur, prev = pool[s], pool[(s - 1) % pool_n]
-        args.append((ctypes.byref(dims), p(h), p(cur["x"]), p(prev["x"]), p(cur["B"]), p(prev["B"]),
-                     p(cur["C"]), p(cur["dt"]), p(A), p(cur["lam"]), p(cur["theta"]), p(y), sp))
+
+    def args(s, strm):
+        cur, prev = pool[s % pool_n], pool[(s - 1) % pool_n]
+        return (ctypes.byref(dims), p(hs[s % nstate]), p(cur["x"]), p(prev["x"]), p(cur["B"]),
+                p(prev["B"]), p(cur["C"]), p(cur["dt"]), p(A), p(cur["lam"]), p(cur["theta"]),
+                p(y), strm)
 
     def launch(s):
-        st = lib.m3_decode_step(*args[s % pool_n])
+        st = lib.m3_decode_step(*args(s, sp))
         if st != 0:
             raise RuntimeError(f"m3_decode_step failed: {m3.m3_status_str(st)}")
 
@@ -181,7 +206,8 @@ def bench_decode(name, steps, warmup, pool_n=8, prep=False):
     stream_ms = start.elapsed_time(end)
 
     # the timed K steps: one HIP graph holding the K launches (what a decode
-    # loop captures), replayed once untimed to load it, then timed
+    # loop captures), replayed once untimed to load it, then `replays` times,
+    # each replay timed on its own; the median replay is the figure
     g = torch.cuda.CUDAGraph()
     gs = torch.cuda.Stream()
     gs.wait_stream(stream)
@@ -189,22 +215,20 @@ def bench_decode(name, steps, warmup, pool_n=8, prep=False):
         with torch.cuda.graph(g, stream=gs):
             cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for s in range(steps):
-                st = lib.m3_decode_step(*(args[s % pool_n][:-1] + (cap,)))
+                st = lib.m3_decode_step(*args(s, cap))
                 if st != 0:
                     raise RuntimeError(m3.m3_status_str(st))
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(stream)
-    g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms = _replay_ms(g, stream, replays)
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
+    total_ms = sorted(ms)[len(ms) // 2]
     nbytes = decode_bytes(w)
     return dict(workload=w, steps=steps, total_ms=total_ms, step_ms=total_ms / steps,
-                stream_step_ms=stream_ms / steps, wall_s=wall, bytes=nbytes, pool=pool_n)
+                stream_step_ms=stream_ms / steps, wall_s=wall, bytes=nbytes, pool=pool_n,
+                spread=_spread(ms, steps), states=nstate)
 
 
 def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
@@ -269,13 +293,20 @@ def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
                               timing=f"HIP events around a graph of {calls} calls"))
 
 
-def bench_prefill(name, steps, warmup, prep=False):
-    """prep: with the in-kernel B/C preparation (m3_dims.bc)."""
+def default_chunk(rank):
+    """The chunk length a prefill with m3_dims.chunk = 0 takes (see m3ssm.h)."""
+    return 128 if rank == 1 else 64
+
+
+def bench_prefill(name, steps, warmup, prep=False, chunk=0):
+    """prep: with the in-kernel B/C preparation (m3_dims.bc).  chunk: the
+    chunk length to ask for (0: the library's default for the shape; the
+    result does not depend on it)."""
     import torch
     from linear_recurrent_sequence_mamba_amd import binding as m3
     from linear_recurrent_sequence_mamba_amd import inputs as I
 
-    w = I.WORKLOADS[name]
+    w = I.WORKLOADS[name].with_(chunk=chunk)
     dev = torch.device("cuda:0")
     t0 = time.time()
     n_sets = 2 if prefill_bytes(w) < 1e9 else 1   # two sets when one would fit in cache
@@ -309,7 +340,8 @@ def bench_prefill(name, steps, warmup, prep=False):
     ms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
     call_ms = sum(ms) / len(ms)
     return dict(workload=w, steps=steps, call_ms=call_ms, call_p50_ms=ms[len(ms) // 2],
-                bytes=prefill_bytes(w), tokens=w.batch * w.seqlen, ws_bytes=ws.numel())
+                bytes=prefill_bytes(w), tokens=w.batch * w.seqlen, ws_bytes=ws.numel(),
+                chunk=chunk or default_chunk(w.rank))
 
 
 def bench_prefill_varlen(name, steps, warmup):
@@ -326,7 +358,7 @@ def bench_prefill_varlen(name, steps, warmup):
     d = {k: (None if v is None else v.to(dev)) for k, v in I.packed_inputs(w, lengths).items()}
     log(f"[{name}] {len(lengths)} sequences, generated in {time.time() - t0:.1f}s")
     S, T = len(lengths), w.seqlen
-    dims = m3.make_dims(S, T, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, m3.M3_BF16, m3.M3_F32)
+    dims = m3.make_dims(S, T, w.nheads, w.headdim, w.dstate, w.rank, 0, m3.M3_BF16, m3.M3_F32)
     ws = m3.workspace(dims, dev, varlen=True)
     y = torch.empty((T, w.nheads, w.headdim, w.rank), dtype=torch.float32, device=dev)
     hT = torch.empty((S, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
@@ -373,7 +405,7 @@ def bench_backward(name, steps, warmup):
     d = {k: (None if v is None else v.to(dev)) for k, v in I.prefill_inputs(w).items()}
     gen = torch.Generator(device="cpu").manual_seed(w.cfg_id)
     dy = torch.randn(tuple(d["x"].shape), generator=gen).to(dev)
-    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk,
+    dims = m3.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, 64,
                         m3.M3_BF16, m3.M3_F32)
     n = m3.m3_prefill_backward_workspace_size(dims)
     ws = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=dev)
@@ -450,13 +482,13 @@ def copy_reference(state_bytes, reps=50):
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands, on a bounded sample
-def cpu_decode(name, budget_s=8.0):
+def cpu_decode(name, budget_s=8.0, nthreads=0, nb=16):
+    """nthreads 0: every host thread (OpenMP over (b, h)); nb batch rows of
+    the sample, every head."""
     from linear_recurrent_sequence_mamba_amd import inputs as I
     from oracle import oracle
-    import numpy as np
 
     w = I.WORKLOADS[name]
-    nb = 16  # batch rows of the sample; every head
     d = I.decode_step_inputs(w, 0)
     f = {k: I.to_f64(v)[:nb] for k, v in d.items()}
     h = I.to_f64(I.decode_state(w))[:nb]
@@ -465,19 +497,21 @@ def cpu_decode(name, budget_s=8.0):
     steps, t0 = 0, time.perf_counter()
     while True:
         y, h = oracle.decode_step(h, f["x"], f["x"], f["B"], f["B"], f["C"], f["dt"], A,
-                                  f["lam"], f["theta"])
+                                  f["lam"], f["theta"], nthreads=nthreads)
         steps += 1
         if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
     full_s = el / steps * (w.batch / nb)
+    cores = nthreads or oracle.max_threads()
     return dict(value=round(decode_bytes(w) / full_s / 1e9, 3), unit="GB/s",
-                us_per_step=round(full_s * 1e6, 1), cores=oracle.max_threads(), kind="oracle",
+                us_per_step=round(full_s * 1e6, 1), cores=cores, kind="oracle",
                 sample=f"{steps} decode steps of {nb} of {w.batch} batch rows x {w.nheads} heads "
-                       f"(fp64, OpenMP over (b,h)); time scaled by {w.batch // nb} to the full step")
+                       f"(fp64, {cores} thread{'s' if cores > 1 else ''}, OpenMP over (b,h)); "
+                       f"mean time scaled by {w.batch // nb} to the full step")
 
 
-def cpu_prefill(name, heads, tokens, budget_note=""):
+def cpu_prefill(name, heads, tokens, nthreads=0):
     from linear_recurrent_sequence_mamba_amd import inputs as I
     from oracle import oracle
 
@@ -486,14 +520,23 @@ def cpu_prefill(name, heads, tokens, budget_note=""):
     d = I.prefill_inputs(ws)
     f = {k: I.to_f64(v) for k, v in d.items()}
     t0 = time.perf_counter()
-    oracle.scan(f["x"], f["dt"], f["A"], f["lam"], f["theta"], f["B"], f["C"])
+    oracle.scan(f["x"], f["dt"], f["A"], f["lam"], f["theta"], f["B"], f["C"], nthreads=nthreads)
     el = time.perf_counter() - t0
     # heads and tokens are independent/sequential units of identical work
     full_s = el * (w.nheads / heads) * (w.batch) * (w.seqlen / tokens)
+    cores = nthreads or oracle.max_threads()
     return dict(value=round(w.batch * w.seqlen / full_s, 1), unit="tokens/s",
-                cores=oracle.max_threads(), kind="oracle",
-                sample=f"{heads} heads x {tokens} tokens of one sequence (fp64); time scaled "
-                       f"linearly to {w.batch} x {w.seqlen} tokens x {w.nheads} heads")
+                cores=cores, kind="oracle",
+                sample=f"{heads} heads x {tokens} tokens of one sequence (fp64, {cores} "
+                       f"thread{'s' if cores > 1 else ''}); time scaled linearly to "
+                       f"{w.batch} x {w.seqlen} tokens x {w.nheads} heads")
+
+
+def with_single_thread(all_cores, one):
+    """The all-core baseline with the one-thread run beside it."""
+    all_cores = dict(all_cores)
+    all_cores["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    return all_cores
 
 
 # ---------------------------------------------------------------------------
@@ -527,6 +570,12 @@ def main():
         res["siso_decode"] = bench_decode("siso_decode", a.steps, a.warmup)
     if want("mimo_decode"):
         res["mimo_decode"] = bench_decode("mimo_decode", a.steps, a.warmup)
+    # the same steps alternating between two states (537 MB, more than the
+    # last-level cache): what a model with several layers sees
+    cold = {}
+    for name in ("siso_decode", "mimo_decode"):
+        if want(name + "_cold"):
+            cold[name] = bench_decode(name, a.steps, a.warmup, cold=True)
     if want("siso_prefill"):
         res["siso_prefill"] = bench_prefill("siso_prefill", a.prefill_steps, 2)
     if want("mimo_prefill"):
@@ -560,29 +609,38 @@ def main():
     cpu = {}
     if not a.no_cpu_baseline:
         t0 = time.time()
+        # every host thread, then one thread on a smaller sample
         if "siso_decode" in res:
-            cpu["siso_decode"] = cpu_decode("siso_decode", 8.0)
+            cpu["siso_decode"] = with_single_thread(cpu_decode("siso_decode", 6.0),
+                                                    cpu_decode("siso_decode", 3.0, 1, nb=2))
         if "mimo_decode" in res:
-            cpu["mimo_decode"] = cpu_decode("mimo_decode", 6.0)
+            cpu["mimo_decode"] = with_single_thread(cpu_decode("mimo_decode", 5.0),
+                                                    cpu_decode("mimo_decode", 3.0, 1, nb=2))
         if "siso_prefill" in res:
-            cpu["siso_prefill"] = cpu_prefill("siso_prefill", heads=8, tokens=2048)
+            cpu["siso_prefill"] = with_single_thread(
+                cpu_prefill("siso_prefill", heads=8, tokens=2048),
+                cpu_prefill("siso_prefill", heads=4, tokens=2048, nthreads=1))
         if "mimo_prefill" in res:
-            cpu["mimo_prefill"] = cpu_prefill("mimo_prefill", heads=4, tokens=4096)
+            cpu["mimo_prefill"] = with_single_thread(
+                cpu_prefill("mimo_prefill", heads=4, tokens=4096),
+                cpu_prefill("mimo_prefill", heads=2, tokens=4096, nthreads=1))
         log(f"cpu baselines took {time.time() - t0:.1f}s")
 
     def decode_entry(r, tag):
         w = r["workload"]
         gbs = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
-        traffic = counters_for(tag)
+        traffic = counters_for(tag) if r["states"] == 1 else None
+        sp = r["spread"]
         return dict(
-            us_per_step=round(r["step_ms"] * 1e3, 2),
+            us_per_step=round(r["step_ms"] * 1e3, 2), us_per_step_spread=sp,
             stream_launch_us_per_step=round(r["stream_step_ms"] * 1e3, 2),
             hbm_gbs=round(gbs, 1), tokens_per_s=round(w.batch / (r["step_ms"] * 1e-3), 1),
-            algorithmic_bytes=r["bytes"], input_pool=r["pool"],
+            algorithmic_bytes=r["bytes"], input_pool=r["pool"], states=r["states"],
             roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                           frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
                           kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}",
-                          timing="HIP events around a graph of the K launches (one kernel per step)"),
+                          timing=f"HIP events around each of {sp['replays']} replays of a graph "
+                                 f"of the K launches (one kernel per step); median replay"),
             cpu_baseline=cpu.get(tag))
 
     def prefill_entry(r, tag):
@@ -593,10 +651,11 @@ def main():
                 tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
                 sequences=r["nseq"], lengths=r["lengths"], algorithmic_bytes=r["bytes"],
                 workspace_bytes=r["ws_bytes"], hbm_frac=round(ach / HBM_PEAK_GBS, 4))
-        fl = prefill_flops(r["workload"])
+        fl = prefill_flops(r["workload"].with_(chunk=r["chunk"]))
         tf = fl / (r["call_ms"] * 1e-3) / 1e12
         return dict(
             ms_per_call=round(r["call_ms"], 4), p50_ms=round(r["call_p50_ms"], 4),
+            chunk=r["chunk"],
             tokens_per_s=round(r["tokens"] / (r["call_ms"] * 1e-3), 1),
             algorithmic_bytes=r["bytes"], workspace_bytes=r["ws_bytes"],
             roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -611,6 +670,12 @@ def main():
     workloads = {}
     for tag, r in res.items():
         workloads[tag] = decode_entry(r, tag) if "decode" in tag else prefill_entry(r, tag)
+    for base, r in cold.items():
+        e = decode_entry(r, base + "_cold")
+        e.pop("cpu_baseline")
+        if base in workloads:
+            e["step_time_vs_cache_warm"] = round(e["us_per_step"] / workloads[base]["us_per_step"], 3)
+        workloads[base + "_cold"] = e
     workloads.update(tok)   # several tokens per call (m3_decode_tokens), same shapes
     for k, e in bwd.items():
         base = k.replace("_backward", "")
@@ -648,9 +713,11 @@ def main():
                             "batch": 128, "nheads": 64, "headdim": 64, "dstate": 128, "rank": 1,
                             "input_dtype": "bf16", "state_dtype": "f32", "parallelism": "none"},
                     roofline=e["roofline"], cpu_baseline=e["cpu_baseline"])
-    if "mimo_decode" in workloads and "siso_decode" in workloads:
-        workloads["mimo_decode"]["step_time_vs_siso"] = round(
-            workloads["mimo_decode"]["us_per_step"] / workloads["siso_decode"]["us_per_step"], 3)
+    for sfx in ("", "_cold"):   # ratios of the median replays
+        if "mimo_decode" + sfx in workloads and "siso_decode" + sfx in workloads:
+            workloads["mimo_decode" + sfx]["step_time_vs_siso"] = round(
+                workloads["mimo_decode" + sfx]["us_per_step"]
+                / workloads["siso_decode" + sfx]["us_per_step"], 3)
     line["workloads"] = workloads
     if copy_ref is not None:
         line["hbm_copy_reference"] = copy_ref

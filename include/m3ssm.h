@@ -96,6 +96,26 @@ typedef struct {
   int32_t rms;           /* nonzero: RMS-normalise over N                  */
 } m3_bc_prep;
 
+/* Optional angle projection inside the kernels [the same article, section
+ * 1.2: the rotation angles are data-dependent, a projection of the layer's
+ * input like B and C].  With dims->tp set, the theta argument is not read
+ * (it may be NULL) and every call uses, for token row i and head group g,
+ *     theta[i][g][k] = sum_j W[g][k][j] * u[i][j],   k < N/2, j < dim,
+ * in fp32 (bf16 products are exact), then interprets theta as usual (a rate
+ * multiplied by dt_t, or the angle itself with M3_THETA_IS_ANGLE).  Reading:
+ * one linear map per head group, no bias, no activation.  u has the token
+ * layout of the call without the head axis: [Bsz, T, dim] (prefill),
+ * [T, dim] (packed prefill), [Bsz, dim] (decode step); W is [G, N/2, dim].
+ * Both are DEVICE pointers in in_dtype, 16-byte aligned; dim must be a
+ * positive multiple of 32 (else M3_ERR_SHAPE).  Supported by
+ * m3_scan_prefill, m3_scan_prefill_varlen and m3_decode_step;
+ * m3_decode_tokens and m3_scan_prefill_backward return M3_ERR_UNSUPPORTED. */
+typedef struct {
+  const void* u;   /* token rows of the projection's input                 */
+  const void* W;   /* [G, N/2, dim]                                        */
+  int32_t dim;     /* projection width                                     */
+} m3_theta_proj;
+
 typedef struct {
   int32_t batch;     /* Bsz >= 1                                           */
   int32_t seqlen;    /* T >= 1 (ignored by the decode step)                */
@@ -109,6 +129,7 @@ typedef struct {
   uint32_t flags;    /* M3_THETA_IS_ANGLE | M3_A_PER_TOKEN                 */
   int32_t ngroups;   /* G, groups sharing B, C, theta; 0 = nheads; G | H   */
   const m3_bc_prep* bc; /* host pointer; NULL = B and C are used as given */
+  const m3_theta_proj* tp; /* host pointer; NULL = theta is read as given */
 } m3_dims;
 
 /* Bytes of device workspace m3_scan_prefill needs for `dims` (0 if dims is
@@ -128,6 +149,14 @@ size_t m3_prefill_workspace_size(const m3_dims* dims);
  * one token's inputs stays in its (batch, head) and in its chunk and later
  * chunks, but may also reach the outputs of the earlier tokens of its own
  * chunk (masked products multiply it by zero).
+ * Precision: fp32 inputs run their chunk contractions on fp32 matrix-core
+ * operands.  bf16 inputs run them on bf16 hi + lo splits of every operand
+ * computed in fp32 (rotated B and C, masked Gram tiles, chunk states; about
+ * 2^-17 relative each; x is exact as one bf16 part).  bf16 keeps fp32's
+ * exponent range, so there is no range limit beyond fp32's own.
+ * Chunk length: dims->chunk = 0 takes 128 for a single input and 64
+ * otherwise; 64 and, at R = 1, 128 may be asked for (else
+ * M3_ERR_UNSUPPORTED).  It changes only the summation order.
  * ws must be at least m3_prefill_workspace_size(dims) bytes. */
 m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
                           const float* A, const void* lam, const void* theta,

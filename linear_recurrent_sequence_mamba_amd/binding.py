@@ -31,13 +31,18 @@ class m3_bc_prep(ctypes.Structure):
                 ("eps", ctypes.c_float), ("rms", ctypes.c_int32)]
 
 
+class m3_theta_proj(ctypes.Structure):
+    _fields_ = [("u", ctypes.c_void_p), ("W", ctypes.c_void_p), ("dim", ctypes.c_int32)]
+
+
 class m3_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("ngroups", ctypes.c_int32), ("bc", ctypes.POINTER(m3_bc_prep))]
+                ("ngroups", ctypes.c_int32), ("bc", ctypes.POINTER(m3_bc_prep)),
+                ("tp", ctypes.POINTER(m3_theta_proj))]
 
 
 class BCPrep:
@@ -60,6 +65,23 @@ class BCPrep:
             _check(name, getattr(self, name), (N,), torch.float32, optional=True)
         for name in ("B_bias", "C_bias"):
             _check(name, getattr(self, name), (H, N, R), torch.float32, optional=True)
+
+
+class ThetaProj:
+    """The in-kernel angle projection (m3_theta_proj): theta = W u per token
+    row and head group; u [rows..., D] and W [G, N/2, D] device tensors in
+    the input dtype."""
+
+    def __init__(self, u, W):
+        self.u, self.W = u, W
+        self.dim = int(W.shape[-1])
+
+    def struct(self) -> m3_theta_proj:
+        return m3_theta_proj(_ptr(self.u), _ptr(self.W), self.dim)
+
+    def check(self, rows, G, N, dtype):
+        _check("tp.u", self.u, tuple(rows) + (self.dim,), dtype)
+        _check("tp.W", self.W, (G, N // 2, self.dim), dtype)
 
 
 class M3Error(RuntimeError):
@@ -120,14 +142,20 @@ def m3_status_str(status: int) -> str:
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, rank=1, chunk=0,
-              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0, ngroups=0, bc=None) -> m3_dims:
-    """bc: a BCPrep (kept alive by the returned dims) or None."""
+              in_dtype=M3_BF16, out_dtype=M3_F32, flags=0, ngroups=0, bc=None,
+              tp=None) -> m3_dims:
+    """bc: a BCPrep, tp: a ThetaProj (both kept alive by the returned dims)
+    or None."""
     d = m3_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, in_dtype,
                 out_dtype, flags, ngroups)
     if bc is not None:
         d._bc_struct = bc.struct()
         d._bc = bc
         d.bc = ctypes.pointer(d._bc_struct)
+    if tp is not None:
+        d._tp_struct = tp.struct()
+        d._tp = tp
+        d.tp = ctypes.pointer(d._tp_struct)
     return d
 
 
@@ -135,6 +163,11 @@ def _check_bc(d: m3_dims):
     bc = getattr(d, "_bc", None)
     if bc is not None:
         bc.check(d.nheads, d.dstate, d.rank)
+
+
+def _proj(d: m3_dims):
+    """The dims' ThetaProj, or None (theta is then a required input)."""
+    return getattr(d, "_tp", None)
 
 
 def groups(d: m3_dims) -> int:
@@ -193,7 +226,9 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
         _check("dt", dt, (Bsz, T, H), ti)
         _check("A", A, (Bsz, T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
         _check("lam", lam, (Bsz, T, H), ti)
-        _check("theta", theta, (Bsz, T, G, N // 2), ti)
+        _check("theta", theta, (Bsz, T, G, N // 2), ti, optional=_proj(d) is not None)
+        if _proj(d) is not None:
+            _proj(d).check((Bsz, T), G, N, ti)
         _check("B", B, (Bsz, T, G, N, R), ti)
         _check("C", C, (Bsz, T, G, N, R), ti)
         _check("h0", h0, (Bsz, H, P, N), torch.float32, optional=True)
@@ -281,7 +316,9 @@ def m3_scan_prefill_varlen(dims: m3_dims, cu_seqlens, x, dt, A, lam, theta, B, C
         _check("dt", dt, (T, H), ti)
         _check("A", A, (T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
         _check("lam", lam, (T, H), ti)
-        _check("theta", theta, (T, G, N // 2), ti)
+        _check("theta", theta, (T, G, N // 2), ti, optional=_proj(d) is not None)
+        if _proj(d) is not None:
+            _proj(d).check((T,), G, N, ti)
         _check("B", B, (T, G, N, R), ti)
         _check("C", C, (T, G, N, R), ti)
         _check("h0", h0, (S, H, P, N), torch.float32, optional=True)
@@ -319,7 +356,9 @@ def m3_decode_step(dims: m3_dims, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam
         _check("dt_t", dt_t, (Bsz, H), ti)
         _check("A", A, (Bsz, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
         _check("lam_t", lam_t, (Bsz, H), ti)
-        _check("theta_t", theta_t, (Bsz, G, N // 2), ti)
+        _check("theta_t", theta_t, (Bsz, G, N // 2), ti, optional=_proj(d) is not None)
+        if _proj(d) is not None:
+            _proj(d).check((Bsz,), G, N, ti)
         _check("y_t", y_t, (Bsz, H, P, R), to)
     _check_bc(d)
     st = _lib().m3_decode_step(ctypes.byref(d), _ptr(h), _ptr(x_t), _ptr(x_prev), _ptr(B_t),
@@ -359,13 +398,14 @@ def m3_decode_tokens(dims: m3_dims, h, x, x_prev, B, B_prev, C, dt, A, lam, thet
 # allocation helpers (torch only provides the memory)
 def scan_prefill(x, dt, A, lam, theta, B, C, h0=None, x_prev=None, B_prev=None,
                  chunk=0, out_dtype=torch.float32, flags=0, want_hT=True, ws=None,
-                 stream=None, bc=None):
+                 stream=None, bc=None, tp=None):
     """Allocate y (and hT, workspace) and call m3_scan_prefill.  Returns (y, hT).
-    B, C and theta may have fewer head slots than x (head groups)."""
+    B, C and theta may have fewer head slots than x (head groups); with tp
+    (a ThetaProj) theta may be None."""
     Bsz, T, H, P, R = x.shape
     G, N = B.shape[2], B.shape[3]
     d = make_dims(Bsz, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G, bc)
+                  0 if G == H else G, bc, tp)
     y = torch.empty((Bsz, T, H, P, R), dtype=out_dtype, device=x.device)
     hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
     if ws is None:
@@ -406,14 +446,14 @@ def scan_prefill_backward(x, dt, A, lam, theta, B, C, dy, h0=None, x_prev=None, 
 
 def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=None,
                         B_prev=None, chunk=0, out_dtype=torch.float32, flags=0, want_hT=True,
-                        ws=None, stream=None, bc=None):
+                        ws=None, stream=None, bc=None, tp=None):
     """Allocate y (and hT, workspace) and call m3_scan_prefill_varlen on
     sequences packed into x [T, H, P, R].  Returns (y, hT)."""
     T, H, P, R = x.shape
     G, N = B.shape[1], B.shape[2]
     S = cu_seqlens.numel() - 1
     d = make_dims(S, T, H, P, N, R, chunk, dtype_code(x.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G, bc)
+                  0 if G == H else G, bc, tp)
     y = torch.empty((T, H, P, R), dtype=out_dtype, device=x.device)
     hT = torch.empty((S, H, P, N), dtype=torch.float32, device=x.device) if want_hT else None
     if ws is None:
@@ -424,14 +464,15 @@ def scan_prefill_varlen(cu_seqlens, x, dt, A, lam, theta, B, C, h0=None, x_prev=
 
 
 def decode_step(h, x_t, B_t, C_t, dt_t, A, lam_t, theta_t, x_prev=None, B_prev=None,
-                out_dtype=torch.float32, flags=0, y_t=None, stream=None, bc=None):
+                out_dtype=torch.float32, flags=0, y_t=None, stream=None, bc=None, tp=None):
     """Advance h in place by one token; returns y_t (allocated unless given).
-    B_t, C_t and theta_t may have fewer head slots than h (head groups)."""
+    B_t, C_t and theta_t may have fewer head slots than h (head groups);
+    with tp (a ThetaProj) theta_t may be None."""
     Bsz, H, P, N = h.shape
     R = x_t.shape[-1]
     G = B_t.shape[1]
     d = make_dims(Bsz, 1, H, P, N, R, 0, dtype_code(x_t.dtype), dtype_code(out_dtype), flags,
-                  0 if G == H else G, bc)
+                  0 if G == H else G, bc, tp)
     if y_t is None:
         y_t = torch.empty((Bsz, H, P, R), dtype=out_dtype, device=h.device)
     m3_decode_step(d, h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t, stream)

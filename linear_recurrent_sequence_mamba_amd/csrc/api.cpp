@@ -57,52 +57,48 @@ m3_status bc_args(const m3_dims* d, m3::BCPrep* out) {
   return M3_OK;
 }
 
+// the angle projection of dims->tp into kernel arguments (off when absent)
+m3_status tp_args(const m3_dims* d, m3::ThetaProj* out) {
+  *out = m3::ThetaProj{};
+  const m3_theta_proj* tp = d->tp;
+  if (!tp) return M3_OK;
+  if (tp->dim <= 0 || tp->dim % 32 != 0) return M3_ERR_SHAPE;
+  if (!tp->u || !tp->W) return M3_ERR_NULL;
+  if (misaligned(tp->u) || misaligned(tp->W)) return M3_ERR_ALIGN;
+  out->u = tp->u;
+  out->W = tp->W;
+  out->dim = tp->dim;
+  out->on = 1;
+  return M3_OK;
+}
+
+// the backward's chunk length (64 unless the caller asks)
 int chunk_of(const m3_dims* d) { return d->chunk > 0 ? d->chunk : 64; }
-
-}  // namespace
-
-extern "C" {
-
-const char* m3_status_str(m3_status s) {
-  // a C caller may pass any int; read its bits as an int, since a C++ load
-  // of an enum value outside the enumerators' range is undefined
-  int v;
-  memcpy(&v, &s, sizeof v);
-  switch (v) {
-    case M3_OK: return "ok";
-    case M3_ERR_NULL: return "required pointer is NULL";
-    case M3_ERR_SHAPE: return "invalid shape or flags";
-    case M3_ERR_DTYPE: return "unsupported dtype";
-    case M3_ERR_UNSUPPORTED: return "no kernel for this (headdim, dstate, rank, chunk)";
-    case M3_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case M3_ERR_WORKSPACE: return "workspace missing or too small";
-    case M3_ERR_HIP: return "HIP launch failed";
-  }
-  return "unknown status";
+// a forward prefill's chunk length: the caller's, or the library's default
+// for the shape
+int prefill_chunk_of(const m3_dims* d) {
+  return d->chunk > 0 ? d->chunk
+                      : m3::prefill_default_chunk(d->headdim, d->dstate, d->rank,
+                                                  d->in_dtype == M3_BF16);
 }
 
-int m3_last_hip_error(void) { return g_last_hip_error; }
-
-size_t m3_prefill_workspace_size(const m3_dims* d) {
-  if (check_dims(d, true) != M3_OK) return 0;
-  return m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
-                                     d->rank, chunk_of(d), d->bc != nullptr);
-}
-
-m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
-                          const void* lam, const void* theta, const void* B, const void* C,
-                          const float* h0, const void* x_prev, const void* B_prev, void* y,
-                          float* hT, void* ws, size_t ws_bytes, void* stream) {
+// m3_scan_prefill with the caller's workspace
+m3_status scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
+                       const void* lam, const void* theta, const void* B, const void* C,
+                       const float* h0, const void* x_prev, const void* B_prev, void* y,
+                       float* hT, void* ws, size_t ws_bytes, void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
   m3::BCPrep bcp;
   if ((st = bc_args(d, &bcp)) != M3_OK) return st;
-  if (!x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
+  m3::ThetaProj tpa;
+  if ((st = tp_args(d, &tpa)) != M3_OK) return st;
+  if (!x || !dt || !A || !lam || (!theta && !tpa.on) || !B || !C || !y) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return M3_ERR_ALIGN;
-  const int Q = chunk_of(d);
+  const int Q = prefill_chunk_of(d);
   const int in_bf16 = d->in_dtype == M3_BF16;
   if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16))
     return M3_ERR_UNSUPPORTED;
@@ -135,12 +131,52 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   a.bc = bcp;
+  a.tp = tpa;
   m3::prefill_carve(a, ws);
   hipError_t err = hipSuccess;
   if (m3::launch_prefill(a, in_bf16, d->out_dtype == M3_BF16,
                          static_cast<hipStream_t>(stream), &err) != 0)
     return M3_ERR_UNSUPPORTED;
   return hip_status(err);
+}
+
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_status_str(m3_status s) {
+  // a C caller may pass any int; read its bits as an int, since a C++ load
+  // of an enum value outside the enumerators' range is undefined
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "required pointer is NULL";
+    case M3_ERR_SHAPE: return "invalid shape or flags";
+    case M3_ERR_DTYPE: return "unsupported dtype";
+    case M3_ERR_UNSUPPORTED: return "no kernel for this (headdim, dstate, rank, chunk)";
+    case M3_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case M3_ERR_WORKSPACE: return "workspace missing or too small";
+    case M3_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int m3_last_hip_error(void) { return g_last_hip_error; }
+
+size_t m3_prefill_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true) != M3_OK) return 0;
+  return m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
+                                     d->rank, prefill_chunk_of(d), d->bc != nullptr);
+}
+
+m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
+                          const void* lam, const void* theta, const void* B, const void* C,
+                          const float* h0, const void* x_prev, const void* B_prev, void* y,
+                          float* hT, void* ws, size_t ws_bytes, void* stream) {
+  return scan_prefill(d, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws, ws_bytes,
+                      stream);
 }
 
 size_t m3_prefill_backward_workspace_size(const m3_dims* d) {
@@ -159,7 +195,7 @@ m3_status m3_scan_prefill_backward(const m3_dims* d, const void* x, const void* 
                                    void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
-  if (d->bc) return M3_ERR_UNSUPPORTED;
+  if (d->bc || d->tp) return M3_ERR_UNSUPPORTED;
   if (!x || !dt || !A || !lam || !theta || !B || !C || !dy) return M3_ERR_NULL;
   if (!dx || !ddt || !dA || !dlam || !dtheta || !dB || !dC) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
@@ -222,7 +258,7 @@ m3_status m3_scan_prefill_backward(const m3_dims* d, const void* x, const void* 
 size_t m3_prefill_varlen_workspace_size(const m3_dims* d) {
   if (check_dims(d, true) != M3_OK) return 0;
   return m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim, d->dstate,
-                                            d->rank, chunk_of(d), d->bc != nullptr);
+                                            d->rank, prefill_chunk_of(d), d->bc != nullptr);
 }
 
 m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, const void* x,
@@ -234,16 +270,19 @@ m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, co
   if (st != M3_OK) return st;
   m3::BCPrep bcp;
   if ((st = bc_args(d, &bcp)) != M3_OK) return st;
-  if (!cu_seqlens || !x || !dt || !A || !lam || !theta || !B || !C || !y) return M3_ERR_NULL;
+  m3::ThetaProj tpa;
+  if ((st = tp_args(d, &tpa)) != M3_OK) return st;
+  if (!cu_seqlens || !x || !dt || !A || !lam || (!theta && !tpa.on) || !B || !C || !y)
+    return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws};
   for (const void* p : ptrs)
     if (p && misaligned(p)) return M3_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return M3_ERR_ALIGN;
-  const int Q = chunk_of(d);
+  const int Q = prefill_chunk_of(d);
   const int in_bf16 = d->in_dtype == M3_BF16;
   if (!m3::prefill_supported(d->headdim, d->dstate, d->rank, Q, in_bf16) ||
-      !m3::prefill_offsets_fit(d->nheads, d->headdim, d->dstate, d->rank))
+      !m3::prefill_offsets_fit(d->nheads, d->headdim, d->dstate, d->rank, Q))
     return M3_ERR_UNSUPPORTED;
   const size_t need = m3::prefill_varlen_workspace_bytes(d->batch, d->seqlen, d->nheads,
                                                          d->headdim, d->dstate, d->rank, Q,
@@ -275,6 +314,7 @@ m3_status m3_scan_prefill_varlen(const m3_dims* d, const int32_t* cu_seqlens, co
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   a.bc = bcp;
+  a.tp = tpa;
   m3::prefill_varlen_carve(a, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = m3::launch_varlen_map(a, cu_seqlens, s);
@@ -292,7 +332,9 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
   if (st != M3_OK) return st;
   m3::BCPrep bcp;
   if ((st = bc_args(d, &bcp)) != M3_OK) return st;
-  if (!h || !x_t || !B_t || !C_t || !dt_t || !A || !lam_t || !theta_t || !y_t)
+  m3::ThetaProj tpa;
+  if ((st = tp_args(d, &tpa)) != M3_OK) return st;
+  if (!h || !x_t || !B_t || !C_t || !dt_t || !A || !lam_t || (!theta_t && !tpa.on) || !y_t)
     return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {h, x_t, x_prev, B_t, B_prev, C_t, dt_t, A, lam_t, theta_t, y_t};
@@ -323,6 +365,7 @@ m3_status m3_decode_step(const m3_dims* d, float* h, const void* x_t, const void
   a.flags = d->flags;
   a.has_prev = x_prev != nullptr;
   a.bc = bcp;
+  a.tp = tpa;
   hipError_t err = hipSuccess;
   if (m3::launch_decode(a, d->in_dtype == M3_BF16, d->out_dtype == M3_BF16,
                         static_cast<int>(units), static_cast<hipStream_t>(stream), &err) != 0)
@@ -338,6 +381,7 @@ m3_status m3_decode_tokens(const m3_dims* d, float* h, const void* x, const void
   if (st != M3_OK) return st;
   m3::BCPrep bcp;
   if ((st = bc_args(d, &bcp)) != M3_OK) return st;
+  if (d->tp) return M3_ERR_UNSUPPORTED;
   if (!h || !x || !B || !C || !dt || !A || !lam || !theta || !y) return M3_ERR_NULL;
   if ((x_prev == nullptr) != (B_prev == nullptr)) return M3_ERR_NULL;
   const void* ptrs[] = {h, x, x_prev, B, B_prev, C, dt, A, lam, theta, y};

@@ -299,7 +299,7 @@ __global__ __launch_bounds__((BwdGeo<P, N>::NT)) void k_bwd_chunk(BackwardArgs g
     sm.dcs[tid] = sm.dgam[tid] = sm.dbpr[tid] = sm.dmend[tid] = 0.0f;
   }
   if (tid < NP) sm.dphi_end[tid] = 0.0f;
-  __syncthreads();   // th_raw (in ub) is free
+  __syncthreads();   // the table scratch (in ub) is free
 
   // rotated B and C rows, x and dy
   const int64_t gi = group_index(a, b, c0, h);
@@ -862,7 +862,7 @@ void backward_carve(BackwardArgs& g, void* ws) {
 int launch_backward(const BackwardArgs& g0, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
   BackwardArgs g = g0;
   const PrefillArgs& a = g.f;
-  if (!backward_supported(a.P, a.N, a.R, a.Q) || !prefill_offsets_fit(a.H, a.P, a.N, a.R)) return -1;
+  if (!backward_supported(a.P, a.N, a.R, a.Q) || !prefill_offsets_fit(a.H, a.P, a.N, a.R, a.Q)) return -1;
   // the forward chunk entry states and h_T, into the workspace
   PrefillArgs fw = a;
   fw.states_only = 1;

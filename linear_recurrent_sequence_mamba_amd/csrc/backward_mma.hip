@@ -776,7 +776,7 @@ struct TSmem {
 // a single input's t-side block is 64 KB of LDS: two fit on a CU once the
 // registers allow two waves per SIMD (a few spill; the call measured 2-3% faster)
 template <class Pol, int R>
-constexpr int t_min_waves() { return R == 1 && std::is_same<Pol, PolF16>::value ? 2 : 1; }
+constexpr int t_min_waves() { return R == 1 && std::is_same<Pol, PolHalf>::value ? 2 : 1; }
 
 template <class Pol, typename TI, typename TY, int P, int N, int R>
 __global__ __launch_bounds__((GeoU<P, N, R>::NT)) __attribute__((amdgpu_waves_per_eu(t_min_waves<Pol, R>()))) void k_bwd_t(BackwardArgs g) {
@@ -1338,7 +1338,7 @@ int dispatch_mma(const BackwardArgs& g, hipStream_t s, hipError_t* e) {
 
 int launch_backward_mma(const BackwardArgs& g, int in_bf16, int dy_bf16, hipStream_t s, hipError_t* e) {
   if (in_bf16)
-    return dy_bf16 ? dispatch_mma<PolF16, bf16_t, bf16_t>(g, s, e) : dispatch_mma<PolF16, bf16_t, float>(g, s, e);
+    return dy_bf16 ? dispatch_mma<PolHalf, bf16_t, bf16_t>(g, s, e) : dispatch_mma<PolHalf, bf16_t, float>(g, s, e);
   return dy_bf16 ? dispatch_mma<PolF32, float, bf16_t>(g, s, e) : dispatch_mma<PolF32, float, float>(g, s, e);
 }
 

@@ -4,12 +4,14 @@
 // public ABI.
 #pragma once
 
+#include <type_traits>
+
 #include "m3_device.h"
 #include "m3_launch.h"
 
 namespace m3 {
 
-constexpr int kQ = 64;         // chunk length
+constexpr int kQ = 64;         // default chunk length (the backward's only one)
 constexpr int kRB = 64;        // virtual rows per output block / u-block
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
@@ -29,19 +31,36 @@ __device__ __forceinline__ f2 cos_sin_reduced(float ang) {
 // The angle table is token-major [t][k] for kernels whose lanes run along
 // the pairs of one token, or pair-major [k][t] (rows padded by one entry, so
 // both a column and a row of the table fall on distinct banks) for kernels
-// whose lanes run along the tokens.
-template <int N, bool ROT, bool KMAJ = false>
+// whose lanes run along the tokens.  Q is the chunk length.
+template <int N, bool ROT, bool KMAJ = false, int Q = kQ>
 struct Tables {
   static constexpr int NP = N / 2;
-  static constexpr int TS = KMAJ ? kQ + 1 : NP;   // row stride
-  double cs[kQ];      // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
-  float dt[kQ];
-  float gam[kQ];      // lam dt
-  float bpr[kQ];      // (1 - lam) dt
-  float aux[kQ];      // e^{cs_t} (outputs) or the chunk-state weights W_t
+  static constexpr int CQ = Q;
+  static constexpr int TS = KMAJ ? Q + 1 : NP;   // row stride
+  double cs[Q];       // chunk-local cumulative log-decay sum_{r<=t} dt_r A_r
+  float dt[Q];
+  float gam[Q];       // lam dt
+  float bpr[Q];       // (1 - lam) dt
+  float aux[Q];       // e^{cs_t} (outputs) or the chunk-state weights W_t
   double phi_end[NP];
-  alignas(16) typename std::conditional<ROT, f2, float>::type tab[(KMAJ ? NP : kQ) * TS];
+  alignas(16) typename std::conditional<ROT, f2, float>::type tab[(KMAJ ? NP : Q) * TS];
   static __device__ __forceinline__ int at(int t, int k) { return KMAJ ? k * TS + t : t * TS + k; }
+  // the phase input of (t, k), held in the angle's own slot until
+  // chunk_tables replaces it by the angle (by the same thread)
+  __device__ __forceinline__ void put_raw(int t, int k, float v) {
+    if constexpr (ROT) {
+      tab[at(t, k)] = f2{v, 0.0f};
+    } else {
+      tab[at(t, k)] = v;
+    }
+  }
+  __device__ __forceinline__ float raw(int t, int k) const {
+    if constexpr (ROT) {
+      return tab[at(t, k)].x;
+    } else {
+      return tab[at(t, k)];
+    }
+  }
   // Phi_t (mode 0) or Phi_end - Phi_t (mode 1), reduced to [-pi, pi]
   __device__ __forceinline__ void set(int t, int k, float ang) {
     if constexpr (ROT) {
@@ -95,6 +114,7 @@ struct ChunkRef {
   bool next;
   int64_t id;
 };
+template <int Q = kQ>
 __device__ __forceinline__ bool chunk_ref(const PrefillArgs& a, int c, int h, int b, ChunkRef& r) {
   if (c >= a.nchunk) return false;   // grid padding
   if (a.cmap) {
@@ -102,62 +122,18 @@ __device__ __forceinline__ bool chunk_ref(const PrefillArgs& a, int c, int h, in
     if (e.x < 0) return false;
     r.bt = 0;
     r.t0 = e.y;
-    r.Lc = min(kQ, e.z - e.y);
-    r.next = e.y + kQ < e.z;
+    r.Lc = min(Q, e.z - e.y);
+    r.next = e.y + Q < e.z;
     r.id = (int64_t)h * a.nchunk + c;
   } else {
     r.bt = b;
-    r.t0 = c * kQ;
-    r.Lc = min(kQ, a.T - r.t0);
+    r.t0 = c * Q;
+    r.Lc = min(Q, a.T - r.t0);
     r.next = c + 1 < a.nchunk;
     r.id = ((int64_t)b * a.H + h) * a.nchunk + c;
   }
   return true;
 }
-
-// Raw 16-byte vectors of eight input elements, held in registers between
-// the load that is issued early and the store into LDS.
-template <typename TI>
-struct Vec8;
-template <>
-struct Vec8<bf16_t> {
-  uint4 u;
-  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { u = uint4{0u, 0u, 0u, 0u}; }
-  __device__ __forceinline__ void get(float* v) const {
-    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
-    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
-  }
-  // the values, or zeros when keep is false
-  __device__ __forceinline__ void get(float* v, bool keep) const {
-    const uint32_t m = keep ? 0xffffffffu : 0u;
-    const uint4 k = uint4{u.x & m, u.y & m, u.z & m, u.w & m};
-    v[0] = __uint_as_float(k.x << 16); v[1] = __uint_as_float(k.x & 0xffff0000u);
-    v[2] = __uint_as_float(k.y << 16); v[3] = __uint_as_float(k.y & 0xffff0000u);
-    v[4] = __uint_as_float(k.z << 16); v[5] = __uint_as_float(k.z & 0xffff0000u);
-    v[6] = __uint_as_float(k.w << 16); v[7] = __uint_as_float(k.w & 0xffff0000u);
-  }
-};
-template <>
-struct Vec8<float> {
-  f4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f4*>(p);
-    b = *reinterpret_cast<const f4*>(p + 4);
-  }
-  __device__ __forceinline__ void zero() { a = b = f4{0, 0, 0, 0}; }
-  __device__ __forceinline__ void get(float* v) const {
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  __device__ __forceinline__ void get(float* v, bool keep) const {
-    get(v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = keep ? v[j] : 0.0f;
-  }
-};
 
 // One 64-virtual-row block of a per-token array with E elements per token
 // (B or C: E = N R; x: E = P R) as 16-byte vectors spread over the block's
@@ -206,12 +182,14 @@ struct RowBlock {
   __device__ __forceinline__ void get(int i, float* v) const { raw[i].get(v, (okm >> i) & 1u); }
 };
 
-// Q x N/2 phase inputs of the chunk plus the first wave's token scalars
-template <typename TI, int N, int NT>
+// Q x N/2 phase inputs of the chunk plus the token scalars of the first Q
+// threads
+template <typename TI, int N, int NT, int Q = kQ>
 struct ThetaBlock {
+  static_assert(NT >= Q, "one thread per token for the token scalars");
   static constexpr int NP = N / 2;
   static constexpr int VPT = NP / 8;
-  static constexpr int NV = kQ * VPT;
+  static constexpr int NV = Q * VPT;
   static constexpr int IT = (NV + NT - 1) / NT;
   Vec8<TI> raw[IT];
   uint32_t okm;      // bit i: raw[i] holds phases of the chunk's tokens
@@ -219,18 +197,21 @@ struct ThetaBlock {
   float d_, l_, A_;  // as loaded (any value when !tok)
   // every lane loads from a valid address (the chunk's first token when it
   // has none of its own) and the values are masked where they are read: no
-  // branch around a load, so no load waits for the ones before it
+  // branch around a load, so no load waits for the ones before it.  With
+  // the angle projection the phases are not read (project_theta makes them).
   __device__ __forceinline__ void load(const PrefillArgs& a, int b, int h, int c0, int Lc) {
-    const TI* __restrict__ th = static_cast<const TI*>(a.theta) + group_index(a, b, c0, h) * NP;
-    const int tstride = a.G * NP;
     okm = 0u;
+    if (!a.tp.on) {   // block-uniform
+      const TI* __restrict__ th = static_cast<const TI*>(a.theta) + group_index(a, b, c0, h) * NP;
+      const int tstride = a.G * NP;
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int vi = threadIdx.x + NT * i;
-      const int t = vi / VPT, kv = vi % VPT;
-      const bool ok = vi < NV && t < Lc;
-      raw[i].load(th + (ok ? t * tstride + 8 * kv : 0));
-      okm |= static_cast<uint32_t>(ok) << i;
+      for (int i = 0; i < IT; ++i) {
+        const int vi = threadIdx.x + NT * i;
+        const int t = vi / VPT, kv = vi % VPT;
+        const bool ok = vi < NV && t < Lc;
+        raw[i].load(th + (ok ? t * tstride + 8 * kv : 0));
+        okm |= static_cast<uint32_t>(ok) << i;
+      }
     }
     const int tid = threadIdx.x;
     tok = tid < Lc;
@@ -252,47 +233,60 @@ struct ThetaBlock {
 // then the angles reduced to [-pi, pi]: Phi_t (mode 0) or Phi_end - Phi_t
 // (mode 1), kept as (cos, sin) or as the angle (see Tables).  scr is LDS
 // scratch that is free until the tables are built.
-template <int N, int NT>
+template <int N, int NT, int Q = kQ>
 struct TableScratch {
-  float th_raw[kQ * (N / 2)];
-  double seg[NT];
+  double seg[NT];        // each thread's total of its segment of one pair's phases
+  double wtot[Q / 64];   // each wave's total of the log-decay scan
 };
 
-template <typename TI, int N, int NT, bool ROT, bool KMAJ>
-__device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& tb_in, int Lc,
-                             Tables<N, ROT, KMAJ>& tb, TableScratch<N, NT>& scr, int mode) {
-  float* th_raw = scr.th_raw;
+template <typename TI, int N, int NT, bool ROT, bool KMAJ, int Q>
+__device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT, Q>& tb_in, int Lc,
+                             Tables<N, ROT, KMAJ, Q>& tb, TableScratch<N, NT, Q>& scr, int mode) {
+  using TB = ThetaBlock<TI, N, NT, Q>;
+  static_assert(Q % 64 == 0, "whole waves of tokens");
   constexpr int NP = N / 2;
   const int tid = threadIdx.x;
-  if (tid < 64) {
+  double lv = 0.0;
+  if (tid < Q) {   // each wave scans its 64 tokens; later waves add the earlier totals below
     const float d = tb_in.d(), l = tb_in.l();
-    double lv = (double)d * (double)tb_in.A();
+    lv = (double)d * (double)tb_in.A();
+    const int lane = tid & 63;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(lv, off, 64);
-      if (tid >= off) lv += o;
+      if (lane >= off) lv += o;
     }
-    tb.cs[tid] = lv;
+    if constexpr (Q > 64) {
+      if (lane == 63) scr.wtot[tid >> 6] = lv;
+    }
     tb.dt[tid] = d;
     tb.gam[tid] = l * d;
     tb.bpr[tid] = (1.0f - l) * d;
   }
+  if (!a.tp.on) {   // else project_theta has put the phase inputs (block-uniform)
 #pragma unroll
-  for (int i = 0; i < ThetaBlock<TI, N, NT>::IT; ++i) {
-    const int vi = tid + NT * i;
-    if (vi < ThetaBlock<TI, N, NT>::NV) {
-      float v[8];
-      tb_in.get(i, v);
-      const int t = vi / ThetaBlock<TI, N, NT>::VPT, kv = vi % ThetaBlock<TI, N, NT>::VPT;
+    for (int i = 0; i < TB::IT; ++i) {
+      const int vi = tid + NT * i;
+      if (vi < TB::NV) {
+        float v[8];
+        tb_in.get(i, v);
+        const int t = vi / TB::VPT, kv = vi % TB::VPT;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) th_raw[t * NP + 8 * kv + j] = v[j];
+        for (int j = 0; j < 8; ++j) tb.put_raw(t, 8 * kv + j, v[j]);
+      }
     }
   }
   __syncthreads();
+  if (tid < Q) {
+    if constexpr (Q > 64) {
+      for (int w = 0; w < (tid >> 6); ++w) lv += scr.wtot[w];
+    }
+    tb.cs[tid] = lv;   // read after the barriers below
+  }
 
   constexpr int NSEG = NT / NP;
-  constexpr int SEG = kQ / NSEG;
-  static_assert(NSEG >= 1 && kQ % NSEG == 0, "phase segments");
+  constexpr int SEG = Q / NSEG;
+  static_assert(NSEG >= 1 && Q % NSEG == 0, "phase segments");
   const int k = tid % NP, sg = tid / NP;
   const bool angle = (a.flags & kThetaIsAngle) != 0;
   double loc[SEG];
@@ -300,7 +294,7 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
     const int t = sg * SEG + i;
-    const double tv = (double)th_raw[t * NP + k];
+    const double tv = (double)tb.raw(t, k);
     run += angle ? tv : tv * (double)tb.dt[t];
     loc[i] = run;
   }
@@ -320,6 +314,59 @@ __device__ void chunk_tables(const PrefillArgs& a, const ThetaBlock<TI, N, NT>& 
     }
   }
   __syncthreads();
+}
+
+// The angle projection of a chunk [xxxxx.co.kr Mamba-3 article, section
+// 1.2: data-dependent angles]: th[t][k] = sum_j W[g][k][j] u[t][j] for the
+// chunk's tokens t < Lc (zero for the rows past them), head group g, into
+// the chunk's angle table, where chunk_tables reads them.  A 16 x 16 (token, pair) tile per
+// wave at a time on the matrix cores, reading the operands straight from
+// global memory in the fragment layout: bf16 inputs on
+// v_mfma_f32_16x16x32_bf16 (exact products, fp32 sums), fp32 inputs on
+// v_mfma_f32_16x16x4_f32.  Lane l holds token row l % 16 of the A operand and
+// pair l % 16 of the B operand; its D values are pair l % 16 of tokens
+// 4 (l / 16) .. 4 (l / 16) + 3.
+template <typename TI, int N, int NT, int Q, class Tab>
+__device__ void project_theta(const PrefillArgs& a, int bt, int h, int c0, int Lc, Tab& tb) {
+  constexpr int NP = N / 2;
+  constexpr int TT = Q / 16, KT = (NP + 15) / 16;
+  const int D = a.tp.dim;
+  const TI* __restrict__ U = static_cast<const TI*>(a.tp.u) + ((int64_t)bt * a.T + c0) * D;
+  const TI* __restrict__ Wg = static_cast<const TI*>(a.tp.W) + (int64_t)head_group(a, h) * NP * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  for (int tile = wave; tile < TT * KT; tile += NT / 64) {
+    const int t0 = 16 * (tile / KT), k0 = 16 * (tile % KT);
+    // rows past the chunk or the pairs read a valid row; their results are dropped
+    const TI* __restrict__ ur = U + (int64_t)min(t0 + l16, Lc - 1) * D;
+    const TI* __restrict__ wr = Wg + (int64_t)min(k0 + l16, NP - 1) * D;
+    f4 acc = f4{0, 0, 0, 0};
+    if constexpr (std::is_same<TI, bf16_t>::value) {
+      for (int j0 = 0; j0 < D; j0 += 32) {
+        const uint4 av = *reinterpret_cast<const uint4*>(ur + j0 + 8 * g);
+        const uint4 bv = *reinterpret_cast<const uint4*>(wr + j0 + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bh8, av),
+                                                      __builtin_bit_cast(bh8, bv), acc, 0, 0, 0);
+      }
+    } else {
+      for (int j0 = 0; j0 < D; j0 += 16) {
+        const f4 av = *reinterpret_cast<const f4*>(ur + j0 + 4 * g);
+        const f4 bv = *reinterpret_cast<const f4*>(wr + j0 + 4 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
+      }
+    }
+    const int k = k0 + l16;
+    if (k < NP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * g + i;
+        tb.put_raw(t, k, t < Lc ? acc[i] : 0.0f);
+      }
+    }
+  }
 }
 
 // element i of an input array of type T

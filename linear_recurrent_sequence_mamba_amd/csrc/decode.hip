@@ -35,22 +35,57 @@ template <typename TI, int N>
 struct TokenIn {
   Raw1<TI> d, l, th;
   float A;
+  float thp;   // with the angle projection: the projected phase input of pair threadIdx.x / TPP
 };
+
+// with the angle projection, TPP consecutive threads make one pair's phase
+// input between them
+template <int N>
+constexpr int proj_tpp() { return 256 / (N / 2); }
 
 // (batch, group) slot of B, C and theta for the unit bh = (batch, head)
 __device__ __forceinline__ int64_t group_slot(const DecodeArgs& a, int bh) {
   return (int64_t)(bh / a.H) * a.G + (bh % a.H) / (a.H / a.G);
 }
 
-template <typename TI, int N>
+template <typename TI, int N, bool PROJ>
 __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh) {
   TokenIn<TI, N> in;
   const int head = bh % a.H;
   in.d.load(static_cast<const TI*>(a.dt), bh);
   in.l.load(static_cast<const TI*>(a.lam), bh);
   in.A = (a.flags & kAPerToken) ? a.A[bh] : a.A[head];
-  const int k = min(static_cast<int>(threadIdx.x), N / 2 - 1);
-  in.th.load(static_cast<const TI*>(a.theta), group_slot(a, bh) * (N / 2) + k);
+  if constexpr (PROJ) {
+    // the angle projection [xxxxx.co.kr Mamba-3 article, section 1.2]:
+    // theta_k = sum_j W[g][k][j] u[b][j], each of TPP threads summing every
+    // TPP-th 16-byte piece of the row, then a lane-group sum (before the
+    // state stream, which waits for nothing issued after it)
+    constexpr int TPP = proj_tpp<N>();
+    constexpr int VPV = 16 / sizeof(TI);
+    static_assert(TPP >= 1 && TPP <= 64 && (TPP & (TPP - 1)) == 0, "pair groups of lanes");
+    const int D = a.tp.dim;
+    const int k = threadIdx.x / TPP, part = threadIdx.x % TPP;
+    const TI* __restrict__ ur = static_cast<const TI*>(a.tp.u) + (int64_t)(bh / a.H) * D;
+    const TI* __restrict__ wr = static_cast<const TI*>(a.tp.W) +
+                                ((group_slot(a, bh) % a.G) * (N / 2) + k) * (int64_t)D;
+    float s = 0.0f;
+    for (int v = part; v < D / VPV; v += TPP) {
+      if constexpr (VPV == 8) {
+        float uv[8], wv[8];
+        ld8(ur, (int64_t)v * 8, uv);
+        ld8(wr, (int64_t)v * 8, wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += uv[e] * wv[e];
+      } else {
+        const f4 uv = ld4(ur, (int64_t)v * 4), wv = ld4(wr, (int64_t)v * 4);
+        s += uv.x * wv.x + uv.y * wv.y + uv.z * wv.z + uv.w * wv.w;
+      }
+    }
+    in.thp = group_sum<TPP>(s);
+  } else {
+    const int k = min(static_cast<int>(threadIdx.x), N / 2 - 1);
+    in.th.load(static_cast<const TI*>(a.theta), group_slot(a, bh) * (N / 2) + k);
+  }
   // the compiler may not move these loads past this point (towards their
   // uses, which come after the state stream)
   asm volatile("" ::: "memory");
@@ -58,16 +93,17 @@ __device__ __forceinline__ TokenIn<TI, N> token_load(const DecodeArgs& a, int bh
 }
 
 // alpha, beta, gamma; (cos, sin) of the token's phase per pair into LDS
-template <typename TI, int N>
+template <typename TI, int N, bool PROJ>
 __device__ __forceinline__ void token_finish(const DecodeArgs& a, const TokenIn<TI, N>& in,
                                              float& alpha, float& beta, float& gamma, f2* cs_sh) {
   const float d = in.d.f(), l = in.l.f();
   alpha = expf(d * in.A);
   beta = (1.0f - l) * d * alpha;
   gamma = l * d;
-  const int k = threadIdx.x;
-  if (k < N / 2) {
-    const float th = in.th.f();
+  constexpr int TPP = PROJ ? proj_tpp<N>() : 1;
+  const int k = threadIdx.x / TPP;
+  if (k < N / 2 && threadIdx.x % TPP == 0) {
+    const float th = PROJ ? in.thp : in.th.f();
     const float phi = (a.flags & kThetaIsAngle) ? th : d * th;
     float s, c;
     sincosf(phi, &s, &c);
@@ -77,7 +113,7 @@ __device__ __forceinline__ void token_finish(const DecodeArgs& a, const TokenIn<
 
 // --------------------------------------------------------------------------
 // single input / single output
-template <typename TI, typename TO, int N, bool PREV, bool PREP>
+template <typename TI, typename TO, int N, bool PREV, bool PREP, bool PROJ>
 __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   constexpr int LPR = N / 4;           // lanes per state row
   constexpr int RPW = 64 / LPR;        // rows per wave per pass
@@ -97,7 +133,7 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   const TI* __restrict__ xp = static_cast<const TI*>(a.xp) + (int64_t)bh * P;
   TO* __restrict__ y = static_cast<TO*>(a.y) + (int64_t)bh * P;
 
-  const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
+  const TokenIn<TI, N> tin = token_load<TI, N, PROJ>(a, bh);
   const int64_t vec = group_slot(a, bh) * N + n0;
   f4 bt = ld4(static_cast<const TI*>(a.Bt), vec);
   f4 bp = PREV ? ld4(static_cast<const TI*>(a.Bp), vec) : f4{0, 0, 0, 0};
@@ -128,7 +164,7 @@ __global__ __launch_bounds__(256) void k_decode_siso(DecodeArgs a) {
   }
 
   float alpha, beta, gamma;
-  token_finish<TI, N>(a, tin, alpha, beta, gamma, cs_sh);
+  token_finish<TI, N, PROJ>(a, tin, alpha, beta, gamma, cs_sh);
   if constexpr (PREP) {
     // a row's N/4 lanes hold the whole of B, B_prev and C
     auto prep = [&](f4 v, f4 w, f4 b) {
@@ -183,7 +219,7 @@ __device__ __forceinline__ int ncol(int t, int g) { return 16 * t + 4 * g; }
 
 // (the B/C preparation's prologue would otherwise cost the rank <= 4
 // kernels a wave per SIMD: the register count is held to four waves)
-template <typename TI, typename TO, int N, int R, bool PREV, bool PREP>
+template <typename TI, typename TO, int N, int R, bool PREV, bool PREP, bool PROJ>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(DecodeArgs a) {
   constexpr int NT = N / 16;          // 16-column tiles per state row block
@@ -210,7 +246,7 @@ __attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(
   const TI* __restrict__ xp = static_cast<const TI*>(a.xp) + (int64_t)bh * P * R;
   TO* __restrict__ y = static_cast<TO*>(a.y) + (int64_t)bh * P * R;
 
-  const TokenIn<TI, N> tin = token_load<TI, N>(a, bh);
+  const TokenIn<TI, N> tin = token_load<TI, N, PROJ>(a, bh);
   float eb[PER], ep[PER], ec[PER];
   {
     const int64_t gs = group_slot(a, bh);
@@ -259,7 +295,7 @@ __attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(
   }
 
   float alpha, beta, gamma;
-  token_finish<TI, N>(a, tin, alpha, beta, gamma, cs_sh);
+  token_finish<TI, N, PROJ>(a, tin, alpha, beta, gamma, cs_sh);
   if constexpr (RP != R) {
     for (int i = tid; i < N * RP; i += 256) bt_sh[i] = bp_sh[i] = c_sh[i] = 0.0f;
     __syncthreads();
@@ -400,30 +436,40 @@ __attribute__((amdgpu_waves_per_eu(PREP && R <= 4 ? 4 : 1))) void k_decode_mimo(
 }
 
 // --------------------------------------------------------------------------
-template <typename TI, typename TO, int N>
-static hipError_t launch_siso(const DecodeArgs& a, int units, hipStream_t s) {
+template <typename TI, typename TO, int N, bool PROJ>
+static hipError_t launch_siso_p(const DecodeArgs& a, int units, hipStream_t s) {
   const dim3 g(units), b(256);
   if (a.bc.on) {
-    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, true>), g, b, 0, s, a);
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, true, PROJ>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, true, PROJ>), g, b, 0, s, a);
   } else {
-    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, false>), g, b, 0, s, a);
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso<TI, TO, N, true, false, PROJ>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso<TI, TO, N, false, false, PROJ>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
+template <typename TI, typename TO, int N>
+static hipError_t launch_siso(const DecodeArgs& a, int units, hipStream_t s) {
+  return a.tp.on ? launch_siso_p<TI, TO, N, true>(a, units, s)
+                 : launch_siso_p<TI, TO, N, false>(a, units, s);
+}
 
-template <typename TI, typename TO, int N, int R>
-static hipError_t launch_mimo(const DecodeArgs& a, int units, hipStream_t s) {
+template <typename TI, typename TO, int N, int R, bool PROJ>
+static hipError_t launch_mimo_p(const DecodeArgs& a, int units, hipStream_t s) {
   const dim3 g(units), b(256);
   if (a.bc.on) {
-    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, true>), g, b, 0, s, a);
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, true, PROJ>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, true, PROJ>), g, b, 0, s, a);
   } else {
-    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, false>), g, b, 0, s, a);
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, true, false, PROJ>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo<TI, TO, N, R, false, false, PROJ>), g, b, 0, s, a);
   }
   return hipGetLastError();
+}
+template <typename TI, typename TO, int N, int R>
+static hipError_t launch_mimo(const DecodeArgs& a, int units, hipStream_t s) {
+  return a.tp.on ? launch_mimo_p<TI, TO, N, R, true>(a, units, s)
+                 : launch_mimo_p<TI, TO, N, R, false>(a, units, s);
 }
 
 template <typename TI, typename TO>

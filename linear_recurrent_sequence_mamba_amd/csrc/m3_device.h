@@ -13,6 +13,8 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bh8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bh2 __attribute__((ext_vector_type(2)));
 
 // bf16 travels as raw 16-bit patterns; fp32 as float.
 struct bf16_t {
@@ -136,6 +138,50 @@ struct RawVec<bf16_t, K> {
         o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
       }
     }
+  }
+};
+
+// Raw 16-byte vectors of eight input elements, held in registers between
+// the load that is issued early and the store into LDS.
+template <typename TI>
+struct Vec8;
+template <>
+struct Vec8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { u = uint4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+  // the values, or zeros when keep is false
+  __device__ __forceinline__ void get(float* v, bool keep) const {
+    const uint32_t m = keep ? 0xffffffffu : 0u;
+    const uint4 k = uint4{u.x & m, u.y & m, u.z & m, u.w & m};
+    v[0] = __uint_as_float(k.x << 16); v[1] = __uint_as_float(k.x & 0xffff0000u);
+    v[2] = __uint_as_float(k.y << 16); v[3] = __uint_as_float(k.y & 0xffff0000u);
+    v[4] = __uint_as_float(k.z << 16); v[5] = __uint_as_float(k.z & 0xffff0000u);
+    v[6] = __uint_as_float(k.w << 16); v[7] = __uint_as_float(k.w & 0xffff0000u);
+  }
+};
+template <>
+struct Vec8<float> {
+  f4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f4*>(p);
+    b = *reinterpret_cast<const f4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void get(float* v, bool keep) const {
+    get(v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = keep ? v[j] : 0.0f;
   }
 };
 

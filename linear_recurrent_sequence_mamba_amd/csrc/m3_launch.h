@@ -24,6 +24,15 @@ struct BCPrep {
   int on;
 };
 
+// the angle projection applied inside the kernels when `on`:
+// theta[.., g, k] = sum_j W[g][k][j] u[.., j] (u and W in the input dtype)
+struct ThetaProj {
+  const void* u;   // [tokens, D]
+  const void* W;   // [G, N/2, D]
+  int dim;         // D, a multiple of 32
+  int on;
+};
+
 struct DecodeArgs {
   float* h;
   const void* x;
@@ -42,6 +51,7 @@ struct DecodeArgs {
   uint32_t flags;
   int has_prev;
   BCPrep bc;
+  ThetaProj tp;
 };
 
 bool decode_supported(int P, int N, int R);
@@ -81,12 +91,16 @@ struct PrefillArgs {
   uint32_t flags;
   int has_prev;
   BCPrep bc;
+  ThetaProj tp;
   float* rsB;      // with bc.on: [units, Q, R] inverse RMS of the chunk's B rows
   int states_only; // stop after the chunk entry states (and h_T): no outputs
 };
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16);
-bool prefill_offsets_fit(int H, int P, int N, int R);
+// the chunk length a prefill call with dims->chunk = 0 takes
+constexpr int kPrefillChunkR1 = 128;
+int prefill_default_chunk(int P, int N, int R, int in_bf16);
+bool prefill_offsets_fit(int H, int P, int N, int R, int Q);
 size_t prefill_workspace_bytes(int Bsz, int T, int H, int P, int N, int R, int Q, bool prep);
 // carve-ups read a.bc.on, so set it first
 void prefill_carve(PrefillArgs& a, void* ws);

@@ -270,6 +270,171 @@ struct PolF16 {
 };
 
 
+// PolB16: the same three-product split with bf16 parts on
+// v_mfma_f32_16x16x32_bf16.  hi = bf16(x) (round to nearest even), lo =
+// bf16(x - hi) with x - hi exact in fp32, so hi + lo carries 16-17
+// significant bits (relative error <= 2^-17) and, since bf16 has fp32's
+// exponent range, every finite fp32 operand splits without overflow or
+// precision lost to subnormals (fp16 parts would overflow above 65504 and
+// lose bits below about 2^-3 of lo's range).  x, a bf16 input, is exact
+// as one bf16 part.
+struct PolB16 {
+  static constexpr int KS = 32;
+  static constexpr int DT = 2;
+  struct Frag {
+    bh8 hi, lo;
+  };
+  typedef bh8 XFrag;
+  static constexpr int PAD = 4;   // as PolF16: rows 2 (mod 32) dwords long
+  template <int ROWS, int K>
+  struct Store {
+    uint16_t hi[ROWS][K + PAD];
+    uint16_t lo[ROWS][K + PAD];
+  };
+  template <int ROWS, int K>
+  struct XStore {
+    uint16_t v[ROWS][K + PAD];
+  };
+  static __device__ __forceinline__ bh8 ld8(const uint16_t* p) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + 4);
+    return __builtin_bit_cast(bh8, uint4{a.x, a.y, b.x, b.y});
+  }
+  static __device__ __forceinline__ void st8(uint16_t* p, uint4 v) {
+    *reinterpret_cast<uint2*>(p) = uint2{v.x, v.y};
+    *reinterpret_cast<uint2*>(p + 4) = uint2{v.z, v.w};
+  }
+  // two values, packed (element 0 in the low half).  The empty asm makes
+  // each input one fixed register value, so FP contraction cannot form lo
+  // from an unrounded product that hi was not rounded from.
+  static __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    asm("" : "+v"(x0), "+v"(x1));
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bh2));
+    const float h0 = __uint_as_float(h << 16), h1 = __uint_as_float(h & 0xffff0000u);
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0 - h0, x1 - h1}, bh2));
+  }
+  static __device__ __forceinline__ void split8(const float* v, uint4& hi, uint4& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+    hi = uint4{h[0], h[1], h[2], h[3]};
+    lo = uint4{l[0], l[1], l[2], l[3]};
+  }
+  // one bf16 value exactly (x is a bf16 input)
+  static __device__ __forceinline__ uint16_t exact(float x) {
+    return static_cast<uint16_t>(__float_as_uint(x) >> 16);
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ void put(Store<ROWS, K>& s, int r, int k, float x) {
+    uint32_t h, l;
+    split2(x, 0.0f, h, l);
+    s.hi[r][k] = static_cast<uint16_t>(h);
+    s.lo[r][k] = static_cast<uint16_t>(l);
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ void putx(XStore<ROWS, K>& s, int r, int k, float x) {
+    s.v[r][k] = exact(x);
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ void put8(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    uint4 hi, lo;
+    split8(v, hi, lo);
+    st8(&s.hi[r][k0], hi);
+    st8(&s.lo[r][k0], lo);
+  }
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putn(Store<ROWS, K>& s, int r, int k0, const float* v) {
+    if constexpr (M == 4) {
+      uint32_t h0, l0, h1, l1;
+      split2(v[0], v[1], h0, l0);
+      split2(v[2], v[3], h1, l1);
+      *reinterpret_cast<uint2*>(&s.hi[r][k0]) = uint2{h0, h1};
+      *reinterpret_cast<uint2*>(&s.lo[r][k0]) = uint2{l0, l1};
+    } else if constexpr (M == 2) {
+      uint32_t h0, l0;
+      split2(v[0], v[1], h0, l0);
+      *reinterpret_cast<uint32_t*>(&s.hi[r][k0]) = h0;
+      *reinterpret_cast<uint32_t*>(&s.lo[r][k0]) = l0;
+    } else {
+      static_assert(M == 1, "putn");
+      put(s, r, k0, v[0]);
+    }
+  }
+  template <int M, int ROWS, int K>
+  static __device__ __forceinline__ void putxn(XStore<ROWS, K>& s, int r, int k0, const float* v) {
+    if constexpr (M == 4) {
+      *reinterpret_cast<uint2*>(&s.v[r][k0]) =
+          uint2{exact(v[0]) | (static_cast<uint32_t>(exact(v[1])) << 16),
+                exact(v[2]) | (static_cast<uint32_t>(exact(v[3])) << 16)};
+    } else if constexpr (M == 2) {
+      *reinterpret_cast<uint32_t*>(&s.v[r][k0]) =
+          exact(v[0]) | (static_cast<uint32_t>(exact(v[1])) << 16);
+    } else {
+      static_assert(M == 1, "putxn");
+      s.v[r][k0] = exact(v[0]);
+    }
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ Frag frag(const Store<ROWS, K>& s, int row0, int k0, int lane) {
+    const int r = row0 + (lane & 15), k = k0 + 8 * (lane >> 4);
+    return Frag{ld8(&s.hi[r][k]), ld8(&s.lo[r][k])};
+  }
+  static __device__ __forceinline__ Frag make(const float* v) {
+    uint4 hi, lo;
+    split8(v, hi, lo);
+    return Frag{__builtin_bit_cast(bh8, hi), __builtin_bit_cast(bh8, lo)};
+  }
+  // slot 8g+j <-> k0 + 4g + j (j < 4) and k0 + 16 + 4g + (j - 4) (j >= 4)
+  template <int ROWS, int K>
+  static __device__ __forceinline__ XFrag fragx_d(const XStore<ROWS, K>& s, int col0, int k0, int lane) {
+    const int r = col0 + (lane & 15), g = lane >> 4;
+    const uint2 a = *reinterpret_cast<const uint2*>(&s.v[r][k0 + 4 * g]);
+    const uint2 b = *reinterpret_cast<const uint2*>(&s.v[r][k0 + 16 + 4 * g]);
+    return __builtin_bit_cast(bh8, uint4{a.x, a.y, b.x, b.y});
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ XFrag fragx_c(const XStore<ROWS, K>& s, int col0, int k0, int lane) {
+    return ld8(&s.v[col0 + (lane & 15)][k0 + 8 * (lane >> 4)]);
+  }
+  static __device__ __forceinline__ Frag frag_from_d(const f4* d) {
+    const float v[8] = {d[0].x, d[0].y, d[0].z, d[0].w, d[1].x, d[1].y, d[1].z, d[1].w};
+    return make(v);
+  }
+  static __device__ __forceinline__ f4 mma(const Frag& a, const Frag& b, f4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+  }
+  static __device__ __forceinline__ f4 mma_x(const Frag& a, const XFrag& b, f4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b, acc, 0, 0, 0);
+    return acc;
+  }
+  static __device__ __forceinline__ f4 mma_xa(const XFrag& a, const Frag& b, f4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.lo, acc, 0, 0, 0);
+    return acc;
+  }
+  template <int ROWS, int K>
+  static __device__ __forceinline__ Frag fragp(const Store<ROWS, K>& s, int col0, int k0, int lane) {
+    const int r = col0 + (lane & 15), g = lane >> 4;
+    const uint2 a = *reinterpret_cast<const uint2*>(&s.hi[r][k0 + 4 * g]);
+    const uint2 b = *reinterpret_cast<const uint2*>(&s.hi[r][k0 + 16 + 4 * g]);
+    const uint2 c = *reinterpret_cast<const uint2*>(&s.lo[r][k0 + 4 * g]);
+    const uint2 d = *reinterpret_cast<const uint2*>(&s.lo[r][k0 + 16 + 4 * g]);
+    return Frag{__builtin_bit_cast(bh8, uint4{a.x, a.y, b.x, b.y}),
+                __builtin_bit_cast(bh8, uint4{c.x, c.y, d.x, d.y})};
+  }
+};
+
+// the policy of bf16 inputs
+#ifndef M3_HALF_POLICY
+#define M3_HALF_POLICY PolB16
+#endif
+typedef M3_HALF_POLICY PolHalf;
+
 // the B/C preparation of one vector of eight elements (e0 .. e0 + 7 of
 // token t's N x R row), in place; NoPrep leaves it as loaded
 struct NoPrep {

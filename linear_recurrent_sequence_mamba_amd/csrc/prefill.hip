@@ -49,9 +49,9 @@ namespace m3 {
 // the chunk's Q*R virtual rows (two tiles w and 2NW-1-w when TPW = 2, which
 // balances the causal work across waves).  Up to 16 waves per block, so the
 // rank-4 chunk (16 tiles) has one tile per wave.
-template <int P, int N, int R, int MAXW = 16>
+template <int P, int N, int R, int MAXW = 16, int Q = kQ>
 struct Geo {
-  static constexpr int ROWS = kQ * R;
+  static constexpr int ROWS = Q * R;
   static constexpr int TILES = ROWS / 16;
   static constexpr int NW = (TILES >= 16 && MAXW >= 16) ? 16 : (TILES >= 8 ? 8 : 4);
   static constexpr int TPW = TILES / NW;
@@ -66,15 +66,15 @@ struct Geo {
 // B/C preparation tables of one block: the weight [N], one head's bias
 // [N][R] and the inverse RMS [t][r] of the chunk's tokens.  NoTab stands in
 // when the preparation is off.
-template <int N, int R>
+template <int N, int R, int Q = kQ>
 struct alignas(16) PrepTab {
   float w[N];
   float b[N * R];
-  float inv[kQ * R];
+  float inv[Q * R];
 };
 struct NoTab {};
-template <bool PREP, int N, int R>
-using PrepTabT = typename std::conditional<PREP, PrepTab<N, R>, NoTab>::type;
+template <bool PREP, int N, int R, int Q>
+using PrepTabT = typename std::conditional<PREP, PrepTab<N, R, Q>, NoTab>::type;
 
 // weight and bias of head h (1 and 0 where the arrays are absent), loaded
 // into registers early and stored into a PrepTab once the tables exist
@@ -94,7 +94,8 @@ struct PrepLoad {
       v[i] = e < NE ? r : 0.0f;
     }
   }
-  __device__ __forceinline__ void store(PrepTab<N, R>& t) const {
+  template <int Q>
+  __device__ __forceinline__ void store(PrepTab<N, R, Q>& t) const {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int e = threadIdx.x + NT * i;
@@ -106,9 +107,9 @@ struct PrepLoad {
 
 // the preparation of one vector of eight elements (e0 .. e0 + 7 of token t's
 // N x R row) in place from the block's tables (NoPrep: left as loaded)
-template <int N, int R>
+template <int N, int R, int Q>
 struct TabPrep {
-  const PrepTab<N, R>* tab;
+  const PrepTab<N, R, Q>* tab;
   // the vector's R inverse RMS, 8/R weights and 8 biases in 16-byte (or
   // smaller) LDS reads
   __device__ __forceinline__ void operator()(int t, int e0, float* v) const {
@@ -184,7 +185,7 @@ __device__ __forceinline__ void row_sumsq(const RowBlock<TI, E, R, NT, false, RO
 // sum of token t0 + tl goes to part[wave][t0 + tl] (zero for a block that
 // was not loaded, live false).  The caller adds the waves' parts in wave
 // order after a barrier.
-template <typename TI, int E, int NT, int ROWS>
+template <int Q, typename TI, int E, int NT, int ROWS>
 __device__ __forceinline__ void row_sumsq_tf(const RowBlock<TI, E, 1, NT, true, ROWS>& rb, int t0,
                                              bool live, float* part) {
   using RBk = RowBlock<TI, E, 1, NT, true, ROWS>;
@@ -205,7 +206,7 @@ __device__ __forceinline__ void row_sumsq_tf(const RowBlock<TI, E, 1, NT, true, 
 #pragma unroll
   for (int off = NTOK; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
   const int lane = threadIdx.x & 63;
-  if (lane < NTOK) part[(threadIdx.x >> 6) * kQ + t0 + lane] = s;
+  if (lane < NTOK) part[(threadIdx.x >> 6) * Q + t0 + lane] = s;
 }
 
 // --------------------------------------------------------------------------
@@ -220,31 +221,31 @@ __device__ __forceinline__ void row_sumsq_tf(const RowBlock<TI, E, 1, NT, true, 
 template <int R>
 constexpr int k1_rows() { return R == 1 ? 32 : kRB; }
 
-template <class Pol, typename TI, int P, int N, int R, bool PREP>
+template <class Pol, typename TI, int P, int N, int R, bool PREP, int Q>
 struct K1Smem {
   static constexpr int UBR = k1_rows<R>();
-  Tables<N, false, true> tb;
+  Tables<N, false, true, Q> tb;
   union U {
     typename Pol::template Store<N, UBR> bw;   // (W_u R(Phi_end - Phi_u) B_u)^T  [n][v]
-    TableScratch<N, Geo<P, N, R, 8>::NT> scr;
+    TableScratch<N, Geo<P, N, R, 8, Q>::NT, Q> scr;
+    // single rank with the preparation: each wave's part of every token's
+    // sum of squares [wave][t] (between the tables and the first staging)
+    float sq[(PREP && R == 1) ? Geo<P, N, R, 8, Q>::NW * Q : 1];
   } u;
   typename Pol::template XStore<P, UBR> xs;    // x^T  [p][v]
-  PrepTabT<PREP, N, R> pb;                     // B preparation
-  // single rank with the preparation: each wave's part of every token's
-  // sum of squares [wave][t]
-  float sq[(PREP && R == 1) ? Geo<P, N, R, 8>::NW * kQ : 1];
+  PrepTabT<PREP, N, R, Q> pb;                  // B preparation
 };
 
-template <class Pol, typename TI, int P, int N, int R, bool PREP>
-__global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillArgs a) {
-  using G = Geo<P, N, R, 8>;
-  __shared__ K1Smem<Pol, TI, P, N, R, PREP> sm;
+template <class Pol, typename TI, int P, int N, int R, bool PREP, int Q>
+__global__ __launch_bounds__((Geo<P, N, R, 8, Q>::NT)) void k_chunk_state(PrefillArgs a) {
+  using G = Geo<P, N, R, 8, Q>;
+  __shared__ K1Smem<Pol, TI, P, N, R, PREP, Q> sm;
   constexpr int UBR = k1_rows<R>(), NUB = G::ROWS / UBR;   // staged u-blocks
   constexpr int NQ = G::PT * G::NTL;              // output tiles (p-tile, n-tile)
   constexpr int QPW = (NQ + G::NW - 1) / G::NW;   // per wave
   const int h = blockIdx.y;
   ChunkRef ck;
-  if (!chunk_ref(a, blockIdx.x, h, blockIdx.z, ck)) return;
+  if (!chunk_ref<Q>(a, blockIdx.x, h, blockIdx.z, ck)) return;
   const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
   const int rows = Lc * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -261,7 +262,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   if constexpr (PREP) {
     pl.load(a.bc.Bw, a.bc.Bb, h);
   }
-  ThetaBlock<TI, N, G::NT> thb;
+  ThetaBlock<TI, N, G::NT, Q> thb;
   thb.load(a, b, h, c0, Lc);
   // with R >= 2 a token's row of B (N R values) or x (P R) is long enough
   // for lanes to walk it (whole lines per load); single-rank rows are
@@ -276,9 +277,10 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     }
   }
 
+  if (a.tp.on) project_theta<TI, N, G::NT, Q>(a, b, h, c0, Lc, sm.tb);
   chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 1);
   const double cs_end = sm.tb.cs[Lc - 1];
-  if (tid < kQ) {
+  if (tid < Q) {
     float w = 0.0f;
     if (tid < Lc) {
       const float wt = sm.tb.gam[tid] + (tid < Lc - 1 ? sm.tb.bpr[tid + 1] : 0.0f);
@@ -291,12 +293,12 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   if (tid == 0) a.decay[chunk_id] = expf((float)cs_end);
   float* __restrict__ rsB = nullptr;
   if constexpr (PREP) {
-    rsB = a.rsB + chunk_id * (kQ * R);
+    rsB = a.rsB + chunk_id * (Q * R);
     pl.store(sm.pb);
 #pragma unroll
     for (int ub = 0; ub < NUB; ++ub) {
       if constexpr (TFK1) {   // every u-block writes its tokens' parts (zeros past the chunk)
-        row_sumsq_tf(bb[ub], ub * UBR, ub * UBR < rows, sm.sq);
+        row_sumsq_tf<Q>(bb[ub], ub * UBR, ub * UBR < rows, sm.u.sq);
       } else {
         if (ub * UBR < rows) row_sumsq(bb[ub], a.bc, N, ub * UBR / R, Lc, sm.pb.inv);
       }
@@ -305,15 +307,15 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   __syncthreads();   // W_t visible (and the B preparation tables)
   if constexpr (PREP) {
     if constexpr (TFK1) {   // the waves' parts in wave order -> inverse RMS
-      if (tid < kQ) {
+      if (tid < Q) {
         float ss = 0.0f;
 #pragma unroll
-        for (int w = 0; w < G::NW; ++w) ss += sm.sq[w * kQ + tid];
+        for (int w = 0; w < G::NW; ++w) ss += sm.u.sq[w * Q + tid];
         sm.pb.inv[tid] = bc_inv_rms(a.bc, ss, N);
       }
       __syncthreads();
     }
-    if (tid < kQ * R) rsB[tid] = sm.pb.inv[tid];
+    if (tid < Q * R) rsB[tid] = sm.pb.inv[tid];
   }
 
   f4 acc[QPW];
@@ -326,7 +328,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
     if (ub > 0) __syncthreads();   // the previous block's LDS reads are done
     if constexpr (PREP)
       store_rows_T<Pol, TI, N, R, G::NT, TFK1, UBR>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * UBR / R, Lc,
-                                                    TabPrep<N, R>{&sm.pb});
+                                                    TabPrep<N, R, Q>{&sm.pb});
     else
       store_rows_T<Pol, TI, N, R, G::NT, TFK1, UBR>(bb[ub], sm.u.bw, sm.tb, sm.tb.aux, ub * UBR / R, Lc,
                                                     NoPrep{});
@@ -351,7 +353,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
   // with no branch around it: a chunk with no next one reads its own tokens
   // and drops the term.
   const bool nxt = ck.next;
-  const int64_t nx = token_index(a, b, nxt ? c0 + kQ : c0, h);
+  const int64_t nx = token_index(a, b, nxt ? c0 + Q : c0, h);
   Raw1<TI> dnr, lnr;
   dnr.load(static_cast<const TI*>(a.dt), nx);
   lnr.load(static_cast<const TI*>(a.lam), nx);
@@ -383,7 +385,7 @@ __global__ __launch_bounds__((Geo<P, N, R, 8>::NT)) void k_chunk_state(PrefillAr
         if constexpr (PREP) {   // the last token's B, prepared like the staged rows
 #pragma unroll
           for (int e = 0; e < 4 * R; ++e)
-            br[e] = br[e] * sm.pb.inv[(kQ - 1) * R + e % R] * sm.pb.w[n + e / R] + sm.pb.b[n * R + e];
+            br[e] = br[e] * sm.pb.inv[(Q - 1) * R + e % R] * sm.pb.w[n + e / R] + sm.pb.b[n * R + e];
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -505,9 +507,9 @@ __global__ __launch_bounds__(64) void k_state_pass(PrefillArgs a) {
 // chunk (16 tiles) is split over two blocks of 8 waves (virtual rows 0..127
 // and 128..255), so that two blocks fit on a CU and one block's loads and
 // table work overlap the other's MFMA work.
-template <int P, int N, int R>
+template <int P, int N, int R, int Q = kQ>
 struct Geo3 {
-  static constexpr int ROWS = kQ * R;            // virtual rows per chunk
+  static constexpr int ROWS = Q * R;             // virtual rows per chunk
   static constexpr int TILES = ROWS / 16;
   static constexpr int SPLIT = TILES > 8 ? TILES / 8 : 1;
   static constexpr int NW = TILES / SPLIT;       // waves (= tiles) per block
@@ -520,11 +522,11 @@ struct Geo3 {
                 "output block geometry");
 };
 
-template <class Pol, typename TI, int P, int N, int R, bool PREP>
+template <class Pol, typename TI, int P, int N, int R, bool PREP, int Q>
 struct K3Smem {
   // with R a multiple of 4 each token-pair mask value serves 16 virtual
   // (row, column) pairs, so the block's mask rows are tabulated once
-  static constexpr int MT = R % 4 == 0 ? Geo3<P, N, R>::BROWS / R : 1;
+  static constexpr int MT = R % 4 == 0 ? Geo3<P, N, R, Q>::BROWS / R : 1;
   static constexpr int UB = 32;                // virtual rows per staged u-block
   // a single-input chunk (one 4-wave block) keeps its LDS small enough for
   // three blocks per CU: C rows staged 32 at a time, Shat in two halves,
@@ -533,16 +535,16 @@ struct K3Smem {
   static constexpr int CRB = LEAN ? 32 : kRB;  // C rows per staged piece
   static constexpr int SHP = LEAN && P >= 32 ? P / 2 : P;  // Shat rows per staged part (whole tiles)
   static constexpr int NBUF = LEAN ? 1 : 2;    // u-block buffers
-  Tables<N, false> tb;
+  Tables<N, false, false, Q> tb;
   union U {
     typename Pol::template Store<CRB, N> st;   // rotated C rows        [v][n]
     typename Pol::template Store<SHP, N> sh;   // Shat                  [p][n]
     typename Pol::template Store<UB, N> bst[NBUF];  // rotated B rows
-    TableScratch<N, Geo3<P, N, R>::NT> scr;
+    TableScratch<N, Geo3<P, N, R, Q>::NT, Q> scr;
   } u;
   typename Pol::template XStore<P, UB> xs[NBUF];  // x^T of a u-block   [p][v]
-  float msk[MT][kQ + 1];                       // M[t - t_lo][u]
-  PrepTabT<PREP, N, R> pb, pc;                 // B and C preparation
+  float msk[MT][Q + 1];                       // M[t - t_lo][u]
+  PrepTabT<PREP, N, R, Q> pb, pc;                 // B and C preparation
 };
 
 // four consecutive outputs (one token's four ranks) in one store
@@ -557,16 +559,17 @@ __device__ __forceinline__ void st4_out(bf16_t* __restrict__ p, int64_t i, f4 v)
 
 // the rank-4 bf16 kernel runs two 8-wave blocks per CU (four waves per
 // SIMD); the B/C preparation's few extra registers must not break that
-template <class Pol, int R, bool PREP>
+template <class Pol, int R, bool PREP, int Q>
 constexpr int k3_min_waves() {
-  return (PREP && R % 4 == 0 && std::is_same<Pol, PolF16>::value) ? 4 : 1;
+  // (and an 8-wave single-input block of 128 tokens, likewise two per CU)
+  return ((PREP && R % 4 == 0 && std::is_same<Pol, PolHalf>::value) || (R == 1 && Q > kQ)) ? 4 : 1;
 }
 
-template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP>
-__global__ __launch_bounds__((Geo3<P, N, R>::NT))
-__attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_output(PrefillArgs a) {
-  using G = Geo3<P, N, R>;
-  using SMT = K3Smem<Pol, TI, P, N, R, PREP>;
+template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP, int Q>
+__global__ __launch_bounds__((Geo3<P, N, R, Q>::NT))
+__attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP, Q>()))) void k_chunk_output(PrefillArgs a) {
+  using G = Geo3<P, N, R, Q>;
+  using SMT = K3Smem<Pol, TI, P, N, R, PREP, Q>;
   __shared__ SMT sm;
   constexpr int NKS = N / Pol::KS;
   constexpr int UG = 16 * Pol::DT;          // u rows per A fragment built from D tiles
@@ -583,7 +586,7 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   }
   const int h = blockIdx.y;
   ChunkRef ck;
-  if (!chunk_ref(a, c, h, blockIdx.z, ck)) return;
+  if (!chunk_ref<Q>(a, c, h, blockIdx.z, ck)) return;
   const int b = ck.bt, c0 = ck.t0, Lc = ck.Lc;
   const int rows = Lc * R;
   const int v0 = half * G::BROWS;           // this block's rows: [v0, vend)
@@ -608,17 +611,17 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
     PrepLoad<N, R, G::NT> plb, plc;
     plb.load(a.bc.Bw, a.bc.Bb, h);
     plc.load(a.bc.Cw, a.bc.Cb, h);
-    const float rsb_in = a.rsB[chunk_id * (kQ * R) + min(tid, kQ * R - 1)];   // (no branch around the read)
-    const float rsb = tid < kQ * R ? rsb_in : 0.0f;
+    const float rsb_in = a.rsB[chunk_id * (Q * R) + min(tid, Q * R - 1)];   // (no branch around the read)
+    const float rsb = tid < Q * R ? rsb_in : 0.0f;
     plb.store(sm.pb);
     plc.store(sm.pc);
-    if (tid < kQ * R) sm.pb.inv[tid] = rsb;
+    if (tid < Q * R) sm.pb.inv[tid] = rsb;
   }
   // all loads go out first (the load counter retires in order): phase
   // inputs and token scalars, this block's C rows, the entry state, and the
   // first u-blocks of B and x
   constexpr int CRB = SMT::CRB, NCB = G::BROWS / CRB, NBUF = SMT::NBUF;
-  ThetaBlock<TI, N, G::NT> thb;
+  ThetaBlock<TI, N, G::NT, Q> thb;
   thb.load(a, b, h, c0, Lc);
   RowBlock<TI, N * R, R, G::NT, false, CRB> cb[NCB];
 #pragma unroll
@@ -645,14 +648,15 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
     }
   }
 
+  if (a.tp.on) project_theta<TI, N, G::NT, Q>(a, b, h, c0, Lc, sm.tb);
   chunk_tables<TI, N, G::NT>(a, thb, Lc, sm.tb, sm.u.scr, 0);
-  if (tid < kQ) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
+  if (tid < Q) sm.tb.aux[tid] = tid < Lc ? expf((float)sm.tb.cs[tid]) : 0.0f;
   // decay mask M[t][u] = e^{cs_t - cs_u} w_{t,u} of this block's tokens
   // (zero above the diagonal and past the chunk's end)
   const int tlo = v0 / R;
   if constexpr (R % 4 == 0) {
-    for (int idx = tid; idx < SMT::MT * kQ; idx += G::NT) {
-      const int tr = idx / kQ, u = idx % kQ, t = tlo + tr;
+    for (int idx = tid; idx < SMT::MT * Q; idx += G::NT) {
+      const int tr = idx / Q, u = idx % Q, t = tlo + tr;
       float m = 0.0f;
       if (t < Lc && u <= t) {
         const float w = sm.tb.gam[u] + (u < t ? sm.tb.bpr[u + 1] : 0.0f);
@@ -679,7 +683,7 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
       if (k > 0) __syncthreads();
       if constexpr (PREP)
         store_rows<Pol, TI, N, R, G::NT, CRB>(cb[k], sm.u.st, sm.tb, (v0 + k * CRB) / R, Lc,
-                                              TabPrep<N, R>{&sm.pc});
+                                              TabPrep<N, R, Q>{&sm.pc});
       else
         store_rows<Pol, TI, N, R, G::NT, CRB>(cb[k], sm.u.st, sm.tb, (v0 + k * CRB) / R, Lc, NoPrep{});
       __syncthreads();
@@ -724,11 +728,11 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
   const int tt = vrow / R;
   const bool row_ok = vrow < rows;
   const int tmax = min(Lc - 1, (16 * tile + 15) / R);
-  const double cst = sm.tb.cs[min(tt, kQ - 1)];
+  const double cst = sm.tb.cs[min(tt, Q - 1)];
   auto stage = [&](int k) {
     if constexpr (PREP)
       store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % NBUF], sm.tb, k * UB / R, Lc,
-                                           TabPrep<N, R>{&sm.pb});
+                                           TabPrep<N, R, Q>{&sm.pb});
     else
       store_rows<Pol, TI, N, R, G::NT, UB>(bb[k % NS], sm.u.bst[k % NBUF], sm.tb, k * UB / R, Lc, NoPrep{});
     store_x_T<Pol, TI, P, R, G::NT, UB, (R < 2)>(xb[k % NS], sm.xs[k % NBUF]);
@@ -816,56 +820,66 @@ __attribute__((amdgpu_waves_per_eu(k3_min_waves<Pol, R, PREP>()))) void k_chunk_
 }
 
 // --------------------------------------------------------------------------
-template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP>
+template <class Pol, typename TI, typename TO, int P, int N, int R, bool PREP, int Q>
 static hipError_t run_prefill(const PrefillArgs& a, hipStream_t s) {
-  using G1 = Geo<P, N, R, 8>;
+  using G1 = Geo<P, N, R, 8, Q>;
   // packed sequences: one row of chunk slots per head
   const int nz = a.cmap ? 1 : a.Bsz;
-  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R, PREP>), dim3(a.nchunk, a.H, nz), dim3(G1::NT), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_state<Pol, TI, P, N, R, PREP, Q>), dim3(a.nchunk, a.H, nz), dim3(G1::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static_assert(P * N % 256 == 0, "state pass: whole waves per (batch, head)");
   hipLaunchKernelGGL((k_state_pass<TI, N, R>), dim3(a.Bsz * a.H * (P * N / 256)), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.states_only) return e;
-  using G3 = Geo3<P, N, R>;
+  using G3 = Geo3<P, N, R, Q>;
   // a split chunk's blocks are 8 apart in launch order: pad to whole groups of 8
   const int nx = G3::SPLIT == 1 ? a.nchunk : G3::SPLIT * ((a.nchunk + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R, PREP>), dim3(nx, a.H, nz), dim3(G3::NT), 0, s, a);
+  hipLaunchKernelGGL((k_chunk_output<Pol, TI, TO, P, N, R, PREP, Q>), dim3(nx, a.H, nz), dim3(G3::NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <class Pol, typename TI, typename TO>
 static int dispatch_shape(const PrefillArgs& a, hipStream_t s, hipError_t* e) {
-#define M3_SHAPE(PP, NN, RR)                                  \
-  if constexpr (NN % Pol::KS == 0) {                          \
-    if (a.P == PP && a.N == NN && a.R == RR) {                \
-      *e = a.bc.on ? run_prefill<Pol, TI, TO, PP, NN, RR, true>(a, s)  \
-                   : run_prefill<Pol, TI, TO, PP, NN, RR, false>(a, s); \
-      return 0;                                               \
-    }                                                         \
+#define M3_SHAPE(PP, NN, RR, QQ)                                          \
+  if constexpr (NN % Pol::KS == 0) {                                      \
+    if (a.P == PP && a.N == NN && a.R == RR && a.Q == QQ) {               \
+      *e = a.bc.on ? run_prefill<Pol, TI, TO, PP, NN, RR, true, QQ>(a, s)  \
+                   : run_prefill<Pol, TI, TO, PP, NN, RR, false, QQ>(a, s); \
+      return 0;                                                           \
+    }                                                                     \
   }
-  M3_SHAPE(16, 16, 1)
-  M3_SHAPE(64, 128, 1)
-  M3_SHAPE(64, 128, 4)
-  M3_SHAPE(64, 128, 2)
-  M3_SHAPE(32, 64, 1)
-  M3_SHAPE(32, 64, 4)
-  M3_SHAPE(64, 64, 1)
-  M3_SHAPE(64, 64, 4)
+  M3_SHAPE(16, 16, 1, 64)
+  M3_SHAPE(64, 128, 1, 64)
+  M3_SHAPE(64, 128, 4, 64)
+  M3_SHAPE(64, 128, 2, 64)
+  M3_SHAPE(32, 64, 1, 64)
+  M3_SHAPE(32, 64, 4, 64)
+  M3_SHAPE(64, 64, 1, 64)
+  M3_SHAPE(64, 64, 4, 64)
+  // 128-token chunks for a single input: half the chunk states
+  M3_SHAPE(16, 16, 1, 128)
+  M3_SHAPE(64, 128, 1, 128)
+  M3_SHAPE(32, 64, 1, 128)
+  M3_SHAPE(64, 64, 1, 128)
 #undef M3_SHAPE
   return -1;
 }
 
 bool prefill_supported(int P, int N, int R, int Q, int in_bf16) {
-  if (Q != kQ) return false;
   const bool shape = (P == 16 && N == 16 && R == 1) ||
                      (P == 64 && N == 128 && (R == 1 || R == 2 || R == 4)) ||
                      (P == 32 && N == 64 && (R == 1 || R == 4)) ||
                      (P == 64 && N == 64 && (R == 1 || R == 4));
   if (!shape) return false;
-  if (in_bf16 && N % 32 != 0) return false;  // fp16 fragments span 32 state columns
+  if (!(Q == kQ || (Q == 128 && R == 1))) return false;
+  if (in_bf16 && N % 32 != 0) return false;  // 16-bit fragments span 32 state columns
   return true;
+}
+
+int prefill_default_chunk(int P, int N, int R, int in_bf16) {
+  (void)P, (void)N, (void)in_bf16;
+  return R == 1 ? kPrefillChunkR1 : kQ;
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -887,7 +901,7 @@ static char* carve_units(PrefillArgs& a, size_t units, char* p) {
   a.rsB = nullptr;
   if (a.bc.on) {
     a.rsB = reinterpret_cast<float*>(p);
-    p += align256(units * kQ * a.R * 4);
+    p += align256(units * a.Q * a.R * 4);
   }
   return p;
 }
@@ -947,7 +961,7 @@ __device__ __forceinline__ int block_scan(int v, int* wtot, Op op) {
 // threads walks the offsets in tiles, carrying the running maximum offset
 // and the running chunk count from tile to tile
 __global__ __launch_bounds__(1024) void k_varlen_seqs(const int32_t* __restrict__ cu, int S, int T,
-                                                      int4* __restrict__ seqs) {
+                                                      int Q, int4* __restrict__ seqs) {
   __shared__ int wtot[16];
   __shared__ int edge[1025];
   __shared__ int tile_sum;
@@ -962,7 +976,7 @@ __global__ __launch_bounds__(1024) void k_varlen_seqs(const int32_t* __restrict_
     __syncthreads();
     const bool is_seq = i >= 1 && i <= S;   // offset i closes sequence i - 1
     const int len = is_seq ? edge[tid + 1] - edge[tid] : 0;
-    const int nch = (len + kQ - 1) / kQ;
+    const int nch = (len + Q - 1) / Q;
     const int incl = block_scan(nch, wtot, [](int x, int y) { return x + y; });
     if (is_seq) seqs[i - 1] = int4{carry_sum + incl - nch, nch, edge[tid], len};
     if (tid == 1023) tile_sum = incl;
@@ -976,7 +990,7 @@ __global__ __launch_bounds__(1024) void k_varlen_seqs(const int32_t* __restrict_
 // cmap[j] for every slot j: the sequence whose chunks cover slot j (the
 // last one starting at or before j) or -1 past the last chunk
 __global__ __launch_bounds__(256) void k_varlen_slots(const int4* __restrict__ seqs, int S, int nslot,
-                                                      int4* __restrict__ cmap) {
+                                                      int Q, int4* __restrict__ cmap) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= nslot) return;
   int lo = 0, hi = S;   // seqs[lo].x <= j (seqs[0].x = 0); hi = S or seqs[hi].x > j
@@ -987,29 +1001,29 @@ __global__ __launch_bounds__(256) void k_varlen_slots(const int4* __restrict__ s
   }
   const int4 q = seqs[lo];
   const int c = j - q.x;
-  cmap[j] = c < q.y ? int4{lo, q.z + c * kQ, q.z + q.w, c} : int4{-1, 0, 0, 0};
+  cmap[j] = c < q.y ? int4{lo, q.z + c * Q, q.z + q.w, c} : int4{-1, 0, 0, 0};
 }
 
 hipError_t launch_varlen_map(const PrefillArgs& a, const int32_t* cu, hipStream_t s) {
-  hipLaunchKernelGGL(k_varlen_seqs, dim3(1), dim3(1024), 0, s, cu, a.Bsz, a.T, a.seqs);
+  hipLaunchKernelGGL(k_varlen_seqs, dim3(1), dim3(1024), 0, s, cu, a.Bsz, a.T, a.Q, a.seqs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_varlen_slots, dim3((a.nchunk + 255) / 256), dim3(256), 0, s, a.seqs, a.Bsz,
-                     a.nchunk, a.cmap);
+                     a.nchunk, a.Q, a.cmap);
   return hipGetLastError();
 }
 
-bool prefill_offsets_fit(int H, int P, int N, int R) {
+bool prefill_offsets_fit(int H, int P, int N, int R, int Q) {
   // in-chunk element offsets are 32-bit: Q tokens of the widest per-token row
   const int64_t row = (int64_t)H * std::max(N, P) * R;
-  return (int64_t)kQ * row < (int64_t(1) << 31);
+  return (int64_t)Q * row < (int64_t(1) << 31);
 }
 
 int launch_prefill(const PrefillArgs& a, int in_bf16, int out_bf16, hipStream_t s, hipError_t* e) {
-  if (!prefill_offsets_fit(a.H, a.P, a.N, a.R)) return -1;
+  if (!prefill_offsets_fit(a.H, a.P, a.N, a.R, a.Q)) return -1;
   if (in_bf16) {
-    return out_bf16 ? dispatch_shape<PolF16, bf16_t, bf16_t>(a, s, e)
-                    : dispatch_shape<PolF16, bf16_t, float>(a, s, e);
+    return out_bf16 ? dispatch_shape<PolHalf, bf16_t, bf16_t>(a, s, e)
+                    : dispatch_shape<PolHalf, bf16_t, float>(a, s, e);
   }
   return out_bf16 ? dispatch_shape<PolF32, float, bf16_t>(a, s, e)
                   : dispatch_shape<PolF32, float, float>(a, s, e);

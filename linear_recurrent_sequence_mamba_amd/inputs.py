@@ -178,6 +178,20 @@ def token_decay(w: Workload, lead: tuple, stream: int = 0) -> torch.Tensor:
                             .astype(np.float32))
 
 
+def theta_proj_inputs(w: Workload, lead: tuple, dim: int, groups: int | None = None,
+                      stream: int = 0):
+    """Inputs of the in-kernel angle projection: u ~ N(0, 1) of shape lead +
+    (dim,) and W ~ N(0, (pi / 2)^2 / dim) of shape [G, N/2, dim] (so the
+    angles come out ~N(0, (pi/2)^2), the spread of U(-pi, pi)), cast to the
+    input dtype.  Returns (u, W) as CPU tensors."""
+    rng = np.random.default_rng([w.cfg_id, 0x7E, stream])
+    G = groups or w.nheads
+    u = rng.standard_normal(tuple(lead) + (dim,), dtype=np.float32)
+    W = (rng.standard_normal((G, w.dstate // 2, dim), dtype=np.float32)
+         * np.float32(0.5 * math.pi / math.sqrt(dim)))
+    return _cast(u, w.torch_dtype), _cast(W, w.torch_dtype)
+
+
 def prefill_inputs(w: Workload, stream: int = 0, h0: str | None = None,
                    with_prev: bool = False) -> dict:
     """Inputs of one prefill call as CPU torch tensors (input dtype; A, h0 fp32).

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for s in range(8):
-        assert m3.m3_status_str(s)
+        assert m3.m3_status_str(s) != "unknown status"
     assert m3.m3_status_str(99) == "unknown status"
 
 
@@ -87,10 +87,15 @@ def _backward(d, ws_bytes=1 << 40, **over):
 
 
 def test_workspace_size():
+    # one P x N state per chunk: a single input takes 128-token chunks by
+    # default, 64-token ones when asked
     d = _dims(batch=4, seqlen=2048, nheads=32)
     n = m3.m3_prefill_workspace_size(d)
-    chunks = 4 * 32 * 32
-    assert n >= chunks * 64 * 128 * 4
+    assert 4 * 32 * 16 * 64 * 128 * 4 <= n < 4 * 32 * 17 * 64 * 128 * 4
+    n64 = m3.m3_prefill_workspace_size(_dims(batch=4, seqlen=2048, nheads=32, chunk=64))
+    assert 4 * 32 * 32 * 64 * 128 * 4 <= n64 < 4 * 32 * 33 * 64 * 128 * 4
+    assert m3.m3_prefill_workspace_size(_dims(rank=4)) == \
+        m3.m3_prefill_workspace_size(_dims(rank=4, chunk=64))
     assert m3.m3_prefill_workspace_size(_dims(dstate=7)) == 0
     assert m3.library().m3_prefill_workspace_size(None) == 0
 
@@ -160,14 +165,34 @@ def test_backward_specific_errors():
     assert _backward(d) == 4                                    # no B/C preparation
 
 
+def test_theta_proj_errors():
+    """The angle projection: width a positive multiple of 32, both arrays
+    given and aligned; not offered by the multi-token decode or the backward."""
+    def with_tp(dim=64, u=P16, W=P16):
+        d = _dims()
+        tp = m3.m3_theta_proj(u, W, dim)
+        d._keep = tp
+        d.tp = ctypes.pointer(tp)
+        return d
+    for call in (_decode, _prefill, _varlen):
+        assert call(with_tp(dim=48)) == 2                       # not a multiple of 32
+        assert call(with_tp(dim=0)) == 2
+        assert call(with_tp(u=None)) == 1
+        assert call(with_tp(W=P_MIS)) == 5
+        assert call(_dims(), th=None) == 1                      # theta needed without it
+    assert _tokens(with_tp()) == 4
+    assert _backward(with_tp()) == 4
+
+
 def test_varlen_workspace_size():
     # S sequences over T tokens take at most min(T, (T + 63 S) / 64) chunks;
     # the per-chunk state (P N fp32) dominates the workspace
-    for S, T in ((1, 100), (7, 100), (300, 100), (5, 64 * 40)):
-        d = _dims(batch=S, seqlen=T, nheads=3)
-        slots = min(T, (T + 63 * S) // 64)
-        n = m3.m3_prefill_varlen_workspace_size(d)
-        assert 3 * slots * 64 * 128 * 4 <= n <= 3 * slots * (64 * 128 + 129) * 4 + 16 * (S + slots) + 1280
+    for Q in (64, 128):
+        for S, T in ((1, 100), (7, 100), (300, 100), (5, 64 * 40)):
+            d = _dims(batch=S, seqlen=T, nheads=3, chunk=Q)
+            slots = min(T, (T + (Q - 1) * S) // Q)
+            n = m3.m3_prefill_varlen_workspace_size(d)
+            assert 3 * slots * 64 * 128 * 4 <= n <= 3 * slots * (64 * 128 + 129) * 4 + 16 * (S + slots) + 1280
     assert m3.m3_prefill_varlen_workspace_size(_dims(dstate=7)) == 0
     # one sequence needs as many chunks as the dense call
     assert m3.m3_prefill_varlen_workspace_size(_dims(batch=1)) >= \

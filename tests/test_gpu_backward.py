@@ -2,11 +2,14 @@
 against the fp64 oracle's adjoint (oracle.scan_backward, itself pinned by
 finite differences of the forward scan).
 
-Gate: the gradients are sums over many more terms than an output of the
-forward scan (a token's dt collects the whole remaining sequence's decay
-gradient, dA sums over every token), so the fp32 error is held to 1e-4 for
-fp32 inputs and to the forward's 3e-3 for bf16 inputs (both sides take the
-same rounded inputs; the measured errors are printed)."""
+Gates.  bf16 inputs: the forward's 3e-3 for every gradient.  fp32 inputs: the
+forward's 1e-5 for the gradients that are elementwise products of chunk
+contractions (x, B, C, lam, h0, x_prev, B_prev), and 2e-5 for dt, A and
+theta: each of those is a suffix sum over the chunk's tokens (up to 64
+terms, then carried from chunk to chunk) of terms that carry the
+elementwise gradients' own rounding, so its error can reach about twice
+theirs (measured up to 8.7e-6, against up to 6.4e-6 for the others).  Both
+sides take the same rounded inputs; the measured errors are printed."""
 import numpy as np
 import pytest
 import torch
@@ -14,11 +17,13 @@ import torch
 from linear_recurrent_sequence_mamba_amd import binding as m3
 from linear_recurrent_sequence_mamba_amd import inputs as I
 from oracle import oracle
-from tests.util import cpu64, cuda, rel_err, say
+from tests.util import PAIR_TOL, cpu64, cuda, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
-GTOL = {torch.float32: 1e-4, torch.bfloat16: 3e-3}
+GTOL = {torch.float32: 1e-5, torch.bfloat16: 3e-3}
+# fp32 inputs: the suffix-summed gradients (see the module docstring)
+GTOL_SUFFIX32 = {"dt": 2e-5, "A": 2e-5, "theta": 2e-5}
 KEYS = ("x", "dt", "A", "lam", "theta", "B", "C", "h0", "x_prev", "B_prev")
 
 
@@ -77,7 +82,8 @@ def _check(w, d, dy, dhT, flags=0, tol=None):
             continue
         errs[k] = rel_err(cpu64(got[k]), ref[k])
     say("  " + "  ".join(f"d{k} {v:.1e}" for k, v in errs.items()) + f"  (tol {tol:.0e})")
-    bad = {k: v for k, v in errs.items() if not v <= tol}
+    gate = lambda k: max(tol, GTOL_SUFFIX32.get(k, 0.0)) if w.torch_dtype == torch.float32 else tol
+    bad = {k: v for k, v in errs.items() if not v <= gate(k)}
     assert not bad, bad
 
 
@@ -166,6 +172,20 @@ def test_backward_mimo_variants():
 
 
 @pytest.mark.parametrize("R", [1, 4])
+def test_backward_bf16_operand_range(R):
+    """bf16 inputs with x scaled by 1e4 and B, C by 1e-3: the bf16 hi + lo
+    matrix-core operands keep fp32's range, so the gate is unchanged."""
+    w = I.Workload("g", 137, 2, 150, 2, 64, 128, R, 64, "bf16")
+    d = I.prefill_inputs(w, h0="normal", with_prev=True)
+    scale = lambda t, c: (t.to(torch.float32) * c).to(torch.bfloat16)
+    for k, c in (("x", 1e4), ("x_prev", 1e4), ("B", 1e-3), ("B_prev", 1e-3), ("C", 1e-3)):
+        d[k] = scale(d[k], c)
+    dy, dhT = _cotangents(w, d)
+    say(f"backward bf16 range R={R}")
+    _check(w, d, dy, dhT)
+
+
+@pytest.mark.parametrize("R", [1, 4])
 def test_backward_is_deterministic_and_matches_split(R):
     """Two calls give identical gradients; the h0 gradient of the second half
     of a split scan is the dhT that the first half's backward needs."""
@@ -194,7 +214,8 @@ def test_backward_is_deterministic_and_matches_split(R):
     e = rel_err(cpu64(gx), cpu64(g1["x"]))
     eb = rel_err(cpu64(gB), cpu64(g1["B"]))
     say(f"  split: dx err {e:.1e}  dB err {eb:.1e}")
-    assert e <= 1e-4 and eb <= 1e-4
+    # GPU against GPU: both round differently (bf16 operand splits)
+    assert e <= PAIR_TOL[w.torch_dtype] and eb <= PAIR_TOL[w.torch_dtype]
 
 
 @pytest.mark.parametrize("name", ["siso_prefill", "mimo_prefill"])

@@ -9,7 +9,7 @@ import torch
 from linear_recurrent_sequence_mamba_amd import binding as m3
 from linear_recurrent_sequence_mamba_amd import inputs as I
 from oracle import oracle
-from tests.util import TOL, cpu64, cuda, rel_err, say
+from tests.util import PAIR_TOL, TOL, cpu64, cuda, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,9 @@ def test_prefill_prep_split_equals_whole():
           for kk, v in d.items()}
     d2.update(h0=h1.cpu(), x_prev=d["x"][:, k - 1].contiguous(), B_prev=d["B"][:, k - 1].contiguous())
     y2, h2 = _gpu_scan(d2, params)
-    assert rel_err(cpu64(torch.cat([y1, y2], 1)), cpu64(y)) <= 1e-5
-    assert rel_err(cpu64(h2), cpu64(hT)) <= 1e-5
+    # the two evaluations differ only in rounding
+    assert rel_err(cpu64(torch.cat([y1, y2], 1)), cpu64(y)) <= PAIR_TOL[torch.bfloat16]
+    assert rel_err(cpu64(h2), cpu64(hT)) <= PAIR_TOL[torch.bfloat16]
 
 
 @pytest.mark.parametrize("R", [1, 4])

@@ -6,6 +6,12 @@ import torch
 
 # Gates: max relative error (with an RMS floor) for fp32 and bf16 inputs.
 TOL = {torch.float32: 1e-5, torch.bfloat16: 3e-3}
+# GPU against GPU: two evaluations of one result that round differently (a
+# split prefill and the whole one, a decode step after a prefill).  Each is
+# within its own rounding of the exact result: fp32 matrix-core operands for
+# fp32 inputs; for bf16 inputs bf16 hi + lo operand splits, about 2^-17 per
+# operand, chained through two products (measured up to 6e-5 apart).
+PAIR_TOL = {torch.float32: 1e-5, torch.bfloat16: 3e-4}
 
 
 def rel_err(got, ref) -> float:
