@@ -21,7 +21,9 @@
  * Conventions shared by every call:
  *  - Every tensor pointer is a DEVICE pointer, owned by the caller, dense
  *    and row-major (last index fastest), 16-byte aligned.
- *  - The library never allocates, frees or synchronises.  Work is queued on
+ *  - The library never allocates, frees or synchronises (the one buffer it
+ *    holds, that of m3_scan_prefill_noalloc, is static device memory that
+ *    comes with the loaded code).  Work is queued on
  *    `stream` (a hipStream_t passed as void*; NULL = the default stream) and
  *    the call returns at once.  Argument checks run on the host before any
  *    launch; a failed check returns its status and launches nothing.
@@ -64,7 +66,9 @@ typedef enum {
   M3_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this (P, N, R, Q)    */
   M3_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned              */
   M3_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required       */
-  M3_ERR_HIP = 7          /* a HIP launch failed                           */
+  M3_ERR_HIP = 7,         /* a HIP launch failed                           */
+  M3_ERR_TOO_LARGE = 8    /* m3_scan_prefill_noalloc: the call needs more
+                             than M3_NOALLOC_SCRATCH_BYTES of workspace    */
 } m3_status;
 
 typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
@@ -108,8 +112,9 @@ typedef struct {
  * [T, dim] (packed prefill), [Bsz, dim] (decode step); W is [G, N/2, dim].
  * Both are DEVICE pointers in in_dtype, 16-byte aligned; dim must be a
  * positive multiple of 32 (else M3_ERR_SHAPE).  Supported by
- * m3_scan_prefill, m3_scan_prefill_varlen and m3_decode_step;
- * m3_decode_tokens and m3_scan_prefill_backward return M3_ERR_UNSUPPORTED. */
+ * m3_scan_prefill, m3_scan_prefill_noalloc, m3_scan_prefill_varlen and
+ * m3_decode_step; m3_decode_tokens and m3_scan_prefill_backward return
+ * M3_ERR_UNSUPPORTED. */
 typedef struct {
   const void* u;   /* token rows of the projection's input                 */
   const void* W;   /* [G, N/2, dim]                                        */
@@ -163,6 +168,31 @@ m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
                           const void* B, const void* C, const float* h0,
                           const void* x_prev, const void* B_prev, void* y,
                           float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): m3_scan_prefill without the ws/ws_bytes arguments.  Its
+ * workspace is a buffer inside the library, M3_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by each GPU the library runs on until the process
+ * ends; the call itself allocates nothing.  A call whose
+ * m3_prefill_workspace_size(dims) is larger returns M3_ERR_TOO_LARGE and
+ * launches nothing (at P = 64, N = 128: about 2000 chunk-heads, e.g.
+ * Bsz * H * ceil(T / 64) <= 2000).  Every call on one GPU uses that GPU's one
+ * buffer, which keeps the last call's contents (the prefill workspace needs
+ * no particular contents on entry): calls that overlap in time on one GPU,
+ * on different streams or from different threads, race and give wrong
+ * results; calls queued on one stream do not overlap.  `stream` must
+ * belong to the current device (else M3_ERR_HIP).  The first call on a
+ * device looks up that device's copy of the buffer (hipGetSymbolAddress),
+ * so a caller that captures graphs makes one call on each device before
+ * capturing.  Results are bit-identical to m3_scan_prefill with the same
+ * arguments. */
+#define M3_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+m3_status m3_scan_prefill_noalloc(const m3_dims* dims, const void* x, const void* dt,
+                                  const float* A, const void* lam, const void* theta,
+                                  const void* B, const void* C, const float* h0,
+                                  const void* x_prev, const void* B_prev, void* y,
+                                  float* hT, void* stream);
 
 /* Bytes of device workspace m3_scan_prefill_backward needs for `dims` (0
  * if dims is invalid). */

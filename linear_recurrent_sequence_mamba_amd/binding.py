@@ -22,7 +22,9 @@ M3_THETA_IS_ANGLE = 1 << 0
 M3_A_PER_TOKEN = 1 << 1
 
 STATUS = {0: "M3_OK", 1: "M3_ERR_NULL", 2: "M3_ERR_SHAPE", 3: "M3_ERR_DTYPE",
-          4: "M3_ERR_UNSUPPORTED", 5: "M3_ERR_ALIGN", 6: "M3_ERR_WORKSPACE", 7: "M3_ERR_HIP"}
+          4: "M3_ERR_UNSUPPORTED", 5: "M3_ERR_ALIGN", 6: "M3_ERR_WORKSPACE", 7: "M3_ERR_HIP",
+          8: "M3_ERR_TOO_LARGE"}
+M3_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class m3_bc_prep(ctypes.Structure):
@@ -108,6 +110,8 @@ def _lib():
         lib.m3_prefill_workspace_size.argtypes = [dp]
         lib.m3_scan_prefill.restype = ctypes.c_int
         lib.m3_scan_prefill.argtypes = [dp] + [vp] * 13 + [sz, vp]
+        lib.m3_scan_prefill_noalloc.restype = ctypes.c_int
+        lib.m3_scan_prefill_noalloc.argtypes = [dp] + [vp] * 12 + [vp]
         lib.m3_prefill_backward_workspace_size.restype = sz
         lib.m3_prefill_backward_workspace_size.argtypes = [dp]
         lib.m3_scan_prefill_backward.restype = ctypes.c_int
@@ -248,6 +252,37 @@ def m3_scan_prefill(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_pre
                                 _stream(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_prefill")
+
+
+def m3_scan_prefill_noalloc(dims: m3_dims, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev,
+                            y, hT, stream=None) -> None:
+    """m3_scan_prefill with the library's own scratch buffer (no workspace
+    argument; calls that overlap on one GPU race)."""
+    d = dims
+    ti, to = _TORCH.get(d.in_dtype), _TORCH.get(d.out_dtype)
+    if ti is not None and to is not None:
+        Bsz, T, H, P, N, R = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.rank
+        G = groups(d)
+        _check("x", x, (Bsz, T, H, P, R), ti)
+        _check("dt", dt, (Bsz, T, H), ti)
+        _check("A", A, (Bsz, T, H) if d.flags & M3_A_PER_TOKEN else (H,), torch.float32)
+        _check("lam", lam, (Bsz, T, H), ti)
+        _check("theta", theta, (Bsz, T, G, N // 2), ti, optional=_proj(d) is not None)
+        if _proj(d) is not None:
+            _proj(d).check((Bsz, T), G, N, ti)
+        _check("B", B, (Bsz, T, G, N, R), ti)
+        _check("C", C, (Bsz, T, G, N, R), ti)
+        _check("h0", h0, (Bsz, H, P, N), torch.float32, optional=True)
+        _check("x_prev", x_prev, (Bsz, H, P, R), ti, optional=True)
+        _check("B_prev", B_prev, (Bsz, G, N, R), ti, optional=True)
+        _check("y", y, (Bsz, T, H, P, R), to)
+        _check("hT", hT, (Bsz, H, P, N), torch.float32, optional=True)
+    _check_bc(d)
+    st = _lib().m3_scan_prefill_noalloc(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(lam),
+                                        _ptr(theta), _ptr(B), _ptr(C), _ptr(h0), _ptr(x_prev),
+                                        _ptr(B_prev), _ptr(y), _ptr(hT), _stream(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_prefill_noalloc")
 
 
 def m3_prefill_backward_workspace_size(dims: m3_dims) -> int:

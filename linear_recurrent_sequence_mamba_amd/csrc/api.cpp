@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/m3ssm.h"
 #include "m3_launch.h"
 
@@ -82,11 +84,49 @@ int prefill_chunk_of(const m3_dims* d) {
                                                   d->in_dtype == M3_BF16);
 }
 
-// m3_scan_prefill with the caller's workspace
+// ---------------------------------------------------------------------------
+// The scratch buffer of m3_scan_prefill_noalloc: one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory, so every host use goes through the device
+// address that hipGetSymbolAddress returns for the current device, looked up
+// once per device and kept.
+static __device__ __align__(256) unsigned char scratch[M3_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // this device's copy of `scratch`, or null until looked up
+
+// the device address of `scratch` on the device of `stream` (the current
+// device for the null stream), which must be the current device
+hipError_t scratch_of_stream_device(void* stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// m3_scan_prefill with the caller's workspace, or (noalloc) with this
+// device's copy of `scratch`
 m3_status scan_prefill(const m3_dims* d, const void* x, const void* dt, const float* A,
                        const void* lam, const void* theta, const void* B, const void* C,
                        const float* h0, const void* x_prev, const void* B_prev, void* y,
-                       float* hT, void* ws, size_t ws_bytes, void* stream) {
+                       float* hT, void* ws, size_t ws_bytes, bool noalloc, void* stream) {
   m3_status st = check_dims(d, true);
   if (st != M3_OK) return st;
   m3::BCPrep bcp;
@@ -104,6 +144,12 @@ m3_status scan_prefill(const m3_dims* d, const void* x, const void* dt, const fl
     return M3_ERR_UNSUPPORTED;
   const size_t need = m3::prefill_workspace_bytes(d->batch, d->seqlen, d->nheads, d->headdim,
                                                   d->dstate, d->rank, Q, bcp.on != 0);
+  if (noalloc) {
+    if (need > M3_NOALLOC_SCRATCH_BYTES) return M3_ERR_TOO_LARGE;
+    hipError_t e = scratch_of_stream_device(stream, &ws);
+    if (e != hipSuccess) return hip_status(e);
+    ws_bytes = M3_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < need) return M3_ERR_WORKSPACE;
 
   m3::PrefillArgs a{};
@@ -159,6 +205,7 @@ const char* m3_status_str(m3_status s) {
     case M3_ERR_ALIGN: return "pointer not 16-byte aligned";
     case M3_ERR_WORKSPACE: return "workspace missing or too small";
     case M3_ERR_HIP: return "HIP launch failed";
+    case M3_ERR_TOO_LARGE: return "call needs more than the built-in scratch buffer";
   }
   return "unknown status";
 }
@@ -176,6 +223,15 @@ m3_status m3_scan_prefill(const m3_dims* d, const void* x, const void* dt, const
                           const float* h0, const void* x_prev, const void* B_prev, void* y,
                           float* hT, void* ws, size_t ws_bytes, void* stream) {
   return scan_prefill(d, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, ws, ws_bytes,
+                      false, stream);
+}
+
+m3_status m3_scan_prefill_noalloc(const m3_dims* d, const void* x, const void* dt,
+                                  const float* A, const void* lam, const void* theta,
+                                  const void* B, const void* C, const float* h0,
+                                  const void* x_prev, const void* B_prev, void* y, float* hT,
+                                  void* stream) {
+  return scan_prefill(d, x, dt, A, lam, theta, B, C, h0, x_prev, B_prev, y, hT, nullptr, 0, true,
                       stream);
 }
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert m3.m3_status_str(s) != "unknown status"
     assert m3.m3_status_str(99) == "unknown status"
 
@@ -71,6 +71,13 @@ def _prefill(d, ws_bytes=1 << 40, **over):
     return m3.library().m3_scan_prefill(ctypes.byref(d), *args.values(), ws_bytes, None)
 
 
+def _noalloc(d, **over):
+    args = dict(x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None, Bp=None,
+                y=P16, hT=None)
+    args.update(over)
+    return m3.library().m3_scan_prefill_noalloc(ctypes.byref(d), *args.values(), None)
+
+
 def _varlen(d, ws_bytes=1 << 40, **over):
     args = dict(cu=P16, x=P16, dt=P16, A=P16, lam=P16, th=P16, B=P16, C=P16, h0=None, xp=None,
                 Bp=None, y=P16, hT=None, ws=P16)
@@ -100,7 +107,7 @@ def test_workspace_size():
     assert m3.library().m3_prefill_workspace_size(None) == 0
 
 
-@pytest.mark.parametrize("call", [_decode, _tokens, _prefill, _varlen, _backward])
+@pytest.mark.parametrize("call", [_decode, _tokens, _prefill, _noalloc, _varlen, _backward])
 def test_error_paths(call):
     assert m3.library().m3_decode_step(None, *([None] * 12)) == 1
     assert call(_dims(), x=None) == 1                           # NULL input
@@ -139,6 +146,17 @@ def test_prefill_specific_errors():
     assert _prefill(_dims(), hT=P_MIS) == 5
 
 
+def test_noalloc_specific_errors():
+    """Calls whose workspace would exceed the library's scratch buffer are
+    refused before anything is looked up or launched."""
+    assert _noalloc(_dims(seqlen=0)) == 2
+    assert _noalloc(_dims(chunk=32)) == 4
+    big = _dims(batch=4, seqlen=2048, nheads=32)
+    assert m3.m3_prefill_workspace_size(big) > m3.M3_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == 8
+    assert _noalloc(big, hT=P_MIS) == 5
+
+
 def test_varlen_specific_errors():
     assert _varlen(_dims(), cu=None) == 1
     assert _varlen(_dims(), cu=ctypes.c_void_p(4098)) == 5      # offsets are int32
@@ -174,7 +192,7 @@ def test_theta_proj_errors():
         d._keep = tp
         d.tp = ctypes.pointer(tp)
         return d
-    for call in (_decode, _prefill, _varlen):
+    for call in (_decode, _prefill, _noalloc, _varlen):
         assert call(with_tp(dim=48)) == 2                       # not a multiple of 32
         assert call(with_tp(dim=0)) == 2
         assert call(with_tp(u=None)) == 1
