@@ -96,6 +96,105 @@ __device__ __forceinline__ float rows_sum(float* v, int j) {
 }  // namespace
 
 // --------------------------------------------------------------------------
+// Single input.  The token inputs of KG consecutive tokens (dt, lam, A, the
+// phases, B and C rows, and x of the block's rows) are staged in LDS by the
+// whole block in one round trip, double-buffered: group g + 1's loads are in
+// flight while group g's tokens are applied.  Fetching each token's inputs
+// one token ahead left every token waiting for a memory round trip, several
+// per call, while the block's state stayed idle in registers.
+constexpr int kTokGroup = 4;
+
+template <typename TI, int N, int NR>
+struct TokGroup {
+  float d[kTokGroup], l[kTokGroup], A[kTokGroup];
+  float th[kTokGroup][N / 2];
+  f4 b[kTokGroup][N / 4];
+  f4 c[kTokGroup][N / 4];
+  float x[kTokGroup][NR];
+};
+
+// One group's inputs in registers, as loaded, spread over the block's 256
+// threads: 8-element vectors of B and C (then of the phases), one x element
+// and one token scalar per thread item.  Every lane loads from a valid
+// address (tokens past K and rows past P read the last ones; items past the
+// counts read the first) and the extra values are not stored.
+template <typename TI, int N, int NR>
+struct TokGroupLoad {
+  static constexpr int NBC = kTokGroup * N / 4;        // B and C vectors
+  static constexpr int NTH = kTokGroup * (N / 2) / 8;  // phase vectors
+  static constexpr int NX = kTokGroup * NR;            // x elements
+  static constexpr int IBC = (NBC + 255) / 256, ITH = (NTH + 255) / 256, IX = (NX + 255) / 256;
+  Vec8<TI> bc[IBC], th[ITH];
+  Raw1<TI> x[IX], d, l;
+  float A;
+  __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k0, int prow0) {
+    const int tid = threadIdx.x;
+    const int klast = a.K - 1;
+#pragma unroll
+    for (int i = 0; i < IBC; ++i) {
+      const int v = min(tid + 256 * i, NBC - 1);
+      const int j = v / (N / 4), w = v % (N / 4);   // token, vector (B: w < N/8)
+      const TI* src = static_cast<const TI*>(w < N / 8 ? a.Bt : a.Ct);
+      bc[i].load(src + tok_group(a, bh, min(k0 + j, klast)) * N + 8 * (w % (N / 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < ITH; ++i) {
+      const int v = min(tid + 256 * i, NTH - 1);
+      const int j = v / (N / 16), w = v % (N / 16);
+      th[i].load(static_cast<const TI*>(a.theta) + tok_group(a, bh, min(k0 + j, klast)) * (N / 2) +
+                 8 * w);
+    }
+#pragma unroll
+    for (int i = 0; i < IX; ++i) {
+      const int e = min(tid + 256 * i, NX - 1);
+      const int j = e / NR, r = e % NR;
+      x[i].load(static_cast<const TI*>(a.x),
+                tok_head(a, bh, min(k0 + j, klast)) * a.P + min(prow0 + r, a.P - 1));
+    }
+    const int j = min(tid % kTokGroup, kTokGroup - 1);
+    const int64_t t = tok_head(a, bh, min(k0 + j, klast));
+    d.load(static_cast<const TI*>(a.dt), t);
+    l.load(static_cast<const TI*>(a.lam), t);
+    A = (a.flags & kAPerToken) ? a.A[t] : a.A[bh % a.H];
+  }
+  __device__ __forceinline__ void store(TokGroup<TI, N, NR>& g) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < IBC; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NBC) {
+        const int j = v / (N / 4), w = v % (N / 4);
+        float e[8];
+        bc[i].get(e);
+        f4* dst = w < N / 8 ? &g.b[j][2 * w] : &g.c[j][2 * (w - N / 8)];
+        dst[0] = f4{e[0], e[1], e[2], e[3]};
+        dst[1] = f4{e[4], e[5], e[6], e[7]};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ITH; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NTH) {
+        const int j = v / (N / 16), w = v % (N / 16);
+        float e[8];
+        th[i].get(e);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g.th[j][8 * w + q] = e[q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < IX; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NX) g.x[e / NR][e % NR] = x[i].f();
+    }
+    if (tid < kTokGroup) {
+      g.d[tid] = d.f();
+      g.l[tid] = l.f();
+      g.A[tid] = A;
+    }
+  }
+};
+
 // four waves per SIMD (at most 128 registers) for the 8-row blocks; the
 // B/C preparation needs more registers than that
 template <typename TI, typename TO, int N, int UNR, bool PREV, bool PREP>
@@ -104,42 +203,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
   constexpr int LPR = N / 4;      // lanes per state row
   constexpr int RPW = 64 / LPR;   // rows per wave per pass
   constexpr int RPB = 4 * RPW;    // rows per block per pass
-  // a unit's rows may be split over several blocks (UNR * RPB rows each)
-  const int nblk = (a.P + UNR * RPB - 1) / (UNR * RPB);
+  constexpr int NR = UNR * RPB;   // rows per block
+  static_assert(N % 16 == 0, "whole phase vectors per token");
+  __shared__ TokGroup<TI, N, NR> grp[2];
+  // a unit's rows may be split over several blocks (NR rows each)
+  const int nblk = (a.P + NR - 1) / NR;
   const int bh = blockIdx.x / nblk;
   const int P = a.P;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n0 = 4 * (lane % LPR);
-  const int rsub = (blockIdx.x % nblk) * UNR * RPB + wave * RPW + lane / LPR;
+  const int prow0 = (blockIdx.x % nblk) * NR;     // the block's first row
+  const int rloc = wave * RPW + lane / LPR;        // this lane's first row, within the block
+  const int rsub = prow0 + rloc;
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
-  const TI* __restrict__ X = static_cast<const TI*>(a.x);
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.Bt);
-  const TI* __restrict__ Cg = static_cast<const TI*>(a.Ct);
   TO* __restrict__ Y = static_cast<TO*>(a.y);
+  const int ngrp = (a.K + kTokGroup - 1) / kTokGroup;
 
-  // a lane's own two pairs (columns n0..n0+3) need their two phases only:
-  // no table, no barrier between tokens
-  const TI* __restrict__ Tg = static_cast<const TI*>(a.theta);
-  const TI* __restrict__ Dg = static_cast<const TI*>(a.dt);
-  const TI* __restrict__ Lg = static_cast<const TI*>(a.lam);
-  auto scal = [&](int k, float& d, float& l, float& A, f2& th) {
-    const int64_t t = tok_head(a, bh, k);
-    d = ld1(Dg, t);
-    l = ld1(Lg, t);
-    A = (a.flags & kAPerToken) ? a.A[t] : a.A[bh % a.H];
-    th = ld2(Tg, tok_group(a, bh, k) * (N / 2) + n0 / 2);
-  };
-  // token 0's inputs go out first, then the whole state of the unit
-  float dk, lk, Ak;
-  f2 thk;
-  scal(0, dk, lk, Ak, thk);
-  f4 bk = ld4(Bg, tok_group(a, bh, 0) * N + n0);
-  f4 ck = ld4(Cg, tok_group(a, bh, 0) * N + n0);
-  float xk[UNR];
-#pragma unroll
-  for (int u = 0; u < UNR; ++u) xk[u] = ld1(X, tok_head(a, bh, 0) * P + min(u * RPB + rsub, P - 1));
-  // the token before the first one: x_prev, B_prev (or zero)
+  // the first group's inputs go out first, then the token before the first
+  // one, then the block's state
+  TokGroupLoad<TI, N, NR> gl;
+  gl.load(a, bh, 0, prow0);
   f4 bo = PREV ? ld4(static_cast<const TI*>(a.Bp), unit_group(a, bh) * N + n0) : f4{0, 0, 0, 0};
   float xo[UNR];
 #pragma unroll
@@ -154,91 +238,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
     bbias = ld4_or(a.bc.Bb, hb0, bbias);
     cbias = ld4_or(a.bc.Cb, hb0, cbias);
   }
+  // the token-side reads stay ahead of the state stream
+  asm volatile("" ::: "memory");
+  f4 v[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) v[u] = ld4_state(hb + (int64_t)min(u * RPB + rsub, P - 1) * N + n0);
   // a row's N/4 lanes hold a token's whole B and C
   auto prep = [&](f4 u, f4 w, f4 b) {
     const float inv = bc_inv_rms(a.bc, group_sum<LPR>(u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w), N);
     return u * inv * w + b;
   };
-  f4 v[UNR];
-#pragma unroll
-  for (int u = 0; u < UNR; ++u) v[u] = ld4_state(hb + (int64_t)min(u * RPB + rsub, P - 1) * N + n0);
   if (PREP && PREV) bo = prep(bo, bw, bbias);   // bo always holds a prepared B
+  gl.store(grp[0]);
+  __syncthreads();
 
-  for (int k = 0; k < a.K; ++k) {
-    // the next token's inputs fly, as loaded, while this one is applied (the
-    // last token re-reads its own and drops them: no branch around a load)
-    const int kn = min(k + 1, a.K - 1);
-    const int64_t tn = tok_head(a, bh, kn);
-    Raw1<TI> dn, ln, xn[UNR];
-    dn.load(Dg, tn);
-    ln.load(Lg, tn);
-    const float An = (a.flags & kAPerToken) ? a.A[tn] : a.A[bh % a.H];
-    RawVec<TI, 2> thn;
-    RawVec<TI, 4> bn, cn;
-    thn.load(Tg + tok_group(a, bh, kn) * (N / 2) + n0 / 2);
-    bn.load(Bg + tok_group(a, bh, kn) * N + n0);
-    cn.load(Cg + tok_group(a, bh, kn) * N + n0);
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) xn[u].load(X, tn * P + min(u * RPB + rsub, P - 1));
-    const float alpha = expf(dk * Ak);
-    const float beta = (1.0f - lk) * dk * alpha;
-    const float gamma = lk * dk;
-    const bool ang = (a.flags & kThetaIsAngle) != 0;
-    const f2 r0 = cos_sin_turns(ang ? thk.x : dk * thk.x);
-    const f2 r1 = cos_sin_turns(ang ? thk.y : dk * thk.y);
-    if constexpr (PREP) {
-      bk = prep(bk, bw, bbias);
-      ck = prep(ck, cw, cbias);
-    }
-    const f4 bt = gamma * bk, bp = beta * bo;
-    TO* __restrict__ yk = Y + tok_head(a, bh, k) * P;
-    float part[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      f4 s = alpha * v[u] + xo[u] * bp;
-      s = rot2pairs(s, r0, r1);
-      s += xk[u] * bt;
-      v[u] = s;
-      part[u] = s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w;
-    }
-    // y of the lane's UNR rows: summed over the row's LPR lanes
-    float tot[UNR];
-    if constexpr (UNR <= LPR) {
-      tot[0] = rows_sum<LPR, UNR>(part, lane % LPR);
-    } else {
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) tot[u] = group_sum<LPR>(part[u]);
-    }
-    // the next token's inputs come into use before this token's y stores: a
-    // loaded value used after a store would wait for the store as well
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      xo[u] = xk[u];
-      xk[u] = xn[u].f();
-    }
-    bo = bk;
-    {
-      float t4[4], t2[2];
-      bn.get(t4);
-      bk = f4{t4[0], t4[1], t4[2], t4[3]};
-      cn.get(t4);
-      ck = f4{t4[0], t4[1], t4[2], t4[3]};
-      thn.get(t2);
-      thk = f2{t2[0], t2[1]};
-    }
-    dk = dn.f();
-    lk = ln.f();
-    Ak = An;
-    if constexpr (UNR <= LPR) {
-      const int j = lane % LPR;
-      const int p = (j / (LPR / UNR)) * RPB + rsub;
-      if (j % (LPR / UNR) == 0 && p < P) st1(yk, p, tot[0]);
-    } else {
+  const bool ang = (a.flags & kThetaIsAngle) != 0;
+  for (int gi = 0; gi < ngrp; ++gi) {
+    const TokGroup<TI, N, NR>& gc = grp[gi & 1];
+    const bool more = gi + 1 < ngrp;   // block-uniform
+    if (more) gl.load(a, bh, (gi + 1) * kTokGroup, prow0);
+    const int kend = min(kTokGroup, a.K - gi * kTokGroup);
+    for (int j = 0; j < kend; ++j) {
+      const int k = gi * kTokGroup + j;
+      const float dk = gc.d[j], lk = gc.l[j];
+      const float alpha = expf(dk * gc.A[j]);
+      const float beta = (1.0f - lk) * dk * alpha;
+      const float gamma = lk * dk;
+      const f2 thk = *reinterpret_cast<const f2*>(&gc.th[j][n0 / 2]);   // pairs n0/2, n0/2 + 1
+      const f2 r0 = cos_sin_turns(ang ? thk.x : dk * thk.x);
+      const f2 r1 = cos_sin_turns(ang ? thk.y : dk * thk.y);
+      f4 bk = gc.b[j][n0 / 4], ck = gc.c[j][n0 / 4];
+      if constexpr (PREP) {
+        bk = prep(bk, bw, bbias);
+        ck = prep(ck, cw, cbias);
+      }
+      const f4 bt = gamma * bk, bp = beta * bo;
+      TO* __restrict__ yk = Y + tok_head(a, bh, k) * P;
+      float part[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int p = u * RPB + rsub;
-        if ((lane % LPR) == 0 && p < P) st1(yk, p, tot[u]);
+        const float xk = gc.x[j][u * RPB + rloc];
+        f4 s = alpha * v[u] + xo[u] * bp;
+        s = rot2pairs(s, r0, r1);
+        s += xk * bt;
+        v[u] = s;
+        xo[u] = xk;
+        part[u] = s.x * ck.x + s.y * ck.y + s.z * ck.z + s.w * ck.w;
       }
+      bo = bk;
+      // y of the lane's UNR rows: summed over the row's LPR lanes
+      if constexpr (UNR <= LPR) {
+        const float tot = rows_sum<LPR, UNR>(part, lane % LPR);
+        const int jj = lane % LPR;
+        const int p = (jj / (LPR / UNR)) * RPB + rsub;
+        if (jj % (LPR / UNR) == 0 && p < P) st1(yk, p, tot);
+      } else {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const float tot = group_sum<LPR>(part[u]);
+          const int p = u * RPB + rsub;
+          if ((lane % LPR) == 0 && p < P) st1(yk, p, tot);
+        }
+      }
+    }
+    if (more) {   // the buffer written here was last read by group gi - 1
+      gl.store(grp[(gi + 1) & 1]);
+      __syncthreads();
     }
   }
 #pragma unroll
@@ -456,16 +521,26 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
     for (int kb = 0; kb < KB; ++kb) xo[kb] = 0.0f;
   }
 
+  // token 1's inputs, as loaded: the loads run two tokens ahead of their
+  // use, so that a token's wait for its inputs overlaps two tokens of work
+  TokScalars<TI, N> scn;
+  Raw1<TI> ebn[PER], ecn[PER], xn[KB];
+  {
+    const int k1 = min(1, a.K - 1);
+    scn.load(a, bh, k1);
+    load_bc_raw(k1, ebn, ecn);
+    load_x(X + tok_head(a, bh, k1) * P * R, xn);
+  }
   for (int k = 0; k < a.K; ++k) {
-    // token k + 1's inputs, as loaded (the last token re-reads its own and
-    // drops them): no branch around the loads, no conversion before the
+    // token k + 2's inputs, as loaded (the last tokens re-read the last one
+    // and drop it): no branch around the loads, no conversion before the
     // state update below
-    const int kn = min(k + 1, a.K - 1);
-    TokScalars<TI, N> scn;
-    scn.load(a, bh, kn);
-    Raw1<TI> ebn[PER], ecn[PER], xn[KB];
-    load_bc_raw(kn, ebn, ecn);
-    load_x(X + tok_head(a, bh, kn) * P * R, xn);
+    const int kn2 = min(k + 2, a.K - 1);
+    TokScalars<TI, N> scn2;
+    scn2.load(a, bh, kn2);
+    Raw1<TI> ebn2[PER], ecn2[PER], xn2[KB];
+    load_bc_raw(kn2, ebn2, ecn2);
+    load_x(X + tok_head(a, bh, kn2) * P * R, xn2);
     const Tok& tb = sm.tok[k & 1];
     const float alpha = expf(sc.d() * sc.A);
     float yp[RP];
@@ -509,11 +584,16 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
       eo[q] = eb[q];
       eb[q] = ebn[q].f();
       ec[q] = ecn[q].f();
+      ebn[q] = ebn2[q];
+      ecn[q] = ecn2[q];
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xo[kb] = xk[kb];
     xval(xn, xk);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xn[kb] = xn2[kb];
     sc = scn;
+    scn = scn2;
     // token k + 1's operands into the other buffer (last read at token k - 1,
     // before the previous barrier), before token k's y stores: a loaded value
     // used after a store would wait for the store as well
