@@ -16,8 +16,8 @@
 //    is split over several blocks.
 //  * k_decode_mimo_tok (R > 1): one 16-row block of the state per wave,
 //    P <= 64, in the MFMA D layout (the rank-R terms are MFMA products with
-//    K = R, as in the single-step kernel); rows enter and leave through a
-//    per-wave LDS transpose so that loads and stores cover whole lines.
+//    K = R, as in the single-step kernel), loaded and stored in that layout;
+//    the token tables of a group of tokens are built once per block.
 #include "m3_device.h"
 #include "m3_launch.h"
 
@@ -314,37 +314,169 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
 }
 
 // --------------------------------------------------------------------------
-// D row 4g + i of tile t is state column 16t + 4g + i (as in the single-step
-// kernel): a lane's accumulator is the 16-byte vector of 4 consecutive
-// columns of its row.
+// Rank R > 1.  Each wave holds one 16-row block of the state in the MFMA D
+// layout for all K tokens: D row 4g + i of tile t is state column
+// 16t + 4g + i and D column i16 is state row p, so a lane's accumulator is
+// the 16-byte vector of columns 16t + 4g .. + 3 of its row, loaded and
+// stored in place.  The rank-R terms are MFMA products with K = R (as in the
+// single-step kernel).
+//
+// The inputs of a group of KG tokens are prepared once per block and read
+// by every wave: the pair rotations and the token scalars, B of the token
+// before the group's first (row 0: B_prev for the call's first token, else
+// the previous token's B, read again) and of the group's tokens, and C.
+// With one group per call (K <= KG) the block passes one barrier before
+// its first token and none after; a longer call refills the tables between
+// groups.
+template <int N, int R>
+struct MGroup {
+  static constexpr int RP = (R + 3) & ~3;
+  float al[kTokGroup], be[kTokGroup], ga[kTokGroup];
+  f2 cs[kTokGroup][N / 2];
+  float b[kTokGroup + 1][N * RP];   // [n][r], r padded to RP with zeros
+  float c[kTokGroup][N * RP];
+};
+
+// One group's B and C rows (8-element vectors), phases and token scalars
+// in registers, as loaded, spread over the block's 256 threads.  Vectors
+// 0 .. (KG+1) VR - 1 are the B rows 0..KG, the rest the C rows.  Every lane
+// reads a valid address (tokens past K re-read the last; items past the
+// counts re-read the last item) and only stores what belongs to the group.
+template <typename TI, int N, int R>
+struct MGroupLoad {
+  static constexpr int NE = N * R, VR = NE / 8;
+  static constexpr int NB = (kTokGroup + 1) * VR, NV = NB + kTokGroup * VR;
+  static constexpr int NA = kTokGroup * (N / 2);
+  static constexpr int IV = (NV + 255) / 256, IA = (NA + 255) / 256;
+  static_assert(NE % 8 == 0, "whole 8-element vectors per row");
+  Vec8<TI> bc[IV];
+  Raw1<TI> th[IA], dth[IA];
+  Raw1<TI> d, l;
+  float A;
+  bool b0_zero;   // row 0 is the call's first token's B_{-1} and there is none
+  template <bool PREV>
+  __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k0) {
+    const int tid = threadIdx.x;
+    const int klast = a.K - 1;
+    const TI* Bt = static_cast<const TI*>(a.Bt);
+    const TI* Ct = static_cast<const TI*>(a.Ct);
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int v = min(tid + 256 * i, NV - 1);
+      const TI* src;
+      if (v < NB) {
+        const int k = k0 - 1 + v / VR;   // token of B row v / VR
+        src = (k < 0 && PREV) ? static_cast<const TI*>(a.Bp) + unit_group(a, bh) * NE
+                              : Bt + tok_group(a, bh, min(max(k, 0), klast)) * NE;
+      } else {
+        src = Ct + tok_group(a, bh, min(k0 + (v - NB) / VR, klast)) * NE;
+      }
+      bc[i].load(src + 8 * (v % VR));
+    }
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int e = min(tid + 256 * i, NA - 1);
+      const int k = min(k0 + e / (N / 2), klast);
+      th[i].load(static_cast<const TI*>(a.theta), tok_group(a, bh, k) * (N / 2) + e % (N / 2));
+      dth[i].load(static_cast<const TI*>(a.dt), tok_head(a, bh, k));
+    }
+    const int64_t t = tok_head(a, bh, min(k0 + min(tid, kTokGroup - 1), klast));
+    d.load(static_cast<const TI*>(a.dt), t);
+    l.load(static_cast<const TI*>(a.lam), t);
+    A = (a.flags & kAPerToken) ? a.A[t] : a.A[bh % a.H];
+    b0_zero = !PREV && k0 == 0;
+  }
+  // raw rows into the tables (row 0 zeroed when there is no B_{-1}),
+  // rotations and scalars
+  __device__ __forceinline__ void store(const DecodeArgs& a, MGroup<N, R>& G) const {
+    constexpr int RP = MGroup<N, R>::RP;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NV) {
+        float e[8];
+        bc[i].get(e, !(b0_zero && v < VR));
+        float* row = v < NB ? G.b[v / VR] : G.c[(v - NB) / VR];
+        const int e0 = 8 * (v % VR);
+        if constexpr (RP == R) {
+          *reinterpret_cast<f4*>(row + e0) = f4{e[0], e[1], e[2], e[3]};
+          *reinterpret_cast<f4*>(row + e0 + 4) = f4{e[4], e[5], e[6], e[7]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) row[((e0 + q) / R) * RP + (e0 + q) % R] = e[q];
+        }
+      }
+    }
+    const bool ang = (a.flags & kThetaIsAngle) != 0;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NA) {
+        const float th_ = th[i].f();
+        G.cs[e / (N / 2)][e % (N / 2)] = cos_sin_turns(ang ? th_ : dth[i].f() * th_);
+      }
+    }
+    if (tid < kTokGroup) {
+      const float dd = d.f(), ll = l.f();
+      const float alpha = expf(dd * A);
+      G.al[tid] = alpha;
+      G.be[tid] = (1.0f - ll) * dd * alpha;
+      G.ga[tid] = ll * dd;
+    }
+  }
+};
+
+// The B/C preparation of a group's tables in place: the inverse RMS of
+// every (row, rank column) over its N entries (four lanes per column, each
+// adding its entries n = lane, lane + 4, ... in order, then two xor steps:
+// a fixed order), then x * inv * w[n] + bias[n][r].  Barriers between the
+// passes; the caller's barrier ends the last.
+template <int N, int R>
+__device__ __forceinline__ void mgroup_prep(const BCPrep& bc, MGroup<N, R>& G, float (*inv)[R],
+                                            const float (*pw)[N], const float (*pb)[N * R]) {
+  constexpr int RP = MGroup<N, R>::RP;
+  constexpr int ROWS = 2 * kTokGroup + 1;   // B rows 0..KG, then C rows
+  constexpr int NC = ROWS * R;
+  const int tid = threadIdx.x;
+  __syncthreads();   // the raw rows are in place
+  for (int c0 = 0; c0 < NC; c0 += 64) {   // 64 columns x 4 lanes per pass
+    const int cc = c0 + tid / 4;
+    const int col = min(cc, NC - 1);
+    const int row = col / R, r = col % R;
+    const float* src = row <= kTokGroup ? G.b[row] : G.c[row - kTokGroup - 1];
+    float s = 0.0f;
+    for (int n = tid % 4; n < N; n += 4) {
+      const float v = src[n * RP + r];
+      s += v * v;
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (cc < NC && tid % 4 == 0) inv[row][r] = bc_inv_rms(bc, s, N);
+  }
+  __syncthreads();
+  for (int i = tid; i < ROWS * N * R; i += 256) {
+    const int row = i / (N * R), j = i % (N * R), n = j / R, r = j % R;
+    const bool isb = row <= kTokGroup;
+    float* dst = isb ? &G.b[row][n * RP + r] : &G.c[row - kTokGroup - 1][n * RP + r];
+    *dst = *dst * inv[row][r] * pw[isb ? 0 : 1][n] + pb[isb ? 0 : 1][j];
+  }
+}
+
+// (four waves per SIMD at rank <= 4, at most 128 registers: the state's 32,
+// the next group's inputs in flight and one tile's operands)
 template <typename TI, typename TO, int N, int R, bool PREV, bool PREP>
-__global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
-  constexpr int NT = N / 16;
-  constexpr int KB = (R + 3) / 4;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 : 1))) void k_decode_mimo_tok(DecodeArgs a) {
+  constexpr int NT = N / 16;          // 16-column tiles of a row block
+  constexpr int KB = (R + 3) / 4;     // K blocks of 4 for the MFMA
   constexpr int RP = (R + 3) & ~3;
   constexpr int NE = N * R;
-  constexpr int PER = (NE + 255) / 256;
-  constexpr int V4 = N / 4;
-  constexpr int LV = 16 * V4 / 64;
-  // per-token operands, double-buffered (token k + 1's are written while
-  // token k is applied: one barrier per token); the row transposes at the
-  // start and the end share the space
-  struct Tok {
-    f2 cs[N / 2];
-    float bp[N * RP];     // beta_k * B_{k-1}   [n][r]
-    float bt[N * RP];     // gamma_k * B_k      [n][r]
-    float c[N * RP];      // C_k                [n][r]
-  };
-  __shared__ union {
-    Tok tok[2];
-    f4 tr[4][16][N / 4 + 1];
-  } sm;
-  // B/C preparation: this head's weights and biases ([0] B, [1] C), and
-  // each wave's partial sums of squares per rank column of the B, C and
-  // (first token) B_prev that a table build prepares
+  __shared__ MGroup<N, R> G;
+  // B/C preparation: this head's weights ([0] B, [1] C), biases, and the
+  // inverse RMS of the group's rows
   __shared__ float pw_sh[PREP ? 2 : 1][PREP ? N : 1];
   __shared__ float pb_sh[PREP ? 2 : 1][PREP ? NE : 1];
-  __shared__ float part_sh[4][3][R];
+  __shared__ float inv_sh[PREP ? 2 * kTokGroup + 1 : 1][R];
 
   const int bh = blockIdx.x;
   const int P = a.P;
@@ -355,273 +487,164 @@ __global__ __launch_bounds__(256) void k_decode_mimo_tok(DecodeArgs a) {
   const int g = lane >> 4;
   const bool rows = wave * 16 < P;   // this wave's 16-row block exists
   const int p = wave * 16 + i16;
+  const int prow = rows ? p : 0;     // a valid row for every lane's reads
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
   const TI* __restrict__ X = static_cast<const TI*>(a.x);
-  const TI* __restrict__ Bg = static_cast<const TI*>(a.Bt);
-  const TI* __restrict__ Cg = static_cast<const TI*>(a.Ct);
   TO* __restrict__ Y = static_cast<TO*>(a.y);
+  const int ngrp = (a.K + kTokGroup - 1) / kTokGroup;
 
-  auto load_bc = [&](int k, float* eb, float* ec) {
-    const TI* __restrict__ Bk = Bg + tok_group(a, bh, k) * NE;
-    const TI* __restrict__ Ck = Cg + tok_group(a, bh, k) * NE;
+  // x of the lane's row and ranks 4kb + g for the token before the group's
+  // first (j = 0) and the group's tokens (j = 1..KG), as loaded
+  auto load_x = [&](int k0, Raw1<TI> (*xr)[KB]) {
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int i = min(tid + 256 * q, NE - 1);
-      eb[q] = ld1(Bk, i);
-      ec[q] = ld1(Ck, i);
-    }
-  };
-  // the next token's B and C elements, as loaded
-  auto load_bc_raw = [&](int k, Raw1<TI>* eb, Raw1<TI>* ec) {
-    const TI* __restrict__ Bk = Bg + tok_group(a, bh, k) * NE;
-    const TI* __restrict__ Ck = Cg + tok_group(a, bh, k) * NE;
+    for (int j = 0; j <= kTokGroup; ++j) {
+      const int k = k0 - 1 + j;
+      const TI* src = (k < 0 && PREV) ? static_cast<const TI*>(a.xp) + (int64_t)bh * P * R
+                                      : X + tok_head(a, bh, min(max(k, 0), a.K - 1)) * P * R;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int i = min(tid + 256 * q, NE - 1);
-      eb[q].load(Bk, i);
-      ec[q].load(Ck, i);
-    }
-  };
-  // x of this lane's rank r = 4 kb + g, as loaded (lanes with no such row or
-  // rank read element 0; xval zeroes them): no branch around the load
-  auto load_x = [&](const TI* __restrict__ src, Raw1<TI>* xr) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int r = 4 * kb + g;
-      xr[kb].load(src, (rows && r < R) ? (int64_t)p * R + r : 0);
-    }
-  };
-  auto xval = [&](const Raw1<TI>* xr, float* xv) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xv[kb] = (rows && 4 * kb + g < R) ? xr[kb].f() : 0.0f;
-  };
-  // token operands into buffer tb: beta/gamma-scaled B, C, phases.  With
-  // the preparation, eb and ec (and eo when prep_prev) are raw on entry and
-  // prepared on return: each wave reduces its elements' squares per rank
-  // column into part_sh, and after a barrier every thread sums the four
-  // waves' parts (the sums' last readers are past the barrier that ends
-  // each token, before the next build writes them).
-  auto put_tables = [&](Tok& tb, const TokScalars<TI, N>& sc, float* eb, float* eo, float* ec,
-                        bool prep_prev) {
-    float alpha, beta, gamma;
-    sc.finish(a, alpha, beta, gamma, tb.cs);
-    if constexpr (PREP) {
-      auto wave_parts = [&](const float* e, int arr) {
-        float part[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int i = tid + 256 * q;
-          const float v = i < NE ? e[q] : 0.0f;
-#pragma unroll
-          for (int r = 0; r < R; ++r) part[r] += (i % R == r) ? v * v : 0.0f;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = group_sum<64>(part[r]);
-        if (lane == 0) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) part_sh[wave][arr][r] = part[r];
-        }
-      };
-      wave_parts(eb, 0);
-      wave_parts(ec, 2);
-      if (prep_prev) wave_parts(eo, 1);
-      __syncthreads();
-      auto inv = [&](int arr, int r) {
-        return bc_inv_rms(a.bc, part_sh[0][arr][r] + part_sh[1][arr][r] + part_sh[2][arr][r] +
-                                    part_sh[3][arr][r], N);
-      };
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int i = min(tid + 256 * q, NE - 1);
-        const int r = i % R, n = i / R;
-        eb[q] = eb[q] * inv(0, r) * pw_sh[0][n] + pb_sh[0][i];
-        ec[q] = ec[q] * inv(2, r) * pw_sh[1][n] + pb_sh[1][i];
-        if (prep_prev) eo[q] = eo[q] * inv(1, r) * pw_sh[0][n] + pb_sh[0][i];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int i = tid + 256 * q;
-      if (i < NE) {
-        const int j = (i / R) * RP + i % R;
-        tb.bt[j] = gamma * eb[q];
-        tb.bp[j] = beta * eo[q];
-        tb.c[j] = ec[q];
+      for (int kb = 0; kb < KB; ++kb) {
+        const int r = min(4 * kb + g, R - 1);
+        xr[j][kb].load(src, (int64_t)prow * R + r);
       }
     }
   };
+  // the value of x (j, kb) for this lane: zero with no row, no rank
+  // 4kb + g, or no x_{-1}
+  auto xval = [&](const Raw1<TI> (*xr)[KB], int j, int kb, int k0) {
+    const bool live = rows && 4 * kb + g < R && (PREV || k0 + j > 0);
+    return live ? xr[j][kb].f() : 0.0f;
+  };
 
-  TokScalars<TI, N> sc;
-  sc.load(a, bh, 0);
-  float eb[PER], ec[PER], eo[PER];
-  load_bc(0, eb, ec);
-  float xk[KB], xo[KB];
-  Raw1<TI> xkr[KB], xor_[KB];
-  load_x(X + tok_head(a, bh, 0) * P * R, xkr);
-  if (PREV) {
-    const TI* __restrict__ Bp = static_cast<const TI*>(a.Bp) + unit_group(a, bh) * NE;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) eo[q] = ld1(Bp, min(tid + 256 * q, NE - 1));
-    load_x(static_cast<const TI*>(a.xp) + (int64_t)bh * P * R, xor_);
-  } else {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) eo[q] = 0.0f;
-  }
-
-  // the wave's 16 state rows, row-contiguous, then into the D layout
-  f4 v[NT];
-  if (rows) {
-    f4 raw[LV];
-#pragma unroll
-    for (int j = 0; j < LV; ++j) {
-      const int q = lane + 64 * j;
-      raw[j] = ld4_state(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4));
-    }
-#pragma unroll
-    for (int j = 0; j < LV; ++j) {
-      const int q = lane + 64 * j;
-      sm.tr[wave][q / V4][q % V4] = raw[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = sm.tr[wave][i16][(16 * t + 4 * g) / 4];
-  } else {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = f4{0, 0, 0, 0};
-  }
-  if constexpr (PREP) {   // this head's weights and biases (1 and 0 when absent)
+  // the first group's inputs go out first, then the state
+  MGroupLoad<TI, N, R> gl;
+  gl.template load<PREV>(a, bh, 0);
+  Raw1<TI> xr[kTokGroup + 1][KB];
+  load_x(0, xr);
+  float wv[PREP ? 4 : 1][PREP ? (NE + 255) / 256 : 1];
+  if constexpr (PREP) {   // weights and this head's biases (1 and 0 when absent)
     const int64_t hb0 = (int64_t)(bh % a.H) * NE;
-    for (int i = tid; i < N; i += 256) {
-      pw_sh[0][i] = ld_or(a.bc.Bw, i, 1.0f);
-      pw_sh[1][i] = ld_or(a.bc.Cw, i, 1.0f);
-    }
-    for (int i = tid; i < NE; i += 256) {
-      pb_sh[0][i] = ld_or(a.bc.Bb, hb0 + i, 0.0f);
-      pb_sh[1][i] = ld_or(a.bc.Cb, hb0 + i, 0.0f);
-    }
-  }
-  __syncthreads();   // every wave's transpose is read before the tables take the space
-  if constexpr (RP != R) {
-    for (int i = tid; i < N * RP; i += 256)
-      sm.tok[0].bt[i] = sm.tok[0].bp[i] = sm.tok[0].c[i] = sm.tok[1].bt[i] = sm.tok[1].bp[i] =
-          sm.tok[1].c[i] = 0.0f;
-    __syncthreads();
-  }
-  put_tables(sm.tok[0], sc, eb, eo, ec, PREV);
-  __syncthreads();
-  xval(xkr, xk);
-  if (PREV) {
-    xval(xor_, xo);
-  } else {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xo[kb] = 0.0f;
+    for (int q = 0; q < (NE + 255) / 256; ++q) {
+      const int i = min(tid + 256 * q, NE - 1);
+      wv[0][q] = ld_or(a.bc.Bw, min(i, N - 1), 1.0f);
+      wv[1][q] = ld_or(a.bc.Cw, min(i, N - 1), 1.0f);
+      wv[2][q] = ld_or(a.bc.Bb, hb0 + i, 0.0f);
+      wv[3][q] = ld_or(a.bc.Cb, hb0 + i, 0.0f);
+    }
   }
+  asm volatile("" ::: "memory");   // the token-side reads stay ahead of the state stream
+  f4 v[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) v[t] = ld4_state(hb + (int64_t)prow * N + 16 * t + 4 * g);
 
-  // token 1's inputs, as loaded: the loads run two tokens ahead of their
-  // use, so that a token's wait for its inputs overlaps two tokens of work
-  TokScalars<TI, N> scn;
-  Raw1<TI> ebn[PER], ecn[PER], xn[KB];
-  {
-    const int k1 = min(1, a.K - 1);
-    scn.load(a, bh, k1);
-    load_bc_raw(k1, ebn, ecn);
-    load_x(X + tok_head(a, bh, k1) * P * R, xn);
+  if constexpr (RP != R) {   // the padding columns stay zero for every group
+    for (int i = tid; i < (2 * kTokGroup + 1) * N; i += 256) {
+      float* row = i < (kTokGroup + 1) * N ? G.b[i / N] : G.c[i / N - kTokGroup - 1];
+#pragma unroll
+      for (int r = R; r < RP; ++r) row[(i % N) * RP + r] = 0.0f;
+    }
   }
-  for (int k = 0; k < a.K; ++k) {
-    // token k + 2's inputs, as loaded (the last tokens re-read the last one
-    // and drop it): no branch around the loads, no conversion before the
-    // state update below
-    const int kn2 = min(k + 2, a.K - 1);
-    TokScalars<TI, N> scn2;
-    scn2.load(a, bh, kn2);
-    Raw1<TI> ebn2[PER], ecn2[PER], xn2[KB];
-    load_bc_raw(kn2, ebn2, ecn2);
-    load_x(X + tok_head(a, bh, kn2) * P * R, xn2);
-    const Tok& tb = sm.tok[k & 1];
-    const float alpha = expf(sc.d() * sc.A);
-    float yp[RP];
+  if constexpr (PREP) {
 #pragma unroll
-    for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
-    if (rows) {
+    for (int q = 0; q < (NE + 255) / 256; ++q) {
+      const int i = tid + 256 * q;
+      if (i < N) {
+        pw_sh[0][i] = wv[0][q];
+        pw_sh[1][i] = wv[1][q];
+      }
+      if (i < NE) {
+        pb_sh[0][i] = wv[2][q];
+        pb_sh[1][i] = wv[3][q];
+      }
+    }
+  }
+  gl.store(a, G);
+  if constexpr (PREP) mgroup_prep<N, R>(a.bc, G, inv_sh, pw_sh, pb_sh);
+  __syncthreads();
+
+  // lane bases of the LDS operands: A-operand row i16 is state column
+  // 16t + i16 (k lane group g), D rows 4g .. 4g + 3 are columns 16t + 4g ..
+  const float* __restrict__ b_l = &G.b[0][0] + i16 * RP + g;
+  const float* __restrict__ c_l = &G.c[0][0] + 4 * g * RP;
+  const f2* __restrict__ cs_l = &G.cs[0][0] + 2 * g;
+  for (int gi = 0; gi < ngrp; ++gi) {
+    const int k0 = gi * kTokGroup;
+    const bool more = gi + 1 < ngrp;   // block-uniform
+    Raw1<TI> xn[kTokGroup + 1][KB];
+    if (more) {
+      gl.template load<PREV>(a, bh, k0 + kTokGroup);
+      load_x(k0 + kTokGroup, xn);
+    }
+    const int kend = min(kTokGroup, a.K - k0);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f4 acc = alpha * v[t];
-        const int nA = 16 * t + 4 * (i16 >> 2) + (i16 & 3);   // state column of A-operand row i16
+    for (int j = 0; j < kTokGroup; ++j) {   // unrolled: xr indexed by constants
+      if (j >= kend) break;
+      const float alpha = G.al[j];
+      float xo[KB], xk[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb.bp[nA * RP + 4 * kb + g], xo[kb], acc, 0, 0, 0);
-        const int n = 16 * t + 4 * g;
-        acc = rot2pairs(acc, tb.cs[n / 2], tb.cs[n / 2 + 1]);
+      for (int kb = 0; kb < KB; ++kb) {
+        xo[kb] = G.be[j] * xval(xr, j, kb, k0);
+        xk[kb] = G.ga[j] * xval(xr, j + 1, kb, k0);
+      }
+      float yp[RP];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb.bt[nA * RP + 4 * kb + g], xk[kb], acc, 0, 0, 0);
-        v[t] = acc;
+      for (int r = 0; r < RP; ++r) yp[r] = 0.0f;
+      if (rows) {   // wave-uniform
 #pragma unroll
-        for (int rb = 0; rb < RP; rb += 4) {
-          const f4 c0 = *reinterpret_cast<const f4*>(&tb.c[(n + 0) * RP + rb]);
-          const f4 c1 = *reinterpret_cast<const f4*>(&tb.c[(n + 1) * RP + rb]);
-          const f4 c2 = *reinterpret_cast<const f4*>(&tb.c[(n + 2) * RP + rb]);
-          const f4 c3 = *reinterpret_cast<const f4*>(&tb.c[(n + 3) * RP + rb]);
+        for (int t = 0; t < NT; ++t) {
+          // every LDS operand is a lane base plus a constant offset
+          const int tb = j * (N * RP) + 16 * t * RP;
+          f4 acc = alpha * v[t];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            yp[rb + q] += acc.x * c0[q] + acc.y * c1[q] + acc.z * c2[q] + acc.w * c3[q];
+          for (int kb = 0; kb < KB; ++kb)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b_l[tb + 4 * kb], xo[kb], acc, 0, 0, 0);
+          acc = rot2pairs(acc, cs_l[j * (N / 2) + 8 * t], cs_l[j * (N / 2) + 8 * t + 1]);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b_l[tb + N * RP + 4 * kb], xk[kb], acc, 0, 0, 0);
+          v[t] = acc;
+#pragma unroll
+          for (int rb = 0; rb < RP; rb += 4) {
+            const f4 c0 = *reinterpret_cast<const f4*>(c_l + tb + 0 * RP + rb);
+            const f4 c1 = *reinterpret_cast<const f4*>(c_l + tb + 1 * RP + rb);
+            const f4 c2 = *reinterpret_cast<const f4*>(c_l + tb + 2 * RP + rb);
+            const f4 c3 = *reinterpret_cast<const f4*>(c_l + tb + 3 * RP + rb);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              yp[rb + q] += acc.x * c0[q] + acc.y * c1[q] + acc.z * c2[q] + acc.w * c3[q];
+          }
+          // one tile's LDS operands at a time (registers and occupancy)
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // one tile's LDS operands at a time (registers and occupancy)
-        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         yp[r] += __shfl_xor(yp[r], 16, 64);
         yp[r] += __shfl_xor(yp[r], 32, 64);
       }
+      if (rows && g == 0) {
+        TO* __restrict__ yk = Y + tok_head(a, bh, k0 + j) * P * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) st1(yk, (int64_t)p * R + r, yp[r]);
+      }
     }
+    if (more) {   // every wave is past the group's tokens before its tables change
+      __syncthreads();
+      gl.store(a, G);
+      if constexpr (PREP) mgroup_prep<N, R>(a.bc, G, inv_sh, pw_sh, pb_sh);
+      __syncthreads();
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      eo[q] = eb[q];
-      eb[q] = ebn[q].f();
-      ec[q] = ecn[q].f();
-      ebn[q] = ebn2[q];
-      ecn[q] = ecn2[q];
+      for (int j = 0; j <= kTokGroup; ++j)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) xr[j][kb] = xn[j][kb];
     }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xo[kb] = xk[kb];
-    xval(xn, xk);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xn[kb] = xn2[kb];
-    sc = scn;
-    scn = scn2;
-    // token k + 1's operands into the other buffer (last read at token k - 1,
-    // before the previous barrier), before token k's y stores: a loaded value
-    // used after a store would wait for the store as well
-    if (k + 1 < a.K) put_tables(sm.tok[(k + 1) & 1], sc, eb, eo, ec, false);
-    if (rows && g == 0) {
-      TO* __restrict__ yk = Y + tok_head(a, bh, k) * P * R;
-#pragma unroll
-      for (int r = 0; r < R; ++r) st1(yk, (int64_t)p * R + r, yp[r]);
-    }
-    __syncthreads();
   }
 
-  // the wave's rows back to HBM, row-contiguous (every wave is past the
-  // last token's tables: the loop ends with a barrier)
   if (rows) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[t];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int j = 0; j < LV; ++j) {
-      const int q = lane + 64 * j;
-      st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4), sm.tr[wave][q / V4][q % V4]);
-    }
+    for (int t = 0; t < NT; ++t) st4_stream(hb + (int64_t)p * N + 16 * t + 4 * g, v[t]);
   }
 }
-
 // --------------------------------------------------------------------------
 namespace {
 

@@ -231,12 +231,15 @@ __device__ __forceinline__ void st1(T* __restrict__ p, int64_t i, float v) {
   p[i] = from_f32<T>(v);
 }
 
-// 16-byte state access.  Loads use the default (cached) policy and stores
-// are non-temporal: on gfx950 this pair streams the decode state fastest
-// (measured: 84 us per B=128 H=64 P=64 N=128 step against 88 us with
-// non-temporal loads and 95 us with cached stores).
+// 16-byte state access, both non-temporal.  A decode step streams a state
+// larger than the 256 MB last-level cache, and in a model with several
+// layers every step's state was pushed out by the other layers' steps.
+// Measured on B=128 H=64 P=64 N=128 single-input steps: 88.0 us when one
+// state is updated every step and 88.6 us when two alternate, against 82.3
+// and 101.2 us with cached loads (which win only while the last step's
+// state is still partly cached, and lose more once it is not).
 __device__ __forceinline__ f4 ld4_state(const float* p) {
-  return *reinterpret_cast<const f4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
 }
 __device__ __forceinline__ void st4_stream(float* p, f4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
