@@ -16,8 +16,9 @@
 //    is split over several blocks.
 //  * k_decode_mimo_tok (R > 1): one 16-row block of the state per wave,
 //    P <= 64, in the MFMA D layout (the rank-R terms are MFMA products with
-//    K = R, as in the single-step kernel), loaded and stored in that layout;
-//    the token tables of a group of tokens are built once per block.
+//    K = R, as in the single-step kernel), loaded in that layout and stored
+//    through a per-wave LDS transpose (whole lines per store); the token
+//    tables of a group of tokens are built once per block.
 #include "m3_device.h"
 #include "m3_launch.h"
 
@@ -317,8 +318,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
 // Rank R > 1.  Each wave holds one 16-row block of the state in the MFMA D
 // layout for all K tokens: D row 4g + i of tile t is state column
 // 16t + 4g + i and D column i16 is state row p, so a lane's accumulator is
-// the 16-byte vector of columns 16t + 4g .. + 3 of its row, loaded and
-// stored in place.  The rank-R terms are MFMA products with K = R (as in the
+// the 16-byte vector of columns 16t + 4g .. + 3 of its row, loaded in
+// place.  The rank-R terms are MFMA products with K = R (as in the
 // single-step kernel).
 //
 // The inputs of a group of KG tokens are prepared once per block and read
@@ -471,7 +472,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 
   constexpr int KB = (R + 3) / 4;     // K blocks of 4 for the MFMA
   constexpr int RP = (R + 3) & ~3;
   constexpr int NE = N * R;
-  __shared__ MGroup<N, R> G;
+  // the group tables, and at the end each wave's rows for the store
+  __shared__ union {
+    MGroup<N, R> G;
+    f4 tr[4][16][N / 4 + 1];
+  } sm;
+  MGroup<N, R>& G = sm.G;
   // B/C preparation: this head's weights ([0] B, [1] C), biases, and the
   // inverse RMS of the group's rows
   __shared__ float pw_sh[PREP ? 2 : 1][PREP ? N : 1];
@@ -640,11 +646,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 
     }
   }
 
+  // the wave's rows back to HBM through LDS, row-contiguous, so that each
+  // store instruction covers whole lines (direct stores from the D layout
+  // write half lines, which the counters show costing about a quarter more
+  // write traffic)
+  __syncthreads();   // every wave is past the last group's tables
   if (rows) {
+    constexpr int V4 = N / 4, LV = 16 * V4 / 64;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) st4_stream(hb + (int64_t)p * N + 16 * t + 4 * g, v[t]);
+    for (int t = 0; t < NT; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < LV; ++j) {
+      const int q = lane + 64 * j;
+      st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4), sm.tr[wave][q / V4][q % V4]);
+    }
   }
 }
+
 // --------------------------------------------------------------------------
 namespace {
 
