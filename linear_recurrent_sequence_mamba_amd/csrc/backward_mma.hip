@@ -6,7 +6,7 @@
 // form of prefill.hip).  With rank R every token is R virtual rows (t, r)
 // of the chunk, and every contraction over them is a dense product of the
 // chunk's Q R = 64 R rows, here on MFMA tiles (mfma_pol.h: fp32 operands
-// for fp32 inputs, fp16 hi + lo splits for bf16 inputs):
+// for fp32 inputs, bf16 hi + lo splits for bf16 inputs):
 //   K1 = Ct Bt^T,  K2 = dY X^T,  W1 = M o K1,  W2 = M o K2   (M: decay mask)
 //   dx  = W1^T dY + diag(m_end) Bt Gt^T
 //   dBt = W2^T Ct + diag(m_end) X Gt

@@ -3,10 +3,12 @@
 // public ABI.
 //
 // A policy fixes how fp32 operands reach the matrix cores: PolF32 keeps
-// them in fp32 (v_mfma_f32_16x16x4_f32); PolF16 splits each into fp16
-// hi + lo parts and forms a product as hi*hi + hi*lo + lo*hi on
-// v_mfma_f32_16x16x32_f16 (about fp32 accuracy), with x (exact in fp16)
-// used unsplit.  Fragments follow the 16x16 MFMA lane layout: lane l holds
+// them in fp32 (v_mfma_f32_16x16x4_f32, the fp32-input path); PolB16 (the
+// bf16-input path, PolHalf) splits each into bf16 hi + lo parts and forms a
+// product as hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (about fp32
+// accuracy, fp32's exponent range), with x (a bf16 input, exact) used
+// unsplit; PolF16 does the same with fp16 parts (more bits, fp16's range)
+// and is kept for comparison.  Fragments follow the 16x16 MFMA lane layout: lane l holds
 // row (or column) l % 16 and k group l / 16; a D tile holds column l % 16
 // and rows 4 (l / 16) .. 4 (l / 16) + 3, so D tiles turn into A operands
 // of the transposed product without a trip through LDS (frag_from_d), and

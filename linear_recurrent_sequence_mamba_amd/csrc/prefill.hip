@@ -33,9 +33,9 @@
 //
 // MFMA operands: with fp32 inputs, v_mfma_f32_16x16x4_f32 on fp32 operands.
 // With bf16 inputs every operand computed in fp32 (rotated B and C, the
-// masked Gram, the state) is split into fp16 hi + lo parts and each product
-// is hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_f16 (about fp32 accuracy);
-// x is exact in fp16 and used unsplit.
+// masked Gram, the state) is split into bf16 hi + lo parts and each product
+// is hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (about fp32 accuracy
+// and fp32's exponent range); x, a bf16 input, is exact and used unsplit.
 #include "chunk_common.h"
 #include "mfma_pol.h"
 
