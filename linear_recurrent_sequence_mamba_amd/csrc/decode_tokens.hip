@@ -327,8 +327,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
 // before the group's first (row 0: B_prev for the call's first token, else
 // the previous token's B, read again) and of the group's tokens, and C.
 // With one group per call (K <= KG) the block passes one barrier before
-// its first token and none after; a longer call refills the tables between
-// groups.
+// its first token and one before the rows go back through LDS; a longer
+// call refills the tables between groups.
 template <int N, int R>
 struct MGroup {
   static constexpr int RP = (R + 3) & ~3;
