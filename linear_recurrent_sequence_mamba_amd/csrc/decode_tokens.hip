@@ -22,6 +22,12 @@
 #include "m3_device.h"
 #include "m3_launch.h"
 
+#ifndef M3_MONEG_WAVES
+#define M3_MONEG_WAVES 4
+#endif
+#ifndef M3_ONEG_WAVES
+#define M3_ONEG_WAVES 6
+#endif
 namespace m3 {
 
 namespace {
@@ -198,8 +204,10 @@ struct TokGroupLoad {
 
 // four waves per SIMD (at most 128 registers) for the 8-row blocks; the
 // B/C preparation needs more registers than that
-template <typename TI, typename TO, int N, int UNR, bool PREV, bool PREP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 && !PREP ? 4 : 1))) void k_decode_siso_tok(
+// ONEG: a call of at most kTokGroup tokens (one group), which needs no
+// registers for the next group's inputs
+template <typename TI, typename TO, int N, int UNR, bool PREV, bool PREP, bool ONEG = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_ONEG_WAVES : UNR == 8 && !PREP ? 4 : 1))) void k_decode_siso_tok(
     DecodeArgs a) {
   constexpr int LPR = N / 4;      // lanes per state row
   constexpr int RPW = 64 / LPR;   // rows per wave per pass
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
   const int rsub = prow0 + rloc;
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
   TO* __restrict__ Y = static_cast<TO*>(a.y);
-  const int ngrp = (a.K + kTokGroup - 1) / kTokGroup;
+  const int ngrp = ONEG ? 1 : (a.K + kTokGroup - 1) / kTokGroup;
 
   // the first group's inputs go out first, then the token before the first
   // one, then the block's state
@@ -256,7 +264,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(UNR == 8 &&
   const bool ang = (a.flags & kThetaIsAngle) != 0;
   for (int gi = 0; gi < ngrp; ++gi) {
     const TokGroup<TI, N, NR>& gc = grp[gi & 1];
-    const bool more = gi + 1 < ngrp;   // block-uniform
+    const bool more = !ONEG && gi + 1 < ngrp;   // block-uniform
     if (more) gl.load(a, bh, (gi + 1) * kTokGroup, prow0);
     const int kend = min(kTokGroup, a.K - gi * kTokGroup);
     for (int j = 0; j < kend; ++j) {
@@ -466,16 +474,19 @@ __device__ __forceinline__ void mgroup_prep(const BCPrep& bc, MGroup<N, R>& G, f
 
 // (four waves per SIMD at rank <= 4, at most 128 registers: the state's 32,
 // the next group's inputs in flight and one tile's operands)
-template <typename TI, typename TO, int N, int R, bool PREV, bool PREP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 : 1))) void k_decode_mimo_tok(DecodeArgs a) {
+template <typename TI, typename TO, int N, int R, bool PREV, bool PREP, bool ONEG = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_MONEG_WAVES : R <= 4 ? 4 : 1))) void k_decode_mimo_tok(DecodeArgs a) {
   constexpr int NT = N / 16;          // 16-column tiles of a row block
   constexpr int KB = (R + 3) / 4;     // K blocks of 4 for the MFMA
   constexpr int RP = (R + 3) & ~3;
   constexpr int NE = N * R;
-  // the group tables, and at the end each wave's rows for the store
+  // the group tables, and at the end each wave's rows for the store (half
+  // a row at a time, so that the buffer is no larger than the tables)
+  constexpr int NHALF = NT >= 2 ? 2 : 1;
+  constexpr int HC = N / NHALF;       // columns per transposed piece
   __shared__ union {
     MGroup<N, R> G;
-    f4 tr[4][16][N / 4 + 1];
+    f4 tr[4][16][HC / 4 + 1];
   } sm;
   MGroup<N, R>& G = sm.G;
   // B/C preparation: this head's weights ([0] B, [1] C), biases, and the
@@ -497,7 +508,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 
   float* __restrict__ hb = a.h + (int64_t)bh * P * N;
   const TI* __restrict__ X = static_cast<const TI*>(a.x);
   TO* __restrict__ Y = static_cast<TO*>(a.y);
-  const int ngrp = (a.K + kTokGroup - 1) / kTokGroup;
+  const int ngrp = ONEG ? 1 : (a.K + kTokGroup - 1) / kTokGroup;
 
   // x of the lane's row and ranks 4kb + g for the token before the group's
   // first (j = 0) and the group's tokens (j = 1..KG), as loaded
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 
   const f2* __restrict__ cs_l = &G.cs[0][0] + 2 * g;
   for (int gi = 0; gi < ngrp; ++gi) {
     const int k0 = gi * kTokGroup;
-    const bool more = gi + 1 < ngrp;   // block-uniform
+    const bool more = !ONEG && gi + 1 < ngrp;   // block-uniform
     Raw1<TI> xn[kTokGroup + 1][KB];
     if (more) {
       gl.template load<PREV>(a, bh, k0 + kTokGroup);
@@ -652,16 +663,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 4 
   // write traffic)
   __syncthreads();   // every wave is past the last group's tables
   if (rows) {
-    constexpr int V4 = N / 4, LV = 16 * V4 / 64;
+    constexpr int V4 = HC / 4, LV = 16 * V4 / 64, TH = NT / NHALF;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[t];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int hf = 0; hf < NHALF; ++hf) {
 #pragma unroll
-    for (int j = 0; j < LV; ++j) {
-      const int q = lane + 64 * j;
-      st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + 4 * (q % V4), sm.tr[wave][q / V4][q % V4]);
+      for (int t = 0; t < TH; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[hf * TH + t];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < LV; ++j) {
+        const int q = lane + 64 * j;
+        st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + hf * HC + 4 * (q % V4),
+                   sm.tr[wave][q / V4][q % V4]);
+      }
+      // this half's reads are done before the next half's writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
@@ -677,6 +696,9 @@ hipError_t launch_siso_tok(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.bc.on) {
     if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, true>), g, b, 0, s, a);
+  } else if (UNR == 8 && a.K <= kTokGroup) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, false, true>), g, b, 0, s, a);
   } else {
     if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, false>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, false>), g, b, 0, s, a);
@@ -690,6 +712,9 @@ hipError_t launch_mimo_tok(const DecodeArgs& a, int units, hipStream_t s) {
   if (a.bc.on) {
     if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false, true>), g, b, 0, s, a);
+  } else if (R <= 4 && a.K <= kTokGroup) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true, false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false, false, true>), g, b, 0, s, a);
   } else {
     if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, true, false>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_decode_mimo_tok<TI, TO, N, R, false, false>), g, b, 0, s, a);
