@@ -78,15 +78,28 @@ def test_tokens_shapes(P, N, R, dt):
     _check(w, _inputs(w))
 
 
+@pytest.mark.parametrize("P,N,R,dt", [
+    (64, 64, 4, "bf16"), (32, 64, 2, "bf16"), (48, 16, 3, "f32"), (64, 128, 4, "f32"),
+    (64, 128, 1, "f32"), (64, 64, 1, "bf16"), (16, 32, 2, "bf16"),
+])
+def test_tokens_shapes_one_group(P, N, R, dt):
+    """Calls of at most four tokens take kernels specialised for one group
+    of tokens (single input with eight row passes, rank <= 4)."""
+    w = I.Workload("t", 100, 2, 3, 3, P, N, R, 64, dt)
+    say(f"decode_tokens one group P={P} N={N} R={R} {dt}")
+    _check(w, _inputs(w))
+
+
+@pytest.mark.parametrize("K", [4, 6])
 @pytest.mark.parametrize("flags", [m3.M3_THETA_IS_ANGLE, m3.M3_A_PER_TOKEN])
 @pytest.mark.parametrize("R", [1, 4])
-def test_tokens_flags(flags, R):
-    w = I.Workload("t", 97, 2, 6, 3, 64, 128, R, 64, "bf16")
+def test_tokens_flags(flags, R, K):
+    w = I.Workload("t", 97, 2, K, 3, 64, 128, R, 64, "bf16")
     d = _inputs(w)
     if flags & m3.M3_A_PER_TOKEN:
         rng = np.random.default_rng(7)
-        d["A"] = torch.from_numpy(-np.exp(rng.uniform(-4, 0, size=(2, 6, 3))).astype(np.float32))
-    say(f"decode_tokens flags={flags} R={R}")
+        d["A"] = torch.from_numpy(-np.exp(rng.uniform(-4, 0, size=(2, K, 3))).astype(np.float32))
+    say(f"decode_tokens flags={flags} R={R} K={K}")
     _check(w, d, flags=flags)
 
 
