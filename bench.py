@@ -6,10 +6,14 @@
 Headline: the SISO decode step at B=128, H=64, P=64, N=128 (bf16 inputs, fp32
 state carried in HBM): K sequential steps after W warm-up steps, every step a
 fresh token from a pool of distinct resident input sets, the state updated in
-place.  `value` is the algorithmic HBM traffic of the K steps divided by their
-wall time on the GPU (GB/s); `us_per_step` is the same time per step.
-`roofline` compares the decode kernel's average duration (HIP events around
-each launch, on the launch stream) with the 8 TB/s HBM peak.
+place.  The K launches are captured in one HIP graph, replayed 11 times with HIP
+events around each replay on the launch stream; `value` is the algorithmic HBM
+traffic of the K steps divided by the median replay's time (GB/s) and
+`us_per_step` the same time per step (with the replays' spread).  `roofline`
+compares that rate with the 8 TB/s HBM peak; `traffic` is the counter-measured
+HBM bytes per launch when the committed counter summary matches the sources.
+The same steps alternating between two states larger together than the
+last-level cache are reported as "*_decode_cold".
 
 In the same run and the same JSON line, under "workloads": the MIMO rank-4
 decode step (same shape), the SISO chunked prefill (B=4, T=2048, H=32) and the
