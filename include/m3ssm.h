@@ -128,7 +128,7 @@ typedef struct {
   int32_t headdim;   /* P                                                  */
   int32_t dstate;    /* N, even                                            */
   int32_t rank;      /* R >= 1; 1 = single input / single output           */
-  int32_t chunk;     /* prefill chunk length Q; 0 = library default (64)   */
+  int32_t chunk;     /* prefill chunk length Q; 0 = library default        */
   int32_t in_dtype;  /* m3_dtype of x, B, C, dt, lam, theta, x_prev, B_prev */
   int32_t out_dtype; /* m3_dtype of y                                      */
   uint32_t flags;    /* M3_THETA_IS_ANGLE | M3_A_PER_TOKEN                 */
@@ -177,7 +177,7 @@ m3_status m3_scan_prefill(const m3_dims* dims, const void* x, const void* dt,
  * ends; the call itself allocates nothing.  A call whose
  * m3_prefill_workspace_size(dims) is larger returns M3_ERR_TOO_LARGE and
  * launches nothing (at P = 64, N = 128: about 2000 chunk-heads, e.g.
- * Bsz * H * ceil(T / 64) <= 2000).  Every call on one GPU uses that GPU's one
+ * Bsz * H * ceil(T / Q) <= 2000).  Every call on one GPU uses that GPU's one
  * buffer, which keeps the last call's contents (the prefill workspace needs
  * no particular contents on entry): calls that overlap in time on one GPU,
  * on different streams or from different threads, race and give wrong
