@@ -544,6 +544,331 @@ def with_single_thread(all_cores, one):
 
 
 # ---------------------------------------------------------------------------
+# The rocprofv3 summaries under profiles/, written from the CSV files of
+# profiled runs of this script (no GPU needed):
+#   python bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR BENCH_JSON
+#   python bench.py --summarize-sq SQ1_DIR SQ2_DIR
+PROFILE_COPY_BYTES = 268435456   # the device copy of copy_reference(), the counters' calibration
+SRC_DECODE = ["decode.hip", "m3_device.h", "m3_launch.h"]
+SRC_TOKENS = ["decode_tokens.hip", "m3_device.h", "m3_launch.h"]
+SRC_PREFILL = ["prefill.hip", "mfma_pol.h", "chunk_common.h", "m3_device.h", "m3_launch.h"]
+SRC_BACKWARD = ["backward.hip", "backward_mma.hip"] + SRC_PREFILL
+PROF_STATS_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_default -o bench -- "
+                  "python3 bench.py --steps 200 > gpurun_out/prof_bench.json")
+PROF_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{d} -o bench -- "
+                "python3 bench.py --steps 100 --no-cpu-baseline")
+PROF_SUM_CMD = ("python3 bench.py --summarize-profiles gpurun_out/prof_default gpurun_out/pmc_fetch "
+                "gpurun_out/pmc_write gpurun_out/prof_bench.json")
+SQ_ARGS = ("--only siso_prefill,mimo_prefill,siso_prefill_backward,mimo_prefill_backward "
+           "--no-cpu-baseline --prefill-steps 2")
+SQ_SETS = ("SQ_WAVES SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+           "SQ_INSTS_LDS SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
+           "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY "
+           "SQ_ACTIVE_INST_ANY SQ_INSTS_SALU")
+MFMA_BF16_FLOPS = 2 * 16 * 16 * 32   # one v_mfma_f32_16x16x32_bf16
+PREFILL_KERNELS = ("k_chunk_state", "k_state_pass", "k_chunk_output", "k_varlen_", "k_bwd_")
+
+
+def _prof_short(name):
+    """A kernel's template name without namespaces, return type and arguments."""
+    n = name.replace("(anonymous namespace)::", "").replace("m3::", "")
+    if n.endswith(")"):   # drop the argument list
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i]
+                break
+    return n.replace("void ", "").strip()
+
+
+def _prof_csv(d, suffix):
+    import csv
+    for root, _, files in sorted(os.walk(d)):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(root, f), newline="") as fh:
+                    return list(csv.DictReader(fh))
+    raise SystemExit(f"no *{suffix} under {d}")
+
+
+def _prof_grid(r):
+    if r.get("Grid_Size"):
+        return int(r["Grid_Size"])
+    return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+
+
+def _prof_calls(disp):
+    """(short name, grid, value) in dispatch order -> the prefill calls: a call
+    is a run of prefill kernels that ends at any other kernel or where its
+    first kernel (name and grid) comes again."""
+    calls, cur = [], None
+    for s, g, v in disp:
+        if not s.startswith(PREFILL_KERNELS):
+            if cur:
+                calls.append(cur)
+            cur = None
+            continue
+        if cur and (s, g) == cur[0][:2]:
+            calls.append(cur)
+            cur = None
+        if cur is None:
+            cur = []
+        cur.append((s, g, v))
+    if cur:
+        calls.append(cur)
+    return calls
+
+
+def _prof_flavour(sig):
+    """The bench workload a call's kernel sequence belongs to."""
+    import re
+    names = [s for s, _ in sig]
+    rank = 1
+    for n in names:
+        m = re.match(r"k_chunk_state<[^>]*, (\d+), (?:true|false)", n) or re.match(r"k_bwd_u<[^>]*, (\d+)>", n)
+        if m:
+            rank = int(m.group(1))
+    base = "mimo_prefill" if rank > 1 else "siso_prefill"
+    if any(n.startswith("k_bwd_") for n in names):
+        return base + "_backward"
+    if any(n.startswith("k_varlen") for n in names):
+        return base + "_varlen"
+    if any(n.startswith(("k_chunk_state", "k_chunk_output")) and ", true" in n for n in names):
+        return base + "_bcprep"
+    return base
+
+
+def _prof_call_means(disp):
+    """flavour -> (kernel signature, mean value per kernel position, calls)."""
+    calls = _prof_calls(disp)
+    sigs, per = [], {}
+    for c in calls:
+        sig = tuple((s, g) for s, g, _ in c)
+        if sig not in sigs:
+            sigs.append(sig)
+        per.setdefault(sigs.index(sig), []).append([v for _, _, v in c])
+    out = {}
+    for i, vals in per.items():
+        cols = list(zip(*vals))
+        out[_prof_flavour(sigs[i])] = (sigs[i], [sum(c) / len(c) for c in cols], len(vals))
+    return out
+
+
+def _prof_counter(d, counter):
+    rs = [r for r in _prof_csv(d, "counter_collection.csv") if r.get("Counter_Name", counter) == counter]
+    rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(_prof_short(r["Kernel_Name"]), _prof_grid(r), float(r["Counter_Value"]), r["Kernel_Name"])
+            for r in rs]
+
+
+def summarize_profiles(stats_dir, fetch_dir, write_dir, bench_json, out_dir):
+    """kernel_stats_default_bench.txt, hbm_counters_default_bench.txt and
+    hbm_counters.json from a --kernel-trace --stats run and a FETCH_SIZE and a
+    WRITE_SIZE run of the default bench."""
+    import re
+    fetch, write = _prof_counter(fetch_dir, "FETCH_SIZE"), _prof_counter(write_dir, "WRITE_SIZE")
+    with open(bench_json) as fh:
+        W = json.loads(fh.read().strip().splitlines()[-1])["workloads"]
+
+    def means(disp):
+        acc, full = {}, {}
+        for s, g, v, n in disp:
+            acc.setdefault((s, g), []).append(v)
+            full[(s, g)] = n
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}, full
+
+    fm, fullname = means(fetch)
+    wm, _ = means(write)
+    # calibration: the device copy of PROFILE_COPY_BYTES (its WRITE_SIZE nearest that size)
+    cw = min(((v, s, g) for s, g, v, _ in write if "copy" in s.lower()),
+             key=lambda t: abs(t[0] - PROFILE_COPY_BYTES / 1024))
+    cfv = [v for s, g, v, _ in fetch if (s, g) == (cw[1], cw[2])]
+    cf = sum(cfv) / len(cfv)
+    fs, wsc = PROFILE_COPY_BYTES / 1024 / cf, PROFILE_COPY_BYTES / 1024 / cw[0]
+
+    def hbm(key):
+        f, n = fm[key]
+        w = wm.get(key, (0.0, 0))[0]
+        return f * 1024 * fs + w * 1024 * wsc, f, w, n
+
+    fcm = _prof_call_means([(s, g, v) for s, g, v, _ in fetch])
+    wcm = _prof_call_means([(s, g, v) for s, g, v, _ in write])
+    call_bytes = {}
+    for kind, (sig, fv, ncalls) in fcm.items():
+        wsig, wv, _ = wcm[kind]
+        assert wsig == sig, kind
+        per_k = [(sig[i][0], fv[i], wv[i], fv[i] * 1024 * fs + wv[i] * 1024 * wsc) for i in range(len(sig))]
+        call_bytes[kind] = (sum(x[3] for x in per_k), sig, per_k, ncalls)
+
+    def is_m3(n):
+        return "m3::" in n
+
+    def bools(s):
+        return re.findall(r"\b(true|false)\b", s)
+
+    def match(prefix, pred=lambda s: True):
+        ks = [k for k in fm if k[0].startswith(prefix) and pred(k[0])]
+        return max(ks, key=lambda k: fm[k][1]) if ks else None   # several grids: the most dispatched
+
+    out = {"note": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), mean over dispatches of one "
+                   "kernel and grid, scaled by the factors a 268435456-byte device copy reads in the same run",
+           "fetch_scale": round(fs, 4), "write_scale": round(wsc, 4), "kernels": {}}
+    K = out["kernels"]
+    for key in sorted(fm):
+        if not is_m3(fullname[key]):
+            continue
+        b, f, w, n = hbm(key)
+        s = key[0]
+        src = (SRC_TOKENS if "_tok<" in s else SRC_DECODE if s.startswith("k_decode")
+               else SRC_BACKWARD if s.startswith("k_bwd") else SRC_PREFILL)
+        K[f"{fullname[key]} grid {key[1]}"] = dict(
+            kernel=fullname[key], grid=key[1], fetch_kib=round(f, 1), write_kib=round(w, 1), dispatches=n,
+            hbm_bytes_per_launch=round(b), sources=src, source_hash=source_hash(src))
+    last3 = lambda v: lambda s: bools(s)[-3:] == v
+    tags = {
+        "siso_decode": match("k_decode_siso<", last3(["true", "false", "false"])),
+        "mimo_decode": match("k_decode_mimo<", last3(["true", "false", "false"])),
+        "siso_decode_bcprep": match("k_decode_siso<", last3(["true", "true", "false"])),
+        "mimo_decode_bcprep": match("k_decode_mimo<", last3(["true", "true", "false"])),
+        "siso_decode_k4": match("k_decode_siso_tok<"),
+        "mimo_decode_k4": match("k_decode_mimo_tok<"),
+    }
+    for tag, key in tags.items():
+        if key is None:
+            continue
+        b, f, w, n = hbm(key)
+        base = tag.replace("_bcprep", "")
+        alg = (W.get(tag) or {}).get("algorithmic_bytes") or (W.get(base) or {}).get("algorithmic_bytes")
+        src = SRC_TOKENS if "k4" in tag else SRC_DECODE
+        K[tag] = dict(kernel=fullname[key], fetch_kib=round(f, 1), write_kib=round(w, 1), dispatches=n,
+                      hbm_bytes_per_launch=round(b), sources=src, source_hash=source_hash(src),
+                      algorithmic_bytes=alg, traffic_over_algorithmic=round(b / alg, 4) if alg else None)
+    for kind, (tot, sig, per_k, ncalls) in call_bytes.items():
+        base = kind.replace("_bcprep", "")
+        alg = (W.get(kind) or {}).get("algorithmic_bytes") or (W.get(base) or {}).get("algorithmic_bytes")
+        src = SRC_BACKWARD if "backward" in kind else SRC_PREFILL
+        K[kind] = dict(kernel="whole call: " + ", ".join(s for s, g in sig), hbm_bytes_per_launch=round(tot),
+                       algorithmic_bytes=alg, traffic_over_algorithmic=round(tot / alg, 4) if alg else None,
+                       sources=src, source_hash=source_hash(src), calls=ncalls,
+                       per_kernel=[dict(kernel=k_, fetch_kib=round(f_, 1), write_kib=round(w_, 1),
+                                        hbm_mb=round(b_ / 1e6, 1)) for k_, f_, w_, b_ in per_k])
+    with open(os.path.join(out_dir, "hbm_counters.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+
+    # kernel statistics and the prefill calls' kernel times (from the trace)
+    lines = sorted(((float(r["Percentage"]), _prof_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+                    for r in _prof_csv(stats_dir, "kernel_stats.csv")), reverse=True)
+    kt = ["# Kernel durations of the default bench run, rocprofv3 on MI355X (gfx950)", "#",
+          "# commands (from the repository root, after `export TMPDIR=/tmp`):",
+          f"#   {PROF_STATS_CMD}", f"#   {PROF_SUM_CMD}", "#",
+          f"# {'kernel':78s} {'calls':>7s} {'avg_us':>12s} {'min_us':>12s} {'max_us':>12s} {'pct':>8s}"]
+    for pct, name, calls, avg, mn, mx in lines:
+        kt.append(f"{name[:80]:80s} {calls:7d} {avg:12.2f} {mn:12.2f} {mx:12.2f} {pct:8.4g}")
+    tr = sorted(_prof_csv(stats_dir, "kernel_trace.csv"), key=lambda r: int(r.get("Dispatch_Id", 0) or 0))
+    tcm = _prof_call_means([(_prof_short(r["Kernel_Name"]), _prof_grid(r),
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in tr])
+    kt += ["", "# per call: each prefill flavour's calls, kernel by kernel in dispatch order (mean over calls)"]
+    for kind, (sig, tv, ncalls) in tcm.items():
+        parts = " + ".join(f"{s.split('<')[0]} {t:.1f}" for (s, _), t in zip(sig, tv))
+        kt.append(f"{kind:24s} {ncalls:3d} calls  {sum(tv):9.1f} us per call = {parts}")
+    with open(os.path.join(out_dir, "kernel_stats_default_bench.txt"), "w") as fh:
+        fh.write("\n".join(kt) + "\n")
+
+    ht = ["# HBM traffic per dispatch from rocprofv3 hardware counters, MI355X (gfx950)", "#",
+          "# commands (from the repository root, after `export TMPDIR=/tmp`), one counter per run:",
+          "#   " + PROF_PMC_CMD.format(c="FETCH_SIZE", d="fetch"),
+          "#   " + PROF_PMC_CMD.format(c="WRITE_SIZE", d="write"),
+          f"#   {PROF_SUM_CMD}",
+          "# sources: gpurun_out/pmc_{fetch,write}/bench_counter_collection.csv (KiB per dispatch)", "#",
+          f"# calibration: the same runs copy a {PROFILE_COPY_BYTES:,}-byte buffer (torch copy_, {cw[1]});",
+          f"#   that copy reads FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw[0]:.1f} KiB, so FETCH_SIZE is scaled by",
+          f"#   {fs:.4f} and WRITE_SIZE by {wsc:.4f} to give bytes moved to or from HBM.",
+          "# FETCH_SIZE counts L2 misses, whether the last-level cache (MALL) or HBM serves them: equal",
+          "#   counts for a step on one state and on two alternating states say nothing about where they hit.",
+          "#",
+          f"# per kernel{'':60s} {'grid':>10s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'HBM_MB':>10s} {'disp':>6s}"]
+    for key in sorted(fm):
+        if is_m3(fullname[key]):
+            b, f, w, n = hbm(key)
+            ht.append(f"{key[0][:70]:70s} {key[1]:10d} {f:12.1f} {w:12.1f} {b / 1e6:10.1f} {n:6d}")
+    ht.append("")
+    for kind, (tot, sig, per_k, ncalls) in call_bytes.items():
+        ht.append(f"{kind} ({ncalls} calls): " + " + ".join(f"{k_.split('<')[0]} {b_ / 1e6:.1f}"
+                                                           for k_, _, _, b_ in per_k) + f" = {tot / 1e6:.1f} MB")
+    ht.append("")
+    for tag in list(tags) + list(call_bytes):
+        e = K.get(tag)
+        if e:
+            r, alg = e.get("traffic_over_algorithmic"), e.get("algorithmic_bytes")
+            extra = "" if r is None else f"  ({r:.4f}x the algorithmic {alg / 1e6:.1f} MB)"
+            ht.append(f"{tag:26s} {e['hbm_bytes_per_launch'] / 1e6:10.1f} MB per launch{extra}")
+    ht += ["",
+           "# per-call lines: each prefill flavour's calls, kernel by kernel in dispatch order (mean over calls)",
+           "# algorithmic bytes (each input read once, outputs written once, the state read and written once):",
+           "#   from the bench run's workloads; prefill kernels also carry the chunk-state workspace traffic",
+           "#   (written by k_chunk_state, read and rewritten by k_state_pass, read by k_chunk_output) and",
+           "#   k_chunk_state re-reads x, B and theta."]
+    with open(os.path.join(out_dir, "hbm_counters_default_bench.txt"), "w") as fh:
+        fh.write("\n".join(ht) + "\n")
+
+
+def summarize_sq(sq1_dir, sq2_dir, out_dir):
+    """mfma_valu_prefill_backward.txt from two SQ counter runs of the prefill
+    and backward workloads."""
+    def counters(d):
+        acc = {}
+        for r in _prof_csv(d, "counter_collection.csv"):
+            n = _prof_short(r["Kernel_Name"])
+            if n.startswith("k_"):
+                acc.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in acc.items()}
+
+    c1, c2 = counters(sq1_dir), counters(sq2_dir)
+    times = {}
+    for r in _prof_csv(sq1_dir, "kernel_trace.csv"):
+        times.setdefault(_prof_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = []
+    for n, c in c1.items():
+        t = sum(times[n]) / len(times[n]) if times.get(n) else float("nan")
+        mf, va, lds = c.get("SQ_INSTS_MFMA", 0.0), c.get("SQ_INSTS_VALU", 0.0), c.get("SQ_INSTS_LDS", 0.0)
+        mfma_ms = mf * MFMA_BF16_FLOPS / (MFMA_PEAK_TFLOPS * 1e12) * 1e3
+        valu_ms = va * 4 / (1024 * 2.4e9) * 1e3
+        conf = c2.get(n, {}).get("SQ_LDS_BANK_CONFLICT", float("nan"))
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        rows.append((t, n, mf, mfma_ms, mfma_ms / (t / 1e3) if t == t else 0.0, va, valu_ms,
+                     valu_ms / (t / 1e3) if t == t else 0.0, conf / lds if lds else 0.0, busy / mf if mf else 0.0))
+    rows.sort(reverse=True)
+    cmd = "rocprofv3 {k}--pmc {s} -f csv -d gpurun_out/pmcM{i} -o run -- python3 bench.py " + SQ_ARGS
+    txt = ["# Matrix-core (MFMA) and VALU use of the prefill and backward kernels, MI355X (gfx950)", "#",
+           "# commands (from the repository root, after `export TMPDIR=/tmp`), one counter set per run:",
+           "#   " + cmd.format(k="--kernel-trace ", s=SQ_SETS[0], i=1), "#   " + cmd.format(k="", s=SQ_SETS[1], i=2),
+           "#   python3 bench.py --summarize-sq gpurun_out/pmcM1 gpurun_out/pmcM2",
+           "# per dispatch, mean over the dispatches of the run; time_us = the kernel-trace durations of the",
+           "#   first run (kernels serialised by the counter collection).", "#",
+           f"# mfma_ms: the executed MFMA work (SQ_INSTS_MFMA x {MFMA_BF16_FLOPS} flops for "
+           "v_mfma_f32_16x16x32_bf16, i.e.",
+           "#   16 x 16 x 32 multiply-adds at 2 flops each, hi/lo operand splits included) at the dense bf16",
+           "#   peak of 2.5 PFLOP/s; mfma_use = mfma_ms / time.",
+           "#   SQ_VALU_MFMA_BUSY_CYCLES reads 16 per such instruction in every kernel (busy/mfma).",
+           "# valu_ms: SQ_INSTS_VALU at one wave64 instruction per 4 cycles per SIMD (1024 SIMDs, 2.4 GHz);",
+           "#   valu_use = valu_ms / time.  The two pipes run side by side (different waves), so the uses do",
+           "#   not add up.",
+           "# lds_conf: SQ_LDS_BANK_CONFLICT cycles per LDS instruction.",
+           "# k_chunk_state and k_state_pass at a single input appear at both chunk lengths (the forward at 128",
+           "#   tokens, the backward's recomputed states at 64); rows of one name and template are merged.", "",
+           f"{'kernel':70s} {'time_us':>8s} {'MFMA_inst':>10s} {'mfma_ms':>8s} {'mfma_use':>8s} {'VALU_inst':>10s} "
+           f"{'valu_ms':>8s} {'valu_use':>8s} {'lds_conf':>8s} {'busy/mfma':>9s}"]
+    for t, n, mf, mms, mu, va, vms, vu, lc, bpm in rows:
+        txt.append(f"{n[:70]:70s} {t:8.1f} {mf:10.3g} {mms:8.3f} {mu:8.3f} {va:10.4g} {vms:8.3f} {vu:8.3f} "
+                   f"{lc:8.3f} {bpm:9.1f}")
+    with open(os.path.join(out_dir, "mfma_valu_prefill_backward.txt"), "w") as fh:
+        fh.write("\n".join(txt) + "\n")
+
+
+# ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,7 +877,19 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of workloads to run (default all)")
+    ap.add_argument("--summarize-profiles", nargs=4, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                    help="write the rocprofv3 summaries under profiles/ from a profiled run's CSV files and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ1_DIR", "SQ2_DIR"),
+                    help="write the MFMA/VALU summary under profiles/ from two SQ counter runs and exit")
+    ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"),
+                    help="directory the summaries go to (default: profiles/)")
     a = ap.parse_args()
+    if a.summarize_profiles or a.summarize_sq:   # no GPU needed
+        if a.summarize_profiles:
+            summarize_profiles(*a.summarize_profiles, a.profiles_out)
+        if a.summarize_sq:
+            summarize_sq(*a.summarize_sq, a.profiles_out)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode and prefill kernels run on a "
               "single MI355X; multi-GPU runs are not part of this library.", file=sys.stderr)
