@@ -293,7 +293,7 @@ def bench_decode_tokens(name, K, calls, warmup=3, pool_n=4):
                 tokens_per_s=round(w.batch * K / (call_ms * 1e-3), 1), algorithmic_bytes=nbytes,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=round(gbs / HBM_PEAK_GBS, 4), traffic=counters_for(f"{name}_k{K}"),
-                              kernel=f"k_decode_{'siso' if w.rank == 1 else 'mimo'}_tok",
+                              kernel="k_decode_siso_tok" if w.rank == 1 else "k_decode_mimo_grp",
                               timing=f"HIP events around a graph of {calls} calls"))
 
 
@@ -720,7 +720,7 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, bench_json, out_dir):
             continue
         b, f, w, n = hbm(key)
         s = key[0]
-        src = (SRC_TOKENS if "_tok<" in s else SRC_DECODE if s.startswith("k_decode")
+        src = (SRC_TOKENS if "_tok<" in s or "_grp<" in s else SRC_DECODE if s.startswith("k_decode")
                else SRC_BACKWARD if s.startswith("k_bwd") else SRC_PREFILL)
         K[f"{fullname[key]} grid {key[1]}"] = dict(
             kernel=fullname[key], grid=key[1], fetch_kib=round(f, 1), write_kib=round(w, 1), dispatches=n,
@@ -732,7 +732,7 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, bench_json, out_dir):
         "siso_decode_bcprep": match("k_decode_siso<", last3(["true", "true", "false"])),
         "mimo_decode_bcprep": match("k_decode_mimo<", last3(["true", "true", "false"])),
         "siso_decode_k4": match("k_decode_siso_tok<"),
-        "mimo_decode_k4": match("k_decode_mimo_tok<"),
+        "mimo_decode_k4": match("k_decode_mimo_grp<"),
     }
     for tag, key in tags.items():
         if key is None:

@@ -14,11 +14,17 @@
 //    (a state row over N/4 lanes, 4 consecutive columns per lane); a block
 //    holds up to 8 rows per lane for all K tokens, and a unit with more rows
 //    is split over several blocks.
-//  * k_decode_mimo_tok (R > 1): one 16-row block of the state per wave,
-//    P <= 64, in the MFMA D layout (the rank-R terms are MFMA products with
-//    K = R, as in the single-step kernel), loaded in that layout and stored
-//    through a per-wave LDS transpose (whole lines per store); the token
-//    tables of a group of tokens are built once per block.
+//  * k_decode_mimo_grp (R = 4): the group form.  Over a group of four
+//    tokens the recurrence unrolls into the chunked form of the prefill, so
+//    the state is decayed and rotated once per group and its products (the
+//    group's outputs, its rank-4 terms) are MFMA contractions with the
+//    state's own registers as operands.
+//  * k_decode_mimo_tok (R = 2, 3, 8): token after token.  One 16-row block
+//    of the state per wave, P <= 64, in the MFMA D layout (the rank-R terms
+//    are MFMA products with K = R, as in the single-step kernel), loaded in
+//    that layout and stored through a per-wave LDS transpose (whole lines
+//    per store); the token tables of a group of tokens are built once per
+//    block.  Both MIMO kernels store the state that way.
 #include "m3_device.h"
 #include "m3_launch.h"
 
@@ -365,7 +371,10 @@ struct MGroupLoad {
   bool b0_zero;   // row 0 is the call's first token's B_{-1} and there is none
   template <bool PREV>
   __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k0) {
-    const int tid = threadIdx.x;
+    load<PREV>(a, bh, k0, threadIdx.x);
+  }
+  template <bool PREV>
+  __device__ __forceinline__ void load(const DecodeArgs& a, int bh, int k0, int tid) {
     const int klast = a.K - 1;
     const TI* Bt = static_cast<const TI*>(a.Bt);
     const TI* Ct = static_cast<const TI*>(a.Ct);
@@ -434,6 +443,42 @@ struct MGroupLoad {
       G.ga[tid] = ll * dd;
     }
   }
+
+  // for the group form (R a multiple of 4): the raw rows as loaded (row 0
+  // zeroed when there is no B_{-1}), the phase of every (token, pair) and
+  // the token scalars
+  template <int SB, int SC>
+  __device__ __forceinline__ void store_raw(const DecodeArgs& a, float (*b)[SB], float (*c)[SC],
+                                            float (*ph)[N / 2], float* d_, float* l_, float* A_,
+                                            int tid) const {
+    static_assert(R % 4 == 0 && SB % 4 == 0 && SC % 4 == 0, "rows of whole 16-byte pieces");
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NV) {
+        float e[8];
+        bc[i].get(e, !(b0_zero && v < VR));
+        float* row = v < NB ? b[v / VR] : c[(v - NB) / VR];
+        const int e0 = 8 * (v % VR);
+        *reinterpret_cast<f4*>(row + e0) = f4{e[0], e[1], e[2], e[3]};
+        *reinterpret_cast<f4*>(row + e0 + 4) = f4{e[4], e[5], e[6], e[7]};
+      }
+    }
+    const bool ang = (a.flags & kThetaIsAngle) != 0;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NA) {
+        const float th_ = th[i].f();
+        ph[e / (N / 2)][e % (N / 2)] = ang ? th_ : dth[i].f() * th_;
+      }
+    }
+    if (tid < kTokGroup) {
+      d_[tid] = d.f();
+      l_[tid] = l.f();
+      A_[tid] = A;
+    }
+  }
 };
 
 // The B/C preparation of a group's tables in place: the inverse RMS of
@@ -441,9 +486,11 @@ struct MGroupLoad {
 // adding its entries n = lane, lane + 4, ... in order, then two xor steps:
 // a fixed order), then x * inv * w[n] + bias[n][r].  Barriers between the
 // passes; the caller's barrier ends the last.
-template <int N, int R>
-__device__ __forceinline__ void mgroup_prep(const BCPrep& bc, MGroup<N, R>& G, float (*inv)[R],
-                                            const float (*pw)[N], const float (*pb)[N * R]) {
+// (b: the B rows 0..KG, c: the C rows; rows of any stride, entry n * RP + r)
+template <int N, int R, int SB, int SC>
+__device__ __forceinline__ void mgroup_prep(const BCPrep& bc, float (*b)[SB], float (*c)[SC],
+                                            float (*inv)[R], const float (*pw)[N],
+                                            const float (*pb)[N * R]) {
   constexpr int RP = MGroup<N, R>::RP;
   constexpr int ROWS = 2 * kTokGroup + 1;   // B rows 0..KG, then C rows
   constexpr int NC = ROWS * R;
@@ -453,7 +500,7 @@ __device__ __forceinline__ void mgroup_prep(const BCPrep& bc, MGroup<N, R>& G, f
     const int cc = c0 + tid / 4;
     const int col = min(cc, NC - 1);
     const int row = col / R, r = col % R;
-    const float* src = row <= kTokGroup ? G.b[row] : G.c[row - kTokGroup - 1];
+    const float* src = row <= kTokGroup ? b[row] : c[row - kTokGroup - 1];
     float s = 0.0f;
     for (int n = tid % 4; n < N; n += 4) {
       const float v = src[n * RP + r];
@@ -467,7 +514,7 @@ __device__ __forceinline__ void mgroup_prep(const BCPrep& bc, MGroup<N, R>& G, f
   for (int i = tid; i < ROWS * N * R; i += 256) {
     const int row = i / (N * R), j = i % (N * R), n = j / R, r = j % R;
     const bool isb = row <= kTokGroup;
-    float* dst = isb ? &G.b[row][n * RP + r] : &G.c[row - kTokGroup - 1][n * RP + r];
+    float* dst = isb ? &b[row][n * RP + r] : &c[row - kTokGroup - 1][n * RP + r];
     *dst = *dst * inv[row][r] * pw[isb ? 0 : 1][n] + pb[isb ? 0 : 1][j];
   }
 }
@@ -576,7 +623,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_M
     }
   }
   gl.store(a, G);
-  if constexpr (PREP) mgroup_prep<N, R>(a.bc, G, inv_sh, pw_sh, pb_sh);
+  if constexpr (PREP) mgroup_prep<N, R>(a.bc, G.b, G.c, inv_sh, pw_sh, pb_sh);
   __syncthreads();
 
   // lane bases of the LDS operands: A-operand row i16 is state column
@@ -648,7 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_M
     if (more) {   // every wave is past the group's tokens before its tables change
       __syncthreads();
       gl.store(a, G);
-      if constexpr (PREP) mgroup_prep<N, R>(a.bc, G, inv_sh, pw_sh, pb_sh);
+      if constexpr (PREP) mgroup_prep<N, R>(a.bc, G.b, G.c, inv_sh, pw_sh, pb_sh);
       __syncthreads();
 #pragma unroll
       for (int j = 0; j <= kTokGroup; ++j)
@@ -686,6 +733,327 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_M
 }
 
 // --------------------------------------------------------------------------
+// Rank 4 in group form.  Unrolling the recurrence over a group of KG tokens
+// (local tokens 1..KG; local token 0 is the one before the group) gives, with
+// the cumulative log-decay cs_j = sum_{i<=j} dt_i A_i and the cumulative phase
+// Phi_j = sum_{i<=j} phi_i of every pair (cs_0 = Phi_0 = 0),
+//   y_j = e^{cs_j} h_0 Ct_j + sum_{u=0..j} e^{cs_j - cs_u} w_{j,u} X_u (Bt_u^T Ct_j),
+//   h_K = rot(e^{cs_K} h_0 + sum_{u=0..K} e^{cs_K - cs_u} w_{K,u} X_u Bt_u^T, Phi_K),
+// where Bt_u and Ct_j are B_u and C_j with every pair rotated by -Phi_u and
+// -Phi_j, w_{j,0} = (1 - lam_1) dt_1 (the left-endpoint term of the group's
+// first token) and w_{j,u} = lam_u dt_u + [u < j] (1 - lam_{u+1}) dt_{u+1}:
+// the chunked form of the prefill, with a chunk of KG tokens [xxxxx.co.kr,
+// sections 1.1-1.3].  So the state is rotated and decayed once per group, and
+// its products are MFMA contractions with the state's own registers as
+// operands:
+//  * the group's outputs: the 16 x 16 block (rows p, columns (token, rank))
+//    of h_0 times the rotated C columns, K = N (v_mfma_f32_16x16x4f32 with
+//    the state's D-layout registers as the A operand), then the columns
+//    scaled by e^{cs_j} and the terms inside the group added as one more
+//    product, X (the lane's own x values) times the masked Gram of the
+//    group's rotated B and C rows (computed once per block on the MFMA, the
+//    four waves taking a quarter of N each);
+//  * the state update: the rank-4 terms of all KG + 1 tokens as MFMA
+//    products with K = 4 (KG + 1), then one rotation by Phi_K.
+// The token work per group is about a third of the token-by-token kernel's,
+// which lets it hide under the state stream.
+constexpr double kTwoPiD = 6.283185307179586476925286766559;
+
+template <int N>
+struct alignas(16) GTab {
+  static constexpr int R = 4, NE = N * R;
+  static constexpr int SB = NE + 16;   // B row stride: the Gram's four rows start in different banks
+  static constexpr int SCT = N + 4;    // row stride of the transposed C
+  float b[kTokGroup + 1][SB];          // B rows of local tokens 0..KG, [n][s]: raw, then rotated
+  union {
+    float c[kTokGroup][NE];            // raw C rows [n][r]
+    float gp[4][32][16];               // the four waves' Gram partials
+  } u;
+  float ct[kTokGroup * R][SCT];        // rotated C, transposed: [(j - 1) R + r][n]
+  float ph[kTokGroup][N / 2];          // phase of each token and pair
+  f2 cph[kTokGroup + 1][N / 2];        // (cos, sin) of Phi_j, j = 0..KG
+  float gm[(kTokGroup + 1) * R][16];   // masked Gram [(u, s)][(j - 1, r)]
+  float msk[kTokGroup][kTokGroup + 1]; // e^{cs_j - cs_u} w_{j,u}, zero where u > j
+  float ecs[kTokGroup * R];            // e^{cs_j} of each output column
+  float coef[kTokGroup + 1];           // e^{cs_K - cs_u} w_{K,u}
+  float ecsK;
+  float d[kTokGroup], l[kTokGroup], A[kTokGroup];
+};
+
+#ifndef M3_GRP_WAVES
+#define M3_GRP_WAVES 5
+#endif
+
+template <typename TI, typename TO, int N, bool PREV, bool PREP, bool ONEG>
+// (one group: five waves per SIMD, 32 KB of LDS at N = 128 and at most 96
+// registers; four with the B/C preparation's tables or with several groups,
+// whose loop needs a few more registers)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG && !PREP ? M3_GRP_WAVES : 4))) void k_decode_mimo_grp(DecodeArgs a) {
+  constexpr int R = 4, KG = kTokGroup, NT = N / 16, NE = N * R;
+  using TB = GTab<N>;
+  constexpr int NHALF = NT >= 2 ? 2 : 1;
+  constexpr int HC = N / NHALF;       // columns per transposed piece of the final store
+  __shared__ union {
+    TB t;
+    f4 tr[4][16][HC / 4 + 1];
+  } sm;
+  TB& T = sm.t;
+  __shared__ float pw_sh[PREP ? 2 : 1][PREP ? N : 1];
+  __shared__ float pb_sh[PREP ? 2 : 1][PREP ? NE : 1];
+  __shared__ float inv_sh[PREP ? 2 * KG + 1 : 1][R];
+
+  const int bh = blockIdx.x;
+  const int P = a.P;
+  const bool rows = (int)(threadIdx.x >> 6) * 16 < P;   // this wave's 16-row block exists
+  float* __restrict__ hb = a.h + (int64_t)bh * P * N;
+  const TI* __restrict__ X = static_cast<const TI*>(a.x);
+  TO* __restrict__ Y = static_cast<TO*>(a.y);
+  const int ngrp = ONEG ? 1 : (a.K + KG - 1) / KG;
+
+  // x of row prow (a valid row for every lane's reads) and rank g for local
+  // tokens 0..KG, as loaded
+  auto load_x = [&](int k0, Raw1<TI>* xr, int prow, int g) {
+#pragma unroll
+    for (int j = 0; j <= KG; ++j) {
+      const int k = k0 - 1 + j;
+      const TI* src = (k < 0 && PREV) ? static_cast<const TI*>(a.xp) + (int64_t)bh * P * R
+                                      : X + tok_head(a, bh, min(max(k, 0), a.K - 1)) * P * R;
+      xr[j].load(src, (int64_t)prow * R + g);
+    }
+  };
+
+  f4 v[NT];   // this wave's 16 rows of the state, in the MFMA D layout
+  for (int gi = 0; gi < ngrp; ++gi) {
+    const int k0 = gi * KG;
+    const bool more = !ONEG && gi + 1 < ngrp;   // block-uniform
+    const int ke = min(KG, a.K - k0);           // tokens in this group
+    // the thread index, opaque to the compiler once per group: the group's
+    // addresses are then formed inside the loop instead of being hoisted out
+    // of it and held in registers across all groups
+    int tid = threadIdx.x;
+    if constexpr (!ONEG) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, i16 = lane & 15, g = lane >> 4;
+    const int prow = rows ? wave * 16 + i16 : 0;
+
+    // the group's inputs: a later group's after the previous group's last
+    // barrier (held in flight across a group they would cost the registers
+    // of a fifth wave per SIMD, and the other resident blocks cover the
+    // wait); at the first group they go out ahead of the state
+    MGroupLoad<TI, N, R> gl;
+    gl.template load<PREV>(a, bh, k0, tid);
+    Raw1<TI> xr[KG + 1];
+    load_x(k0, xr, prow, g);
+    if (gi == 0) {
+      float wv[PREP ? 4 : 1][PREP ? (NE + 255) / 256 : 1];
+      if constexpr (PREP) {   // weights and this head's biases (1 and 0 when absent)
+        const int64_t hb0 = (int64_t)(bh % a.H) * NE;
+#pragma unroll
+        for (int q = 0; q < (NE + 255) / 256; ++q) {
+          const int i = min(tid + 256 * q, NE - 1);
+          wv[0][q] = ld_or(a.bc.Bw, min(i, N - 1), 1.0f);
+          wv[1][q] = ld_or(a.bc.Cw, min(i, N - 1), 1.0f);
+          wv[2][q] = ld_or(a.bc.Bb, hb0 + i, 0.0f);
+          wv[3][q] = ld_or(a.bc.Cb, hb0 + i, 0.0f);
+        }
+      }
+      asm volatile("" ::: "memory");   // the token-side reads stay ahead of the state stream
+#pragma unroll
+      for (int t = 0; t < NT; ++t) v[t] = ld4_state(hb + (int64_t)prow * N + 16 * t + 4 * g);
+      if constexpr (PREP) {
+#pragma unroll
+        for (int q = 0; q < (NE + 255) / 256; ++q) {
+          const int i = tid + 256 * q;
+          if (i < N) {
+            pw_sh[0][i] = wv[0][q];
+            pw_sh[1][i] = wv[1][q];
+          }
+          if (i < NE) {
+            pb_sh[0][i] = wv[2][q];
+            pb_sh[1][i] = wv[3][q];
+          }
+        }
+      }
+    }
+
+    // (1) raw rows, phases and scalars (B/C preparation in place)
+    gl.store_raw(a, T.b, T.u.c, T.ph, T.d, T.l, T.A, tid);
+    if constexpr (PREP) mgroup_prep<N, R>(a.bc, T.b, T.u.c, inv_sh, pw_sh, pb_sh);
+    __syncthreads();
+
+    // (2) cumulative phases (double sums, reduced in turns) and the
+    // decay/weight tables
+    if (tid < N / 2) {
+      double run = 0.0;
+      T.cph[0][tid] = f2{1.0f, 0.0f};
+#pragma unroll
+      for (int j = 1; j <= KG; ++j) {
+        run += (double)T.ph[j - 1][tid];
+        double tu = run * (1.0 / kTwoPiD);
+        tu -= rint(tu);
+        const float tf = (float)tu;
+        T.cph[j][tid] = f2{__builtin_amdgcn_cosf(tf), __builtin_amdgcn_sinf(tf)};
+      }
+    } else if (tid >= 64 && tid < 64 + KG * (KG + 1) + (KG + 1) + 1 + KG) {
+      const int e = tid - 64;
+      // log-decay of local tokens u+1..j and the weight w_{j,u}
+      auto seg = [&](int u, int j) {
+        float s = 0.0f;
+        for (int i = u + 1; i <= j; ++i) s += T.d[i - 1] * T.A[i - 1];
+        return s;
+      };
+      auto wgt = [&](int j, int u) {
+        if (u == 0) return (1.0f - T.l[0]) * T.d[0];
+        const float gam = T.l[u - 1] * T.d[u - 1];
+        return u < j ? gam + (1.0f - T.l[u]) * T.d[u] : gam;
+      };
+      if (e < KG * (KG + 1)) {
+        const int j = e / (KG + 1) + 1, u = e % (KG + 1);
+        T.msk[j - 1][u] = (u <= j && j <= ke) ? expf(seg(u, j)) * wgt(j, u) : 0.0f;
+      } else if (e < KG * (KG + 1) + KG + 1) {
+        const int u = e - KG * (KG + 1);
+        T.coef[u] = u <= ke ? expf(seg(u, ke)) * wgt(ke, u) : 0.0f;
+      } else if (e == KG * (KG + 1) + KG + 1) {
+        T.ecsK = expf(seg(0, ke));
+      } else {
+        const int j = e - (KG * (KG + 1) + KG + 1);   // 1..KG
+        const float ec = expf(seg(0, j));
+#pragma unroll
+        for (int r = 0; r < R; ++r) T.ecs[(j - 1) * R + r] = ec;
+      }
+    }
+    __syncthreads();
+
+    // (3) B rows of tokens 1..KG rotated by -Phi_u in place; C rows rotated
+    // by -Phi_j into the transposed table.  One item is one pair of one
+    // token: its two columns for the four ranks.
+    for (int it = tid; it < 2 * KG * (N / 2); it += 256) {
+      const bool isb = it < KG * (N / 2);
+      const int jt = (isb ? it : it - KG * (N / 2)) / (N / 2) + 1;
+      const int k = it % (N / 2);
+      const f2 cs = T.cph[jt][k];   // rotation by -Phi: (cos, -sin)
+      const float* src = isb ? &T.b[jt][8 * k] : &T.u.c[jt - 1][8 * k];
+      const f4 c0 = *reinterpret_cast<const f4*>(src);       // column 2k, ranks 0..3
+      const f4 c1 = *reinterpret_cast<const f4*>(src + 4);   // column 2k + 1
+      f4 o0, o1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        o0[r] = cs.x * c0[r] + cs.y * c1[r];
+        o1[r] = -cs.y * c0[r] + cs.x * c1[r];
+      }
+      if (isb) {
+        *reinterpret_cast<f4*>(&T.b[jt][8 * k]) = o0;
+        *reinterpret_cast<f4*>(&T.b[jt][8 * k + 4]) = o1;
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          *reinterpret_cast<f2*>(&T.ct[(jt - 1) * R + r][2 * k]) = f2{o0[r], o1[r]};
+      }
+    }
+    __syncthreads();
+
+    // (4) Gram partials: rows (u, s) of Bt (tile 0: u = 0..3, tile 1: u = 4),
+    // columns (j, r) of Ct; wave w sums n over [w N/4, (w + 1) N/4)
+    {
+      f4 d0 = f4{0, 0, 0, 0}, d1 = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < N / 16; ++q) {
+        const int n = wave * (N / 4) + 4 * q + g;
+        const float a0 = T.b[i16 / 4][n * R + i16 % 4];
+        const float a1 = i16 < 4 ? T.b[KG][n * R + i16] : 0.0f;
+        const float bv = T.ct[i16][n];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, d1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        T.u.gp[wave][4 * g + jj][i16] = d0[jj];
+        T.u.gp[wave][16 + 4 * g + jj][i16] = d1[jj];
+      }
+    }
+    __syncthreads();
+    // (5) the sum over the waves, masked: gm[(u, s)][(j - 1, r)]
+    for (int e = tid; e < (KG + 1) * R * 16; e += 256) {
+      const int row = e / 16, col = e % 16;
+      const float s = T.u.gp[0][row][col] + T.u.gp[1][row][col] + T.u.gp[2][row][col] +
+                      T.u.gp[3][row][col];
+      T.gm[row][col] = row / R <= col / R + 1 ? s * T.msk[col / R][row / R] : 0.0f;
+    }
+    __syncthreads();
+
+    // (6) this wave's 16 rows: the group's outputs and the state update
+    if (rows) {   // wave-uniform
+      float xs[KG + 1], xc[KG + 1];
+#pragma unroll
+      for (int u = 0; u <= KG; ++u) {
+        xs[u] = (PREV || k0 + u > 0) ? xr[u].f() : 0.0f;
+        xc[u] = T.coef[u] * xs[u];
+      }
+      const float ecsK = T.ecsK;
+      f4 yacc = f4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // h_0 against the rotated C columns: k = g is column 16t + 4g + i
+        const f4 cv = *reinterpret_cast<const f4*>(&T.ct[i16][16 * t + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yacc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[t][i], cv[i], yacc, 0, 0, 0);
+        // e^{cs_K} h_0 plus the group's rank-4 terms, then the rotation by Phi_K
+        f4 acc = ecsK * v[t];
+#pragma unroll
+        for (int u = 0; u <= KG; ++u)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(T.b[u][(16 * t + i16) * R + g], xc[u], acc, 0, 0, 0);
+        const f4 c2 = *reinterpret_cast<const f4*>(&T.cph[ke][8 * t + 2 * g]);
+        v[t] = rot2pairs(acc, f2{c2.x, c2.y}, f2{c2.z, c2.w});
+        __builtin_amdgcn_sched_barrier(0);   // one tile's operands at a time
+      }
+      // columns scaled by e^{cs_j}, then the terms inside the group, one
+      // product per token u, added only to the columns of tokens j >= u (so
+      // that a NaN in a later token's x never reaches an earlier token's y)
+      yacc = yacc * T.ecs[i16];
+#pragma unroll
+      for (int u = 0; u <= KG; ++u) {
+        const f4 tu = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[u], T.gm[u * R + g][i16], f4{0, 0, 0, 0}, 0, 0, 0);
+        if (u <= i16 / R + 1) yacc = yacc + tu;
+      }
+      // lane: rows 16 wave + 4g + jj, column i16 = (token i16 / 4, rank i16 % 4)
+      if (i16 / R < ke) {
+        TO* __restrict__ yk = Y + tok_head(a, bh, k0 + i16 / R) * P * R;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int pp = wave * 16 + 4 * g + jj;
+          if (pp < P) st1(yk, (int64_t)pp * R + i16 % R, yacc[jj]);
+        }
+      }
+    }
+    if (more) __syncthreads();   // every wave is past the group's tables before they change
+  }
+
+  // the wave's rows back to HBM through LDS, row-contiguous (whole lines per
+  // store instruction)
+  __syncthreads();   // every wave is past the last group's tables
+  if (rows) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, i16 = lane & 15, g = lane >> 4;
+    constexpr int V4 = HC / 4, LV = 16 * V4 / 64, TH = NT / NHALF;
+#pragma unroll
+    for (int hf = 0; hf < NHALF; ++hf) {
+#pragma unroll
+      for (int t = 0; t < TH; ++t) sm.tr[wave][i16][(16 * t + 4 * g) / 4] = v[hf * TH + t];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < LV; ++j) {
+        const int q = lane + 64 * j;
+        st4_stream(hb + (int64_t)(wave * 16 + q / V4) * N + hf * HC + 4 * (q % V4),
+                   sm.tr[wave][q / V4][q % V4]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 namespace {
 
 template <typename TI, typename TO, int N, int UNR>
@@ -702,6 +1070,24 @@ hipError_t launch_siso_tok(const DecodeArgs& a, int units, hipStream_t s) {
   } else {
     if (a.has_prev) hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, true, false>), g, b, 0, s, a);
     else hipLaunchKernelGGL((k_decode_siso_tok<TI, TO, N, UNR, false, false>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// rank 4: the group form (one group of tokens, or several)
+template <typename TI, typename TO, int N>
+hipError_t launch_mimo_grp(const DecodeArgs& a, int units, hipStream_t s) {
+  const dim3 g(units), b(256);
+  const bool one = a.K <= kTokGroup;
+  if (a.bc.on) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, true, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, false, true, false>), g, b, 0, s, a);
+  } else if (one) {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, true, false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, false, false, true>), g, b, 0, s, a);
+  } else {
+    if (a.has_prev) hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, true, false, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mimo_grp<TI, TO, N, false, false, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -758,7 +1144,7 @@ int dispatch_tok(const DecodeArgs& a, int units, hipStream_t s, hipError_t* err)
     switch (a.R) {                                                          \
       case 2: *err = launch_mimo_tok<TI, TO, NN, 2>(a, units, s); return 0; \
       case 3: *err = launch_mimo_tok<TI, TO, NN, 3>(a, units, s); return 0; \
-      case 4: *err = launch_mimo_tok<TI, TO, NN, 4>(a, units, s); return 0; \
+      case 4: *err = launch_mimo_grp<TI, TO, NN>(a, units, s); return 0;    \
       case 8: *err = launch_mimo_tok<TI, TO, NN, 8>(a, units, s); return 0; \
       default: return -1;                                                   \
     }

@@ -71,6 +71,7 @@ def test_tokens_bf16(K, R):
     (64, 128, 1, "f32"), (32, 256, 1, "bf16"), (40, 64, 1, "bf16"), (32, 64, 2, "bf16"),
     (16, 32, 8, "bf16"), (48, 16, 3, "f32"), (64, 128, 4, "f32"),
     (80, 128, 1, "bf16"), (48, 256, 1, "f32"),   # rows of a unit split over blocks
+    (16, 16, 4, "f32"), (48, 32, 4, "bf16"), (32, 64, 4, "f32"),   # rank 4: waves without rows
 ])
 def test_tokens_shapes(P, N, R, dt):
     w = I.Workload("t", 96, 2, 5, 3, P, N, R, 64, dt)
@@ -81,6 +82,7 @@ def test_tokens_shapes(P, N, R, dt):
 @pytest.mark.parametrize("P,N,R,dt", [
     (64, 64, 4, "bf16"), (32, 64, 2, "bf16"), (48, 16, 3, "f32"), (64, 128, 4, "f32"),
     (64, 128, 1, "f32"), (64, 64, 1, "bf16"), (16, 32, 2, "bf16"),
+    (16, 16, 4, "f32"), (48, 32, 4, "bf16"),
 ])
 def test_tokens_shapes_one_group(P, N, R, dt):
     """Calls of at most four tokens take kernels specialised for one group
