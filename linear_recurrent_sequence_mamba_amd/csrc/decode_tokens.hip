@@ -790,6 +790,9 @@ template <typename TI, typename TO, int N, bool PREV, bool PREP, bool ONEG>
 // whose loop needs a few more registers)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG && !PREP ? M3_GRP_WAVES : 4))) void k_decode_mimo_grp(DecodeArgs a) {
   constexpr int R = 4, KG = kTokGroup, NT = N / 16, NE = N * R;
+  // threads 0 .. N/2 - 1 build the phases and threads 64 .. 93 the decay
+  // tables, side by side; one 16-row block per wave (P <= 64)
+  static_assert(N % 16 == 0 && N <= 128, "group-form state width");
   using TB = GTab<N>;
   constexpr int NHALF = NT >= 2 ? 2 : 1;
   constexpr int HC = N / NHALF;       // columns per transposed piece of the final store
