@@ -159,8 +159,9 @@ def test_tokens_full_shape_sampled(name):
 @pytest.mark.parametrize("R", [1, 4])
 def test_tokens_deterministic_and_nan_stays_in_its_head(R):
     """Two calls on the same inputs agree bit for bit; a NaN in one head's x at
-    token 2 reaches that head's state and its outputs from token 2 on, and
-    nothing else (heads are independent and earlier outputs do not see it)."""
+    token 2 (or in its B at token 1) reaches that head's state and its outputs
+    from that token on, and nothing else (heads are independent and earlier
+    outputs do not see it, also inside one group of four tokens)."""
     K = 4
     w = I.Workload("t", 96, 2, K, 4, 64, 128, R, 64, "bf16", "normal")
     d = _inputs(w)
@@ -176,4 +177,14 @@ def test_tokens_deterministic_and_nan_stays_in_its_head(R):
     bad_y = torch.isnan(y).flatten(3).any(dim=3).cpu()          # [batch, token, head]
     expect = torch.zeros_like(bad_y)
     expect[1, 2:, 3] = True
+    assert torch.equal(bad_y, expect)
+    # a NaN in one head's B at token 1 reaches its outputs from token 1 on
+    Bn = d["B"].clone()
+    Bn[0, 1, 2].view(-1)[7] = float("nan")
+    y, h = _gpu(dict(d, B=Bn))
+    bad_h = torch.isnan(h).flatten(2).any(dim=2).cpu()
+    assert bad_h[0, 2] and bad_h.sum() == 1
+    bad_y = torch.isnan(y).flatten(3).any(dim=3).cpu()
+    expect = torch.zeros_like(bad_y)
+    expect[0, 1:, 2] = True
     assert torch.equal(bad_y, expect)
