@@ -548,6 +548,7 @@ def with_single_thread(all_cores, one):
 # profiled runs of this script (no GPU needed):
 #   python bench.py --summarize-profiles STATS_DIR FETCH_DIR WRITE_DIR BENCH_JSON
 #   python bench.py --summarize-sq SQ1_DIR SQ2_DIR
+#   python bench.py --summarize-sq-decode SQ1_DIR SQ2_DIR
 PROFILE_COPY_BYTES = 268435456   # the device copy of copy_reference(), the counters' calibration
 SRC_DECODE = ["decode.hip", "m3_device.h", "m3_launch.h"]
 SRC_TOKENS = ["decode_tokens.hip", "m3_device.h", "m3_launch.h"]
@@ -561,11 +562,14 @@ PROF_SUM_CMD = ("python3 bench.py --summarize-profiles gpurun_out/prof_default g
                 "gpurun_out/pmc_write gpurun_out/prof_bench.json")
 SQ_ARGS = ("--only siso_prefill,mimo_prefill,siso_prefill_backward,mimo_prefill_backward "
            "--no-cpu-baseline --prefill-steps 2")
+SQ_ARGS_DECODE = "--only mimo_decode,mimo_decode_k4 --no-cpu-baseline --steps 20 --warmup 2"
 SQ_SETS = ("SQ_WAVES SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
            "SQ_INSTS_LDS SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
            "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY "
            "SQ_ACTIVE_INST_ANY SQ_INSTS_SALU")
 MFMA_BF16_FLOPS = 2 * 16 * 16 * 32   # one v_mfma_f32_16x16x32_bf16
+MFMA_F32_FLOPS = 2 * 16 * 16 * 4     # one v_mfma_f32_16x16x4_f32 (the decode kernels' only MFMA)
+MFMA_F32_PEAK_TFLOPS = 157.3         # dense fp32 matrix (MI355X)
 PREFILL_KERNELS = ("k_chunk_state", "k_state_pass", "k_chunk_output", "k_varlen_", "k_bwd_")
 
 
@@ -814,9 +818,17 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir, bench_json, out_dir):
         fh.write("\n".join(ht) + "\n")
 
 
-def summarize_sq(sq1_dir, sq2_dir, out_dir):
-    """mfma_valu_prefill_backward.txt from two SQ counter runs of the prefill
-    and backward workloads."""
+def summarize_sq(sq1_dir, sq2_dir, out_dir, kind="prefill"):
+    """mfma_valu_prefill_backward.txt (kind "prefill") or
+    mfma_valu_mimo_decode.txt (kind "decode") from two SQ counter runs of the
+    prefill and backward workloads, or of the rank-4 decode workloads (one
+    step, four tokens per call).  The prefill kernels' MFMAs are bf16
+    16x16x32, priced at the dense bf16 peak; the decode kernels' are fp32
+    16x16x4, priced at the dense fp32 matrix peak."""
+    dec = kind == "decode"
+    flops, peak = (MFMA_F32_FLOPS, MFMA_F32_PEAK_TFLOPS) if dec else (MFMA_BF16_FLOPS, MFMA_PEAK_TFLOPS)
+    args, sum_flag = (SQ_ARGS_DECODE, "--summarize-sq-decode") if dec else (SQ_ARGS, "--summarize-sq")
+    tag = "D" if dec else "M"
     def counters(d):
         acc = {}
         for r in _prof_csv(d, "counter_collection.csv"):
@@ -834,37 +846,46 @@ def summarize_sq(sq1_dir, sq2_dir, out_dir):
     for n, c in c1.items():
         t = sum(times[n]) / len(times[n]) if times.get(n) else float("nan")
         mf, va, lds = c.get("SQ_INSTS_MFMA", 0.0), c.get("SQ_INSTS_VALU", 0.0), c.get("SQ_INSTS_LDS", 0.0)
-        mfma_ms = mf * MFMA_BF16_FLOPS / (MFMA_PEAK_TFLOPS * 1e12) * 1e3
+        mfma_ms = mf * flops / (peak * 1e12) * 1e3
         valu_ms = va * 4 / (1024 * 2.4e9) * 1e3
         conf = c2.get(n, {}).get("SQ_LDS_BANK_CONFLICT", float("nan"))
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
         rows.append((t, n, mf, mfma_ms, mfma_ms / (t / 1e3) if t == t else 0.0, va, valu_ms,
                      valu_ms / (t / 1e3) if t == t else 0.0, conf / lds if lds else 0.0, busy / mf if mf else 0.0))
     rows.sort(reverse=True)
-    cmd = "rocprofv3 {k}--pmc {s} -f csv -d gpurun_out/pmcM{i} -o run -- python3 bench.py " + SQ_ARGS
-    txt = ["# Matrix-core (MFMA) and VALU use of the prefill and backward kernels, MI355X (gfx950)", "#",
+    cmd = "rocprofv3 {k}--pmc {s} -f csv -d gpurun_out/pmc{t}{i} -o run -- python3 bench.py " + args
+    if dec:
+        what = "the rank-4 decode kernels (one step; four tokens per call in group form)"
+        pricing = [f"# mfma_ms: the executed MFMA work (SQ_INSTS_MFMA x {flops} flops for v_mfma_f32_16x16x4_f32,",
+                   "#   i.e. 16 x 16 x 4 multiply-adds at 2 flops each) at the dense fp32 matrix peak of",
+                   "#   157.3 TFLOP/s; mfma_use = mfma_ms / time."]
+    else:
+        what = "the prefill and backward kernels"
+        pricing = [f"# mfma_ms: the executed MFMA work (SQ_INSTS_MFMA x {flops} flops for "
+                   "v_mfma_f32_16x16x32_bf16, i.e.",
+                   "#   16 x 16 x 32 multiply-adds at 2 flops each, hi/lo operand splits included) at the dense bf16",
+                   "#   peak of 2.5 PFLOP/s; mfma_use = mfma_ms / time.",
+                   "#   SQ_VALU_MFMA_BUSY_CYCLES reads 16 per such instruction in every kernel (busy/mfma)."]
+    txt = [f"# Matrix-core (MFMA) and VALU use of {what}, MI355X (gfx950)", "#",
            "# commands (from the repository root, after `export TMPDIR=/tmp`), one counter set per run:",
-           "#   " + cmd.format(k="--kernel-trace ", s=SQ_SETS[0], i=1), "#   " + cmd.format(k="", s=SQ_SETS[1], i=2),
-           "#   python3 bench.py --summarize-sq gpurun_out/pmcM1 gpurun_out/pmcM2",
+           "#   " + cmd.format(k="--kernel-trace ", s=SQ_SETS[0], t=tag, i=1),
+           "#   " + cmd.format(k="", s=SQ_SETS[1], t=tag, i=2),
+           f"#   python3 bench.py {sum_flag} gpurun_out/pmc{tag}1 gpurun_out/pmc{tag}2",
            "# per dispatch, mean over the dispatches of the run; time_us = the kernel-trace durations of the",
-           "#   first run (kernels serialised by the counter collection).", "#",
-           f"# mfma_ms: the executed MFMA work (SQ_INSTS_MFMA x {MFMA_BF16_FLOPS} flops for "
-           "v_mfma_f32_16x16x32_bf16, i.e.",
-           "#   16 x 16 x 32 multiply-adds at 2 flops each, hi/lo operand splits included) at the dense bf16",
-           "#   peak of 2.5 PFLOP/s; mfma_use = mfma_ms / time.",
-           "#   SQ_VALU_MFMA_BUSY_CYCLES reads 16 per such instruction in every kernel (busy/mfma).",
+           "#   first run (kernels serialised by the counter collection).", "#"] + pricing + [
            "# valu_ms: SQ_INSTS_VALU at one wave64 instruction per 4 cycles per SIMD (1024 SIMDs, 2.4 GHz);",
            "#   valu_use = valu_ms / time.  The two pipes run side by side (different waves), so the uses do",
            "#   not add up.",
-           "# lds_conf: SQ_LDS_BANK_CONFLICT cycles per LDS instruction.",
+           "# lds_conf: SQ_LDS_BANK_CONFLICT cycles per LDS instruction."] + ([] if dec else [
            "# k_chunk_state and k_state_pass at a single input appear at both chunk lengths (the forward at 128",
-           "#   tokens, the backward's recomputed states at 64); rows of one name and template are merged.", "",
+           "#   tokens, the backward's recomputed states at 64); rows of one name and template are merged."]) + ["",
            f"{'kernel':70s} {'time_us':>8s} {'MFMA_inst':>10s} {'mfma_ms':>8s} {'mfma_use':>8s} {'VALU_inst':>10s} "
            f"{'valu_ms':>8s} {'valu_use':>8s} {'lds_conf':>8s} {'busy/mfma':>9s}"]
     for t, n, mf, mms, mu, va, vms, vu, lc, bpm in rows:
         txt.append(f"{n[:70]:70s} {t:8.1f} {mf:10.3g} {mms:8.3f} {mu:8.3f} {va:10.4g} {vms:8.3f} {vu:8.3f} "
                    f"{lc:8.3f} {bpm:9.1f}")
-    with open(os.path.join(out_dir, "mfma_valu_prefill_backward.txt"), "w") as fh:
+    name = "mfma_valu_mimo_decode.txt" if dec else "mfma_valu_prefill_backward.txt"
+    with open(os.path.join(out_dir, name), "w") as fh:
         fh.write("\n".join(txt) + "\n")
 
 
@@ -881,14 +902,18 @@ def main():
                     help="write the rocprofv3 summaries under profiles/ from a profiled run's CSV files and exit")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ1_DIR", "SQ2_DIR"),
                     help="write the MFMA/VALU summary under profiles/ from two SQ counter runs and exit")
+    ap.add_argument("--summarize-sq-decode", nargs=2, metavar=("SQ1_DIR", "SQ2_DIR"),
+                    help="the same for the rank-4 decode kernels' SQ counter runs")
     ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"),
                     help="directory the summaries go to (default: profiles/)")
     a = ap.parse_args()
-    if a.summarize_profiles or a.summarize_sq:   # no GPU needed
+    if a.summarize_profiles or a.summarize_sq or a.summarize_sq_decode:   # no GPU needed
         if a.summarize_profiles:
             summarize_profiles(*a.summarize_profiles, a.profiles_out)
         if a.summarize_sq:
             summarize_sq(*a.summarize_sq, a.profiles_out)
+        if a.summarize_sq_decode:
+            summarize_sq(*a.summarize_sq_decode, a.profiles_out, kind="decode")
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode and prefill kernels run on a "

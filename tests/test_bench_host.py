@@ -136,3 +136,44 @@ def test_summarize_cli_needs_no_gpu(tmp_path):
 ])
 def test_kernel_short_names(name, short):
     assert bench._prof_short(name) == short
+
+
+def _sq_dirs(tmp, kernel, mfma, valu, lds, conflicts, dur_ns):
+    """Two SQ counter runs (and the first run's kernel trace) of one dispatch."""
+    sq1, sq2 = os.path.join(tmp, "sq1"), os.path.join(tmp, "sq2")
+    vals = {"SQ_INSTS_MFMA": mfma, "SQ_INSTS_VALU": valu, "SQ_INSTS_LDS": lds}
+    _write(os.path.join(sq1, "x", "run_counter_collection.csv"),
+           [dict(Dispatch_Id=1, Kernel_Name=kernel, Grid_Size=1, Counter_Name=c, Counter_Value=vals.get(c, 1.0))
+            for c in bench.SQ_SETS[0].split()])
+    _write(os.path.join(sq1, "x", "run_kernel_trace.csv"),
+           [dict(Dispatch_Id=1, Kernel_Name=kernel, Grid_Size=1, Start_Timestamp=0, End_Timestamp=dur_ns)])
+    _write(os.path.join(sq2, "x", "run_counter_collection.csv"),
+           [dict(Dispatch_Id=1, Kernel_Name=kernel, Grid_Size=1, Counter_Name=c,
+                 Counter_Value=conflicts if c == "SQ_LDS_BANK_CONFLICT" else 1.0)
+            for c in bench.SQ_SETS[1].split()])
+    return sq1, sq2
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_summarize_sq(tmp_path, kind):
+    """The decode kernels' MFMAs (fp32 16x16x4) are priced at the fp32 matrix
+    peak, the prefill kernels' (bf16 16x16x32) at the bf16 peak."""
+    kern = ("void m3::k_decode_mimo_grp<m3::bf16_t, float, 128, true, false, true>(m3::DecodeArgs)"
+            if kind == "decode" else K3)
+    dirs = _sq_dirs(str(tmp_path), kern, mfma=1e9, valu=2e8, lds=1000.0, conflicts=500.0, dur_ns=1_000_000)
+    out = tmp_path / "out"
+    out.mkdir()
+    bench.summarize_sq(*dirs, str(out), kind=kind)
+    name = "mfma_valu_mimo_decode.txt" if kind == "decode" else "mfma_valu_prefill_backward.txt"
+    txt = (out / name).read_text()
+    row = [ln for ln in txt.splitlines() if ln.startswith(bench._prof_short(kern)[:60])]
+    assert len(row) == 1
+    f = row[0][70:].split()
+    flops, peak = ((2 * 16 * 16 * 4, 157.3) if kind == "decode" else (2 * 16 * 16 * 32, 2500.0))
+    mfma_ms = 1e9 * flops / (peak * 1e12) * 1e3
+    assert float(f[0]) == pytest.approx(1000.0)                      # time_us
+    assert float(f[2]) == pytest.approx(mfma_ms, abs=1e-3)            # mfma_ms
+    assert float(f[3]) == pytest.approx(mfma_ms / 1.0, abs=2e-3)      # use over 1 ms
+    assert float(f[7]) == pytest.approx(0.5)                          # conflict cycles per LDS instruction
+    flag = "--summarize-sq-decode" if kind == "decode" else "--summarize-sq "
+    assert flag in txt
