@@ -753,10 +753,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG ? M3_M
 //    product, X (the lane's own x values) times the masked Gram of the
 //    group's rotated B and C rows (computed once per block on the MFMA, the
 //    four waves taking a quarter of N each);
-//  * the state update: the rank-4 terms of all KG + 1 tokens as MFMA
-//    products with K = 4 (KG + 1), then one rotation by Phi_K.
-// The token work per group is about a third of the token-by-token kernel's,
-// which lets it hide under the state stream.
+//  * the state update: the rank-4 terms of the KG + 1 tokens as MFMA
+//    products with K = 4 per token, then one rotation by Phi_K.
+// The token work per group is about a third of the token-by-token kernel's;
+// what is left of a call's time is mostly each block's memory round trips
+// (its group inputs, then its state).
 constexpr double kTwoPiD = 6.283185307179586476925286766559;
 
 template <int N>
@@ -784,10 +785,10 @@ struct alignas(16) GTab {
 #define M3_GRP_WAVES 5
 #endif
 
-template <typename TI, typename TO, int N, bool PREV, bool PREP, bool ONEG>
 // (one group: five waves per SIMD, 32 KB of LDS at N = 128 and at most 96
 // registers; four with the B/C preparation's tables or with several groups,
 // whose loop needs a few more registers)
+template <typename TI, typename TO, int N, bool PREV, bool PREP, bool ONEG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEG && !PREP ? M3_GRP_WAVES : 4))) void k_decode_mimo_grp(DecodeArgs a) {
   constexpr int R = 4, KG = kTokGroup, NT = N / 16, NE = N * R;
   // threads 0 .. N/2 - 1 build the phases and threads 64 .. 93 the decay
